@@ -1,0 +1,308 @@
+"""CPU oracle for the fused GEMM-Residual-RMSNorm-GEMM block and the SwiGLU
+gate/up block: plain, unfused definitions in numpy float64.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import or call this module.  The library's
+product path (its HIP kernels, C-ABI and Python binding) never imports it, and
+this module imports nothing from the library.
+
+Sources.  The pages are three news articles on the paper "CODA: Rewriting
+Transformer Blocks as GEMM-Epilogue Programs":
+  [JA]  toolin.ai blog, "CODA：LLMと初心者が光速のGPUカーネルを書けるようにする"
+  [RU]  kucoin.com news flash (Russian) on the same paper
+  [FR]  kucoin.com news flash (French) on the same paper
+Their sections are cited by heading: [JA] 核心の洞察 = the insight section,
+[RU] "CODA: В «Финале» спрятаны сокровища", [FR] "CODA : « La fin » cache
+un trésor", [JA] 組み合わせ可能な5種類の「積み木」 / [RU] "Пять «кирпичиков»"
+/ [FR] "Cinq « blocs »" = the five epilogue primitives.
+
+What the pages fix, and the readings taken where they are silent:
+  * GEMM-RMSNorm-GEMM: a GEMM, a residual add, RMS normalisation, then a second
+    GEMM ([RU] insight section: the pattern runs a matmul, a residual add, RMS
+    normalisation, another matmul).  The pages give no formula.  Reading: y =
+    X W1 + R; r_i = (mean_j y_ij^2 + eps)^(-1/2), the mean over the normalised
+    width d, eps inside the root; h = diag(r) y diag(gamma) (a plain scale by
+    gamma, no bias); z = h W2.
+  * The row scale r is one scalar per row and commutes with the second GEMM, so
+    it can be applied after it; the first GEMM only leaves per-tile partial sums
+    of squares that a small kernel combines ([JA] 核心の洞察; [RU] and [FR]
+    insight sections).  ``ref_fwd_rewritten`` and ``ref_partials`` write that
+    rewrite out; it reaches the same z up to rounding order.
+  * The backward is the exact gradient of L = <dz, z>; the pages state a
+    theorem that the backward inherits the forward's block-local structure but
+    not its content ([RU]/[FR] insight sections).  ``ref_bwd`` is the
+    hand-derived gradient of the definitions above, written unfused.
+  * SwiGLU in the activation epilogue ([JA]/[RU]/[FR] primitives sections,
+    "elementwise transform ... activation").  Reading: gu = X W with W =
+    [W_gate | W_up] (gate columns first), a = silu(g) * u with silu(t) =
+    t * sigmoid(t), z = a Wd.
+  * Saved activations are stored for the backward ([JA]/[RU]/[FR] primitives
+    sections, "matrix tile load/store ... saving intermediates").  Reading: the
+    backward functions take the saved tensors (y and r; gu and a) as inputs, so
+    a caller can pass them rounded to the storage dtype.
+
+Every function here is pinned by a test against something other than itself
+(brute-force loops, finite differences, torch CPU autograd, closed forms and
+invariants, a hand-worked example); see the ``tests/test_oracle_*.py`` files.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_rne", "ref_fwd", "ref_fwd_rewritten", "ref_partials", "ref_bwd",
+    "ref_fwd_rows", "ref_bwd_sampled", "sigmoid", "ref_swiglu_fwd",
+    "ref_swiglu_bwd", "ref_swiglu_fwd_rows", "ref_swiglu_bwd_sampled",
+]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding (storage contract of saved activations and outputs)
+# ---------------------------------------------------------------------------
+
+def bf16_rne(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits and fp32's exponent range.  A finite x is
+    written m * 2**e with 0.5 <= |m| < 1 (frexp); below 2**-126 the spacing
+    stays at that of the smallest normal binade.  The value is scaled so that
+    one bf16 step is 1, rounded with numpy's rint (ties to even), and scaled
+    back.  Results beyond the largest bf16 value become +-inf.  This is one
+    rounding straight from float64, not via float32.
+    """
+    x = _f64(x)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    xm = x[fin]
+    _, e = np.frexp(xm)
+    e = np.maximum(e, -125)           # |x| < 2**-126: subnormal spacing 2**-133
+    step_exp = e - 8                  # 8 significant bits
+    q = np.rint(np.ldexp(xm, -step_exp))
+    v = np.ldexp(q, step_exp)
+    max_bf16 = np.ldexp(255.0, 120)   # (2 - 2**-7) * 2**127
+    v = np.where(np.abs(v) > max_bf16, np.copysign(np.inf, v), v)
+    out[fin] = v
+    return out
+
+
+# ---------------------------------------------------------------------------
+# GEMM-Residual-RMSNorm-GEMM, forward
+# ---------------------------------------------------------------------------
+
+def ref_fwd(X, W1, R, gamma, W2, eps: float) -> dict:
+    """Unfused forward: y = X W1 + R; r = (mean_j y^2 + eps)^-1/2;
+    h = diag(r) y diag(gamma); z = h W2.
+
+    Returns y, ms (row mean squares), r, h and z, all float64.
+    The pattern follows [RU]/[FR] insight sections (matmul, residual add, RMS
+    normalisation, matmul); the formula of r is the reading stated in the module
+    header.
+    """
+    X, W1, R, gamma, W2 = map(_f64, (X, W1, R, gamma, W2))
+    y = X @ W1 + R
+    ms = np.mean(y * y, axis=1)
+    r = 1.0 / np.sqrt(ms + eps)
+    h = (y * r[:, None]) * gamma[None, :]
+    z = h @ W2
+    return {"y": y, "ms": ms, "r": r, "h": h, "z": z}
+
+
+def ref_partials(y, BN: int) -> np.ndarray:
+    """Per-row, per-column-tile partial sums of squares.
+
+    P[i, t] = sum of y[i, j]**2 over j in [t*BN, min((t+1)*BN, d)); the last
+    tile may be ragged.  This is the tile-wise reduction the first GEMM's
+    epilogue leaves behind ([RU] insight section: a local "partial RMS" at the
+    end of the first GEMM, combined by a light reduction kernel; [FR] same
+    section).
+    """
+    y = _f64(y)
+    M, d = y.shape
+    T = -(-d // BN)
+    P = np.zeros((M, T))
+    for t in range(T):
+        blk = y[:, t * BN:min((t + 1) * BN, d)]
+        P[:, t] = np.sum(blk * blk, axis=1)
+    return P
+
+
+def ref_fwd_rewritten(X, W1, R, gamma, W2, eps: float, BN: int = 256) -> dict:
+    """The rewritten forward of the pages' insight section: the row scale is
+    deferred past the second GEMM.
+
+    y = X W1 + R; P = per-tile partial sums of squares of y; r_i = (sum_t
+    P[i,t] / d + eps)^-1/2; W2' = diag(gamma) W2; z = diag(r) (y W2').
+    ([JA] 核心の洞察: r commutes with the following matmul so applying it moves
+    into the second GEMM's epilogue; [RU]/[FR] insight sections add the partial
+    RMS and the reduction kernel.)  Same z as ``ref_fwd`` up to rounding order.
+    """
+    X, W1, R, gamma, W2 = map(_f64, (X, W1, R, gamma, W2))
+    y = X @ W1 + R
+    d = y.shape[1]
+    P = ref_partials(y, BN)
+    r = 1.0 / np.sqrt(P.sum(axis=1) / d + eps)
+    W2f = gamma[:, None] * W2
+    z = r[:, None] * (y @ W2f)
+    return {"y": y, "P": P, "r": r, "W2f": W2f, "z": z}
+
+
+# ---------------------------------------------------------------------------
+# GEMM-Residual-RMSNorm-GEMM, backward
+# ---------------------------------------------------------------------------
+
+def ref_bwd(X, W1, gamma, W2, y, r, dz) -> dict:
+    """Exact gradient of L = <dz, z> for the forward of ``ref_fwd``, given the
+    saved y and r.
+
+    With n = diag(r) y and h = n diag(gamma):
+      dW2 = h^T dz;  dh = dz W2^T;  dgamma_j = sum_i dh_ij n_ij;
+      dn = dh diag(gamma);  s_i = sum_j dn_ij y_ij;  c_i = r_i^3 s_i / d;
+      dy = diag(r) dn - diag(c) y;  dR = dy;  dX = dy W1^T;  dW1 = X^T dy.
+    (dr_i/dy_ik = -r_i^3 y_ik / d gives the -c y term.)  The gradient reaches y
+    only through z, so dR = dy.
+    """
+    X, W1, gamma, W2, y, r, dz = map(_f64, (X, W1, gamma, W2, y, r, dz))
+    d = y.shape[1]
+    n = y * r[:, None]
+    h = n * gamma[None, :]
+    dW2 = h.T @ dz
+    dh = dz @ W2.T
+    dgamma = np.sum(dh * n, axis=0)
+    dn = dh * gamma[None, :]
+    s = np.sum(dn * y, axis=1)
+    c = r ** 3 * s / d
+    dy = dn * r[:, None] - c[:, None] * y
+    dX = dy @ W1.T
+    dW1 = X.T @ dy
+    return {"dX": dX, "dW1": dW1, "dR": dy, "dW2": dW2, "dgamma": dgamma,
+            "dh": dh, "dn": dn, "n": n, "s": s, "c": c, "dy": dy}
+
+
+# ---------------------------------------------------------------------------
+# Sampled forms for workloads too large to evaluate whole on the host.
+# They restrict the same definitions to chosen rows or columns.
+# ---------------------------------------------------------------------------
+
+def ref_fwd_rows(X, W1, R, gamma, W2, eps: float, rows) -> dict:
+    """``ref_fwd`` evaluated for the given rows only (rows are independent)."""
+    rows = np.asarray(rows)
+    X = _f64(X[rows])
+    R = _f64(R[rows])
+    out = ref_fwd(X, W1, R, gamma, W2, eps)
+    out["rows"] = rows
+    return out
+
+
+def ref_bwd_sampled(X, W1, gamma, W2, y, r, dz, rows, cols_d, cols_N) -> dict:
+    """``ref_bwd`` with dX and dR restricted to ``rows``, dW1 to the columns
+    ``cols_d`` and dW2 to the columns ``cols_N``; dgamma, s and c in full.
+
+    s and c need every row's dh, so dh = dz W2^T is formed whole (the one
+    large product).  The rest is the definitions restricted.
+    """
+    X, W1, gamma, W2, y, r = map(_f64, (X, W1, gamma, W2, y, r))
+    dz = _f64(dz)
+    d = y.shape[1]
+    n = y * r[:, None]
+    dh = dz @ W2.T
+    dgamma = np.sum(dh * n, axis=0)
+    dn = dh * gamma[None, :]
+    s = np.sum(dn * y, axis=1)
+    c = r ** 3 * s / d
+    rows = np.asarray(rows)
+    cols_d = np.asarray(cols_d)
+    cols_N = np.asarray(cols_N)
+    dy_rows = dn[rows] * r[rows, None] - c[rows, None] * y[rows]
+    dX_rows = dy_rows @ W1.T
+    dy_cols = dn[:, cols_d] * r[:, None] - c[:, None] * y[:, cols_d]
+    dW1_cols = X.T @ dy_cols
+    h = n * gamma[None, :]
+    dW2_cols = h.T @ dz[:, cols_N]
+    return {"rows": rows, "cols_d": cols_d, "cols_N": cols_N,
+            "dR_rows": dy_rows, "dX_rows": dX_rows, "dW1_cols": dW1_cols,
+            "dW2_cols": dW2_cols, "dgamma": dgamma, "s": s, "c": c}
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU gate/up GEMM with the activation in the epilogue
+# ---------------------------------------------------------------------------
+
+def sigmoid(t) -> np.ndarray:
+    """Logistic function 1/(1+exp(-t)), using exp(t)/(1+exp(t)) for t < 0 so
+    that no exp overflows."""
+    t = _f64(t)
+    out = np.empty_like(t)
+    pos = t >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-t[pos]))
+    et = np.exp(t[~pos])
+    out[~pos] = et / (1.0 + et)
+    return out
+
+
+def ref_swiglu_fwd(X, W, Wd) -> dict:
+    """gu = X W; g = gu[:, :F], u = gu[:, F:]; a = g sigmoid(g) u; z = a Wd."""
+    X, W, Wd = map(_f64, (X, W, Wd))
+    F = W.shape[1] // 2
+    gu = X @ W
+    g, u = gu[:, :F], gu[:, F:]
+    a = g * sigmoid(g) * u
+    z = a @ Wd
+    return {"gu": gu, "a": a, "z": z}
+
+
+def ref_swiglu_bwd(X, W, Wd, gu, a, dz) -> dict:
+    """Exact gradient of L = <dz, z> for ``ref_swiglu_fwd`` given saved gu, a.
+
+    da = dz Wd^T; with sg = sigmoid(g):
+      dg = da u sg (1 + g (1 - sg));  du = da g sg;
+      dWd = a^T dz;  dgu = [dg | du];  dW = X^T dgu;  dX = dgu W^T.
+    """
+    X, W, Wd, gu, a, dz = map(_f64, (X, W, Wd, gu, a, dz))
+    F = W.shape[1] // 2
+    g, u = gu[:, :F], gu[:, F:]
+    sg = sigmoid(g)
+    da = dz @ Wd.T
+    dg = da * u * sg * (1.0 + g * (1.0 - sg))
+    du = da * g * sg
+    dgu = np.concatenate([dg, du], axis=1)
+    return {"dX": dgu @ W.T, "dW": X.T @ dgu, "dWd": a.T @ dz,
+            "dgu": dgu, "da": da}
+
+
+def ref_swiglu_fwd_rows(X, W, Wd, rows) -> dict:
+    """``ref_swiglu_fwd`` for the given rows only."""
+    rows = np.asarray(rows)
+    out = ref_swiglu_fwd(_f64(X[rows]), W, Wd)
+    out["rows"] = rows
+    return out
+
+
+def ref_swiglu_bwd_sampled(X, W, Wd, gu, a, dz, rows, cols_W, cols_Wd) -> dict:
+    """``ref_swiglu_bwd`` with dX and dgu restricted to ``rows``, dW to columns
+    ``cols_W`` (indices into [0, 2F)) and dWd to columns ``cols_Wd``."""
+    X, W, Wd = map(_f64, (X, W, Wd))
+    F = W.shape[1] // 2
+    rows = np.asarray(rows)
+    cols_W = np.asarray(cols_W)
+    cols_Wd = np.asarray(cols_Wd)
+    dz = _f64(dz)
+    gu = _f64(gu)
+    # rows: the whole gradient chain restricted to these rows
+    sub = ref_swiglu_bwd(X[rows], W, Wd, gu[rows], _f64(a[rows]), dz[rows])
+    # dW columns: need dgu[:, cols] over every row
+    jg = cols_W % F
+    is_gate = cols_W < F
+    da_c = dz @ Wd.T[:, jg]
+    g = gu[:, jg]
+    u = gu[:, F + jg]
+    sg = sigmoid(g)
+    dgu_c = np.where(is_gate[None, :], da_c * u * sg * (1.0 + g * (1.0 - sg)), da_c * g * sg)
+    dW_cols = X.T @ dgu_c
+    dWd_cols = _f64(a).T @ dz[:, cols_Wd]
+    return {"rows": rows, "cols_W": cols_W, "cols_Wd": cols_Wd,
+            "dX_rows": sub["dX"], "dgu_rows": sub["dgu"],
+            "dW_cols": dW_cols, "dWd_cols": dWd_cols}

@@ -1,0 +1,392 @@
+"""Pins of the CPU oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` takes an object ``O`` exposing the oracle's functions and
+raises AssertionError when the oracle disagrees with the pinned fact.  The
+oracle tests call them with the real oracle; the mutation tests call them with
+copies that carry one planted mistake and require that some pin fails.
+
+Kinds of pin used here:
+  * brute force: pure-Python loops over tiny inputs, written from the
+    definitions independently of numpy;
+  * finite differences: the backward against central differences of the
+    forward's loss L = <dz, z>;
+  * library routines: torch CPU float64 ``F.rms_norm``, ``F.silu`` and autograd;
+  * closed forms and hand-worked examples (tests/golden/);
+  * invariants of the mathematics (homogeneity, linearity in a weight).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from types import SimpleNamespace
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def oracle_namespace(**overrides):
+    import oracle
+    ns = {k: getattr(oracle, k) for k in oracle.__all__}
+    ns.update(overrides)
+    return SimpleNamespace(**ns)
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    scale = max(1.0, float(np.max(np.abs(b))) if b.size else 1.0)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol * scale, f"{what}: max abs err {err:.3e} > {tol:.1e} * {scale:.3g}"
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _coda_case(seed, M, K, d, N, eps=1e-6):
+    g = _rng(seed)
+    return dict(X=g.standard_normal((M, K)), W1=g.standard_normal((K, d)) / math.sqrt(K),
+                R=g.standard_normal((M, d)), gamma=1 + 0.1 * g.standard_normal(d),
+                W2=g.standard_normal((d, N)) / math.sqrt(d), dz=g.standard_normal((M, N)),
+                eps=eps)
+
+
+def _loss_fwd(O, c):
+    z = O.ref_fwd(c["X"], c["W1"], c["R"], c["gamma"], c["W2"], c["eps"])["z"]
+    return float(np.sum(c["dz"] * z))
+
+
+def _bwd_exact(O, c):
+    f = O.ref_fwd(c["X"], c["W1"], c["R"], c["gamma"], c["W2"], c["eps"])
+    return O.ref_bwd(c["X"], c["W1"], c["gamma"], c["W2"], f["y"], f["r"], c["dz"]), f
+
+
+# ---------------------------------------------------------------- forward pins
+
+def pin_fwd_bruteforce(O):
+    """Pure-Python loops at M,K,d,N = 3,4,5,6 against ref_fwd (y, r, z)."""
+    c = _coda_case(11, 3, 4, 5, 6, eps=1e-3)
+    X, W1, R, gm, W2 = (c[k].tolist() for k in ("X", "W1", "R", "gamma", "W2"))
+    M, K, d, N = 3, 4, 5, 6
+    y = [[sum(X[i][k] * W1[k][j] for k in range(K)) + R[i][j] for j in range(d)] for i in range(M)]
+    r = [1.0 / math.sqrt(sum(v * v for v in y[i]) / d + c["eps"]) for i in range(M)]
+    z = [[sum(r[i] * y[i][j] * gm[j] * W2[j][n] for j in range(d)) for n in range(N)] for i in range(M)]
+    f = O.ref_fwd(c["X"], c["W1"], c["R"], c["gamma"], c["W2"], c["eps"])
+    _close(f["y"], y, 1e-13, "y vs loops")
+    _close(f["r"], r, 1e-13, "r vs loops")
+    _close(f["z"], z, 1e-13, "z vs loops")
+
+
+def pin_fwd_torch_rmsnorm(O):
+    """torch CPU float64: F.rms_norm(X W1 + R, (d,), gamma, eps) @ W2 (library routine)."""
+    import torch
+    import torch.nn.functional as F
+    c = _coda_case(12, 16, 24, 40, 56, eps=1e-5)
+    t = {k: torch.from_numpy(np.asarray(c[k])) for k in ("X", "W1", "R", "gamma", "W2")}
+    yt = t["X"] @ t["W1"] + t["R"]
+    ht = F.rms_norm(yt, (yt.shape[1],), t["gamma"], c["eps"])
+    zt = ht @ t["W2"]
+    f = O.ref_fwd(c["X"], c["W1"], c["R"], c["gamma"], c["W2"], c["eps"])
+    _close(f["h"], ht.numpy(), 1e-13, "h vs torch rms_norm")
+    _close(f["z"], zt.numpy(), 1e-13, "z vs torch rms_norm")
+
+
+def pin_fwd_constant_rows(O):
+    """W1 = 0 and rows of R constant (c_i): r_i = (c_i^2 + eps)^-1/2 and
+    z_i = r_i c_i sum_j gamma_j W2[j, :] (closed form)."""
+    g = _rng(13)
+    M, K, d, N, eps = 5, 7, 9, 4, 0.3
+    cvals = np.array([0.0, 1.0, -2.0, 0.5, 3.0])
+    R = np.repeat(cvals[:, None], d, axis=1)
+    gamma = 1 + 0.1 * g.standard_normal(d)
+    W2 = g.standard_normal((d, N))
+    f = O.ref_fwd(g.standard_normal((M, K)), np.zeros((K, d)), R, gamma, W2, eps)
+    r_cf = 1.0 / np.sqrt(cvals ** 2 + eps)
+    _close(f["r"], r_cf, 1e-14, "r closed form")
+    _close(f["z"], (r_cf * cvals)[:, None] * (gamma @ W2)[None, :], 1e-13, "z closed form")
+
+
+def pin_fwd_scale_invariance(O):
+    """With eps = 0, z(aX, aR) = z(X, R) for a > 0 (RMSNorm is 0-homogeneous)."""
+    c = _coda_case(14, 6, 8, 10, 12, eps=0.0)
+    z1 = O.ref_fwd(c["X"], c["W1"], c["R"], c["gamma"], c["W2"], 0.0)["z"]
+    z2 = O.ref_fwd(3.7 * c["X"], c["W1"], 3.7 * c["R"], c["gamma"], c["W2"], 0.0)["z"]
+    _close(z2, z1, 1e-13, "scale invariance")
+
+
+def pin_partials(O):
+    """P from loops at a ragged tile width, and sum_t P[i, t] = d * ms_i."""
+    g = _rng(15)
+    y = g.standard_normal((4, 23))
+    BN = 8
+    P = O.ref_partials(y, BN)
+    loops = [[sum(float(y[i, j]) ** 2 for j in range(t * BN, min(t * BN + BN, 23))) for t in range(3)]
+             for i in range(4)]
+    _close(P, loops, 1e-14, "partials vs loops")
+    c = _coda_case(16, 5, 6, 40, 7)
+    f = O.ref_fwd(c["X"], c["W1"], c["R"], c["gamma"], c["W2"], c["eps"])
+    _close(O.ref_partials(f["y"], 16).sum(axis=1), 40 * f["ms"], 1e-13, "sum of partials")
+
+
+def pin_rewrite_equals_unfused(O):
+    """z = diag(r) (y (diag(gamma) W2)) with r from partials equals the unfused z."""
+    c = _coda_case(17, 9, 16, 48, 20, eps=1e-5)
+    a = O.ref_fwd(c["X"], c["W1"], c["R"], c["gamma"], c["W2"], c["eps"])
+    b = O.ref_fwd_rewritten(c["X"], c["W1"], c["R"], c["gamma"], c["W2"], c["eps"], BN=16)
+    _close(b["r"], a["r"], 1e-14, "r rewritten")
+    _close(b["z"], a["z"], 1e-13, "z rewritten")
+    # and both agree with plain loops on a tiny case
+    pin_fwd_bruteforce(O)
+
+
+def _golden_eval(expr, env):
+    return eval(expr, {"__builtins__": {}}, env)  # expressions from a committed fixture
+
+
+def pin_golden_coda(O):
+    """The hand-worked 2x2 cases of tests/golden/coda_worked_example.json."""
+    with open(os.path.join(GOLDEN, "coda_worked_example.json")) as fh:
+        gold = json.load(fh)
+    inp = {k: np.array(v, dtype=np.float64) for k, v in gold["inputs"].items()}
+    env = {"rho": math.sqrt(0.4)}
+    for case in gold["cases"]:
+        eps = case["eps"]
+        f = O.ref_fwd(inp["X"], inp["W1"], inp["R"], inp["gamma"], inp["W2"], eps)
+        b = O.ref_bwd(inp["X"], inp["W1"], inp["gamma"], inp["W2"], f["y"], f["r"], inp["dz"])
+        got = {"y": f["y"], "r": f["r"], "z": f["z"], **{k: b[k] for k in
+               ("dgamma", "dR", "dX", "dW1", "dW2")}}
+        for k, v in case["expect"].items():
+            want = np.vectorize(lambda e: _golden_eval(e, env), otypes=[float])(np.array(v))
+            _close(got[k], want, 1e-14, f"golden eps={eps} {k}")
+
+
+# --------------------------------------------------------------- backward pins
+
+def pin_bwd_finite_differences(O):
+    """Central differences of L = <dz, z> for every input element, tiny shape."""
+    c = _coda_case(21, 3, 4, 5, 6, eps=1e-2)
+    b, _ = _bwd_exact(O, c)
+    grads = {"X": b["dX"], "W1": b["dW1"], "R": b["dR"], "gamma": b["dgamma"], "W2": b["dW2"]}
+    for name, grad in grads.items():
+        base = c[name]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            hstep = 1e-6 * max(1.0, abs(base[idx]))
+            cp = dict(c)
+            arr = base.copy(); arr[idx] += hstep; cp[name] = arr
+            lp = _loss_fwd(O, cp)
+            arr = base.copy(); arr[idx] -= hstep; cp[name] = arr
+            lm = _loss_fwd(O, cp)
+            fd[idx] = (lp - lm) / (2 * hstep)
+        _close(grad, fd, 1e-7, f"d{name} vs finite differences")
+
+
+def pin_bwd_torch_autograd(O):
+    """torch CPU float64 autograd through matmul + add + F.rms_norm + matmul."""
+    import torch
+    import torch.nn.functional as F
+    c = _coda_case(22, 12, 20, 32, 28, eps=1e-5)
+    t = {k: torch.tensor(np.asarray(c[k]), requires_grad=True) for k in ("X", "W1", "R", "gamma", "W2")}
+    y = t["X"] @ t["W1"] + t["R"]
+    z = F.rms_norm(y, (y.shape[1],), t["gamma"], c["eps"]) @ t["W2"]
+    (z * torch.from_numpy(c["dz"])).sum().backward()
+    b, _ = _bwd_exact(O, c)
+    for k, g in (("X", "dX"), ("W1", "dW1"), ("R", "dR"), ("gamma", "dgamma"), ("W2", "dW2")):
+        _close(b[g], t[k].grad.numpy(), 1e-12, f"{g} vs torch autograd")
+
+
+def pin_bwd_invariants(O):
+    """Identities of the mathematics:
+    <dW2, W2> = <dgamma, gamma> = <dz, z> (z linear in W2 and in gamma);
+    sum_j dy_ij y_ij = eps r_i^3 s_i (derivative of z(a y) at a = 1);
+    <dX, X> + <dR, R> = <dW1, W1> + <dR, R> = eps sum_i r_i^3 s_i;
+    dgamma_j = sum_n (n^T dz)_jn W2_jn (second route);
+    s_i = (1/r_i) sum_n dz_in z_in.
+    """
+    c = _coda_case(23, 10, 14, 18, 22, eps=0.05)
+    b, f = _bwd_exact(O, c)
+    L = float(np.sum(c["dz"] * f["z"]))
+    _close(np.sum(b["dW2"] * c["W2"]), L, 1e-12, "<dW2,W2>")
+    _close(np.sum(b["dgamma"] * c["gamma"]), L, 1e-12, "<dgamma,gamma>")
+    # s from its definition, independent of O's intermediate values
+    dn = (c["dz"] @ c["W2"].T) * c["gamma"][None, :]
+    s = np.sum(dn * f["y"], axis=1)
+    rhs = c["eps"] * f["r"] ** 3 * s
+    _close(np.sum(b["dR"] * f["y"], axis=1), rhs, 1e-12, "row identity")
+    tot = float(np.sum(rhs))
+    _close(np.sum(b["dX"] * c["X"]) + np.sum(b["dR"] * c["R"]), tot, 1e-12, "<dX,X>+<dR,R>")
+    _close(np.sum(b["dW1"] * c["W1"]) + np.sum(b["dR"] * c["R"]), tot, 1e-12, "<dW1,W1>+<dR,R>")
+    n = f["y"] * f["r"][:, None]
+    _close(b["dgamma"], np.sum((n.T @ c["dz"]) * c["W2"], axis=1), 1e-12, "dgamma second route")
+    _close(s, np.sum(c["dz"] * f["z"], axis=1) / f["r"], 1e-12, "s from z")
+
+
+def pin_sampled_forms(O):
+    """The row/column-restricted forms equal the corresponding slices of the
+    full forms (which the pins above tie to the mathematics)."""
+    c = _coda_case(24, 20, 12, 16, 24, eps=1e-4)
+    f = O.ref_fwd(c["X"], c["W1"], c["R"], c["gamma"], c["W2"], c["eps"])
+    rows = np.array([0, 7, 19])
+    fr = O.ref_fwd_rows(c["X"], c["W1"], c["R"], c["gamma"], c["W2"], c["eps"], rows)
+    for k in ("y", "r", "z"):
+        _close(fr[k], f[k][rows], 1e-14, f"rows {k}")
+    b = O.ref_bwd(c["X"], c["W1"], c["gamma"], c["W2"], f["y"], f["r"], c["dz"])
+    cd, cn = np.array([1, 5, 15]), np.array([0, 11, 23])
+    bs = O.ref_bwd_sampled(c["X"], c["W1"], c["gamma"], c["W2"], f["y"], f["r"], c["dz"], rows, cd, cn)
+    _close(bs["dX_rows"], b["dX"][rows], 1e-13, "sampled dX")
+    _close(bs["dR_rows"], b["dR"][rows], 1e-13, "sampled dR")
+    _close(bs["dW1_cols"], b["dW1"][:, cd], 1e-13, "sampled dW1")
+    _close(bs["dW2_cols"], b["dW2"][:, cn], 1e-13, "sampled dW2")
+    _close(bs["dgamma"], b["dgamma"], 1e-13, "sampled dgamma")
+
+
+# ----------------------------------------------------------------- SwiGLU pins
+
+def _swiglu_case(seed, M, d, F):
+    g = _rng(seed)
+    return dict(X=g.standard_normal((M, d)), W=g.standard_normal((d, 2 * F)) / math.sqrt(d),
+                Wd=g.standard_normal((F, d)) / math.sqrt(F), dz=g.standard_normal((M, d)))
+
+
+def _swiglu_loss(O, c):
+    return float(np.sum(c["dz"] * O.ref_swiglu_fwd(c["X"], c["W"], c["Wd"])["z"]))
+
+
+def _swiglu_bwd(O, c):
+    f = O.ref_swiglu_fwd(c["X"], c["W"], c["Wd"])
+    return O.ref_swiglu_bwd(c["X"], c["W"], c["Wd"], f["gu"], f["a"], c["dz"]), f
+
+
+def pin_swiglu_bruteforce(O):
+    """Loops at M, d, F = 3, 4, 5 against ref_swiglu_fwd (gate columns first)."""
+    c = _swiglu_case(31, 3, 4, 5)
+    X, W, Wd = (c[k].tolist() for k in ("X", "W", "Wd"))
+    M, d, F = 3, 4, 5
+    gu = [[sum(X[i][k] * W[k][j] for k in range(d)) for j in range(2 * F)] for i in range(M)]
+    a = [[gu[i][j] / (1.0 + math.exp(-gu[i][j])) * gu[i][F + j] for j in range(F)] for i in range(M)]
+    z = [[sum(a[i][j] * Wd[j][n] for j in range(F)) for n in range(d)] for i in range(M)]
+    f = O.ref_swiglu_fwd(c["X"], c["W"], c["Wd"])
+    _close(f["gu"], gu, 1e-13, "gu vs loops")
+    _close(f["a"], a, 1e-13, "a vs loops")
+    _close(f["z"], z, 1e-13, "z vs loops")
+
+
+def pin_swiglu_finite_differences(O):
+    c = _swiglu_case(32, 3, 4, 5)
+    b, _ = _swiglu_bwd(O, c)
+    for name, grad in (("X", b["dX"]), ("W", b["dW"]), ("Wd", b["dWd"])):
+        base = c[name]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            hstep = 1e-6 * max(1.0, abs(base[idx]))
+            cp = dict(c)
+            arr = base.copy(); arr[idx] += hstep; cp[name] = arr
+            lp = _swiglu_loss(O, cp)
+            arr = base.copy(); arr[idx] -= hstep; cp[name] = arr
+            lm = _swiglu_loss(O, cp)
+            fd[idx] = (lp - lm) / (2 * hstep)
+        _close(grad, fd, 1e-7, f"swiglu d{name} vs finite differences")
+
+
+def pin_swiglu_torch(O):
+    """torch CPU float64: F.silu(g) * u with autograd (library routine)."""
+    import torch
+    import torch.nn.functional as Fn
+    c = _swiglu_case(33, 16, 24, 40)
+    t = {k: torch.tensor(c[k], requires_grad=True) for k in ("X", "W", "Wd")}
+    gu = t["X"] @ t["W"]
+    F = c["W"].shape[1] // 2
+    z = (Fn.silu(gu[:, :F]) * gu[:, F:]) @ t["Wd"]
+    (z * torch.from_numpy(c["dz"])).sum().backward()
+    f = O.ref_swiglu_fwd(c["X"], c["W"], c["Wd"])
+    _close(f["z"], z.detach().numpy(), 1e-13, "swiglu z vs torch")
+    b, _ = _swiglu_bwd(O, c)
+    for k in ("X", "W", "Wd"):
+        _close(b["d" + k], t[k].grad.numpy(), 1e-12, f"swiglu d{k} vs torch")
+
+
+def pin_swiglu_invariants(O):
+    """<dWd, Wd> = <dz, z>; <dW[:, F:], W[:, F:]> = <dz, z> (z linear in Wd and
+    in W_up); at g = 0, dg = da u / 2; a huge negative gate gives no NaN."""
+    c = _swiglu_case(34, 9, 12, 14)
+    b, f = _swiglu_bwd(O, c)
+    L = float(np.sum(c["dz"] * f["z"]))
+    F = 14
+    _close(np.sum(b["dWd"] * c["Wd"]), L, 1e-12, "<dWd,Wd>")
+    _close(np.sum(b["dW"][:, F:] * c["W"][:, F:]), L, 1e-12, "<dWu,Wu>")
+    W = c["W"].copy(); W[:, :F] = 0.0
+    f0 = O.ref_swiglu_fwd(c["X"], W, c["Wd"])
+    b0 = O.ref_swiglu_bwd(c["X"], W, c["Wd"], f0["gu"], f0["a"], c["dz"])
+    da = c["dz"] @ c["Wd"].T
+    _close(b0["dgu"][:, :F], 0.5 * da * f0["gu"][:, F:], 1e-13, "g=0 gate gradient")
+    s = O.sigmoid(np.array([-800.0, -30.0, 0.0, 30.0, 800.0]))
+    assert np.all(np.isfinite(s)), "sigmoid overflow"
+    _close(s, [0.0, math.exp(-30) / (1 + math.exp(-30)), 0.5, 1 / (1 + math.exp(-30)), 1.0], 1e-15, "sigmoid")
+
+
+def pin_golden_swiglu(O):
+    with open(os.path.join(GOLDEN, "swiglu_worked_example.json")) as fh:
+        gold = json.load(fh)
+    env = {"L3": math.log(3.0)}
+    ev = np.vectorize(lambda e: _golden_eval(e, env), otypes=[float])
+    for case in gold["cases"]:
+        inp = {k: ev(np.array(v)) for k, v in case["inputs"].items()}
+        f = O.ref_swiglu_fwd(inp["X"], inp["W"], inp["Wd"])
+        b = O.ref_swiglu_bwd(inp["X"], inp["W"], inp["Wd"], f["gu"], f["a"], inp["dz"])
+        got = {**f, **b}
+        for k, v in case["expect"].items():
+            _close(got[k], ev(np.array(v)), 1e-14, f"swiglu golden {k}")
+
+
+def pin_swiglu_sampled(O):
+    c = _swiglu_case(35, 20, 8, 12)
+    b, f = _swiglu_bwd(O, c)
+    rows, cw, cd = np.array([0, 9, 19]), np.array([0, 5, 12, 23]), np.array([1, 7])
+    fr = O.ref_swiglu_fwd_rows(c["X"], c["W"], c["Wd"], rows)
+    for k in ("gu", "a", "z"):
+        _close(fr[k], f[k][rows], 1e-14, f"swiglu rows {k}")
+    s = O.ref_swiglu_bwd_sampled(c["X"], c["W"], c["Wd"], f["gu"], f["a"], c["dz"], rows, cw, cd)
+    _close(s["dX_rows"], b["dX"][rows], 1e-13, "swiglu sampled dX")
+    _close(s["dgu_rows"], b["dgu"][rows], 1e-13, "swiglu sampled dgu")
+    _close(s["dW_cols"], b["dW"][:, cw], 1e-13, "swiglu sampled dW")
+    _close(s["dWd_cols"], b["dWd"][:, cd], 1e-13, "swiglu sampled dWd")
+
+
+# ------------------------------------------------------------------- bf16 pins
+
+def pin_bf16_rne(O):
+    """Known values, ties to even, one rounding from float64, range ends, and
+    agreement with torch's float32 -> bfloat16 conversion (round-to-nearest-even)
+    on values that are exact in float32."""
+    import torch
+    cases = {
+        1.0: 1.0,
+        1.0 + 2.0 ** -8: 1.0,                           # tie -> even (1.0)
+        1.0 + 3 * 2.0 ** -8: 1.0 + 2.0 ** -6,           # tie -> even (mantissa 2)
+        1.0 + 2.0 ** -8 + 2.0 ** -40: 1.0 + 2.0 ** -7,  # above the tie: one rounding from f64
+        -1.0 - 2.0 ** -8 - 2.0 ** -40: -1.0 - 2.0 ** -7,
+        2.0 ** -130 + 2.0 ** -134: 2.0 ** -130,          # subnormal spacing 2^-133
+        3.0 * 2.0 ** -134: 2.0 ** -132,                  # 1.5 steps -> tie -> even (2 steps)
+        float(np.ldexp(255.0, 120)): float(np.ldexp(255.0, 120)),
+        float(np.ldexp(511.0, 119)): math.inf,           # rounds up past the largest value
+        0.0: 0.0,
+    }
+    for x, want in cases.items():
+        g = float(O.bf16_rne(np.array([x]))[0])
+        assert g == want, f"bf16_rne({x!r}) = {g!r}, want {want!r}"
+    v = _rng(41).standard_normal(20000).astype(np.float32) * np.float32(37.0)
+    t = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.bf16_rne(v.astype(np.float64)), t), "bf16_rne vs torch"
+
+
+ALL_PINS = [
+    pin_fwd_bruteforce, pin_fwd_torch_rmsnorm, pin_fwd_constant_rows,
+    pin_fwd_scale_invariance, pin_partials, pin_rewrite_equals_unfused,
+    pin_golden_coda, pin_bwd_finite_differences, pin_bwd_torch_autograd,
+    pin_bwd_invariants, pin_sampled_forms, pin_swiglu_bruteforce,
+    pin_swiglu_finite_differences, pin_swiglu_torch, pin_swiglu_invariants,
+    pin_golden_swiglu, pin_swiglu_sampled, pin_bf16_rne,
+]

@@ -1,0 +1,159 @@
+"""Each planted mistake in a copy of the oracle must fail at least one pin.
+
+The mistakes are the plausible ones: a dropped term, a wrong sign or index, a
+transposed operand, a wrong normalising width, epsilon in the wrong place, the
+gate and up halves swapped, rounding ties away from zero.  They live here, on
+the CPU, in copies; the oracle itself is untouched.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins as P
+
+
+def _f(*a):
+    return [np.asarray(x, dtype=np.float64) for x in a]
+
+
+def fwd_eps_outside(X, W1, R, gamma, W2, eps):
+    X, W1, R, gamma, W2 = _f(X, W1, R, gamma, W2)
+    y = X @ W1 + R
+    ms = np.mean(y * y, axis=1)
+    r = 1.0 / np.sqrt(ms) + eps
+    h = y * r[:, None] * gamma
+    return {"y": y, "ms": ms, "r": r, "h": h, "z": h @ W2}
+
+
+def fwd_mean_over_N(X, W1, R, gamma, W2, eps):
+    X, W1, R, gamma, W2 = _f(X, W1, R, gamma, W2)
+    y = X @ W1 + R
+    ms = np.sum(y * y, axis=1) / W2.shape[1]
+    r = 1.0 / np.sqrt(ms + eps)
+    h = y * r[:, None] * gamma
+    return {"y": y, "ms": ms, "r": r, "h": h, "z": h @ W2}
+
+
+def fwd_one_plus_gamma(X, W1, R, gamma, W2, eps):
+    out = oracle.ref_fwd(X, W1, R, np.asarray(gamma) + 1.0, W2, eps)
+    return out
+
+
+def fwd_no_residual(X, W1, R, gamma, W2, eps):
+    return oracle.ref_fwd(X, W1, np.zeros_like(np.asarray(R, dtype=np.float64)), gamma, W2, eps)
+
+
+def _bwd_variant(kind):
+    def bwd(X, W1, gamma, W2, y, r, dz):
+        X, W1, gamma, W2, y, r, dz = _f(X, W1, gamma, W2, y, r, dz)
+        d = y.shape[1]
+        n = y * r[:, None]
+        h = n * gamma
+        dW2 = h.T @ dz
+        dh = dz @ W2.T
+        dgamma = np.sum(dh * (y if kind == "dgamma_y" else n), axis=0)
+        dn = dh * gamma
+        s = np.sum(dn * y, axis=1)
+        c = r ** 3 * s / d
+        if kind == "drop_c":
+            dy = dn * r[:, None]
+        elif kind == "sign_c":
+            dy = dn * r[:, None] + c[:, None] * y
+        elif kind == "r_squared":
+            dy = dn * r[:, None] - (r ** 2 * s / d)[:, None] * y
+        else:
+            dy = dn * r[:, None] - c[:, None] * y
+        dX = dy @ W1.T
+        dW1 = (X.T @ dn) if kind == "dW1_uses_dn" else (X.T @ dy)
+        if kind == "dW2_no_gamma":
+            dW2 = n.T @ dz
+        return {"dX": dX, "dW1": dW1, "dR": dy, "dW2": dW2, "dgamma": dgamma,
+                "dh": dh, "dn": dn, "n": n, "s": s, "c": c, "dy": dy}
+    return bwd
+
+
+def partials_off_by_one(y, BN):
+    y = np.asarray(y, dtype=np.float64)
+    M, d = y.shape
+    T = -(-d // BN)
+    P = np.zeros((M, T))
+    for t in range(T):
+        blk = y[:, t * BN + 1:min((t + 1) * BN + 1, d)]
+        P[:, t] = np.sum(blk * blk, axis=1)
+    return P
+
+
+def swiglu_fwd_swapped(X, W, Wd):
+    X, W, Wd = _f(X, W, Wd)
+    F = W.shape[1] // 2
+    gu = X @ W
+    g, u = gu[:, F:], gu[:, :F]
+    a = g * oracle.sigmoid(g) * u
+    return {"gu": gu, "a": a, "z": a @ Wd}
+
+
+def swiglu_bwd_no_factor(X, W, Wd, gu, a, dz):
+    X, W, Wd, gu, a, dz = _f(X, W, Wd, gu, a, dz)
+    F = W.shape[1] // 2
+    g, u = gu[:, :F], gu[:, F:]
+    sg = oracle.sigmoid(g)
+    da = dz @ Wd.T
+    dg = da * u * sg
+    du = da * g * sg
+    dgu = np.concatenate([dg, du], axis=1)
+    return {"dX": dgu @ W.T, "dW": X.T @ dgu, "dWd": a.T @ dz, "dgu": dgu, "da": da}
+
+
+def swiglu_bwd_transposed(X, W, Wd, gu, a, dz):
+    out = dict(oracle.ref_swiglu_bwd(X, W, Wd, gu, a, dz))
+    out["dWd"] = out["dWd"][:, ::-1]  # columns in the wrong order
+    return out
+
+
+def bf16_half_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    _, e = np.frexp(x[fin])
+    e = np.maximum(e, -125) - 8
+    v = np.ldexp(np.trunc(np.ldexp(x[fin], -e) + np.copysign(0.5, x[fin])), e)
+    out[fin] = v
+    return out
+
+
+def bf16_via_f32(x):
+    import torch
+    t = torch.from_numpy(np.asarray(x, dtype=np.float64).astype(np.float32))
+    return t.to(torch.bfloat16).to(torch.float64).numpy()
+
+
+MUTANTS = {
+    "fwd_eps_outside_sqrt": {"ref_fwd": fwd_eps_outside},
+    "fwd_mean_over_N": {"ref_fwd": fwd_mean_over_N},
+    "fwd_one_plus_gamma": {"ref_fwd": fwd_one_plus_gamma},
+    "fwd_no_residual": {"ref_fwd": fwd_no_residual},
+    "bwd_drop_c_term": {"ref_bwd": _bwd_variant("drop_c")},
+    "bwd_sign_c_term": {"ref_bwd": _bwd_variant("sign_c")},
+    "bwd_r_squared": {"ref_bwd": _bwd_variant("r_squared")},
+    "bwd_dgamma_uses_y": {"ref_bwd": _bwd_variant("dgamma_y")},
+    "bwd_dW1_uses_dn": {"ref_bwd": _bwd_variant("dW1_uses_dn")},
+    "bwd_dW2_no_gamma": {"ref_bwd": _bwd_variant("dW2_no_gamma")},
+    "partials_off_by_one": {"ref_partials": partials_off_by_one},
+    "swiglu_gate_up_swapped": {"ref_swiglu_fwd": swiglu_fwd_swapped},
+    "swiglu_bwd_missing_factor": {"ref_swiglu_bwd": swiglu_bwd_no_factor},
+    "swiglu_bwd_dWd_columns": {"ref_swiglu_bwd": swiglu_bwd_transposed},
+    "bf16_ties_away": {"bf16_rne": bf16_half_away},
+    "bf16_double_rounding": {"bf16_rne": bf16_via_f32},
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    O = P.oracle_namespace(**MUTANTS[name])
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(O)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"
