@@ -1,0 +1,242 @@
+"""MI355X-native fused GEMM-Residual-RMSNorm-GEMM block and SwiGLU block.
+
+Thin Python binding over the C-ABI library ``libcoda.so`` (include/coda.h).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensors, allocates outputs and workspaces with torch, and passes
+raw device pointers and torch's current HIP stream.  There is no CPU or
+PyTorch fallback: without the built library every call raises.
+
+Low-level calls (same names and argument order as the C functions, outputs
+preallocated by the caller):
+    coda_fwd, coda_bwd, coda_swiglu_fwd, coda_swiglu_bwd
+Convenience calls (allocate outputs):
+    fwd(X, W1, R, gamma, W2, eps)        -> (z, y, r)
+    bwd(X, W1, gamma, W2, y, r, dz)      -> (dX, dW1, dR, dW2, dgamma)
+    swiglu_fwd(X, W, Wd)                 -> (z, gu, a)
+    swiglu_bwd(X, W, Wd, gu, a, dz)      -> (dX, dW, dWd)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "CodaError", "lib_path", "load_library", "coda_fwd", "coda_bwd", "coda_swiglu_fwd",
+    "coda_swiglu_bwd", "fwd", "bwd", "swiglu_fwd", "swiglu_bwd", "fwd_workspace_bytes",
+    "bwd_workspace_bytes", "swiglu_bwd_workspace_bytes", "version",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+CODA_F32, CODA_BF16 = 0, 1
+
+
+class CodaError(RuntimeError):
+    """A non-zero coda_status from the library."""
+
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed: {msg}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG, "libcoda.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libcoda.so (built in-tree by build.py).  torch is imported first so
+    that the library binds to the HIP runtime torch already loaded."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m gemm_epilogue_fusion_gemm1_amd.build`; "
+            "there is no fallback implementation")
+    import torch  # noqa: F401  (binds libamdhip64 before the library is loaded)
+    L = ctypes.CDLL(path)
+    i64, sz, vp, f32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+    i32 = ctypes.c_int
+    L.coda_status_str.restype = ctypes.c_char_p
+    L.coda_status_str.argtypes = [i32]
+    L.coda_version.restype = ctypes.c_char_p
+    L.coda_version.argtypes = []
+    for name, args in {
+        "coda_fwd_workspace_bytes": [i32, i64, i64, i64, i64],
+        "coda_bwd_workspace_bytes": [i32, i64, i64, i64, i64],
+        "coda_swiglu_fwd_workspace_bytes": [i32, i64, i64, i64],
+        "coda_swiglu_bwd_workspace_bytes": [i32, i64, i64, i64],
+    }.items():
+        getattr(L, name).restype = sz
+        getattr(L, name).argtypes = args
+    L.coda_fwd.restype = i32
+    L.coda_fwd.argtypes = [i32, i64, i64, i64, i64, f32] + [vp] * 8 + [vp, sz, vp]
+    L.coda_bwd.restype = i32
+    L.coda_bwd.argtypes = [i32, i64, i64, i64, i64] + [vp] * 12 + [vp, sz, vp]
+    L.coda_swiglu_fwd.restype = i32
+    L.coda_swiglu_fwd.argtypes = [i32, i64, i64, i64] + [vp] * 6 + [vp, sz, vp]
+    L.coda_swiglu_bwd.restype = i32
+    L.coda_swiglu_bwd.argtypes = [i32, i64, i64, i64] + [vp] * 9 + [vp, sz, vp]
+    _LIB = L
+    return L
+
+
+def version() -> str:
+    return load_library().coda_version().decode()
+
+
+# ----------------------------------------------------------------- helpers
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return CODA_BF16
+    if t.dtype == torch.float32:
+        return CODA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: expected torch.bfloat16 or torch.float32")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("every tensor must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError("every tensor must be contiguous (row-major)")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        msg = load_library().coda_status_str(status).decode()
+        raise CodaError(fn, status, msg)
+
+
+def _shape(t, *dims, name=""):
+    if tuple(t.shape) != tuple(dims):
+        raise ValueError(f"{name}: expected shape {tuple(dims)}, got {tuple(t.shape)}")
+
+
+def _workspace(nbytes, device):
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def fwd_workspace_bytes(dtype_code, M, K, d, N) -> int:
+    return int(load_library().coda_fwd_workspace_bytes(dtype_code, M, K, d, N))
+
+
+def bwd_workspace_bytes(dtype_code, M, K, d, N) -> int:
+    return int(load_library().coda_bwd_workspace_bytes(dtype_code, M, K, d, N))
+
+
+def swiglu_bwd_workspace_bytes(dtype_code, M, d, F) -> int:
+    return int(load_library().coda_swiglu_bwd_workspace_bytes(dtype_code, M, d, F))
+
+
+# ------------------------------------------------------ C-ABI passthroughs
+
+def coda_fwd(X, W1, R, gamma, W2, eps, y, r, z, workspace):
+    """coda_fwd with caller-owned outputs y [M,d], r [M] (fp32), z [M,N]."""
+    L = load_library()
+    M, K = X.shape
+    d, N = W1.shape[1], W2.shape[1]
+    _check("coda_fwd", L.coda_fwd(
+        _dtype_code(X), M, K, d, N, float(eps), _ptr(X), _ptr(W1), _ptr(R), _ptr(gamma), _ptr(W2),
+        _ptr(y), _ptr(r), _ptr(z), _ptr(workspace), workspace.numel(), _stream()))
+
+
+def coda_bwd(X, W1, gamma, W2, y, r, dz, dX, dW1, dR, dW2, dgamma, workspace):
+    L = load_library()
+    M, K = X.shape
+    d, N = W1.shape[1], W2.shape[1]
+    _check("coda_bwd", L.coda_bwd(
+        _dtype_code(X), M, K, d, N, _ptr(X), _ptr(W1), _ptr(gamma), _ptr(W2), _ptr(y), _ptr(r),
+        _ptr(dz), _ptr(dX), _ptr(dW1), _ptr(dR), _ptr(dW2), _ptr(dgamma), _ptr(workspace),
+        workspace.numel(), _stream()))
+
+
+def coda_swiglu_fwd(X, W, Wd, gu, a, z, workspace=None):
+    L = load_library()
+    M, d = X.shape
+    F = Wd.shape[0]
+    ws = _ptr(workspace) if workspace is not None else None
+    _check("coda_swiglu_fwd", L.coda_swiglu_fwd(
+        _dtype_code(X), M, d, F, _ptr(X), _ptr(W), _ptr(Wd), _ptr(gu), _ptr(a), _ptr(z), ws,
+        0 if workspace is None else workspace.numel(), _stream()))
+
+
+def coda_swiglu_bwd(X, W, Wd, gu, a, dz, dX, dW, dWd, workspace):
+    L = load_library()
+    M, d = X.shape
+    F = Wd.shape[0]
+    _check("coda_swiglu_bwd", L.coda_swiglu_bwd(
+        _dtype_code(X), M, d, F, _ptr(X), _ptr(W), _ptr(Wd), _ptr(gu), _ptr(a), _ptr(dz),
+        _ptr(dX), _ptr(dW), _ptr(dWd), _ptr(workspace), workspace.numel(), _stream()))
+
+
+# ------------------------------------------------------ convenience calls
+
+def fwd(X, W1, R, gamma, W2, eps):
+    """z = RMSNorm(X W1 + R) * gamma @ W2, fused.  Returns (z, y, r)."""
+    import torch
+    M, K = X.shape
+    d, N = W1.shape[1], W2.shape[1]
+    _shape(W1, K, d, name="W1"); _shape(R, M, d, name="R")
+    _shape(gamma, d, name="gamma"); _shape(W2, d, N, name="W2")
+    y = torch.empty((M, d), dtype=X.dtype, device=X.device)
+    r = torch.empty((M,), dtype=torch.float32, device=X.device)
+    z = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    ws = _workspace(fwd_workspace_bytes(_dtype_code(X), M, K, d, N), X.device)
+    coda_fwd(X, W1, R, gamma, W2, eps, y, r, z, ws)
+    return z, y, r
+
+
+def bwd(X, W1, gamma, W2, y, r, dz):
+    """Gradients of <dz, z> from the saved (y, r).  Returns (dX, dW1, dR, dW2, dgamma)."""
+    import torch
+    M, K = X.shape
+    d, N = W1.shape[1], W2.shape[1]
+    _shape(y, M, d, name="y"); _shape(r, M, name="r"); _shape(dz, M, N, name="dz")
+    dX = torch.empty_like(X)
+    dW1 = torch.empty_like(W1)
+    dR = torch.empty((M, d), dtype=X.dtype, device=X.device)
+    dW2 = torch.empty_like(W2)
+    dgamma = torch.empty((d,), dtype=torch.float32, device=X.device)
+    ws = _workspace(bwd_workspace_bytes(_dtype_code(X), M, K, d, N), X.device)
+    coda_bwd(X, W1, gamma, W2, y, r, dz, dX, dW1, dR, dW2, dgamma, ws)
+    return dX, dW1, dR, dW2, dgamma
+
+
+def swiglu_fwd(X, W, Wd):
+    """z = (silu(X W_gate) * (X W_up)) @ Wd, fused.  Returns (z, gu, a)."""
+    import torch
+    M, d = X.shape
+    F = Wd.shape[0]
+    _shape(W, d, 2 * F, name="W"); _shape(Wd, F, d, name="Wd")
+    gu = torch.empty((M, 2 * F), dtype=X.dtype, device=X.device)
+    a = torch.empty((M, F), dtype=X.dtype, device=X.device)
+    z = torch.empty((M, d), dtype=X.dtype, device=X.device)
+    coda_swiglu_fwd(X, W, Wd, gu, a, z)
+    return z, gu, a
+
+
+def swiglu_bwd(X, W, Wd, gu, a, dz):
+    """Gradients of <dz, z> from the saved (gu, a).  Returns (dX, dW, dWd)."""
+    import torch
+    M, d = X.shape
+    F = Wd.shape[0]
+    _shape(gu, M, 2 * F, name="gu"); _shape(a, M, F, name="a"); _shape(dz, M, d, name="dz")
+    dX = torch.empty_like(X)
+    dW = torch.empty_like(W)
+    dWd = torch.empty_like(Wd)
+    ws = _workspace(swiglu_bwd_workspace_bytes(_dtype_code(X), M, d, F), X.device)
+    coda_swiglu_bwd(X, W, Wd, gu, a, dz, dX, dW, dWd, ws)
+    return dX, dW, dWd

@@ -1,0 +1,347 @@
+// C-ABI of the fused block (include/coda.h): argument checks, workspace
+// layout and the launch sequence of each entry point.  Every check runs
+// before the first HIP call, so a rejected call touches neither the device
+// nor the stream.
+#include "../../include/coda.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+using coda::GemmArgs;
+
+constexpr uint64_t kMaxTensorBytes = 0x7FFFFFF0ull;   // buffer descriptors address < 2 GiB
+constexpr size_t kAlign = 256;
+
+size_t esize(coda_dtype t) { return t == CODA_BF16 ? 2 : 4; }
+bool dtype_ok(int t) { return t == CODA_F32 || t == CODA_BF16; }
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool dim_ok(coda_dtype t, int64_t v) {
+  const int64_t q = t == CODA_BF16 ? 8 : 4;
+  return v >= q && v % q == 0 && v <= (int64_t)1 << 24;
+}
+bool bytes_ok(coda_dtype t, int64_t a, int64_t b) {
+  return (uint64_t)a * (uint64_t)b * esize(t) <= kMaxTensorBytes;
+}
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range rng(const void* p, uint64_t bytes) { return {(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes}; }
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Outputs may not overlap inputs, other outputs or the workspace.
+template <int NI, int NO>
+bool alias_free(const Range (&in)[NI], const Range (&out)[NO]) {
+  for (int o = 0; o < NO; ++o) {
+    if (out[o].hi == out[o].lo) continue;
+    for (int i = 0; i < NI; ++i)
+      if (in[i].hi != in[i].lo && overlap(out[o], in[i])) return false;
+    for (int p = o + 1; p < NO; ++p)
+      if (out[p].hi != out[p].lo && overlap(out[o], out[p])) return false;
+  }
+  return true;
+}
+
+coda_status hip_status(hipError_t e) { return e == hipSuccess ? CODA_OK : CODA_ERR_HIP; }
+
+// ------------------------------------------------------------- workspaces
+struct FwdWs {
+  size_t P, W2f, total;
+  int Tn;
+};
+FwdWs fwd_ws(coda_dtype t, int64_t M, int64_t d, int64_t N) {
+  FwdWs w;
+  w.Tn = (int)cdiv(d, t == CODA_BF16 ? coda::kTileN : coda::kTileF32);
+  w.P = 0;
+  w.W2f = round_up((size_t)M * w.Tn * 4);
+  w.total = w.W2f + round_up((size_t)d * N * esize(t));
+  return w;
+}
+
+struct BwdWs {
+  size_t n, S, G, c, total;
+  int Tn, Tm;
+};
+BwdWs bwd_ws(int64_t M, int64_t d) {
+  BwdWs w;
+  w.Tn = (int)cdiv(d, coda::kTileN);
+  w.Tm = (int)cdiv(M, coda::kTileM);
+  w.n = 0;
+  w.S = round_up((size_t)M * d * 2);
+  w.G = w.S + round_up((size_t)M * w.Tn * 4);
+  w.c = w.G + round_up((size_t)w.Tm * d * 4);
+  w.total = w.c + round_up((size_t)M * 4);
+  return w;
+}
+
+GemmArgs gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, uint64_t A_elems,
+              const void* B, int64_t ldb, uint64_t B_elems, void* C, int64_t ldc) {
+  GemmArgs g{};
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.A = A;
+  g.lda = lda;
+  g.A_bytes = (uint32_t)(A_elems * 2);
+  g.B = B;
+  g.ldb = ldb;
+  g.B_bytes = (uint32_t)(B_elems * 2);
+  g.C = C;
+  g.ldc = ldc;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* coda_status_str(coda_status s) {
+  switch (s) {
+    case CODA_OK: return "CODA_OK";
+    case CODA_ERR_NULL: return "CODA_ERR_NULL: a required pointer is NULL";
+    case CODA_ERR_SHAPE: return "CODA_ERR_SHAPE: a size is out of range or not a multiple of 8 (bf16) / 4 (f32)";
+    case CODA_ERR_ALIGN: return "CODA_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+    case CODA_ERR_ALIAS: return "CODA_ERR_ALIAS: an output overlaps an input, another output or the workspace";
+    case CODA_ERR_DTYPE: return "CODA_ERR_DTYPE: unknown dtype";
+    case CODA_ERR_EPS: return "CODA_ERR_EPS: eps must be finite and > 0";
+    case CODA_ERR_WORKSPACE: return "CODA_ERR_WORKSPACE: workspace missing or too small";
+    case CODA_ERR_UNSUPPORTED: return "CODA_ERR_UNSUPPORTED: not implemented for this dtype";
+    case CODA_ERR_HIP: return "CODA_ERR_HIP: a HIP call or kernel launch failed";
+  }
+  return "CODA_ERR_UNKNOWN";
+}
+
+const char* coda_version(void) { return "coda-mi355x 0.1.0 gfx950"; }
+
+size_t coda_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N) {
+  (void)K;
+  if (!dtype_ok(dtype) || M < 1 || d < 1 || N < 1) return 0;
+  return fwd_ws(dtype, M, d, N).total;
+}
+
+coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N, float eps,
+                     const void* X, const void* W1, const void* R, const void* gamma,
+                     const void* W2, void* y, float* r, void* z, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
+  if (!X || !W1 || !R || !gamma || !W2 || !y || !r || !z) return CODA_ERR_NULL;
+  if (!dim_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, d) || !dim_ok(dtype, N))
+    return CODA_ERR_SHAPE;
+  if (!bytes_ok(dtype, M, K) || !bytes_ok(dtype, K, d) || !bytes_ok(dtype, M, d) ||
+      !bytes_ok(dtype, d, N) || !bytes_ok(dtype, M, N))
+    return CODA_ERR_SHAPE;
+  if (!std::isfinite(eps) || !(eps > 0.0f)) return CODA_ERR_EPS;
+  for (const void* p : {X, W1, R, gamma, W2, (const void*)y, (const void*)r, (const void*)z})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  const FwdWs ws = fwd_ws(dtype, M, d, N);
+  if (!workspace || workspace_bytes < ws.total) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const size_t e = esize(dtype);
+  const Range in[] = {rng(X, M * K * e), rng(W1, K * d * e), rng(R, M * d * e), rng(gamma, d * e),
+                      rng(W2, d * N * e)};
+  const Range out[] = {rng(y, M * d * e), rng(r, M * 4), rng(z, M * N * e),
+                       rng(workspace, ws.total)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)workspace;
+  float* P = (float*)(wsb + ws.P);
+  void* W2f = wsb + ws.W2f;
+  hipError_t err;
+  if ((err = coda::launch_fold_gamma(dtype == CODA_BF16, gamma, W2, W2f, d, N, s)) != hipSuccess)
+    return hip_status(err);
+
+  GemmArgs g1 = gemm(M, d, K, X, K, M * K, W1, d, K * d, y, d);
+  g1.E = R;
+  g1.lde = d;
+  g1.part_row = P;
+  g1.ld_part_row = ws.Tn;
+  GemmArgs g2 = gemm(M, N, d, y, d, M * d, W2f, N, d * N, z, N);
+  g2.vrow = r;
+  if (dtype == CODA_BF16) {
+    if ((err = coda::launch_gemm_bf16(g1, true, false, coda::EPI_RESID_SUMSQ, s)) != hipSuccess)
+      return hip_status(err);
+    if ((err = coda::launch_row_rsqrt(P, ws.Tn, ws.Tn, M, d, eps, r, s)) != hipSuccess)
+      return hip_status(err);
+    return hip_status(coda::launch_gemm_bf16(g2, true, false, coda::EPI_ROWSCALE, s));
+  }
+  if ((err = coda::launch_gemm_f32(g1, coda::EPI_RESID_SUMSQ, s)) != hipSuccess)
+    return hip_status(err);
+  if ((err = coda::launch_row_rsqrt(P, ws.Tn, ws.Tn, M, d, eps, r, s)) != hipSuccess)
+    return hip_status(err);
+  return hip_status(coda::launch_gemm_f32(g2, coda::EPI_ROWSCALE, s));
+}
+
+size_t coda_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N) {
+  (void)K;
+  (void)N;
+  if (dtype != CODA_BF16 || M < 1 || d < 1) return 0;
+  return bwd_ws(M, d).total;
+}
+
+coda_status coda_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N,
+                     const void* X, const void* W1, const void* gamma, const void* W2,
+                     const void* y, const float* r, const void* dz, void* dX, void* dW1,
+                     void* dR, void* dW2, float* dgamma, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
+  if (!X || !W1 || !gamma || !W2 || !y || !r || !dz || !dX || !dW1 || !dR || !dW2 || !dgamma)
+    return CODA_ERR_NULL;
+  if (!dim_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, d) || !dim_ok(dtype, N))
+    return CODA_ERR_SHAPE;
+  if (!bytes_ok(dtype, M, K) || !bytes_ok(dtype, K, d) || !bytes_ok(dtype, M, d) ||
+      !bytes_ok(dtype, d, N) || !bytes_ok(dtype, M, N))
+    return CODA_ERR_SHAPE;
+  if (dtype != CODA_BF16) return CODA_ERR_UNSUPPORTED;
+  for (const void* p : {X, W1, gamma, W2, y, (const void*)r, dz, (const void*)dX,
+                        (const void*)dW1, (const void*)dR, (const void*)dW2, (const void*)dgamma})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  const BwdWs ws = bwd_ws(M, d);
+  if (!workspace || workspace_bytes < ws.total) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const size_t e = 2;
+  const Range in[] = {rng(X, M * K * e), rng(W1, K * d * e), rng(gamma, d * e), rng(W2, d * N * e),
+                      rng(y, M * d * e), rng(r, M * 4), rng(dz, M * N * e)};
+  const Range out[] = {rng(dX, M * K * e), rng(dW1, K * d * e), rng(dR, M * d * e),
+                       rng(dW2, d * N * e), rng(dgamma, d * 4), rng(workspace, ws.total)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)workspace;
+  void* n = wsb + ws.n;
+  float* S = (float*)(wsb + ws.S);
+  float* G = (float*)(wsb + ws.G);
+  float* c = (float*)(wsb + ws.c);
+  hipError_t err;
+
+  // B1: dh = dz W2^T; epilogue -> dn (into dR), row partials S, column partials G
+  GemmArgs b1 = gemm(M, d, N, dz, N, M * N, W2, N, d * N, dR, d);
+  b1.E = y;
+  b1.lde = d;
+  b1.vrow = r;
+  b1.vcol = gamma;
+  b1.part_row = S;
+  b1.ld_part_row = ws.Tn;
+  b1.part_col = G;
+  b1.ld_part_col = d;
+  if ((err = coda::launch_gemm_bf16(b1, true, true, coda::EPI_DN, s)) != hipSuccess)
+    return hip_status(err);
+  // R2: c = r^3 s / d, dgamma
+  if ((err = coda::launch_bwd_reduce(S, ws.Tn, ws.Tn, r, M, d, G, ws.Tm, c, dgamma, s)) !=
+      hipSuccess)
+    return hip_status(err);
+  // E2: dR = r dn - c y (in place), n = r y
+  if ((err = coda::launch_dy_n(dR, n, y, r, c, M, d, s)) != hipSuccess) return hip_status(err);
+  // B2: dW2 = diag(gamma) n^T dz
+  GemmArgs b2 = gemm(d, N, M, n, d, M * d, dz, N, M * N, dW2, N);
+  b2.vcol = gamma;
+  if ((err = coda::launch_gemm_bf16(b2, false, false, coda::EPI_ROWSCALE, s)) != hipSuccess)
+    return hip_status(err);
+  // B3: dX = dy W1^T
+  GemmArgs b3 = gemm(M, K, d, dR, d, M * d, W1, d, K * d, dX, K);
+  if ((err = coda::launch_gemm_bf16(b3, true, true, coda::EPI_STORE, s)) != hipSuccess)
+    return hip_status(err);
+  // B4: dW1 = X^T dy
+  GemmArgs b4 = gemm(K, d, M, X, K, M * K, dR, d, M * d, dW1, d);
+  return hip_status(coda::launch_gemm_bf16(b4, false, false, coda::EPI_STORE, s));
+}
+
+size_t coda_swiglu_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t d, int64_t F) {
+  (void)dtype;
+  (void)M;
+  (void)d;
+  (void)F;
+  return 0;
+}
+
+coda_status coda_swiglu_fwd(coda_dtype dtype, int64_t M, int64_t d, int64_t F, const void* X,
+                            const void* W, const void* Wd, void* gu, void* a, void* z,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
+  if (!X || !W || !Wd || !gu || !a || !z) return CODA_ERR_NULL;
+  if (!dim_ok(dtype, M) || !dim_ok(dtype, d) || !dim_ok(dtype, F)) return CODA_ERR_SHAPE;
+  if (!bytes_ok(dtype, M, d) || !bytes_ok(dtype, d, 2 * F) || !bytes_ok(dtype, F, d) ||
+      !bytes_ok(dtype, M, 2 * F))
+    return CODA_ERR_SHAPE;
+  if (dtype != CODA_BF16) return CODA_ERR_UNSUPPORTED;
+  for (const void* p : {X, W, Wd, (const void*)gu, (const void*)a, (const void*)z})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  const size_t e = 2;
+  const Range in[] = {rng(X, M * d * e), rng(W, d * 2 * F * e), rng(Wd, F * d * e)};
+  const Range out[] = {rng(gu, M * 2 * F * e), rng(a, M * F * e), rng(z, M * d * e)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err;
+  GemmArgs s1 = gemm(M, F, d, X, d, M * d, W, 2 * F, d * 2 * F, gu, 2 * F);
+  s1.C2 = a;
+  s1.ldc2 = F;
+  s1.F = (int)F;
+  if ((err = coda::launch_gemm_bf16(s1, true, false, coda::EPI_SWIGLU, s)) != hipSuccess)
+    return hip_status(err);
+  GemmArgs s2 = gemm(M, d, F, a, F, M * F, Wd, d, F * d, z, d);
+  return hip_status(coda::launch_gemm_bf16(s2, true, false, coda::EPI_STORE, s));
+}
+
+size_t coda_swiglu_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t d, int64_t F) {
+  (void)d;
+  if (dtype != CODA_BF16 || M < 1 || F < 1) return 0;
+  return round_up((size_t)M * 2 * F * 2);
+}
+
+coda_status coda_swiglu_bwd(coda_dtype dtype, int64_t M, int64_t d, int64_t F, const void* X,
+                            const void* W, const void* Wd, const void* gu, const void* a,
+                            const void* dz, void* dX, void* dW, void* dWd, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
+  if (!X || !W || !Wd || !gu || !a || !dz || !dX || !dW || !dWd) return CODA_ERR_NULL;
+  if (!dim_ok(dtype, M) || !dim_ok(dtype, d) || !dim_ok(dtype, F)) return CODA_ERR_SHAPE;
+  if (!bytes_ok(dtype, M, d) || !bytes_ok(dtype, d, 2 * F) || !bytes_ok(dtype, F, d) ||
+      !bytes_ok(dtype, M, 2 * F))
+    return CODA_ERR_SHAPE;
+  if (dtype != CODA_BF16) return CODA_ERR_UNSUPPORTED;
+  for (const void* p : {X, W, Wd, gu, a, dz, (const void*)dX, (const void*)dW, (const void*)dWd})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  const size_t need = coda_swiglu_bwd_workspace_bytes(dtype, M, d, F);
+  if (!workspace || workspace_bytes < need) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const size_t e = 2;
+  const Range in[] = {rng(X, M * d * e), rng(W, d * 2 * F * e), rng(Wd, F * d * e),
+                      rng(gu, M * 2 * F * e), rng(a, M * F * e), rng(dz, M * d * e)};
+  const Range out[] = {rng(dX, M * d * e), rng(dW, d * 2 * F * e), rng(dWd, F * d * e),
+                       rng(workspace, need)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  void* dgu = workspace;
+  hipError_t err;
+  // S3: da = dz Wd^T; epilogue -> dgu from the saved gu
+  GemmArgs s3 = gemm(M, F, d, dz, d, M * d, Wd, d, F * d, dgu, 2 * F);
+  s3.E = gu;
+  s3.lde = 2 * F;
+  s3.F = (int)F;
+  if ((err = coda::launch_gemm_bf16(s3, true, true, coda::EPI_SWIGLU_BWD, s)) != hipSuccess)
+    return hip_status(err);
+  // S4: dWd = a^T dz
+  GemmArgs s4 = gemm(F, d, M, a, F, M * F, dz, d, M * d, dWd, d);
+  if ((err = coda::launch_gemm_bf16(s4, false, false, coda::EPI_STORE, s)) != hipSuccess)
+    return hip_status(err);
+  // S5: dX = dgu W^T
+  GemmArgs s5 = gemm(M, d, 2 * F, dgu, 2 * F, M * 2 * F, W, 2 * F, d * 2 * F, dX, d);
+  if ((err = coda::launch_gemm_bf16(s5, true, true, coda::EPI_STORE, s)) != hipSuccess)
+    return hip_status(err);
+  // S6: dW = X^T dgu
+  GemmArgs s6 = gemm(d, 2 * F, M, X, d, M * d, dgu, 2 * F, M * 2 * F, dW, 2 * F);
+  return hip_status(coda::launch_gemm_bf16(s6, false, false, coda::EPI_STORE, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,722 @@
+// HIP kernels of the fused GEMM-Residual-RMSNorm-GEMM block and the SwiGLU
+// block for CDNA4 (gfx950).
+//
+// The method (CODA, "Rewriting Transformer Blocks as GEMM-Epilogue Programs",
+// as reported by the toolin.ai blog section 核心の洞察 and the kucoin.com
+// news flashes, sections "CODA: В «Финале» спрятаны сокровища" and
+// "CODA : « La fin » cache un trésor"): a GEMM is a tiled multiply-accumulate
+// main loop plus an epilogue that runs while the output tile is still in
+// registers; memory-bound neighbours of a GEMM (residual add, the RMS row
+// scale, SwiGLU) are rewritten to run inside that epilogue.  Here:
+//
+//  * one bf16 MFMA main loop (v_mfma_f32_32x32x16_bf16, fp32 accumulators),
+//    256x256 output tile per 256-thread workgroup, 4 waves of 128x128, K
+//    step 64, LDS double buffered;
+//  * operands of either layout (contraction index contiguous or not) are
+//    staged into one LDS format, "k-octet planes": plane q holds, for every
+//    row m of the tile, the 8 consecutive k values 8q..8q+7 as one 16-byte
+//    slot, with one pad slot per 8 rows so that 8 lanes reading 8 rows, or
+//    writing 8 octets of one row, hit 8 different bank groups;
+//  * epilogues selected at compile time (launch.hpp: Epi) work on the
+//    accumulator registers in place: residual add + per-tile partial sums of
+//    squares, row scale, the RMSNorm-backward epilogue, SwiGLU and its
+//    backward.  Row reductions use a halving butterfly of lane shuffles;
+//    the two waves that share rows combine through LDS in a fixed order, so
+//    every result is run-to-run deterministic (no atomics).
+#include "launch.hpp"
+
+namespace coda {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = kTileM;
+constexpr int BN = kTileN;
+constexpr int BK = 64;
+constexpr int NT = 256;
+constexpr int PLANE = (BM + BM / 8) * 16 + 16;   // 4624 B; == 16 (mod 128)
+constexpr int OPER_BYTES = (BK / 8) * PLANE;     // one operand tile
+constexpr int STAGE_BYTES = 2 * OPER_BYTES;      // A + B
+constexpr int LDS_BYTES = 2 * STAGE_BYTES;       // two stages
+constexpr uint32_t OOB = 0x80000000u;            // voffset past every extent -> loads 0
+static_assert(BM == BN, "operand tiles share one LDS geometry");
+static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
+
+__device__ __forceinline__ int slot16(int m) { return (m + (m >> 3)) * 16; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  // raw buffer: stride 0, num_records in bytes; dword3 0x00020000 = 32-bit data format
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
+__device__ __forceinline__ float bf2f(__bf16 h) { return (float)h; }
+__device__ __forceinline__ __bf16 f2bf(float f) { return (__bf16)f; }  // round to nearest even
+
+// Tile id -> (tile_m, tile_n).  Workgroups are dealt round-robin over the 8
+// XCDs (wg % 8), each with its own L2; consecutive logical tiles are given to
+// one XCD so that the tiles resident on an XCD share operand rows/columns.
+// Within that order, groups of GM tile-rows are walked column by column.
+__device__ __forceinline__ void map_tile(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int q = total >> 3, rem = total & 7;
+  const int x = wg & 7, i = wg >> 3;
+  const int t = (x < rem) ? x * (q + 1) + i : rem * (q + 1) + (x - rem) * q + i;
+  constexpr int GM = 8;
+  const int group = GM * tiles_n;
+  const int gidx = t / group;
+  const int first_m = gidx * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int in = t - gidx * group;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+// ---------------------------------------------------------------------------
+// Operand staging: global -> registers (buffer loads, out-of-range -> 0) ->
+// LDS k-octet planes.
+// ---------------------------------------------------------------------------
+
+// Contraction index contiguous: rows of the tile are MN, 64 k per row.
+// Thread t loads row p*32 + t/8 (p = 0..7), k chunk t%8: one 16-byte octet
+// per load, stored unchanged into plane t%8.
+struct LoaderKMajor {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t base;      // byte offset of (row0 + t/8, 8*(t%8))
+  uint32_t pstride;   // 32 rows in bytes
+  uint32_t rowmask;   // bit p: row p*32 + t/8 is inside the matrix
+  int kchunk;         // 8*(t%8)
+  int K;
+  int lds_off[8];
+
+  __device__ void init(const void* ptr, uint32_t bytes, int64_t ld, int row0, int rows, int K_,
+                       int t) {
+    rs = make_rsrc(ptr, bytes);
+    const int r = t >> 3, c = t & 7;
+    kchunk = c * 8;
+    K = K_;
+    const uint32_t ldb = (uint32_t)(ld * 2);
+    base = (uint32_t)(row0 + r) * ldb + (uint32_t)(kchunk * 2);
+    pstride = 32u * ldb;
+    rowmask = 0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      if (row0 + p * 32 + r < rows) rowmask |= 1u << p;
+      lds_off[p] = c * PLANE + slot16(p * 32 + r);
+    }
+  }
+  __device__ void load(int k0, u32x4 (&v)[8]) const {
+    const bool kok = (k0 + kchunk) < K;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const bool ok = kok && ((rowmask >> p) & 1u);
+      const uint32_t off = ok ? base + p * pstride + (uint32_t)(k0 * 2) : OOB;
+      v[p] = bload16(rs, off);
+    }
+  }
+  __device__ void store(char* lds, const u32x4 (&v)[8]) const {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) *(u32x4*)(lds + lds_off[p]) = v[p];
+  }
+};
+
+// Contraction index strided: the matrix is [K rows][MN cols].  Thread t owns
+// octet q = t/32 and MN chunk c = t%32: it loads the 8 k rows 8q..8q+7 of the
+// 8 columns 8c..8c+7, transposes the 8x8 block in registers, and stores one
+// octet per column.  GATED maps tile columns onto the [gate | up] halves of
+// a [d, 2F] weight: within each 128-column half of the tile, the first 64
+// columns are gate columns j and the next 64 the up columns F + j of the
+// same j, so one lane ends up holding a gate and its up value.
+template <bool GATED>
+struct LoaderMNMajor {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t base;      // byte offset of (k = 8q, col)
+  uint32_t ldb;       // row pitch in bytes
+  int krow;           // 8q
+  int K;
+  bool colok;
+  int lds_off;
+
+  __device__ void init(const void* ptr, uint32_t bytes, int64_t ld, int col0, int cols, int K_,
+                       int t, int F, int tn) {
+    rs = make_rsrc(ptr, bytes);
+    const int q = t >> 5, c = t & 31;
+    krow = q * 8;
+    K = K_;
+    ldb = (uint32_t)(ld * 2);
+    int col;
+    if (GATED) {
+      const int lc = c * 8;                       // tile column 0..255
+      const int half = lc >> 7, sub = lc & 127;
+      const int j = tn * 128 + half * 64 + (sub & 63);
+      colok = j < F;
+      col = (sub < 64) ? j : F + j;
+    } else {
+      col = col0 + c * 8;
+      colok = col < cols;
+    }
+    base = (uint32_t)krow * ldb + (uint32_t)col * 2u;
+    lds_off = q * PLANE + slot16(c * 8);
+  }
+  __device__ void load(int k0, u32x4 (&v)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool ok = colok && (k0 + krow + i) < K;
+      const uint32_t off = ok ? base + (uint32_t)(k0 + i) * ldb : OOB;
+      v[i] = bload16(rs, off);
+    }
+  }
+  __device__ void store(char* lds, const u32x4 (&v)[8]) const {
+    // v[i] holds row k = 8q+i, columns 8c..8c+7 (two per dword).  Output
+    // octet m holds column 8c+m, rows 8q..8q+7 (two per dword).
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      u32x4 o;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = v[2 * w][m >> 1], hi = v[2 * w + 1][m >> 1];
+        o[w] = (m & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+      }
+      // column 8c+m sits in slot 8c+m+c, i.e. (8c+m)+((8c+m)>>3) for m < 8
+      *(u32x4*)(lds + lds_off + m * 16) = o;
+    }
+  }
+};
+
+template <bool KMAJ, bool GATED>
+struct LoaderSel;
+template <bool GATED>
+struct LoaderSel<true, GATED> { using type = LoaderKMajor; };
+template <bool GATED>
+struct LoaderSel<false, GATED> { using type = LoaderMNMajor<GATED>; };
+
+// ---------------------------------------------------------------------------
+// Epilogue helpers
+// ---------------------------------------------------------------------------
+
+// Accumulator layout of v_mfma_f32_32x32x16_bf16: lane l, register r holds
+// row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the 32x32 block.
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// Sum of v[0..15] of every lane over the 32 lanes of its half-wave, one
+// result per row: halving butterfly (each exchange halves the values kept).
+// On return lane l holds the sum for register index (l & 31) >> 1.
+__device__ __forceinline__ float halfwave_rowsum16(const float (&v)[16], int lane) {
+  float w[8];
+  {
+    const bool b = lane & 16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float keep = b ? v[i + 8] : v[i];
+      const float send = b ? v[i] : v[i + 8];
+      w[i] = keep + __shfl_xor(send, 16);
+    }
+  }
+  float x[4];
+  {
+    const bool b = lane & 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float keep = b ? w[i + 4] : w[i];
+      const float send = b ? w[i] : w[i + 4];
+      x[i] = keep + __shfl_xor(send, 8);
+    }
+  }
+  float y[2];
+  {
+    const bool b = lane & 4;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float keep = b ? x[i + 2] : x[i];
+      const float send = b ? x[i] : x[i + 2];
+      y[i] = keep + __shfl_xor(send, 4);
+    }
+  }
+  const bool b = lane & 2;
+  float z = (b ? y[1] : y[0]) + __shfl_xor(b ? y[0] : y[1], 2);
+  z += __shfl_xor(z, 1);
+  return z;
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+__device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
+// ---------------------------------------------------------------------------
+// The bf16 MFMA GEMM: C[M,N] = A[M,K] B[K,N] (+ epilogue EPI)
+// ---------------------------------------------------------------------------
+template <bool AK, bool BKM, int EPI>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  constexpr bool GATED = (EPI == EPI_SWIGLU);
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
+
+  const int tiles_m = (g.M + BM - 1) / BM;
+  const int tiles_n = GATED ? (g.N + 127) / 128 : (g.N + BN - 1) / BN;
+  int tm, tn;
+  map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int row0 = tm * BM, col0 = tn * BN;
+
+  typename LoaderSel<AK, false>::type la;
+  typename LoaderSel<BKM, GATED>::type lb;
+  if constexpr (AK) la.init(g.A, g.A_bytes, g.lda, row0, g.M, g.K, t);
+  else la.init(g.A, g.A_bytes, g.lda, row0, g.M, g.K, t, 0, tm);
+  if constexpr (BKM) lb.init(g.B, g.B_bytes, g.ldb, col0, g.N, g.K, t);
+  else lb.init(g.B, g.B_bytes, g.ldb, col0, g.N, g.K, t, g.F, tn);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  const int nk = (g.K + BK - 1) / BK;
+  u32x4 ra[8], rb[8];
+  la.load(0, ra);
+  lb.load(0, rb);
+  la.store(smem, ra);
+  lb.store(smem + OPER_BYTES, rb);
+  __syncthreads();
+
+  const int l32 = lane & 31, khalf = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      la.load((kt + 1) * BK, ra);
+      lb.load((kt + 1) * BK, rb);
+    }
+    const char* sa = smem + cur * STAGE_BYTES;
+    const char* sb = sa + OPER_BYTES;
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      const int q = 2 * s + khalf;
+      bf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[i] = *(const bf16x8*)(sa + q * PLANE + slot16(wm * 128 + i * 32 + l32));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[j] = *(const bf16x8*)(sb + q * PLANE + slot16(wn * 128 + j * 32 + l32));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      char* nxt = smem + (cur ^ 1) * STAGE_BYTES;
+      la.store(nxt, ra);
+      lb.store(nxt + OPER_BYTES, rb);
+    }
+    __syncthreads();
+  }
+
+  // ------------------------------ epilogue ------------------------------
+  const int lrow0 = wm * 128;                 // wave's first local row
+  const int lcol0 = wn * 128 + l32;           // lane's local column in block j=0
+
+  if constexpr (EPI == EPI_STORE || EPI == EPI_ROWSCALE) {
+    __bf16* C = (__bf16*)g.C;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + lrow0 + i * 32 + acc_row(r, lane);
+        if (row >= g.M) continue;
+        float sc = 1.0f;
+        if constexpr (EPI == EPI_ROWSCALE) sc = g.vrow ? g.vrow[row] : bf2f(((const __bf16*)g.vcol)[row]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = col0 + lcol0 + j * 32;
+          if (col < g.N) C[(int64_t)row * g.ldc + col] = f2bf(sc * acc[i][j][r]);
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_RESID_SUMSQ) {
+    __bf16* C = (__bf16*)g.C;
+    const __bf16* E = (const __bf16*)g.E;
+    float* red = (float*)smem;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float sq[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + lrow0 + i * 32 + acc_row(r, lane);
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = col0 + lcol0 + j * 32;
+          if (row < g.M && col < g.N) {
+            const int64_t e = (int64_t)row * g.lde + col;
+            const float yv = acc[i][j][r] + bf2f(E[e]);
+            C[(int64_t)row * g.ldc + col] = f2bf(yv);
+            s += yv * yv;
+          }
+        }
+        sq[r] = s;
+      }
+      const float tot = halfwave_rowsum16(sq, lane);
+      if ((lane & 1) == 0) {
+        const int rr = l32 >> 1;
+        red[wn * BM + lrow0 + i * 32 + acc_row(rr, lane)] = tot;
+      }
+    }
+    __syncthreads();
+    const int row = row0 + t;
+    if (row < g.M) g.part_row[(int64_t)row * g.ld_part_row + tn] = red[t] + red[BM + t];
+  } else if constexpr (EPI == EPI_DN) {
+    // dh = acc; dn = gamma_j dh (stored); per-row sum_j dn*y; per-column sum_i dh*r*y
+    __bf16* C = (__bf16*)g.C;
+    const __bf16* Y = (const __bf16*)g.E;
+    const __bf16* gam = (const __bf16*)g.vcol;
+    float* red = (float*)smem;           // [2][BM] row partials
+    float* redc = red + 2 * BM;          // [2][BN] column partials
+    float gj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = col0 + lcol0 + j * 32;
+      gj[j] = col < g.N ? bf2f(gam[col]) : 0.0f;
+    }
+    float csum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float rs[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + lrow0 + i * 32 + acc_row(r, lane);
+        const float rv = row < g.M ? g.vrow[row] : 0.0f;
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = col0 + lcol0 + j * 32;
+          if (row < g.M && col < g.N) {
+            const float dh = acc[i][j][r];
+            const float yv = bf2f(Y[(int64_t)row * g.lde + col]);
+            const float dn = gj[j] * dh;
+            C[(int64_t)row * g.ldc + col] = f2bf(dn);
+            s += dn * yv;
+            csum[j] += dh * rv * yv;
+          }
+        }
+        rs[r] = s;
+      }
+      const float tot = halfwave_rowsum16(rs, lane);
+      if ((lane & 1) == 0) red[wn * BM + lrow0 + i * 32 + acc_row(l32 >> 1, lane)] = tot;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float c2 = csum[j] + __shfl_xor(csum[j], 32);
+      if (lane < 32) redc[wm * BN + wn * 128 + j * 32 + l32] = c2;
+    }
+    __syncthreads();
+    const int row = row0 + t;
+    if (row < g.M) g.part_row[(int64_t)row * g.ld_part_row + tn] = red[t] + red[BM + t];
+    const int col = col0 + t;
+    if (col < g.N) g.part_col[(int64_t)tm * g.ld_part_col + col] = redc[t] + redc[BN + t];
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    // blocks j = 0,1 hold gate columns, j = 2,3 the up columns of the same j
+    __bf16* GU = (__bf16*)g.C;
+    __bf16* Aout = (__bf16*)g.C2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + lrow0 + i * 32 + acc_row(r, lane);
+        if (row >= g.M) continue;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int jj = tn * 128 + wn * 64 + j * 32 + l32;
+          if (jj < g.F) {
+            const float gv = acc[i][j][r], uv = acc[i][j + 2][r];
+            GU[(int64_t)row * g.ldc + jj] = f2bf(gv);
+            GU[(int64_t)row * g.ldc + g.F + jj] = f2bf(uv);
+            Aout[(int64_t)row * g.ldc2 + jj] = f2bf(silu_f(gv) * uv);
+          }
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+    // da = acc [M, F]; g, u from the saved gu; dgu = [dg | du]
+    __bf16* DGU = (__bf16*)g.C;
+    const __bf16* GU = (const __bf16*)g.E;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + lrow0 + i * 32 + acc_row(r, lane);
+        if (row >= g.M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = col0 + lcol0 + j * 32;
+          if (col < g.N) {
+            const float da = acc[i][j][r];
+            const float gv = bf2f(GU[(int64_t)row * g.lde + col]);
+            const float uv = bf2f(GU[(int64_t)row * g.lde + g.F + col]);
+            const float sg = sigmoid_f(gv);
+            DGU[(int64_t)row * g.ldc + col] = f2bf(da * uv * sg * (1.0f + gv * (1.0f - sg)));
+            DGU[(int64_t)row * g.ldc + g.F + col] = f2bf(da * gv * sg);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 forward path: a plain LDS-tiled FMA GEMM (64x64 tile, 4x4 per thread)
+// with the same epilogue semantics.  A is [M,K] (k contiguous), B is [K,N].
+// ---------------------------------------------------------------------------
+constexpr int FT = kTileF32;
+constexpr int FK = 16;
+
+template <int EPI>
+__global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
+  __shared__ float sA[FK][FT + 4];
+  __shared__ float sB[FK][FT + 4];
+  __shared__ float red[FT][17];
+  const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+  const int tiles_n = (g.N + FT - 1) / FT;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int row0 = tm * FT, col0 = tn * FT;
+  const float* A = (const float*)g.A;
+  const float* B = (const float*)g.B;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < g.K; k0 += FK) {
+    for (int e = t; e < FT * FK; e += 256) {
+      const int m = e / FK, k = e % FK;
+      const int gr = row0 + m, gk = k0 + k;
+      sA[k][m] = (gr < g.M && gk < g.K) ? A[(int64_t)gr * g.lda + gk] : 0.0f;
+      const int kk = e / FT, n = e % FT;
+      const int gk2 = k0 + kk, gc = col0 + n;
+      sB[kk][n] = (gk2 < g.K && gc < g.N) ? B[(int64_t)gk2 * g.ldb + gc] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < FK; ++k) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sA[k][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = sB[k][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  float* C = (float*)g.C;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = row0 + ty * 4 + i;
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = col0 + tx * 4 + j;
+      if (row < g.M && col < g.N) {
+        float v = acc[i][j];
+        if constexpr (EPI == EPI_RESID_SUMSQ) {
+          v += ((const float*)g.E)[(int64_t)row * g.lde + col];
+          s += v * v;
+        } else if constexpr (EPI == EPI_ROWSCALE) {
+          v *= g.vrow[row];
+        }
+        C[(int64_t)row * g.ldc + col] = v;
+      }
+    }
+    if constexpr (EPI == EPI_RESID_SUMSQ) red[ty * 4 + i][tx] = s;
+  }
+  if constexpr (EPI == EPI_RESID_SUMSQ) {
+    __syncthreads();
+    if (t < FT) {
+      const int row = row0 + t;
+      float s = 0.0f;
+      for (int x = 0; x < 16; ++x) s += red[t][x];
+      if (row < g.M) g.part_row[(int64_t)row * g.ld_part_row + tn] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Small kernels
+// ---------------------------------------------------------------------------
+__global__ void fold_gamma_bf16(const __bf16* __restrict__ gamma, const __bf16* __restrict__ W2,
+                                __bf16* __restrict__ W2f, int64_t d, int64_t N) {
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // one 8-element chunk
+  const int64_t e0 = v * 8;
+  if (e0 >= d * N) return;
+  const int64_t j = e0 / N;
+  const float gj = bf2f(gamma[j]);
+  const bf16x8 w = *(const bf16x8*)(W2 + e0);
+  bf16x8 o;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = f2bf(gj * bf2f(w[k]));
+  *(bf16x8*)(W2f + e0) = o;
+}
+
+__global__ void fold_gamma_f32(const float* __restrict__ gamma, const float* __restrict__ W2,
+                               float* __restrict__ W2f, int64_t d, int64_t N) {
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t e0 = v * 4;
+  if (e0 >= d * N) return;
+  const float gj = gamma[e0 / N];
+  f32x4 w = *(const f32x4*)(W2 + e0);
+  *(f32x4*)(W2f + e0) = w * gj;
+}
+
+__global__ void row_rsqrt_kernel(const float* __restrict__ P, int64_t ldp, int T, int64_t M,
+                                 float inv_d, float eps, float* __restrict__ r) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M) return;
+  float s = 0.0f;
+  for (int k = 0; k < T; ++k) s += P[i * ldp + k];
+  r[i] = 1.0f / sqrtf(s * inv_d + eps);
+}
+
+__global__ void bwd_reduce_kernel(const float* __restrict__ S, int64_t lds, int Tn,
+                                  const float* __restrict__ r, int64_t M, float inv_d,
+                                  const float* __restrict__ G, int Tm, int64_t d,
+                                  float* __restrict__ c, float* __restrict__ dgamma) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < M) {
+    float s = 0.0f;
+    for (int k = 0; k < Tn; ++k) s += S[i * lds + k];
+    const float ri = r[i];
+    c[i] = ri * ri * ri * s * inv_d;
+  } else if (i < M + d) {
+    const int64_t j = i - M;
+    float s = 0.0f;
+    for (int k = 0; k < Tm; ++k) s += G[(int64_t)k * d + j];
+    dgamma[j] = s;
+  }
+}
+
+__global__ void dy_n_kernel(__bf16* __restrict__ dR, __bf16* __restrict__ n,
+                            const __bf16* __restrict__ y, const float* __restrict__ r,
+                            const float* __restrict__ c, int64_t M, int64_t d) {
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t e0 = v * 8;
+  if (e0 >= M * d) return;
+  const int64_t i = e0 / d;
+  const float ri = r[i], ci = c[i];
+  const bf16x8 dn = *(const bf16x8*)(dR + e0);
+  const bf16x8 yv = *(const bf16x8*)(y + e0);
+  bf16x8 o, nn;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float yk = bf2f(yv[k]);
+    o[k] = f2bf(ri * bf2f(dn[k]) - ci * yk);
+    nn[k] = f2bf(ri * yk);
+  }
+  *(bf16x8*)(dR + e0) = o;
+  *(bf16x8*)(n + e0) = nn;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <bool AK, bool BKM, int EPI>
+static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
+  const int tiles_m = (g.M + BM - 1) / BM;
+  const int tiles_n = (EPI == EPI_SWIGLU) ? (g.N + 127) / 128 : (g.N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, EPI>), dim3(tiles_m * tiles_n), dim3(NT), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStream_t s) {
+  // The combinations the block uses:
+  //   forward GEMMs:      A k-major, B mn-major  (X W1, y W2f, X W, a Wd)
+  //   input gradients:    A k-major, B k-major   (dz W2^T, dy W1^T, dz Wd^T, dgu W^T)
+  //   weight gradients:   A mn-major, B mn-major (n^T dz, X^T dy, a^T dz, X^T dgu)
+  if (ak && !bk) {
+    switch (epi) {
+      case EPI_STORE: return launch_one<true, false, EPI_STORE>(g, s);
+      case EPI_RESID_SUMSQ: return launch_one<true, false, EPI_RESID_SUMSQ>(g, s);
+      case EPI_ROWSCALE: return launch_one<true, false, EPI_ROWSCALE>(g, s);
+      case EPI_SWIGLU: return launch_one<true, false, EPI_SWIGLU>(g, s);
+      default: break;
+    }
+  } else if (ak && bk) {
+    switch (epi) {
+      case EPI_STORE: return launch_one<true, true, EPI_STORE>(g, s);
+      case EPI_DN: return launch_one<true, true, EPI_DN>(g, s);
+      case EPI_SWIGLU_BWD: return launch_one<true, true, EPI_SWIGLU_BWD>(g, s);
+      default: break;
+    }
+  } else if (!ak && !bk) {
+    switch (epi) {
+      case EPI_STORE: return launch_one<false, false, EPI_STORE>(g, s);
+      case EPI_ROWSCALE: return launch_one<false, false, EPI_ROWSCALE>(g, s);
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_f32(const GemmArgs& g, Epi epi, hipStream_t s) {
+  const int tiles = ((g.M + FT - 1) / FT) * ((g.N + FT - 1) / FT);
+  switch (epi) {
+    case EPI_RESID_SUMSQ:
+      hipLaunchKernelGGL((gemm_f32_kernel<EPI_RESID_SUMSQ>), dim3(tiles), dim3(256), 0, s, g);
+      break;
+    case EPI_ROWSCALE:
+      hipLaunchKernelGGL((gemm_f32_kernel<EPI_ROWSCALE>), dim3(tiles), dim3(256), 0, s, g);
+      break;
+    case EPI_STORE:
+      hipLaunchKernelGGL((gemm_f32_kernel<EPI_STORE>), dim3(tiles), dim3(256), 0, s, g);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_gamma(bool bf16, const void* gamma, const void* W2, void* W2f, int64_t d,
+                             int64_t N, hipStream_t s) {
+  const int per = bf16 ? 8 : 4;
+  const int64_t chunks = (d * N) / per;
+  const int blocks = (int)((chunks + 255) / 256);
+  if (bf16)
+    hipLaunchKernelGGL(fold_gamma_bf16, dim3(blocks), dim3(256), 0, s, (const __bf16*)gamma,
+                       (const __bf16*)W2, (__bf16*)W2f, d, N);
+  else
+    hipLaunchKernelGGL(fold_gamma_f32, dim3(blocks), dim3(256), 0, s, (const float*)gamma,
+                       (const float*)W2, (float*)W2f, d, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_rsqrt(const float* P, int64_t ldp, int T, int64_t M, int64_t d, float eps,
+                            float* r, hipStream_t s) {
+  hipLaunchKernelGGL(row_rsqrt_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, P, ldp,
+                     T, M, 1.0f / (float)d, eps, r);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce(const float* S, int64_t lds, int Tn, const float* r, int64_t M,
+                             int64_t d, const float* G, int Tm, float* c, float* dgamma,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((M + d + 255) / 256)), dim3(256), 0, s, S,
+                     lds, Tn, r, M, 1.0f / (float)d, G, Tm, d, c, dgamma);
+  return hipGetLastError();
+}
+
+hipError_t launch_dy_n(void* dR, void* n, const void* y, const float* r, const float* c,
+                       int64_t M, int64_t d, hipStream_t s) {
+  const int64_t chunks = (M * d) / 8;
+  hipLaunchKernelGGL(dy_n_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
+                     (__bf16*)dR, (__bf16*)n, (const __bf16*)y, r, c, M, d);
+  return hipGetLastError();
+}
+
+}  // namespace coda

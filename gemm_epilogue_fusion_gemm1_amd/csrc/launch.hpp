@@ -1,0 +1,63 @@
+// Internal interface between the C-ABI (api.cpp) and the kernels
+// (kernels.hip).  Not installed; the public interface is include/coda.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace coda {
+
+// Output tile of the bf16 MFMA GEMM kernels and of the fp32 fallback kernel.
+// The partial-sum workspaces are laid out per tile, so the C-ABI sizes them
+// from these constants.
+constexpr int kTileM = 256;
+constexpr int kTileN = 256;
+constexpr int kTileF32 = 64;
+
+// Epilogue selector of the GEMM kernels.
+enum Epi : int {
+  EPI_STORE = 0,       // C = acc
+  EPI_RESID_SUMSQ = 1, // y = acc + E; C = y; part_row[i][tile_n] = sum_{j in tile} y_ij^2
+  EPI_ROWSCALE = 2,    // C = vrow[i] * acc
+  EPI_DN = 3,          // dh = acc; C = dn = gamma_j dh; part_row = sum_j dn*y; part_col = sum_i dh*r*y
+  EPI_SWIGLU = 4,      // gate/up pair: C = gu (both halves), C2 = silu(g) * u
+  EPI_SWIGLU_BWD = 5,  // da = acc; C = dgu from the saved gu in E
+};
+
+// Operand layouts.  "K-major" = the contraction index is contiguous in memory.
+struct GemmArgs {
+  int M, N, K;                   // C is M x N (EPI_SWIGLU: N = F gate columns)
+  const void* A; int64_t lda;    // A: M x K logical
+  const void* B; int64_t ldb;    // B: K x N logical
+  void* C; int64_t ldc;
+  void* C2; int64_t ldc2;        // EPI_SWIGLU: a [M, F]
+  const void* E; int64_t lde;    // epilogue matrix input: R (RESID), y (DN), gu (SWIGLU_BWD)
+  const float* vrow;             // per-row vector: r (ROWSCALE in fwd, DN)
+  const void* vcol;              // per-column / per-row vector in dtype: gamma
+  float* part_row; int64_t ld_part_row;   // [M][tiles_n]
+  float* part_col; int64_t ld_part_col;   // [tiles_m][N]
+  int F;                         // SwiGLU half width (gate columns)
+  uint32_t A_bytes, B_bytes;     // buffer extents for hardware bounds checks
+};
+
+// Launchers: enqueue on `stream`, return the hipGetLastError() after launch.
+// a_kmajor / b_kmajor select the operand layouts; every epilogue is
+// instantiated for the layout combinations the block uses.
+hipError_t launch_gemm_bf16(const GemmArgs& g, bool a_kmajor, bool b_kmajor, Epi epi,
+                            hipStream_t stream);
+hipError_t launch_gemm_f32(const GemmArgs& g, Epi epi, hipStream_t stream);
+
+// W2f[j][n] = gamma[j] * W2[j][n] (rounded to the element type).
+hipError_t launch_fold_gamma(bool bf16, const void* gamma, const void* W2, void* W2f,
+                             int64_t d, int64_t N, hipStream_t stream);
+// r[i] = (sum_t P[i][t] / d + eps)^(-1/2)
+hipError_t launch_row_rsqrt(const float* P, int64_t ldp, int T, int64_t M, int64_t d, float eps,
+                            float* r, hipStream_t stream);
+// c[i] = r_i^3 * (sum_t S[i][t]) / d ;  dgamma[j] = sum_tau G[tau][j]
+hipError_t launch_bwd_reduce(const float* S, int64_t lds, int Tn, const float* r, int64_t M,
+                             int64_t d, const float* G, int Tm, float* c, float* dgamma,
+                             hipStream_t stream);
+// in place: dR[i][j] = r_i dR[i][j] - c_i y[i][j]  (dR holds dn on entry);  n = r_i y
+hipError_t launch_dy_n(void* dR, void* n, const void* y, const float* r, const float* c,
+                       int64_t M, int64_t d, hipStream_t stream);
+
+}  // namespace coda

@@ -1,0 +1,169 @@
+/*
+ * coda.h - C-ABI of the fused GEMM-Residual-RMSNorm-GEMM block and the fused
+ * SwiGLU gate/up block, forward and backward, on one AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Sources (the pages are three news articles on the paper "CODA: Rewriting
+ * Transformer Blocks as GEMM-Epilogue Programs"):
+ *   [JA] toolin.ai blog "CODA：LLMと初心者が光速のGPUカーネルを書けるようにする"
+ *   [RU] kucoin.com news flash (Russian) on the paper
+ *   [FR] kucoin.com news flash (French) on the paper
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are row-major and contiguous, with shapes as written beside each
+ * argument; a weight is stored [in, out].  Every pointer is a DEVICE pointer
+ * (HIP device memory of the current device) unless it is marked host.  The
+ * caller owns every buffer, including the workspace; the library allocates
+ * no device memory and keeps no state between calls, so calls are reentrant.
+ *
+ * Element types: `dtype` is the type of every tensor argument except r,
+ * dgamma and the workspace: CODA_BF16 (bfloat16, 2 bytes) or CODA_F32.
+ * r and dgamma are always float32.  Arithmetic accumulates in float32; bf16
+ * results are rounded to nearest even.
+ *
+ * Execution: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the call returns without waiting.  Results are ready when the
+ * stream reaches that point.  Calls that share a workspace or outputs on
+ * different streams race.
+ *
+ * Shapes: every size must be >= 1 and a multiple of 8 (bf16) or 4 (f32), so
+ * that each row starts on a 16-byte boundary.  Sizes need not be multiples of
+ * the kernels' tile sizes; edge tiles are masked.  Each tensor must fit in
+ * 2 GiB.
+ *
+ * Errors: every argument is checked before anything is enqueued; a failing
+ * check returns a non-zero coda_status and enqueues nothing.  A HIP launch
+ * failure returns CODA_ERR_HIP.  No C++ exception crosses this interface.
+ * coda_status_str() names each status.
+ */
+#ifndef CODA_H
+#define CODA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CODA_OK = 0,
+  CODA_ERR_NULL = 1,        /* a required pointer is NULL */
+  CODA_ERR_SHAPE = 2,       /* a size is < 1, not a multiple of 8 (bf16) / 4 (f32), or too large */
+  CODA_ERR_ALIGN = 3,       /* a tensor pointer is not 16-byte aligned */
+  CODA_ERR_ALIAS = 4,       /* an output overlaps an input, another output or the workspace */
+  CODA_ERR_DTYPE = 5,       /* dtype is not a coda_dtype value */
+  CODA_ERR_EPS = 6,         /* eps is not finite or not > 0 */
+  CODA_ERR_WORKSPACE = 7,   /* workspace is NULL or smaller than the matching *_workspace_bytes */
+  CODA_ERR_UNSUPPORTED = 8, /* valid request this build does not implement (e.g. f32 backward) */
+  CODA_ERR_HIP = 9          /* a HIP runtime call or kernel launch failed */
+} coda_status;
+
+typedef enum { CODA_F32 = 0, CODA_BF16 = 1 } coda_dtype;
+
+/* Name of a status code (static string; never NULL). */
+const char* coda_status_str(coda_status s);
+
+/* Library version string, e.g. "coda-mi355x 0.1.0 gfx950" (static). */
+const char* coda_version(void);
+
+/* ------------------------------------------------------------------------
+ * Forward of the GEMM-Residual-RMSNorm-GEMM block.
+ *
+ * Computes, per [RU] and [FR] insight sections ("CODA: В «Финале» спрятаны
+ * сокровища" / "CODA : « La fin » cache un trésor") and [JA] 核心の洞察:
+ *   y = X W1 + R                         (first GEMM, residual in its epilogue)
+ *   r_i = (mean_j y_ij^2 + eps)^(-1/2)   (from per-tile partial sums of
+ *                                         squares left by the first GEMM's
+ *                                         epilogue, combined by a small kernel)
+ *   z = diag(r) (y (diag(gamma) W2))     (second GEMM with gamma folded into
+ *                                         W2 and r applied in its epilogue)
+ * which equals RMSNorm(y) * gamma @ W2 up to rounding.
+ *
+ *   X     [M,K]  in      W1 [K,d] in     R [M,d] in (residual)
+ *   gamma [d]    in      W2 [d,N] in
+ *   y     [M,d]  out     the residual stream X W1 + R, saved for the backward
+ *                        (rounded to dtype; the partial sums use it unrounded)
+ *   r     [M]    out     float32 row scales, saved for the backward
+ *   z     [M,N]  out
+ *   eps   > 0, finite
+ *   workspace: >= coda_fwd_workspace_bytes(dtype, M, K, d, N) bytes, device,
+ *              16-byte aligned, contents ignored; holds the partial sums and
+ *              the folded weight diag(gamma) W2 during the call.
+ * Outputs must not overlap inputs, each other or the workspace.
+ * ---------------------------------------------------------------------- */
+size_t coda_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N);
+coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N, float eps,
+                     const void* X, const void* W1, const void* R, const void* gamma,
+                     const void* W2, void* y, float* r, void* z,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backward of the same block: the exact gradient of L = <dz, z>, given the
+ * tensors saved by coda_fwd (y, r).  The pages state that a block-local
+ * forward gives a block-local backward ([RU]/[FR] insight sections) and quote
+ * this kernel's speed-up ([JA] 実験結果, [RU] "Результаты эксперимента"); the
+ * gradient itself is the calculus of the forward above:
+ *   n = diag(r) y;  dW2 = diag(gamma) n^T dz;  dh = dz W2^T;
+ *   dgamma_j = sum_i dh_ij n_ij;  dn = dh diag(gamma);  s_i = sum_j dn_ij y_ij;
+ *   dy = diag(r) dn - diag(r^3 s / d) y;  dR = dy;
+ *   dX = dy W1^T;  dW1 = X^T dy.
+ *
+ *   X [M,K], W1 [K,d], gamma [d], W2 [d,N], y [M,d], r [M] (float32),
+ *   dz [M,N]: in.   dX [M,K], dW1 [K,d], dR [M,d], dW2 [d,N]: out (dtype).
+ *   dgamma [d]: out, float32.
+ *   workspace: >= coda_bwd_workspace_bytes(dtype, M, K, d, N) bytes.
+ * CODA_F32 returns CODA_ERR_UNSUPPORTED in this build.
+ * ---------------------------------------------------------------------- */
+size_t coda_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N);
+coda_status coda_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N,
+                     const void* X, const void* W1, const void* gamma, const void* W2,
+                     const void* y, const float* r, const void* dz,
+                     void* dX, void* dW1, void* dR, void* dW2, float* dgamma,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * SwiGLU gate/up GEMM with the activation in its epilogue, then the
+ * down-projection ([JA] 組み合わせ可能な5種類の「積み木」, [RU] "Пять
+ * «кирпичиков»", [FR] "Cinq « blocs »": the elementwise-transform primitive
+ * covers activations; the matrix-tile store primitive saves intermediates):
+ *   gu = X W,  W = [W_gate | W_up]  (gate columns 0..F-1, up columns F..2F-1)
+ *   a  = silu(g) * u,  silu(t) = t / (1 + exp(-t)),  g = gu[:, :F], u = gu[:, F:]
+ *   z  = a Wd
+ *
+ *   X [M,d], W [d,2F], Wd [F,d]: in.   gu [M,2F], a [M,F]: out, saved for the
+ *   backward.   z [M,d]: out.   No workspace is needed (pass NULL, 0).
+ * CODA_F32 returns CODA_ERR_UNSUPPORTED in this build.
+ * ---------------------------------------------------------------------- */
+size_t coda_swiglu_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t d, int64_t F);
+coda_status coda_swiglu_fwd(coda_dtype dtype, int64_t M, int64_t d, int64_t F,
+                            const void* X, const void* W, const void* Wd,
+                            void* gu, void* a, void* z,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * SwiGLU backward: exact gradient of L = <dz, z> given the saved gu and a
+ * (the pages quote its speed-up: [JA] 実験結果, [RU] "Результаты
+ * эксперимента"):
+ *   da = dz Wd^T;  sg = sigmoid(g);
+ *   dg = da u sg (1 + g (1 - sg));  du = da g sg;  dgu = [dg | du];
+ *   dWd = a^T dz;  dW = X^T dgu;  dX = dgu W^T.
+ *
+ *   X [M,d], W [d,2F], Wd [F,d], gu [M,2F], a [M,F], dz [M,d]: in.
+ *   dX [M,d], dW [d,2F], dWd [F,d]: out.
+ *   workspace: >= coda_swiglu_bwd_workspace_bytes(...) bytes (holds dgu).
+ * CODA_F32 returns CODA_ERR_UNSUPPORTED in this build.
+ * ---------------------------------------------------------------------- */
+size_t coda_swiglu_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t d, int64_t F);
+coda_status coda_swiglu_bwd(coda_dtype dtype, int64_t M, int64_t d, int64_t F,
+                            const void* X, const void* W, const void* Wd,
+                            const void* gu, const void* a, const void* dz,
+                            void* dX, void* dW, void* dWd,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CODA_H */

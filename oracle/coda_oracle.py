@@ -51,7 +51,7 @@ import numpy as np
 
 __all__ = [
     "bf16_rne", "ref_fwd", "ref_fwd_rewritten", "ref_partials", "ref_bwd",
-    "ref_fwd_rows", "ref_bwd_sampled", "sigmoid", "ref_swiglu_fwd",
+    "ref_y_r", "ref_fwd_rows", "ref_bwd_sampled", "sigmoid", "ref_swiglu_fwd",
     "ref_swiglu_bwd", "ref_swiglu_fwd_rows", "ref_swiglu_bwd_sampled",
 ]
 
@@ -187,6 +187,14 @@ def ref_bwd(X, W1, gamma, W2, y, r, dz) -> dict:
 # They restrict the same definitions to chosen rows or columns.
 # ---------------------------------------------------------------------------
 
+def ref_y_r(X, W1, R, eps: float) -> dict:
+    """The first half of ``ref_fwd``: y = X W1 + R and r, without the second GEMM."""
+    X, W1, R = map(_f64, (X, W1, R))
+    y = X @ W1 + R
+    r = 1.0 / np.sqrt(np.mean(y * y, axis=1) + eps)
+    return {"y": y, "r": r}
+
+
 def ref_fwd_rows(X, W1, R, gamma, W2, eps: float, rows) -> dict:
     """``ref_fwd`` evaluated for the given rows only (rows are independent)."""
     rows = np.asarray(rows)
@@ -281,28 +289,38 @@ def ref_swiglu_fwd_rows(X, W, Wd, rows) -> dict:
     return out
 
 
-def ref_swiglu_bwd_sampled(X, W, Wd, gu, a, dz, rows, cols_W, cols_Wd) -> dict:
-    """``ref_swiglu_bwd`` with dX and dgu restricted to ``rows``, dW to columns
-    ``cols_W`` (indices into [0, 2F)) and dWd to columns ``cols_Wd``."""
-    X, W, Wd = map(_f64, (X, W, Wd))
+def ref_swiglu_bwd_sampled(X, W, Wd, dz, rows, cols_W, rows_Wd, saved_bf16: bool = True) -> dict:
+    """``ref_swiglu_bwd`` restricted: dX and dgu on ``rows``, dW on the columns
+    ``cols_W`` (indices into [0, 2F)), dWd on the rows ``rows_Wd`` (indices
+    into [0, F)).
+
+    The saved gu and a are recomputed here from X and W, only where needed,
+    and rounded to bf16 when ``saved_bf16`` (the storage contract of the
+    saved activations); the arithmetic is that of ``ref_swiglu_bwd``.
+    """
+    X, W, Wd, dz = map(_f64, (X, W, Wd, dz))
     F = W.shape[1] // 2
+    keep = bf16_rne if saved_bf16 else (lambda v: v)
     rows = np.asarray(rows)
     cols_W = np.asarray(cols_W)
-    cols_Wd = np.asarray(cols_Wd)
-    dz = _f64(dz)
-    gu = _f64(gu)
-    # rows: the whole gradient chain restricted to these rows
-    sub = ref_swiglu_bwd(X[rows], W, Wd, gu[rows], _f64(a[rows]), dz[rows])
-    # dW columns: need dgu[:, cols] over every row
+    rows_Wd = np.asarray(rows_Wd)
+    # rows: the whole gradient chain for these tokens
+    gu_r = X[rows] @ W
+    g_r, u_r = gu_r[:, :F], gu_r[:, F:]
+    a_r = g_r * sigmoid(g_r) * u_r
+    sub = ref_swiglu_bwd(X[rows], W, Wd, keep(gu_r), keep(a_r), dz[rows])
+    # dW columns: dgu[:, c] over every token
     jg = cols_W % F
     is_gate = cols_W < F
-    da_c = dz @ Wd.T[:, jg]
-    g = gu[:, jg]
-    u = gu[:, F + jg]
+    g = keep(X @ W[:, jg])
+    u = keep(X @ W[:, F + jg])
+    da = dz @ Wd[jg, :].T
     sg = sigmoid(g)
-    dgu_c = np.where(is_gate[None, :], da_c * u * sg * (1.0 + g * (1.0 - sg)), da_c * g * sg)
-    dW_cols = X.T @ dgu_c
-    dWd_cols = _f64(a).T @ dz[:, cols_Wd]
-    return {"rows": rows, "cols_W": cols_W, "cols_Wd": cols_Wd,
+    dgu_c = np.where(is_gate[None, :], da * u * sg * (1.0 + g * (1.0 - sg)), da * g * sg)
+    # dWd rows: a[:, j] over every token
+    gj = X @ W[:, rows_Wd]
+    uj = X @ W[:, F + rows_Wd]
+    a_c = keep(gj * sigmoid(gj) * uj)
+    return {"rows": rows, "cols_W": cols_W, "rows_Wd": rows_Wd,
             "dX_rows": sub["dX"], "dgu_rows": sub["dgu"],
-            "dW_cols": dW_cols, "dWd_cols": dWd_cols}
+            "dW_cols": X.T @ dgu_c, "dWd_rows": a_c.T @ dz}

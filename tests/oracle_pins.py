@@ -233,6 +233,9 @@ def pin_sampled_forms(O):
     fr = O.ref_fwd_rows(c["X"], c["W1"], c["R"], c["gamma"], c["W2"], c["eps"], rows)
     for k in ("y", "r", "z"):
         _close(fr[k], f[k][rows], 1e-14, f"rows {k}")
+    yr = O.ref_y_r(c["X"], c["W1"], c["R"], c["eps"])
+    _close(yr["y"], f["y"], 1e-14, "ref_y_r y")
+    _close(yr["r"], f["r"], 1e-14, "ref_y_r r")
     b = O.ref_bwd(c["X"], c["W1"], c["gamma"], c["W2"], f["y"], f["r"], c["dz"])
     cd, cn = np.array([1, 5, 15]), np.array([0, 11, 23])
     bs = O.ref_bwd_sampled(c["X"], c["W1"], c["gamma"], c["W2"], f["y"], f["r"], c["dz"], rows, cd, cn)
@@ -342,17 +345,22 @@ def pin_golden_swiglu(O):
 
 
 def pin_swiglu_sampled(O):
+    """Row/column-restricted SwiGLU forms equal slices of the full forms, both
+    with exact saved activations and with saved activations rounded to bf16."""
     c = _swiglu_case(35, 20, 8, 12)
-    b, f = _swiglu_bwd(O, c)
-    rows, cw, cd = np.array([0, 9, 19]), np.array([0, 5, 12, 23]), np.array([1, 7])
+    f = O.ref_swiglu_fwd(c["X"], c["W"], c["Wd"])
+    rows, cw, rd = np.array([0, 9, 19]), np.array([0, 5, 12, 23]), np.array([1, 7, 11])
     fr = O.ref_swiglu_fwd_rows(c["X"], c["W"], c["Wd"], rows)
     for k in ("gu", "a", "z"):
         _close(fr[k], f[k][rows], 1e-14, f"swiglu rows {k}")
-    s = O.ref_swiglu_bwd_sampled(c["X"], c["W"], c["Wd"], f["gu"], f["a"], c["dz"], rows, cw, cd)
-    _close(s["dX_rows"], b["dX"][rows], 1e-13, "swiglu sampled dX")
-    _close(s["dgu_rows"], b["dgu"][rows], 1e-13, "swiglu sampled dgu")
-    _close(s["dW_cols"], b["dW"][:, cw], 1e-13, "swiglu sampled dW")
-    _close(s["dWd_cols"], b["dWd"][:, cd], 1e-13, "swiglu sampled dWd")
+    for saved_bf16 in (False, True):
+        keep = O.bf16_rne if saved_bf16 else (lambda v: v)
+        b = O.ref_swiglu_bwd(c["X"], c["W"], c["Wd"], keep(f["gu"]), keep(f["a"]), c["dz"])
+        s = O.ref_swiglu_bwd_sampled(c["X"], c["W"], c["Wd"], c["dz"], rows, cw, rd, saved_bf16)
+        _close(s["dX_rows"], b["dX"][rows], 1e-13, "swiglu sampled dX")
+        _close(s["dgu_rows"], b["dgu"][rows], 1e-13, "swiglu sampled dgu")
+        _close(s["dW_cols"], b["dW"][:, cw], 1e-13, "swiglu sampled dW")
+        _close(s["dWd_rows"], b["dWd"][rd], 1e-13, "swiglu sampled dWd")
 
 
 # ------------------------------------------------------------------- bf16 pins

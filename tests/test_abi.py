@@ -1,0 +1,178 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and rejects bad arguments with the documented status before any HIP
+call (so no GPU is needed; the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "coda.h")
+
+OK, NULL, SHAPE, ALIGN, ALIAS, DTYPE, EPS, WORKSPACE, UNSUPPORTED, HIP = range(10)
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(coda_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from gemm_epilogue_fusion_gemm1_amd import lib_path, load_library
+    if not os.path.exists(lib_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for fn in ("coda_fwd", "coda_bwd", "coda_swiglu_fwd", "coda_swiglu_bwd"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    from gemm_epilogue_fusion_gemm1_amd import lib_path
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (coda_[a-z_0-9]+)", out))
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    for f in declared_functions():
+        assert hasattr(L, f)
+
+
+def test_status_strings_and_version(L):
+    for s in range(10):
+        assert L.coda_status_str(s).decode().startswith("CODA_")
+    assert b"gfx950" in L.coda_version()
+
+
+def test_workspace_sizes(L):
+    M, K, d, N = 8192, 4096, 4096, 11008
+    fw = L.coda_fwd_workspace_bytes(BF16, M, K, d, N)
+    # partials [M, d/256] fp32 + folded weight [d, N] bf16
+    assert fw >= M * (d // 256) * 4 + d * N * 2
+    bw = L.coda_bwd_workspace_bytes(BF16, M, K, d, N)
+    assert bw >= M * d * 2 + M * (d // 256) * 4 + (M // 256) * d * 4 + M * 4
+    assert L.coda_swiglu_bwd_workspace_bytes(BF16, 8192, 4096, 14336) >= 8192 * 2 * 14336 * 2
+    assert L.coda_bwd_workspace_bytes(F32, M, K, d, N) == 0
+    assert L.coda_fwd_workspace_bytes(7, M, K, d, N) == 0
+
+
+class FakeMem:
+    """Distinct, 16-byte aligned fake device addresses, never dereferenced."""
+
+    def __init__(self):
+        self.next = 1 << 40
+
+    def __call__(self, nbytes):
+        p = self.next
+        self.next += (nbytes + 4095) // 4096 * 4096 + 4096
+        return ctypes.c_void_p(p)
+
+
+def fwd_args(dtype=BF16, M=64, K=32, d=48, N=80, eps=1e-6):
+    m = FakeMem()
+    e = 2 if dtype == BF16 else 4
+    a = dict(dtype=dtype, M=M, K=K, d=d, N=N, eps=eps,
+             X=m(M * K * e), W1=m(K * d * e), R=m(M * d * e), gamma=m(d * e), W2=m(d * N * e),
+             y=m(M * d * e), r=m(M * 4), z=m(M * N * e))
+    a["ws_bytes"] = 1 << 20
+    a["ws"] = m(a["ws_bytes"])
+    return a
+
+
+def call_fwd(L, a):
+    return L.coda_fwd(a["dtype"], a["M"], a["K"], a["d"], a["N"], a["eps"], a["X"], a["W1"], a["R"],
+                      a["gamma"], a["W2"], a["y"], a["r"], a["z"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dtype", 5, DTYPE),
+    ("X", None, NULL), ("W2", None, NULL), ("r", None, NULL), ("z", None, NULL),
+    ("M", 0, SHAPE), ("M", -8, SHAPE), ("K", 12, SHAPE), ("d", 4, SHAPE), ("N", 81, SHAPE),
+    ("eps", 0.0, EPS), ("eps", -1e-6, EPS), ("eps", float("nan"), EPS), ("eps", float("inf"), EPS),
+    ("ws", None, WORKSPACE), ("ws_bytes", 16, WORKSPACE),
+])
+def test_fwd_rejects(L, field, value, status):
+    a = fwd_args()
+    a[field] = value
+    assert call_fwd(L, a) == status
+
+
+def test_fwd_rejects_misalignment_and_alias(L):
+    a = fwd_args()
+    a["R"] = ctypes.c_void_p(a["R"].value + 2)
+    assert call_fwd(L, a) == ALIGN
+    a = fwd_args()
+    a["z"] = ctypes.c_void_p(a["X"].value)          # output over an input
+    assert call_fwd(L, a) == ALIAS
+    a = fwd_args()
+    a["y"] = ctypes.c_void_p(a["ws"].value + 256)   # output inside the workspace
+    assert call_fwd(L, a) == ALIAS
+    a = fwd_args()
+    a["r"] = ctypes.c_void_p(a["y"].value + 16)     # two outputs overlap
+    assert call_fwd(L, a) == ALIAS
+
+
+def test_fwd_f32_multiple_of_four(L):
+    a = fwd_args(dtype=F32, M=12, K=20, d=28, N=36)
+    a["ws_bytes"] = 16
+    assert call_fwd(L, a) == WORKSPACE               # shapes 12/20/28/36 pass for f32 ...
+    a = fwd_args(dtype=F32, M=12, K=20, d=30, N=36)
+    assert call_fwd(L, a) == SHAPE                   # ... 30 is not a multiple of 4
+
+
+def test_too_large_tensor(L):
+    a = fwd_args(M=1 << 16, N=1 << 15)               # z would be 4 GiB of bf16
+    assert call_fwd(L, a) == SHAPE
+
+
+def bwd_call(L, **over):
+    m = FakeMem()
+    M, K, d, N = 64, 32, 48, 80
+    a = dict(dtype=BF16, M=M, K=K, d=d, N=N, X=m(M * K * 2), W1=m(K * d * 2), gamma=m(d * 2),
+             W2=m(d * N * 2), y=m(M * d * 2), r=m(M * 4), dz=m(M * N * 2), dX=m(M * K * 2),
+             dW1=m(K * d * 2), dR=m(M * d * 2), dW2=m(d * N * 2), dgamma=m(d * 4),
+             ws=m(1 << 20), ws_bytes=1 << 20)
+    a.update(over)
+    return L.coda_bwd(a["dtype"], a["M"], a["K"], a["d"], a["N"], a["X"], a["W1"], a["gamma"], a["W2"],
+                      a["y"], a["r"], a["dz"], a["dX"], a["dW1"], a["dR"], a["dW2"], a["dgamma"],
+                      a["ws"], a["ws_bytes"], None)
+
+
+def test_bwd_rejects(L):
+    assert bwd_call(L, dtype=9) == DTYPE
+    assert bwd_call(L, dz=None) == NULL
+    assert bwd_call(L, dgamma=None) == NULL
+    assert bwd_call(L, N=84) == SHAPE
+    assert bwd_call(L, dtype=F32) == UNSUPPORTED
+    assert bwd_call(L, ws_bytes=64) == WORKSPACE
+    assert bwd_call(L, ws=None) == WORKSPACE
+    assert bwd_call(L, dgamma=ctypes.c_void_p((1 << 41) + 4)) == ALIGN
+
+
+def test_bwd_alias(L):
+    m = FakeMem()
+    p = m(1 << 16)
+    assert bwd_call(L, dX=p, dW1=ctypes.c_void_p(p.value + 64)) == ALIAS
+
+
+def test_swiglu_rejects(L):
+    m = FakeMem()
+    M, d, F = 64, 32, 40
+    X, W, Wd = m(M * d * 2), m(d * 2 * F * 2), m(F * d * 2)
+    gu, a, z = m(M * 2 * F * 2), m(M * F * 2), m(M * d * 2)
+    assert L.coda_swiglu_fwd(BF16, M, d, F, X, W, Wd, gu, a, None, None, 0, None) == NULL
+    assert L.coda_swiglu_fwd(BF16, M, d, 44, X, W, Wd, gu, a, z, None, 0, None) == SHAPE
+    assert L.coda_swiglu_fwd(F32, M, d, F, X, W, Wd, gu, a, z, None, 0, None) == UNSUPPORTED
+    assert L.coda_swiglu_fwd(BF16, M, d, F, X, W, Wd, gu, gu, z, None, 0, None) == ALIAS
+    dX, dW, dWd, ws = m(M * d * 2), m(d * 2 * F * 2), m(F * d * 2), m(M * 2 * F * 2)
+    need = L.coda_swiglu_bwd_workspace_bytes(BF16, M, d, F)
+    assert L.coda_swiglu_bwd(BF16, M, d, F, X, W, Wd, gu, a, z, dX, dW, dWd, ws, need - 16, None) == WORKSPACE
+    assert L.coda_swiglu_bwd(BF16, M, d, F, X, W, Wd, gu, a, z, dX, dW, X, ws, need, None) == ALIAS
