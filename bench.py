@@ -1,0 +1,356 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused GEMM-Residual-RMSNorm-GEMM block, forward + backward,
+on one MI355X.
+
+One step = coda_fwd + coda_bwd over one batch of the LLaMA-7B-shaped workload
+(M = 8192 tokens, K = d = 4096, N = 11008, bf16 storage, fp32 accumulation),
+inputs resident in HBM.  Printed: ONE JSON line with the throughput (TFLOP/s of
+algorithmic GEMM work, 6 M (K d + d N) per step), the fraction of the MI355X
+dense bf16 MFMA peak, the speed-up over an unfused hipBLASLt + F.rms_norm +
+autograd step on the same GPU, per-kernel times from HIP events recorded on
+the stream the kernels run on, the roofline of the dominant kernel, the same
+figures for the 70B-hidden and SwiGLU workloads under "also", and the CPU
+oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-also] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA peak (vendor figure, no sparsity)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "fused fwd+bwd TFLOP/s & %bf16 MFMA peak; speedup vs unfused, 7B/70B"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_fwdbwd")
+    ap.add_argument("--no-also", action="store_true", help="skip the 70B and SwiGLU workloads")
+    ap.add_argument("--no-unfused", action="store_true", help="skip the unfused torch baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- workloads
+
+class CodaCase:
+    """Device buffers of a GEMM-Residual-RMSNorm-GEMM workload and its two steps."""
+
+    def __init__(self, w, torch, coda, h):
+        dev = torch.device("cuda:0")
+        self.w, self.torch, self.coda = w, torch, coda
+        up = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)  # noqa: E731
+        self.t = {k: up(v) for k, v in h.items()}
+        M, K, d, N = w.M, w.K, w.d, w.N
+        bf = torch.bfloat16
+        self.y = torch.empty((M, d), dtype=bf, device=dev)
+        self.r = torch.empty((M,), dtype=torch.float32, device=dev)
+        self.z = torch.empty((M, N), dtype=bf, device=dev)
+        self.dX = torch.empty((M, K), dtype=bf, device=dev)
+        self.dW1 = torch.empty((K, d), dtype=bf, device=dev)
+        self.dR = torch.empty((M, d), dtype=bf, device=dev)
+        self.dW2 = torch.empty((d, N), dtype=bf, device=dev)
+        self.dg = torch.empty((d,), dtype=torch.float32, device=dev)
+        self.wsf = torch.empty(coda.fwd_workspace_bytes(1, M, K, d, N), dtype=torch.uint8, device=dev)
+        self.wsb = torch.empty(coda.bwd_workspace_bytes(1, M, K, d, N), dtype=torch.uint8, device=dev)
+        self.kernels_per_step = 10
+
+    def flops(self):
+        return self.w.flops_fwd() + self.w.flops_bwd()
+
+    def fused_step(self):
+        t, c = self.t, self.coda
+        c.coda_fwd(t["X"], t["W1"], t["R"], t["gamma"], t["W2"], self.w.eps, self.y, self.r, self.z, self.wsf)
+        c.coda_bwd(t["X"], t["W1"], t["gamma"], t["W2"], self.y, self.r, t["dz"], self.dX, self.dW1,
+                   self.dR, self.dW2, self.dg, self.wsb)
+
+    def unfused_setup(self):
+        torch = self.torch
+        self.leaf = {k: self.t[k].detach().clone().requires_grad_(True) for k in ("X", "W1", "R", "gamma", "W2")}
+
+    def unfused_step(self):
+        torch, F = self.torch, self.torch.nn.functional
+        p = self.leaf
+        y = p["X"] @ p["W1"] + p["R"]
+        z = F.rms_norm(y, (self.w.d,), p["gamma"], self.w.eps) @ p["W2"]
+        torch.autograd.grad(z, [p["X"], p["W1"], p["R"], p["gamma"], p["W2"]], self.t["dz"])
+
+
+class SwigluCase:
+    def __init__(self, w, torch, coda, h):
+        dev = torch.device("cuda:0")
+        self.w, self.torch, self.coda = w, torch, coda
+        self.t = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in h.items()}
+        M, d, F = w.M, w.d, w.F
+        bf = torch.bfloat16
+        self.gu = torch.empty((M, 2 * F), dtype=bf, device=dev)
+        self.a = torch.empty((M, F), dtype=bf, device=dev)
+        self.z = torch.empty((M, d), dtype=bf, device=dev)
+        self.dX = torch.empty((M, d), dtype=bf, device=dev)
+        self.dW = torch.empty((d, 2 * F), dtype=bf, device=dev)
+        self.dWd = torch.empty((F, d), dtype=bf, device=dev)
+        self.ws = torch.empty(coda.swiglu_bwd_workspace_bytes(1, M, d, F), dtype=torch.uint8, device=dev)
+        self.kernels_per_step = 6
+
+    def flops(self):
+        return self.w.flops_fwd() + self.w.flops_bwd()
+
+    def fused_step(self):
+        t, c = self.t, self.coda
+        c.coda_swiglu_fwd(t["X"], t["W"], t["Wd"], self.gu, self.a, self.z)
+        c.coda_swiglu_bwd(t["X"], t["W"], t["Wd"], self.gu, self.a, t["dz"], self.dX, self.dW, self.dWd, self.ws)
+
+    def unfused_setup(self):
+        self.leaf = {k: self.t[k].detach().clone().requires_grad_(True) for k in ("X", "W", "Wd")}
+
+    def unfused_step(self):
+        torch, F = self.torch, self.torch.nn.functional
+        p = self.leaf
+        gu = p["X"] @ p["W"]
+        Fh = self.w.F
+        z = (F.silu(gu[:, :Fh]) * gu[:, Fh:]) @ p["Wd"]
+        torch.autograd.grad(z, [p["X"], p["W"], p["Wd"]], self.t["dz"])
+
+
+def make_case(w, torch, coda):
+    from gemm_epilogue_fusion_gemm1_amd import synth
+    h = synth.workload_inputs(w)
+    return (CodaCase if w.kind == "coda" else SwigluCase)(w, torch, coda, h), h
+
+
+# ------------------------------------------------------------------- timing
+
+def time_steps(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def kernel_table(trace, steps):
+    """Per kernel name: launches, mean ms, algorithmic flops and bytes per launch."""
+    tab = {}
+    for name, ms, fl, by in trace:
+        d = tab.setdefault(name, {"launches": 0, "ms_total": 0.0, "flops": fl, "bytes": by})
+        d["launches"] += 1
+        d["ms_total"] += ms
+    out = {}
+    for name, d in tab.items():
+        mean = d["ms_total"] / d["launches"]
+        row = {"mean_ms": round(mean, 4), "ms_per_step": round(d["ms_total"] / steps, 4),
+               "launches": d["launches"]}
+        if d["flops"] > 0:
+            row["tflops"] = round(d["flops"] / (mean * 1e-3) / 1e12, 1)
+        row["gbs"] = round(d["bytes"] / (mean * 1e-3) / 1e9, 1)
+        row["flops"] = d["flops"]
+        row["bytes"] = d["bytes"]
+        out[name] = row
+    return out
+
+
+def run_case(case, torch, coda, steps, warmup, unfused):
+    """Timed region: `steps` fused steps, every kernel bracketed by HIP events."""
+    for _ in range(warmup):
+        case.fused_step()
+    torch.cuda.synchronize()
+    coda.trace_start(steps * case.kernels_per_step + 8)
+    ms = time_steps(torch, case.fused_step, steps, 0)
+    trace = coda.trace_read()
+    coda.trace_stop()
+    # the same steps without the per-kernel events, to bound their overhead
+    ms_untraced = time_steps(torch, case.fused_step, steps, 1)
+    res = {"ms_per_step": ms, "ms_per_step_untraced": ms_untraced,
+           "kernels": kernel_table(trace, steps)}
+    if unfused:
+        try:
+            torch.backends.cuda.preferred_blas_library("cublaslt")   # hipBLASLt on ROCm
+        except Exception:  # pragma: no cover - older torch
+            pass
+        case.unfused_setup()
+        res["unfused_ms_per_step"] = time_steps(torch, case.unfused_step, steps, warmup)
+        res["unfused_blas"] = str(torch.backends.cuda.preferred_blas_library())
+        del case.leaf
+    return res
+
+
+def summary(case, res):
+    fl = case.flops()
+    tf = fl / (res["ms_per_step"] * 1e-3) / 1e12
+    out = {"tflops": round(tf, 1), "pct_bf16_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+           "ms_per_step": round(res["ms_per_step"], 4),
+           "ms_per_step_untraced": round(res["ms_per_step_untraced"], 4),
+           "flops_per_step": fl}
+    if "unfused_ms_per_step" in res:
+        out["unfused_ms_per_step"] = round(res["unfused_ms_per_step"], 4)
+        out["speedup_vs_unfused"] = round(res["unfused_ms_per_step"] / res["ms_per_step"], 3)
+        out["unfused_blas"] = res["unfused_blas"]
+    return out
+
+
+def roofline(kernels, ms_per_step):
+    """Roofline of the kernel with the largest share of the step."""
+    name = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    k = kernels[name]
+    mean_s = k["mean_ms"] * 1e-3
+    if k["flops"] > 0:
+        ach = k["flops"] / mean_s / 1e12
+        rf = {"kernel": name, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+              "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    else:
+        ach = k["bytes"] / mean_s / 1e9
+        rf = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+              "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+    rf["share_of_step"] = round(k["ms_per_step"] / ms_per_step, 3)
+    rf["traffic"] = measured_traffic(name)
+    return rf
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the kernel source as it is now; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        data = json.load(fh)
+    src = os.path.join(ROOT, "gemm_epilogue_fusion_gemm1_amd", "csrc", "kernels.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if data.get("kernels_hip_sha256") != sha:
+        return None
+    v = data.get("kernels", {}).get(kernel)
+    return None if v is None else v.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(w, h, target_s):
+    """The fp64 oracle (unfused forward + backward) on the first Ms tokens of the
+    same workload, Ms grown until one call takes about `target_s` seconds."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = None
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+
+    def run(Ms):
+        sl = slice(0, Ms)
+        t0 = time.perf_counter()
+        if w.kind == "coda":
+            f = oracle.ref_fwd(h["X"][sl], h["W1"], h["R"][sl], h["gamma"], h["W2"], w.eps)
+            oracle.ref_bwd(h["X"][sl], h["W1"], h["gamma"], h["W2"], f["y"], f["r"], h["dz"][sl])
+            fl = 6.0 * Ms * (w.K * w.d + w.d * w.N)
+        else:
+            f = oracle.ref_swiglu_fwd(h["X"][sl], h["W"], h["Wd"])
+            oracle.ref_swiglu_bwd(h["X"][sl], h["W"], h["Wd"], f["gu"], f["a"], h["dz"][sl])
+            fl = 18.0 * Ms * w.d * w.F
+        return time.perf_counter() - t0, fl
+
+    Ms = 128
+    dt, fl = run(Ms)
+    while dt < target_s / 3 and Ms < w.M:
+        Ms = int(min(w.M, max(2 * Ms, Ms * target_s / max(dt, 1e-3) * 0.8)))
+        Ms -= Ms % 128
+        dt, fl = run(Ms)
+    return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads or cores,
+            "kind": "oracle",
+            "sample": f"{w.name}: first {Ms} of {w.M} tokens, full weights; fp64 numpy "
+                      f"(BLAS threads {threads}, affinity cores {cores}); one fwd+bwd call {dt:.1f} s"}
+
+
+# --------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the fused block is "
+                          "benchmarked on a single MI355X; run with --gpus 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    from gemm_epilogue_fusion_gemm1_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    coda.load_library()
+    unfused = not args.no_unfused
+    w = synth.WORKLOADS[args.workload]
+    print(f"[bench] {w.name}: inputs", file=sys.stderr, flush=True)
+    case, host = make_case(w, torch, coda)
+    print(f"[bench] {w.name}: timing {args.steps} steps", file=sys.stderr, flush=True)
+    res = run_case(case, torch, coda, args.steps, args.warmup, unfused)
+    main_sum = summary(case, res)
+    kernels = res["kernels"]
+    rf = roofline(kernels, res["ms_per_step"])
+    del case
+    torch.cuda.empty_cache()
+
+    also = {}
+    if not args.no_also:
+        for name in ("llama70b_fwdbwd", "swiglu_fwdbwd"):
+            w2 = synth.WORKLOADS[name]
+            print(f"[bench] {name}: inputs + timing", file=sys.stderr, flush=True)
+            c2, _ = make_case(w2, torch, coda)
+            r2 = run_case(c2, torch, coda, max(3, args.steps // 2), max(1, args.warmup // 2), unfused)
+            also[name] = {**summary(c2, r2), "kernels": r2["kernels"]}
+            del c2
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, host, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": main_sum["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_sum["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal inputs of the LLaMA-7B block shape)",
+        "config": {"workload": w.name, "M": w.M, "K": w.K, "d": w.d, "N": w.N, "eps": w.eps,
+                   "step": "coda_fwd + coda_bwd", "parallelism": "single GPU"},
+        "pct_bf16_peak": main_sum["pct_bf16_peak"],
+        "speedup_vs_unfused": main_sum.get("speedup_vs_unfused"),
+        "unfused_ms_per_step": main_sum.get("unfused_ms_per_step"),
+        "unfused_blas": main_sum.get("unfused_blas"),
+        "ms_per_step_untraced": main_sum["ms_per_step_untraced"],
+        "roofline": rf,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "also": also,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,7 +23,8 @@ import os
 __all__ = [
     "CodaError", "lib_path", "load_library", "coda_fwd", "coda_bwd", "coda_swiglu_fwd",
     "coda_swiglu_bwd", "fwd", "bwd", "swiglu_fwd", "swiglu_bwd", "fwd_workspace_bytes",
-    "bwd_workspace_bytes", "swiglu_bwd_workspace_bytes", "version",
+    "bwd_workspace_bytes", "swiglu_bwd_workspace_bytes", "version", "trace_start",
+    "trace_read", "trace_stop",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -79,6 +80,15 @@ def load_library() -> ctypes.CDLL:
     L.coda_swiglu_fwd.argtypes = [i32, i64, i64, i64] + [vp] * 6 + [vp, sz, vp]
     L.coda_swiglu_bwd.restype = i32
     L.coda_swiglu_bwd.argtypes = [i32, i64, i64, i64] + [vp] * 9 + [vp, sz, vp]
+    L.coda_trace_start.restype = i32
+    L.coda_trace_start.argtypes = [i32]
+    L.coda_trace_count.restype = i32
+    L.coda_trace_count.argtypes = []
+    L.coda_trace_get.restype = i32
+    L.coda_trace_get.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
+                                 ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    L.coda_trace_stop.restype = i32
+    L.coda_trace_stop.argtypes = []
     _LIB = L
     return L
 
@@ -139,6 +149,30 @@ def bwd_workspace_bytes(dtype_code, M, K, d, N) -> int:
 
 def swiglu_bwd_workspace_bytes(dtype_code, M, d, F) -> int:
     return int(load_library().coda_swiglu_bwd_workspace_bytes(dtype_code, M, d, F))
+
+
+# ------------------------------------------------------------ tracing
+
+def trace_start(capacity: int) -> None:
+    """Bracket every kernel launch with HIP events (see coda_trace_start)."""
+    _check("coda_trace_start", load_library().coda_trace_start(int(capacity)))
+
+
+def trace_read():
+    """[(kernel name, ms, flops, bytes)] for every launch recorded so far (waits for them)."""
+    L = load_library()
+    out = []
+    name, ms = ctypes.c_char_p(), ctypes.c_float()
+    fl, by = ctypes.c_double(), ctypes.c_double()
+    for i in range(L.coda_trace_count()):
+        _check("coda_trace_get", L.coda_trace_get(i, ctypes.byref(name), ctypes.byref(ms),
+                                                  ctypes.byref(fl), ctypes.byref(by)))
+        out.append((name.value.decode(), float(ms.value), float(fl.value), float(by.value)))
+    return out
+
+
+def trace_stop() -> None:
+    _check("coda_trace_stop", load_library().coda_trace_stop())
 
 
 # ------------------------------------------------------ C-ABI passthroughs

@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "launch.hpp"
 
@@ -50,6 +51,35 @@ bool alias_free(const Range (&in)[NI], const Range (&out)[NO]) {
 }
 
 coda_status hip_status(hipError_t e) { return e == hipSuccess ? CODA_OK : CODA_ERR_HIP; }
+
+// ------------------------------------------------------------- tracing
+struct TraceRec {
+  const char* name;
+  double flops, bytes;
+};
+struct TraceState {
+  bool on = false;
+  int cap = 0, n = 0;
+  std::vector<hipEvent_t> ev;   // two per launch
+  std::vector<TraceRec> rec;
+};
+TraceState g_trace;
+
+// Enqueue one kernel through `f`, bracketed by trace events when tracing is on.
+template <class Fn>
+hipError_t traced(const char* name, double flops, double bytes, hipStream_t s, Fn f) {
+  int i = -1;
+  if (g_trace.on && g_trace.n < g_trace.cap) {
+    i = g_trace.n++;
+    g_trace.rec[i] = {name, flops, bytes};
+    hipEventRecord(g_trace.ev[2 * i], s);
+  }
+  const hipError_t e = f();
+  if (i >= 0) hipEventRecord(g_trace.ev[2 * i + 1], s);
+  return e;
+}
+
+double gemm_flops(int64_t M, int64_t N, int64_t K) { return 2.0 * (double)M * (double)N * (double)K; }
 
 // ------------------------------------------------------------- workspaces
 struct FwdWs {
@@ -155,7 +185,10 @@ coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
   float* P = (float*)(wsb + ws.P);
   void* W2f = wsb + ws.W2f;
   hipError_t err;
-  if ((err = coda::launch_fold_gamma(dtype == CODA_BF16, gamma, W2, W2f, d, N, s)) != hipSuccess)
+  const double eb = (double)e;
+  if ((err = traced("fold_gamma", 0.0, 2.0 * d * N * eb + d * eb, s, [&] {
+         return coda::launch_fold_gamma(dtype == CODA_BF16, gamma, W2, W2f, d, N, s);
+       })) != hipSuccess)
     return hip_status(err);
 
   GemmArgs g1 = gemm(M, d, K, X, K, M * K, W1, d, K * d, y, d);
@@ -165,18 +198,22 @@ coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
   g1.ld_part_row = ws.Tn;
   GemmArgs g2 = gemm(M, N, d, y, d, M * d, W2f, N, d * N, z, N);
   g2.vrow = r;
-  if (dtype == CODA_BF16) {
-    if ((err = coda::launch_gemm_bf16(g1, true, false, coda::EPI_RESID_SUMSQ, s)) != hipSuccess)
-      return hip_status(err);
-    if ((err = coda::launch_row_rsqrt(P, ws.Tn, ws.Tn, M, d, eps, r, s)) != hipSuccess)
-      return hip_status(err);
-    return hip_status(coda::launch_gemm_bf16(g2, true, false, coda::EPI_ROWSCALE, s));
-  }
-  if ((err = coda::launch_gemm_f32(g1, coda::EPI_RESID_SUMSQ, s)) != hipSuccess)
+  const bool bf = dtype == CODA_BF16;
+  const double k1_bytes = (M * K + K * d + 2.0 * M * d) * eb + M * ws.Tn * 4.0;
+  if ((err = traced("k1_gemm_resid_sumsq", gemm_flops(M, d, K), k1_bytes, s, [&] {
+         return bf ? coda::launch_gemm_bf16(g1, true, false, coda::EPI_RESID_SUMSQ, s)
+                   : coda::launch_gemm_f32(g1, coda::EPI_RESID_SUMSQ, s);
+       })) != hipSuccess)
     return hip_status(err);
-  if ((err = coda::launch_row_rsqrt(P, ws.Tn, ws.Tn, M, d, eps, r, s)) != hipSuccess)
+  if ((err = traced("r1_row_rsqrt", 0.0, M * ws.Tn * 4.0 + M * 4.0, s, [&] {
+         return coda::launch_row_rsqrt(P, ws.Tn, ws.Tn, M, d, eps, r, s);
+       })) != hipSuccess)
     return hip_status(err);
-  return hip_status(coda::launch_gemm_f32(g2, coda::EPI_ROWSCALE, s));
+  const double k2_bytes = (M * d + d * N + M * N) * eb + M * 4.0;
+  return hip_status(traced("k2_gemm_rowscale", gemm_flops(M, N, d), k2_bytes, s, [&] {
+    return bf ? coda::launch_gemm_bf16(g2, true, false, coda::EPI_ROWSCALE, s)
+              : coda::launch_gemm_f32(g2, coda::EPI_ROWSCALE, s);
+  }));
 }
 
 size_t coda_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N) {
@@ -231,26 +268,41 @@ coda_status coda_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
   b1.ld_part_row = ws.Tn;
   b1.part_col = G;
   b1.ld_part_col = d;
-  if ((err = coda::launch_gemm_bf16(b1, true, true, coda::EPI_DN, s)) != hipSuccess)
-    return hip_status(err);
-  // R2: c = r^3 s / d, dgamma
-  if ((err = coda::launch_bwd_reduce(S, ws.Tn, ws.Tn, r, M, d, G, ws.Tm, c, dgamma, s)) !=
+  const double md = 2.0 * M * d, dn2 = 2.0 * d * N, mn = 2.0 * M * N, mk = 2.0 * M * K, kd = 2.0 * K * d;
+  if ((err = traced("b1_gemm_dh_epilogue", gemm_flops(M, d, N),
+                    mn + dn2 + 2.0 * md + M * ws.Tn * 4.0 + ws.Tm * d * 4.0 + M * 4.0 + 2.0 * d, s,
+                    [&] { return coda::launch_gemm_bf16(b1, true, true, coda::EPI_DN, s); })) !=
       hipSuccess)
     return hip_status(err);
+  // R2: c = r^3 s / d, dgamma
+  if ((err = traced("r2_bwd_reduce", 0.0, M * ws.Tn * 4.0 + ws.Tm * d * 4.0 + 8.0 * M + 4.0 * d, s,
+                    [&] {
+                      return coda::launch_bwd_reduce(S, ws.Tn, ws.Tn, r, M, d, G, ws.Tm, c, dgamma,
+                                                     s);
+                    })) != hipSuccess)
+    return hip_status(err);
   // E2: dR = r dn - c y (in place), n = r y
-  if ((err = coda::launch_dy_n(dR, n, y, r, c, M, d, s)) != hipSuccess) return hip_status(err);
+  if ((err = traced("e2_dy_n", 0.0, 4.0 * md + 8.0 * M, s,
+                    [&] { return coda::launch_dy_n(dR, n, y, r, c, M, d, s); })) != hipSuccess)
+    return hip_status(err);
   // B2: dW2 = diag(gamma) n^T dz
   GemmArgs b2 = gemm(d, N, M, n, d, M * d, dz, N, M * N, dW2, N);
   b2.vcol = gamma;
-  if ((err = coda::launch_gemm_bf16(b2, false, false, coda::EPI_ROWSCALE, s)) != hipSuccess)
+  if ((err = traced("b2_gemm_dW2", gemm_flops(d, N, M), md + mn + dn2 + 2.0 * d, s, [&] {
+         return coda::launch_gemm_bf16(b2, false, false, coda::EPI_ROWSCALE, s);
+       })) != hipSuccess)
     return hip_status(err);
   // B3: dX = dy W1^T
   GemmArgs b3 = gemm(M, K, d, dR, d, M * d, W1, d, K * d, dX, K);
-  if ((err = coda::launch_gemm_bf16(b3, true, true, coda::EPI_STORE, s)) != hipSuccess)
+  if ((err = traced("b3_gemm_dX", gemm_flops(M, K, d), md + kd + mk, s, [&] {
+         return coda::launch_gemm_bf16(b3, true, true, coda::EPI_STORE, s);
+       })) != hipSuccess)
     return hip_status(err);
   // B4: dW1 = X^T dy
   GemmArgs b4 = gemm(K, d, M, X, K, M * K, dR, d, M * d, dW1, d);
-  return hip_status(coda::launch_gemm_bf16(b4, false, false, coda::EPI_STORE, s));
+  return hip_status(traced("b4_gemm_dW1", gemm_flops(K, d, M), mk + md + kd, s, [&] {
+    return coda::launch_gemm_bf16(b4, false, false, coda::EPI_STORE, s);
+  }));
 }
 
 size_t coda_swiglu_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t d, int64_t F) {
@@ -286,10 +338,15 @@ coda_status coda_swiglu_fwd(coda_dtype dtype, int64_t M, int64_t d, int64_t F, c
   s1.C2 = a;
   s1.ldc2 = F;
   s1.F = (int)F;
-  if ((err = coda::launch_gemm_bf16(s1, true, false, coda::EPI_SWIGLU, s)) != hipSuccess)
+  const double Md = 2.0 * M * d, dF2 = 4.0 * d * F, MF = 2.0 * M * F, Fd = 2.0 * F * d;
+  if ((err = traced("s1_gemm_gateup_swiglu", gemm_flops(M, 2 * F, d), Md + dF2 + 3.0 * MF, s, [&] {
+         return coda::launch_gemm_bf16(s1, true, false, coda::EPI_SWIGLU, s);
+       })) != hipSuccess)
     return hip_status(err);
   GemmArgs s2 = gemm(M, d, F, a, F, M * F, Wd, d, F * d, z, d);
-  return hip_status(coda::launch_gemm_bf16(s2, true, false, coda::EPI_STORE, s));
+  return hip_status(traced("s2_gemm_down", gemm_flops(M, d, F), MF + Fd + Md, s, [&] {
+    return coda::launch_gemm_bf16(s2, true, false, coda::EPI_STORE, s);
+  }));
 }
 
 size_t coda_swiglu_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t d, int64_t F) {
@@ -329,19 +386,71 @@ coda_status coda_swiglu_bwd(coda_dtype dtype, int64_t M, int64_t d, int64_t F, c
   s3.E = gu;
   s3.lde = 2 * F;
   s3.F = (int)F;
-  if ((err = coda::launch_gemm_bf16(s3, true, true, coda::EPI_SWIGLU_BWD, s)) != hipSuccess)
+  const double Md = 2.0 * M * d, dF2 = 4.0 * d * F, MF = 2.0 * M * F, Fd = 2.0 * F * d;
+  if ((err = traced("s3_gemm_da_swiglu_bwd", gemm_flops(M, F, d), Md + Fd + 4.0 * MF, s, [&] {
+         return coda::launch_gemm_bf16(s3, true, true, coda::EPI_SWIGLU_BWD, s);
+       })) != hipSuccess)
     return hip_status(err);
   // S4: dWd = a^T dz
   GemmArgs s4 = gemm(F, d, M, a, F, M * F, dz, d, M * d, dWd, d);
-  if ((err = coda::launch_gemm_bf16(s4, false, false, coda::EPI_STORE, s)) != hipSuccess)
+  if ((err = traced("s4_gemm_dWd", gemm_flops(F, d, M), MF + Md + Fd, s, [&] {
+         return coda::launch_gemm_bf16(s4, false, false, coda::EPI_STORE, s);
+       })) != hipSuccess)
     return hip_status(err);
   // S5: dX = dgu W^T
   GemmArgs s5 = gemm(M, d, 2 * F, dgu, 2 * F, M * 2 * F, W, 2 * F, d * 2 * F, dX, d);
-  if ((err = coda::launch_gemm_bf16(s5, true, true, coda::EPI_STORE, s)) != hipSuccess)
+  if ((err = traced("s5_gemm_dX", gemm_flops(M, d, 2 * F), 2.0 * MF + dF2 + Md, s, [&] {
+         return coda::launch_gemm_bf16(s5, true, true, coda::EPI_STORE, s);
+       })) != hipSuccess)
     return hip_status(err);
   // S6: dW = X^T dgu
   GemmArgs s6 = gemm(d, 2 * F, M, X, d, M * d, dgu, 2 * F, M * 2 * F, dW, 2 * F);
-  return hip_status(coda::launch_gemm_bf16(s6, false, false, coda::EPI_STORE, s));
+  return hip_status(traced("s6_gemm_dW", gemm_flops(d, 2 * F, M), Md + 2.0 * MF + dF2, s, [&] {
+    return coda::launch_gemm_bf16(s6, false, false, coda::EPI_STORE, s);
+  }));
+}
+
+coda_status coda_trace_start(int capacity) {
+  if (capacity < 1 || capacity > (1 << 20)) return CODA_ERR_SHAPE;
+  coda_trace_stop();
+  g_trace.ev.assign(2 * (size_t)capacity, nullptr);
+  for (auto& e : g_trace.ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      coda_trace_stop();
+      return CODA_ERR_HIP;
+    }
+  }
+  g_trace.rec.assign(capacity, TraceRec{nullptr, 0.0, 0.0});
+  g_trace.cap = capacity;
+  g_trace.n = 0;
+  g_trace.on = true;
+  return CODA_OK;
+}
+
+int coda_trace_count(void) { return g_trace.n; }
+
+coda_status coda_trace_get(int index, const char** name, float* ms, double* flops, double* bytes) {
+  if (index < 0 || index >= g_trace.n) return CODA_ERR_SHAPE;
+  if (!name || !ms || !flops || !bytes) return CODA_ERR_NULL;
+  if (hipEventSynchronize(g_trace.ev[2 * index + 1]) != hipSuccess) return CODA_ERR_HIP;
+  if (hipEventElapsedTime(ms, g_trace.ev[2 * index], g_trace.ev[2 * index + 1]) != hipSuccess)
+    return CODA_ERR_HIP;
+  *name = g_trace.rec[index].name;
+  *flops = g_trace.rec[index].flops;
+  *bytes = g_trace.rec[index].bytes;
+  return CODA_OK;
+}
+
+coda_status coda_trace_stop(void) {
+  coda_status st = CODA_OK;
+  for (auto& e : g_trace.ev)
+    if (e && hipEventDestroy(e) != hipSuccess) st = CODA_ERR_HIP;
+  g_trace.ev.clear();
+  g_trace.rec.clear();
+  g_trace.cap = g_trace.n = 0;
+  g_trace.on = false;
+  return st;
 }
 
 }  // extern "C"

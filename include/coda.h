@@ -15,7 +15,8 @@
  * argument; a weight is stored [in, out].  Every pointer is a DEVICE pointer
  * (HIP device memory of the current device) unless it is marked host.  The
  * caller owns every buffer, including the workspace; the library allocates
- * no device memory and keeps no state between calls, so calls are reentrant.
+ * no device memory and keeps no state between calls (apart from the optional
+ * kernel tracing at the end of this header), so calls are reentrant.
  *
  * Element types: `dtype` is the type of every tensor argument except r,
  * dgamma and the workspace: CODA_BF16 (bfloat16, 2 bytes) or CODA_F32.
@@ -161,6 +162,27 @@ coda_status coda_swiglu_bwd(coda_dtype dtype, int64_t M, int64_t d, int64_t F,
                             const void* gu, const void* a, const void* dz,
                             void* dX, void* dW, void* dWd,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Kernel tracing (measurement aid; off by default).
+ *
+ * coda_trace_start(capacity) creates 2*capacity timing events (host call,
+ * allocates; do it before the region to be measured).  While tracing is on,
+ * every kernel the entry points above enqueue is bracketed by two of those
+ * events on the same stream, together with the kernel's name and its
+ * algorithmic work: GEMM flops (2*M*N*K) and the minimum HBM bytes the
+ * kernel must move.  Launches beyond `capacity` are not recorded.
+ * coda_trace_count() = launches recorded; coda_trace_get(i, ...) waits for
+ * launch i's events and returns its name (static string), elapsed
+ * milliseconds, flops and bytes.  coda_trace_stop() destroys the events.
+ * Tracing state is process-global and not thread-safe: while it is on, one
+ * host thread at a time may call the library.  Returns CODA_ERR_HIP if an
+ * event call fails, CODA_ERR_SHAPE for a bad capacity or index.
+ * ---------------------------------------------------------------------- */
+coda_status coda_trace_start(int capacity);
+int coda_trace_count(void);
+coda_status coda_trace_get(int index, const char** name, float* ms, double* flops, double* bytes);
+coda_status coda_trace_stop(void);
 
 #ifdef __cplusplus
 }

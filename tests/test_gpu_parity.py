@@ -169,7 +169,8 @@ def test_zero_rows_and_determinism(torch_dev):
 def test_numerics_no_worse_than_unfused_torch(torch_dev):
     """The pages report the rewritten form's error as comparable to the
     unfused PyTorch reference and sometimes smaller, thanks to the fp32
-    main-loop accumulator (toolin.ai 実験結果 / kucoin.com results sections).
+    main-loop accumulator (kucoin.com ru/fr news flashes, results sections
+    "Результаты эксперимента" / "Résultats de l'expérience").
     Check: error(fused) <= 1.5 x error(unfused torch bf16), both against the
     oracle."""
     torch, dev = torch_dev
