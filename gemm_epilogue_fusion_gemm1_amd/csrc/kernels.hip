@@ -12,11 +12,13 @@
 //  * one bf16 MFMA main loop (v_mfma_f32_32x32x16_bf16, fp32 accumulators),
 //    256x256 output tile per 256-thread workgroup, 4 waves of 128x128, K
 //    step 64, LDS double buffered;
-//  * operands of either layout (contraction index contiguous or not) are
-//    staged into one LDS format, "k-octet planes": plane q holds, for every
-//    row m of the tile, the 8 consecutive k values 8q..8q+7 as one 16-byte
-//    slot, with one pad slot per 8 rows so that 8 lanes reading 8 rows, or
-//    writing 8 octets of one row, hit 8 different bank groups;
+//  * operand tiles are staged in LDS in the layout they have in memory,
+//    with 16-byte chunks XOR-swizzled so that every LDS access of the loop
+//    is free of bank conflicts on gfx950's 64-bank LDS (16 lanes x 16 bytes
+//    per cycle).  A tile whose contraction index is contiguous is read as
+//    MFMA fragments with ds_read_b128; a tile whose MN index is contiguous is
+//    read with two ds_read_b64_tr_b16 (transpose reads) per fragment, so no
+//    operand is ever transposed in registers;
 //  * epilogues selected at compile time (launch.hpp: Epi) work on the
 //    accumulator registers in place: residual add + per-tile partial sums of
 //    squares, row scale, the RMSNorm-backward epilogue, SwiGLU and its
@@ -38,15 +40,25 @@ constexpr int BM = kTileM;
 constexpr int BN = kTileN;
 constexpr int BK = 64;
 constexpr int NT = 256;
-constexpr int PLANE = (BM + BM / 8) * 16 + 16;   // 4624 B; == 16 (mod 128)
-constexpr int OPER_BYTES = (BK / 8) * PLANE;     // one operand tile
+constexpr int OPER_BYTES = BM * BK * 2;         // one operand tile, 32 KiB, unpadded
 constexpr int STAGE_BYTES = 2 * OPER_BYTES;      // A + B
 constexpr int LDS_BYTES = 2 * STAGE_BYTES;       // two stages
 constexpr uint32_t OOB = 0x80000000u;            // voffset past every extent -> loads 0
 static_assert(BM == BN, "operand tiles share one LDS geometry");
 static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
 
-__device__ __forceinline__ int slot16(int m) { return (m + (m >> 3)) * 16; }
+// LDS tile layouts (256 MN x 64 K, bf16):
+//  K-contiguous:  row m (128 B) at m*128; its 16-byte k chunk q (k = 8q..8q+7)
+//                 sits at chunk position q ^ ((m >> 1) & 7).  16 lanes that
+//                 read chunk q of rows m..m+15 (m % 16 == 0) hit 16 distinct
+//                 16-byte bank groups; 16 lanes that write 8 chunks of 2 rows
+//                 fill 256 contiguous bytes.
+//  MN-contiguous: row k (512 B) at k*512; its 16-byte MN chunk c (mn =
+//                 8c..8c+7) sits at chunk position c ^ ((k & 3) << 2).  A
+//                 transpose read touches 4 rows x 4 chunks per 32 lanes, which
+//                 the swizzle spreads over all 16 bank groups.
+__device__ __forceinline__ int kmaj_off(int m, int q) { return m * 128 + ((q ^ ((m >> 1) & 7)) << 4); }
+__device__ __forceinline__ int mnmaj_off(int k, int c) { return k * 512 + ((c ^ ((k & 3) << 2)) << 4); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   // raw buffer: stride 0, num_records in bytes; dword3 0x00020000 = 32-bit data format
@@ -84,9 +96,10 @@ __device__ __forceinline__ void map_tile(int wg, int tiles_m, int tiles_n, int& 
 // LDS k-octet planes.
 // ---------------------------------------------------------------------------
 
-// Contraction index contiguous: rows of the tile are MN, 64 k per row.
-// Thread t loads row p*32 + t/8 (p = 0..7), k chunk t%8: one 16-byte octet
-// per load, stored unchanged into plane t%8.
+// Contraction index contiguous: the matrix is [MN rows][K].  Thread t loads
+// row p*32 + t/8 (p = 0..7), k chunk t%8, one 16-byte load each.  Loads past K
+// or past the last row get an out-of-range offset and read zeros, so the loop
+// needs no branch.
 struct LoaderKMajor {
   __amdgpu_buffer_rsrc_t rs;
   uint32_t base;      // byte offset of (row0 + t/8, 8*(t%8))
@@ -94,10 +107,10 @@ struct LoaderKMajor {
   uint32_t rowmask;   // bit p: row p*32 + t/8 is inside the matrix
   int kchunk;         // 8*(t%8)
   int K;
-  int lds_off[8];
+  int lds0;           // LDS offset of load p = 0; load p adds p * 32 rows * 128 B
 
   __device__ void init(const void* ptr, uint32_t bytes, int64_t ld, int row0, int rows, int K_,
-                       int t) {
+                       int t, int, int) {
     rs = make_rsrc(ptr, bytes);
     const int r = t >> 3, c = t & 7;
     kchunk = c * 8;
@@ -107,10 +120,9 @@ struct LoaderKMajor {
     pstride = 32u * ldb;
     rowmask = 0;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < 8; ++p)
       if (row0 + p * 32 + r < rows) rowmask |= 1u << p;
-      lds_off[p] = c * PLANE + slot16(p * 32 + r);
-    }
+    lds0 = kmaj_off(r, c);          // (r + 32p) >> 1 & 7 == r >> 1 & 7
   }
   __device__ void load(int k0, u32x4 (&v)[8]) const {
     const bool kok = (k0 + kchunk) < K;
@@ -123,32 +135,31 @@ struct LoaderKMajor {
   }
   __device__ void store(char* lds, const u32x4 (&v)[8]) const {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) *(u32x4*)(lds + lds_off[p]) = v[p];
+    for (int p = 0; p < 8; ++p) *(u32x4*)(lds + lds0 + p * 4096) = v[p];
   }
 };
 
-// Contraction index strided: the matrix is [K rows][MN cols].  Thread t owns
-// octet q = t/32 and MN chunk c = t%32: it loads the 8 k rows 8q..8q+7 of the
-// 8 columns 8c..8c+7, transposes the 8x8 block in registers, and stores one
-// octet per column.  GATED maps tile columns onto the [gate | up] halves of
-// a [d, 2F] weight: within each 128-column half of the tile, the first 64
-// columns are gate columns j and the next 64 the up columns F + j of the
-// same j, so one lane ends up holding a gate and its up value.
+// Contraction index strided: the matrix is [K rows][MN cols].  Thread t loads
+// MN chunk t%32 (8 columns) of the k rows t/32 + 8p (p = 0..7); each 16-byte
+// load is stored unchanged.  GATED maps tile columns onto the [gate | up]
+// halves of a [d, 2F] weight: within each 128-column half of the tile, the
+// first 64 columns are gate columns j and the next 64 the up columns F + j of
+// the same j, so one lane ends up holding a gate and its up value.
 template <bool GATED>
 struct LoaderMNMajor {
   __amdgpu_buffer_rsrc_t rs;
-  uint32_t base;      // byte offset of (k = 8q, col)
+  uint32_t base;      // byte offset of (k = t/32, col)
   uint32_t ldb;       // row pitch in bytes
-  int krow;           // 8q
+  int krow;           // t/32
   int K;
   bool colok;
-  int lds_off;
+  int lds0;
 
   __device__ void init(const void* ptr, uint32_t bytes, int64_t ld, int col0, int cols, int K_,
                        int t, int F, int tn) {
     rs = make_rsrc(ptr, bytes);
     const int q = t >> 5, c = t & 31;
-    krow = q * 8;
+    krow = q;
     K = K_;
     ldb = (uint32_t)(ld * 2);
     int col;
@@ -163,30 +174,19 @@ struct LoaderMNMajor {
       colok = col < cols;
     }
     base = (uint32_t)krow * ldb + (uint32_t)col * 2u;
-    lds_off = q * PLANE + slot16(c * 8);
+    lds0 = mnmaj_off(q, c);         // (q + 8p) & 3 == q & 3
   }
   __device__ void load(int k0, u32x4 (&v)[8]) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool ok = colok && (k0 + krow + i) < K;
-      const uint32_t off = ok ? base + (uint32_t)(k0 + i) * ldb : OOB;
-      v[i] = bload16(rs, off);
+    for (int p = 0; p < 8; ++p) {
+      const bool ok = colok && (k0 + krow + 8 * p) < K;
+      const uint32_t off = ok ? base + (uint32_t)(k0 + 8 * p) * ldb : OOB;
+      v[p] = bload16(rs, off);
     }
   }
   __device__ void store(char* lds, const u32x4 (&v)[8]) const {
-    // v[i] holds row k = 8q+i, columns 8c..8c+7 (two per dword).  Output
-    // octet m holds column 8c+m, rows 8q..8q+7 (two per dword).
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      u32x4 o;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t lo = v[2 * w][m >> 1], hi = v[2 * w + 1][m >> 1];
-        o[w] = (m & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-      }
-      // column 8c+m sits in slot 8c+m+c, i.e. (8c+m)+((8c+m)>>3) for m < 8
-      *(u32x4*)(lds + lds_off + m * 16) = o;
-    }
+    for (int p = 0; p < 8; ++p) *(u32x4*)(lds + lds0 + p * 4096) = v[p];
   }
 };
 
@@ -196,6 +196,56 @@ template <bool GATED>
 struct LoaderSel<true, GATED> { using type = LoaderKMajor; };
 template <bool GATED>
 struct LoaderSel<false, GATED> { using type = LoaderMNMajor<GATED>; };
+
+// MFMA operand fragments of v_mfma_f32_32x32x16_bf16: lane l supplies row
+// (or column) l%32 of a 32-wide block and the 8 k values 16s + 8(l/32) + 0..7
+// of sub-step s.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <bool KMAJ>
+struct FragReader;
+
+// K-contiguous tile: one ds_read_b128 per fragment.
+template <>
+struct FragReader<true> {
+  int off[4];   // per sub-step s, for block 0; block i adds i * 32 rows * 128 B
+  __device__ void init(int mn0, int lane) {
+    const int l32 = lane & 31, khalf = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) off[s] = kmaj_off(mn0 + l32, 2 * s + khalf);
+  }
+  __device__ bf16x8 read(const char* tile, int s, int i) const {
+    return *(const bf16x8*)(tile + off[s] + i * 4096);
+  }
+};
+
+// MN-contiguous tile: two transpose reads per fragment.  Within a 16-lane
+// group, ds_read_b64_tr_b16 hands output lane i element i%4 of the 8 bytes
+// addressed by source lanes 4k + i/4 (k = 0..3).  Source lane j points at
+// (k row K0 + j/4, columns c0 + 4(j%4)..+3), so output lane i receives
+// column c0 + i at rows K0..K0+3.
+template <>
+struct FragReader<false> {
+  int off[4];   // per block i (32 columns); sub-step s and half h add rows
+  __device__ void init(int mn0, int lane) {
+    const int j = lane & 15, khalf = lane >> 5;
+    const int krow = 8 * khalf + (j >> 2);                  // + 16 s + 4 h
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int mn = mn0 + i * 32 + (lane & 16) + 4 * (j & 3);
+      off[i] = mnmaj_off(krow, mn >> 3) + ((mn & 7) << 1);  // (krow + 16s + 4h) & 3 == krow & 3
+    }
+  }
+  __device__ bf16x8 read(const char* tile, int s, int i) const {
+    const char* p = tile + off[i] + s * 16 * 512;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 512));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Epilogue helpers
@@ -267,10 +317,8 @@ gemm_bf16_kernel(GemmArgs g) {
 
   typename LoaderSel<AK, false>::type la;
   typename LoaderSel<BKM, GATED>::type lb;
-  if constexpr (AK) la.init(g.A, g.A_bytes, g.lda, row0, g.M, g.K, t);
-  else la.init(g.A, g.A_bytes, g.lda, row0, g.M, g.K, t, 0, tm);
-  if constexpr (BKM) lb.init(g.B, g.B_bytes, g.ldb, col0, g.N, g.K, t);
-  else lb.init(g.B, g.B_bytes, g.ldb, col0, g.N, g.K, t, g.F, tn);
+  la.init(g.A, g.A_bytes, g.lda, row0, g.M, g.K, t, 0, tm);
+  lb.init(g.B, g.B_bytes, g.ldb, col0, g.N, g.K, t, g.F, tn);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -278,46 +326,68 @@ gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
+  // Software pipeline (one K step = four 16-wide MFMA sub-steps):
+  //   s0, s1: MFMAs; the fragments of the next sub-step are read meanwhile
+  //   s2:     the next tile, already in registers, is written to the free
+  //           LDS stage; the global loads two steps ahead are issued into
+  //           the same registers (a full K step of latency cover)
+  //   s3:     barrier, then the next stage's first fragments are read while
+  //           the last 16 MFMAs of this step run.
+  // Fragments are double-buffered in registers.  Loads past K read zeros,
+  // so the loop has no branches.
   const int nk = (g.K + BK - 1) / BK;
+  const int l32 = lane & 31;
+  FragReader<AK> fra;
+  FragReader<BKM> frb;
+  fra.init(wm * 128, lane);
+  frb.init(wn * 128, lane);
   u32x4 ra[8], rb[8];
+  bf16x8 fa[2][4], fb[2][4];
+
+  auto read_frags = [&](const char* stage, int s, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = fra.read(stage, s, i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = frb.read(stage + OPER_BYTES, s, j);
+  };
+  auto mfma16 = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+
   la.load(0, ra);
   lb.load(0, rb);
   la.store(smem, ra);
   lb.store(smem + OPER_BYTES, rb);
+  la.load(BK, ra);
+  lb.load(BK, rb);
   __syncthreads();
-
-  const int l32 = lane & 31, khalf = lane >> 5;
+  read_frags(smem, 0, fa[0], fb[0]);
+  int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load((kt + 1) * BK, ra);
-      lb.load((kt + 1) * BK, rb);
-    }
-    const char* sa = smem + cur * STAGE_BYTES;
-    const char* sb = sa + OPER_BYTES;
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int q = 2 * s + khalf;
-      bf16x8 fa[4], fb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = *(const bf16x8*)(sa + q * PLANE + slot16(wm * 128 + i * 32 + l32));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        fb[j] = *(const bf16x8*)(sb + q * PLANE + slot16(wn * 128 + j * 32 + l32));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      char* nxt = smem + (cur ^ 1) * STAGE_BYTES;
-      la.store(nxt, ra);
-      lb.store(nxt + OPER_BYTES, rb);
-    }
+    const char* sc = smem + cur * STAGE_BYTES;
+    char* sn = smem + (cur ^ 1) * STAGE_BYTES;
+    read_frags(sc, 1, fa[1], fb[1]);
+    mfma16(fa[0], fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(sc, 2, fa[0], fb[0]);
+    mfma16(fa[1], fb[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(sc, 3, fa[1], fb[1]);
+    la.store(sn, ra);
+    lb.store(sn + OPER_BYTES, rb);
+    la.load((kt + 2) * BK, ra);
+    lb.load((kt + 2) * BK, rb);
+    mfma16(fa[0], fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+    read_frags(sn, 0, fa[0], fb[0]);
+    mfma16(fa[1], fb[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    cur ^= 1;
   }
 
   // ------------------------------ epilogue ------------------------------
