@@ -39,7 +39,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int BM = kTileM;
 constexpr int BN = kTileN;
 constexpr int BK = 64;
-constexpr int NT = 256;
 constexpr int OPER_BYTES = BM * BK * 2;         // one operand tile, 32 KiB, unpadded
 constexpr int STAGE_BYTES = 2 * OPER_BYTES;      // A + B
 constexpr int LDS_BYTES = 2 * STAGE_BYTES;       // two stages
@@ -92,22 +91,42 @@ __device__ __forceinline__ void map_tile(int wg, int tiles_m, int tiles_n, int& 
 }
 
 // ---------------------------------------------------------------------------
+// Workgroup shape.  A GEMM workgroup computes a BM x BN output tile with a
+// WM x WN grid of waves; each wave owns a TM x TN sub-tile made of FM x FN
+// 32x32 MFMA blocks.  With 8 waves (2 x 4) two waves share each SIMD, so one
+// wave's waits (LDS, global loads, the per-step barrier) are covered by the
+// other wave's MFMAs.
+// ---------------------------------------------------------------------------
+template <int WM_, int WN_>
+struct Grid {
+  static constexpr int WM = WM_, WN = WN_, NT = 64 * WM_ * WN_;
+  static constexpr int TM = BM / WM_, TN = BN / WN_;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int LP = BM * BK / 8 / NT;     // 16-byte loads per thread per operand
+  static_assert(FM >= 1 && FN >= 1 && LP >= 1, "tile too small for the wave grid");
+};
+
+// ---------------------------------------------------------------------------
 // Operand staging: global -> registers (buffer loads, out-of-range -> 0) ->
-// LDS k-octet planes.
+// LDS.  Each 16-byte load is stored unchanged; only its chunk position is
+// swizzled.
 // ---------------------------------------------------------------------------
 
-// Contraction index contiguous: the matrix is [MN rows][K].  Thread t loads
-// row p*32 + t/8 (p = 0..7), k chunk t%8, one 16-byte load each.  Loads past K
-// or past the last row get an out-of-range offset and read zeros, so the loop
-// needs no branch.
+// Contraction index contiguous: the matrix is [MN rows][K].  Thread t loads k
+// chunk t%8 of rows t/8 + p*(NT/8), p < LP.  Loads past K or past the last
+// row get an out-of-range offset and read zeros, so the loop needs no branch.
+template <int NT, bool GATED>
 struct LoaderKMajor {
+  static constexpr int LP = BM * BK / 8 / NT;
+  static constexpr int RSTEP = NT / 8;            // rows between a thread's loads
+  static_assert(RSTEP % 16 == 0, "swizzle period");
   __amdgpu_buffer_rsrc_t rs;
   uint32_t base;      // byte offset of (row0 + t/8, 8*(t%8))
-  uint32_t pstride;   // 32 rows in bytes
-  uint32_t rowmask;   // bit p: row p*32 + t/8 is inside the matrix
+  uint32_t pstride;   // RSTEP rows in bytes
+  uint32_t rowmask;   // bit p: load p's row is inside the matrix
   int kchunk;         // 8*(t%8)
   int K;
-  int lds0;           // LDS offset of load p = 0; load p adds p * 32 rows * 128 B
+  int lds0;
 
   __device__ void init(const void* ptr, uint32_t bytes, int64_t ld, int row0, int rows, int K_,
                        int t, int, int) {
@@ -117,36 +136,39 @@ struct LoaderKMajor {
     K = K_;
     const uint32_t ldb = (uint32_t)(ld * 2);
     base = (uint32_t)(row0 + r) * ldb + (uint32_t)(kchunk * 2);
-    pstride = 32u * ldb;
+    pstride = (uint32_t)RSTEP * ldb;
     rowmask = 0;
 #pragma unroll
-    for (int p = 0; p < 8; ++p)
-      if (row0 + p * 32 + r < rows) rowmask |= 1u << p;
-    lds0 = kmaj_off(r, c);          // (r + 32p) >> 1 & 7 == r >> 1 & 7
+    for (int p = 0; p < LP; ++p)
+      if (row0 + p * RSTEP + r < rows) rowmask |= 1u << p;
+    lds0 = kmaj_off(r, c);          // (r + p RSTEP) >> 1 & 7 == r >> 1 & 7
   }
-  __device__ void load(int k0, u32x4 (&v)[8]) const {
+  __device__ void load(int k0, u32x4 (&v)[LP]) const {
     const bool kok = (k0 + kchunk) < K;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < LP; ++p) {
       const bool ok = kok && ((rowmask >> p) & 1u);
       const uint32_t off = ok ? base + p * pstride + (uint32_t)(k0 * 2) : OOB;
       v[p] = bload16(rs, off);
     }
   }
-  __device__ void store(char* lds, const u32x4 (&v)[8]) const {
+  __device__ void store(char* lds, const u32x4 (&v)[LP]) const {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) *(u32x4*)(lds + lds0 + p * 4096) = v[p];
+    for (int p = 0; p < LP; ++p) *(u32x4*)(lds + lds0 + p * RSTEP * 128) = v[p];
   }
 };
 
 // Contraction index strided: the matrix is [K rows][MN cols].  Thread t loads
-// MN chunk t%32 (8 columns) of the k rows t/32 + 8p (p = 0..7); each 16-byte
-// load is stored unchanged.  GATED maps tile columns onto the [gate | up]
-// halves of a [d, 2F] weight: within each 128-column half of the tile, the
-// first 64 columns are gate columns j and the next 64 the up columns F + j of
-// the same j, so one lane ends up holding a gate and its up value.
-template <bool GATED>
+// MN chunk t%32 (8 columns) of the k rows t/32 + p*(NT/32), p < LP.  GATED
+// maps tile columns onto the [gate | up] halves of a [d, 2F] weight: the tile
+// is cut into groups of TN columns (one wave's width) whose first half holds
+// gate columns j and second half the up columns F + j of the same j, so one
+// lane ends up holding a gate and its up value.
+template <int NT, bool GATED, int TN = 64>
 struct LoaderMNMajor {
+  static constexpr int LP = BM * BK / 8 / NT;
+  static constexpr int KSTEP = NT / 32;           // k rows between a thread's loads
+  static_assert(KSTEP % 4 == 0, "swizzle period");
   __amdgpu_buffer_rsrc_t rs;
   uint32_t base;      // byte offset of (k = t/32, col)
   uint32_t ldb;       // row pitch in bytes
@@ -164,52 +186,54 @@ struct LoaderMNMajor {
     ldb = (uint32_t)(ld * 2);
     int col;
     if (GATED) {
+      constexpr int GH = TN / 2;
       const int lc = c * 8;                       // tile column 0..255
-      const int half = lc >> 7, sub = lc & 127;
-      const int j = tn * 128 + half * 64 + (sub & 63);
+      const int grp = lc / TN, sub = lc % TN;
+      const int j = tn * (BN / 2) + grp * GH + (sub % GH);
       colok = j < F;
-      col = (sub < 64) ? j : F + j;
+      col = (sub < GH) ? j : F + j;
     } else {
       col = col0 + c * 8;
       colok = col < cols;
     }
     base = (uint32_t)krow * ldb + (uint32_t)col * 2u;
-    lds0 = mnmaj_off(q, c);         // (q + 8p) & 3 == q & 3
+    lds0 = mnmaj_off(q, c);         // (q + p KSTEP) & 3 == q & 3
   }
-  __device__ void load(int k0, u32x4 (&v)[8]) const {
+  __device__ void load(int k0, u32x4 (&v)[LP]) const {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const bool ok = colok && (k0 + krow + 8 * p) < K;
-      const uint32_t off = ok ? base + (uint32_t)(k0 + 8 * p) * ldb : OOB;
+    for (int p = 0; p < LP; ++p) {
+      const bool ok = colok && (k0 + krow + KSTEP * p) < K;
+      const uint32_t off = ok ? base + (uint32_t)(k0 + KSTEP * p) * ldb : OOB;
       v[p] = bload16(rs, off);
     }
   }
-  __device__ void store(char* lds, const u32x4 (&v)[8]) const {
+  __device__ void store(char* lds, const u32x4 (&v)[LP]) const {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) *(u32x4*)(lds + lds0 + p * 4096) = v[p];
+    for (int p = 0; p < LP; ++p) *(u32x4*)(lds + lds0 + p * KSTEP * 512) = v[p];
   }
 };
 
-template <bool KMAJ, bool GATED>
+template <bool KMAJ, int NT, bool GATED, int TN>
 struct LoaderSel;
-template <bool GATED>
-struct LoaderSel<true, GATED> { using type = LoaderKMajor; };
-template <bool GATED>
-struct LoaderSel<false, GATED> { using type = LoaderMNMajor<GATED>; };
+template <int NT, bool GATED, int TN>
+struct LoaderSel<true, NT, GATED, TN> { using type = LoaderKMajor<NT, GATED>; };
+template <int NT, bool GATED, int TN>
+struct LoaderSel<false, NT, GATED, TN> { using type = LoaderMNMajor<NT, GATED, TN>; };
 
 // MFMA operand fragments of v_mfma_f32_32x32x16_bf16: lane l supplies row
 // (or column) l%32 of a 32-wide block and the 8 k values 16s + 8(l/32) + 0..7
 // of sub-step s.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <bool KMAJ>
+template <bool KMAJ, int NB>
 struct FragReader;
 
 // K-contiguous tile: one ds_read_b128 per fragment.
-template <>
-struct FragReader<true> {
-  int off[4];   // per sub-step s, for block 0; block i adds i * 32 rows * 128 B
+template <int NB>
+struct FragReader<true, NB> {
+  int off[4];   // per sub-step s, for block 0; block i adds 32 rows * 128 B
   __device__ void init(int mn0, int lane) {
     const int l32 = lane & 31, khalf = lane >> 5;
 #pragma unroll
@@ -225,14 +249,14 @@ struct FragReader<true> {
 // addressed by source lanes 4k + i/4 (k = 0..3).  Source lane j points at
 // (k row K0 + j/4, columns c0 + 4(j%4)..+3), so output lane i receives
 // column c0 + i at rows K0..K0+3.
-template <>
-struct FragReader<false> {
-  int off[4];   // per block i (32 columns); sub-step s and half h add rows
+template <int NB>
+struct FragReader<false, NB> {
+  int off[NB];  // per block i (32 columns); sub-step s and half h add k rows
   __device__ void init(int mn0, int lane) {
     const int j = lane & 15, khalf = lane >> 5;
     const int krow = 8 * khalf + (j >> 2);                  // + 16 s + 4 h
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NB; ++i) {
       const int mn = mn0 + i * 32 + (lane & 16) + 4 * (j & 3);
       off[i] = mnmaj_off(krow, mn >> 3) + ((mn & 7) << 1);  // (krow + 16s + 4h) & 3 == krow & 3
     }
@@ -241,7 +265,6 @@ struct FragReader<false> {
     const char* p = tile + off[i] + s * 16 * 512;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 512));
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
     const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
   }
@@ -301,30 +324,33 @@ __device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __ex
 // ---------------------------------------------------------------------------
 // The bf16 MFMA GEMM: C[M,N] = A[M,K] B[K,N] (+ epilogue EPI)
 // ---------------------------------------------------------------------------
-template <bool AK, bool BKM, int EPI>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int WMv, int WNv, bool AK, bool BKM, int EPI>
+__global__ void __launch_bounds__(64 * WMv * WNv)
+    __attribute__((amdgpu_waves_per_eu(WMv * WNv / 4, WMv * WNv / 4)))
 gemm_bf16_kernel(GemmArgs g) {
+  using G = Grid<WMv, WNv>;
+  constexpr int FM = G::FM, FN = G::FN, TM = G::TM, TN = G::TN, LP = G::LP;
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   constexpr bool GATED = (EPI == EPI_SWIGLU);
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
+  const int lane = t & 63, wave = t >> 6, wm = wave / WNv, wn = wave % WNv;
 
   const int tiles_m = (g.M + BM - 1) / BM;
-  const int tiles_n = GATED ? (g.N + 127) / 128 : (g.N + BN - 1) / BN;
+  const int tiles_n = GATED ? (g.N + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
   int tm, tn;
   map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int row0 = tm * BM, col0 = tn * BN;
 
-  typename LoaderSel<AK, false>::type la;
-  typename LoaderSel<BKM, GATED>::type lb;
+  typename LoaderSel<AK, G::NT, false, TN>::type la;
+  typename LoaderSel<BKM, G::NT, GATED, TN>::type lb;
   la.init(g.A, g.A_bytes, g.lda, row0, g.M, g.K, t, 0, tm);
   lb.init(g.B, g.B_bytes, g.ldb, col0, g.N, g.K, t, g.F, tn);
 
-  f32x16 acc[4][4];
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
   // Software pipeline (one K step = four 16-wide MFMA sub-steps):
   //   s0, s1: MFMAs; the fragments of the next sub-step are read meanwhile
@@ -332,29 +358,29 @@ gemm_bf16_kernel(GemmArgs g) {
   //           LDS stage; the global loads two steps ahead are issued into
   //           the same registers (a full K step of latency cover)
   //   s3:     barrier, then the next stage's first fragments are read while
-  //           the last 16 MFMAs of this step run.
+  //           the last MFMAs of this step run.
   // Fragments are double-buffered in registers.  Loads past K read zeros,
   // so the loop has no branches.
   const int nk = (g.K + BK - 1) / BK;
   const int l32 = lane & 31;
-  FragReader<AK> fra;
-  FragReader<BKM> frb;
-  fra.init(wm * 128, lane);
-  frb.init(wn * 128, lane);
-  u32x4 ra[8], rb[8];
-  bf16x8 fa[2][4], fb[2][4];
+  FragReader<AK, FM> fra;
+  FragReader<BKM, FN> frb;
+  fra.init(wm * TM, lane);
+  frb.init(wn * TN, lane);
+  u32x4 ra[LP], rb[LP];
+  bf16x8 fa[2][FM], fb[2][FN];
 
-  auto read_frags = [&](const char* stage, int s, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+  auto read_frags = [&](const char* stage, int s, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = fra.read(stage, s, i);
+    for (int i = 0; i < FM; ++i) a[i] = fra.read(stage, s, i);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = frb.read(stage + OPER_BYTES, s, j);
+    for (int j = 0; j < FN; ++j) b[j] = frb.read(stage + OPER_BYTES, s, j);
   };
-  auto mfma16 = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[4]) {
+  auto mfmas = [&](const bf16x8 (&a)[FM], const bf16x8 (&b)[FN]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   };
 
@@ -371,33 +397,35 @@ gemm_bf16_kernel(GemmArgs g) {
     const char* sc = smem + cur * STAGE_BYTES;
     char* sn = smem + (cur ^ 1) * STAGE_BYTES;
     read_frags(sc, 1, fa[1], fb[1]);
-    mfma16(fa[0], fb[0]);
+    mfmas(fa[0], fb[0]);
     __builtin_amdgcn_sched_barrier(0);
     read_frags(sc, 2, fa[0], fb[0]);
-    mfma16(fa[1], fb[1]);
+    mfmas(fa[1], fb[1]);
     __builtin_amdgcn_sched_barrier(0);
     read_frags(sc, 3, fa[1], fb[1]);
     la.store(sn, ra);
     lb.store(sn + OPER_BYTES, rb);
     la.load((kt + 2) * BK, ra);
     lb.load((kt + 2) * BK, rb);
-    mfma16(fa[0], fb[0]);
+    mfmas(fa[0], fb[0]);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     read_frags(sn, 0, fa[0], fb[0]);
-    mfma16(fa[1], fb[1]);
+    mfmas(fa[1], fb[1]);
     __builtin_amdgcn_sched_barrier(0);
     cur ^= 1;
   }
 
   // ------------------------------ epilogue ------------------------------
-  const int lrow0 = wm * 128;                 // wave's first local row
-  const int lcol0 = wn * 128 + l32;           // lane's local column in block j=0
+  // Lane holds, for block (i, j) and register r: local row
+  // wm*TM + 32i + acc_row(r, lane), local column wn*TN + 32j + lane%32.
+  const int lrow0 = wm * TM;
+  const int lcol0 = wn * TN + l32;
 
   if constexpr (EPI == EPI_STORE || EPI == EPI_ROWSCALE) {
     __bf16* C = (__bf16*)g.C;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = row0 + lrow0 + i * 32 + acc_row(r, lane);
@@ -405,7 +433,7 @@ gemm_bf16_kernel(GemmArgs g) {
         float sc = 1.0f;
         if constexpr (EPI == EPI_ROWSCALE) sc = g.vrow ? g.vrow[row] : bf2f(((const __bf16*)g.vcol)[row]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < FN; ++j) {
           const int col = col0 + lcol0 + j * 32;
           if (col < g.N) C[(int64_t)row * g.ldc + col] = f2bf(sc * acc[i][j][r]);
         }
@@ -414,20 +442,19 @@ gemm_bf16_kernel(GemmArgs g) {
   } else if constexpr (EPI == EPI_RESID_SUMSQ) {
     __bf16* C = (__bf16*)g.C;
     const __bf16* E = (const __bf16*)g.E;
-    float* red = (float*)smem;
+    float* red = (float*)smem;                  // [WN][BM] row partials
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FM; ++i) {
       float sq[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = row0 + lrow0 + i * 32 + acc_row(r, lane);
         float s = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < FN; ++j) {
           const int col = col0 + lcol0 + j * 32;
           if (row < g.M && col < g.N) {
-            const int64_t e = (int64_t)row * g.lde + col;
-            const float yv = acc[i][j][r] + bf2f(E[e]);
+            const float yv = acc[i][j][r] + bf2f(E[(int64_t)row * g.lde + col]);
             C[(int64_t)row * g.ldc + col] = f2bf(yv);
             s += yv * yv;
           }
@@ -435,30 +462,34 @@ gemm_bf16_kernel(GemmArgs g) {
         sq[r] = s;
       }
       const float tot = halfwave_rowsum16(sq, lane);
-      if ((lane & 1) == 0) {
-        const int rr = l32 >> 1;
-        red[wn * BM + lrow0 + i * 32 + acc_row(rr, lane)] = tot;
-      }
+      if ((lane & 1) == 0) red[wn * BM + lrow0 + i * 32 + acc_row(l32 >> 1, lane)] = tot;
     }
     __syncthreads();
-    const int row = row0 + t;
-    if (row < g.M) g.part_row[(int64_t)row * g.ld_part_row + tn] = red[t] + red[BM + t];
+    if (t < BM) {
+      const int row = row0 + t;
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WNv; ++w) s += red[w * BM + t];
+      if (row < g.M) g.part_row[(int64_t)row * g.ld_part_row + tn] = s;
+    }
   } else if constexpr (EPI == EPI_DN) {
     // dh = acc; dn = gamma_j dh (stored); per-row sum_j dn*y; per-column sum_i dh*r*y
     __bf16* C = (__bf16*)g.C;
     const __bf16* Y = (const __bf16*)g.E;
     const __bf16* gam = (const __bf16*)g.vcol;
-    float* red = (float*)smem;           // [2][BM] row partials
-    float* redc = red + 2 * BM;          // [2][BN] column partials
-    float gj[4];
+    float* red = (float*)smem;                  // [WN][BM] row partials
+    float* redc = red + WNv * BM;               // [WM][BN] column partials
+    float gj[FN];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < FN; ++j) {
       const int col = col0 + lcol0 + j * 32;
       gj[j] = col < g.N ? bf2f(gam[col]) : 0.0f;
     }
-    float csum[4] = {0.f, 0.f, 0.f, 0.f};
+    float csum[FN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < FN; ++j) csum[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
       float rs[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -466,7 +497,7 @@ gemm_bf16_kernel(GemmArgs g) {
         const float rv = row < g.M ? g.vrow[row] : 0.0f;
         float s = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < FN; ++j) {
           const int col = col0 + lcol0 + j * 32;
           if (row < g.M && col < g.N) {
             const float dh = acc[i][j][r];
@@ -483,30 +514,40 @@ gemm_bf16_kernel(GemmArgs g) {
       if ((lane & 1) == 0) red[wn * BM + lrow0 + i * 32 + acc_row(l32 >> 1, lane)] = tot;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < FN; ++j) {
       const float c2 = csum[j] + __shfl_xor(csum[j], 32);
-      if (lane < 32) redc[wm * BN + wn * 128 + j * 32 + l32] = c2;
+      if (lane < 32) redc[wm * BN + wn * TN + j * 32 + l32] = c2;
     }
     __syncthreads();
-    const int row = row0 + t;
-    if (row < g.M) g.part_row[(int64_t)row * g.ld_part_row + tn] = red[t] + red[BM + t];
-    const int col = col0 + t;
-    if (col < g.N) g.part_col[(int64_t)tm * g.ld_part_col + col] = redc[t] + redc[BN + t];
+    if (t < BM) {
+      const int row = row0 + t;
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WNv; ++w) s += red[w * BM + t];
+      if (row < g.M) g.part_row[(int64_t)row * g.ld_part_row + tn] = s;
+    }
+    if (t < BN) {
+      const int col = col0 + t;
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WMv; ++w) s += redc[w * BN + t];
+      if (col < g.N) g.part_col[(int64_t)tm * g.ld_part_col + col] = s;
+    }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    // blocks j = 0,1 hold gate columns, j = 2,3 the up columns of the same j
+    // blocks j < FN/2 hold gate columns, j + FN/2 the up columns of the same j
     __bf16* GU = (__bf16*)g.C;
     __bf16* Aout = (__bf16*)g.C2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = row0 + lrow0 + i * 32 + acc_row(r, lane);
         if (row >= g.M) continue;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int jj = tn * 128 + wn * 64 + j * 32 + l32;
+        for (int j = 0; j < FN / 2; ++j) {
+          const int jj = tn * (BN / 2) + wn * (TN / 2) + j * 32 + l32;
           if (jj < g.F) {
-            const float gv = acc[i][j][r], uv = acc[i][j + 2][r];
+            const float gv = acc[i][j][r], uv = acc[i][j + FN / 2][r];
             GU[(int64_t)row * g.ldc + jj] = f2bf(gv);
             GU[(int64_t)row * g.ldc + g.F + jj] = f2bf(uv);
             Aout[(int64_t)row * g.ldc2 + jj] = f2bf(silu_f(gv) * uv);
@@ -519,13 +560,13 @@ gemm_bf16_kernel(GemmArgs g) {
     __bf16* DGU = (__bf16*)g.C;
     const __bf16* GU = (const __bf16*)g.E;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = row0 + lrow0 + i * 32 + acc_row(r, lane);
         if (row >= g.M) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < FN; ++j) {
           const int col = col0 + lcol0 + j * 32;
           if (col < g.N) {
             const float da = acc[i][j][r];
@@ -696,11 +737,15 @@ __global__ void dy_n_kernel(__bf16* __restrict__ dR, __bf16* __restrict__ n,
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+// Wave grid used for every bf16 GEMM: 2 x 4 waves (two per SIMD).
+constexpr int kWavesM = 2, kWavesN = 4;
+
 template <bool AK, bool BKM, int EPI>
 static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   const int tiles_m = (g.M + BM - 1) / BM;
-  const int tiles_n = (EPI == EPI_SWIGLU) ? (g.N + 127) / 128 : (g.N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, EPI>), dim3(tiles_m * tiles_n), dim3(NT), 0, s, g);
+  const int tiles_n = (EPI == EPI_SWIGLU) ? (g.N + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_bf16_kernel<kWavesM, kWavesN, AK, BKM, EPI>), dim3(tiles_m * tiles_n),
+                     dim3(64 * kWavesM * kWavesN), 0, s, g);
   return hipGetLastError();
 }
 
