@@ -10,8 +10,8 @@
 // scale, SwiGLU) are rewritten to run inside that epilogue.  Here:
 //
 //  * one bf16 MFMA main loop (v_mfma_f32_32x32x16_bf16, fp32 accumulators),
-//    256x256 output tile per 256-thread workgroup, 4 waves of 128x128, K
-//    step 64, LDS double buffered;
+//    256x256 output tile per 512-thread workgroup, 8 waves of 128x64 (two
+//    per SIMD), K step 64, LDS double buffered;
 //  * operand tiles are staged in LDS in the layout they have in memory,
 //    with 16-byte chunks XOR-swizzled so that every LDS access of the loop
 //    is free of bank conflicts on gfx950's 64-bank LDS (16 lanes x 16 bytes
@@ -22,9 +22,10 @@
 //  * epilogues selected at compile time (launch.hpp: Epi) work on the
 //    accumulator registers in place: residual add + per-tile partial sums of
 //    squares, row scale, the RMSNorm-backward epilogue, SwiGLU and its
-//    backward.  Row reductions use a halving butterfly of lane shuffles;
-//    the two waves that share rows combine through LDS in a fixed order, so
-//    every result is run-to-run deterministic (no atomics).
+//    backward.  The epilogue moves the accumulators through LDS into a
+//    row-major assignment (16-byte global accesses, row sums in 3 lane
+//    shuffles); waves that share rows or columns combine through LDS in a
+//    fixed order, so every result is run-to-run deterministic (no atomics).
 #include "launch.hpp"
 
 namespace coda {
@@ -75,12 +76,21 @@ __device__ __forceinline__ __bf16 f2bf(float f) { return (__bf16)f; }  // round 
 // XCDs (wg % 8), each with its own L2; consecutive logical tiles are given to
 // one XCD so that the tiles resident on an XCD share operand rows/columns.
 // Within that order, groups of GM tile-rows are walked column by column.
+#ifndef CODA_TILE_GROUP_M
+#define CODA_TILE_GROUP_M 8
+#endif
+#ifndef CODA_XCD_REMAP
+#define CODA_XCD_REMAP 1
+#endif
 __device__ __forceinline__ void map_tile(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
-  const int q = total >> 3, rem = total & 7;
-  const int x = wg & 7, i = wg >> 3;
-  const int t = (x < rem) ? x * (q + 1) + i : rem * (q + 1) + (x - rem) * q + i;
-  constexpr int GM = 8;
+  int t = wg;
+  if (CODA_XCD_REMAP) {
+    const int q = total >> 3, rem = total & 7;
+    const int x = wg & 7, i = wg >> 3;
+    t = (x < rem) ? x * (q + 1) + i : rem * (q + 1) + (x - rem) * q + i;
+  }
+  constexpr int GM = CODA_TILE_GROUP_M;
   const int group = GM * tiles_n;
   const int gidx = t / group;
   const int first_m = gidx * GM;
@@ -274,48 +284,14 @@ struct FragReader<false, NB> {
 // Epilogue helpers
 // ---------------------------------------------------------------------------
 
-// Accumulator layout of v_mfma_f32_32x32x16_bf16: lane l, register r holds
-// row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the 32x32 block.
-__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-
-// Sum of v[0..15] of every lane over the 32 lanes of its half-wave, one
-// result per row: halving butterfly (each exchange halves the values kept).
-// On return lane l holds the sum for register index (l & 31) >> 1.
-__device__ __forceinline__ float halfwave_rowsum16(const float (&v)[16], int lane) {
-  float w[8];
-  {
-    const bool b = lane & 16;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float keep = b ? v[i + 8] : v[i];
-      const float send = b ? v[i] : v[i + 8];
-      w[i] = keep + __shfl_xor(send, 16);
-    }
-  }
-  float x[4];
-  {
-    const bool b = lane & 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float keep = b ? w[i + 4] : w[i];
-      const float send = b ? w[i] : w[i + 4];
-      x[i] = keep + __shfl_xor(send, 8);
-    }
-  }
-  float y[2];
-  {
-    const bool b = lane & 4;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float keep = b ? x[i + 2] : x[i];
-      const float send = b ? x[i] : x[i + 2];
-      y[i] = keep + __shfl_xor(send, 4);
-    }
-  }
-  const bool b = lane & 2;
-  float z = (b ? y[1] : y[0]) + __shfl_xor(b ? y[0] : y[1], 2);
-  z += __shfl_xor(z, 1);
-  return z;
+// Accumulator layout.  The MFMA is issued with the B fragment as its first
+// operand and the A fragment as its second, so it accumulates C^T blocks:
+// lane l, register r of block (i, j) holds C[row = 32i + l%32][col = 32j +
+// 8(r/4) + 4(l/32) + r%4].  A lane thus owns one row and, per group of four
+// registers, four consecutive columns, which the epilogue writes to LDS as
+// 16-byte vectors.
+__device__ __forceinline__ f32x4 quad(const f32x16& a, int g) {
+  return f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
 }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
@@ -381,7 +357,7 @@ gemm_bf16_kernel(GemmArgs g) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
   };
 
   la.load(0, ra);
@@ -417,165 +393,195 @@ gemm_bf16_kernel(GemmArgs g) {
   }
 
   // ------------------------------ epilogue ------------------------------
-  // Lane holds, for block (i, j) and register r: local row
-  // wm*TM + 32i + acc_row(r, lane), local column wn*TN + 32j + lane%32.
-  const int lrow0 = wm * TM;
-  const int lcol0 = wn * TN + l32;
+  // The accumulators are moved, 32 rows (one block row i) at a time, through
+  // a wave-private LDS region (32 rows x 64 fp32, 16-byte chunks swizzled by
+  // row) into a row-major assignment: in pass p, lane l owns row
+  // 32i + 8p + l/8 of the wave tile and its 8 consecutive columns 8(l%8)..+7.
+  // Every global load and store of the epilogue is then a 16-byte vector and
+  // 8 lanes cover one 128-byte row segment.  Only the cross-wave reductions
+  // need a workgroup barrier.
+  static_assert(TN == 64 && FN == 2, "row-major epilogue assumes 64-column wave tiles");
+  __syncthreads();                                  // main loop done: LDS is free
+  char* region = smem + wave * 8192;
+  float* red = (float*)(smem + 8 * 8192);           // [WN][BM] row partials
+  float* redc = red + WNv * BM;                     // [WM][BN] column partials
+  const int c8 = lane & 7, rsub = lane >> 3;
+  const int gcol = col0 + wn * TN + 8 * c8;         // first global column of the lane
+  const bool colok = gcol < g.N;
+  auto dump = [&](int i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = j * 8 + 2 * q + (lane >> 5);
+        *(f32x4*)(region + l32 * 256 + ((c ^ (l32 & 15)) << 4)) = quad(acc[i][j], q);
+      }
+  };
+  auto fetch8 = [&](int r, int cpair, f32x4& lo, f32x4& hi) {   // 8 fp32: columns 8*cpair..+7 of region row r
+    lo = *(const f32x4*)(region + r * 256 + (((2 * cpair) ^ (r & 15)) << 4));
+    hi = *(const f32x4*)(region + r * 256 + (((2 * cpair + 1) ^ (r & 15)) << 4));
+  };
+  auto ld8 = [&](const __bf16* p, f32x4& lo, f32x4& hi) {
+    const bf16x8 v = *(const bf16x8*)p;
+    lo = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    hi = f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+  };
+  auto st8 = [&](__bf16* p, f32x4 lo, f32x4 hi) {
+    *(bf16x8*)p = bf16x8{f2bf(lo[0]), f2bf(lo[1]), f2bf(lo[2]), f2bf(lo[3]),
+                         f2bf(hi[0]), f2bf(hi[1]), f2bf(hi[2]), f2bf(hi[3])};
+  };
+  auto sum8 = [](float v) {                          // over the 8 lanes of a row
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    return v;
+  };
 
-  if constexpr (EPI == EPI_STORE || EPI == EPI_ROWSCALE) {
+  if constexpr (EPI == EPI_STORE || EPI == EPI_ROWSCALE || EPI == EPI_RESID_SUMSQ ||
+                EPI == EPI_DN || EPI == EPI_SWIGLU_BWD) {
     __bf16* C = (__bf16*)g.C;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + lrow0 + i * 32 + acc_row(r, lane);
-        if (row >= g.M) continue;
-        float sc = 1.0f;
-        if constexpr (EPI == EPI_ROWSCALE) sc = g.vrow ? g.vrow[row] : bf2f(((const __bf16*)g.vcol)[row]);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = col0 + lcol0 + j * 32;
-          if (col < g.N) C[(int64_t)row * g.ldc + col] = f2bf(sc * acc[i][j][r]);
-        }
-      }
+    f32x4 glo{}, ghi{}, clo{0.f, 0.f, 0.f, 0.f}, chi{0.f, 0.f, 0.f, 0.f};
+    if constexpr (EPI == EPI_DN) {
+      if (colok) ld8((const __bf16*)g.vcol + gcol, glo, ghi);
     }
-  } else if constexpr (EPI == EPI_RESID_SUMSQ) {
-    __bf16* C = (__bf16*)g.C;
-    const __bf16* E = (const __bf16*)g.E;
-    float* red = (float*)smem;                  // [WN][BM] row partials
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      float sq[16];
+      dump(i);
+      __builtin_amdgcn_s_waitcnt(0xc07f);           // this wave's LDS writes are done
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + lrow0 + i * 32 + acc_row(r, lane);
-        float s = 0.0f;
+      for (int p = 0; p < 4; ++p) {
+        const int r = 8 * p + rsub;
+        const int lrow_t = wm * TM + i * 32 + r;     // row within the workgroup tile
+        const int row = row0 + lrow_t;
+        const bool ok = colok && row < g.M;
+        f32x4 lo, hi;
+        fetch8(r, c8, lo, hi);
+        const int64_t o = (int64_t)row * g.ldc + gcol;
+        if constexpr (EPI == EPI_STORE) {
+          if (ok) st8(C + o, lo, hi);
+        } else if constexpr (EPI == EPI_ROWSCALE) {
+          if (ok) {
+            const float sc = g.vrow ? g.vrow[row] : bf2f(((const __bf16*)g.vcol)[row]);
+            st8(C + o, lo * sc, hi * sc);
+          }
+        } else if constexpr (EPI == EPI_RESID_SUMSQ) {
+          float s = 0.0f;
+          if (ok) {
+            f32x4 elo, ehi;
+            ld8((const __bf16*)g.E + (int64_t)row * g.lde + gcol, elo, ehi);
+            lo += elo;
+            hi += ehi;
+            st8(C + o, lo, hi);
+            const f32x4 sq = lo * lo + hi * hi;
+            s = sq[0] + sq[1] + sq[2] + sq[3];
+          }
+          s = sum8(s);
+          if (c8 == 0) red[wn * BM + lrow_t] = s;
+        } else if constexpr (EPI == EPI_DN) {
+          // dh = acc; dn = gamma dh (stored); row sum of dn*y; column sums of dh*r*y
+          float s = 0.0f;
+          if (ok) {
+            f32x4 ylo, yhi;
+            ld8((const __bf16*)g.E + (int64_t)row * g.lde + gcol, ylo, yhi);
+            const float rv = g.vrow[row];
+            const f32x4 dlo = lo * glo, dhi = hi * ghi;
+            st8(C + o, dlo, dhi);
+            const f32x4 sp = dlo * ylo + dhi * yhi;
+            s = sp[0] + sp[1] + sp[2] + sp[3];
+            clo += lo * ylo * rv;
+            chi += hi * yhi * rv;
+          }
+          s = sum8(s);
+          if (c8 == 0) red[wn * BM + lrow_t] = s;
+        } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+          // da = acc [M, F]; g, u from the saved gu; dgu = [dg | du]
+          if (ok) {
+            const __bf16* gp = (const __bf16*)g.E + (int64_t)row * g.lde + gcol;
+            f32x4 g0, g1, u0, u1;
+            ld8(gp, g0, g1);
+            ld8(gp + g.F, u0, u1);
+            f32x4 dg0, dg1, du0, du1;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = col0 + lcol0 + j * 32;
-          if (row < g.M && col < g.N) {
-            const float yv = acc[i][j][r] + bf2f(E[(int64_t)row * g.lde + col]);
-            C[(int64_t)row * g.ldc + col] = f2bf(yv);
-            s += yv * yv;
+            for (int e = 0; e < 4; ++e) {
+              float sg = sigmoid_f(g0[e]);
+              dg0[e] = lo[e] * u0[e] * sg * (1.0f + g0[e] * (1.0f - sg));
+              du0[e] = lo[e] * g0[e] * sg;
+              sg = sigmoid_f(g1[e]);
+              dg1[e] = hi[e] * u1[e] * sg * (1.0f + g1[e] * (1.0f - sg));
+              du1[e] = hi[e] * g1[e] * sg;
+            }
+            st8(C + o, dg0, dg1);
+            st8(C + o + g.F, du0, du1);
           }
         }
-        sq[r] = s;
       }
-      const float tot = halfwave_rowsum16(sq, lane);
-      if ((lane & 1) == 0) red[wn * BM + lrow0 + i * 32 + acc_row(l32 >> 1, lane)] = tot;
     }
-    __syncthreads();
-    if (t < BM) {
-      const int row = row0 + t;
-      float s = 0.0f;
+    if constexpr (EPI == EPI_RESID_SUMSQ || EPI == EPI_DN) {
+      if constexpr (EPI == EPI_DN) {
+        // column partials: reduce over the 8 row groups of lanes (l/8), then
+        // combine the WM waves that share these columns through LDS
 #pragma unroll
-      for (int w = 0; w < WNv; ++w) s += red[w * BM + t];
-      if (row < g.M) g.part_row[(int64_t)row * g.ld_part_row + tn] = s;
-    }
-  } else if constexpr (EPI == EPI_DN) {
-    // dh = acc; dn = gamma_j dh (stored); per-row sum_j dn*y; per-column sum_i dh*r*y
-    __bf16* C = (__bf16*)g.C;
-    const __bf16* Y = (const __bf16*)g.E;
-    const __bf16* gam = (const __bf16*)g.vcol;
-    float* red = (float*)smem;                  // [WN][BM] row partials
-    float* redc = red + WNv * BM;               // [WM][BN] column partials
-    float gj[FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = col0 + lcol0 + j * 32;
-      gj[j] = col < g.N ? bf2f(gam[col]) : 0.0f;
-    }
-    float csum[FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) csum[j] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      float rs[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + lrow0 + i * 32 + acc_row(r, lane);
-        const float rv = row < g.M ? g.vrow[row] : 0.0f;
+        for (int e = 0; e < 4; ++e) {
+          clo[e] += __shfl_xor(clo[e], 8);
+          clo[e] += __shfl_xor(clo[e], 16);
+          clo[e] += __shfl_xor(clo[e], 32);
+          chi[e] += __shfl_xor(chi[e], 8);
+          chi[e] += __shfl_xor(chi[e], 16);
+          chi[e] += __shfl_xor(chi[e], 32);
+        }
+        if (lane < 8) {
+          *(f32x4*)(redc + wm * BN + wn * TN + 8 * c8) = clo;
+          *(f32x4*)(redc + wm * BN + wn * TN + 8 * c8 + 4) = chi;
+        }
+      }
+      __syncthreads();
+      if (t < BM) {
+        const int row = row0 + t;
         float s = 0.0f;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = col0 + lcol0 + j * 32;
-          if (row < g.M && col < g.N) {
-            const float dh = acc[i][j][r];
-            const float yv = bf2f(Y[(int64_t)row * g.lde + col]);
-            const float dn = gj[j] * dh;
-            C[(int64_t)row * g.ldc + col] = f2bf(dn);
-            s += dn * yv;
-            csum[j] += dh * rv * yv;
-          }
-        }
-        rs[r] = s;
+        for (int w = 0; w < WNv; ++w) s += red[w * BM + t];
+        if (row < g.M) g.part_row[(int64_t)row * g.ld_part_row + tn] = s;
       }
-      const float tot = halfwave_rowsum16(rs, lane);
-      if ((lane & 1) == 0) red[wn * BM + lrow0 + i * 32 + acc_row(l32 >> 1, lane)] = tot;
-    }
+      if constexpr (EPI == EPI_DN) {
+        if (t < BN) {
+          const int col = col0 + t;
+          float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const float c2 = csum[j] + __shfl_xor(csum[j], 32);
-      if (lane < 32) redc[wm * BN + wn * TN + j * 32 + l32] = c2;
-    }
-    __syncthreads();
-    if (t < BM) {
-      const int row = row0 + t;
-      float s = 0.0f;
-#pragma unroll
-      for (int w = 0; w < WNv; ++w) s += red[w * BM + t];
-      if (row < g.M) g.part_row[(int64_t)row * g.ld_part_row + tn] = s;
-    }
-    if (t < BN) {
-      const int col = col0 + t;
-      float s = 0.0f;
-#pragma unroll
-      for (int w = 0; w < WMv; ++w) s += redc[w * BN + t];
-      if (col < g.N) g.part_col[(int64_t)tm * g.ld_part_col + col] = s;
+          for (int w = 0; w < WMv; ++w) s += redc[w * BN + t];
+          if (col < g.N) g.part_col[(int64_t)tm * g.ld_part_col + col] = s;
+        }
+      }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    // blocks j < FN/2 hold gate columns, j + FN/2 the up columns of the same j
+    // The wave tile's 64 columns are 32 gate columns j and the 32 up columns
+    // of the same j.  Pass p: lane l owns row 16p + l/4 and gate/up column
+    // group l%4 (8 columns each).
     __bf16* GU = (__bf16*)g.C;
     __bf16* Aout = (__bf16*)g.C2;
+    const int c4 = lane & 3, r4 = lane >> 2;
+    const int jj = tn * (BN / 2) + wn * (TN / 2) + 8 * c4;
+    const bool jok = jj < g.F;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      dump(i);
+      __builtin_amdgcn_s_waitcnt(0xc07f);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + lrow0 + i * 32 + acc_row(r, lane);
-        if (row >= g.M) continue;
+      for (int p = 0; p < 2; ++p) {
+        const int r = 16 * p + r4;
+        const int row = row0 + wm * TM + i * 32 + r;
+        f32x4 g0, g1, u0, u1;
+        fetch8(r, c4, g0, g1);
+        fetch8(r, 4 + c4, u0, u1);
+        if (jok && row < g.M) {
+          st8(GU + (int64_t)row * g.ldc + jj, g0, g1);
+          st8(GU + (int64_t)row * g.ldc + g.F + jj, u0, u1);
+          f32x4 a0, a1;
 #pragma unroll
-        for (int j = 0; j < FN / 2; ++j) {
-          const int jj = tn * (BN / 2) + wn * (TN / 2) + j * 32 + l32;
-          if (jj < g.F) {
-            const float gv = acc[i][j][r], uv = acc[i][j + FN / 2][r];
-            GU[(int64_t)row * g.ldc + jj] = f2bf(gv);
-            GU[(int64_t)row * g.ldc + g.F + jj] = f2bf(uv);
-            Aout[(int64_t)row * g.ldc2 + jj] = f2bf(silu_f(gv) * uv);
+          for (int e = 0; e < 4; ++e) {
+            a0[e] = silu_f(g0[e]) * u0[e];
+            a1[e] = silu_f(g1[e]) * u1[e];
           }
-        }
-      }
-    }
-  } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-    // da = acc [M, F]; g, u from the saved gu; dgu = [dg | du]
-    __bf16* DGU = (__bf16*)g.C;
-    const __bf16* GU = (const __bf16*)g.E;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + lrow0 + i * 32 + acc_row(r, lane);
-        if (row >= g.M) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = col0 + lcol0 + j * 32;
-          if (col < g.N) {
-            const float da = acc[i][j][r];
-            const float gv = bf2f(GU[(int64_t)row * g.lde + col]);
-            const float uv = bf2f(GU[(int64_t)row * g.lde + g.F + col]);
-            const float sg = sigmoid_f(gv);
-            DGU[(int64_t)row * g.ldc + col] = f2bf(da * uv * sg * (1.0f + gv * (1.0f - sg)));
-            DGU[(int64_t)row * g.ldc + g.F + col] = f2bf(da * gv * sg);
-          }
+          st8(Aout + (int64_t)row * g.ldc2 + jj, a0, a1);
         }
       }
     }
