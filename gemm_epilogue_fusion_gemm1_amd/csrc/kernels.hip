@@ -39,25 +39,46 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = kTileM;
 constexpr int BN = kTileN;
-constexpr int BK = 64;
-constexpr int OPER_BYTES = BM * BK * 2;         // one operand tile, 32 KiB, unpadded
-constexpr int STAGE_BYTES = 2 * OPER_BYTES;      // A + B
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;       // two stages
 constexpr uint32_t OOB = 0x80000000u;            // voffset past every extent -> loads 0
-static_assert(BM == BN, "operand tiles share one LDS geometry");
-static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
 
-// LDS tile layouts (256 MN x 64 K, bf16):
-//  K-contiguous:  row m (128 B) at m*128; its 16-byte k chunk q (k = 8q..8q+7)
-//                 sits at chunk position q ^ ((m >> 1) & 7).  16 lanes that
-//                 read chunk q of rows m..m+15 (m % 16 == 0) hit 16 distinct
-//                 16-byte bank groups; 16 lanes that write 8 chunks of 2 rows
-//                 fill 256 contiguous bytes.
+// K step and depth of the LDS ring of one GEMM instantiation.  K-contiguous
+// operands want 128-byte row segments (K step 64, two stages); when both
+// operands are MN-contiguous a K step of 32 with a four-stage ring hides more
+// load latency.  Both fill 128 KiB of LDS.
+template <int BKv, int NSTv>
+struct KCfg {
+  static constexpr int BK = BKv;                       // K step
+  static constexpr int NSTAGE = NSTv;                  // LDS ring of K steps
+  static constexpr int OPER_BYTES = BM * BK * 2;       // one operand tile, unpadded
+  static constexpr int STAGE_BYTES = 2 * OPER_BYTES;   // A + B
+  static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
+  static constexpr int KROW = BK * 2;                  // bytes of one K-contiguous tile row
+  static constexpr int KCH = BK / 8;                   // 16-byte chunks per such row
+  static constexpr int KRP = 256 / KROW;               // such rows per 256-byte bank line
+  static_assert(BK == 32 || BK == 64, "K step");
+  static_assert(NSTAGE >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring");
+  static_assert(LDS_BYTES >= 8 * 8192 + 6144, "epilogue staging fits in the ring");
+  // K-contiguous tile: row m at m*KROW, chunk q at position q ^ ((m/KRP) % KCH)
+  static __device__ __forceinline__ int kmaj_off(int m, int q) {
+    return m * KROW + ((q ^ ((m / KRP) % KCH)) << 4);
+  }
+};
+static_assert(BM == BN, "operand tiles share one LDS geometry");
+
+// LDS tile layouts (256 MN x 32 K, bf16):
+// (BK = K step; see KCfg)
+//  K-contiguous:  row m (2 BK bytes) at m*2BK; its 16-byte k chunk q (k =
+//                 8q..8q+7) sits at chunk position q ^ ((m / KRP) % KCH),
+//                 KRP rows sharing one 256-byte bank line.  16 lanes that read
+//                 chunk q of rows m..m+15 (m % 16 == 0) hit 16 distinct 16-byte
+//                 bank groups.
 //  MN-contiguous: row k (512 B) at k*512; its 16-byte MN chunk c (mn =
 //                 8c..8c+7) sits at chunk position c ^ ((k & 3) << 2).  A
 //                 transpose read touches 4 rows x 4 chunks per 32 lanes, which
 //                 the swizzle spreads over all 16 bank groups.
-__device__ __forceinline__ int kmaj_off(int m, int q) { return m * 128 + ((q ^ ((m >> 1) & 7)) << 4); }
+// Both are filled by direct-to-LDS buffer loads: one 64-lane load writes 1 KiB
+// of contiguous LDS (lane l at +16 l), so the swizzle is applied by choosing
+// which global chunk each lane fetches.
 __device__ __forceinline__ int mnmaj_off(int k, int c) { return k * 512 + ((c ^ ((k & 3) << 2)) << 4); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
@@ -112,123 +133,134 @@ struct Grid {
   static constexpr int WM = WM_, WN = WN_, NT = 64 * WM_ * WN_;
   static constexpr int TM = BM / WM_, TN = BN / WN_;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int LP = BM * BK / 8 / NT;     // 16-byte loads per thread per operand
-  static_assert(FM >= 1 && FN >= 1 && LP >= 1, "tile too small for the wave grid");
+  static_assert(FM >= 1 && FN >= 1, "tile too small for the wave grid");
 };
 
 // ---------------------------------------------------------------------------
-// Operand staging: global -> registers (buffer loads, out-of-range -> 0) ->
-// LDS.  Each 16-byte load is stored unchanged; only its chunk position is
-// swizzled.
+// Operand staging: buffer loads straight into LDS (no register staging).
+// Out-of-range chunks get an out-of-range offset and land as zeros, so edge
+// tiles and K tails need no branch.  Each wave fills LP KiB per operand tile.
 // ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) char lds_char;
 
-// Contraction index contiguous: the matrix is [MN rows][K].  Thread t loads k
-// chunk t%8 of rows t/8 + p*(NT/8), p < LP.  Loads past K or past the last
-// row get an out-of-range offset and read zeros, so the loop needs no branch.
-template <int NT, bool GATED>
+// One 64-lane direct-to-LDS load: lane l's 16 bytes at global `voff` land at
+// LDS byte `dst` + 16 l (dst is wave-uniform and goes through M0).  It is
+// issued from inline assembly so that the compiler does not track it as a
+// pending LDS write: the kernel itself waits (s_waitcnt vmcnt) and synchronises
+// (barrier) before any wave reads the stage it fills, and otherwise the
+// compiler would make every LDS read of the loop wait for all such loads.  No
+// other code in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, lds_char* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)dst);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rs), "s"(m0)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Contraction index contiguous: the matrix is [MN rows][K].  Load p of wave w
+// fills the 1 KiB of tile rows R(LP w + p) .. +R-1 (R = 1024 / 2BK): lane l
+// takes row +l/KCH and the k chunk whose swizzled position is l%KCH.
+template <class KC, int NT, bool GATED>
 struct LoaderKMajor {
-  static constexpr int LP = BM * BK / 8 / NT;
-  static constexpr int RSTEP = NT / 8;            // rows between a thread's loads
-  static_assert(RSTEP % 16 == 0, "swizzle period");
+  static constexpr int LP = KC::OPER_BYTES / 1024 / (NT / 64);
   __amdgpu_buffer_rsrc_t rs;
-  uint32_t base;      // byte offset of (row0 + t/8, 8*(t%8))
-  uint32_t pstride;   // RSTEP rows in bytes
-  uint32_t rowmask;   // bit p: load p's row is inside the matrix
-  int kchunk;         // 8*(t%8)
+  uint32_t gbase[LP];   // byte offset of the lane's row and chunk at k0 = 0
+  int kq[LP];           // k offset of the lane's chunk
+  bool rowok[LP];
   int K;
-  int lds0;
+  int ldsoff;           // wave's first byte within an operand tile
 
   __device__ void init(const void* ptr, uint32_t bytes, int64_t ld, int row0, int rows, int K_,
                        int t, int, int) {
     rs = make_rsrc(ptr, bytes);
-    const int r = t >> 3, c = t & 7;
-    kchunk = c * 8;
     K = K_;
+    const int w = t >> 6, l = t & 63;
     const uint32_t ldb = (uint32_t)(ld * 2);
-    base = (uint32_t)(row0 + r) * ldb + (uint32_t)(kchunk * 2);
-    pstride = (uint32_t)RSTEP * ldb;
-    rowmask = 0;
-#pragma unroll
-    for (int p = 0; p < LP; ++p)
-      if (row0 + p * RSTEP + r < rows) rowmask |= 1u << p;
-    lds0 = kmaj_off(r, c);          // (r + p RSTEP) >> 1 & 7 == r >> 1 & 7
-  }
-  __device__ void load(int k0, u32x4 (&v)[LP]) const {
-    const bool kok = (k0 + kchunk) < K;
 #pragma unroll
     for (int p = 0; p < LP; ++p) {
-      const bool ok = kok && ((rowmask >> p) & 1u);
-      const uint32_t off = ok ? base + p * pstride + (uint32_t)(k0 * 2) : OOB;
-      v[p] = bload16(rs, off);
+      const int m = (1024 / KC::KROW) * (LP * w + p) + l / KC::KCH;
+      const int q = (l % KC::KCH) ^ ((m / KC::KRP) % KC::KCH);
+      kq[p] = 8 * q;
+      rowok[p] = row0 + m < rows;
+      gbase[p] = (uint32_t)(row0 + m) * ldb + (uint32_t)(16 * q);
     }
+    ldsoff = __builtin_amdgcn_readfirstlane(w) * LP * 1024;
   }
-  __device__ void store(char* lds, const u32x4 (&v)[LP]) const {
+  __device__ void issue(lds_char* tile, int k0) const {
 #pragma unroll
-    for (int p = 0; p < LP; ++p) *(u32x4*)(lds + lds0 + p * RSTEP * 128) = v[p];
+    for (int p = 0; p < LP; ++p) {
+      const bool ok = rowok[p] && (k0 + kq[p]) < K;
+      dma16(rs, ok ? gbase[p] + (uint32_t)(k0 * 2) : OOB, tile + ldsoff + p * 1024);
+    }
   }
 };
 
-// Contraction index strided: the matrix is [K rows][MN cols].  Thread t loads
-// MN chunk t%32 (8 columns) of the k rows t/32 + p*(NT/32), p < LP.  GATED
-// maps tile columns onto the [gate | up] halves of a [d, 2F] weight: the tile
-// is cut into groups of TN columns (one wave's width) whose first half holds
-// gate columns j and second half the up columns F + j of the same j, so one
-// lane ends up holding a gate and its up value.
-template <int NT, bool GATED, int TN = 64>
+// Contraction index strided: the matrix is [K rows][MN cols].  Load p of
+// wave w fills tile k rows 2(LP w + p) and +1: lane l takes row +l/32 and the
+// MN chunk whose swizzled position is l%32.  GATED maps tile columns onto the
+// [gate | up] halves of a [d, 2F] weight: the tile is cut into groups of TN
+// columns (one wave's width) whose first half holds gate columns j and second
+// half the up columns F + j of the same j, so one lane ends up holding a gate
+// and its up value.
+template <class KC, int NT, bool GATED, int TN = 64>
 struct LoaderMNMajor {
-  static constexpr int LP = BM * BK / 8 / NT;
-  static constexpr int KSTEP = NT / 32;           // k rows between a thread's loads
-  static_assert(KSTEP % 4 == 0, "swizzle period");
+  static constexpr int LP = KC::OPER_BYTES / 1024 / (NT / 64);
   __amdgpu_buffer_rsrc_t rs;
-  uint32_t base;      // byte offset of (k = t/32, col)
-  uint32_t ldb;       // row pitch in bytes
-  int krow;           // t/32
+  uint32_t gbase[LP];
+  int kk[LP];
+  bool colok[LP];
+  uint32_t ldb;
   int K;
-  bool colok;
-  int lds0;
+  int ldsoff;
 
   __device__ void init(const void* ptr, uint32_t bytes, int64_t ld, int col0, int cols, int K_,
                        int t, int F, int tn) {
     rs = make_rsrc(ptr, bytes);
-    const int q = t >> 5, c = t & 31;
-    krow = q;
     K = K_;
     ldb = (uint32_t)(ld * 2);
-    int col;
-    if (GATED) {
-      constexpr int GH = TN / 2;
-      const int lc = c * 8;                       // tile column 0..255
-      const int grp = lc / TN, sub = lc % TN;
-      const int j = tn * (BN / 2) + grp * GH + (sub % GH);
-      colok = j < F;
-      col = (sub < GH) ? j : F + j;
-    } else {
-      col = col0 + c * 8;
-      colok = col < cols;
-    }
-    base = (uint32_t)krow * ldb + (uint32_t)col * 2u;
-    lds0 = mnmaj_off(q, c);         // (q + p KSTEP) & 3 == q & 3
-  }
-  __device__ void load(int k0, u32x4 (&v)[LP]) const {
+    const int w = t >> 6, l = t & 63;
 #pragma unroll
     for (int p = 0; p < LP; ++p) {
-      const bool ok = colok && (k0 + krow + KSTEP * p) < K;
-      const uint32_t off = ok ? base + (uint32_t)(k0 + KSTEP * p) * ldb : OOB;
-      v[p] = bload16(rs, off);
+      const int k = 2 * (LP * w + p) + (l >> 5);
+      const int c = (l & 31) ^ ((k & 3) << 2);
+      int col;
+      bool ok;
+      if (GATED) {
+        constexpr int GH = TN / 2;
+        const int lc = c * 8;                     // tile column 0..255
+        const int grp = lc / TN, sub = lc % TN;
+        const int j = tn * (BN / 2) + grp * GH + (sub % GH);
+        ok = j < F;
+        col = (sub < GH) ? j : F + j;
+      } else {
+        col = col0 + c * 8;
+        ok = col < cols;
+      }
+      kk[p] = k;
+      colok[p] = ok;
+      gbase[p] = (uint32_t)k * ldb + (uint32_t)col * 2u;
     }
+    ldsoff = __builtin_amdgcn_readfirstlane(w) * LP * 1024;
   }
-  __device__ void store(char* lds, const u32x4 (&v)[LP]) const {
+  __device__ void issue(lds_char* tile, int k0) const {
 #pragma unroll
-    for (int p = 0; p < LP; ++p) *(u32x4*)(lds + lds0 + p * KSTEP * 512) = v[p];
+    for (int p = 0; p < LP; ++p) {
+      const bool ok = colok[p] && (k0 + kk[p]) < K;
+      dma16(rs, ok ? gbase[p] + (uint32_t)k0 * ldb : OOB, tile + ldsoff + p * 1024);
+    }
   }
 };
 
-template <bool KMAJ, int NT, bool GATED, int TN>
+template <bool KMAJ, class KC, int NT, bool GATED, int TN>
 struct LoaderSel;
-template <int NT, bool GATED, int TN>
-struct LoaderSel<true, NT, GATED, TN> { using type = LoaderKMajor<NT, GATED>; };
-template <int NT, bool GATED, int TN>
-struct LoaderSel<false, NT, GATED, TN> { using type = LoaderMNMajor<NT, GATED, TN>; };
+template <class KC, int NT, bool GATED, int TN>
+struct LoaderSel<true, KC, NT, GATED, TN> { using type = LoaderKMajor<KC, NT, GATED>; };
+template <class KC, int NT, bool GATED, int TN>
+struct LoaderSel<false, KC, NT, GATED, TN> { using type = LoaderMNMajor<KC, NT, GATED, TN>; };
 
 // MFMA operand fragments of v_mfma_f32_32x32x16_bf16: lane l supplies row
 // (or column) l%32 of a 32-wide block and the 8 k values 16s + 8(l/32) + 0..7
@@ -237,20 +269,20 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <bool KMAJ, int NB>
+template <bool KMAJ, class KC, int NB>
 struct FragReader;
 
 // K-contiguous tile: one ds_read_b128 per fragment.
-template <int NB>
-struct FragReader<true, NB> {
-  int off[4];   // per sub-step s, for block 0; block i adds 32 rows * 128 B
+template <class KC, int NB>
+struct FragReader<true, KC, NB> {
+  int off[KC::BK / 16];   // per sub-step s, for block 0; block i adds 32 rows
   __device__ void init(int mn0, int lane) {
     const int l32 = lane & 31, khalf = lane >> 5;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) off[s] = kmaj_off(mn0 + l32, 2 * s + khalf);
+    for (int s = 0; s < KC::BK / 16; ++s) off[s] = KC::kmaj_off(mn0 + l32, 2 * s + khalf);
   }
   __device__ bf16x8 read(const char* tile, int s, int i) const {
-    return *(const bf16x8*)(tile + off[s] + i * 4096);
+    return *(const bf16x8*)(tile + off[s] + i * 32 * KC::KROW);
   }
 };
 
@@ -259,8 +291,8 @@ struct FragReader<true, NB> {
 // addressed by source lanes 4k + i/4 (k = 0..3).  Source lane j points at
 // (k row K0 + j/4, columns c0 + 4(j%4)..+3), so output lane i receives
 // column c0 + i at rows K0..K0+3.
-template <int NB>
-struct FragReader<false, NB> {
+template <class KC, int NB>
+struct FragReader<false, KC, NB> {
   int off[NB];  // per block i (32 columns); sub-step s and half h add k rows
   __device__ void init(int mn0, int lane) {
     const int j = lane & 15, khalf = lane >> 5;
@@ -300,13 +332,16 @@ __device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __ex
 // ---------------------------------------------------------------------------
 // The bf16 MFMA GEMM: C[M,N] = A[M,K] B[K,N] (+ epilogue EPI)
 // ---------------------------------------------------------------------------
-template <int WMv, int WNv, bool AK, bool BKM, int EPI>
+template <int WMv, int WNv, int BKv, int NSTv, bool AK, bool BKM, int EPI>
 __global__ void __launch_bounds__(64 * WMv * WNv)
     __attribute__((amdgpu_waves_per_eu(WMv * WNv / 4, WMv * WNv / 4)))
 gemm_bf16_kernel(GemmArgs g) {
   using G = Grid<WMv, WNv>;
-  constexpr int FM = G::FM, FN = G::FN, TM = G::TM, TN = G::TN, LP = G::LP;
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  using KC = KCfg<BKv, NSTv>;
+  constexpr int FM = G::FM, FN = G::FN, TM = G::TM, TN = G::TN;
+  constexpr int BK = KC::BK, NSTAGE = KC::NSTAGE, OPER_BYTES = KC::OPER_BYTES;
+  constexpr int STAGE_BYTES = KC::STAGE_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[KC::LDS_BYTES];
   constexpr bool GATED = (EPI == EPI_SWIGLU);
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6, wm = wave / WNv, wn = wave % WNv;
@@ -317,8 +352,8 @@ gemm_bf16_kernel(GemmArgs g) {
   map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int row0 = tm * BM, col0 = tn * BN;
 
-  typename LoaderSel<AK, G::NT, false, TN>::type la;
-  typename LoaderSel<BKM, G::NT, GATED, TN>::type lb;
+  typename LoaderSel<AK, KC, G::NT, false, TN>::type la;
+  typename LoaderSel<BKM, KC, G::NT, GATED, TN>::type lb;
   la.init(g.A, g.A_bytes, g.lda, row0, g.M, g.K, t, 0, tm);
   lb.init(g.B, g.B_bytes, g.ldb, col0, g.N, g.K, t, g.F, tn);
 
@@ -328,23 +363,31 @@ gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-  // Software pipeline (one K step = four 16-wide MFMA sub-steps):
-  //   s0, s1: MFMAs; the fragments of the next sub-step are read meanwhile
-  //   s2:     the next tile, already in registers, is written to the free
-  //           LDS stage; the global loads two steps ahead are issued into
-  //           the same registers (a full K step of latency cover)
-  //   s3:     barrier, then the next stage's first fragments are read while
-  //           the last MFMAs of this step run.
-  // Fragments are double-buffered in registers.  Loads past K read zeros,
-  // so the loop has no branches.
+  // Software pipeline over a ring of NSTAGE LDS stages (one K step = BK/16
+  // MFMA sub-steps of 16):
+  //   - the direct-to-LDS loads of step k+NSTAGE-1 are issued at the start of
+  //     step k into the stage step k-1 used (free since the barrier that ended
+  //     step k-1);
+  //   - each sub-step issues the MFMAs of its fragments while the fragments
+  //     of the next sub-step are read;
+  //   - before the last sub-step's MFMAs: wait until this wave's loads of
+  //     step k+1 have landed, barrier (all waves' loads of step k+1 are then
+  //     in LDS, and every wave is done reading step k-1's stage), and read
+  //     step k+1's first fragments while the last MFMAs of step k run.
+  // Fragments are double-buffered in registers.  Loads past K read zeros.
   const int nk = (g.K + BK - 1) / BK;
-  const int l32 = lane & 31;
-  FragReader<AK, FM> fra;
-  FragReader<BKM, FN> frb;
+  FragReader<AK, KC, FM> fra;
+  FragReader<BKM, KC, FN> frb;
   fra.init(wm * TM, lane);
   frb.init(wn * TN, lane);
-  u32x4 ra[LP], rb[LP];
   bf16x8 fa[2][FM], fb[2][FN];
+  lds_char* lsm = (lds_char*)smem;
+  constexpr int NSUB = BK / 16;
+  constexpr int LPW = OPER_BYTES / 1024 / (G::NT / 64) * 2;   // loads per wave per step
+  constexpr int VM_NEXT = (NSTAGE - 2) * LPW;                 // loads allowed in flight
+  static_assert(VM_NEXT < 64, "vmcnt range");
+  // s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 (7 and 15 = no wait)
+  constexpr int WAIT_NEXT = (VM_NEXT & 15) | ((VM_NEXT >> 4) << 14) | (7 << 4) | (15 << 8);
 
   auto read_frags = [&](const char* stage, int s, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
 #pragma unroll
@@ -359,38 +402,34 @@ gemm_bf16_kernel(GemmArgs g) {
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
   };
+  auto issue = [&](int step) {
+    lds_char* st = lsm + (step % NSTAGE) * STAGE_BYTES;
+    la.issue(st, step * BK);
+    lb.issue(st + OPER_BYTES, step * BK);
+  };
 
-  la.load(0, ra);
-  lb.load(0, rb);
-  la.store(smem, ra);
-  lb.store(smem + OPER_BYTES, rb);
-  la.load(BK, ra);
-  lb.load(BK, rb);
+#pragma unroll
+  for (int st = 0; st < NSTAGE - 1; ++st) issue(st);
+  __builtin_amdgcn_s_waitcnt(WAIT_NEXT);     // step 0 has landed
   __syncthreads();
   read_frags(smem, 0, fa[0], fb[0]);
-  int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const char* sc = smem + cur * STAGE_BYTES;
-    char* sn = smem + (cur ^ 1) * STAGE_BYTES;
-    read_frags(sc, 1, fa[1], fb[1]);
-    mfmas(fa[0], fb[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(sc, 2, fa[0], fb[0]);
-    mfmas(fa[1], fb[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(sc, 3, fa[1], fb[1]);
-    la.store(sn, ra);
-    lb.store(sn + OPER_BYTES, rb);
-    la.load((kt + 2) * BK, ra);
-    lb.load((kt + 2) * BK, rb);
-    mfmas(fa[0], fb[0]);
-    __builtin_amdgcn_sched_barrier(0);
+    const char* sc = smem + (kt % NSTAGE) * STAGE_BYTES;
+    const char* sn = smem + ((kt + 1) % NSTAGE) * STAGE_BYTES;
+    issue(kt + NSTAGE - 1);
+#pragma unroll
+    for (int s = 0; s + 1 < NSUB; ++s) {
+      read_frags(sc, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      mfmas(fa[s & 1], fb[s & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(WAIT_NEXT);   // this wave's loads of step kt+1 have landed
     __syncthreads();
     read_frags(sn, 0, fa[0], fb[0]);
-    mfmas(fa[1], fb[1]);
+    mfmas(fa[(NSUB - 1) & 1], fb[(NSUB - 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
-    cur ^= 1;
   }
+  __builtin_amdgcn_s_waitcnt(0);             // no load may still write into LDS
 
   // ------------------------------ epilogue ------------------------------
   // The accumulators are moved, 32 rows (one block row i) at a time, through
@@ -401,6 +440,7 @@ gemm_bf16_kernel(GemmArgs g) {
   // 8 lanes cover one 128-byte row segment.  Only the cross-wave reductions
   // need a workgroup barrier.
   static_assert(TN == 64 && FN == 2, "row-major epilogue assumes 64-column wave tiles");
+  const int l32 = lane & 31;
   __syncthreads();                                  // main loop done: LDS is free
   char* region = smem + wave * 8192;
   float* red = (float*)(smem + 8 * 8192);           // [WN][BM] row partials
@@ -748,10 +788,13 @@ constexpr int kWavesM = 2, kWavesN = 4;
 
 template <bool AK, bool BKM, int EPI>
 static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
+  // K step / ring depth: 64 x 2 when an operand is K-contiguous, else 32 x 4
+  constexpr int BKv = (AK || BKM) ? 64 : 32;
+  constexpr int NSTv = (AK || BKM) ? 2 : 4;
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (EPI == EPI_SWIGLU) ? (g.N + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<kWavesM, kWavesN, AK, BKM, EPI>), dim3(tiles_m * tiles_n),
-                     dim3(64 * kWavesM * kWavesN), 0, s, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<kWavesM, kWavesN, BKv, NSTv, AK, BKM, EPI>),
+                     dim3(tiles_m * tiles_n), dim3(64 * kWavesM * kWavesN), 0, s, g);
   return hipGetLastError();
 }
 
