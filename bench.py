@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused torch baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 5 times (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
 
 
@@ -294,6 +297,16 @@ def main():
     from gemm_epilogue_fusion_gemm1_amd import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": 5}), flush=True)
+        return
     coda.load_library()
     unfused = not args.no_unfused
     w = synth.WORKLOADS[args.workload]

@@ -97,6 +97,12 @@ __device__ __forceinline__ __bf16 f2bf(float f) { return (__bf16)f; }  // round 
 // XCDs (wg % 8), each with its own L2; consecutive logical tiles are given to
 // one XCD so that the tiles resident on an XCD share operand rows/columns.
 // Within that order, groups of GM tile-rows are walked column by column.
+#ifndef CODA_SCHED
+#define CODA_SCHED 0
+#endif
+#ifndef CODA_SETPRIO
+#define CODA_SETPRIO 0
+#endif
 #ifndef CODA_TILE_GROUP_M
 #define CODA_TILE_GROUP_M 8
 #endif
@@ -402,6 +408,33 @@ gemm_bf16_kernel(GemmArgs g) {
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
   };
+  // Scheduling hints for one sub-step region (reads of the next fragments +
+  // MFMAs of the current ones): interleave one LDS read with one MFMA so the
+  // reads are issued early in the sub-step.
+  constexpr int NREAD = FM * (AK ? 1 : 2) + FN * (BKM ? 1 : 2);
+  constexpr int NMFMA = FM * FN;
+  auto sched_sub = [&]() {
+#if CODA_SCHED == 1
+    constexpr int NPAIR = NREAD < NMFMA ? NREAD : NMFMA;
+#pragma unroll
+    for (int x = 0; x < NPAIR; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    }
+    if (NREAD > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NPAIR, 0);
+    if (NMFMA > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NPAIR, 0);
+#endif
+  };
+  auto prio_hi = [&]() {
+#if CODA_SETPRIO == 1
+    __builtin_amdgcn_s_setprio(1);
+#endif
+  };
+  auto prio_lo = [&]() {
+#if CODA_SETPRIO == 1
+    __builtin_amdgcn_s_setprio(0);
+#endif
+  };
   auto issue = [&](int step) {
     lds_char* st = lsm + (step % NSTAGE) * STAGE_BYTES;
     la.issue(st, step * BK);
@@ -420,13 +453,19 @@ gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int s = 0; s + 1 < NSUB; ++s) {
       read_frags(sc, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      prio_hi();
       mfmas(fa[s & 1], fb[s & 1]);
+      prio_lo();
+      sched_sub();
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(WAIT_NEXT);   // this wave's loads of step kt+1 have landed
     __syncthreads();
     read_frags(sn, 0, fa[0], fb[0]);
+    prio_hi();
     mfmas(fa[(NSUB - 1) & 1], fb[(NSUB - 1) & 1]);
+    prio_lo();
+    sched_sub();
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_waitcnt(0);             // no load may still write into LDS
@@ -784,7 +823,10 @@ __global__ void dy_n_kernel(__bf16* __restrict__ dR, __bf16* __restrict__ n,
 // Launchers
 // ---------------------------------------------------------------------------
 // Wave grid used for every bf16 GEMM: 2 x 4 waves (two per SIMD).
-constexpr int kWavesM = 2, kWavesN = 4;
+#ifndef CODA_WAVES_M
+#define CODA_WAVES_M 2
+#endif
+constexpr int kWavesM = CODA_WAVES_M, kWavesN = 8 / CODA_WAVES_M;
 
 template <bool AK, bool BKM, int EPI>
 static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
