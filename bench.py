@@ -70,7 +70,7 @@ class CodaCase:
         self.dg = torch.empty((d,), dtype=torch.float32, device=dev)
         self.wsf = torch.empty(coda.fwd_workspace_bytes(1, M, K, d, N), dtype=torch.uint8, device=dev)
         self.wsb = torch.empty(coda.bwd_workspace_bytes(1, M, K, d, N), dtype=torch.uint8, device=dev)
-        self.kernels_per_step = 10
+        self.kernels_per_step = 8
 
     def flops(self):
         return self.w.flops_fwd() + self.w.flops_bwd()

@@ -82,16 +82,19 @@ hipError_t traced(const char* name, double flops, double bytes, hipStream_t s, F
 double gemm_flops(int64_t M, int64_t N, int64_t K) { return 2.0 * (double)M * (double)N * (double)K; }
 
 // ------------------------------------------------------------- workspaces
+// Forward workspace: P [M, Tn] fp32 partial sums of squares, yg [M, d] = y * gamma
+// (the second GEMM's A operand, written by the first GEMM's epilogue).
 struct FwdWs {
-  size_t P, W2f, total;
+  size_t P, yg, total;
   int Tn;
 };
 FwdWs fwd_ws(coda_dtype t, int64_t M, int64_t d, int64_t N) {
+  (void)N;
   FwdWs w;
   w.Tn = (int)cdiv(d, t == CODA_BF16 ? coda::kTileN : coda::kTileF32);
   w.P = 0;
-  w.W2f = round_up((size_t)M * w.Tn * 4);
-  w.total = w.W2f + round_up((size_t)d * N * esize(t));
+  w.yg = round_up((size_t)M * w.Tn * 4);
+  w.total = w.yg + round_up((size_t)M * d * esize(t));
   return w;
 }
 
@@ -183,36 +186,49 @@ coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
   hipStream_t s = (hipStream_t)stream;
   char* wsb = (char*)workspace;
   float* P = (float*)(wsb + ws.P);
-  void* W2f = wsb + ws.W2f;
+  void* yg = wsb + ws.yg;
   hipError_t err;
   const double eb = (double)e;
-  if ((err = traced("fold_gamma", 0.0, 2.0 * d * N * eb + d * eb, s, [&] {
-         return coda::launch_fold_gamma(dtype == CODA_BF16, gamma, W2, W2f, d, N, s);
-       })) != hipSuccess)
-    return hip_status(err);
 
+  // K1: y = X W1 + R; epilogue stores y, yg = y * gamma and the partial sums of squares
   GemmArgs g1 = gemm(M, d, K, X, K, M * K, W1, d, K * d, y, d);
   g1.E = R;
   g1.lde = d;
   g1.part_row = P;
   g1.ld_part_row = ws.Tn;
-  GemmArgs g2 = gemm(M, N, d, y, d, M * d, W2f, N, d * N, z, N);
-  g2.vrow = r;
+  g1.C2 = yg;
+  g1.ldc2 = d;
+  g1.vcol = gamma;
+  // K2: z = diag(r) (yg W2)
+  GemmArgs g2 = gemm(M, N, d, yg, d, M * d, W2, N, d * N, z, N);
   const bool bf = dtype == CODA_BF16;
-  const double k1_bytes = (M * K + K * d + 2.0 * M * d) * eb + M * ws.Tn * 4.0;
+  const double k1_bytes = (M * K + K * d + 3.0 * M * d + d) * eb + M * ws.Tn * 4.0;
   if ((err = traced("k1_gemm_resid_sumsq", gemm_flops(M, d, K), k1_bytes, s, [&] {
          return bf ? coda::launch_gemm_bf16(g1, true, false, coda::EPI_RESID_SUMSQ, s)
                    : coda::launch_gemm_f32(g1, coda::EPI_RESID_SUMSQ, s);
        })) != hipSuccess)
     return hip_status(err);
+  const double k2_bytes = (M * d + d * N + M * N) * eb + M * ws.Tn * 4.0 + M * 4.0;
+  if (bf) {
+    // r is formed in K2's epilogue from the partial sums (and written by the
+    // tiles of the first column)
+    g2.part_row = P;
+    g2.ld_part_row = ws.Tn;
+    g2.nparts = ws.Tn;
+    g2.inv_d = 1.0f / (float)d;
+    g2.eps = eps;
+    g2.r_out = r;
+    return hip_status(traced("k2_gemm_rsqrt_rowscale", gemm_flops(M, N, d), k2_bytes, s, [&] {
+      return coda::launch_gemm_bf16(g2, true, false, coda::EPI_RSQRT_SCALE, s);
+    }));
+  }
   if ((err = traced("r1_row_rsqrt", 0.0, M * ws.Tn * 4.0 + M * 4.0, s, [&] {
          return coda::launch_row_rsqrt(P, ws.Tn, ws.Tn, M, d, eps, r, s);
        })) != hipSuccess)
     return hip_status(err);
-  const double k2_bytes = (M * d + d * N + M * N) * eb + M * 4.0;
+  g2.vrow = r;
   return hip_status(traced("k2_gemm_rowscale", gemm_flops(M, N, d), k2_bytes, s, [&] {
-    return bf ? coda::launch_gemm_bf16(g2, true, false, coda::EPI_ROWSCALE, s)
-              : coda::launch_gemm_f32(g2, coda::EPI_ROWSCALE, s);
+    return coda::launch_gemm_f32(g2, coda::EPI_ROWSCALE, s);
   }));
 }
 
@@ -268,9 +284,11 @@ coda_status coda_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
   b1.ld_part_row = ws.Tn;
   b1.part_col = G;
   b1.ld_part_col = d;
+  b1.C2 = n;                      // n = r * y, the A operand of the dW2 GEMM
+  b1.ldc2 = d;
   const double md = 2.0 * M * d, dn2 = 2.0 * d * N, mn = 2.0 * M * N, mk = 2.0 * M * K, kd = 2.0 * K * d;
   if ((err = traced("b1_gemm_dh_epilogue", gemm_flops(M, d, N),
-                    mn + dn2 + 2.0 * md + M * ws.Tn * 4.0 + ws.Tm * d * 4.0 + M * 4.0 + 2.0 * d, s,
+                    mn + dn2 + 3.0 * md + M * ws.Tn * 4.0 + ws.Tm * d * 4.0 + M * 4.0 + 2.0 * d, s,
                     [&] { return coda::launch_gemm_bf16(b1, true, true, coda::EPI_DN, s); })) !=
       hipSuccess)
     return hip_status(err);
@@ -281,9 +299,9 @@ coda_status coda_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
                                                      s);
                     })) != hipSuccess)
     return hip_status(err);
-  // E2: dR = r dn - c y (in place), n = r y
-  if ((err = traced("e2_dy_n", 0.0, 4.0 * md + 8.0 * M, s,
-                    [&] { return coda::launch_dy_n(dR, n, y, r, c, M, d, s); })) != hipSuccess)
+  // E2: dR = r dn - c y (in place)
+  if ((err = traced("e2_dy", 0.0, 3.0 * md + 8.0 * M, s,
+                    [&] { return coda::launch_dy(dR, y, r, c, M, d, s); })) != hipSuccess)
     return hip_status(err);
   // B2: dW2 = diag(gamma) n^T dz
   GemmArgs b2 = gemm(d, N, M, n, d, M * d, dz, N, M * N, dW2, N);

@@ -517,11 +517,29 @@ gemm_bf16_kernel(GemmArgs g) {
   };
 
   if constexpr (EPI == EPI_STORE || EPI == EPI_ROWSCALE || EPI == EPI_RESID_SUMSQ ||
-                EPI == EPI_DN || EPI == EPI_SWIGLU_BWD) {
+                EPI == EPI_DN || EPI == EPI_SWIGLU_BWD || EPI == EPI_RSQRT_SCALE) {
     __bf16* C = (__bf16*)g.C;
     f32x4 glo{}, ghi{}, clo{0.f, 0.f, 0.f, 0.f}, chi{0.f, 0.f, 0.f, 0.f};
-    if constexpr (EPI == EPI_DN) {
-      if (colok) ld8((const __bf16*)g.vcol + gcol, glo, ghi);
+    if constexpr (EPI == EPI_DN || EPI == EPI_RESID_SUMSQ) {
+      if (colok && g.vcol) ld8((const __bf16*)g.vcol + gcol, glo, ghi);
+    }
+    float* rrow = red + WNv * BM + WMv * BN;        // [BM] row scales (EPI_RSQRT_SCALE)
+    if constexpr (EPI == EPI_RSQRT_SCALE) {
+      // r for the tile's rows from the first GEMM's partial sums, summed in
+      // the same order as the stand-alone reduction kernel
+      if (t < BM) {
+        const int row = row0 + t;
+        float r = 0.0f;
+        if (row < g.M) {
+          const float* P = g.part_row + (int64_t)row * g.ld_part_row;
+          float sp = 0.0f;
+          for (int k = 0; k < g.nparts; ++k) sp += P[k];
+          r = 1.0f / sqrtf(sp * g.inv_d + g.eps);
+          if (tn == 0) g.r_out[row] = r;
+        }
+        rrow[t] = r;
+      }
+      __syncthreads();
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -543,6 +561,11 @@ gemm_bf16_kernel(GemmArgs g) {
             const float sc = g.vrow ? g.vrow[row] : bf2f(((const __bf16*)g.vcol)[row]);
             st8(C + o, lo * sc, hi * sc);
           }
+        } else if constexpr (EPI == EPI_RSQRT_SCALE) {
+          if (ok) {
+            const float sc = rrow[lrow_t];
+            st8(C + o, lo * sc, hi * sc);
+          }
         } else if constexpr (EPI == EPI_RESID_SUMSQ) {
           float s = 0.0f;
           if (ok) {
@@ -551,6 +574,7 @@ gemm_bf16_kernel(GemmArgs g) {
             lo += elo;
             hi += ehi;
             st8(C + o, lo, hi);
+            if (g.C2) st8((__bf16*)g.C2 + (int64_t)row * g.ldc2 + gcol, lo * glo, hi * ghi);
             const f32x4 sq = lo * lo + hi * hi;
             s = sq[0] + sq[1] + sq[2] + sq[3];
           }
@@ -565,6 +589,7 @@ gemm_bf16_kernel(GemmArgs g) {
             const float rv = g.vrow[row];
             const f32x4 dlo = lo * glo, dhi = hi * ghi;
             st8(C + o, dlo, dhi);
+            if (g.C2) st8((__bf16*)g.C2 + (int64_t)row * g.ldc2 + gcol, ylo * rv, yhi * rv);
             const f32x4 sp = dlo * ylo + dhi * yhi;
             s = sp[0] + sp[1] + sp[2] + sp[3];
             clo += lo * ylo * rv;
@@ -723,6 +748,7 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
         if constexpr (EPI == EPI_RESID_SUMSQ) {
           v += ((const float*)g.E)[(int64_t)row * g.lde + col];
           s += v * v;
+          if (g.C2) ((float*)g.C2)[(int64_t)row * g.ldc2 + col] = v * ((const float*)g.vcol)[col];
         } else if constexpr (EPI == EPI_ROWSCALE) {
           v *= g.vrow[row];
         }
@@ -745,30 +771,6 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // Small kernels
 // ---------------------------------------------------------------------------
-__global__ void fold_gamma_bf16(const __bf16* __restrict__ gamma, const __bf16* __restrict__ W2,
-                                __bf16* __restrict__ W2f, int64_t d, int64_t N) {
-  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // one 8-element chunk
-  const int64_t e0 = v * 8;
-  if (e0 >= d * N) return;
-  const int64_t j = e0 / N;
-  const float gj = bf2f(gamma[j]);
-  const bf16x8 w = *(const bf16x8*)(W2 + e0);
-  bf16x8 o;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) o[k] = f2bf(gj * bf2f(w[k]));
-  *(bf16x8*)(W2f + e0) = o;
-}
-
-__global__ void fold_gamma_f32(const float* __restrict__ gamma, const float* __restrict__ W2,
-                               float* __restrict__ W2f, int64_t d, int64_t N) {
-  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t e0 = v * 4;
-  if (e0 >= d * N) return;
-  const float gj = gamma[e0 / N];
-  f32x4 w = *(const f32x4*)(W2 + e0);
-  *(f32x4*)(W2f + e0) = w * gj;
-}
-
 __global__ void row_rsqrt_kernel(const float* __restrict__ P, int64_t ldp, int T, int64_t M,
                                  float inv_d, float eps, float* __restrict__ r) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -796,9 +798,9 @@ __global__ void bwd_reduce_kernel(const float* __restrict__ S, int64_t lds, int 
   }
 }
 
-__global__ void dy_n_kernel(__bf16* __restrict__ dR, __bf16* __restrict__ n,
-                            const __bf16* __restrict__ y, const float* __restrict__ r,
-                            const float* __restrict__ c, int64_t M, int64_t d) {
+__global__ void dy_kernel(__bf16* __restrict__ dR, const __bf16* __restrict__ y,
+                          const float* __restrict__ r, const float* __restrict__ c, int64_t M,
+                          int64_t d) {
   const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t e0 = v * 8;
   if (e0 >= M * d) return;
@@ -806,15 +808,10 @@ __global__ void dy_n_kernel(__bf16* __restrict__ dR, __bf16* __restrict__ n,
   const float ri = r[i], ci = c[i];
   const bf16x8 dn = *(const bf16x8*)(dR + e0);
   const bf16x8 yv = *(const bf16x8*)(y + e0);
-  bf16x8 o, nn;
+  bf16x8 o;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float yk = bf2f(yv[k]);
-    o[k] = f2bf(ri * bf2f(dn[k]) - ci * yk);
-    nn[k] = f2bf(ri * yk);
-  }
+  for (int k = 0; k < 8; ++k) o[k] = f2bf(ri * bf2f(dn[k]) - ci * bf2f(yv[k]));
   *(bf16x8*)(dR + e0) = o;
-  *(bf16x8*)(n + e0) = nn;
 }
 
 }  // namespace
@@ -849,7 +846,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStr
     switch (epi) {
       case EPI_STORE: return launch_one<true, false, EPI_STORE>(g, s);
       case EPI_RESID_SUMSQ: return launch_one<true, false, EPI_RESID_SUMSQ>(g, s);
-      case EPI_ROWSCALE: return launch_one<true, false, EPI_ROWSCALE>(g, s);
+      case EPI_RSQRT_SCALE: return launch_one<true, false, EPI_RSQRT_SCALE>(g, s);
       case EPI_SWIGLU: return launch_one<true, false, EPI_SWIGLU>(g, s);
       default: break;
     }
@@ -888,20 +885,6 @@ hipError_t launch_gemm_f32(const GemmArgs& g, Epi epi, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_fold_gamma(bool bf16, const void* gamma, const void* W2, void* W2f, int64_t d,
-                             int64_t N, hipStream_t s) {
-  const int per = bf16 ? 8 : 4;
-  const int64_t chunks = (d * N) / per;
-  const int blocks = (int)((chunks + 255) / 256);
-  if (bf16)
-    hipLaunchKernelGGL(fold_gamma_bf16, dim3(blocks), dim3(256), 0, s, (const __bf16*)gamma,
-                       (const __bf16*)W2, (__bf16*)W2f, d, N);
-  else
-    hipLaunchKernelGGL(fold_gamma_f32, dim3(blocks), dim3(256), 0, s, (const float*)gamma,
-                       (const float*)W2, (float*)W2f, d, N);
-  return hipGetLastError();
-}
-
 hipError_t launch_row_rsqrt(const float* P, int64_t ldp, int T, int64_t M, int64_t d, float eps,
                             float* r, hipStream_t s) {
   hipLaunchKernelGGL(row_rsqrt_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, P, ldp,
@@ -917,11 +900,11 @@ hipError_t launch_bwd_reduce(const float* S, int64_t lds, int Tn, const float* r
   return hipGetLastError();
 }
 
-hipError_t launch_dy_n(void* dR, void* n, const void* y, const float* r, const float* c,
-                       int64_t M, int64_t d, hipStream_t s) {
+hipError_t launch_dy(void* dR, const void* y, const float* r, const float* c, int64_t M, int64_t d,
+                     hipStream_t s) {
   const int64_t chunks = (M * d) / 8;
-  hipLaunchKernelGGL(dy_n_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
-                     (__bf16*)dR, (__bf16*)n, (const __bf16*)y, r, c, M, d);
+  hipLaunchKernelGGL(dy_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
+                     (__bf16*)dR, (const __bf16*)y, r, c, M, d);
   return hipGetLastError();
 }
 

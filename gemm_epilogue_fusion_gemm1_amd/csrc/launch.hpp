@@ -16,11 +16,15 @@ constexpr int kTileF32 = 64;
 // Epilogue selector of the GEMM kernels.
 enum Epi : int {
   EPI_STORE = 0,       // C = acc
-  EPI_RESID_SUMSQ = 1, // y = acc + E; C = y; part_row[i][tile_n] = sum_{j in tile} y_ij^2
-  EPI_ROWSCALE = 2,    // C = vrow[i] * acc
-  EPI_DN = 3,          // dh = acc; C = dn = gamma_j dh; part_row = sum_j dn*y; part_col = sum_i dh*r*y
+  EPI_RESID_SUMSQ = 1, // y = acc + E; C = y; part_row[i][tile_n] = sum_{j in tile} y_ij^2;
+                       // if C2: C2 = y * vcol (the RMSNorm weight, by column)
+  EPI_ROWSCALE = 2,    // C = vrow[i] * acc  (vrow NULL: vcol[i], bf16)
+  EPI_DN = 3,          // dh = acc; C = dn = gamma_j dh; part_row = sum_j dn*y; part_col = sum_i dh*r*y;
+                       // if C2: C2 = n = r_i y
   EPI_SWIGLU = 4,      // gate/up pair: C = gu (both halves), C2 = silu(g) * u
   EPI_SWIGLU_BWD = 5,  // da = acc; C = dgu from the saved gu in E
+  EPI_RSQRT_SCALE = 6, // r_i = (sum_t part_row[i][t] * inv_d + eps)^-1/2; C = r_i acc;
+                       // tiles of column 0 write r to r_out
 };
 
 // Operand layouts.  "K-major" = the contraction index is contiguous in memory.
@@ -36,6 +40,7 @@ struct GemmArgs {
   float* part_row; int64_t ld_part_row;   // [M][tiles_n]
   float* part_col; int64_t ld_part_col;   // [tiles_m][N]
   int F;                         // SwiGLU half width (gate columns)
+  int nparts; float inv_d; float eps; float* r_out;   // EPI_RSQRT_SCALE
   uint32_t A_bytes, B_bytes;     // buffer extents for hardware bounds checks
 };
 
@@ -46,9 +51,6 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool a_kmajor, bool b_kmajor, Epi
                             hipStream_t stream);
 hipError_t launch_gemm_f32(const GemmArgs& g, Epi epi, hipStream_t stream);
 
-// W2f[j][n] = gamma[j] * W2[j][n] (rounded to the element type).
-hipError_t launch_fold_gamma(bool bf16, const void* gamma, const void* W2, void* W2f,
-                             int64_t d, int64_t N, hipStream_t stream);
 // r[i] = (sum_t P[i][t] / d + eps)^(-1/2)
 hipError_t launch_row_rsqrt(const float* P, int64_t ldp, int T, int64_t M, int64_t d, float eps,
                             float* r, hipStream_t stream);
@@ -56,8 +58,8 @@ hipError_t launch_row_rsqrt(const float* P, int64_t ldp, int T, int64_t M, int64
 hipError_t launch_bwd_reduce(const float* S, int64_t lds, int Tn, const float* r, int64_t M,
                              int64_t d, const float* G, int Tm, float* c, float* dgamma,
                              hipStream_t stream);
-// in place: dR[i][j] = r_i dR[i][j] - c_i y[i][j]  (dR holds dn on entry);  n = r_i y
-hipError_t launch_dy_n(void* dR, void* n, const void* y, const float* r, const float* c,
-                       int64_t M, int64_t d, hipStream_t stream);
+// in place: dR[i][j] = r_i dR[i][j] - c_i y[i][j]  (dR holds dn on entry)
+hipError_t launch_dy(void* dR, const void* y, const float* r, const float* c, int64_t M, int64_t d,
+                     hipStream_t stream);
 
 }  // namespace coda

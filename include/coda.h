@@ -78,8 +78,10 @@ const char* coda_version(void);
  *   r_i = (mean_j y_ij^2 + eps)^(-1/2)   (from per-tile partial sums of
  *                                         squares left by the first GEMM's
  *                                         epilogue, combined by a small kernel)
- *   z = diag(r) (y (diag(gamma) W2))     (second GEMM with gamma folded into
- *                                         W2 and r applied in its epilogue)
+ *   z = diag(r) ((y diag(gamma)) W2)     (second GEMM; gamma is applied in
+ *                                         the first GEMM's epilogue, which also
+ *                                         writes y * gamma, and r in the second
+ *                                         GEMM's epilogue)
  * which equals RMSNorm(y) * gamma @ W2 up to rounding.
  *
  *   X     [M,K]  in      W1 [K,d] in     R [M,d] in (residual)
@@ -90,8 +92,8 @@ const char* coda_version(void);
  *   z     [M,N]  out
  *   eps   > 0, finite
  *   workspace: >= coda_fwd_workspace_bytes(dtype, M, K, d, N) bytes, device,
- *              16-byte aligned, contents ignored; holds the partial sums and
- *              the folded weight diag(gamma) W2 during the call.
+ *              16-byte aligned, contents ignored; holds the partial sums
+ *              [M, ceil(d/256)] (fp32) and y * gamma [M, d] during the call.
  * Outputs must not overlap inputs, each other or the workspace.
  * ---------------------------------------------------------------------- */
 size_t coda_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N);
