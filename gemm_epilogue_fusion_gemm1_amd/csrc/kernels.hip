@@ -97,12 +97,6 @@ __device__ __forceinline__ __bf16 f2bf(float f) { return (__bf16)f; }  // round 
 // XCDs (wg % 8), each with its own L2; consecutive logical tiles are given to
 // one XCD so that the tiles resident on an XCD share operand rows/columns.
 // Within that order, groups of GM tile-rows are walked column by column.
-#ifndef CODA_SCHED
-#define CODA_SCHED 0
-#endif
-#ifndef CODA_SETPRIO
-#define CODA_SETPRIO 0
-#endif
 #ifndef CODA_TILE_GROUP_M
 #define CODA_TILE_GROUP_M 8
 #endif
@@ -169,14 +163,19 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, 
 
 // Contraction index contiguous: the matrix is [MN rows][K].  Load p of wave w
 // fills the 1 KiB of tile rows R(LP w + p) .. +R-1 (R = 1024 / 2BK): lane l
-// takes row +l/KCH and the k chunk whose swizzled position is l%KCH.
+// takes row +l/KCH and the k chunk whose swizzled position is l%KCH.  The
+// swizzle repeats every two loads, so a lane keeps one base offset and one
+// chunk per load parity and derives the rest.
 template <class KC, int NT, bool GATED>
 struct LoaderKMajor {
   static constexpr int LP = KC::OPER_BYTES / 1024 / (NT / 64);
+  static constexpr int R = 1024 / KC::KROW;       // tile rows per load
+  static_assert(LP % 2 == 0 && (2 * R / KC::KRP) % KC::KCH == 0, "swizzle period");
   __amdgpu_buffer_rsrc_t rs;
-  uint32_t gbase[LP];   // byte offset of the lane's row and chunk at k0 = 0
-  int kq[LP];           // k offset of the lane's chunk
-  bool rowok[LP];
+  uint32_t gbase[2];    // byte offset of the lane's row and chunk at k0 = 0 (loads 0 and 1)
+  int kq[2];            // k offset of the lane's chunk (even / odd loads)
+  int row;              // the lane's row in load 0, minus the row count
+  uint32_t pair;        // bytes between loads p and p + 2
   int K;
   int ldsoff;           // wave's first byte within an operand tile
 
@@ -187,50 +186,51 @@ struct LoaderKMajor {
     const int w = t >> 6, l = t & 63;
     const uint32_t ldb = (uint32_t)(ld * 2);
 #pragma unroll
-    for (int p = 0; p < LP; ++p) {
-      const int m = (1024 / KC::KROW) * (LP * w + p) + l / KC::KCH;
+    for (int p = 0; p < 2; ++p) {
+      const int m = R * (LP * w + p) + l / KC::KCH;
       const int q = (l % KC::KCH) ^ ((m / KC::KRP) % KC::KCH);
       kq[p] = 8 * q;
-      rowok[p] = row0 + m < rows;
       gbase[p] = (uint32_t)(row0 + m) * ldb + (uint32_t)(16 * q);
     }
+    row = row0 + R * LP * w + l / KC::KCH - rows;
+    pair = 2u * R * ldb;
     ldsoff = __builtin_amdgcn_readfirstlane(w) * LP * 1024;
   }
   __device__ void issue(lds_char* tile, int k0) const {
 #pragma unroll
     for (int p = 0; p < LP; ++p) {
-      const bool ok = rowok[p] && (k0 + kq[p]) < K;
-      dma16(rs, ok ? gbase[p] + (uint32_t)(k0 * 2) : OOB, tile + ldsoff + p * 1024);
+      const bool ok = (row + R * p) < 0 && (k0 + kq[p & 1]) < K;
+      dma16(rs, ok ? gbase[p & 1] + (uint32_t)(p >> 1) * pair + (uint32_t)(k0 * 2) : OOB,
+            tile + ldsoff + p * 1024);
     }
   }
 };
 
 // Contraction index strided: the matrix is [K rows][MN cols].  Load p of
 // wave w fills tile k rows 2(LP w + p) and +1: lane l takes row +l/32 and the
-// MN chunk whose swizzled position is l%32.  GATED maps tile columns onto the
-// [gate | up] halves of a [d, 2F] weight: the tile is cut into groups of TN
-// columns (one wave's width) whose first half holds gate columns j and second
-// half the up columns F + j of the same j, so one lane ends up holding a gate
-// and its up value.
+// MN chunk whose swizzled position is l%32 (the swizzle repeats every two
+// loads).  GATED maps tile columns onto the [gate | up] halves of a [d, 2F]
+// weight: the tile is cut into groups of TN columns (one wave's width) whose
+// first half holds gate columns j and second half the up columns F + j of the
+// same j, so one lane ends up holding a gate and its up value.
 template <class KC, int NT, bool GATED, int TN = 64>
 struct LoaderMNMajor {
   static constexpr int LP = KC::OPER_BYTES / 1024 / (NT / 64);
+  static_assert(LP % 2 == 0, "swizzle period");
   __amdgpu_buffer_rsrc_t rs;
-  uint32_t gbase[LP];
-  int kk[LP];
-  bool colok[LP];
+  uint32_t gbase[2];    // loads 0 and 1 at k0 = 0
+  bool colok[2];
+  int krow;             // the lane's k row in load 0, minus K
   uint32_t ldb;
-  int K;
   int ldsoff;
 
   __device__ void init(const void* ptr, uint32_t bytes, int64_t ld, int col0, int cols, int K_,
                        int t, int F, int tn) {
     rs = make_rsrc(ptr, bytes);
-    K = K_;
     ldb = (uint32_t)(ld * 2);
     const int w = t >> 6, l = t & 63;
 #pragma unroll
-    for (int p = 0; p < LP; ++p) {
+    for (int p = 0; p < 2; ++p) {
       const int k = 2 * (LP * w + p) + (l >> 5);
       const int c = (l & 31) ^ ((k & 3) << 2);
       int col;
@@ -246,17 +246,18 @@ struct LoaderMNMajor {
         col = col0 + c * 8;
         ok = col < cols;
       }
-      kk[p] = k;
       colok[p] = ok;
       gbase[p] = (uint32_t)k * ldb + (uint32_t)col * 2u;
     }
+    krow = 2 * LP * w + (l >> 5) - K_;
     ldsoff = __builtin_amdgcn_readfirstlane(w) * LP * 1024;
   }
   __device__ void issue(lds_char* tile, int k0) const {
 #pragma unroll
     for (int p = 0; p < LP; ++p) {
-      const bool ok = colok[p] && (k0 + kk[p]) < K;
-      dma16(rs, ok ? gbase[p] + (uint32_t)k0 * ldb : OOB, tile + ldsoff + p * 1024);
+      const bool ok = colok[p & 1] && (k0 + krow + 2 * p) < 0;
+      dma16(rs, ok ? gbase[p & 1] + (uint32_t)(k0 + 4 * (p >> 1)) * ldb : OOB,
+            tile + ldsoff + p * 1024);
     }
   }
 };
@@ -408,39 +409,17 @@ gemm_bf16_kernel(GemmArgs g) {
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
   };
-  // Scheduling hints for one sub-step region (reads of the next fragments +
-  // MFMAs of the current ones): interleave one LDS read with one MFMA so the
-  // reads are issued early in the sub-step.
-  constexpr int NREAD = FM * (AK ? 1 : 2) + FN * (BKM ? 1 : 2);
-  constexpr int NMFMA = FM * FN;
-  auto sched_sub = [&]() {
-#if CODA_SCHED == 1
-    constexpr int NPAIR = NREAD < NMFMA ? NREAD : NMFMA;
-#pragma unroll
-    for (int x = 0; x < NPAIR; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    }
-    if (NREAD > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NPAIR, 0);
-    if (NMFMA > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NPAIR, 0);
-#endif
-  };
-  auto prio_hi = [&]() {
-#if CODA_SETPRIO == 1
-    __builtin_amdgcn_s_setprio(1);
-#endif
-  };
-  auto prio_lo = [&]() {
-#if CODA_SETPRIO == 1
-    __builtin_amdgcn_s_setprio(0);
-#endif
-  };
   auto issue = [&](int step) {
     lds_char* st = lsm + (step % NSTAGE) * STAGE_BYTES;
     la.issue(st, step * BK);
     lb.issue(st + OPER_BYTES, step * BK);
   };
 
+  // The compiler interleaves each sub-step's LDS reads and MFMAs; with two
+  // waves per SIMD that measured faster than any forced order (all reads
+  // first, reads after one MFMA, one read per MFMA), and than issuing the
+  // next stage's loads earlier (right after the barrier, or after the first
+  // MFMAs of the last sub-step).  sched_barrier keeps the sub-steps apart.
 #pragma unroll
   for (int st = 0; st < NSTAGE - 1; ++st) issue(st);
   __builtin_amdgcn_s_waitcnt(WAIT_NEXT);     // step 0 has landed
@@ -453,19 +432,13 @@ gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int s = 0; s + 1 < NSUB; ++s) {
       read_frags(sc, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-      prio_hi();
       mfmas(fa[s & 1], fb[s & 1]);
-      prio_lo();
-      sched_sub();
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(WAIT_NEXT);   // this wave's loads of step kt+1 have landed
     __syncthreads();
     read_frags(sn, 0, fa[0], fb[0]);
-    prio_hi();
     mfmas(fa[(NSUB - 1) & 1], fb[(NSUB - 1) & 1]);
-    prio_lo();
-    sched_sub();
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_waitcnt(0);             // no load may still write into LDS
@@ -820,10 +793,7 @@ __global__ void dy_kernel(__bf16* __restrict__ dR, const __bf16* __restrict__ y,
 // Launchers
 // ---------------------------------------------------------------------------
 // Wave grid used for every bf16 GEMM: 2 x 4 waves (two per SIMD).
-#ifndef CODA_WAVES_M
-#define CODA_WAVES_M 2
-#endif
-constexpr int kWavesM = CODA_WAVES_M, kWavesN = 8 / CODA_WAVES_M;
+constexpr int kWavesM = 2, kWavesN = 4;
 
 template <bool AK, bool BKM, int EPI>
 static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
