@@ -7,10 +7,12 @@ One step = coda_fwd + coda_bwd over one batch of the LLaMA-7B-shaped workload
 inputs resident in HBM.  Printed: ONE JSON line with the throughput (TFLOP/s of
 algorithmic GEMM work, 6 M (K d + d N) per step), the fraction of the MI355X
 dense bf16 MFMA peak, the speed-up over an unfused hipBLASLt + F.rms_norm +
-autograd step on the same GPU, per-kernel times from HIP events recorded on
-the stream the kernels run on, the roofline of the dominant kernel, the same
-figures for the 70B-hidden and SwiGLU workloads under "also", and the CPU
-oracle timed on a bounded sample of the same workload.
+autograd step on the same GPU (for the step, and for the forward and the
+backward alone), the median / min / max step time, per-kernel times from HIP
+events recorded on the stream the kernels run on, the roofline of the
+dominant kernel, the same figures for the 70B-hidden, SwiGLU and 1B-hidden
+(forward only) workloads under "also", and the CPU oracle timed on a bounded
+sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-also] [--no-cpu-baseline]
 """
@@ -38,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_fwdbwd")
-    ap.add_argument("--no-also", action="store_true", help="skip the 70B and SwiGLU workloads")
+    ap.add_argument("--no-also", action="store_true", help="skip the 70B, SwiGLU and 1B workloads")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused torch baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
@@ -69,28 +71,29 @@ class CodaCase:
         self.dW2 = torch.empty((d, N), dtype=bf, device=dev)
         self.dg = torch.empty((d,), dtype=torch.float32, device=dev)
         self.wsf = torch.empty(coda.fwd_workspace_bytes(1, M, K, d, N), dtype=torch.uint8, device=dev)
-        self.wsb = torch.empty(coda.bwd_workspace_bytes(1, M, K, d, N), dtype=torch.uint8, device=dev)
-        self.kernels_per_step = 8
+        self.backward = w.backward
+        if self.backward:
+            self.wsb = torch.empty(coda.bwd_workspace_bytes(1, M, K, d, N), dtype=torch.uint8, device=dev)
+        self.kernels_per_step = 8 if self.backward else 2
+        self.leaf_names = ("X", "W1", "R", "gamma", "W2")
 
     def flops(self):
-        return self.w.flops_fwd() + self.w.flops_bwd()
+        return self.w.flops_fwd() + (self.w.flops_bwd() if self.backward else 0.0)
 
-    def fused_step(self):
+    def fused_fwd(self):
         t, c = self.t, self.coda
         c.coda_fwd(t["X"], t["W1"], t["R"], t["gamma"], t["W2"], self.w.eps, self.y, self.r, self.z, self.wsf)
+
+    def fused_bwd(self):
+        t, c = self.t, self.coda
         c.coda_bwd(t["X"], t["W1"], t["gamma"], t["W2"], self.y, self.r, t["dz"], self.dX, self.dW1,
                    self.dR, self.dW2, self.dg, self.wsb)
 
-    def unfused_setup(self):
-        torch = self.torch
-        self.leaf = {k: self.t[k].detach().clone().requires_grad_(True) for k in ("X", "W1", "R", "gamma", "W2")}
-
-    def unfused_step(self):
-        torch, F = self.torch, self.torch.nn.functional
+    def unfused_fwd(self):
+        F = self.torch.nn.functional
         p = self.leaf
         y = p["X"] @ p["W1"] + p["R"]
-        z = F.rms_norm(y, (self.w.d,), p["gamma"], self.w.eps) @ p["W2"]
-        torch.autograd.grad(z, [p["X"], p["W1"], p["R"], p["gamma"], p["W2"]], self.t["dz"])
+        return F.rms_norm(y, (self.w.d,), p["gamma"], self.w.eps) @ p["W2"]
 
 
 class SwigluCase:
@@ -107,26 +110,68 @@ class SwigluCase:
         self.dW = torch.empty((d, 2 * F), dtype=bf, device=dev)
         self.dWd = torch.empty((F, d), dtype=bf, device=dev)
         self.ws = torch.empty(coda.swiglu_bwd_workspace_bytes(1, M, d, F), dtype=torch.uint8, device=dev)
+        self.backward = w.backward
         self.kernels_per_step = 6
+        self.leaf_names = ("X", "W", "Wd")
 
     def flops(self):
-        return self.w.flops_fwd() + self.w.flops_bwd()
+        return self.w.flops_fwd() + (self.w.flops_bwd() if self.backward else 0.0)
 
-    def fused_step(self):
+    def fused_fwd(self):
         t, c = self.t, self.coda
         c.coda_swiglu_fwd(t["X"], t["W"], t["Wd"], self.gu, self.a, self.z)
+
+    def fused_bwd(self):
+        t, c = self.t, self.coda
         c.coda_swiglu_bwd(t["X"], t["W"], t["Wd"], self.gu, self.a, t["dz"], self.dX, self.dW, self.dWd, self.ws)
 
-    def unfused_setup(self):
-        self.leaf = {k: self.t[k].detach().clone().requires_grad_(True) for k in ("X", "W", "Wd")}
-
-    def unfused_step(self):
-        torch, F = self.torch, self.torch.nn.functional
+    def unfused_fwd(self):
+        F = self.torch.nn.functional
         p = self.leaf
         gu = p["X"] @ p["W"]
         Fh = self.w.F
-        z = (F.silu(gu[:, :Fh]) * gu[:, Fh:]) @ p["Wd"]
-        torch.autograd.grad(z, [p["X"], p["W"], p["Wd"]], self.t["dz"])
+        return (F.silu(gu[:, :Fh]) * gu[:, Fh:]) @ p["Wd"]
+
+
+class _Steps:
+    """The fused and unfused step functions of a case: forward, backward, and
+    the training step (forward + backward; the forward alone for a
+    forward-only workload).  The unfused forward records the autograd graph
+    when the workload has a backward; the unfused backward replays one
+    recorded graph (retain_graph)."""
+
+    @staticmethod
+    def fused_step(case):
+        case.fused_fwd()
+        if case.backward:
+            case.fused_bwd()
+
+    @staticmethod
+    def unfused_setup(case):
+        grad = case.backward
+        case.leaf = {k: case.t[k].detach().clone().requires_grad_(grad) for k in case.leaf_names}
+        case.graph = case.unfused_fwd() if grad else None
+
+    @staticmethod
+    def unfused_fwd(case):
+        if case.backward:
+            case.unfused_fwd()
+        else:
+            with case.torch.no_grad():
+                case.unfused_fwd()
+
+    @staticmethod
+    def unfused_bwd(case):
+        case.torch.autograd.grad(case.graph, [case.leaf[k] for k in case.leaf_names], case.t["dz"],
+                                 retain_graph=True)
+
+    @staticmethod
+    def unfused_step(case):
+        if case.backward:
+            z = case.unfused_fwd()
+            case.torch.autograd.grad(z, [case.leaf[k] for k in case.leaf_names], case.t["dz"])
+        else:
+            _Steps.unfused_fwd(case)
 
 
 def make_case(w, torch, coda):
@@ -137,17 +182,26 @@ def make_case(w, torch, coda):
 
 # ------------------------------------------------------------------- timing
 
-def time_steps(torch, fn, steps, warmup):
+def time_steps(torch, fn, steps, warmup, per_step=None):
+    """Mean ms per step over `steps` steps after `warmup` untimed ones.  With
+    `per_step` (a dict), an event is also recorded between steps and the
+    median / min / max step time is stored there."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_step is not None else 2)]
+    ev[0].record()
+    for i in range(steps):
         fn()
-    e.record()
+        if per_step is not None:
+            ev[i + 1].record()
+    ev[-1].record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / steps
+    if per_step is not None:
+        t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        per_step.update({"median_ms": round(t[len(t) // 2], 4), "min_ms": round(t[0], 4),
+                         "max_ms": round(t[-1], 4)})
+    return ev[0].elapsed_time(ev[-1]) / steps
 
 
 def kernel_table(trace, steps):
@@ -176,22 +230,30 @@ def run_case(case, torch, coda, steps, warmup, unfused):
     time is the throughput), the second with every kernel bracketed by HIP
     events recorded by the library on the kernel's stream (per-kernel
     durations; the events add a few microseconds between kernels)."""
-    ms = time_steps(torch, case.fused_step, steps, warmup)
+    dist = {}
+    step = lambda: _Steps.fused_step(case)  # noqa: E731
+    ms = time_steps(torch, step, steps, warmup, dist)
     coda.trace_start(steps * case.kernels_per_step + 8)
-    ms_traced = time_steps(torch, case.fused_step, steps, 0)
+    ms_traced = time_steps(torch, step, steps, 0)
     trace = coda.trace_read()
     coda.trace_stop()
-    res = {"ms_per_step": ms, "ms_per_step_traced": ms_traced,
+    res = {"ms_per_step": ms, "ms_per_step_traced": ms_traced, "step_times": dist,
            "kernels": kernel_table(trace, steps)}
+    if case.backward:
+        res["fwd_ms"] = time_steps(torch, case.fused_fwd, steps, 1)
+        res["bwd_ms"] = time_steps(torch, case.fused_bwd, steps, 1)
     if unfused:
         try:
             torch.backends.cuda.preferred_blas_library("cublaslt")   # hipBLASLt on ROCm
         except Exception:  # pragma: no cover - older torch
             pass
-        case.unfused_setup()
-        res["unfused_ms_per_step"] = time_steps(torch, case.unfused_step, steps, warmup)
+        _Steps.unfused_setup(case)
+        res["unfused_ms_per_step"] = time_steps(torch, lambda: _Steps.unfused_step(case), steps, warmup)
+        if case.backward:
+            res["unfused_fwd_ms"] = time_steps(torch, lambda: _Steps.unfused_fwd(case), steps, 1)
+            res["unfused_bwd_ms"] = time_steps(torch, lambda: _Steps.unfused_bwd(case), steps, 1)
         res["unfused_blas"] = str(torch.backends.cuda.preferred_blas_library())
-        del case.leaf
+        del case.leaf, case.graph
     return res
 
 
@@ -202,10 +264,19 @@ def summary(case, res):
            "ms_per_step": round(res["ms_per_step"], 4),
            "ms_per_step_traced": round(res["ms_per_step_traced"], 4),
            "flops_per_step": fl}
+    out["step_times"] = res["step_times"]
     if "unfused_ms_per_step" in res:
         out["unfused_ms_per_step"] = round(res["unfused_ms_per_step"], 4)
         out["speedup_vs_unfused"] = round(res["unfused_ms_per_step"] / res["ms_per_step"], 3)
         out["unfused_blas"] = res["unfused_blas"]
+    for part, fl in (("fwd", case.w.flops_fwd()), ("bwd", case.w.flops_bwd())):
+        if f"{part}_ms" in res:
+            d = {"ms": round(res[f"{part}_ms"], 4),
+                 "tflops": round(fl / (res[f"{part}_ms"] * 1e-3) / 1e12, 1)}
+            if f"unfused_{part}_ms" in res:
+                d["unfused_ms"] = round(res[f"unfused_{part}_ms"], 4)
+                d["speedup_vs_unfused"] = round(res[f"unfused_{part}_ms"] / res[f"{part}_ms"], 3)
+            out[part] = d
     return out
 
 
@@ -322,7 +393,7 @@ def main():
 
     also = {}
     if not args.no_also:
-        for name in ("llama70b_fwdbwd", "swiglu_fwdbwd"):
+        for name in ("llama70b_fwdbwd", "swiglu_fwdbwd", "llama1b_fwd"):
             w2 = synth.WORKLOADS[name]
             print(f"[bench] {name}: inputs + timing", file=sys.stderr, flush=True)
             c2, _ = make_case(w2, torch, coda)
@@ -356,6 +427,9 @@ def main():
         "unfused_ms_per_step": main_sum.get("unfused_ms_per_step"),
         "unfused_blas": main_sum.get("unfused_blas"),
         "ms_per_step_traced": main_sum["ms_per_step_traced"],
+        "step_times": main_sum["step_times"],
+        "fwd": main_sum.get("fwd"),
+        "bwd": main_sum.get("bwd"),
         "roofline": rf,
         "cpu_baseline": cpu,
         "kernels": kernels,

@@ -753,19 +753,35 @@ __global__ void row_rsqrt_kernel(const float* __restrict__ P, int64_t ldp, int T
   r[i] = 1.0f / sqrtf(s * inv_d + eps);
 }
 
+// c and dgamma.  Rows: four lanes per row, each summing every fourth partial
+// (consecutive lanes read consecutive 16-byte pieces of the [M][Tn] array),
+// then two shuffles.  Columns: one lane per column over the Tm row tiles.
+// Every sum has a fixed order, so the result is run-to-run identical.
 __global__ void bwd_reduce_kernel(const float* __restrict__ S, int64_t lds, int Tn,
                                   const float* __restrict__ r, int64_t M, float inv_d,
                                   const float* __restrict__ G, int Tm, int64_t d,
                                   float* __restrict__ c, float* __restrict__ dgamma) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < M) {
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row_threads = ((M * 4 + 255) / 256) * 256;   // whole blocks for the row part
+  if (v < row_threads) {
+    const int64_t i = v >> 2;
+    const int q = (int)(v & 3);
     float s = 0.0f;
-    for (int k = 0; k < Tn; ++k) s += S[i * lds + k];
-    const float ri = r[i];
-    c[i] = ri * ri * ri * s * inv_d;
-  } else if (i < M + d) {
-    const int64_t j = i - M;
+    if (i < M) {
+#pragma unroll 4
+      for (int k = q; k < Tn; k += 4) s += S[i * lds + k];
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    if (i < M && q == 0) {
+      const float ri = r[i];
+      c[i] = ri * ri * ri * s * inv_d;
+    }
+  } else {
+    const int64_t j = v - row_threads;
+    if (j >= d) return;
     float s = 0.0f;
+#pragma unroll 8
     for (int k = 0; k < Tm; ++k) s += G[(int64_t)k * d + j];
     dgamma[j] = s;
   }
@@ -865,7 +881,8 @@ hipError_t launch_row_rsqrt(const float* P, int64_t ldp, int T, int64_t M, int64
 hipError_t launch_bwd_reduce(const float* S, int64_t lds, int Tn, const float* r, int64_t M,
                              int64_t d, const float* G, int Tm, float* c, float* dgamma,
                              hipStream_t s) {
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((M + d + 255) / 256)), dim3(256), 0, s, S,
+  const int64_t threads = ((M * 4 + 255) / 256) * 256 + d;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, S,
                      lds, Tn, r, M, 1.0f / (float)d, G, Tm, d, c, dgamma);
   return hipGetLastError();
 }
