@@ -82,8 +82,10 @@ hipError_t traced(const char* name, double flops, double bytes, hipStream_t s, F
 double gemm_flops(int64_t M, int64_t N, int64_t K) { return 2.0 * (double)M * (double)N * (double)K; }
 
 // ------------------------------------------------------------- workspaces
-// Forward workspace: P [M, Tn] fp32 partial sums of squares, yg [M, d] = y * gamma
-// (the second GEMM's A operand, written by the first GEMM's epilogue).
+// Forward workspace: P [M, Tn] fp32 partial sums of squares, yg = y * gamma
+// (the second GEMM's A operand, written by the first GEMM's epilogue): bf16
+// stored transposed, [d, M], so that both operands of the second GEMM are
+// MN-contiguous; fp32 stored [M, d].
 struct FwdWs {
   size_t P, yg, total;
   int Tn;
@@ -190,6 +192,7 @@ coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
   hipError_t err;
   const double eb = (double)e;
 
+  const bool bf = dtype == CODA_BF16;
   // K1: y = X W1 + R; epilogue stores y, yg = y * gamma and the partial sums of squares
   GemmArgs g1 = gemm(M, d, K, X, K, M * K, W1, d, K * d, y, d);
   g1.E = R;
@@ -197,11 +200,11 @@ coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
   g1.part_row = P;
   g1.ld_part_row = ws.Tn;
   g1.C2 = yg;
-  g1.ldc2 = d;
+  g1.ldc2 = bf ? M : d;
+  g1.c2_trans = bf ? 1 : 0;
   g1.vcol = gamma;
-  // K2: z = diag(r) (yg W2)
-  GemmArgs g2 = gemm(M, N, d, yg, d, M * d, W2, N, d * N, z, N);
-  const bool bf = dtype == CODA_BF16;
+  // K2: z = diag(r) (yg W2); bf16 reads yg^T [d, M] as an MN-contiguous A
+  GemmArgs g2 = gemm(M, N, d, yg, bf ? M : d, M * d, W2, N, d * N, z, N);
   const double k1_bytes = (M * K + K * d + 3.0 * M * d + d) * eb + M * ws.Tn * 4.0;
   if ((err = traced("k1_gemm_resid_sumsq", gemm_flops(M, d, K), k1_bytes, s, [&] {
          return bf ? coda::launch_gemm_bf16(g1, true, false, coda::EPI_RESID_SUMSQ, s)
@@ -219,7 +222,7 @@ coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
     g2.eps = eps;
     g2.r_out = r;
     return hip_status(traced("k2_gemm_rsqrt_rowscale", gemm_flops(M, N, d), k2_bytes, s, [&] {
-      return coda::launch_gemm_bf16(g2, true, false, coda::EPI_RSQRT_SCALE, s);
+      return coda::launch_gemm_bf16(g2, false, false, coda::EPI_RSQRT_SCALE, s);
     }));
   }
   if ((err = traced("r1_row_rsqrt", 0.0, M * ws.Tn * 4.0 + M * 4.0, s, [&] {

@@ -547,7 +547,14 @@ gemm_bf16_kernel(GemmArgs g) {
             lo += elo;
             hi += ehi;
             st8(C + o, lo, hi);
-            if (g.C2) st8((__bf16*)g.C2 + (int64_t)row * g.ldc2 + gcol, lo * glo, hi * ghi);
+            if (g.C2) {
+              if (g.c2_trans) {                         // y * gamma back into the region
+                *(f32x4*)(region + r * 256 + (((2 * c8) ^ (r & 15)) << 4)) = lo * glo;
+                *(f32x4*)(region + r * 256 + (((2 * c8 + 1) ^ (r & 15)) << 4)) = hi * ghi;
+              } else {
+                st8((__bf16*)g.C2 + (int64_t)row * g.ldc2 + gcol, lo * glo, hi * ghi);
+              }
+            }
             const f32x4 sq = lo * lo + hi * hi;
             s = sq[0] + sq[1] + sq[2] + sq[3];
           }
@@ -589,6 +596,31 @@ gemm_bf16_kernel(GemmArgs g) {
             }
             st8(C + o, dg0, dg1);
             st8(C + o + g.F, du0, du1);
+          }
+        }
+      }
+      if constexpr (EPI == EPI_RESID_SUMSQ) {
+        // y * gamma transposed: C2[col][row].  In pass q, lanes 4c..4c+3 take
+        // column 16q + c of the wave's 64 and rows 8(l%4)..+7 each, so one
+        // store instruction writes 16 columns x 64 contiguous bytes.
+        if (g.C2 && g.c2_trans) {
+          __builtin_amdgcn_s_waitcnt(0xc07f);         // this wave's LDS writes are done
+          const int rg = 8 * (lane & 3);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = 16 * q + (lane >> 2);
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int r = rg + e;
+              v[e] = *(const float*)(region + r * 256 + (((c >> 2) ^ (r & 15)) << 4) + (c & 3) * 4);
+            }
+            const int colT = col0 + wn * TN + c;
+            const int rowT = row0 + wm * TM + i * 32 + rg;
+            if (colT < g.N && rowT < g.M)
+              *(bf16x8*)((__bf16*)g.C2 + (int64_t)colT * g.ldc2 + rowT) =
+                  bf16x8{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3]),
+                         f2bf(v[4]), f2bf(v[5]), f2bf(v[6]), f2bf(v[7])};
           }
         }
       }
@@ -825,14 +857,14 @@ static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStream_t s) {
   // The combinations the block uses:
-  //   forward GEMMs:      A k-major, B mn-major  (X W1, y W2f, X W, a Wd)
+  //   forward GEMMs:      A k-major, B mn-major  (X W1, X W, a Wd)
   //   input gradients:    A k-major, B k-major   (dz W2^T, dy W1^T, dz Wd^T, dgu W^T)
-  //   weight gradients:   A mn-major, B mn-major (n^T dz, X^T dy, a^T dz, X^T dgu)
+  //   both mn-major:      (y gamma)^T-stored times W2, and the weight
+  //                       gradients n^T dz, X^T dy, a^T dz, X^T dgu
   if (ak && !bk) {
     switch (epi) {
       case EPI_STORE: return launch_one<true, false, EPI_STORE>(g, s);
       case EPI_RESID_SUMSQ: return launch_one<true, false, EPI_RESID_SUMSQ>(g, s);
-      case EPI_RSQRT_SCALE: return launch_one<true, false, EPI_RSQRT_SCALE>(g, s);
       case EPI_SWIGLU: return launch_one<true, false, EPI_SWIGLU>(g, s);
       default: break;
     }
@@ -847,6 +879,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStr
     switch (epi) {
       case EPI_STORE: return launch_one<false, false, EPI_STORE>(g, s);
       case EPI_ROWSCALE: return launch_one<false, false, EPI_ROWSCALE>(g, s);
+      case EPI_RSQRT_SCALE: return launch_one<false, false, EPI_RSQRT_SCALE>(g, s);
       default: break;
     }
   }

@@ -17,7 +17,8 @@ constexpr int kTileF32 = 64;
 enum Epi : int {
   EPI_STORE = 0,       // C = acc
   EPI_RESID_SUMSQ = 1, // y = acc + E; C = y; part_row[i][tile_n] = sum_{j in tile} y_ij^2;
-                       // if C2: C2 = y * vcol (the RMSNorm weight, by column)
+                       // if C2: C2 = y * vcol (the RMSNorm weight, by column), stored
+                       // transposed (C2[j][i], ldc2 = its row length) when c2_trans
   EPI_ROWSCALE = 2,    // C = vrow[i] * acc  (vrow NULL: vcol[i], bf16)
   EPI_DN = 3,          // dh = acc; C = dn = gamma_j dh; part_row = sum_j dn*y; part_col = sum_i dh*r*y;
                        // if C2: C2 = n = r_i y
@@ -41,6 +42,7 @@ struct GemmArgs {
   float* part_col; int64_t ld_part_col;   // [tiles_m][N]
   int F;                         // SwiGLU half width (gate columns)
   int nparts; float inv_d; float eps; float* r_out;   // EPI_RSQRT_SCALE
+  int c2_trans;                  // EPI_RESID_SUMSQ: C2 stored transposed
   uint32_t A_bytes, B_bytes;     // buffer extents for hardware bounds checks
 };
 
