@@ -27,13 +27,13 @@ class Workload:
     """One synthetic workload: its shapes, dtype, epsilon and seed."""
 
     name: str
-    kind: str            # "coda" (GEMM-Residual-RMSNorm-GEMM) or "swiglu"
+    kind: str            # "coda" (GEMM-Residual-RMSNorm-GEMM), "swiglu", or "mlp" (the two chained)
     dtype: str           # "f32" or "bf16"
     M: int
-    K: int = 0           # coda: GEMM1 reduction width
-    d: int = 0           # coda: normalised width; swiglu: model width
+    K: int = 0           # coda, mlp: GEMM1 reduction width
+    d: int = 0           # coda, mlp: normalised width; swiglu: model width
     N: int = 0           # coda: GEMM2 output width
-    F: int = 0           # swiglu: hidden width (gate and up halves)
+    F: int = 0           # swiglu, mlp: hidden width (gate and up halves)
     eps: float = 0.0
     seed: int = 0
     backward: bool = True
@@ -43,7 +43,10 @@ class Workload:
         """Algorithmic GEMM flops of the forward pass (elementwise work excluded)."""
         if self.kind == "coda":
             return 2.0 * self.M * (self.K * self.d + self.d * self.N)
-        return 2.0 * self.M * self.d * 2 * self.F + 2.0 * self.M * self.F * self.d
+        swiglu = 2.0 * self.M * self.d * 2 * self.F + 2.0 * self.M * self.F * self.d
+        if self.kind == "mlp":
+            return 2.0 * self.M * self.K * self.d + swiglu
+        return swiglu
 
     def flops_bwd(self) -> float:
         """Algorithmic GEMM flops of the backward pass: two products per forward GEMM."""
@@ -68,6 +71,10 @@ WORKLOADS = {
         Workload("swiglu_fwdbwd", "swiglu", "bf16", M=8192, d=4096, F=14336,
                  seed=1004, backward=True,
                  note="SwiGLU gate/up GEMM with fused epilogue, then down-projection"),
+        Workload("llama7b_mlp_fwdbwd", "mlp", "bf16", M=8192, K=4096, d=4096, F=11008,
+                 eps=1e-6, seed=1005, backward=True,
+                 note="LLaMA-7B-shaped MLP sub-layer: projection + residual, RMS norm, "
+                      "SwiGLU gate/up, down projection; forward+backward with dy_in"),
     ]
 }
 
@@ -127,10 +134,31 @@ def swiglu_inputs(M: int, d: int, F: int, seed: int, dtype: str = "bf16",
     return {k: _quantise(v, dtype) for k, v in out.items()}
 
 
+def mlp_inputs(M: int, K: int, d: int, F: int, seed: int, dtype: str = "bf16",
+               with_dz: bool = True) -> dict:
+    """X, R ~ N(0,1); W1 ~ N(0,1/K); gamma = 1 + 0.1 N(0,1); W = [W_gate | W_up]
+    ~ N(0,1/d); Wd ~ N(0,1/F); dz, dy_in ~ N(0,1)."""
+    s = np.random.SeedSequence(seed).spawn(8)
+    out = {
+        "X": _normal(s[0], (M, K), 1.0),
+        "R": _normal(s[1], (M, d), 1.0),
+        "W1": _normal(s[2], (K, d), 1.0 / math.sqrt(K)),
+        "gamma": np.float32(1.0) + np.float32(0.1) * _normal(s[3], (d,), 1.0),
+        "W": _normal(s[4], (d, 2 * F), 1.0 / math.sqrt(d)),
+        "Wd": _normal(s[5], (F, d), 1.0 / math.sqrt(F)),
+    }
+    if with_dz:
+        out["dz"] = _normal(s[6], (M, d), 1.0)
+        out["dy_in"] = _normal(s[7], (M, d), 1.0)
+    return {k: _quantise(v, dtype) for k, v in out.items()}
+
+
 def workload_inputs(w: Workload, with_dz: bool | None = None) -> dict:
     """Inputs of a named workload (dz only when it has a backward pass)."""
     if with_dz is None:
         with_dz = w.backward
     if w.kind == "coda":
         return coda_inputs(w.M, w.K, w.d, w.N, w.seed, w.dtype, with_dz)
+    if w.kind == "mlp":
+        return mlp_inputs(w.M, w.K, w.d, w.F, w.seed, w.dtype, with_dz)
     return swiglu_inputs(w.M, w.d, w.F, w.seed, w.dtype, with_dz)

@@ -40,6 +40,13 @@ What the pages fix, and the readings taken where they are silent:
     sections, "matrix tile load/store ... saving intermediates").  Reading: the
     backward functions take the saved tensors (y and r; gu and a) as inputs, so
     a caller can pass them rounded to the storage dtype.
+  * The two patterns chained as in a LLaMA MLP sub-layer (``ref_mlp_*``): the
+    pages name both inside a transformer block (the residual add and RMS
+    normalisation around a matmul, and SwiGLU as the activation epilogue,
+    [RU]/[FR] insight and primitives sections).  Reading: the normalised h
+    feeds the gate/up GEMM in place of the second GEMM, h W = [g | u], a =
+    silu(g) u, z = a Wd; y is the residual stream, so its gradient may also
+    receive a term dy_in from later layers, added to dy.
 
 Every function here is pinned by a test against something other than itself
 (brute-force loops, finite differences, torch CPU autograd, closed forms and
@@ -53,6 +60,7 @@ __all__ = [
     "bf16_rne", "ref_fwd", "ref_fwd_rewritten", "ref_partials", "ref_bwd",
     "ref_y_r", "ref_fwd_rows", "ref_bwd_sampled", "sigmoid", "ref_swiglu_fwd",
     "ref_swiglu_bwd", "ref_swiglu_fwd_rows", "ref_swiglu_bwd_sampled",
+    "ref_mlp_fwd", "ref_mlp_bwd", "ref_mlp_fwd_rows", "ref_mlp_bwd_sampled",
 ]
 
 
@@ -154,16 +162,18 @@ def ref_fwd_rewritten(X, W1, R, gamma, W2, eps: float, BN: int = 256) -> dict:
 # GEMM-Residual-RMSNorm-GEMM, backward
 # ---------------------------------------------------------------------------
 
-def ref_bwd(X, W1, gamma, W2, y, r, dz) -> dict:
-    """Exact gradient of L = <dz, z> for the forward of ``ref_fwd``, given the
-    saved y and r.
+def ref_bwd(X, W1, gamma, W2, y, r, dz, dy_in=None) -> dict:
+    """Exact gradient of L = <dz, z> (+ <dy_in, y>) for the forward of
+    ``ref_fwd``, given the saved y and r.
 
     With n = diag(r) y and h = n diag(gamma):
       dW2 = h^T dz;  dh = dz W2^T;  dgamma_j = sum_i dh_ij n_ij;
       dn = dh diag(gamma);  s_i = sum_j dn_ij y_ij;  c_i = r_i^3 s_i / d;
-      dy = diag(r) dn - diag(c) y;  dR = dy;  dX = dy W1^T;  dW1 = X^T dy.
-    (dr_i/dy_ik = -r_i^3 y_ik / d gives the -c y term.)  The gradient reaches y
-    only through z, so dR = dy.
+      dy = diag(r) dn - diag(c) y (+ dy_in);  dR = dy;  dX = dy W1^T;
+      dW1 = X^T dy.
+    (dr_i/dy_ik = -r_i^3 y_ik / d gives the -c y term.)  Without dy_in the
+    gradient reaches y only through z, so dR = dy; dy_in is the gradient the
+    residual stream y receives from elsewhere, and it adds to dy.
     """
     X, W1, gamma, W2, y, r, dz = map(_f64, (X, W1, gamma, W2, y, r, dz))
     d = y.shape[1]
@@ -176,6 +186,8 @@ def ref_bwd(X, W1, gamma, W2, y, r, dz) -> dict:
     s = np.sum(dn * y, axis=1)
     c = r ** 3 * s / d
     dy = dn * r[:, None] - c[:, None] * y
+    if dy_in is not None:
+        dy = dy + _f64(dy_in)
     dX = dy @ W1.T
     dW1 = X.T @ dy
     return {"dX": dX, "dW1": dW1, "dR": dy, "dW2": dW2, "dgamma": dgamma,
@@ -324,3 +336,98 @@ def ref_swiglu_bwd_sampled(X, W, Wd, dz, rows, cols_W, rows_Wd, saved_bf16: bool
     return {"rows": rows, "cols_W": cols_W, "rows_Wd": rows_Wd,
             "dX_rows": sub["dX"], "dgu_rows": sub["dgu"],
             "dW_cols": X.T @ dgu_c, "dWd_rows": a_c.T @ dz}
+
+
+# ---------------------------------------------------------------------------
+# The two patterns chained: a LLaMA MLP sub-layer
+# ---------------------------------------------------------------------------
+
+def ref_mlp_fwd(X, W1, R, gamma, W, Wd, eps: float) -> dict:
+    """Projection + residual, RMS normalisation, SwiGLU gate/up, down projection.
+
+    y = X W1 + R;  r_i = (mean_j y_ij^2 + eps)^(-1/2);  h = diag(r) y diag(gamma);
+    gu = h W (W = [W_gate | W_up]);  g = gu[:, :F], u = gu[:, F:];
+    a = g sigmoid(g) u;  z = a Wd.
+    ([RU]/[FR] insight sections for the residual + RMS pattern around a
+    matmul; [JA]/[RU]/[FR] primitives sections for SwiGLU as the activation.)
+    """
+    X, W1, R, gamma, W, Wd = map(_f64, (X, W1, R, gamma, W, Wd))
+    y = X @ W1 + R
+    r = 1.0 / np.sqrt(np.mean(y * y, axis=1) + eps)
+    h = y * r[:, None] * gamma[None, :]
+    F = W.shape[1] // 2
+    gu = h @ W
+    g, u = gu[:, :F], gu[:, F:]
+    a = g * sigmoid(g) * u
+    z = a @ Wd
+    return {"y": y, "r": r, "h": h, "gu": gu, "a": a, "z": z}
+
+
+def ref_mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in=None) -> dict:
+    """Exact gradient of L = <dz, z> (+ <dy_in, y>) for ``ref_mlp_fwd``, given
+    the saved y, r, gu and a.
+
+    The SwiGLU part first, from the saved gu and a (as ``ref_swiglu_bwd``):
+      da = dz Wd^T;  dg = da u sg (1 + g (1 - sg));  du = da g sg;
+      dgu = [dg | du];  dWd = a^T dz.
+    Then h W is the second GEMM of the RMS-normalised block with dgu as its
+    output gradient, so the rest is ``ref_bwd`` with W2 = W and dz = dgu:
+      dW = h^T dgu;  dh = dgu W^T;  dgamma;  dy (+ dy_in);  dR;  dX;  dW1.
+    """
+    X, W1, gamma, W, Wd, y, r, gu, a, dz = map(_f64, (X, W1, gamma, W, Wd, y, r, gu, a, dz))
+    F = W.shape[1] // 2
+    g, u = gu[:, :F], gu[:, F:]
+    sg = sigmoid(g)
+    da = dz @ Wd.T
+    dg = da * u * sg * (1.0 + g * (1.0 - sg))
+    du = da * g * sg
+    dgu = np.concatenate([dg, du], axis=1)
+    dWd = a.T @ dz
+    b = ref_bwd(X, W1, gamma, W, y, r, dgu, dy_in)
+    return {"dX": b["dX"], "dW1": b["dW1"], "dR": b["dR"], "dW": b["dW2"], "dWd": dWd,
+            "dgamma": b["dgamma"], "dgu": dgu, "da": da, "dh": b["dh"], "s": b["s"], "c": b["c"]}
+
+
+def ref_mlp_fwd_rows(X, W1, R, gamma, W, Wd, eps: float, rows) -> dict:
+    """``ref_mlp_fwd`` evaluated for the given rows only (rows are independent)."""
+    rows = np.asarray(rows)
+    out = ref_mlp_fwd(_f64(X[rows]), W1, _f64(R[rows]), gamma, W, Wd, eps)
+    out["rows"] = rows
+    return out
+
+
+def ref_mlp_bwd_sampled(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in, rows, cols_d, cols_2F,
+                        rows_F) -> dict:
+    """``ref_mlp_bwd`` with dX and dR restricted to ``rows``, dW1 to the columns
+    ``cols_d``, dW to the columns ``cols_2F``, dWd to the rows ``rows_F``;
+    dgamma, s and c in full.
+
+    s and c need every row's dh, so dgu (from da = dz Wd^T) and dh = dgu W^T
+    are formed whole.  The rest is the definitions restricted.  dy_in may be
+    None.
+    """
+    X, W1, gamma, W, Wd, y, r, gu, a, dz = map(_f64, (X, W1, gamma, W, Wd, y, r, gu, a, dz))
+    d = y.shape[1]
+    F = W.shape[1] // 2
+    g, u = gu[:, :F], gu[:, F:]
+    sg = sigmoid(g)
+    da = dz @ Wd.T
+    dgu = np.concatenate([da * u * sg * (1.0 + g * (1.0 - sg)), da * g * sg], axis=1)
+    n = y * r[:, None]
+    dh = dgu @ W.T
+    dgamma = np.sum(dh * n, axis=0)
+    dn = dh * gamma[None, :]
+    s = np.sum(dn * y, axis=1)
+    c = r ** 3 * s / d
+    rows, cols_d, cols_2F, rows_F = map(np.asarray, (rows, cols_d, cols_2F, rows_F))
+    dy_rows = dn[rows] * r[rows, None] - c[rows, None] * y[rows]
+    dy_cols = dn[:, cols_d] * r[:, None] - c[:, None] * y[:, cols_d]
+    if dy_in is not None:
+        dy_in = _f64(dy_in)
+        dy_rows = dy_rows + dy_in[rows]
+        dy_cols = dy_cols + dy_in[:, cols_d]
+    h = n * gamma[None, :]
+    return {"rows": rows, "cols_d": cols_d, "cols_2F": cols_2F, "rows_F": rows_F,
+            "dR_rows": dy_rows, "dX_rows": dy_rows @ W1.T, "dW1_cols": X.T @ dy_cols,
+            "dW_cols": h.T @ dgu[:, cols_2F], "dWd_rows": a[:, rows_F].T @ dz,
+            "dgamma": dgamma, "s": s, "c": c}

@@ -363,6 +363,134 @@ def pin_swiglu_sampled(O):
         _close(s["dWd_rows"], b["dWd"][rd], 1e-13, "swiglu sampled dWd")
 
 
+# -------------------------------------------------- MLP sub-layer (chained) pins
+
+def _mlp_case(seed, M, K, d, F, eps=1e-2):
+    g = _rng(seed)
+    return dict(X=g.standard_normal((M, K)), W1=g.standard_normal((K, d)) / math.sqrt(K),
+                R=g.standard_normal((M, d)), gamma=1 + 0.1 * g.standard_normal(d),
+                W=g.standard_normal((d, 2 * F)) / math.sqrt(d),
+                Wd=g.standard_normal((F, d)) / math.sqrt(F), dz=g.standard_normal((M, d)),
+                dy_in=g.standard_normal((M, d)), eps=eps)
+
+
+def _mlp_loss(O, c):
+    f = O.ref_mlp_fwd(c["X"], c["W1"], c["R"], c["gamma"], c["W"], c["Wd"], c["eps"])
+    return float(np.sum(c["dz"] * f["z"]) + np.sum(c["dy_in"] * f["y"]))
+
+
+def _mlp_bwd(O, c, dy_in=True):
+    f = O.ref_mlp_fwd(c["X"], c["W1"], c["R"], c["gamma"], c["W"], c["Wd"], c["eps"])
+    b = O.ref_mlp_bwd(c["X"], c["W1"], c["gamma"], c["W"], c["Wd"], f["y"], f["r"], f["gu"], f["a"],
+                      c["dz"], c["dy_in"] if dy_in else None)
+    return b, f
+
+
+def pin_mlp_finite_differences(O):
+    """Central differences of L = <dz, z> + <dy_in, y> through the whole chain
+    (projection + residual, RMS norm, SwiGLU, down projection), tiny shape."""
+    c = _mlp_case(51, 3, 4, 5, 3)
+    b, _ = _mlp_bwd(O, c)
+    grads = {"X": b["dX"], "W1": b["dW1"], "R": b["dR"], "gamma": b["dgamma"], "W": b["dW"],
+             "Wd": b["dWd"]}
+    for name, grad in grads.items():
+        base = c[name]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            hstep = 1e-6 * max(1.0, abs(base[idx]))
+            cp = dict(c)
+            arr = base.copy(); arr[idx] += hstep; cp[name] = arr
+            lp = _mlp_loss(O, cp)
+            arr = base.copy(); arr[idx] -= hstep; cp[name] = arr
+            lm = _mlp_loss(O, cp)
+            fd[idx] = (lp - lm) / (2 * hstep)
+        _close(grad, fd, 1e-7, f"mlp d{name} vs finite differences")
+
+
+def pin_mlp_torch(O):
+    """torch CPU float64: matmul + add, F.rms_norm, matmul, F.silu(g) * u,
+    matmul, with autograd of <dz, z> + <dy_in, y> (library routines)."""
+    import torch
+    import torch.nn.functional as Fn
+    c = _mlp_case(52, 12, 20, 16, 12, eps=1e-5)
+    t = {k: torch.tensor(np.asarray(c[k]), requires_grad=True) for k in ("X", "W1", "R", "gamma", "W", "Wd")}
+    y = t["X"] @ t["W1"] + t["R"]
+    gu = Fn.rms_norm(y, (y.shape[1],), t["gamma"], c["eps"]) @ t["W"]
+    F = c["W"].shape[1] // 2
+    z = (Fn.silu(gu[:, :F]) * gu[:, F:]) @ t["Wd"]
+    ((z * torch.from_numpy(c["dz"])).sum() + (y * torch.from_numpy(c["dy_in"])).sum()).backward()
+    b, f = _mlp_bwd(O, c)
+    _close(f["z"], z.detach().numpy(), 1e-13, "mlp z vs torch")
+    _close(f["gu"], gu.detach().numpy(), 1e-13, "mlp gu vs torch")
+    for k in ("X", "W1", "R", "gamma", "W", "Wd"):
+        _close(b["d" + k], t[k].grad.numpy(), 1e-12, f"mlp d{k} vs torch")
+
+
+def pin_mlp_invariants(O):
+    """<dWd, Wd> = <dW[:, F:], W[:, F:]> = <dz, z> (z is linear in Wd and in
+    W_up); without dy_in, sum_j dy_ij y_ij = eps r_i^3 s_i (z depends on y only
+    through diag(r) y, which is homogeneous of degree 0 at eps = 0); dy_in
+    passes into dR, dX and dW1 unchanged: dR(dy_in) - dR(0) = dy_in."""
+    c = _mlp_case(53, 9, 10, 12, 7, eps=0.05)
+    b, f = _mlp_bwd(O, c, dy_in=False)
+    L = float(np.sum(c["dz"] * f["z"]))
+    F = 7
+    _close(np.sum(b["dWd"] * c["Wd"]), L, 1e-12, "mlp <dWd,Wd>")
+    _close(np.sum(b["dW"][:, F:] * c["W"][:, F:]), L, 1e-12, "mlp <dWu,Wu>")
+    _close(np.sum(b["dR"] * f["y"], axis=1), c["eps"] * f["r"] ** 3 * b["s"], 1e-12, "mlp row identity")
+    b1, _ = _mlp_bwd(O, c, dy_in=True)
+    _close(b1["dR"] - b["dR"], c["dy_in"], 1e-12, "dy_in into dR")
+    _close(b1["dX"] - b["dX"], c["dy_in"] @ c["W1"].T, 1e-12, "dy_in into dX")
+    _close(b1["dW"], b["dW"], 1e-13, "dy_in does not reach dW")
+
+
+def pin_mlp_sampled(O):
+    """Row/column-restricted MLP forms equal slices of the full forms."""
+    c = _mlp_case(54, 20, 12, 16, 10, eps=1e-4)
+    f = O.ref_mlp_fwd(c["X"], c["W1"], c["R"], c["gamma"], c["W"], c["Wd"], c["eps"])
+    rows = np.array([0, 7, 19])
+    fr = O.ref_mlp_fwd_rows(c["X"], c["W1"], c["R"], c["gamma"], c["W"], c["Wd"], c["eps"], rows)
+    for k in ("y", "r", "gu", "a", "z"):
+        _close(fr[k], f[k][rows], 1e-14, f"mlp rows {k}")
+    cd, c2, rf = np.array([1, 5, 15]), np.array([0, 9, 11, 19]), np.array([2, 3, 9])
+    for dy_in in (None, c["dy_in"]):
+        b = O.ref_mlp_bwd(c["X"], c["W1"], c["gamma"], c["W"], c["Wd"], f["y"], f["r"], f["gu"], f["a"],
+                          c["dz"], dy_in)
+        bs = O.ref_mlp_bwd_sampled(c["X"], c["W1"], c["gamma"], c["W"], c["Wd"], f["y"], f["r"], f["gu"],
+                                   f["a"], c["dz"], dy_in, rows, cd, c2, rf)
+        _close(bs["dX_rows"], b["dX"][rows], 1e-13, "mlp sampled dX")
+        _close(bs["dR_rows"], b["dR"][rows], 1e-13, "mlp sampled dR")
+        _close(bs["dW1_cols"], b["dW1"][:, cd], 1e-13, "mlp sampled dW1")
+        _close(bs["dW_cols"], b["dW"][:, c2], 1e-13, "mlp sampled dW")
+        _close(bs["dWd_rows"], b["dWd"][rf], 1e-13, "mlp sampled dWd")
+        _close(bs["dgamma"], b["dgamma"], 1e-13, "mlp sampled dgamma")
+
+
+def pin_bwd_dy_in_finite_differences(O):
+    """``ref_bwd`` with dy_in: central differences of <dz, z> + <dy_in, y> for
+    the block's own forward, tiny shape."""
+    c = _coda_case(25, 3, 4, 5, 6, eps=1e-2)
+    dy_in = _rng(26).standard_normal((3, 5))
+
+    def loss(cc):
+        f = O.ref_fwd(cc["X"], cc["W1"], cc["R"], cc["gamma"], cc["W2"], cc["eps"])
+        return float(np.sum(cc["dz"] * f["z"]) + np.sum(dy_in * f["y"]))
+    f = O.ref_fwd(c["X"], c["W1"], c["R"], c["gamma"], c["W2"], c["eps"])
+    b = O.ref_bwd(c["X"], c["W1"], c["gamma"], c["W2"], f["y"], f["r"], c["dz"], dy_in)
+    for name, grad in (("X", b["dX"]), ("W1", b["dW1"]), ("R", b["dR"])):
+        base = c[name]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            hstep = 1e-6 * max(1.0, abs(base[idx]))
+            cp = dict(c)
+            arr = base.copy(); arr[idx] += hstep; cp[name] = arr
+            lp = loss(cp)
+            arr = base.copy(); arr[idx] -= hstep; cp[name] = arr
+            lm = loss(cp)
+            fd[idx] = (lp - lm) / (2 * hstep)
+        _close(grad, fd, 1e-7, f"dy_in: d{name} vs finite differences")
+
+
 # ------------------------------------------------------------------- bf16 pins
 
 def pin_bf16_rne(O):
@@ -396,5 +524,6 @@ ALL_PINS = [
     pin_golden_coda, pin_bwd_finite_differences, pin_bwd_torch_autograd,
     pin_bwd_invariants, pin_sampled_forms, pin_swiglu_bruteforce,
     pin_swiglu_finite_differences, pin_swiglu_torch, pin_swiglu_invariants,
-    pin_golden_swiglu, pin_swiglu_sampled, pin_bf16_rne,
+    pin_golden_swiglu, pin_swiglu_sampled, pin_bf16_rne, pin_mlp_finite_differences,
+    pin_mlp_torch, pin_mlp_invariants, pin_mlp_sampled, pin_bwd_dy_in_finite_differences,
 ]

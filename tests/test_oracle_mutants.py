@@ -44,7 +44,7 @@ def fwd_no_residual(X, W1, R, gamma, W2, eps):
 
 
 def _bwd_variant(kind):
-    def bwd(X, W1, gamma, W2, y, r, dz):
+    def bwd(X, W1, gamma, W2, y, r, dz, dy_in=None):
         X, W1, gamma, W2, y, r, dz = _f(X, W1, gamma, W2, y, r, dz)
         d = y.shape[1]
         n = y * r[:, None]
@@ -63,6 +63,8 @@ def _bwd_variant(kind):
             dy = dn * r[:, None] - (r ** 2 * s / d)[:, None] * y
         else:
             dy = dn * r[:, None] - c[:, None] * y
+        if dy_in is not None:
+            dy = dy + np.asarray(dy_in, dtype=np.float64)
         dX = dy @ W1.T
         dW1 = (X.T @ dn) if kind == "dW1_uses_dn" else (X.T @ dy)
         if kind == "dW2_no_gamma":
@@ -110,6 +112,41 @@ def swiglu_bwd_transposed(X, W, Wd, gu, a, dz):
     return out
 
 
+def _mlp_fwd_variant(kind):
+    def fwd(X, W1, R, gamma, W, Wd, eps):
+        X, W1, R, gamma, W, Wd = _f(X, W1, R, gamma, W, Wd)
+        y = X @ W1 + R
+        r = 1.0 / np.sqrt(np.mean(y * y, axis=1) + eps)
+        h = y * (1.0 if kind == "r_after_silu" else r[:, None]) * gamma[None, :]
+        F = W.shape[1] // 2
+        gu = h @ W
+        g, u = gu[:, :F], gu[:, F:]
+        a = g * oracle.sigmoid(g) * u
+        if kind == "r_after_silu":
+            a = a * r[:, None]
+        return {"y": y, "r": r, "h": h, "gu": gu, "a": a, "z": a @ Wd}
+    return fwd
+
+
+def _mlp_bwd_variant(kind):
+    def bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in=None):
+        if kind == "drop_dy_in":
+            dy_in = None
+        if kind == "dy_in_sign" and dy_in is not None:
+            dy_in = -np.asarray(dy_in, dtype=np.float64)
+        out = dict(oracle.ref_mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in))
+        if kind == "dW_without_r":
+            F = np.asarray(W).shape[1] // 2
+            out["dW"] = (np.asarray(y, dtype=np.float64) * np.asarray(gamma)[None, :]).T @ out["dgu"]
+        if kind == "dgu_halves_swapped":
+            Fh = out["dgu"].shape[1] // 2
+            dgu = np.concatenate([out["dgu"][:, Fh:], out["dgu"][:, :Fh]], axis=1)
+            b = oracle.ref_bwd(X, W1, gamma, W, y, r, dgu, dy_in)
+            out.update({"dX": b["dX"], "dW1": b["dW1"], "dR": b["dR"], "dW": b["dW2"], "dgamma": b["dgamma"]})
+        return out
+    return bwd
+
+
 def bf16_half_away(x):
     x = np.asarray(x, dtype=np.float64)
     out = np.array(x, copy=True)
@@ -143,6 +180,11 @@ MUTANTS = {
     "swiglu_bwd_missing_factor": {"ref_swiglu_bwd": swiglu_bwd_no_factor},
     "swiglu_bwd_dWd_columns": {"ref_swiglu_bwd": swiglu_bwd_transposed},
     "bf16_ties_away": {"bf16_rne": bf16_half_away},
+    "mlp_r_after_silu": {"ref_mlp_fwd": _mlp_fwd_variant("r_after_silu")},
+    "mlp_bwd_drops_dy_in": {"ref_mlp_bwd": _mlp_bwd_variant("drop_dy_in")},
+    "mlp_bwd_dy_in_sign": {"ref_mlp_bwd": _mlp_bwd_variant("dy_in_sign")},
+    "mlp_bwd_dW_without_r": {"ref_mlp_bwd": _mlp_bwd_variant("dW_without_r")},
+    "mlp_bwd_dgu_halves_swapped": {"ref_mlp_bwd": _mlp_bwd_variant("dgu_halves_swapped")},
     "bf16_double_rounding": {"bf16_rne": bf16_via_f32},
 }
 
