@@ -342,7 +342,7 @@ def ref_swiglu_bwd_sampled(X, W, Wd, dz, rows, cols_W, rows_Wd, saved_bf16: bool
 # The two patterns chained: a LLaMA MLP sub-layer
 # ---------------------------------------------------------------------------
 
-def ref_mlp_fwd(X, W1, R, gamma, W, Wd, eps: float) -> dict:
+def ref_mlp_fwd(X, W1, R, gamma, W, Wd, eps: float, h_round=None) -> dict:
     """Projection + residual, RMS normalisation, SwiGLU gate/up, down projection.
 
     y = X W1 + R;  r_i = (mean_j y_ij^2 + eps)^(-1/2);  h = diag(r) y diag(gamma);
@@ -350,22 +350,36 @@ def ref_mlp_fwd(X, W1, R, gamma, W, Wd, eps: float) -> dict:
     a = g sigmoid(g) u;  z = a Wd.
     ([RU]/[FR] insight sections for the residual + RMS pattern around a
     matmul; [JA]/[RU]/[FR] primitives sections for SwiGLU as the activation.)
+
+    With the row scale deferred past the gate/up GEMM (the insight sections'
+    rewrite), the GEMM's input is y diag(gamma), an intermediate a fused path
+    stores between the two GEMMs; ``h_round``, if given, is applied to it:
+    gu = diag(r) (h_round(y diag(gamma)) W).  Without it, gu = h W exactly.
     """
     X, W1, R, gamma, W, Wd = map(_f64, (X, W1, R, gamma, W, Wd))
     y = X @ W1 + R
     r = 1.0 / np.sqrt(np.mean(y * y, axis=1) + eps)
     h = y * r[:, None] * gamma[None, :]
     F = W.shape[1] // 2
-    gu = h @ W
+    if h_round is None:
+        gu = h @ W
+    else:
+        gu = r[:, None] * (_f64(h_round(y * gamma[None, :])) @ W)
     g, u = gu[:, :F], gu[:, F:]
     a = g * sigmoid(g) * u
     z = a @ Wd
     return {"y": y, "r": r, "h": h, "gu": gu, "a": a, "z": z}
 
 
-def ref_mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in=None) -> dict:
+def ref_mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in=None, dgu_round=None) -> dict:
     """Exact gradient of L = <dz, z> (+ <dy_in, y>) for ``ref_mlp_fwd``, given
     the saved y, r, gu and a.
+
+    dgu is the one intermediate of this backward that a fused path must store
+    between its two halves (the primitives sections' tile store of
+    intermediates); ``dgu_round``, if given, is applied to it before the second
+    half, so that the oracle can follow the storage contract the way the
+    callers pass the saved y rounded (e.g. ``bf16_rne``).
 
     The SwiGLU part first, from the saved gu and a (as ``ref_swiglu_bwd``):
       da = dz Wd^T;  dg = da u sg (1 + g (1 - sg));  du = da g sg;
@@ -383,28 +397,30 @@ def ref_mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in=None) -> dict:
     du = da * g * sg
     dgu = np.concatenate([dg, du], axis=1)
     dWd = a.T @ dz
+    if dgu_round is not None:
+        dgu = _f64(dgu_round(dgu))
     b = ref_bwd(X, W1, gamma, W, y, r, dgu, dy_in)
     return {"dX": b["dX"], "dW1": b["dW1"], "dR": b["dR"], "dW": b["dW2"], "dWd": dWd,
             "dgamma": b["dgamma"], "dgu": dgu, "da": da, "dh": b["dh"], "s": b["s"], "c": b["c"]}
 
 
-def ref_mlp_fwd_rows(X, W1, R, gamma, W, Wd, eps: float, rows) -> dict:
+def ref_mlp_fwd_rows(X, W1, R, gamma, W, Wd, eps: float, rows, h_round=None) -> dict:
     """``ref_mlp_fwd`` evaluated for the given rows only (rows are independent)."""
     rows = np.asarray(rows)
-    out = ref_mlp_fwd(_f64(X[rows]), W1, _f64(R[rows]), gamma, W, Wd, eps)
+    out = ref_mlp_fwd(_f64(X[rows]), W1, _f64(R[rows]), gamma, W, Wd, eps, h_round)
     out["rows"] = rows
     return out
 
 
 def ref_mlp_bwd_sampled(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in, rows, cols_d, cols_2F,
-                        rows_F) -> dict:
+                        rows_F, dgu_round=None) -> dict:
     """``ref_mlp_bwd`` with dX and dR restricted to ``rows``, dW1 to the columns
     ``cols_d``, dW to the columns ``cols_2F``, dWd to the rows ``rows_F``;
     dgamma, s and c in full.
 
     s and c need every row's dh, so dgu (from da = dz Wd^T) and dh = dgu W^T
     are formed whole.  The rest is the definitions restricted.  dy_in may be
-    None.
+    None.  ``dgu_round`` as in ``ref_mlp_bwd``.
     """
     X, W1, gamma, W, Wd, y, r, gu, a, dz = map(_f64, (X, W1, gamma, W, Wd, y, r, gu, a, dz))
     d = y.shape[1]
@@ -413,6 +429,8 @@ def ref_mlp_bwd_sampled(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in, rows, cols_
     sg = sigmoid(g)
     da = dz @ Wd.T
     dgu = np.concatenate([da * u * sg * (1.0 + g * (1.0 - sg)), da * g * sg], axis=1)
+    if dgu_round is not None:
+        dgu = _f64(dgu_round(dgu))
     n = y * r[:, None]
     dh = dgu @ W.T
     dgamma = np.sum(dh * n, axis=0)

@@ -452,18 +452,75 @@ def pin_mlp_sampled(O):
     fr = O.ref_mlp_fwd_rows(c["X"], c["W1"], c["R"], c["gamma"], c["W"], c["Wd"], c["eps"], rows)
     for k in ("y", "r", "gu", "a", "z"):
         _close(fr[k], f[k][rows], 1e-14, f"mlp rows {k}")
+    fq = O.ref_mlp_fwd(c["X"], c["W1"], c["R"], c["gamma"], c["W"], c["Wd"], c["eps"], O.bf16_rne)
+    fqr = O.ref_mlp_fwd_rows(c["X"], c["W1"], c["R"], c["gamma"], c["W"], c["Wd"], c["eps"], rows, O.bf16_rne)
+    for k in ("gu", "a", "z"):
+        _close(fqr[k], fq[k][rows], 1e-14, f"mlp rows (stored operand) {k}")
     cd, c2, rf = np.array([1, 5, 15]), np.array([0, 9, 11, 19]), np.array([2, 3, 9])
-    for dy_in in (None, c["dy_in"]):
+    for dy_in, rnd in ((None, None), (c["dy_in"], None), (c["dy_in"], O.bf16_rne)):
         b = O.ref_mlp_bwd(c["X"], c["W1"], c["gamma"], c["W"], c["Wd"], f["y"], f["r"], f["gu"], f["a"],
-                          c["dz"], dy_in)
+                          c["dz"], dy_in, rnd)
         bs = O.ref_mlp_bwd_sampled(c["X"], c["W1"], c["gamma"], c["W"], c["Wd"], f["y"], f["r"], f["gu"],
-                                   f["a"], c["dz"], dy_in, rows, cd, c2, rf)
+                                   f["a"], c["dz"], dy_in, rows, cd, c2, rf, rnd)
         _close(bs["dX_rows"], b["dX"][rows], 1e-13, "mlp sampled dX")
         _close(bs["dR_rows"], b["dR"][rows], 1e-13, "mlp sampled dR")
         _close(bs["dW1_cols"], b["dW1"][:, cd], 1e-13, "mlp sampled dW1")
         _close(bs["dW_cols"], b["dW"][:, c2], 1e-13, "mlp sampled dW")
         _close(bs["dWd_rows"], b["dWd"][rf], 1e-13, "mlp sampled dWd")
         _close(bs["dgamma"], b["dgamma"], 1e-13, "mlp sampled dgamma")
+
+
+def pin_mlp_dgu_rounding(O):
+    """With dgu rounded for storage, the second half is the block backward of
+    ``ref_bwd`` fed that rounded dgu (the MLP's dh GEMM input), and the
+    rounding only moves what depends on dgu: dWd and dgu's own first half
+    stay as without it."""
+    c = _mlp_case(55, 10, 12, 16, 9, eps=1e-3)
+    f = O.ref_mlp_fwd(c["X"], c["W1"], c["R"], c["gamma"], c["W"], c["Wd"], c["eps"])
+    b0 = O.ref_mlp_bwd(c["X"], c["W1"], c["gamma"], c["W"], c["Wd"], f["y"], f["r"], f["gu"], f["a"],
+                       c["dz"], c["dy_in"])
+    b1 = O.ref_mlp_bwd(c["X"], c["W1"], c["gamma"], c["W"], c["Wd"], f["y"], f["r"], f["gu"], f["a"],
+                       c["dz"], c["dy_in"], O.bf16_rne)
+    # dgu from its definition, independent of O's intermediates
+    F = 9
+    g, u = f["gu"][:, :F], f["gu"][:, F:]
+    sg = 1.0 / (1.0 + np.exp(-g))
+    da = c["dz"] @ c["Wd"].T
+    dgu = np.concatenate([da * u * sg * (1 + g * (1 - sg)), da * g * sg], axis=1)
+    dgu_r = O.bf16_rne(dgu)           # pinned on its own by pin_bf16_rne
+    ref = O.ref_bwd(c["X"], c["W1"], c["gamma"], c["W"], f["y"], f["r"], dgu_r, c["dy_in"])
+    _close(b1["dW"], ref["dW2"], 1e-12, "rounded dgu: dW")
+    _close(b1["dgamma"], ref["dgamma"], 1e-12, "rounded dgu: dgamma")
+    _close(b1["dX"], ref["dX"], 1e-12, "rounded dgu: dX")
+    _close(b1["dWd"], b0["dWd"], 1e-15, "rounding dgu leaves dWd")
+    assert float(np.max(np.abs(b1["dgamma"] - b0["dgamma"]))) > 0.0, "rounding had no effect"
+
+
+def pin_mlp_stored_operand_bruteforce(O):
+    """With the gate/up GEMM's stored input rounded (h_round = bf16_rne),
+    pure-Python loops over a tiny case: y = X W1 + R, r from y,
+    gu_ij = r_i * sum_k round(y_ik gamma_k) W_kj, a = g sigmoid(g) u, z = a Wd;
+    y and r do not depend on the rounding."""
+    c = _mlp_case(56, 3, 4, 5, 2, eps=1e-3)
+    X, W1, R, gm, W, Wd = (c[k] for k in ("X", "W1", "R", "gamma", "W", "Wd"))
+    M, K = X.shape
+    d, F = W1.shape[1], 2
+    f = O.ref_mlp_fwd(X, W1, R, gm, W, Wd, c["eps"], O.bf16_rne)
+    f0 = O.ref_mlp_fwd(X, W1, R, gm, W, Wd, c["eps"])
+    for i in range(M):
+        y = [sum(X[i][k] * W1[k][j] for k in range(K)) + R[i][j] for j in range(d)]
+        r = 1.0 / math.sqrt(sum(v * v for v in y) / d + c["eps"])
+        hy = [float(O.bf16_rne(np.array([y[k] * gm[k]]))[0]) for k in range(d)]
+        gu = [r * sum(hy[k] * W[k][j] for k in range(d)) for j in range(2 * F)]
+        a = [gu[j] / (1.0 + math.exp(-gu[j])) * gu[F + j] for j in range(F)]
+        z = [sum(a[j] * Wd[j][m] for j in range(F)) for m in range(d)]
+        _close(f["y"][i], y, 1e-13, "stored operand: y")
+        _close(f["r"][i], r, 1e-13, "stored operand: r")
+        _close(f["gu"][i], gu, 1e-13, "stored operand: gu")
+        _close(f["a"][i], a, 1e-13, "stored operand: a")
+        _close(f["z"][i], z, 1e-13, "stored operand: z")
+    _close(f["y"], f0["y"], 0.0, "rounding leaves y")
+    assert float(np.max(np.abs(f["gu"] - f0["gu"]))) > 0.0, "rounding had no effect"
 
 
 def pin_bwd_dy_in_finite_differences(O):
@@ -525,5 +582,7 @@ ALL_PINS = [
     pin_bwd_invariants, pin_sampled_forms, pin_swiglu_bruteforce,
     pin_swiglu_finite_differences, pin_swiglu_torch, pin_swiglu_invariants,
     pin_golden_swiglu, pin_swiglu_sampled, pin_bf16_rne, pin_mlp_finite_differences,
-    pin_mlp_torch, pin_mlp_invariants, pin_mlp_sampled, pin_bwd_dy_in_finite_differences,
+    pin_mlp_torch, pin_mlp_invariants, pin_mlp_sampled, pin_mlp_dgu_rounding,
+    pin_mlp_stored_operand_bruteforce,
+    pin_bwd_dy_in_finite_differences,
 ]

@@ -113,13 +113,16 @@ def swiglu_bwd_transposed(X, W, Wd, gu, a, dz):
 
 
 def _mlp_fwd_variant(kind):
-    def fwd(X, W1, R, gamma, W, Wd, eps):
+    def fwd(X, W1, R, gamma, W, Wd, eps, h_round=None):
         X, W1, R, gamma, W, Wd = _f(X, W1, R, gamma, W, Wd)
         y = X @ W1 + R
         r = 1.0 / np.sqrt(np.mean(y * y, axis=1) + eps)
         h = y * (1.0 if kind == "r_after_silu" else r[:, None]) * gamma[None, :]
         F = W.shape[1] // 2
-        gu = h @ W
+        if kind == "round_inside_r" or h_round is None:
+            gu = (h_round(h) if h_round is not None else h) @ W
+        else:
+            gu = r[:, None] * (h_round(y * gamma[None, :]) @ W)
         g, u = gu[:, :F], gu[:, F:]
         a = g * oracle.sigmoid(g) * u
         if kind == "r_after_silu":
@@ -129,18 +132,20 @@ def _mlp_fwd_variant(kind):
 
 
 def _mlp_bwd_variant(kind):
-    def bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in=None):
+    def bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in=None, dgu_round=None):
         if kind == "drop_dy_in":
             dy_in = None
         if kind == "dy_in_sign" and dy_in is not None:
             dy_in = -np.asarray(dy_in, dtype=np.float64)
-        out = dict(oracle.ref_mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in))
+        out = dict(oracle.ref_mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in, dgu_round))
         if kind == "dW_without_r":
             F = np.asarray(W).shape[1] // 2
             out["dW"] = (np.asarray(y, dtype=np.float64) * np.asarray(gamma)[None, :]).T @ out["dgu"]
         if kind == "dgu_halves_swapped":
             Fh = out["dgu"].shape[1] // 2
             dgu = np.concatenate([out["dgu"][:, Fh:], out["dgu"][:, :Fh]], axis=1)
+            if dgu_round is not None:
+                dgu = dgu_round(dgu)
             b = oracle.ref_bwd(X, W1, gamma, W, y, r, dgu, dy_in)
             out.update({"dX": b["dX"], "dW1": b["dW1"], "dR": b["dR"], "dW": b["dW2"], "dgamma": b["dgamma"]})
         return out
@@ -181,10 +186,12 @@ MUTANTS = {
     "swiglu_bwd_dWd_columns": {"ref_swiglu_bwd": swiglu_bwd_transposed},
     "bf16_ties_away": {"bf16_rne": bf16_half_away},
     "mlp_r_after_silu": {"ref_mlp_fwd": _mlp_fwd_variant("r_after_silu")},
+    "mlp_round_inside_r": {"ref_mlp_fwd": _mlp_fwd_variant("round_inside_r")},
     "mlp_bwd_drops_dy_in": {"ref_mlp_bwd": _mlp_bwd_variant("drop_dy_in")},
     "mlp_bwd_dy_in_sign": {"ref_mlp_bwd": _mlp_bwd_variant("dy_in_sign")},
     "mlp_bwd_dW_without_r": {"ref_mlp_bwd": _mlp_bwd_variant("dW_without_r")},
     "mlp_bwd_dgu_halves_swapped": {"ref_mlp_bwd": _mlp_bwd_variant("dgu_halves_swapped")},
+    "mlp_bwd_ignores_dgu_round": {"ref_mlp_bwd": (lambda *a, **k: oracle.ref_mlp_bwd(*a[:11]))},
     "bf16_double_rounding": {"bf16_rne": bf16_via_f32},
 }
 
