@@ -1,4 +1,5 @@
-"""MI355X-native fused GEMM-Residual-RMSNorm-GEMM block and SwiGLU block.
+"""MI355X-native fused GEMM-Residual-RMSNorm-GEMM block, SwiGLU block, and the
+two chained as an MLP sub-layer.
 
 Thin Python binding over the C-ABI library ``libcoda.so`` (include/coda.h).
 Every step of the computation runs in the library's HIP kernels; this module
@@ -8,12 +9,15 @@ PyTorch fallback: without the built library every call raises.
 
 Low-level calls (same names and argument order as the C functions, outputs
 preallocated by the caller):
-    coda_fwd, coda_bwd, coda_swiglu_fwd, coda_swiglu_bwd
+    coda_fwd, coda_bwd, coda_swiglu_fwd, coda_swiglu_bwd, coda_mlp_fwd, coda_mlp_bwd
 Convenience calls (allocate outputs):
     fwd(X, W1, R, gamma, W2, eps)        -> (z, y, r)
     bwd(X, W1, gamma, W2, y, r, dz)      -> (dX, dW1, dR, dW2, dgamma)
     swiglu_fwd(X, W, Wd)                 -> (z, gu, a)
     swiglu_bwd(X, W, Wd, gu, a, dz)      -> (dX, dW, dWd)
+    mlp_fwd(X, W1, R, gamma, W, Wd, eps) -> (z, y, r, gu, a)
+    mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in=None)
+                                         -> (dX, dW1, dR, dW, dWd, dgamma)
 """
 from __future__ import annotations
 
@@ -22,9 +26,10 @@ import os
 
 __all__ = [
     "CodaError", "lib_path", "load_library", "coda_fwd", "coda_bwd", "coda_swiglu_fwd",
-    "coda_swiglu_bwd", "fwd", "bwd", "swiglu_fwd", "swiglu_bwd", "fwd_workspace_bytes",
-    "bwd_workspace_bytes", "swiglu_bwd_workspace_bytes", "version", "trace_start",
-    "trace_read", "trace_stop",
+    "coda_swiglu_bwd", "coda_mlp_fwd", "coda_mlp_bwd", "fwd", "bwd", "swiglu_fwd",
+    "swiglu_bwd", "mlp_fwd", "mlp_bwd", "fwd_workspace_bytes", "bwd_workspace_bytes",
+    "swiglu_bwd_workspace_bytes", "mlp_fwd_workspace_bytes", "mlp_bwd_workspace_bytes",
+    "version", "trace_start", "trace_read", "trace_stop",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -69,6 +74,8 @@ def load_library() -> ctypes.CDLL:
         "coda_bwd_workspace_bytes": [i32, i64, i64, i64, i64],
         "coda_swiglu_fwd_workspace_bytes": [i32, i64, i64, i64],
         "coda_swiglu_bwd_workspace_bytes": [i32, i64, i64, i64],
+        "coda_mlp_fwd_workspace_bytes": [i32, i64, i64, i64, i64],
+        "coda_mlp_bwd_workspace_bytes": [i32, i64, i64, i64, i64],
     }.items():
         getattr(L, name).restype = sz
         getattr(L, name).argtypes = args
@@ -80,6 +87,10 @@ def load_library() -> ctypes.CDLL:
     L.coda_swiglu_fwd.argtypes = [i32, i64, i64, i64] + [vp] * 6 + [vp, sz, vp]
     L.coda_swiglu_bwd.restype = i32
     L.coda_swiglu_bwd.argtypes = [i32, i64, i64, i64] + [vp] * 9 + [vp, sz, vp]
+    L.coda_mlp_fwd.restype = i32
+    L.coda_mlp_fwd.argtypes = [i32, i64, i64, i64, i64, f32] + [vp] * 11 + [vp, sz, vp]
+    L.coda_mlp_bwd.restype = i32
+    L.coda_mlp_bwd.argtypes = [i32, i64, i64, i64, i64] + [vp] * 17 + [vp, sz, vp]
     L.coda_trace_start.restype = i32
     L.coda_trace_start.argtypes = [i32]
     L.coda_trace_count.restype = i32
@@ -151,6 +162,14 @@ def swiglu_bwd_workspace_bytes(dtype_code, M, d, F) -> int:
     return int(load_library().coda_swiglu_bwd_workspace_bytes(dtype_code, M, d, F))
 
 
+def mlp_fwd_workspace_bytes(dtype_code, M, K, d, F) -> int:
+    return int(load_library().coda_mlp_fwd_workspace_bytes(dtype_code, M, K, d, F))
+
+
+def mlp_bwd_workspace_bytes(dtype_code, M, K, d, F) -> int:
+    return int(load_library().coda_mlp_bwd_workspace_bytes(dtype_code, M, K, d, F))
+
+
 # ------------------------------------------------------------ tracing
 
 def trace_start(capacity: int) -> None:
@@ -216,6 +235,29 @@ def coda_swiglu_bwd(X, W, Wd, gu, a, dz, dX, dW, dWd, workspace):
         _ptr(dX), _ptr(dW), _ptr(dWd), _ptr(workspace), workspace.numel(), _stream()))
 
 
+def coda_mlp_fwd(X, W1, R, gamma, W, Wd, eps, y, r, gu, a, z, workspace):
+    L = load_library()
+    M, K = X.shape
+    d = W1.shape[1]
+    F = Wd.shape[0]
+    _check("coda_mlp_fwd", L.coda_mlp_fwd(
+        _dtype_code(X), M, K, d, F, float(eps), _ptr(X), _ptr(W1), _ptr(R), _ptr(gamma), _ptr(W),
+        _ptr(Wd), _ptr(y), _ptr(r), _ptr(gu), _ptr(a), _ptr(z), _ptr(workspace), workspace.numel(),
+        _stream()))
+
+
+def coda_mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in, dX, dW1, dR, dW, dWd, dgamma,
+                 workspace):
+    L = load_library()
+    M, K = X.shape
+    d = W1.shape[1]
+    F = Wd.shape[0]
+    _check("coda_mlp_bwd", L.coda_mlp_bwd(
+        _dtype_code(X), M, K, d, F, _ptr(X), _ptr(W1), _ptr(gamma), _ptr(W), _ptr(Wd), _ptr(y),
+        _ptr(r), _ptr(gu), _ptr(a), _ptr(dz), _ptr(dy_in), _ptr(dX), _ptr(dW1), _ptr(dR), _ptr(dW),
+        _ptr(dWd), _ptr(dgamma), _ptr(workspace), workspace.numel(), _stream()))
+
+
 # ------------------------------------------------------ convenience calls
 
 def fwd(X, W1, R, gamma, W2, eps):
@@ -274,3 +316,44 @@ def swiglu_bwd(X, W, Wd, gu, a, dz):
     ws = _workspace(swiglu_bwd_workspace_bytes(_dtype_code(X), M, d, F), X.device)
     coda_swiglu_bwd(X, W, Wd, gu, a, dz, dX, dW, dWd, ws)
     return dX, dW, dWd
+
+
+def mlp_fwd(X, W1, R, gamma, W, Wd, eps):
+    """The MLP sub-layer: z = silu(g) u Wd with [g | u] = RMSNorm(X W1 + R) * gamma @ W,
+    fused.  Returns (z, y, r, gu, a)."""
+    import torch
+    M, K = X.shape
+    d = W1.shape[1]
+    F = Wd.shape[0]
+    _shape(W1, K, d, name="W1"); _shape(R, M, d, name="R"); _shape(gamma, d, name="gamma")
+    _shape(W, d, 2 * F, name="W"); _shape(Wd, F, d, name="Wd")
+    y = torch.empty((M, d), dtype=X.dtype, device=X.device)
+    r = torch.empty((M,), dtype=torch.float32, device=X.device)
+    gu = torch.empty((M, 2 * F), dtype=X.dtype, device=X.device)
+    a = torch.empty((M, F), dtype=X.dtype, device=X.device)
+    z = torch.empty((M, d), dtype=X.dtype, device=X.device)
+    ws = _workspace(mlp_fwd_workspace_bytes(_dtype_code(X), M, K, d, F), X.device)
+    coda_mlp_fwd(X, W1, R, gamma, W, Wd, eps, y, r, gu, a, z, ws)
+    return z, y, r, gu, a
+
+
+def mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in=None):
+    """Gradients of <dz, z> + <dy_in, y> from the saved (y, r, gu, a).
+    Returns (dX, dW1, dR, dW, dWd, dgamma)."""
+    import torch
+    M, K = X.shape
+    d = W1.shape[1]
+    F = Wd.shape[0]
+    _shape(y, M, d, name="y"); _shape(r, M, name="r"); _shape(gu, M, 2 * F, name="gu")
+    _shape(a, M, F, name="a"); _shape(dz, M, d, name="dz")
+    if dy_in is not None:
+        _shape(dy_in, M, d, name="dy_in")
+    dX = torch.empty_like(X)
+    dW1 = torch.empty_like(W1)
+    dR = torch.empty((M, d), dtype=X.dtype, device=X.device)
+    dW = torch.empty_like(W)
+    dWd = torch.empty_like(Wd)
+    dgamma = torch.empty((d,), dtype=torch.float32, device=X.device)
+    ws = _workspace(mlp_bwd_workspace_bytes(_dtype_code(X), M, K, d, F), X.device)
+    coda_mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in, dX, dW1, dR, dW, dWd, dgamma, ws)
+    return dX, dW1, dR, dW, dWd, dgamma

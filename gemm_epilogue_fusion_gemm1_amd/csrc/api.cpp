@@ -133,6 +133,90 @@ GemmArgs gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, uint6
   return g;
 }
 
+// K1: y = X W1 + R; the epilogue stores y, yg = y * gamma (bf16: transposed,
+// [d, M]) and the per-tile partial sums of squares P.
+hipError_t launch_k1(bool bf, int64_t M, int64_t K, int64_t d, const void* X, const void* W1,
+                     const void* R, const void* gamma, void* y, const FwdWs& ws, float* P,
+                     void* yg, hipStream_t s) {
+  const double eb = bf ? 2.0 : 4.0;
+  GemmArgs g1 = gemm(M, d, K, X, K, M * K, W1, d, K * d, y, d);
+  g1.E = R;
+  g1.lde = d;
+  g1.part_row = P;
+  g1.ld_part_row = ws.Tn;
+  g1.C2 = yg;
+  g1.ldc2 = bf ? M : d;
+  g1.c2_trans = bf ? 1 : 0;
+  g1.vcol = gamma;
+  const double k1_bytes = (M * K + K * d + 3.0 * M * d + d) * eb + M * ws.Tn * 4.0;
+  return traced("k1_gemm_resid_sumsq", gemm_flops(M, d, K), k1_bytes, s, [&] {
+    return bf ? coda::launch_gemm_bf16(g1, true, false, coda::EPI_RESID_SUMSQ, s)
+              : coda::launch_gemm_f32(g1, coda::EPI_RESID_SUMSQ, s);
+  });
+}
+
+// The RMS-normalised block's backward after its second GEMM, given that
+// GEMM's output gradient dz [M, N] and weight W2 [d, N]: B1 (dh = dz W2^T and
+// the dn / n / s / dgamma epilogue), R2, E2 (dy, plus dy_in when not NULL),
+// B2 (dW2), B3 (dX), B4 (dW1).  `nm` names the six launches for tracing.
+hipError_t launch_norm_bwd(int64_t M, int64_t K, int64_t d, int64_t N, const void* X,
+                           const void* W1, const void* gamma, const void* W2, const void* y,
+                           const float* r, const void* dz, const void* dy_in, void* dX, void* dW1,
+                           void* dR, void* dW2, float* dgamma, const BwdWs& ws, char* wsb,
+                           const char* const (&nm)[6], hipStream_t s) {
+  void* n = wsb + ws.n;
+  float* S = (float*)(wsb + ws.S);
+  float* G = (float*)(wsb + ws.G);
+  float* c = (float*)(wsb + ws.c);
+  hipError_t err;
+
+  // B1: dh = dz W2^T; epilogue -> dn (into dR), row partials S, column partials G
+  GemmArgs b1 = gemm(M, d, N, dz, N, M * N, W2, N, d * N, dR, d);
+  b1.E = y;
+  b1.lde = d;
+  b1.vrow = r;
+  b1.vcol = gamma;
+  b1.part_row = S;
+  b1.ld_part_row = ws.Tn;
+  b1.part_col = G;
+  b1.ld_part_col = d;
+  b1.C2 = n;                      // n = r * y, the A operand of the dW2 GEMM
+  b1.ldc2 = d;
+  const double md = 2.0 * M * d, dn2 = 2.0 * d * N, mn = 2.0 * M * N, mk = 2.0 * M * K, kd = 2.0 * K * d;
+  if ((err = traced(nm[0], gemm_flops(M, d, N),
+                    mn + dn2 + 3.0 * md + M * ws.Tn * 4.0 + ws.Tm * d * 4.0 + M * 4.0 + 2.0 * d, s,
+                    [&] { return coda::launch_gemm_bf16(b1, true, true, coda::EPI_DN, s); })) !=
+      hipSuccess)
+    return err;
+  // R2: c = r^3 s / d, dgamma
+  if ((err = traced(nm[1], 0.0, M * ws.Tn * 4.0 + ws.Tm * d * 4.0 + 8.0 * M + 4.0 * d, s, [&] {
+         return coda::launch_bwd_reduce(S, ws.Tn, ws.Tn, r, M, d, G, ws.Tm, c, dgamma, s);
+       })) != hipSuccess)
+    return err;
+  // E2: dR = r dn - c y (+ dy_in), in place
+  if ((err = traced(nm[2], 0.0, (dy_in ? 4.0 : 3.0) * md + 8.0 * M, s,
+                    [&] { return coda::launch_dy(dR, y, r, c, dy_in, M, d, s); })) != hipSuccess)
+    return err;
+  // B2: dW2 = diag(gamma) n^T dz
+  GemmArgs b2 = gemm(d, N, M, n, d, M * d, dz, N, M * N, dW2, N);
+  b2.vcol = gamma;
+  if ((err = traced(nm[3], gemm_flops(d, N, M), md + mn + dn2 + 2.0 * d, s, [&] {
+         return coda::launch_gemm_bf16(b2, false, false, coda::EPI_ROWSCALE, s);
+       })) != hipSuccess)
+    return err;
+  // B3: dX = dy W1^T
+  GemmArgs b3 = gemm(M, K, d, dR, d, M * d, W1, d, K * d, dX, K);
+  if ((err = traced(nm[4], gemm_flops(M, K, d), md + kd + mk, s, [&] {
+         return coda::launch_gemm_bf16(b3, true, true, coda::EPI_STORE, s);
+       })) != hipSuccess)
+    return err;
+  // B4: dW1 = X^T dy
+  GemmArgs b4 = gemm(K, d, M, X, K, M * K, dR, d, M * d, dW1, d);
+  return traced(nm[5], gemm_flops(K, d, M), mk + md + kd, s, [&] {
+    return coda::launch_gemm_bf16(b4, false, false, coda::EPI_STORE, s);
+  });
+}
+
 }  // namespace
 
 extern "C" {
@@ -193,24 +277,10 @@ coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
   const double eb = (double)e;
 
   const bool bf = dtype == CODA_BF16;
-  // K1: y = X W1 + R; epilogue stores y, yg = y * gamma and the partial sums of squares
-  GemmArgs g1 = gemm(M, d, K, X, K, M * K, W1, d, K * d, y, d);
-  g1.E = R;
-  g1.lde = d;
-  g1.part_row = P;
-  g1.ld_part_row = ws.Tn;
-  g1.C2 = yg;
-  g1.ldc2 = bf ? M : d;
-  g1.c2_trans = bf ? 1 : 0;
-  g1.vcol = gamma;
+  if ((err = launch_k1(bf, M, K, d, X, W1, R, gamma, y, ws, P, yg, s)) != hipSuccess)
+    return hip_status(err);
   // K2: z = diag(r) (yg W2); bf16 reads yg^T [d, M] as an MN-contiguous A
   GemmArgs g2 = gemm(M, N, d, yg, bf ? M : d, M * d, W2, N, d * N, z, N);
-  const double k1_bytes = (M * K + K * d + 3.0 * M * d + d) * eb + M * ws.Tn * 4.0;
-  if ((err = traced("k1_gemm_resid_sumsq", gemm_flops(M, d, K), k1_bytes, s, [&] {
-         return bf ? coda::launch_gemm_bf16(g1, true, false, coda::EPI_RESID_SUMSQ, s)
-                   : coda::launch_gemm_f32(g1, coda::EPI_RESID_SUMSQ, s);
-       })) != hipSuccess)
-    return hip_status(err);
   const double k2_bytes = (M * d + d * N + M * N) * eb + M * ws.Tn * 4.0 + M * 4.0;
   if (bf) {
     // r is formed in K2's epilogue from the partial sums (and written by the
@@ -269,61 +339,11 @@ coda_status coda_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
                        rng(dW2, d * N * e), rng(dgamma, d * 4), rng(workspace, ws.total)};
   if (!alias_free(in, out)) return CODA_ERR_ALIAS;
 
-  hipStream_t s = (hipStream_t)stream;
-  char* wsb = (char*)workspace;
-  void* n = wsb + ws.n;
-  float* S = (float*)(wsb + ws.S);
-  float* G = (float*)(wsb + ws.G);
-  float* c = (float*)(wsb + ws.c);
-  hipError_t err;
-
-  // B1: dh = dz W2^T; epilogue -> dn (into dR), row partials S, column partials G
-  GemmArgs b1 = gemm(M, d, N, dz, N, M * N, W2, N, d * N, dR, d);
-  b1.E = y;
-  b1.lde = d;
-  b1.vrow = r;
-  b1.vcol = gamma;
-  b1.part_row = S;
-  b1.ld_part_row = ws.Tn;
-  b1.part_col = G;
-  b1.ld_part_col = d;
-  b1.C2 = n;                      // n = r * y, the A operand of the dW2 GEMM
-  b1.ldc2 = d;
-  const double md = 2.0 * M * d, dn2 = 2.0 * d * N, mn = 2.0 * M * N, mk = 2.0 * M * K, kd = 2.0 * K * d;
-  if ((err = traced("b1_gemm_dh_epilogue", gemm_flops(M, d, N),
-                    mn + dn2 + 3.0 * md + M * ws.Tn * 4.0 + ws.Tm * d * 4.0 + M * 4.0 + 2.0 * d, s,
-                    [&] { return coda::launch_gemm_bf16(b1, true, true, coda::EPI_DN, s); })) !=
-      hipSuccess)
-    return hip_status(err);
-  // R2: c = r^3 s / d, dgamma
-  if ((err = traced("r2_bwd_reduce", 0.0, M * ws.Tn * 4.0 + ws.Tm * d * 4.0 + 8.0 * M + 4.0 * d, s,
-                    [&] {
-                      return coda::launch_bwd_reduce(S, ws.Tn, ws.Tn, r, M, d, G, ws.Tm, c, dgamma,
-                                                     s);
-                    })) != hipSuccess)
-    return hip_status(err);
-  // E2: dR = r dn - c y (in place)
-  if ((err = traced("e2_dy", 0.0, 3.0 * md + 8.0 * M, s,
-                    [&] { return coda::launch_dy(dR, y, r, c, M, d, s); })) != hipSuccess)
-    return hip_status(err);
-  // B2: dW2 = diag(gamma) n^T dz
-  GemmArgs b2 = gemm(d, N, M, n, d, M * d, dz, N, M * N, dW2, N);
-  b2.vcol = gamma;
-  if ((err = traced("b2_gemm_dW2", gemm_flops(d, N, M), md + mn + dn2 + 2.0 * d, s, [&] {
-         return coda::launch_gemm_bf16(b2, false, false, coda::EPI_ROWSCALE, s);
-       })) != hipSuccess)
-    return hip_status(err);
-  // B3: dX = dy W1^T
-  GemmArgs b3 = gemm(M, K, d, dR, d, M * d, W1, d, K * d, dX, K);
-  if ((err = traced("b3_gemm_dX", gemm_flops(M, K, d), md + kd + mk, s, [&] {
-         return coda::launch_gemm_bf16(b3, true, true, coda::EPI_STORE, s);
-       })) != hipSuccess)
-    return hip_status(err);
-  // B4: dW1 = X^T dy
-  GemmArgs b4 = gemm(K, d, M, X, K, M * K, dR, d, M * d, dW1, d);
-  return hip_status(traced("b4_gemm_dW1", gemm_flops(K, d, M), mk + md + kd, s, [&] {
-    return coda::launch_gemm_bf16(b4, false, false, coda::EPI_STORE, s);
-  }));
+  static const char* const names[6] = {"b1_gemm_dh_epilogue", "r2_bwd_reduce", "e2_dy",
+                                       "b2_gemm_dW2", "b3_gemm_dX", "b4_gemm_dW1"};
+  return hip_status(launch_norm_bwd(M, K, d, N, X, W1, gamma, W2, y, r, dz, nullptr, dX, dW1, dR,
+                                    dW2, dgamma, ws, (char*)workspace, names,
+                                    (hipStream_t)stream));
 }
 
 size_t coda_swiglu_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t d, int64_t F) {
@@ -472,6 +492,141 @@ coda_status coda_trace_stop(void) {
   g_trace.cap = g_trace.n = 0;
   g_trace.on = false;
   return st;
+}
+
+// ------------------------------------------------------- MLP sub-layer chain
+
+size_t coda_mlp_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t F) {
+  (void)K;
+  (void)F;
+  if (dtype != CODA_BF16 || M < 1 || d < 1) return 0;
+  return fwd_ws(dtype, M, d, 0).total;
+}
+
+coda_status coda_mlp_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t F, float eps,
+                         const void* X, const void* W1, const void* R, const void* gamma,
+                         const void* W, const void* Wd, void* y, float* r, void* gu, void* a,
+                         void* z, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
+  if (!X || !W1 || !R || !gamma || !W || !Wd || !y || !r || !gu || !a || !z) return CODA_ERR_NULL;
+  if (!dim_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, d) || !dim_ok(dtype, F))
+    return CODA_ERR_SHAPE;
+  if (!bytes_ok(dtype, M, K) || !bytes_ok(dtype, K, d) || !bytes_ok(dtype, M, d) ||
+      !bytes_ok(dtype, d, 2 * F) || !bytes_ok(dtype, F, d) || !bytes_ok(dtype, M, 2 * F))
+    return CODA_ERR_SHAPE;
+  if (!std::isfinite(eps) || !(eps > 0.0f)) return CODA_ERR_EPS;
+  if (dtype != CODA_BF16) return CODA_ERR_UNSUPPORTED;
+  for (const void* p : {X, W1, R, gamma, W, Wd, (const void*)y, (const void*)r, (const void*)gu,
+                        (const void*)a, (const void*)z})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  const FwdWs ws = fwd_ws(dtype, M, d, 0);
+  if (!workspace || workspace_bytes < ws.total) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const size_t e = 2;
+  const Range in[] = {rng(X, M * K * e), rng(W1, K * d * e), rng(R, M * d * e), rng(gamma, d * e),
+                      rng(W, d * 2 * F * e), rng(Wd, F * d * e)};
+  const Range out[] = {rng(y, M * d * e), rng(r, M * 4), rng(gu, M * 2 * F * e),
+                       rng(a, M * F * e), rng(z, M * d * e), rng(workspace, ws.total)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)workspace;
+  float* P = (float*)(wsb + ws.P);
+  void* yg = wsb + ws.yg;
+  hipError_t err;
+  if ((err = launch_k1(true, M, K, d, X, W1, R, gamma, y, ws, P, yg, s)) != hipSuccess)
+    return hip_status(err);
+  // M1: [g | u] = diag(r) (yg W); epilogue: r from the partial sums (tiles of
+  // the first column store it), both halves scaled by r, gu and a = silu(g) u
+  GemmArgs m1 = gemm(M, F, d, yg, M, M * d, W, 2 * F, d * 2 * F, gu, 2 * F);
+  m1.C2 = a;
+  m1.ldc2 = F;
+  m1.F = (int)F;
+  m1.part_row = P;
+  m1.ld_part_row = ws.Tn;
+  m1.nparts = ws.Tn;
+  m1.inv_d = 1.0f / (float)d;
+  m1.eps = eps;
+  m1.r_out = r;
+  const double Md = 2.0 * M * d, dF2 = 4.0 * d * F, MF = 2.0 * M * F, Fd = 2.0 * F * d;
+  if ((err = traced("m1_gemm_gateup_rsqrt_swiglu", gemm_flops(M, 2 * F, d),
+                    Md + dF2 + 3.0 * MF + M * ws.Tn * 4.0 + M * 4.0, s, [&] {
+                      return coda::launch_gemm_bf16(m1, false, false, coda::EPI_RSQRT_SWIGLU, s);
+                    })) != hipSuccess)
+    return hip_status(err);
+  // M2: z = a Wd
+  GemmArgs m2 = gemm(M, d, F, a, F, M * F, Wd, d, F * d, z, d);
+  return hip_status(traced("m2_gemm_down", gemm_flops(M, d, F), MF + Fd + Md, s, [&] {
+    return coda::launch_gemm_bf16(m2, true, false, coda::EPI_STORE, s);
+  }));
+}
+
+size_t coda_mlp_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t F) {
+  (void)K;
+  if (dtype != CODA_BF16 || M < 1 || d < 1 || F < 1) return 0;
+  return round_up((size_t)M * 2 * F * 2) + bwd_ws(M, d).total;
+}
+
+coda_status coda_mlp_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t F,
+                         const void* X, const void* W1, const void* gamma, const void* W,
+                         const void* Wd, const void* y, const float* r, const void* gu,
+                         const void* a, const void* dz, const void* dy_in, void* dX, void* dW1,
+                         void* dR, void* dW, void* dWd, float* dgamma, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
+  if (!X || !W1 || !gamma || !W || !Wd || !y || !r || !gu || !a || !dz || !dX || !dW1 || !dR ||
+      !dW || !dWd || !dgamma)
+    return CODA_ERR_NULL;
+  if (!dim_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, d) || !dim_ok(dtype, F))
+    return CODA_ERR_SHAPE;
+  if (!bytes_ok(dtype, M, K) || !bytes_ok(dtype, K, d) || !bytes_ok(dtype, M, d) ||
+      !bytes_ok(dtype, d, 2 * F) || !bytes_ok(dtype, F, d) || !bytes_ok(dtype, M, 2 * F))
+    return CODA_ERR_SHAPE;
+  if (dtype != CODA_BF16) return CODA_ERR_UNSUPPORTED;
+  for (const void* p : {X, W1, gamma, W, Wd, y, (const void*)r, gu, a, dz, (const void*)dX,
+                        (const void*)dW1, (const void*)dR, (const void*)dW, (const void*)dWd,
+                        (const void*)dgamma})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  if (dy_in && !aligned16(dy_in)) return CODA_ERR_ALIGN;
+  const size_t dgu_bytes = round_up((size_t)M * 2 * F * 2);
+  const BwdWs ws = bwd_ws(M, d);
+  if (!workspace || workspace_bytes < dgu_bytes + ws.total) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const size_t e = 2;
+  const Range in[] = {rng(X, M * K * e), rng(W1, K * d * e), rng(gamma, d * e),
+                      rng(W, d * 2 * F * e), rng(Wd, F * d * e), rng(y, M * d * e), rng(r, M * 4),
+                      rng(gu, M * 2 * F * e), rng(a, M * F * e), rng(dz, M * d * e),
+                      rng(dy_in, dy_in ? M * d * e : 0)};
+  const Range out[] = {rng(dX, M * K * e), rng(dW1, K * d * e), rng(dR, M * d * e),
+                       rng(dW, d * 2 * F * e), rng(dWd, F * d * e), rng(dgamma, d * 4),
+                       rng(workspace, dgu_bytes + ws.total)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)workspace;
+  void* dgu = wsb;
+  hipError_t err;
+  // M3: da = dz Wd^T; epilogue -> dgu = [dg | du] from the saved gu
+  GemmArgs m3 = gemm(M, F, d, dz, d, M * d, Wd, d, F * d, dgu, 2 * F);
+  m3.E = gu;
+  m3.lde = 2 * F;
+  m3.F = (int)F;
+  const double Md = 2.0 * M * d, MF = 2.0 * M * F, Fd = 2.0 * F * d;
+  if ((err = traced("m3_gemm_da_swiglu_bwd", gemm_flops(M, F, d), Md + Fd + 4.0 * MF, s, [&] {
+         return coda::launch_gemm_bf16(m3, true, true, coda::EPI_SWIGLU_BWD, s);
+       })) != hipSuccess)
+    return hip_status(err);
+  // M4: dWd = a^T dz
+  GemmArgs m4 = gemm(F, d, M, a, F, M * F, dz, d, M * d, dWd, d);
+  if ((err = traced("m4_gemm_dWd", gemm_flops(F, d, M), MF + Md + Fd, s, [&] {
+         return coda::launch_gemm_bf16(m4, false, false, coda::EPI_STORE, s);
+       })) != hipSuccess)
+    return hip_status(err);
+  // the normalised block's backward with [g | u] = h W as its second GEMM
+  static const char* const names[6] = {"m5_gemm_dh_epilogue", "m6_bwd_reduce", "m7_dy",
+                                       "m8_gemm_dW", "m9_gemm_dX", "m10_gemm_dW1"};
+  return hip_status(launch_norm_bwd(M, K, d, 2 * F, X, W1, gamma, W, y, r, dgu, dy_in, dX, dW1, dR,
+                                    dW, dgamma, ws, wsb + dgu_bytes, names, s));
 }
 
 }  // extern "C"

@@ -349,7 +349,7 @@ gemm_bf16_kernel(GemmArgs g) {
   constexpr int BK = KC::BK, NSTAGE = KC::NSTAGE, OPER_BYTES = KC::OPER_BYTES;
   constexpr int STAGE_BYTES = KC::STAGE_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[KC::LDS_BYTES];
-  constexpr bool GATED = (EPI == EPI_SWIGLU);
+  constexpr bool GATED = (EPI == EPI_SWIGLU || EPI == EPI_RSQRT_SWIGLU);
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6, wm = wave / WNv, wn = wave % WNv;
 
@@ -482,6 +482,24 @@ gemm_bf16_kernel(GemmArgs g) {
     *(bf16x8*)p = bf16x8{f2bf(lo[0]), f2bf(lo[1]), f2bf(lo[2]), f2bf(lo[3]),
                          f2bf(hi[0]), f2bf(hi[1]), f2bf(hi[2]), f2bf(hi[3])};
   };
+  // EPI_RSQRT_*: r for the tile's rows from the first GEMM's partial sums,
+  // summed in the same order as the stand-alone reduction kernel, into rrow
+  float* rrow = red + WNv * BM + WMv * BN;          // [BM] row scales
+  auto tile_row_rsqrt = [&]() {
+    if (t < BM) {
+      const int row = row0 + t;
+      float r = 0.0f;
+      if (row < g.M) {
+        const float* P = g.part_row + (int64_t)row * g.ld_part_row;
+        float sp = 0.0f;
+        for (int k = 0; k < g.nparts; ++k) sp += P[k];
+        r = 1.0f / sqrtf(sp * g.inv_d + g.eps);
+        if (tn == 0) g.r_out[row] = r;
+      }
+      rrow[t] = r;
+    }
+    __syncthreads();
+  };
   auto sum8 = [](float v) {                          // over the 8 lanes of a row
     v += __shfl_xor(v, 1);
     v += __shfl_xor(v, 2);
@@ -496,24 +514,7 @@ gemm_bf16_kernel(GemmArgs g) {
     if constexpr (EPI == EPI_DN || EPI == EPI_RESID_SUMSQ) {
       if (colok && g.vcol) ld8((const __bf16*)g.vcol + gcol, glo, ghi);
     }
-    float* rrow = red + WNv * BM + WMv * BN;        // [BM] row scales (EPI_RSQRT_SCALE)
-    if constexpr (EPI == EPI_RSQRT_SCALE) {
-      // r for the tile's rows from the first GEMM's partial sums, summed in
-      // the same order as the stand-alone reduction kernel
-      if (t < BM) {
-        const int row = row0 + t;
-        float r = 0.0f;
-        if (row < g.M) {
-          const float* P = g.part_row + (int64_t)row * g.ld_part_row;
-          float sp = 0.0f;
-          for (int k = 0; k < g.nparts; ++k) sp += P[k];
-          r = 1.0f / sqrtf(sp * g.inv_d + g.eps);
-          if (tn == 0) g.r_out[row] = r;
-        }
-        rrow[t] = r;
-      }
-      __syncthreads();
-    }
+    if constexpr (EPI == EPI_RSQRT_SCALE) tile_row_rsqrt();
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       dump(i);
@@ -661,10 +662,12 @@ gemm_bf16_kernel(GemmArgs g) {
         }
       }
     }
-  } else if constexpr (EPI == EPI_SWIGLU) {
+  } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_RSQRT_SWIGLU) {
     // The wave tile's 64 columns are 32 gate columns j and the 32 up columns
     // of the same j.  Pass p: lane l owns row 16p + l/4 and gate/up column
-    // group l%4 (8 columns each).
+    // group l%4 (8 columns each).  EPI_RSQRT_SWIGLU first scales both by the
+    // row's RMS factor r (the GEMM's A operand is the un-normalised y gamma).
+    if constexpr (EPI == EPI_RSQRT_SWIGLU) tile_row_rsqrt();
     __bf16* GU = (__bf16*)g.C;
     __bf16* Aout = (__bf16*)g.C2;
     const int c4 = lane & 3, r4 = lane >> 2;
@@ -681,6 +684,13 @@ gemm_bf16_kernel(GemmArgs g) {
         f32x4 g0, g1, u0, u1;
         fetch8(r, c4, g0, g1);
         fetch8(r, 4 + c4, u0, u1);
+        if constexpr (EPI == EPI_RSQRT_SWIGLU) {
+          const float sc = rrow[wm * TM + i * 32 + r];
+          g0 *= sc;
+          g1 *= sc;
+          u0 *= sc;
+          u1 *= sc;
+        }
         if (jok && row < g.M) {
           st8(GU + (int64_t)row * g.ldc + jj, g0, g1);
           st8(GU + (int64_t)row * g.ldc + g.F + jj, u0, u1);
@@ -820,8 +830,8 @@ __global__ void bwd_reduce_kernel(const float* __restrict__ S, int64_t lds, int 
 }
 
 __global__ void dy_kernel(__bf16* __restrict__ dR, const __bf16* __restrict__ y,
-                          const float* __restrict__ r, const float* __restrict__ c, int64_t M,
-                          int64_t d) {
+                          const float* __restrict__ r, const float* __restrict__ c,
+                          const __bf16* __restrict__ dy_in, int64_t M, int64_t d) {
   const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t e0 = v * 8;
   if (e0 >= M * d) return;
@@ -830,8 +840,14 @@ __global__ void dy_kernel(__bf16* __restrict__ dR, const __bf16* __restrict__ y,
   const bf16x8 dn = *(const bf16x8*)(dR + e0);
   const bf16x8 yv = *(const bf16x8*)(y + e0);
   bf16x8 o;
+  if (dy_in) {
+    const bf16x8 din = *(const bf16x8*)(dy_in + e0);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) o[k] = f2bf(ri * bf2f(dn[k]) - ci * bf2f(yv[k]));
+    for (int k = 0; k < 8; ++k) o[k] = f2bf(ri * bf2f(dn[k]) - ci * bf2f(yv[k]) + bf2f(din[k]));
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] = f2bf(ri * bf2f(dn[k]) - ci * bf2f(yv[k]));
+  }
   *(bf16x8*)(dR + e0) = o;
 }
 
@@ -849,7 +865,8 @@ static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   constexpr int BKv = (AK || BKM) ? 64 : 32;
   constexpr int NSTv = (AK || BKM) ? 2 : 4;
   const int tiles_m = (g.M + BM - 1) / BM;
-  const int tiles_n = (EPI == EPI_SWIGLU) ? (g.N + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
+  const int tiles_n = (EPI == EPI_SWIGLU || EPI == EPI_RSQRT_SWIGLU) ? (g.N + BN / 2 - 1) / (BN / 2)
+                                                                      : (g.N + BN - 1) / BN;
   hipLaunchKernelGGL((gemm_bf16_kernel<kWavesM, kWavesN, BKv, NSTv, AK, BKM, EPI>),
                      dim3(tiles_m * tiles_n), dim3(64 * kWavesM * kWavesN), 0, s, g);
   return hipGetLastError();
@@ -880,6 +897,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStr
       case EPI_STORE: return launch_one<false, false, EPI_STORE>(g, s);
       case EPI_ROWSCALE: return launch_one<false, false, EPI_ROWSCALE>(g, s);
       case EPI_RSQRT_SCALE: return launch_one<false, false, EPI_RSQRT_SCALE>(g, s);
+      case EPI_RSQRT_SWIGLU: return launch_one<false, false, EPI_RSQRT_SWIGLU>(g, s);
       default: break;
     }
   }
@@ -920,11 +938,11 @@ hipError_t launch_bwd_reduce(const float* S, int64_t lds, int Tn, const float* r
   return hipGetLastError();
 }
 
-hipError_t launch_dy(void* dR, const void* y, const float* r, const float* c, int64_t M, int64_t d,
-                     hipStream_t s) {
+hipError_t launch_dy(void* dR, const void* y, const float* r, const float* c, const void* dy_in,
+                     int64_t M, int64_t d, hipStream_t s) {
   const int64_t chunks = (M * d) / 8;
   hipLaunchKernelGGL(dy_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
-                     (__bf16*)dR, (const __bf16*)y, r, c, M, d);
+                     (__bf16*)dR, (const __bf16*)y, r, c, (const __bf16*)dy_in, M, d);
   return hipGetLastError();
 }
 

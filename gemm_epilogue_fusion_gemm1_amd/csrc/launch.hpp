@@ -26,6 +26,8 @@ enum Epi : int {
   EPI_SWIGLU_BWD = 5,  // da = acc; C = dgu from the saved gu in E
   EPI_RSQRT_SCALE = 6, // r_i = (sum_t part_row[i][t] * inv_d + eps)^-1/2; C = r_i acc;
                        // tiles of column 0 write r to r_out
+  EPI_RSQRT_SWIGLU = 7,  // r_i as EPI_RSQRT_SCALE; gate/up pair scaled by r_i, then as
+                         // EPI_SWIGLU: C = gu (both halves), C2 = silu(g) * u
 };
 
 // Operand layouts.  "K-major" = the contraction index is contiguous in memory.
@@ -60,8 +62,9 @@ hipError_t launch_row_rsqrt(const float* P, int64_t ldp, int T, int64_t M, int64
 hipError_t launch_bwd_reduce(const float* S, int64_t lds, int Tn, const float* r, int64_t M,
                              int64_t d, const float* G, int Tm, float* c, float* dgamma,
                              hipStream_t stream);
-// in place: dR[i][j] = r_i dR[i][j] - c_i y[i][j]  (dR holds dn on entry)
-hipError_t launch_dy(void* dR, const void* y, const float* r, const float* c, int64_t M, int64_t d,
-                     hipStream_t stream);
+// in place: dR[i][j] = r_i dR[i][j] - c_i y[i][j] (+ dy_in[i][j] when dy_in is
+// not NULL)  (dR holds dn on entry)
+hipError_t launch_dy(void* dR, const void* y, const float* r, const float* c, const void* dy_in,
+                     int64_t M, int64_t d, hipStream_t stream);
 
 }  // namespace coda

@@ -166,6 +166,63 @@ coda_status coda_swiglu_bwd(coda_dtype dtype, int64_t M, int64_t d, int64_t F,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * The two patterns chained as a LLaMA MLP sub-layer: projection + residual,
+ * RMS normalisation, SwiGLU gate/up, down projection.  The pages name the
+ * residual add and RMS normalisation around a matmul, and SwiGLU as the
+ * activation epilogue, inside a transformer block ([RU]/[FR] insight
+ * sections; [JA]/[RU]/[FR] primitives sections).  Here the normalised input
+ * feeds the gate/up GEMM in place of the second GEMM of coda_fwd:
+ *   y = X W1 + R;  r_i = (mean_j y_ij^2 + eps)^(-1/2);
+ *   [g | u] = diag(r) (y diag(gamma)) W,  W = [W_gate | W_up];
+ *   a = silu(g) * u;  z = a Wd.
+ * The first GEMM's epilogue leaves the partial sums of squares and y*gamma;
+ * the gate/up GEMM's epilogue forms r, scales both accumulators by it and
+ * applies SwiGLU.
+ *
+ *   X [M,K], W1 [K,d], R [M,d], gamma [d], W [d,2F], Wd [F,d]: in.
+ *   y [M,d], r [M] (float32), gu [M,2F] (the r-scaled [g | u]), a [M,F]:
+ *   out, saved for the backward.   z [M,d]: out.
+ *   workspace: >= coda_mlp_fwd_workspace_bytes(...) bytes, 16-byte aligned,
+ *   contents ignored (partial sums and y*gamma).
+ * Errors as coda_fwd; CODA_F32 returns CODA_ERR_UNSUPPORTED in this build.
+ * ---------------------------------------------------------------------- */
+size_t coda_mlp_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t F);
+coda_status coda_mlp_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t F, float eps,
+                         const void* X, const void* W1, const void* R, const void* gamma,
+                         const void* W, const void* Wd, void* y, float* r, void* gu, void* a,
+                         void* z, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backward of the MLP sub-layer: the exact gradient of
+ * L = <dz, z> + <dy_in, y>, given the tensors saved by coda_mlp_fwd.  dy_in
+ * is the gradient the residual stream y receives from later layers; it is
+ * optional (NULL = zero) and is added to dy.
+ *   da = dz Wd^T;  sg = sigmoid(g);  dgu = [da u sg (1 + g (1 - sg)) | da g sg];
+ *   dWd = a^T dz;
+ *   then the block backward of coda_bwd with dz := dgu and W2 := W:
+ *   n = diag(r) y;  dW = diag(gamma) n^T dgu;  dh = dgu W^T;
+ *   dgamma_j = sum_i dh_ij n_ij;  dn = dh diag(gamma);  s_i = sum_j dn_ij y_ij;
+ *   dy = diag(r) dn - diag(r^3 s / d) y + dy_in;  dR = dy;
+ *   dX = dy W1^T;  dW1 = X^T dy.
+ *
+ *   X [M,K], W1 [K,d], gamma [d], W [d,2F], Wd [F,d], y [M,d], r [M]
+ *   (float32), gu [M,2F], a [M,F], dz [M,d], dy_in [M,d] or NULL: in.
+ *   dX [M,K], dW1 [K,d], dR [M,d], dW [d,2F], dWd [F,d]: out (dtype).
+ *   dgamma [d]: out, float32.
+ *   workspace: >= coda_mlp_bwd_workspace_bytes(...) bytes (dgu, then the
+ *   block backward's n, partial sums and c).
+ * dy_in may not overlap an output (CODA_ERR_ALIAS).  Other errors as
+ * coda_bwd; CODA_F32 returns CODA_ERR_UNSUPPORTED in this build.
+ * ---------------------------------------------------------------------- */
+size_t coda_mlp_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t F);
+coda_status coda_mlp_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t F,
+                         const void* X, const void* W1, const void* gamma, const void* W,
+                         const void* Wd, const void* y, const float* r, const void* gu,
+                         const void* a, const void* dz, const void* dy_in, void* dX, void* dW1,
+                         void* dR, void* dW, void* dWd, float* dgamma, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Kernel tracing (measurement aid; off by default).
  *
  * coda_trace_start(capacity) creates 2*capacity timing events (host call,

@@ -176,3 +176,62 @@ def test_swiglu_rejects(L):
     need = L.coda_swiglu_bwd_workspace_bytes(BF16, M, d, F)
     assert L.coda_swiglu_bwd(BF16, M, d, F, X, W, Wd, gu, a, z, dX, dW, dWd, ws, need - 16, None) == WORKSPACE
     assert L.coda_swiglu_bwd(BF16, M, d, F, X, W, Wd, gu, a, z, dX, dW, X, ws, need, None) == ALIAS
+
+
+def _mlp_mem(m, M, K, d, F):
+    return dict(X=m(M * K * 2), W1=m(K * d * 2), R=m(M * d * 2), gamma=m(d * 2), W=m(d * 2 * F * 2),
+                Wd=m(F * d * 2), y=m(M * d * 2), r=m(M * 4), gu=m(M * 2 * F * 2), a=m(M * F * 2),
+                z=m(M * d * 2), dz=m(M * d * 2), dy_in=m(M * d * 2), dX=m(M * K * 2), dW1=m(K * d * 2),
+                dR=m(M * d * 2), dW=m(d * 2 * F * 2), dWd=m(F * d * 2), dgamma=m(d * 4),
+                ws=m(1 << 22), ws_bytes=1 << 22)
+
+
+def mlp_fwd_call(L, **over):
+    M, K, d, F = 64, 32, 48, 40
+    a = dict(dtype=BF16, M=M, K=K, d=d, F=F, eps=1e-6, **_mlp_mem(FakeMem(), M, K, d, F))
+    a.update(over)
+    return L.coda_mlp_fwd(a["dtype"], a["M"], a["K"], a["d"], a["F"], a["eps"], a["X"], a["W1"], a["R"],
+                          a["gamma"], a["W"], a["Wd"], a["y"], a["r"], a["gu"], a["a"], a["z"], a["ws"],
+                          a["ws_bytes"], None)
+
+
+def mlp_bwd_call(L, **over):
+    M, K, d, F = 64, 32, 48, 40
+    a = dict(dtype=BF16, M=M, K=K, d=d, F=F, **_mlp_mem(FakeMem(), M, K, d, F))
+    a.update(over)
+    return L.coda_mlp_bwd(a["dtype"], a["M"], a["K"], a["d"], a["F"], a["X"], a["W1"], a["gamma"], a["W"],
+                          a["Wd"], a["y"], a["r"], a["gu"], a["a"], a["dz"], a["dy_in"], a["dX"], a["dW1"],
+                          a["dR"], a["dW"], a["dWd"], a["dgamma"], a["ws"], a["ws_bytes"], None)
+
+
+def test_mlp_workspace_sizes(L):
+    M, K, d, F = 8192, 4096, 4096, 11008
+    assert L.coda_mlp_fwd_workspace_bytes(BF16, M, K, d, F) == L.coda_fwd_workspace_bytes(BF16, M, K, d, 1)
+    # dgu [M, 2F] bf16 + the block backward's workspace
+    assert (L.coda_mlp_bwd_workspace_bytes(BF16, M, K, d, F)
+            >= M * 2 * F * 2 + L.coda_bwd_workspace_bytes(BF16, M, K, d, 2 * F))
+    assert L.coda_mlp_fwd_workspace_bytes(F32, M, K, d, F) == 0
+    assert L.coda_mlp_bwd_workspace_bytes(F32, M, K, d, F) == 0
+
+
+def test_mlp_rejects(L):
+    assert mlp_fwd_call(L, dtype=9) == DTYPE
+    assert mlp_fwd_call(L, Wd=None) == NULL
+    assert mlp_fwd_call(L, F=44) == SHAPE
+    assert mlp_fwd_call(L, eps=0.0) == EPS
+    assert mlp_fwd_call(L, eps=float("nan")) == EPS
+    assert mlp_fwd_call(L, dtype=F32) == UNSUPPORTED
+    assert mlp_fwd_call(L, ws_bytes=64) == WORKSPACE
+    assert mlp_fwd_call(L, gu=ctypes.c_void_p((1 << 41) + 8)) == ALIGN
+    m = FakeMem()
+    m.next = 1 << 44                  # away from the helpers' own fake addresses
+    p = m(1 << 20)
+    assert mlp_fwd_call(L, a=p, z=ctypes.c_void_p(p.value + 64)) == ALIAS
+    assert mlp_bwd_call(L, dtype=9) == DTYPE
+    assert mlp_bwd_call(L, dgamma=None) == NULL
+    assert mlp_bwd_call(L, K=36) == SHAPE
+    assert mlp_bwd_call(L, dtype=F32) == UNSUPPORTED
+    assert mlp_bwd_call(L, ws=None) == WORKSPACE
+    assert mlp_bwd_call(L, dy_in=ctypes.c_void_p((1 << 41) + 4)) == ALIGN
+    d_R = m(64 * 48 * 2)
+    assert mlp_bwd_call(L, dR=d_R, dy_in=d_R) == ALIAS          # dy_in may not overlap an output

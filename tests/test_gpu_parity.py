@@ -3,7 +3,9 @@
 Bars (per output tensor): max|gpu - ref| / max|ref| <= 2e-2 for bf16 inputs
 with fp32 accumulation and <= 1e-5 for the fp32 forward; r per element
 |dr|/r <= 1e-3; dgamma norm-wise <= 1e-3 against the oracle fed the saved y
-rounded to bf16 (the storage contract of the saved activation).
+rounded to bf16 (the storage contract of the saved activation), and for the
+MLP sub-layer also its stored intermediate dgu rounded to bf16 (the error
+against the unrounded dgu is reported beside it).
 
 Small cases run the whole oracle; they span several 256x256 tiles and end in
 ragged edges.  The full-size workloads are checked on sampled rows and
@@ -276,3 +278,95 @@ def test_full_workload_swiglu(torch_dev):
     report("swiglu_fwdbwd", errs)
     for k, v in errs.items():
         assert v <= BF16_TOL, (k, v)
+
+
+# ------------------------------------------------- MLP sub-layer (chained)
+
+SMALL_MLP = [
+    # M, K, d, F
+    (520, 264, 392, 200),       # ragged everywhere, several tiles
+    (8, 8, 8, 8),               # smallest accepted
+    (256, 256, 256, 128),       # one tile per GEMM
+    (264, 136, 272, 520),       # wide hidden layer, K tail
+]
+
+
+def _mlp_oracle(h, eps, dy_in):
+    """The exact forward (for the forward outputs) and the backward under the
+    storage contract: the forward's stored gate/up input y*gamma and the
+    backward's stored dgu rounded to bf16, and the saved y, gu, a in bf16."""
+    f = oracle.ref_mlp_fwd(h["X"], h["W1"], h["R"], h["gamma"], h["W"], h["Wd"], eps)
+    fq = oracle.ref_mlp_fwd(h["X"], h["W1"], h["R"], h["gamma"], h["W"], h["Wd"], eps, oracle.bf16_rne)
+    b = oracle.ref_mlp_bwd(h["X"], h["W1"], h["gamma"], h["W"], h["Wd"], oracle.bf16_rne(fq["y"]), fq["r"],
+                           oracle.bf16_rne(fq["gu"]), oracle.bf16_rne(fq["a"]), h["dz"], dy_in,
+                           dgu_round=oracle.bf16_rne)
+    return f, b
+
+
+@pytest.mark.parametrize("shape", SMALL_MLP, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("with_dy_in", [True, False], ids=["dy_in", "no_dy_in"])
+def test_mlp_fwd_bwd(torch_dev, shape, with_dy_in):
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    M, K, d, F = shape
+    eps = 1e-6
+    h = synth.mlp_inputs(M, K, d, F, seed=400 + M + F)
+    t = {k: up(torch, dev, v, "bf16") for k, v in h.items()}
+    z, y, r, gu, a = coda.mlp_fwd(t["X"], t["W1"], t["R"], t["gamma"], t["W"], t["Wd"], eps)
+    dX, dW1, dR, dW, dWd, dg = coda.mlp_bwd(t["X"], t["W1"], t["gamma"], t["W"], t["Wd"], y, r, gu, a,
+                                            t["dz"], t["dy_in"] if with_dy_in else None)
+    torch.cuda.synchronize()
+    f, b = _mlp_oracle(h, eps, h["dy_in"] if with_dy_in else None)
+    b_exact = oracle.ref_mlp_bwd(h["X"], h["W1"], h["gamma"], h["W"], h["Wd"], f["y"], f["r"], f["gu"],
+                                 f["a"], h["dz"], h["dy_in"] if with_dy_in else None)
+    errs = {"y": rel(host(y), f["y"]), "gu": rel(host(gu), f["gu"]), "a": rel(host(a), f["a"]),
+            "z": rel(host(z), f["z"]), "dX": rel(host(dX), b["dX"]), "dW1": rel(host(dW1), b["dW1"]),
+            "dR": rel(host(dR), b["dR"]), "dW": rel(host(dW), b["dW"]), "dWd": rel(host(dWd), b["dWd"]),
+            "dgamma": rel(dg.cpu().numpy(), b["dgamma"])}
+    rr = float(np.max(np.abs(r.cpu().numpy() - f["r"]) / f["r"]))
+    info = {"dgamma_vs_exact": rel(dg.cpu().numpy(), b_exact["dgamma"])}
+    report(f"mlp {shape} dy_in={with_dy_in}", {**errs, "r": rr, **info})
+    for k, v in errs.items():
+        if k != "dgamma":
+            assert v <= BF16_TOL, (k, v)
+    assert rr <= R_TOL
+    assert errs["dgamma"] <= DGAMMA_TOL
+
+
+def test_full_workload_mlp(torch_dev):
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    w = synth.WORKLOADS["llama7b_mlp_fwdbwd"]
+    print("[parity] llama7b_mlp_fwdbwd: generating inputs", flush=True)
+    h = synth.workload_inputs(w)
+    t = {k: up(torch, dev, v, "bf16") for k, v in h.items()}
+    z, y, r, gu, a = coda.mlp_fwd(t["X"], t["W1"], t["R"], t["gamma"], t["W"], t["Wd"], w.eps)
+    dX, dW1, dR, dW, dWd, dg = coda.mlp_bwd(t["X"], t["W1"], t["gamma"], t["W"], t["Wd"], y, r, gu, a,
+                                            t["dz"], t["dy_in"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed)
+    rows = _rows(w.M, rng, k=24)
+    print("[parity] llama7b_mlp_fwdbwd: oracle forward rows", flush=True)
+    fr = oracle.ref_mlp_fwd_rows(h["X"], h["W1"], h["R"], h["gamma"], h["W"], h["Wd"], w.eps, rows)
+    errs = {"z_rows": rel(host(z[rows]), fr["z"]), "y_rows": rel(host(y[rows]), fr["y"]),
+            "gu_rows": rel(host(gu[rows]), fr["gu"]), "a_rows": rel(host(a[rows]), fr["a"])}
+    print("[parity] llama7b_mlp_fwdbwd: oracle forward, stored operand rounded (full: the backward "
+          "needs every row)", flush=True)
+    f = oracle.ref_mlp_fwd(h["X"], h["W1"], h["R"], h["gamma"], h["W"], h["Wd"], w.eps, oracle.bf16_rne)
+    rr = float(np.max(np.abs(r.cpu().numpy() - f["r"]) / f["r"]))
+    cd = np.unique(np.concatenate([[0, w.d - 1], rng.choice(w.d, 16, replace=False)]))
+    c2 = np.unique(np.concatenate([[0, w.F - 1, w.F, 2 * w.F - 1], rng.choice(2 * w.F, 12, replace=False)]))
+    rf = np.unique(np.concatenate([[0, w.F - 1], rng.choice(w.F, 10, replace=False)]))
+    print("[parity] llama7b_mlp_fwdbwd: oracle backward (sampled)", flush=True)
+    bs = oracle.ref_mlp_bwd_sampled(h["X"], h["W1"], h["gamma"], h["W"], h["Wd"], oracle.bf16_rne(f["y"]),
+                                    f["r"], oracle.bf16_rne(f["gu"]), oracle.bf16_rne(f["a"]), h["dz"],
+                                    h["dy_in"], rows, cd, c2, rf, dgu_round=oracle.bf16_rne)
+    errs.update({"dX_rows": rel(host(dX[rows]), bs["dX_rows"]), "dR_rows": rel(host(dR[rows]), bs["dR_rows"]),
+                 "dW1_cols": rel(host(dW1[:, cd]), bs["dW1_cols"]), "dW_cols": rel(host(dW[:, c2]), bs["dW_cols"]),
+                 "dWd_rows": rel(host(dWd[rf]), bs["dWd_rows"]), "dgamma": rel(dg.cpu().numpy(), bs["dgamma"])})
+    report("llama7b_mlp_fwdbwd", {**errs, "r": rr})
+    assert rr <= R_TOL
+    for k, v in errs.items():
+        if k != "dgamma":
+            assert v <= BF16_TOL, (k, v)
+    assert errs["dgamma"] <= DGAMMA_TOL
