@@ -10,9 +10,9 @@ dense bf16 MFMA peak, the speed-up over an unfused hipBLASLt + F.rms_norm +
 autograd step on the same GPU (for the step, and for the forward and the
 backward alone), the median / min / max step time, per-kernel times from HIP
 events recorded on the stream the kernels run on, the roofline of the
-dominant kernel, the same figures for the 70B-hidden, SwiGLU and 1B-hidden
-(forward only) workloads under "also", and the CPU oracle timed on a bounded
-sample of the same workload.
+dominant kernel, the same figures for the 70B-hidden, SwiGLU, MLP sub-layer
+(the two chained) and 1B-hidden (forward only) workloads under "also", and
+the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-also] [--no-cpu-baseline]
 """
@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_fwdbwd")
-    ap.add_argument("--no-also", action="store_true", help="skip the 70B, SwiGLU and 1B workloads")
+    ap.add_argument("--no-also", action="store_true", help="skip the 70B, SwiGLU, MLP and 1B workloads")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused torch baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
@@ -133,6 +133,59 @@ class SwigluCase:
         return (F.silu(gu[:, :Fh]) * gu[:, Fh:]) @ p["Wd"]
 
 
+class MlpCase:
+    """The MLP sub-layer (projection + residual, RMS norm, SwiGLU, down
+    projection) with the residual stream's incoming gradient dy_in."""
+
+    def __init__(self, w, torch, coda, h):
+        dev = torch.device("cuda:0")
+        self.w, self.torch, self.coda = w, torch, coda
+        self.t = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in h.items()}
+        M, K, d, F = w.M, w.K, w.d, w.F
+        bf = torch.bfloat16
+        self.y = torch.empty((M, d), dtype=bf, device=dev)
+        self.r = torch.empty((M,), dtype=torch.float32, device=dev)
+        self.gu = torch.empty((M, 2 * F), dtype=bf, device=dev)
+        self.a = torch.empty((M, F), dtype=bf, device=dev)
+        self.z = torch.empty((M, d), dtype=bf, device=dev)
+        self.dX = torch.empty((M, K), dtype=bf, device=dev)
+        self.dW1 = torch.empty((K, d), dtype=bf, device=dev)
+        self.dR = torch.empty((M, d), dtype=bf, device=dev)
+        self.dW = torch.empty((d, 2 * F), dtype=bf, device=dev)
+        self.dWd = torch.empty((F, d), dtype=bf, device=dev)
+        self.dg = torch.empty((d,), dtype=torch.float32, device=dev)
+        self.wsf = torch.empty(coda.mlp_fwd_workspace_bytes(1, M, K, d, F), dtype=torch.uint8, device=dev)
+        self.wsb = torch.empty(coda.mlp_bwd_workspace_bytes(1, M, K, d, F), dtype=torch.uint8, device=dev)
+        self.backward = w.backward
+        self.kernels_per_step = 13
+        self.leaf_names = ("X", "W1", "R", "gamma", "W", "Wd")
+
+    def flops(self):
+        return self.w.flops_fwd() + (self.w.flops_bwd() if self.backward else 0.0)
+
+    def fused_fwd(self):
+        t, c = self.t, self.coda
+        c.coda_mlp_fwd(t["X"], t["W1"], t["R"], t["gamma"], t["W"], t["Wd"], self.w.eps, self.y, self.r,
+                       self.gu, self.a, self.z, self.wsf)
+
+    def fused_bwd(self):
+        t, c = self.t, self.coda
+        c.coda_mlp_bwd(t["X"], t["W1"], t["gamma"], t["W"], t["Wd"], self.y, self.r, self.gu, self.a,
+                       t["dz"], t["dy_in"], self.dX, self.dW1, self.dR, self.dW, self.dWd, self.dg, self.wsb)
+
+    def unfused_fwd(self):
+        """Returns the outputs whose gradients the backward is given: (z, y)."""
+        Fn = self.torch.nn.functional
+        p = self.leaf
+        y = p["X"] @ p["W1"] + p["R"]
+        gu = Fn.rms_norm(y, (self.w.d,), p["gamma"], self.w.eps) @ p["W"]
+        Fh = self.w.F
+        return (Fn.silu(gu[:, :Fh]) * gu[:, Fh:]) @ p["Wd"], y
+
+    def grad_outputs(self):
+        return (self.t["dz"], self.t["dy_in"])
+
+
 class _Steps:
     """The fused and unfused step functions of a case: forward, backward, and
     the training step (forward + backward; the forward alone for a
@@ -161,15 +214,18 @@ class _Steps:
                 case.unfused_fwd()
 
     @staticmethod
+    def _grad(case, outs, retain):
+        go = case.grad_outputs() if hasattr(case, "grad_outputs") else case.t["dz"]
+        case.torch.autograd.grad(outs, [case.leaf[k] for k in case.leaf_names], go, retain_graph=retain)
+
+    @staticmethod
     def unfused_bwd(case):
-        case.torch.autograd.grad(case.graph, [case.leaf[k] for k in case.leaf_names], case.t["dz"],
-                                 retain_graph=True)
+        _Steps._grad(case, case.graph, True)
 
     @staticmethod
     def unfused_step(case):
         if case.backward:
-            z = case.unfused_fwd()
-            case.torch.autograd.grad(z, [case.leaf[k] for k in case.leaf_names], case.t["dz"])
+            _Steps._grad(case, case.unfused_fwd(), False)
         else:
             _Steps.unfused_fwd(case)
 
@@ -177,7 +233,8 @@ class _Steps:
 def make_case(w, torch, coda):
     from gemm_epilogue_fusion_gemm1_amd import synth
     h = synth.workload_inputs(w)
-    return (CodaCase if w.kind == "coda" else SwigluCase)(w, torch, coda, h), h
+    cls = {"coda": CodaCase, "swiglu": SwigluCase, "mlp": MlpCase}[w.kind]
+    return cls(w, torch, coda, h), h
 
 
 # ------------------------------------------------------------------- timing
@@ -393,7 +450,7 @@ def main():
 
     also = {}
     if not args.no_also:
-        for name in ("llama70b_fwdbwd", "swiglu_fwdbwd", "llama1b_fwd"):
+        for name in ("llama70b_fwdbwd", "swiglu_fwdbwd", "llama7b_mlp_fwdbwd", "llama1b_fwd"):
             w2 = synth.WORKLOADS[name]
             print(f"[bench] {name}: inputs + timing", file=sys.stderr, flush=True)
             c2, _ = make_case(w2, torch, coda)
