@@ -27,12 +27,13 @@ class Workload:
     """One synthetic workload: its shapes, dtype, epsilon and seed."""
 
     name: str
-    kind: str            # "coda" (GEMM-Residual-RMSNorm-GEMM), "swiglu", or "mlp" (the two chained)
+    kind: str            # "coda" (GEMM-Residual-RMSNorm-GEMM), "swiglu", "mlp" (the two
+                         # chained) or "ce" (LM-head GEMM + cross-entropy)
     dtype: str           # "f32" or "bf16"
     M: int
     K: int = 0           # coda, mlp: GEMM1 reduction width
     d: int = 0           # coda, mlp: normalised width; swiglu: model width
-    N: int = 0           # coda: GEMM2 output width
+    N: int = 0           # coda: GEMM2 output width; ce: vocabulary size V
     F: int = 0           # swiglu, mlp: hidden width (gate and up halves)
     eps: float = 0.0
     seed: int = 0
@@ -43,6 +44,8 @@ class Workload:
         """Algorithmic GEMM flops of the forward pass (elementwise work excluded)."""
         if self.kind == "coda":
             return 2.0 * self.M * (self.K * self.d + self.d * self.N)
+        if self.kind == "ce":
+            return 2.0 * self.M * self.d * self.N
         swiglu = 2.0 * self.M * self.d * 2 * self.F + 2.0 * self.M * self.F * self.d
         if self.kind == "mlp":
             return 2.0 * self.M * self.K * self.d + swiglu
@@ -75,6 +78,10 @@ WORKLOADS = {
                  eps=1e-6, seed=1005, backward=True,
                  note="LLaMA-7B-shaped MLP sub-layer: projection + residual, RMS norm, "
                       "SwiGLU gate/up, down projection; forward+backward with dy_in"),
+        Workload("llama7b_ce_fwdbwd", "ce", "bf16", M=8192, d=4096, N=32000,
+                 seed=1006, backward=True,
+                 note="LLaMA-7B-shaped LM head (vocabulary 32000) with cross-entropy, "
+                      "forward+backward"),
     ]
 }
 
@@ -153,6 +160,20 @@ def mlp_inputs(M: int, K: int, d: int, F: int, seed: int, dtype: str = "bf16",
     return {k: _quantise(v, dtype) for k, v in out.items()}
 
 
+def ce_inputs(M: int, d: int, V: int, seed: int, dtype: str = "bf16", with_dz: bool = True) -> dict:
+    """h ~ N(0,1) (final hidden states); Wv ~ N(0,1/d); labels uniform in
+    [0, V) (int32); dloss = U(0.5, 1.5) / M (a mean reduction's gradient,
+    varied per row; float32)."""
+    s = np.random.SeedSequence(seed).spawn(4)
+    out = {"h": _quantise(_normal(s[0], (M, d), 1.0), dtype),
+           "Wv": _quantise(_normal(s[1], (d, V), 1.0 / math.sqrt(d)), dtype),
+           "labels": np.random.Generator(np.random.PCG64(s[2])).integers(0, V, M).astype(np.int32)}
+    if with_dz:
+        u = np.random.Generator(np.random.PCG64(s[3])).random(M, dtype=np.float32)
+        out["dloss"] = ((np.float32(0.5) + u) / np.float32(M)).astype(np.float32)
+    return out
+
+
 def workload_inputs(w: Workload, with_dz: bool | None = None) -> dict:
     """Inputs of a named workload (dz only when it has a backward pass)."""
     if with_dz is None:
@@ -161,4 +182,6 @@ def workload_inputs(w: Workload, with_dz: bool | None = None) -> dict:
         return coda_inputs(w.M, w.K, w.d, w.N, w.seed, w.dtype, with_dz)
     if w.kind == "mlp":
         return mlp_inputs(w.M, w.K, w.d, w.F, w.seed, w.dtype, with_dz)
+    if w.kind == "ce":
+        return ce_inputs(w.M, w.d, w.N, w.seed, w.dtype, with_dz)
     return swiglu_inputs(w.M, w.d, w.F, w.seed, w.dtype, with_dz)

@@ -47,6 +47,12 @@ What the pages fix, and the readings taken where they are silent:
     feeds the gate/up GEMM in place of the second GEMM, h W = [g | u], a =
     silu(g) u, z = a Wd; y is the residual stream, so its gradient may also
     receive a term dy_in from later layers, added to dy.
+  * Cross-entropy over an LM-head GEMM (``ref_ce_*``): the pages' stateful
+    epilogue primitive keeps a running max and sum of exponentials across the
+    tiles of a row, which cross-entropy uses ([JA]/[RU]/[FR] primitives
+    sections).  Reading: logits = h Wv; lse_i = log sum_j exp(logits_ij);
+    loss_i = lse_i - logits_i,label_i (mean-free, one loss per row); the
+    backward of L = sum_i dloss_i loss_i.
 
 Every function here is pinned by a test against something other than itself
 (brute-force loops, finite differences, torch CPU autograd, closed forms and
@@ -61,6 +67,7 @@ __all__ = [
     "ref_y_r", "ref_fwd_rows", "ref_bwd_sampled", "sigmoid", "ref_swiglu_fwd",
     "ref_swiglu_bwd", "ref_swiglu_fwd_rows", "ref_swiglu_bwd_sampled",
     "ref_mlp_fwd", "ref_mlp_bwd", "ref_mlp_fwd_rows", "ref_mlp_bwd_sampled",
+    "ref_ce_fwd", "ref_ce_bwd", "ref_ce_partials", "ref_ce_fwd_rows", "ref_ce_bwd_sampled",
 ]
 
 
@@ -449,3 +456,94 @@ def ref_mlp_bwd_sampled(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in, rows, cols_
             "dR_rows": dy_rows, "dX_rows": dy_rows @ W1.T, "dW1_cols": X.T @ dy_cols,
             "dW_cols": h.T @ dgu[:, cols_2F], "dWd_rows": a[:, rows_F].T @ dz,
             "dgamma": dgamma, "s": s, "c": c}
+
+
+# ---------------------------------------------------------------------------
+# Cross-entropy over an LM-head GEMM
+# ---------------------------------------------------------------------------
+
+def _logsumexp_rows(x) -> np.ndarray:
+    """log sum_j exp(x_ij) per row, shifted by the row max so nothing overflows."""
+    m = np.max(x, axis=1)
+    return m + np.log(np.sum(np.exp(x - m[:, None]), axis=1))
+
+
+def ref_ce_fwd(h, Wv, labels) -> dict:
+    """logits = h Wv;  lse_i = log sum_j exp(logits_ij);
+    loss_i = lse_i - logits_i,label_i.  ([JA]/[RU]/[FR] primitives sections:
+    cross-entropy over the stateful max / sum-exp epilogue.)"""
+    h, Wv = _f64(h), _f64(Wv)
+    labels = np.asarray(labels, dtype=np.int64)
+    logits = h @ Wv
+    lse = _logsumexp_rows(logits)
+    loss = lse - logits[np.arange(logits.shape[0]), labels]
+    return {"logits": logits, "lse": lse, "loss": loss}
+
+
+def ref_ce_partials(logits, BN: int = 256) -> dict:
+    """The stateful primitive's per-tile state: for each row i and tile t of BN
+    columns, m[i,t] = max_{j in t} logits_ij and s[i,t] = sum_{j in t}
+    exp(logits_ij - m[i,t]); and their combination, the running (max, sum)
+    update m' = max(m, m_t), s' = s exp(m - m') + s_t exp(m_t - m'), taken
+    over the tiles in order, giving lse = m + log s.  Same lse as the
+    definition up to rounding."""
+    x = _f64(logits)
+    M, V = x.shape
+    T = -(-V // BN)
+    m = np.empty((M, T))
+    s = np.empty((M, T))
+    for t in range(T):
+        blk = x[:, t * BN:min((t + 1) * BN, V)]
+        m[:, t] = np.max(blk, axis=1)
+        s[:, t] = np.sum(np.exp(blk - m[:, t:t + 1]), axis=1)
+    run_m = m[:, 0].copy()
+    run_s = s[:, 0].copy()
+    for t in range(1, T):
+        new_m = np.maximum(run_m, m[:, t])
+        run_s = run_s * np.exp(run_m - new_m) + s[:, t] * np.exp(m[:, t] - new_m)
+        run_m = new_m
+    return {"m": m, "s": s, "lse": run_m + np.log(run_s)}
+
+
+def ref_ce_bwd(h, Wv, labels, lse, dloss, logits=None) -> dict:
+    """Exact gradient of L = sum_i dloss_i loss_i for ``ref_ce_fwd``, given the
+    saved lse (and the saved logits, if passed; else they are recomputed):
+      p = exp(logits - lse) (softmax by rows);  dlogits = diag(dloss) (p - onehot(labels));
+      dh = dlogits Wv^T;  dWv = h^T dlogits."""
+    h, Wv = _f64(h), _f64(Wv)
+    labels = np.asarray(labels, dtype=np.int64)
+    lse, dloss = _f64(lse), _f64(dloss)
+    logits = h @ Wv if logits is None else _f64(logits)
+    p = np.exp(logits - lse[:, None])
+    dlogits = p
+    dlogits[np.arange(p.shape[0]), labels] -= 1.0
+    dlogits = dlogits * dloss[:, None]
+    return {"dh": dlogits @ Wv.T, "dWv": h.T @ dlogits, "dlogits": dlogits}
+
+
+def ref_ce_fwd_rows(h, Wv, labels, rows) -> dict:
+    """``ref_ce_fwd`` for the given rows only (rows are independent)."""
+    rows = np.asarray(rows)
+    out = ref_ce_fwd(_f64(h[rows]), Wv, np.asarray(labels)[rows])
+    out["rows"] = rows
+    return out
+
+
+def ref_ce_bwd_sampled(h, Wv, labels, lse, dloss, rows, cols_V, logits=None) -> dict:
+    """``ref_ce_bwd`` with dh restricted to ``rows`` and dWv to the columns
+    ``cols_V``: dh rows need only those rows' dlogits; dWv columns need every
+    row's dlogits in those columns."""
+    h, Wv = _f64(h), _f64(Wv)
+    labels = np.asarray(labels, dtype=np.int64)
+    lse, dloss = _f64(lse), _f64(dloss)
+    rows, cols_V = np.asarray(rows), np.asarray(cols_V)
+
+    def dlog(lg, lab, ls, dl, cols):
+        p = np.exp(lg - ls[:, None])
+        hit = lab[:, None] == cols[None, :]
+        return (p - hit) * dl[:, None]
+    lg_rows = h[rows] @ Wv if logits is None else _f64(logits[rows])
+    dlr = dlog(lg_rows, labels[rows], lse[rows], dloss[rows], np.arange(Wv.shape[1]))
+    lg_cols = h @ Wv[:, cols_V] if logits is None else _f64(logits[:, cols_V])
+    dlc = dlog(lg_cols, labels, lse, dloss, cols_V)
+    return {"rows": rows, "cols_V": cols_V, "dh_rows": dlr @ Wv.T, "dWv_cols": h.T @ dlc}

@@ -523,6 +523,132 @@ def pin_mlp_stored_operand_bruteforce(O):
     assert float(np.max(np.abs(f["gu"] - f0["gu"]))) > 0.0, "rounding had no effect"
 
 
+# ---------------------------------------------------- cross-entropy LM-head pins
+
+def _ce_case(seed, M, d, V, scale=1.0):
+    g = _rng(seed)
+    return dict(h=g.standard_normal((M, d)) * scale, Wv=g.standard_normal((d, V)) / math.sqrt(d),
+                labels=g.integers(0, V, M), dloss=g.standard_normal(M))
+
+
+def pin_ce_torch(O):
+    """torch CPU float64 F.cross_entropy (reduction='none') with autograd of
+    sum_i dloss_i loss_i (library routine)."""
+    import torch
+    import torch.nn.functional as Fn
+    c = _ce_case(61, 12, 16, 300, scale=3.0)
+    th = torch.tensor(c["h"], requires_grad=True)
+    tw = torch.tensor(c["Wv"], requires_grad=True)
+    loss = Fn.cross_entropy(th @ tw, torch.tensor(c["labels"]), reduction="none")
+    (loss * torch.from_numpy(c["dloss"])).sum().backward()
+    f = O.ref_ce_fwd(c["h"], c["Wv"], c["labels"])
+    _close(f["loss"], loss.detach().numpy(), 1e-13, "ce loss vs torch")
+    for logits in (None, f["logits"]):
+        b = O.ref_ce_bwd(c["h"], c["Wv"], c["labels"], f["lse"], c["dloss"], logits)
+        _close(b["dh"], th.grad.numpy(), 1e-12, "ce dh vs torch")
+        _close(b["dWv"], tw.grad.numpy(), 1e-12, "ce dWv vs torch")
+
+
+def pin_ce_finite_differences(O):
+    """Central differences of L = sum_i dloss_i loss_i, tiny shape."""
+    c = _ce_case(62, 3, 4, 7)
+
+    def L(h, Wv):
+        return float(np.sum(c["dloss"] * O.ref_ce_fwd(h, Wv, c["labels"])["loss"]))
+    f = O.ref_ce_fwd(c["h"], c["Wv"], c["labels"])
+    b = O.ref_ce_bwd(c["h"], c["Wv"], c["labels"], f["lse"], c["dloss"])
+    for name, grad in (("h", b["dh"]), ("Wv", b["dWv"])):
+        base = c[name]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            hstep = 1e-6 * max(1.0, abs(base[idx]))
+            hp, wp = c["h"], c["Wv"]
+            arr = base.copy(); arr[idx] += hstep
+            lp = L(arr, wp) if name == "h" else L(hp, arr)
+            arr = base.copy(); arr[idx] -= hstep
+            lm = L(arr, wp) if name == "h" else L(hp, arr)
+            fd[idx] = (lp - lm) / (2 * hstep)
+        _close(grad, fd, 1e-7, f"ce d{name} vs finite differences")
+
+
+def pin_ce_closed_forms(O):
+    """Wv = 0: every logit is 0, lse = log V, loss = log V, softmax uniform so
+    dlogits = dloss (1/V - onehot).  Equal large logits (1000 + shift) give
+    lse = 1000 + shift + log V without overflow.  Adding a constant to every
+    logit of a row (an extra input column of ones) moves lse by it and leaves
+    the loss."""
+    c = _ce_case(63, 5, 6, 40)
+    V = 40
+    f = O.ref_ce_fwd(c["h"], np.zeros((6, V)), c["labels"])
+    _close(f["lse"], np.full(5, math.log(V)), 1e-14, "ce zero weights lse")
+    _close(f["loss"], np.full(5, math.log(V)), 1e-14, "ce zero weights loss")
+    b = O.ref_ce_bwd(c["h"], np.zeros((6, V)), c["labels"], f["lse"], c["dloss"])
+    want = np.full((5, V), 1.0 / V)
+    want[np.arange(5), c["labels"]] -= 1.0
+    _close(b["dlogits"], want * c["dloss"][:, None], 1e-14, "ce uniform dlogits")
+    hb = np.ones((5, 1))
+    Wb = np.full((1, V), 1000.0)
+    fb = O.ref_ce_fwd(hb, Wb, c["labels"])
+    _close(fb["lse"], np.full(5, 1000.0 + math.log(V)), 1e-14, "ce large logits lse")
+    assert np.all(np.isfinite(fb["loss"])), "ce overflow"
+    shift = np.array([0.5, -3.0, 7.0, 0.0, 100.0])
+    ha = np.concatenate([c["h"], shift[:, None]], axis=1)
+    Wa = np.concatenate([c["Wv"], np.ones((1, V))], axis=0)
+    f0 = O.ref_ce_fwd(c["h"], c["Wv"], c["labels"])
+    fa = O.ref_ce_fwd(ha, Wa, c["labels"])
+    _close(fa["lse"], f0["lse"] + shift, 1e-12, "ce shift lse")
+    _close(fa["loss"], f0["loss"], 1e-12, "ce shift loss")
+
+
+def pin_ce_invariants(O):
+    """Softmax rows sum to 1, so every row of dlogits sums to 0 and so does
+    every row of dWv (its columns sum to zero vectors); <dh, h> = <dlogits,
+    logits> = sum_i dloss_i (E_p[logits_i] - logits_i,label), with p from
+    scipy's softmax (library routine)."""
+    from scipy.special import softmax
+    c = _ce_case(64, 9, 8, 50, scale=2.0)
+    f = O.ref_ce_fwd(c["h"], c["Wv"], c["labels"])
+    b = O.ref_ce_bwd(c["h"], c["Wv"], c["labels"], f["lse"], c["dloss"])
+    _close(np.sum(b["dlogits"], axis=1), np.zeros(9), 1e-13, "ce dlogits rows sum to 0")
+    _close(np.sum(b["dWv"], axis=1), np.zeros(8), 1e-12, "ce dWv rows sum to 0")
+    lg = c["h"] @ c["Wv"]
+    p = softmax(lg, axis=1)
+    want = np.sum(c["dloss"] * (np.sum(p * lg, axis=1) - lg[np.arange(9), c["labels"]]))
+    _close(np.sum(b["dh"] * c["h"]), want, 1e-12, "ce <dh,h>")
+
+
+def pin_ce_partials(O):
+    """The tiled running (max, sum-exp) state reaches scipy's logsumexp
+    (library routine), for tile widths that divide V and ones that do not,
+    and with one tile holding the row's largest logits by far."""
+    from scipy.special import logsumexp
+    g = _rng(65)
+    x = g.standard_normal((6, 700)) * 5.0
+    x[2, 650:] += 80.0
+    for BN in (256, 128, 100, 700, 1):
+        p = O.ref_ce_partials(x, BN)
+        _close(p["lse"], logsumexp(x, axis=1), 1e-12, f"ce partials BN={BN}")
+        T = -(-700 // BN)
+        assert p["m"].shape == (6, T) and p["s"].shape == (6, T)
+        _close(p["m"][:, 0], np.max(x[:, :BN], axis=1), 0.0, "ce partial max")
+
+
+def pin_ce_sampled(O):
+    """Row/column-restricted forms equal slices of the full forms, with the
+    logits recomputed and with saved logits passed in."""
+    c = _ce_case(66, 20, 8, 90)
+    f = O.ref_ce_fwd(c["h"], c["Wv"], c["labels"])
+    rows, cols = np.array([0, 7, 19]), np.array([0, 3, 44, 89])
+    fr = O.ref_ce_fwd_rows(c["h"], c["Wv"], c["labels"], rows)
+    for k in ("logits", "lse", "loss"):
+        _close(fr[k], f[k][rows], 1e-14, f"ce rows {k}")
+    b = O.ref_ce_bwd(c["h"], c["Wv"], c["labels"], f["lse"], c["dloss"])
+    for logits in (None, f["logits"]):
+        bs = O.ref_ce_bwd_sampled(c["h"], c["Wv"], c["labels"], f["lse"], c["dloss"], rows, cols, logits)
+        _close(bs["dh_rows"], b["dh"][rows], 1e-13, "ce sampled dh")
+        _close(bs["dWv_cols"], b["dWv"][:, cols], 1e-13, "ce sampled dWv")
+
+
 def pin_bwd_dy_in_finite_differences(O):
     """``ref_bwd`` with dy_in: central differences of <dz, z> + <dy_in, y> for
     the block's own forward, tiny shape."""
@@ -583,6 +709,7 @@ ALL_PINS = [
     pin_swiglu_finite_differences, pin_swiglu_torch, pin_swiglu_invariants,
     pin_golden_swiglu, pin_swiglu_sampled, pin_bf16_rne, pin_mlp_finite_differences,
     pin_mlp_torch, pin_mlp_invariants, pin_mlp_sampled, pin_mlp_dgu_rounding,
-    pin_mlp_stored_operand_bruteforce,
+    pin_mlp_stored_operand_bruteforce, pin_ce_torch, pin_ce_finite_differences,
+    pin_ce_closed_forms, pin_ce_invariants, pin_ce_partials, pin_ce_sampled,
     pin_bwd_dy_in_finite_differences,
 ]

@@ -152,6 +152,45 @@ def _mlp_bwd_variant(kind):
     return bwd
 
 
+def _ce_fwd_variant(kind):
+    def fwd(h, Wv, labels):
+        h, Wv = _f(h, Wv)
+        labels = np.asarray(labels, dtype=np.int64)
+        logits = h @ Wv
+        if kind == "no_max_shift":
+            lse = np.log(np.sum(np.exp(logits), axis=1))
+        else:
+            m = np.max(logits, axis=1)
+            lse = m + np.log(np.sum(np.exp(logits - m[:, None]), axis=1))
+        lab = logits[np.arange(logits.shape[0]), labels]
+        loss = (lab - lse) if kind == "loss_sign" else (lse - lab)
+        return {"logits": logits, "lse": lse, "loss": loss}
+    return fwd
+
+
+def _ce_bwd_variant(kind):
+    def bwd(h, Wv, labels, lse, dloss, logits=None):
+        out = dict(oracle.ref_ce_bwd(h, Wv, labels, lse, dloss, logits))
+        h64, W64 = _f(h, Wv)
+        dl = out["dlogits"]
+        if kind == "no_onehot":
+            dl = dl.copy()
+            dl[np.arange(dl.shape[0]), np.asarray(labels)] += np.asarray(dloss, dtype=np.float64)
+        if kind == "no_dloss":
+            dl = dl / np.asarray(dloss, dtype=np.float64)[:, None]
+        out.update({"dlogits": dl, "dh": dl @ W64.T, "dWv": h64.T @ dl})
+        return out
+    return bwd
+
+
+def ce_partials_no_rescale(logits, BN=256):
+    out = dict(oracle.ref_ce_partials(logits, BN))
+    x = np.asarray(logits, dtype=np.float64)
+    m, s_ = out["m"], out["s"]
+    out["lse"] = np.max(m, axis=1) + np.log(np.sum(s_, axis=1))   # tiles summed without exp(m_t - m)
+    return out
+
+
 def bf16_half_away(x):
     x = np.asarray(x, dtype=np.float64)
     out = np.array(x, copy=True)
@@ -187,6 +226,11 @@ MUTANTS = {
     "bf16_ties_away": {"bf16_rne": bf16_half_away},
     "mlp_r_after_silu": {"ref_mlp_fwd": _mlp_fwd_variant("r_after_silu")},
     "mlp_round_inside_r": {"ref_mlp_fwd": _mlp_fwd_variant("round_inside_r")},
+    "ce_lse_without_max_shift": {"ref_ce_fwd": _ce_fwd_variant("no_max_shift")},
+    "ce_loss_sign": {"ref_ce_fwd": _ce_fwd_variant("loss_sign")},
+    "ce_bwd_no_onehot": {"ref_ce_bwd": _ce_bwd_variant("no_onehot")},
+    "ce_bwd_no_dloss": {"ref_ce_bwd": _ce_bwd_variant("no_dloss")},
+    "ce_partials_no_rescale": {"ref_ce_partials": ce_partials_no_rescale},
     "mlp_bwd_drops_dy_in": {"ref_mlp_bwd": _mlp_bwd_variant("drop_dy_in")},
     "mlp_bwd_dy_in_sign": {"ref_mlp_bwd": _mlp_bwd_variant("dy_in_sign")},
     "mlp_bwd_dW_without_r": {"ref_mlp_bwd": _mlp_bwd_variant("dW_without_r")},
