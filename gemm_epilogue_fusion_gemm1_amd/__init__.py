@@ -1,5 +1,5 @@
-"""MI355X-native fused GEMM-Residual-RMSNorm-GEMM block, SwiGLU block, and the
-two chained as an MLP sub-layer.
+"""MI355X-native fused GEMM-Residual-RMSNorm-GEMM block, SwiGLU block, the two
+chained as an MLP sub-layer, and the LM-head GEMM with cross-entropy.
 
 Thin Python binding over the C-ABI library ``libcoda.so`` (include/coda.h).
 Every step of the computation runs in the library's HIP kernels; this module
@@ -9,7 +9,8 @@ PyTorch fallback: without the built library every call raises.
 
 Low-level calls (same names and argument order as the C functions, outputs
 preallocated by the caller):
-    coda_fwd, coda_bwd, coda_swiglu_fwd, coda_swiglu_bwd, coda_mlp_fwd, coda_mlp_bwd
+    coda_fwd, coda_bwd, coda_swiglu_fwd, coda_swiglu_bwd, coda_mlp_fwd, coda_mlp_bwd,
+    coda_ce_fwd, coda_ce_bwd
 Convenience calls (allocate outputs):
     fwd(X, W1, R, gamma, W2, eps)        -> (z, y, r)
     bwd(X, W1, gamma, W2, y, r, dz)      -> (dX, dW1, dR, dW2, dgamma)
@@ -18,6 +19,8 @@ Convenience calls (allocate outputs):
     mlp_fwd(X, W1, R, gamma, W, Wd, eps) -> (z, y, r, gu, a)
     mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in=None)
                                          -> (dX, dW1, dR, dW, dWd, dgamma)
+    ce_fwd(h, Wv, labels)                -> (loss, lse, logits)
+    ce_bwd(h, Wv, labels, logits, lse, dloss) -> (dh, dWv)
 """
 from __future__ import annotations
 
@@ -27,7 +30,8 @@ import os
 __all__ = [
     "CodaError", "lib_path", "load_library", "coda_fwd", "coda_bwd", "coda_swiglu_fwd",
     "coda_swiglu_bwd", "coda_mlp_fwd", "coda_mlp_bwd", "fwd", "bwd", "swiglu_fwd",
-    "swiglu_bwd", "mlp_fwd", "mlp_bwd", "fwd_workspace_bytes", "bwd_workspace_bytes",
+    "swiglu_bwd", "mlp_fwd", "mlp_bwd", "coda_ce_fwd", "coda_ce_bwd", "ce_fwd", "ce_bwd",
+    "ce_fwd_workspace_bytes", "ce_bwd_workspace_bytes", "fwd_workspace_bytes", "bwd_workspace_bytes",
     "swiglu_bwd_workspace_bytes", "mlp_fwd_workspace_bytes", "mlp_bwd_workspace_bytes",
     "version", "trace_start", "trace_read", "trace_stop",
 ]
@@ -76,6 +80,8 @@ def load_library() -> ctypes.CDLL:
         "coda_swiglu_bwd_workspace_bytes": [i32, i64, i64, i64],
         "coda_mlp_fwd_workspace_bytes": [i32, i64, i64, i64, i64],
         "coda_mlp_bwd_workspace_bytes": [i32, i64, i64, i64, i64],
+        "coda_ce_fwd_workspace_bytes": [i32, i64, i64, i64],
+        "coda_ce_bwd_workspace_bytes": [i32, i64, i64, i64],
     }.items():
         getattr(L, name).restype = sz
         getattr(L, name).argtypes = args
@@ -91,6 +97,10 @@ def load_library() -> ctypes.CDLL:
     L.coda_mlp_fwd.argtypes = [i32, i64, i64, i64, i64, f32] + [vp] * 11 + [vp, sz, vp]
     L.coda_mlp_bwd.restype = i32
     L.coda_mlp_bwd.argtypes = [i32, i64, i64, i64, i64] + [vp] * 17 + [vp, sz, vp]
+    L.coda_ce_fwd.restype = i32
+    L.coda_ce_fwd.argtypes = [i32, i64, i64, i64] + [vp] * 6 + [vp, sz, vp]
+    L.coda_ce_bwd.restype = i32
+    L.coda_ce_bwd.argtypes = [i32, i64, i64, i64] + [vp] * 8 + [vp, sz, vp]
     L.coda_trace_start.restype = i32
     L.coda_trace_start.argtypes = [i32]
     L.coda_trace_count.restype = i32
@@ -168,6 +178,14 @@ def mlp_fwd_workspace_bytes(dtype_code, M, K, d, F) -> int:
 
 def mlp_bwd_workspace_bytes(dtype_code, M, K, d, F) -> int:
     return int(load_library().coda_mlp_bwd_workspace_bytes(dtype_code, M, K, d, F))
+
+
+def ce_fwd_workspace_bytes(dtype_code, M, d, V) -> int:
+    return int(load_library().coda_ce_fwd_workspace_bytes(dtype_code, M, d, V))
+
+
+def ce_bwd_workspace_bytes(dtype_code, M, d, V) -> int:
+    return int(load_library().coda_ce_bwd_workspace_bytes(dtype_code, M, d, V))
 
 
 # ------------------------------------------------------------ tracing
@@ -256,6 +274,31 @@ def coda_mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in, dX, dW1, dR, dW, d
         _dtype_code(X), M, K, d, F, _ptr(X), _ptr(W1), _ptr(gamma), _ptr(W), _ptr(Wd), _ptr(y),
         _ptr(r), _ptr(gu), _ptr(a), _ptr(dz), _ptr(dy_in), _ptr(dX), _ptr(dW1), _ptr(dR), _ptr(dW),
         _ptr(dWd), _ptr(dgamma), _ptr(workspace), workspace.numel(), _stream()))
+
+
+def _labels(t):
+    import torch
+    if t.dtype != torch.int32:
+        raise TypeError(f"labels must be torch.int32, got {t.dtype}")
+    return _ptr(t)
+
+
+def coda_ce_fwd(h, Wv, labels, logits, lse, loss, workspace):
+    L = load_library()
+    M, d = h.shape
+    V = Wv.shape[1]
+    _check("coda_ce_fwd", L.coda_ce_fwd(
+        _dtype_code(h), M, d, V, _ptr(h), _ptr(Wv), _labels(labels), _ptr(logits), _ptr(lse), _ptr(loss),
+        _ptr(workspace), workspace.numel(), _stream()))
+
+
+def coda_ce_bwd(h, Wv, labels, logits, lse, dloss, dh, dWv, workspace):
+    L = load_library()
+    M, d = h.shape
+    V = Wv.shape[1]
+    _check("coda_ce_bwd", L.coda_ce_bwd(
+        _dtype_code(h), M, d, V, _ptr(h), _ptr(Wv), _labels(labels), _ptr(logits), _ptr(lse), _ptr(dloss),
+        _ptr(dh), _ptr(dWv), _ptr(workspace), workspace.numel(), _stream()))
 
 
 # ------------------------------------------------------ convenience calls
@@ -357,3 +400,31 @@ def mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in=None):
     ws = _workspace(mlp_bwd_workspace_bytes(_dtype_code(X), M, K, d, F), X.device)
     coda_mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in, dX, dW1, dR, dW, dWd, dgamma, ws)
     return dX, dW1, dR, dW, dWd, dgamma
+
+
+def ce_fwd(h, Wv, labels):
+    """Per-row cross-entropy of the logits h Wv against labels (int32).
+    Returns (loss, lse, logits); lse and logits are saved for the backward."""
+    import torch
+    M, d = h.shape
+    V = Wv.shape[1]
+    _shape(Wv, d, V, name="Wv"); _shape(labels, M, name="labels")
+    logits = torch.empty((M, V), dtype=h.dtype, device=h.device)
+    lse = torch.empty((M,), dtype=torch.float32, device=h.device)
+    loss = torch.empty((M,), dtype=torch.float32, device=h.device)
+    ws = _workspace(ce_fwd_workspace_bytes(_dtype_code(h), M, d, V), h.device)
+    coda_ce_fwd(h, Wv, labels, logits, lse, loss, ws)
+    return loss, lse, logits
+
+
+def ce_bwd(h, Wv, labels, logits, lse, dloss):
+    """Gradients of sum_i dloss_i loss_i.  Returns (dh, dWv)."""
+    import torch
+    M, d = h.shape
+    V = Wv.shape[1]
+    _shape(logits, M, V, name="logits"); _shape(lse, M, name="lse"); _shape(dloss, M, name="dloss")
+    dh = torch.empty_like(h)
+    dWv = torch.empty_like(Wv)
+    ws = _workspace(ce_bwd_workspace_bytes(_dtype_code(h), M, d, V), h.device)
+    coda_ce_bwd(h, Wv, labels, logits, lse, dloss, dh, dWv, ws)
+    return dh, dWv

@@ -629,4 +629,124 @@ coda_status coda_mlp_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int6
                                     dW, dgamma, ws, wsb + dgu_bytes, names, s));
 }
 
+// ------------------------------------------- LM-head GEMM with cross-entropy
+
+namespace {
+struct CeWs {
+  size_t pmax, psum, lab, total;
+  int T;
+};
+CeWs ce_ws(int64_t M, int64_t V) {
+  CeWs w;
+  w.T = (int)cdiv(V, coda::kTileN);
+  w.pmax = 0;
+  w.psum = round_up((size_t)M * w.T * 4);
+  w.lab = w.psum + round_up((size_t)M * w.T * 4);
+  w.total = w.lab + round_up((size_t)M * 4);
+  return w;
+}
+}  // namespace
+
+size_t coda_ce_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t d, int64_t V) {
+  (void)d;
+  if (dtype != CODA_BF16 || M < 1 || V < 1) return 0;
+  return ce_ws(M, V).total;
+}
+
+coda_status coda_ce_fwd(coda_dtype dtype, int64_t M, int64_t d, int64_t V, const void* h,
+                        const void* Wv, const int32_t* labels, void* logits, float* lse,
+                        float* loss, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
+  if (!h || !Wv || !labels || !logits || !lse || !loss) return CODA_ERR_NULL;
+  if (!dim_ok(dtype, M) || !dim_ok(dtype, d) || !dim_ok(dtype, V)) return CODA_ERR_SHAPE;
+  if (!bytes_ok(dtype, M, d) || !bytes_ok(dtype, d, V) || !bytes_ok(dtype, M, V))
+    return CODA_ERR_SHAPE;
+  if (dtype != CODA_BF16) return CODA_ERR_UNSUPPORTED;
+  for (const void* p : {h, Wv, (const void*)labels, (const void*)logits, (const void*)lse,
+                        (const void*)loss})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  const CeWs ws = ce_ws(M, V);
+  if (!workspace || workspace_bytes < ws.total) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const size_t e = 2;
+  const Range in[] = {rng(h, M * d * e), rng(Wv, d * V * e), rng(labels, M * 4)};
+  const Range out[] = {rng(logits, M * V * e), rng(lse, M * 4), rng(loss, M * 4),
+                       rng(workspace, ws.total)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)workspace;
+  float* pmax = (float*)(wsb + ws.pmax);
+  float* psum = (float*)(wsb + ws.psum);
+  float* lab = (float*)(wsb + ws.lab);
+  hipError_t err;
+  // C1: logits = h Wv; epilogue stores them and each tile's (max, sum-exp) per row
+  GemmArgs c1 = gemm(M, V, d, h, d, M * d, Wv, V, d * V, logits, V);
+  c1.part_row = pmax;
+  c1.part_col = psum;
+  c1.ld_part_row = ws.T;
+  c1.labels = labels;
+  c1.lab_out = lab;
+  const double Md = 2.0 * M * d, dV = 2.0 * d * V, MV = 2.0 * M * V;
+  if ((err = traced("c1_gemm_logits_lse_partials", gemm_flops(M, V, d),
+                    Md + dV + MV + 8.0 * M * ws.T + 8.0 * M, s, [&] {
+                      return coda::launch_gemm_bf16(c1, true, false, coda::EPI_CE_STATS, s);
+                    })) != hipSuccess)
+    return hip_status(err);
+  // C2: lse and loss from the partials
+  return hip_status(traced("c2_ce_combine", 0.0, 8.0 * M * ws.T + 12.0 * M, s, [&] {
+    return coda::launch_ce_combine(pmax, psum, ws.T, ws.T, lab, M, lse, loss, s);
+  }));
+}
+
+size_t coda_ce_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t d, int64_t V) {
+  (void)d;
+  if (dtype != CODA_BF16 || M < 1 || V < 1) return 0;
+  return round_up((size_t)M * V * 2);
+}
+
+coda_status coda_ce_bwd(coda_dtype dtype, int64_t M, int64_t d, int64_t V, const void* h,
+                        const void* Wv, const int32_t* labels, const void* logits,
+                        const float* lse, const float* dloss, void* dh, void* dWv,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
+  if (!h || !Wv || !labels || !logits || !lse || !dloss || !dh || !dWv) return CODA_ERR_NULL;
+  if (!dim_ok(dtype, M) || !dim_ok(dtype, d) || !dim_ok(dtype, V)) return CODA_ERR_SHAPE;
+  if (!bytes_ok(dtype, M, d) || !bytes_ok(dtype, d, V) || !bytes_ok(dtype, M, V))
+    return CODA_ERR_SHAPE;
+  if (dtype != CODA_BF16) return CODA_ERR_UNSUPPORTED;
+  for (const void* p : {h, Wv, (const void*)labels, logits, (const void*)lse,
+                        (const void*)dloss, (const void*)dh, (const void*)dWv})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  const size_t need = coda_ce_bwd_workspace_bytes(dtype, M, d, V);
+  if (!workspace || workspace_bytes < need) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const size_t e = 2;
+  const Range in[] = {rng(h, M * d * e), rng(Wv, d * V * e), rng(labels, M * 4),
+                      rng(logits, M * V * e), rng(lse, M * 4), rng(dloss, M * 4)};
+  const Range out[] = {rng(dh, M * d * e), rng(dWv, d * V * e), rng(workspace, need)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  void* dlog = workspace;
+  hipError_t err;
+  const double Md = 2.0 * M * d, dV = 2.0 * d * V, MV = 2.0 * M * V;
+  // C3: dlogits = dloss (softmax - onehot) from the saved logits and lse
+  if ((err = traced("c3_ce_dlogits", 0.0, 2.0 * MV + 12.0 * M, s, [&] {
+         return coda::launch_ce_dlogits(logits, labels, lse, dloss, dlog, M, V, s);
+       })) != hipSuccess)
+    return hip_status(err);
+  // C4: dh = dlogits Wv^T
+  GemmArgs c4 = gemm(M, d, V, dlog, V, M * V, Wv, V, d * V, dh, d);
+  if ((err = traced("c4_gemm_dh", gemm_flops(M, d, V), MV + dV + Md, s, [&] {
+         return coda::launch_gemm_bf16(c4, true, true, coda::EPI_STORE, s);
+       })) != hipSuccess)
+    return hip_status(err);
+  // C5: dWv = h^T dlogits
+  GemmArgs c5 = gemm(d, V, M, h, d, M * d, dlog, V, M * V, dWv, V);
+  return hip_status(traced("c5_gemm_dWv", gemm_flops(d, V, M), Md + MV + dV, s, [&] {
+    return coda::launch_gemm_bf16(c5, false, false, coda::EPI_STORE, s);
+  }));
+}
+
 }  // extern "C"

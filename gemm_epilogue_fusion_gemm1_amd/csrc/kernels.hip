@@ -485,6 +485,7 @@ gemm_bf16_kernel(GemmArgs g) {
   // EPI_RSQRT_*: r for the tile's rows from the first GEMM's partial sums,
   // summed in the same order as the stand-alone reduction kernel, into rrow
   float* rrow = red + WNv * BM + WMv * BN;          // [BM] row scales
+  float* cered = rrow + BM;                         // [WN][BM] sum-exp partials (EPI_CE_STATS)
   auto tile_row_rsqrt = [&]() {
     if (t < BM) {
       const int row = row0 + t;
@@ -508,7 +509,8 @@ gemm_bf16_kernel(GemmArgs g) {
   };
 
   if constexpr (EPI == EPI_STORE || EPI == EPI_ROWSCALE || EPI == EPI_RESID_SUMSQ ||
-                EPI == EPI_DN || EPI == EPI_SWIGLU_BWD || EPI == EPI_RSQRT_SCALE) {
+                EPI == EPI_DN || EPI == EPI_SWIGLU_BWD || EPI == EPI_RSQRT_SCALE ||
+                EPI == EPI_CE_STATS) {
     __bf16* C = (__bf16*)g.C;
     f32x4 glo{}, ghi{}, clo{0.f, 0.f, 0.f, 0.f}, chi{0.f, 0.f, 0.f, 0.f};
     if constexpr (EPI == EPI_DN || EPI == EPI_RESID_SUMSQ) {
@@ -578,6 +580,33 @@ gemm_bf16_kernel(GemmArgs g) {
           }
           s = sum8(s);
           if (c8 == 0) red[wn * BM + lrow_t] = s;
+        } else if constexpr (EPI == EPI_CE_STATS) {
+          // logits stored; the stateful max / sum-exp of the row over this
+          // wave's 64 columns (8 lanes x 8), columns past N left out
+          float mx = -INFINITY;
+          if (ok) {
+            st8(C + o, lo, hi);
+            mx = fmaxf(fmaxf(fmaxf(lo[0], lo[1]), fmaxf(lo[2], lo[3])),
+                       fmaxf(fmaxf(hi[0], hi[1]), fmaxf(hi[2], hi[3])));
+            const int lab = g.labels[row];
+            if (lab >= gcol && lab < gcol + 8) {
+              const int e = lab - gcol;
+              g.lab_out[row] = e < 4 ? lo[e] : hi[e - 4];
+            }
+          }
+          mx = fmaxf(mx, __shfl_xor(mx, 1));
+          mx = fmaxf(mx, __shfl_xor(mx, 2));
+          mx = fmaxf(mx, __shfl_xor(mx, 4));
+          float se = 0.0f;
+          if (ok) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) se += __expf(lo[e] - mx) + __expf(hi[e] - mx);
+          }
+          se = sum8(se);
+          if (c8 == 0) {
+            red[wn * BM + lrow_t] = mx;
+            cered[wn * BM + lrow_t] = se;
+          }
         } else if constexpr (EPI == EPI_SWIGLU_BWD) {
           // da = acc [M, F]; g, u from the saved gu; dgu = [dg | du]
           if (ok) {
@@ -623,6 +652,24 @@ gemm_bf16_kernel(GemmArgs g) {
                   bf16x8{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3]),
                          f2bf(v[4]), f2bf(v[5]), f2bf(v[6]), f2bf(v[7])};
           }
+        }
+      }
+    }
+    if constexpr (EPI == EPI_CE_STATS) {
+      // combine the WN waves' (max, sum-exp) of each row in wave order
+      __syncthreads();
+      if (t < BM) {
+        const int row = row0 + t;
+        float m = red[t];
+        for (int w = 1; w < WNv; ++w) m = fmaxf(m, red[w * BM + t]);
+        float sm = 0.0f;
+        for (int w = 0; w < WNv; ++w) {
+          const float mw = red[w * BM + t];
+          if (mw > -INFINITY) sm += cered[w * BM + t] * __expf(mw - m);
+        }
+        if (row < g.M) {
+          g.part_row[(int64_t)row * g.ld_part_row + tn] = m;
+          g.part_col[(int64_t)row * g.ld_part_row + tn] = sm;
         }
       }
     }
@@ -882,6 +929,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStr
     switch (epi) {
       case EPI_STORE: return launch_one<true, false, EPI_STORE>(g, s);
       case EPI_RESID_SUMSQ: return launch_one<true, false, EPI_RESID_SUMSQ>(g, s);
+      case EPI_CE_STATS: return launch_one<true, false, EPI_CE_STATS>(g, s);
       case EPI_SWIGLU: return launch_one<true, false, EPI_SWIGLU>(g, s);
       default: break;
     }
@@ -926,6 +974,71 @@ hipError_t launch_row_rsqrt(const float* P, int64_t ldp, int T, int64_t M, int64
                             float* r, hipStream_t s) {
   hipLaunchKernelGGL(row_rsqrt_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, P, ldp,
                      T, M, 1.0f / (float)d, eps, r);
+  return hipGetLastError();
+}
+
+// One wave per row: lane l folds the row's tiles l, l + 64, ... into a running
+// (max, sum-exp) pair, then the 64 lanes combine in a fixed butterfly order.
+__global__ void ce_combine_kernel(const float* __restrict__ pmax, const float* __restrict__ psum,
+                                  int64_t ldp, int T, const float* __restrict__ lab, int64_t M,
+                                  float* __restrict__ lse, float* __restrict__ loss) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  float m = -INFINITY, sm = 0.0f;
+  if (row < M) {
+    for (int t = lane; t < T; t += 64) {
+      const float mt = pmax[row * ldp + t], st = psum[row * ldp + t];
+      const float nm = fmaxf(m, mt);
+      sm = (m > -INFINITY ? sm * __expf(m - nm) : 0.0f) + st * __expf(mt - nm);
+      m = nm;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float mo = __shfl_xor(m, o), so = __shfl_xor(sm, o);
+    const float nm = fmaxf(m, mo);
+    sm = (m > -INFINITY ? sm * __expf(m - nm) : 0.0f) + (mo > -INFINITY ? so * __expf(mo - nm) : 0.0f);
+    m = nm;
+  }
+  if (row < M && lane == 0) {
+    const float l = m + __logf(sm);
+    lse[row] = l;
+    loss[row] = l - lab[row];
+  }
+}
+
+__global__ void ce_dlogits_kernel(const __bf16* __restrict__ logits, const int* __restrict__ labels,
+                                  const float* __restrict__ lse, const float* __restrict__ dloss,
+                                  __bf16* __restrict__ dlogits, int64_t M, int64_t V) {
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t e0 = v * 8;
+  if (e0 >= M * V) return;
+  const int64_t i = e0 / V;
+  const int64_t j0 = e0 - i * V;
+  const float li = lse[i], di = dloss[i];
+  const int lab = labels[i];
+  const bf16x8 x = *(const bf16x8*)(logits + e0);
+  bf16x8 o;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float pk = __expf(bf2f(x[k]) - li);
+    o[k] = f2bf(di * (pk - (j0 + k == lab ? 1.0f : 0.0f)));
+  }
+  *(bf16x8*)(dlogits + e0) = o;
+}
+
+hipError_t launch_ce_combine(const float* pmax, const float* psum, int64_t ldp, int T,
+                             const float* lab, int64_t M, float* lse, float* loss, hipStream_t s) {
+  hipLaunchKernelGGL(ce_combine_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, pmax, psum,
+                     ldp, T, lab, M, lse, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_dlogits(const void* logits, const int* labels, const float* lse,
+                             const float* dloss, void* dlogits, int64_t M, int64_t V, hipStream_t s) {
+  const int64_t chunks = (M * V) / 8;
+  hipLaunchKernelGGL(ce_dlogits_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
+                     (const __bf16*)logits, labels, lse, dloss, (__bf16*)dlogits, M, V);
   return hipGetLastError();
 }
 

@@ -28,6 +28,9 @@ enum Epi : int {
                        // tiles of column 0 write r to r_out
   EPI_RSQRT_SWIGLU = 7,  // r_i as EPI_RSQRT_SCALE; gate/up pair scaled by r_i, then as
                          // EPI_SWIGLU: C = gu (both halves), C2 = silu(g) * u
+  EPI_CE_STATS = 8,      // logits: C = acc; per row and tile: part_row = max_j acc,
+                         // part_col = sum_j exp(acc - max) ([M][tiles_n] each, ld_part_row);
+                         // lab_out[i] = acc[i][labels[i]] (written by the tile holding it)
 };
 
 // Operand layouts.  "K-major" = the contraction index is contiguous in memory.
@@ -45,6 +48,7 @@ struct GemmArgs {
   int F;                         // SwiGLU half width (gate columns)
   int nparts; float inv_d; float eps; float* r_out;   // EPI_RSQRT_SCALE
   int c2_trans;                  // EPI_RESID_SUMSQ: C2 stored transposed
+  const int* labels; float* lab_out;   // EPI_CE_STATS
   uint32_t A_bytes, B_bytes;     // buffer extents for hardware bounds checks
 };
 
@@ -61,6 +65,15 @@ hipError_t launch_row_rsqrt(const float* P, int64_t ldp, int T, int64_t M, int64
 // c[i] = r_i^3 * (sum_t S[i][t]) / d ;  dgamma[j] = sum_tau G[tau][j]
 hipError_t launch_bwd_reduce(const float* S, int64_t lds, int Tn, const float* r, int64_t M,
                              int64_t d, const float* G, int Tm, float* c, float* dgamma,
+                             hipStream_t stream);
+// lse[i] = m + log s over the tiles' (max, sum-exp) pairs combined in order;
+// loss[i] = lse[i] - lab[i]
+hipError_t launch_ce_combine(const float* pmax, const float* psum, int64_t ldp, int T,
+                             const float* lab, int64_t M, float* lse, float* loss,
+                             hipStream_t stream);
+// dlogits[i][j] = dloss[i] (exp(logits[i][j] - lse[i]) - [j == labels[i]])  (bf16)
+hipError_t launch_ce_dlogits(const void* logits, const int* labels, const float* lse,
+                             const float* dloss, void* dlogits, int64_t M, int64_t V,
                              hipStream_t stream);
 // in place: dR[i][j] = r_i dR[i][j] - c_i y[i][j] (+ dy_in[i][j] when dy_in is
 // not NULL)  (dR holds dn on entry)

@@ -223,6 +223,46 @@ coda_status coda_mlp_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int6
                          size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * LM-head GEMM with cross-entropy.  The pages' stateful epilogue primitive
+ * keeps a running max and sum of exponentials across the tiles of a row,
+ * which cross-entropy uses ([JA]/[RU]/[FR] primitives sections):
+ *   logits = h Wv;  lse_i = log sum_j exp(logits_ij);
+ *   loss_i = lse_i - logits_i,labels_i     (one loss per row, no reduction).
+ * The GEMM's epilogue stores the logits (bf16, saved for the backward) and
+ * each 256-column tile's (max, sum-exp) pair per row from the fp32
+ * accumulator, plus the label's fp32 logit; a small kernel combines the
+ * pairs in tile order into lse and loss.
+ *
+ *   h [M,d], Wv [d,V]: in (dtype).  labels [M]: in, int32 in [0, V) (a label
+ *   outside that range is never used as an index; that row's loss is then
+ *   undefined).   logits [M,V]: out (dtype).   lse [M], loss [M]: out, float32.
+ *   workspace: >= coda_ce_fwd_workspace_bytes(...) bytes (the tile pairs).
+ * Errors as coda_fwd (no eps); CODA_F32 returns CODA_ERR_UNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+size_t coda_ce_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t d, int64_t V);
+coda_status coda_ce_fwd(coda_dtype dtype, int64_t M, int64_t d, int64_t V, const void* h,
+                        const void* Wv, const int32_t* labels, void* logits, float* lse,
+                        float* loss, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backward of the cross-entropy LM head: the exact gradient of
+ * L = sum_i dloss_i loss_i given the saved logits and lse (for a mean over
+ * rows, dloss_i = 1/M):
+ *   dlogits = diag(dloss) (exp(logits - lse) - onehot(labels));
+ *   dh = dlogits Wv^T;  dWv = h^T dlogits.
+ *
+ *   h [M,d], Wv [d,V], labels [M] (int32), logits [M,V], lse [M] (float32),
+ *   dloss [M] (float32): in.   dh [M,d], dWv [d,V]: out (dtype).
+ *   workspace: >= coda_ce_bwd_workspace_bytes(...) bytes (holds dlogits).
+ * CODA_F32 returns CODA_ERR_UNSUPPORTED in this build.
+ * ---------------------------------------------------------------------- */
+size_t coda_ce_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t d, int64_t V);
+coda_status coda_ce_bwd(coda_dtype dtype, int64_t M, int64_t d, int64_t V, const void* h,
+                        const void* Wv, const int32_t* labels, const void* logits,
+                        const float* lse, const float* dloss, void* dh, void* dWv,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Kernel tracing (measurement aid; off by default).
  *
  * coda_trace_start(capacity) creates 2*capacity timing events (host call,

@@ -235,3 +235,25 @@ def test_mlp_rejects(L):
     assert mlp_bwd_call(L, dy_in=ctypes.c_void_p((1 << 41) + 4)) == ALIGN
     d_R = m(64 * 48 * 2)
     assert mlp_bwd_call(L, dR=d_R, dy_in=d_R) == ALIAS          # dy_in may not overlap an output
+
+
+def test_ce_rejects(L):
+    m = FakeMem()
+    M, d, V = 64, 32, 200
+    h, Wv, lab = m(M * d * 2), m(d * V * 2), m(M * 4)
+    logits, lse, loss, ws = m(M * V * 2), m(M * 4), m(M * 4), m(1 << 20)
+    need = L.coda_ce_fwd_workspace_bytes(BF16, M, d, V)
+    assert need >= 2 * M * ((V + 255) // 256) * 4 + M * 4
+    assert L.coda_ce_fwd(BF16, M, d, V, h, Wv, None, logits, lse, loss, ws, need, None) == NULL
+    assert L.coda_ce_fwd(BF16, M, d, 204, h, Wv, lab, logits, lse, loss, ws, need, None) == SHAPE
+    assert L.coda_ce_fwd(F32, M, d, V, h, Wv, lab, logits, lse, loss, ws, need, None) == UNSUPPORTED
+    assert L.coda_ce_fwd(BF16, M, d, V, h, Wv, lab, logits, lse, loss, ws, need - 16, None) == WORKSPACE
+    assert L.coda_ce_fwd(BF16, M, d, V, h, Wv, lab, logits, lse, lse, ws, need, None) == ALIAS
+    assert L.coda_ce_fwd(BF16, M, d, V, h, Wv, ctypes.c_void_p(lab.value + 4), logits, lse, loss, ws, need,
+                         None) == ALIGN
+    dl, dh, dWv = m(M * 4), m(M * d * 2), m(d * V * 2)
+    nb = L.coda_ce_bwd_workspace_bytes(BF16, M, d, V)
+    assert nb >= M * V * 2
+    assert L.coda_ce_bwd(BF16, M, d, V, h, Wv, lab, logits, lse, dl, dh, dWv, ws, nb - 16, None) == WORKSPACE
+    assert L.coda_ce_bwd(BF16, M, d, V, h, Wv, lab, logits, lse, dl, dh, h, ws, nb, None) == ALIAS
+    assert L.coda_ce_bwd(9, M, d, V, h, Wv, lab, logits, lse, dl, dh, dWv, ws, nb, None) == DTYPE

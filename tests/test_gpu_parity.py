@@ -370,3 +370,71 @@ def test_full_workload_mlp(torch_dev):
         if k != "dgamma":
             assert v <= BF16_TOL, (k, v)
     assert errs["dgamma"] <= DGAMMA_TOL
+
+
+# ------------------------------------------- LM-head GEMM with cross-entropy
+
+CE_TOL = 1e-4      # fp32 loss / lse: max|diff| / max|ref|
+
+SMALL_CE = [
+    # M, d, V, scale of h
+    (520, 264, 776, 1.0),       # ragged: V = 3 tiles + 8 columns
+    (8, 8, 8, 1.0),             # smallest accepted
+    (256, 256, 256, 1.0),       # one tile
+    (264, 136, 1000, 1.0),      # K tail, V not a multiple of the tile
+    (264, 256, 520, 8.0),       # logits ~ N(0, 64): the running max must keep exp in range
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CE, ids=lambda s: "x".join(map(str, s)))
+def test_ce_fwd_bwd(torch_dev, case):
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    M, d, V, scale = case
+    h = synth.ce_inputs(M, d, V, seed=500 + M + V)
+    if scale != 1.0:
+        h["h"] = synth.round_to_bf16(h["h"] * np.float32(scale))
+    th, tW = up(torch, dev, h["h"], "bf16"), up(torch, dev, h["Wv"], "bf16")
+    tl = torch.from_numpy(h["labels"]).to(dev)
+    td = torch.from_numpy(h["dloss"]).to(dev)
+    loss, lse, logits = coda.ce_fwd(th, tW, tl)
+    dh, dWv = coda.ce_bwd(th, tW, tl, logits, lse, td)
+    torch.cuda.synchronize()
+    f = oracle.ref_ce_fwd(h["h"], h["Wv"], h["labels"])
+    b = oracle.ref_ce_bwd(h["h"], h["Wv"], h["labels"], f["lse"], h["dloss"], oracle.bf16_rne(f["logits"]))
+    errs = {"logits": rel(host(logits), f["logits"]), "loss": rel(loss.cpu().numpy(), f["loss"]),
+            "lse": rel(lse.cpu().numpy(), f["lse"]), "dh": rel(host(dh), b["dh"]),
+            "dWv": rel(host(dWv), b["dWv"])}
+    report(f"ce {case}", errs)
+    assert errs["loss"] <= CE_TOL and errs["lse"] <= CE_TOL, errs
+    for k in ("logits", "dh", "dWv"):
+        assert errs[k] <= BF16_TOL, (k, errs[k])
+
+
+def test_full_workload_ce(torch_dev):
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    w = synth.WORKLOADS["llama7b_ce_fwdbwd"]
+    print("[parity] llama7b_ce_fwdbwd: generating inputs", flush=True)
+    h = synth.workload_inputs(w)
+    th, tW = up(torch, dev, h["h"], "bf16"), up(torch, dev, h["Wv"], "bf16")
+    tl = torch.from_numpy(h["labels"]).to(dev)
+    td = torch.from_numpy(h["dloss"]).to(dev)
+    loss, lse, logits = coda.ce_fwd(th, tW, tl)
+    dh, dWv = coda.ce_bwd(th, tW, tl, logits, lse, td)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed)
+    rows = _rows(w.M, rng, k=24)
+    cols = np.unique(np.concatenate([[0, w.N - 1], rng.choice(w.N, 16, replace=False), h["labels"][rows[:4]]]))
+    print("[parity] llama7b_ce_fwdbwd: oracle forward (full: lse needs every column of every row)", flush=True)
+    f = oracle.ref_ce_fwd(h["h"], h["Wv"], h["labels"])
+    errs = {"loss": rel(loss.cpu().numpy(), f["loss"]), "lse": rel(lse.cpu().numpy(), f["lse"]),
+            "logits_rows": rel(host(logits[rows]), f["logits"][rows])}
+    print("[parity] llama7b_ce_fwdbwd: oracle backward (sampled)", flush=True)
+    bs = oracle.ref_ce_bwd_sampled(h["h"], h["Wv"], h["labels"], f["lse"], h["dloss"], rows, cols,
+                                   logits=oracle.bf16_rne(f["logits"]))
+    errs.update({"dh_rows": rel(host(dh[rows]), bs["dh_rows"]), "dWv_cols": rel(host(dWv[:, cols]), bs["dWv_cols"])})
+    report("llama7b_ce_fwdbwd", errs)
+    assert errs["loss"] <= CE_TOL and errs["lse"] <= CE_TOL, errs
+    for k in ("logits_rows", "dh_rows", "dWv_cols"):
+        assert errs[k] <= BF16_TOL, (k, errs[k])
