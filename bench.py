@@ -11,8 +11,9 @@ autograd step on the same GPU (for the step, and for the forward and the
 backward alone), the median / min / max step time, per-kernel times from HIP
 events recorded on the stream the kernels run on, the roofline of the
 dominant kernel, the same figures for the 70B-hidden, SwiGLU, MLP sub-layer
-(the two chained) and 1B-hidden (forward only) workloads under "also", and
-the CPU oracle timed on a bounded sample of the same workload.
+(the two chained), LM-head cross-entropy and 1B-hidden (forward only)
+workloads under "also", and the CPU oracle timed on a bounded sample of the
+same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-also] [--no-cpu-baseline]
 """
@@ -40,7 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_fwdbwd")
-    ap.add_argument("--no-also", action="store_true", help="skip the 70B, SwiGLU, MLP and 1B workloads")
+    ap.add_argument("--no-also", action="store_true", help="skip the 70B, SwiGLU, MLP, cross-entropy and 1B workloads")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused torch baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
@@ -186,6 +187,51 @@ class MlpCase:
         return (self.t["dz"], self.t["dy_in"])
 
 
+class CeCase:
+    """LM-head GEMM with cross-entropy (per-row loss, saved logits and lse)."""
+
+    def __init__(self, w, torch, coda, h):
+        dev = torch.device("cuda:0")
+        self.w, self.torch, self.coda = w, torch, coda
+        self.t = {"h": torch.from_numpy(h["h"]).to(dev).to(torch.bfloat16),
+                  "Wv": torch.from_numpy(h["Wv"]).to(dev).to(torch.bfloat16),
+                  "labels": torch.from_numpy(h["labels"]).to(dev),
+                  "dloss": torch.from_numpy(h["dloss"]).to(dev)}
+        self.labels64 = self.t["labels"].long()
+        M, d, V = w.M, w.d, w.N
+        bf = torch.bfloat16
+        self.logits = torch.empty((M, V), dtype=bf, device=dev)
+        self.lse = torch.empty((M,), dtype=torch.float32, device=dev)
+        self.loss = torch.empty((M,), dtype=torch.float32, device=dev)
+        self.dh = torch.empty((M, d), dtype=bf, device=dev)
+        self.dWv = torch.empty((d, V), dtype=bf, device=dev)
+        self.wsf = torch.empty(coda.ce_fwd_workspace_bytes(1, M, d, V), dtype=torch.uint8, device=dev)
+        self.wsb = torch.empty(coda.ce_bwd_workspace_bytes(1, M, d, V), dtype=torch.uint8, device=dev)
+        self.backward = w.backward
+        self.kernels_per_step = 5
+        self.leaf_names = ("h", "Wv")
+
+    def flops(self):
+        return self.w.flops_fwd() + (self.w.flops_bwd() if self.backward else 0.0)
+
+    def fused_fwd(self):
+        t = self.t
+        self.coda.coda_ce_fwd(t["h"], t["Wv"], t["labels"], self.logits, self.lse, self.loss, self.wsf)
+
+    def fused_bwd(self):
+        t = self.t
+        self.coda.coda_ce_bwd(t["h"], t["Wv"], t["labels"], self.logits, self.lse, t["dloss"], self.dh,
+                              self.dWv, self.wsb)
+
+    def unfused_fwd(self):
+        Fn = self.torch.nn.functional
+        p = self.leaf
+        return Fn.cross_entropy(p["h"] @ p["Wv"], self.labels64, reduction="none")
+
+    def grad_outputs(self):
+        return self.t["dloss"].to(self.torch.bfloat16)
+
+
 class _Steps:
     """The fused and unfused step functions of a case: forward, backward, and
     the training step (forward + backward; the forward alone for a
@@ -233,7 +279,7 @@ class _Steps:
 def make_case(w, torch, coda):
     from gemm_epilogue_fusion_gemm1_amd import synth
     h = synth.workload_inputs(w)
-    cls = {"coda": CodaCase, "swiglu": SwigluCase, "mlp": MlpCase}[w.kind]
+    cls = {"coda": CodaCase, "swiglu": SwigluCase, "mlp": MlpCase, "ce": CeCase}[w.kind]
     return cls(w, torch, coda, h), h
 
 
@@ -450,7 +496,8 @@ def main():
 
     also = {}
     if not args.no_also:
-        for name in ("llama70b_fwdbwd", "swiglu_fwdbwd", "llama7b_mlp_fwdbwd", "llama1b_fwd"):
+        for name in ("llama70b_fwdbwd", "swiglu_fwdbwd", "llama7b_mlp_fwdbwd", "llama7b_ce_fwdbwd",
+                     "llama1b_fwd"):
             w2 = synth.WORKLOADS[name]
             print(f"[bench] {name}: inputs + timing", file=sys.stderr, flush=True)
             c2, _ = make_case(w2, torch, coda)
