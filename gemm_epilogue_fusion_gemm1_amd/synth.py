@@ -28,7 +28,8 @@ class Workload:
 
     name: str
     kind: str            # "coda" (GEMM-Residual-RMSNorm-GEMM), "swiglu", "mlp" (the two
-                         # chained) or "ce" (LM-head GEMM + cross-entropy)
+                         # chained), "ce" (LM-head GEMM + cross-entropy) or "rope"
+                         # (QKV projection with rotary positions in its epilogue)
     dtype: str           # "f32" or "bf16"
     M: int
     K: int = 0           # coda, mlp: GEMM1 reduction width
@@ -36,6 +37,10 @@ class Workload:
     N: int = 0           # coda: GEMM2 output width; ce: vocabulary size V
     F: int = 0           # swiglu, mlp: hidden width (gate and up halves)
     eps: float = 0.0
+    rot: int = 0         # rope: rotated leading columns (q and k)
+    head: int = 0        # rope: head width
+    seq: int = 0         # rope: tokens per sequence (position = row mod seq)
+    base: float = 0.0    # rope: frequency base
     seed: int = 0
     backward: bool = True
     note: str = ""
@@ -46,6 +51,8 @@ class Workload:
             return 2.0 * self.M * (self.K * self.d + self.d * self.N)
         if self.kind == "ce":
             return 2.0 * self.M * self.d * self.N
+        if self.kind == "rope":
+            return 2.0 * self.M * self.K * self.N
         swiglu = 2.0 * self.M * self.d * 2 * self.F + 2.0 * self.M * self.F * self.d
         if self.kind == "mlp":
             return 2.0 * self.M * self.K * self.d + swiglu
@@ -82,6 +89,10 @@ WORKLOADS = {
                  seed=1006, backward=True,
                  note="LLaMA-7B-shaped LM head (vocabulary 32000) with cross-entropy, "
                       "forward+backward"),
+        Workload("llama7b_qkv_rope_fwdbwd", "rope", "bf16", M=8192, K=4096, N=12288,
+                 rot=8192, head=128, seq=4096, base=10000.0, seed=1007, backward=True,
+                 note="LLaMA-7B-shaped QKV projection with rotary positions on q and k "
+                      "(two 4096-token sequences), forward+backward"),
     ]
 }
 
@@ -174,6 +185,15 @@ def ce_inputs(M: int, d: int, V: int, seed: int, dtype: str = "bf16", with_dz: b
     return out
 
 
+def rope_inputs(M: int, K: int, N: int, seed: int, dtype: str = "bf16", with_dz: bool = True) -> dict:
+    """X ~ N(0,1); W = [Wq | Wk | Wv] ~ N(0,1/K); dY ~ N(0,1)."""
+    s = np.random.SeedSequence(seed).spawn(3)
+    out = {"X": _normal(s[0], (M, K), 1.0), "W": _normal(s[1], (K, N), 1.0 / math.sqrt(K))}
+    if with_dz:
+        out["dY"] = _normal(s[2], (M, N), 1.0)
+    return {k: _quantise(v, dtype) for k, v in out.items()}
+
+
 def workload_inputs(w: Workload, with_dz: bool | None = None) -> dict:
     """Inputs of a named workload (dz only when it has a backward pass)."""
     if with_dz is None:
@@ -184,4 +204,6 @@ def workload_inputs(w: Workload, with_dz: bool | None = None) -> dict:
         return mlp_inputs(w.M, w.K, w.d, w.F, w.seed, w.dtype, with_dz)
     if w.kind == "ce":
         return ce_inputs(w.M, w.d, w.N, w.seed, w.dtype, with_dz)
+    if w.kind == "rope":
+        return rope_inputs(w.M, w.K, w.N, w.seed, w.dtype, with_dz)
     return swiglu_inputs(w.M, w.d, w.F, w.seed, w.dtype, with_dz)

@@ -53,6 +53,13 @@ What the pages fix, and the readings taken where they are silent:
     sections).  Reading: logits = h Wv; lse_i = log sum_j exp(logits_ij);
     loss_i = lse_i - logits_i,label_i (mean-free, one loss per row); the
     backward of L = sum_i dloss_i loss_i.
+  * A rotary-position epilogue on a QKV projection (``ref_rope_*``): the
+    pages list position encodings among the elementwise transforms an
+    epilogue can carry ([JA]/[RU]/[FR] primitives sections).  Reading: Y = X W,
+    then the first N_rot columns (q and k) are rotated head by head (head
+    width D) on the interleaved pairs (2i, 2i+1) by the angle p theta_i, theta_i
+    = base^(-2i/D), p = row mod S (rows are S-token sequences one after
+    another); the remaining columns (v) pass through.
 
 Every function here is pinned by a test against something other than itself
 (brute-force loops, finite differences, torch CPU autograd, closed forms and
@@ -68,6 +75,8 @@ __all__ = [
     "ref_swiglu_bwd", "ref_swiglu_fwd_rows", "ref_swiglu_bwd_sampled",
     "ref_mlp_fwd", "ref_mlp_bwd", "ref_mlp_fwd_rows", "ref_mlp_bwd_sampled",
     "ref_ce_fwd", "ref_ce_bwd", "ref_ce_partials", "ref_ce_fwd_rows", "ref_ce_bwd_sampled",
+    "rope_angles", "ref_rope_rotate", "ref_rope_fwd", "ref_rope_bwd", "ref_rope_fwd_rows",
+    "ref_rope_bwd_sampled",
 ]
 
 
@@ -547,3 +556,74 @@ def ref_ce_bwd_sampled(h, Wv, labels, lse, dloss, rows, cols_V, logits=None) -> 
     lg_cols = h @ Wv[:, cols_V] if logits is None else _f64(logits[:, cols_V])
     dlc = dlog(lg_cols, labels, lse, dloss, cols_V)
     return {"rows": rows, "cols_V": cols_V, "dh_rows": dlr @ Wv.T, "dWv_cols": h.T @ dlc}
+
+
+# ---------------------------------------------------------------------------
+# Rotary position embedding in the epilogue of a QKV projection
+# ---------------------------------------------------------------------------
+
+def rope_angles(M: int, D: int, S: int, base: float) -> np.ndarray:
+    """phi[m, i] = (m mod S) * base^(-2i/D), i = 0..D/2-1."""
+    p = (np.arange(M) % S).astype(np.float64)
+    theta = base ** (-2.0 * np.arange(D // 2, dtype=np.float64) / D)
+    return p[:, None] * theta[None, :]
+
+
+def ref_rope_rotate(Y, N_rot: int, D: int, S: int, base: float, inverse: bool = False) -> np.ndarray:
+    """Rotate the pairs (2i, 2i+1) of every D-wide head in the first N_rot
+    columns by phi[m, i] (by -phi[m, i] when ``inverse``); other columns are
+    copied."""
+    Y = _f64(Y)
+    M = Y.shape[0]
+    out = Y.copy()
+    phi = rope_angles(M, D, S, base)
+    c, sn = np.cos(phi), np.sin(phi)
+    if inverse:
+        sn = -sn
+    for h0 in range(0, N_rot, D):
+        x0 = Y[:, h0:h0 + D:2]
+        x1 = Y[:, h0 + 1:h0 + D:2]
+        out[:, h0:h0 + D:2] = x0 * c - x1 * sn
+        out[:, h0 + 1:h0 + D:2] = x0 * sn + x1 * c
+    return out
+
+
+def ref_rope_fwd(X, W, N_rot: int, D: int, S: int, base: float) -> dict:
+    """Y = rope(X W): the projection, then the rotation of its first N_rot
+    columns ([JA]/[RU]/[FR] primitives sections: elementwise transforms in
+    the epilogue)."""
+    P = _f64(X) @ _f64(W)
+    return {"P": P, "Y": ref_rope_rotate(P, N_rot, D, S, base)}
+
+
+def ref_rope_bwd(X, W, dY, N_rot: int, D: int, S: int, base: float) -> dict:
+    """Exact gradient of L = <dY, Y>: the rotation is orthogonal, so
+    dP = rotate(dY, -phi) on the rotated columns (dY elsewhere);
+    dX = dP W^T;  dW = X^T dP."""
+    X, W = _f64(X), _f64(W)
+    dP = ref_rope_rotate(dY, N_rot, D, S, base, inverse=True)
+    return {"dP": dP, "dX": dP @ W.T, "dW": X.T @ dP}
+
+
+def ref_rope_fwd_rows(X, W, N_rot: int, D: int, S: int, base: float, rows) -> dict:
+    """``ref_rope_fwd`` for the given rows (their positions kept)."""
+    rows = np.asarray(rows)
+    P = _f64(X[rows]) @ _f64(W)
+    M_all = int(np.max(rows)) + 1
+    phi_all = rope_angles(M_all, D, S, base)[rows]
+    c, sn = np.cos(phi_all), np.sin(phi_all)
+    Y = P.copy()
+    for h0 in range(0, N_rot, D):
+        x0, x1 = P[:, h0:h0 + D:2], P[:, h0 + 1:h0 + D:2]
+        Y[:, h0:h0 + D:2] = x0 * c - x1 * sn
+        Y[:, h0 + 1:h0 + D:2] = x0 * sn + x1 * c
+    return {"rows": rows, "P": P, "Y": Y}
+
+
+def ref_rope_bwd_sampled(X, W, dY, N_rot: int, D: int, S: int, base: float, rows, cols_N) -> dict:
+    """``ref_rope_bwd`` with dX restricted to ``rows`` and dW to the columns
+    ``cols_N`` (dP is row-local, so it is formed whole)."""
+    X, W = _f64(X), _f64(W)
+    dP = ref_rope_rotate(dY, N_rot, D, S, base, inverse=True)
+    rows, cols_N = np.asarray(rows), np.asarray(cols_N)
+    return {"rows": rows, "cols_N": cols_N, "dX_rows": dP[rows] @ W.T, "dW_cols": X.T @ dP[:, cols_N]}

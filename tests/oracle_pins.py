@@ -649,6 +649,118 @@ def pin_ce_sampled(O):
         _close(bs["dWv_cols"], b["dWv"][:, cols], 1e-13, "ce sampled dWv")
 
 
+# ------------------------------------------------------------------- RoPE pins
+
+def _rope_case(seed, M, K, N, N_rot, D, S, base=10000.0):
+    g = _rng(seed)
+    return dict(X=g.standard_normal((M, K)), W=g.standard_normal((K, N)) / math.sqrt(K),
+                dY=g.standard_normal((M, N)), N_rot=N_rot, D=D, S=S, base=base)
+
+
+def _rope_args(c):
+    return (c["N_rot"], c["D"], c["S"], c["base"])
+
+
+def pin_rope_bruteforce(O):
+    """Pure-Python loops: P = X W, then for rotated head columns
+    y_2i = p_2i cos - p_2i+1 sin, y_2i+1 = p_2i sin + p_2i+1 cos with the angle
+    (m mod S) base^(-2i/D); other columns unchanged."""
+    c = _rope_case(71, 5, 3, 14, 8, 4, 3, base=100.0)
+    X, W = c["X"], c["W"]
+    f = O.ref_rope_fwd(X, W, *_rope_args(c))
+    for m in range(5):
+        P = [sum(X[m][k] * W[k][j] for k in range(3)) for j in range(14)]
+        want = list(P)
+        for h0 in range(0, 8, 4):
+            for i in range(2):
+                ang = (m % 3) * 100.0 ** (-2.0 * i / 4)
+                a, b = P[h0 + 2 * i], P[h0 + 2 * i + 1]
+                want[h0 + 2 * i] = a * math.cos(ang) - b * math.sin(ang)
+                want[h0 + 2 * i + 1] = a * math.sin(ang) + b * math.cos(ang)
+        _close(f["Y"][m], want, 1e-13, f"rope brute force row {m}")
+
+
+def pin_rope_torch(O):
+    """torch CPU float64 complex form: pairs as complex numbers times
+    polar(1, angle) (torch.polar, view_as_complex), with autograd of <dY, Y>."""
+    import torch
+    c = _rope_case(72, 12, 16, 40, 32, 8, 5)
+    N_rot, D, S, base = _rope_args(c)
+    tX = torch.tensor(c["X"], requires_grad=True)
+    tW = torch.tensor(c["W"], requires_grad=True)
+    P = tX @ tW
+    pos = (torch.arange(12) % S).double()
+    theta = base ** (-torch.arange(0, D, 2, dtype=torch.float64) / D)
+    rot = torch.polar(torch.ones(12, D // 2, dtype=torch.float64), pos[:, None] * theta[None, :])
+    q = torch.view_as_complex(P[:, :N_rot].reshape(12, N_rot // D, D // 2, 2).contiguous())
+    qr = torch.view_as_real(q * rot[:, None, :]).reshape(12, N_rot)
+    Y = torch.cat([qr, P[:, N_rot:]], dim=1)
+    (Y * torch.from_numpy(c["dY"])).sum().backward()
+    f = O.ref_rope_fwd(c["X"], c["W"], N_rot, D, S, base)
+    _close(f["Y"], Y.detach().numpy(), 1e-13, "rope Y vs torch")
+    b = O.ref_rope_bwd(c["X"], c["W"], c["dY"], N_rot, D, S, base)
+    _close(b["dX"], tX.grad.numpy(), 1e-12, "rope dX vs torch")
+    _close(b["dW"], tW.grad.numpy(), 1e-12, "rope dW vs torch")
+
+
+def pin_rope_finite_differences(O):
+    c = _rope_case(73, 3, 4, 10, 8, 4, 2)
+    args = _rope_args(c)
+    b = O.ref_rope_bwd(c["X"], c["W"], c["dY"], *args)
+
+    def L(X, W):
+        return float(np.sum(c["dY"] * O.ref_rope_fwd(X, W, *args)["Y"]))
+    for name, grad in (("X", b["dX"]), ("W", b["dW"])):
+        base_ = c[name]
+        fd = np.zeros_like(base_)
+        for idx in np.ndindex(base_.shape):
+            hstep = 1e-6 * max(1.0, abs(base_[idx]))
+            arr = base_.copy(); arr[idx] += hstep
+            lp = L(arr, c["W"]) if name == "X" else L(c["X"], arr)
+            arr = base_.copy(); arr[idx] -= hstep
+            lm = L(arr, c["W"]) if name == "X" else L(c["X"], arr)
+            fd[idx] = (lp - lm) / (2 * hstep)
+        _close(grad, fd, 1e-7, f"rope d{name} vs finite differences")
+
+
+def pin_rope_properties(O):
+    """Rows at position 0 are left unchanged; the rotation keeps every pair's
+    length; the inverse undoes it; unrotated columns pass through; and the
+    relative-position property: <rot(q, m), rot(k, n)> over a head depends only
+    on m - n (rows of equal content at positions (1, 4) and (3, 6))."""
+    g = _rng(74)
+    N_rot, D, S, base = 16, 8, 7, 10000.0
+    Y = g.standard_normal((14, 20))
+    R = O.ref_rope_rotate(Y, N_rot, D, S, base)
+    _close(R[0], Y[0], 0.0, "position 0")
+    _close(R[7], Y[7], 0.0, "position 0 of the second sequence")
+    _close(R[:, N_rot:], Y[:, N_rot:], 0.0, "unrotated columns")
+    _close(R[:, 0:N_rot:2] ** 2 + R[:, 1:N_rot:2] ** 2, Y[:, 0:N_rot:2] ** 2 + Y[:, 1:N_rot:2] ** 2,
+           1e-13, "pair lengths")
+    _close(O.ref_rope_rotate(R, N_rot, D, S, base, inverse=True), Y, 1e-13, "inverse")
+    q, k = g.standard_normal(20), g.standard_normal(20)
+    Z = np.zeros((7, 20))
+    Z[1], Z[3], Z[4], Z[6] = q, q, k, k
+    RZ = O.ref_rope_rotate(Z, N_rot, D, S, base)
+    for h0 in range(0, N_rot, D):
+        a = float(np.dot(RZ[1, h0:h0 + D], RZ[4, h0:h0 + D]))
+        b = float(np.dot(RZ[3, h0:h0 + D], RZ[6, h0:h0 + D]))
+        _close(a, b, 1e-13, "relative position")
+
+
+def pin_rope_sampled(O):
+    c = _rope_case(75, 20, 6, 24, 16, 8, 6)
+    args = _rope_args(c)
+    f = O.ref_rope_fwd(c["X"], c["W"], *args)
+    rows, cols = np.array([0, 5, 6, 13, 19]), np.array([0, 1, 7, 15, 16, 23])
+    fr = O.ref_rope_fwd_rows(c["X"], c["W"], *args, rows)
+    _close(fr["Y"], f["Y"][rows], 1e-14, "rope rows Y")
+    b = O.ref_rope_bwd(c["X"], c["W"], c["dY"], *args)
+    bs = O.ref_rope_bwd_sampled(c["X"], c["W"], c["dY"], *args, rows, cols)
+    _close(bs["dX_rows"], b["dX"][rows], 1e-13, "rope sampled dX")
+    _close(bs["dW_cols"], b["dW"][:, cols], 1e-13, "rope sampled dW")
+
+
 def pin_bwd_dy_in_finite_differences(O):
     """``ref_bwd`` with dy_in: central differences of <dz, z> + <dy_in, y> for
     the block's own forward, tiny shape."""
@@ -711,5 +823,7 @@ ALL_PINS = [
     pin_mlp_torch, pin_mlp_invariants, pin_mlp_sampled, pin_mlp_dgu_rounding,
     pin_mlp_stored_operand_bruteforce, pin_ce_torch, pin_ce_finite_differences,
     pin_ce_closed_forms, pin_ce_invariants, pin_ce_partials, pin_ce_sampled,
+    pin_rope_bruteforce, pin_rope_torch, pin_rope_finite_differences, pin_rope_properties,
+    pin_rope_sampled,
     pin_bwd_dy_in_finite_differences,
 ]

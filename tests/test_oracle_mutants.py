@@ -191,6 +191,57 @@ def ce_partials_no_rescale(logits, BN=256):
     return out
 
 
+def _rope_rotate_variant(kind):
+    def rot(Y, N_rot, D, S, base, inverse=False):
+        Y = np.asarray(Y, dtype=np.float64)
+        M = Y.shape[0]
+        out = Y.copy()
+        p = np.arange(M) if kind == "no_wrap" else np.arange(M) % S
+        ex = -1.0 if kind == "half_exponent" else -2.0
+        theta = base ** (ex * np.arange(D // 2) / D)
+        phi = p[:, None] * theta[None, :]
+        c, sn = np.cos(phi), np.sin(phi)
+        if inverse != (kind == "sin_sign"):
+            sn = -sn
+        last = Y.shape[1] if kind == "rotate_v" else N_rot
+        for h0 in range(0, last - last % D, D):
+            if kind == "half_split":
+                i0, i1 = slice(h0, h0 + D // 2), slice(h0 + D // 2, h0 + D)
+            else:
+                i0, i1 = slice(h0, h0 + D, 2), slice(h0 + 1, h0 + D, 2)
+            x0, x1 = Y[:, i0], Y[:, i1]
+            out[:, i0] = x0 * c - x1 * sn
+            out[:, i1] = x0 * sn + x1 * c
+        return out
+    return rot
+
+
+def _rope_mutant(kind):
+    """A mistake in the rotation reaches everything built on it."""
+    rot = _rope_rotate_variant(kind)
+
+    def fwd(X, W, N_rot, D, S, base):
+        P = np.asarray(X, dtype=np.float64) @ np.asarray(W, dtype=np.float64)
+        return {"P": P, "Y": rot(P, N_rot, D, S, base)}
+
+    def bwd(X, W, dY, N_rot, D, S, base):
+        X, W = _f(X, W)
+        dP = rot(dY, N_rot, D, S, base, inverse=True)
+        return {"dP": dP, "dX": dP @ W.T, "dW": X.T @ dP}
+
+    def fwd_rows(X, W, N_rot, D, S, base, rows):
+        rows = np.asarray(rows)
+        full = fwd(X, W, N_rot, D, S, base)
+        return {"rows": rows, "P": full["P"][rows], "Y": full["Y"][rows]}
+    return {"ref_rope_rotate": rot, "ref_rope_fwd": fwd, "ref_rope_bwd": bwd, "ref_rope_fwd_rows": fwd_rows}
+
+
+def rope_bwd_forward_rotation(X, W, dY, N_rot, D, S, base):
+    X, W = _f(X, W)
+    dP = oracle.ref_rope_rotate(dY, N_rot, D, S, base, inverse=False)
+    return {"dP": dP, "dX": dP @ W.T, "dW": X.T @ dP}
+
+
 def bf16_half_away(x):
     x = np.asarray(x, dtype=np.float64)
     out = np.array(x, copy=True)
@@ -231,6 +282,12 @@ MUTANTS = {
     "ce_bwd_no_onehot": {"ref_ce_bwd": _ce_bwd_variant("no_onehot")},
     "ce_bwd_no_dloss": {"ref_ce_bwd": _ce_bwd_variant("no_dloss")},
     "ce_partials_no_rescale": {"ref_ce_partials": ce_partials_no_rescale},
+    "rope_half_split_pairs": _rope_mutant("half_split"),
+    "rope_sin_sign": _rope_mutant("sin_sign"),
+    "rope_position_not_wrapped": _rope_mutant("no_wrap"),
+    "rope_half_exponent": _rope_mutant("half_exponent"),
+    "rope_rotates_v": _rope_mutant("rotate_v"),
+    "rope_bwd_forward_rotation": {"ref_rope_bwd": rope_bwd_forward_rotation},
     "mlp_bwd_drops_dy_in": {"ref_mlp_bwd": _mlp_bwd_variant("drop_dy_in")},
     "mlp_bwd_dy_in_sign": {"ref_mlp_bwd": _mlp_bwd_variant("dy_in_sign")},
     "mlp_bwd_dW_without_r": {"ref_mlp_bwd": _mlp_bwd_variant("dW_without_r")},
