@@ -10,7 +10,7 @@ PyTorch fallback: without the built library every call raises.
 Low-level calls (same names and argument order as the C functions, outputs
 preallocated by the caller):
     coda_fwd, coda_bwd, coda_swiglu_fwd, coda_swiglu_bwd, coda_mlp_fwd, coda_mlp_bwd,
-    coda_ce_fwd, coda_ce_bwd
+    coda_ce_fwd, coda_ce_bwd, coda_rope_fwd, coda_rope_bwd
 Convenience calls (allocate outputs):
     fwd(X, W1, R, gamma, W2, eps)        -> (z, y, r)
     bwd(X, W1, gamma, W2, y, r, dz)      -> (dX, dW1, dR, dW2, dgamma)
@@ -21,6 +21,8 @@ Convenience calls (allocate outputs):
                                          -> (dX, dW1, dR, dW, dWd, dgamma)
     ce_fwd(h, Wv, labels)                -> (loss, lse, logits)
     ce_bwd(h, Wv, labels, logits, lse, dloss) -> (dh, dWv)
+    rope_fwd(X, W, N_rot, D, S, base)    -> Y
+    rope_bwd(X, W, dY, N_rot, D, S, base) -> (dX, dW)
 """
 from __future__ import annotations
 
@@ -31,7 +33,8 @@ __all__ = [
     "CodaError", "lib_path", "load_library", "coda_fwd", "coda_bwd", "coda_swiglu_fwd",
     "coda_swiglu_bwd", "coda_mlp_fwd", "coda_mlp_bwd", "fwd", "bwd", "swiglu_fwd",
     "swiglu_bwd", "mlp_fwd", "mlp_bwd", "coda_ce_fwd", "coda_ce_bwd", "ce_fwd", "ce_bwd",
-    "ce_fwd_workspace_bytes", "ce_bwd_workspace_bytes", "fwd_workspace_bytes", "bwd_workspace_bytes",
+    "ce_fwd_workspace_bytes", "ce_bwd_workspace_bytes", "coda_rope_fwd", "coda_rope_bwd", "rope_fwd",
+    "rope_bwd", "rope_fwd_workspace_bytes", "rope_bwd_workspace_bytes", "fwd_workspace_bytes", "bwd_workspace_bytes",
     "swiglu_bwd_workspace_bytes", "mlp_fwd_workspace_bytes", "mlp_bwd_workspace_bytes",
     "version", "trace_start", "trace_read", "trace_stop",
 ]
@@ -82,6 +85,8 @@ def load_library() -> ctypes.CDLL:
         "coda_mlp_bwd_workspace_bytes": [i32, i64, i64, i64, i64],
         "coda_ce_fwd_workspace_bytes": [i32, i64, i64, i64],
         "coda_ce_bwd_workspace_bytes": [i32, i64, i64, i64],
+        "coda_rope_fwd_workspace_bytes": [i32, i64, i64, i64, i64, i64, i64],
+        "coda_rope_bwd_workspace_bytes": [i32, i64, i64, i64, i64, i64, i64],
     }.items():
         getattr(L, name).restype = sz
         getattr(L, name).argtypes = args
@@ -101,6 +106,10 @@ def load_library() -> ctypes.CDLL:
     L.coda_ce_fwd.argtypes = [i32, i64, i64, i64] + [vp] * 6 + [vp, sz, vp]
     L.coda_ce_bwd.restype = i32
     L.coda_ce_bwd.argtypes = [i32, i64, i64, i64] + [vp] * 8 + [vp, sz, vp]
+    L.coda_rope_fwd.restype = i32
+    L.coda_rope_fwd.argtypes = [i32, i64, i64, i64, i64, i64, i64, f32] + [vp] * 3 + [vp, sz, vp]
+    L.coda_rope_bwd.restype = i32
+    L.coda_rope_bwd.argtypes = [i32, i64, i64, i64, i64, i64, i64, f32] + [vp] * 5 + [vp, sz, vp]
     L.coda_trace_start.restype = i32
     L.coda_trace_start.argtypes = [i32]
     L.coda_trace_count.restype = i32
@@ -186,6 +195,14 @@ def ce_fwd_workspace_bytes(dtype_code, M, d, V) -> int:
 
 def ce_bwd_workspace_bytes(dtype_code, M, d, V) -> int:
     return int(load_library().coda_ce_bwd_workspace_bytes(dtype_code, M, d, V))
+
+
+def rope_fwd_workspace_bytes(dtype_code, M, K, N, N_rot, D, S) -> int:
+    return int(load_library().coda_rope_fwd_workspace_bytes(dtype_code, M, K, N, N_rot, D, S))
+
+
+def rope_bwd_workspace_bytes(dtype_code, M, K, N, N_rot, D, S) -> int:
+    return int(load_library().coda_rope_bwd_workspace_bytes(dtype_code, M, K, N, N_rot, D, S))
 
 
 # ------------------------------------------------------------ tracing
@@ -299,6 +316,24 @@ def coda_ce_bwd(h, Wv, labels, logits, lse, dloss, dh, dWv, workspace):
     _check("coda_ce_bwd", L.coda_ce_bwd(
         _dtype_code(h), M, d, V, _ptr(h), _ptr(Wv), _labels(labels), _ptr(logits), _ptr(lse), _ptr(dloss),
         _ptr(dh), _ptr(dWv), _ptr(workspace), workspace.numel(), _stream()))
+
+
+def coda_rope_fwd(X, W, N_rot, D, S, base, Y, workspace):
+    L = load_library()
+    M, K = X.shape
+    N = W.shape[1]
+    _check("coda_rope_fwd", L.coda_rope_fwd(
+        _dtype_code(X), M, K, N, N_rot, D, S, float(base), _ptr(X), _ptr(W), _ptr(Y), _ptr(workspace),
+        workspace.numel(), _stream()))
+
+
+def coda_rope_bwd(X, W, dY, N_rot, D, S, base, dX, dW, workspace):
+    L = load_library()
+    M, K = X.shape
+    N = W.shape[1]
+    _check("coda_rope_bwd", L.coda_rope_bwd(
+        _dtype_code(X), M, K, N, N_rot, D, S, float(base), _ptr(X), _ptr(W), _ptr(dY), _ptr(dX), _ptr(dW),
+        _ptr(workspace), workspace.numel(), _stream()))
 
 
 # ------------------------------------------------------ convenience calls
@@ -428,3 +463,29 @@ def ce_bwd(h, Wv, labels, logits, lse, dloss):
     ws = _workspace(ce_bwd_workspace_bytes(_dtype_code(h), M, d, V), h.device)
     coda_ce_bwd(h, Wv, labels, logits, lse, dloss, dh, dWv, ws)
     return dh, dWv
+
+
+def rope_fwd(X, W, N_rot, D, S, base=10000.0):
+    """Y = X W with rotary positions on the first N_rot columns (interleaved
+    pairs per D-wide head, position = row mod S)."""
+    import torch
+    M, K = X.shape
+    N = W.shape[1]
+    _shape(W, K, N, name="W")
+    Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    ws = _workspace(rope_fwd_workspace_bytes(_dtype_code(X), M, K, N, N_rot, D, S), X.device)
+    coda_rope_fwd(X, W, N_rot, D, S, base, Y, ws)
+    return Y
+
+
+def rope_bwd(X, W, dY, N_rot, D, S, base=10000.0):
+    """Gradients of <dY, Y>.  Returns (dX, dW)."""
+    import torch
+    M, K = X.shape
+    N = W.shape[1]
+    _shape(dY, M, N, name="dY")
+    dX = torch.empty_like(X)
+    dW = torch.empty_like(W)
+    ws = _workspace(rope_bwd_workspace_bytes(_dtype_code(X), M, K, N, N_rot, D, S), X.device)
+    coda_rope_bwd(X, W, dY, N_rot, D, S, base, dX, dW, ws)
+    return dX, dW

@@ -749,4 +749,119 @@ coda_status coda_ce_bwd(coda_dtype dtype, int64_t M, int64_t d, int64_t V, const
   }));
 }
 
+// --------------------------------------- QKV projection with rotary positions
+
+namespace {
+bool rope_args_ok(int64_t N, int64_t N_rot, int64_t D, int64_t S, float base) {
+  return D >= 8 && D % 8 == 0 && D <= 4096 && N_rot >= 0 && N_rot <= N && N_rot % D == 0 && S >= 1 &&
+         S <= (int64_t)1 << 24 && std::isfinite(base) && base > 0.0f;
+}
+size_t rope_table_bytes(int64_t D, int64_t S) { return round_up((size_t)S * (size_t)D * 4); }
+}  // namespace
+
+size_t coda_rope_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t N,
+                                     int64_t N_rot, int64_t D, int64_t S) {
+  (void)M;
+  (void)K;
+  (void)N;
+  (void)N_rot;
+  if (dtype != CODA_BF16 || D < 1 || S < 1) return 0;
+  return rope_table_bytes(D, S);
+}
+
+coda_status coda_rope_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t N, int64_t N_rot,
+                          int64_t D, int64_t S, float base, const void* X, const void* W, void* Y,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
+  if (!X || !W || !Y) return CODA_ERR_NULL;
+  if (!dim_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, N)) return CODA_ERR_SHAPE;
+  if (!bytes_ok(dtype, M, K) || !bytes_ok(dtype, K, N) || !bytes_ok(dtype, M, N))
+    return CODA_ERR_SHAPE;
+  if (!rope_args_ok(N, N_rot, D, S, base)) return CODA_ERR_SHAPE;
+  if (dtype != CODA_BF16) return CODA_ERR_UNSUPPORTED;
+  for (const void* p : {X, W, (const void*)Y})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  const size_t tb = rope_table_bytes(D, S);
+  if (!workspace || workspace_bytes < tb) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const size_t e = 2;
+  const Range in[] = {rng(X, M * K * e), rng(W, K * N * e)};
+  const Range out[] = {rng(Y, M * N * e), rng(workspace, tb)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  float* tab = (float*)workspace;
+  hipError_t err;
+  if ((err = traced("q0_rope_table", 0.0, (double)S * D * 4.0, s, [&] {
+         return coda::launch_rope_table(tab, (int)S, (int)D, (double)base, s);
+       })) != hipSuccess)
+    return hip_status(err);
+  // Q1: Y = rope(X W), the rotation in the epilogue
+  GemmArgs q1 = gemm(M, N, K, X, K, M * K, W, N, K * N, Y, N);
+  q1.rope_tab = tab;
+  q1.rope_rot = (int)N_rot;
+  q1.rope_head = (int)D;
+  q1.rope_seq = (int)S;
+  const double mk = 2.0 * M * K, kn = 2.0 * K * N, mn = 2.0 * M * N;
+  return hip_status(traced("q1_gemm_qkv_rope", gemm_flops(M, N, K), mk + kn + mn + (double)S * D * 4.0, s,
+                           [&] { return coda::launch_gemm_bf16(q1, true, false, coda::EPI_ROPE, s); }));
+}
+
+size_t coda_rope_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t N,
+                                     int64_t N_rot, int64_t D, int64_t S) {
+  (void)K;
+  (void)N_rot;
+  if (dtype != CODA_BF16 || M < 1 || N < 1 || D < 1 || S < 1) return 0;
+  return rope_table_bytes(D, S) + round_up((size_t)M * N * 2);
+}
+
+coda_status coda_rope_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t N, int64_t N_rot,
+                          int64_t D, int64_t S, float base, const void* X, const void* W,
+                          const void* dY, void* dX, void* dW, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
+  if (!X || !W || !dY || !dX || !dW) return CODA_ERR_NULL;
+  if (!dim_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, N)) return CODA_ERR_SHAPE;
+  if (!bytes_ok(dtype, M, K) || !bytes_ok(dtype, K, N) || !bytes_ok(dtype, M, N))
+    return CODA_ERR_SHAPE;
+  if (!rope_args_ok(N, N_rot, D, S, base)) return CODA_ERR_SHAPE;
+  if (dtype != CODA_BF16) return CODA_ERR_UNSUPPORTED;
+  for (const void* p : {X, W, dY, (const void*)dX, (const void*)dW})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  const size_t tb = rope_table_bytes(D, S);
+  const size_t need = tb + round_up((size_t)M * N * 2);
+  if (!workspace || workspace_bytes < need) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const size_t e = 2;
+  const Range in[] = {rng(X, M * K * e), rng(W, K * N * e), rng(dY, M * N * e)};
+  const Range out[] = {rng(dX, M * K * e), rng(dW, K * N * e), rng(workspace, need)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  float* tab = (float*)workspace;
+  void* dP = (char*)workspace + tb;
+  hipError_t err;
+  const double mk = 2.0 * M * K, kn = 2.0 * K * N, mn = 2.0 * M * N;
+  if ((err = traced("q2_rope_table", 0.0, (double)S * D * 4.0, s, [&] {
+         return coda::launch_rope_table(tab, (int)S, (int)D, (double)base, s);
+       })) != hipSuccess)
+    return hip_status(err);
+  // Q3: dP = the transposed rotation of dY
+  if ((err = traced("q3_rope_inverse", 0.0, 2.0 * mn + (double)S * D * 4.0, s, [&] {
+         return coda::launch_rope_inverse(dY, tab, dP, M, N, (int)N_rot, (int)D, (int)S, s);
+       })) != hipSuccess)
+    return hip_status(err);
+  // Q4: dX = dP W^T
+  GemmArgs q4 = gemm(M, K, N, dP, N, M * N, W, N, K * N, dX, K);
+  if ((err = traced("q4_gemm_dX", gemm_flops(M, K, N), mn + kn + mk, s, [&] {
+         return coda::launch_gemm_bf16(q4, true, true, coda::EPI_STORE, s);
+       })) != hipSuccess)
+    return hip_status(err);
+  // Q5: dW = X^T dP
+  GemmArgs q5 = gemm(K, N, M, X, K, M * K, dP, N, M * N, dW, N);
+  return hip_status(traced("q5_gemm_dW", gemm_flops(K, N, M), mk + mn + kn, s, [&] {
+    return coda::launch_gemm_bf16(q5, false, false, coda::EPI_STORE, s);
+  }));
+}
+
 }  // extern "C"

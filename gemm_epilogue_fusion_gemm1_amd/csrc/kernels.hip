@@ -510,7 +510,7 @@ gemm_bf16_kernel(GemmArgs g) {
 
   if constexpr (EPI == EPI_STORE || EPI == EPI_ROWSCALE || EPI == EPI_RESID_SUMSQ ||
                 EPI == EPI_DN || EPI == EPI_SWIGLU_BWD || EPI == EPI_RSQRT_SCALE ||
-                EPI == EPI_CE_STATS) {
+                EPI == EPI_CE_STATS || EPI == EPI_ROPE) {
     __bf16* C = (__bf16*)g.C;
     f32x4 glo{}, ghi{}, clo{0.f, 0.f, 0.f, 0.f}, chi{0.f, 0.f, 0.f, 0.f};
     if constexpr (EPI == EPI_DN || EPI == EPI_RESID_SUMSQ) {
@@ -532,6 +532,29 @@ gemm_bf16_kernel(GemmArgs g) {
         const int64_t o = (int64_t)row * g.ldc + gcol;
         if constexpr (EPI == EPI_STORE) {
           if (ok) st8(C + o, lo, hi);
+        } else if constexpr (EPI == EPI_ROPE) {
+          // the lane's 8 columns are 4 pairs of one head (the head width is a
+          // multiple of 8); cos and sin of their angles from the table
+          if (ok) {
+            if (gcol < g.rope_rot) {
+              const int hd = g.rope_head >> 1;
+              const int64_t ti = (int64_t)(row % g.rope_seq) * hd + ((gcol % g.rope_head) >> 1);
+              const f32x4 cs = *(const f32x4*)(g.rope_tab + ti);
+              const f32x4 sn = *(const f32x4*)(g.rope_tab + (int64_t)g.rope_seq * hd + ti);
+              f32x4 rlo, rhi;
+              rlo[0] = lo[0] * cs[0] - lo[1] * sn[0];
+              rlo[1] = lo[0] * sn[0] + lo[1] * cs[0];
+              rlo[2] = lo[2] * cs[1] - lo[3] * sn[1];
+              rlo[3] = lo[2] * sn[1] + lo[3] * cs[1];
+              rhi[0] = hi[0] * cs[2] - hi[1] * sn[2];
+              rhi[1] = hi[0] * sn[2] + hi[1] * cs[2];
+              rhi[2] = hi[2] * cs[3] - hi[3] * sn[3];
+              rhi[3] = hi[2] * sn[3] + hi[3] * cs[3];
+              st8(C + o, rlo, rhi);
+            } else {
+              st8(C + o, lo, hi);
+            }
+          }
         } else if constexpr (EPI == EPI_ROWSCALE) {
           if (ok) {
             const float sc = g.vrow ? g.vrow[row] : bf2f(((const __bf16*)g.vcol)[row]);
@@ -930,6 +953,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStr
       case EPI_STORE: return launch_one<true, false, EPI_STORE>(g, s);
       case EPI_RESID_SUMSQ: return launch_one<true, false, EPI_RESID_SUMSQ>(g, s);
       case EPI_CE_STATS: return launch_one<true, false, EPI_CE_STATS>(g, s);
+      case EPI_ROPE: return launch_one<true, false, EPI_ROPE>(g, s);
       case EPI_SWIGLU: return launch_one<true, false, EPI_SWIGLU>(g, s);
       default: break;
     }
@@ -974,6 +998,58 @@ hipError_t launch_row_rsqrt(const float* P, int64_t ldp, int T, int64_t M, int64
                             float* r, hipStream_t s) {
   hipLaunchKernelGGL(row_rsqrt_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, P, ldp,
                      T, M, 1.0f / (float)d, eps, r);
+  return hipGetLastError();
+}
+
+__global__ void rope_table_kernel(float* __restrict__ tab, int S, int D, double base) {
+  const int hd = D / 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)S * hd) return;
+  const int p = (int)(idx / hd), i = (int)(idx % hd);
+  const double ang = (double)p * pow(base, -2.0 * (double)i / (double)D);
+  tab[idx] = (float)cos(ang);
+  tab[(int64_t)S * hd + idx] = (float)sin(ang);
+}
+
+__global__ void rope_inverse_kernel(const __bf16* __restrict__ dY, const float* __restrict__ tab,
+                                    __bf16* __restrict__ dP, int64_t M, int64_t N, int N_rot, int D,
+                                    int S) {
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t e0 = v * 8;
+  if (e0 >= M * N) return;
+  const int64_t m = e0 / N;
+  const int64_t c0 = e0 - m * N;
+  const bf16x8 x = *(const bf16x8*)(dY + e0);
+  if (c0 >= N_rot) {
+    *(bf16x8*)(dP + e0) = x;
+    return;
+  }
+  const int hd = D >> 1;
+  const int64_t ti = (int64_t)(m % S) * hd + ((c0 % D) >> 1);
+  const f32x4 cs = *(const f32x4*)(tab + ti);
+  const f32x4 sn = *(const f32x4*)(tab + (int64_t)S * hd + ti);
+  bf16x8 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = bf2f(x[2 * k]), b = bf2f(x[2 * k + 1]);
+    o[2 * k] = f2bf(a * cs[k] + b * sn[k]);
+    o[2 * k + 1] = f2bf(-a * sn[k] + b * cs[k]);
+  }
+  *(bf16x8*)(dP + e0) = o;
+}
+
+hipError_t launch_rope_table(float* tab, int S, int D, double base, hipStream_t s) {
+  const int64_t n = (int64_t)S * (D / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, tab, S, D,
+                     base);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_inverse(const void* dY, const float* tab, void* dP, int64_t M, int64_t N,
+                               int N_rot, int D, int S, hipStream_t s) {
+  const int64_t chunks = (M * N) / 8;
+  hipLaunchKernelGGL(rope_inverse_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
+                     (const __bf16*)dY, tab, (__bf16*)dP, M, N, N_rot, D, S);
   return hipGetLastError();
 }
 

@@ -31,6 +31,9 @@ enum Epi : int {
   EPI_CE_STATS = 8,      // logits: C = acc; per row and tile: part_row = max_j acc,
                          // part_col = sum_j exp(acc - max) ([M][tiles_n] each, ld_part_row);
                          // lab_out[i] = acc[i][labels[i]] (written by the tile holding it)
+  EPI_ROPE = 9,          // C = acc with the pairs (2i, 2i+1) of every rope_head-wide head in
+                         // the first rope_rot columns rotated by the table's angle for
+                         // position (row mod rope_seq)
 };
 
 // Operand layouts.  "K-major" = the contraction index is contiguous in memory.
@@ -49,6 +52,8 @@ struct GemmArgs {
   int nparts; float inv_d; float eps; float* r_out;   // EPI_RSQRT_SCALE
   int c2_trans;                  // EPI_RESID_SUMSQ: C2 stored transposed
   const int* labels; float* lab_out;   // EPI_CE_STATS
+  const float* rope_tab; int rope_rot, rope_head, rope_seq;   // EPI_ROPE: tab = [cos | sin],
+                                                               // each [rope_seq][rope_head / 2]
   uint32_t A_bytes, B_bytes;     // buffer extents for hardware bounds checks
 };
 
@@ -66,6 +71,13 @@ hipError_t launch_row_rsqrt(const float* P, int64_t ldp, int T, int64_t M, int64
 hipError_t launch_bwd_reduce(const float* S, int64_t lds, int Tn, const float* r, int64_t M,
                              int64_t d, const float* G, int Tm, float* c, float* dgamma,
                              hipStream_t stream);
+// tab[p][i] = cos(p base^(-2i/D)), tab[S*D/2 + p*D/2 + i] = sin(...), computed in
+// double and stored as float; p < S, i < D/2
+hipError_t launch_rope_table(float* tab, int S, int D, double base, hipStream_t stream);
+// dP = the pairs of dY's first N_rot columns rotated back by -angle (the
+// transpose of the forward rotation); the other columns copied (bf16)
+hipError_t launch_rope_inverse(const void* dY, const float* tab, void* dP, int64_t M, int64_t N,
+                               int N_rot, int D, int S, hipStream_t stream);
 // lse[i] = m + log s over the tiles' (max, sum-exp) pairs combined in order;
 // loss[i] = lse[i] - lab[i]
 hipError_t launch_ce_combine(const float* pmax, const float* psum, int64_t ldp, int T,

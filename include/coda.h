@@ -263,6 +263,46 @@ coda_status coda_ce_bwd(coda_dtype dtype, int64_t M, int64_t d, int64_t V, const
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * QKV projection with rotary positions in its epilogue.  The pages list
+ * position encodings among the elementwise transforms an epilogue carries
+ * ([JA] 組み合わせ可能な5種類の「積み木」, [RU] "Пять «кирпичиков»", [FR]
+ * "Cinq « blocs »"):
+ *   P = X W;  for each D-wide head in the first N_rot columns (q and k) and
+ *   i < D/2, with phi = (row mod S) * base^(-2i/D):
+ *     Y[:, 2i] = P[:, 2i] cos phi - P[:, 2i+1] sin phi
+ *     Y[:, 2i+1] = P[:, 2i] sin phi + P[:, 2i+1] cos phi
+ *   the remaining columns (v) are copied.  Rows are S-token sequences one
+ *   after another.
+ *
+ *   X [M,K], W [K,N]: in.  Y [M,N]: out.  D a multiple of 8 (<= 4096),
+ *   N_rot a multiple of D and <= N, 1 <= S, base finite and > 0, else
+ *   CODA_ERR_SHAPE.  workspace: >= coda_rope_fwd_workspace_bytes(...) bytes
+ *   (the cos / sin table, S x D floats, built per call in double precision).
+ * CODA_F32 returns CODA_ERR_UNSUPPORTED in this build.
+ * ---------------------------------------------------------------------- */
+size_t coda_rope_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t N,
+                                     int64_t N_rot, int64_t D, int64_t S);
+coda_status coda_rope_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t N, int64_t N_rot,
+                          int64_t D, int64_t S, float base, const void* X, const void* W, void* Y,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backward of the rotary QKV projection: the exact gradient of L = <dY, Y>.
+ * The rotation is orthogonal, so dP is dY rotated back (by -phi) on the
+ * first N_rot columns and dY elsewhere;  dX = dP W^T;  dW = X^T dP.
+ *
+ *   X [M,K], W [K,N], dY [M,N]: in.  dX [M,K], dW [K,N]: out.
+ *   workspace: >= coda_rope_bwd_workspace_bytes(...) bytes (table and dP).
+ * Arguments and errors as coda_rope_fwd.
+ * ---------------------------------------------------------------------- */
+size_t coda_rope_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t N,
+                                     int64_t N_rot, int64_t D, int64_t S);
+coda_status coda_rope_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t N, int64_t N_rot,
+                          int64_t D, int64_t S, float base, const void* X, const void* W,
+                          const void* dY, void* dX, void* dW, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Kernel tracing (measurement aid; off by default).
  *
  * coda_trace_start(capacity) creates 2*capacity timing events (host call,

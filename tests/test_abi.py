@@ -257,3 +257,33 @@ def test_ce_rejects(L):
     assert L.coda_ce_bwd(BF16, M, d, V, h, Wv, lab, logits, lse, dl, dh, dWv, ws, nb - 16, None) == WORKSPACE
     assert L.coda_ce_bwd(BF16, M, d, V, h, Wv, lab, logits, lse, dl, dh, h, ws, nb, None) == ALIAS
     assert L.coda_ce_bwd(9, M, d, V, h, Wv, lab, logits, lse, dl, dh, dWv, ws, nb, None) == DTYPE
+
+
+def test_rope_rejects(L):
+    m = FakeMem()
+    M, K, N = 64, 32, 96
+    X, W, Y = m(M * K * 2), m(K * N * 2), m(M * N * 2)
+    ws = m(1 << 20)
+    need = L.coda_rope_fwd_workspace_bytes(BF16, M, K, N, 64, 32, 16)
+    assert need >= 16 * 32 * 4
+    ok = dict(N_rot=64, D=32, S=16, base=10000.0)
+
+    def fwd(**o):
+        a = {**ok, **o}
+        return L.coda_rope_fwd(a.get("dtype", BF16), M, K, N, a["N_rot"], a["D"], a["S"], a["base"], X, W,
+                               a.get("Y", Y), ws, a.get("ws_bytes", need), None)
+    assert fwd(D=12) == SHAPE            # head width not a multiple of 8
+    assert fwd(N_rot=48) == SHAPE        # rotated columns not whole heads
+    assert fwd(N_rot=128) == SHAPE       # more rotated columns than N
+    assert fwd(S=0) == SHAPE
+    assert fwd(base=-1.0) == SHAPE
+    assert fwd(base=float("inf")) == SHAPE
+    assert fwd(dtype=F32) == UNSUPPORTED
+    assert fwd(ws_bytes=need - 16) == WORKSPACE
+    assert fwd(Y=X) == ALIAS
+    assert L.coda_rope_fwd(BF16, M, K, N, 64, 32, 16, 10000.0, X, None, Y, ws, need, None) == NULL
+    dY, dX, dW = m(M * N * 2), m(M * K * 2), m(K * N * 2)
+    nb = L.coda_rope_bwd_workspace_bytes(BF16, M, K, N, 64, 32, 16)
+    assert nb >= need + M * N * 2
+    assert L.coda_rope_bwd(BF16, M, K, N, 64, 32, 16, 10000.0, X, W, dY, dX, dW, ws, nb - 16, None) == WORKSPACE
+    assert L.coda_rope_bwd(BF16, M, K, N, 64, 32, 16, 10000.0, X, W, dY, dX, X, ws, nb, None) == ALIAS

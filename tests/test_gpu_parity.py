@@ -438,3 +438,57 @@ def test_full_workload_ce(torch_dev):
     assert errs["loss"] <= CE_TOL and errs["lse"] <= CE_TOL, errs
     for k in ("logits_rows", "dh_rows", "dWv_cols"):
         assert errs[k] <= BF16_TOL, (k, errs[k])
+
+
+# ------------------------------------------ QKV projection with rotary positions
+
+SMALL_ROPE = [
+    # M, K, N, N_rot, D, S
+    (520, 264, 776, 512, 128, 200),    # ragged; positions wrap at 200
+    (8, 8, 24, 16, 8, 3),              # smallest head width
+    (256, 256, 384, 256, 64, 256),     # one row tile, v = 128 columns
+    (264, 136, 392, 256, 128, 64),     # N not a multiple of the tile
+    (272, 64, 256, 256, 128, 1),       # S = 1: every row at position 0 (no rotation)
+]
+
+
+@pytest.mark.parametrize("case", SMALL_ROPE, ids=lambda s: "x".join(map(str, s)))
+def test_rope_fwd_bwd(torch_dev, case):
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    M, K, N, N_rot, D, S = case
+    base = 10000.0
+    h = synth.rope_inputs(M, K, N, seed=600 + M + N)
+    t = {k: up(torch, dev, v, "bf16") for k, v in h.items()}
+    Y = coda.rope_fwd(t["X"], t["W"], N_rot, D, S, base)
+    dX, dW = coda.rope_bwd(t["X"], t["W"], t["dY"], N_rot, D, S, base)
+    torch.cuda.synchronize()
+    f = oracle.ref_rope_fwd(h["X"], h["W"], N_rot, D, S, base)
+    b = oracle.ref_rope_bwd(h["X"], h["W"], h["dY"], N_rot, D, S, base)
+    errs = {"Y": rel(host(Y), f["Y"]), "dX": rel(host(dX), b["dX"]), "dW": rel(host(dW), b["dW"])}
+    report(f"rope {case}", errs)
+    for k, v in errs.items():
+        assert v <= BF16_TOL, (k, v)
+
+
+def test_full_workload_rope(torch_dev):
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    w = synth.WORKLOADS["llama7b_qkv_rope_fwdbwd"]
+    print("[parity] llama7b_qkv_rope_fwdbwd: generating inputs", flush=True)
+    h = synth.workload_inputs(w)
+    t = {k: up(torch, dev, v, "bf16") for k, v in h.items()}
+    Y = coda.rope_fwd(t["X"], t["W"], w.rot, w.head, w.seq, w.base)
+    dX, dW = coda.rope_bwd(t["X"], t["W"], t["dY"], w.rot, w.head, w.seq, w.base)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed)
+    rows = np.unique(np.concatenate([_rows(w.M, rng, k=24), [w.seq - 1, w.seq, w.M - 2]]))
+    cols = np.unique(np.concatenate([[0, 1, w.rot - 1, w.rot, w.N - 1], rng.choice(w.N, 16, replace=False)]))
+    print("[parity] llama7b_qkv_rope_fwdbwd: oracle", flush=True)
+    fr = oracle.ref_rope_fwd_rows(h["X"], h["W"], w.rot, w.head, w.seq, w.base, rows)
+    bs = oracle.ref_rope_bwd_sampled(h["X"], h["W"], h["dY"], w.rot, w.head, w.seq, w.base, rows, cols)
+    errs = {"Y_rows": rel(host(Y[rows]), fr["Y"]), "dX_rows": rel(host(dX[rows]), bs["dX_rows"]),
+            "dW_cols": rel(host(dW[:, cols]), bs["dW_cols"])}
+    report("llama7b_qkv_rope_fwdbwd", errs)
+    for k, v in errs.items():
+        assert v <= BF16_TOL, (k, v)
