@@ -11,9 +11,9 @@ autograd step on the same GPU (for the step, and for the forward and the
 backward alone), the median / min / max step time, per-kernel times from HIP
 events recorded on the stream the kernels run on, the roofline of the
 dominant kernel, the same figures for the 70B-hidden, SwiGLU, MLP sub-layer
-(the two chained), LM-head cross-entropy and 1B-hidden (forward only)
-workloads under "also", and the CPU oracle timed on a bounded sample of the
-same workload.
+(the two chained), LM-head cross-entropy, rotary QKV projection and
+1B-hidden (forward only) workloads under "also", and the CPU oracle timed on
+a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-also] [--no-cpu-baseline]
 """
@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_fwdbwd")
-    ap.add_argument("--no-also", action="store_true", help="skip the 70B, SwiGLU, MLP, cross-entropy and 1B workloads")
+    ap.add_argument("--no-also", action="store_true", help="skip the 70B, SwiGLU, MLP, cross-entropy, RoPE and 1B workloads")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused torch baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
@@ -232,6 +232,58 @@ class CeCase:
         return self.t["dloss"].to(self.torch.bfloat16)
 
 
+class RopeCase:
+    """QKV projection with rotary positions on q and k."""
+
+    def __init__(self, w, torch, coda, h):
+        dev = torch.device("cuda:0")
+        self.w, self.torch, self.coda = w, torch, coda
+        self.t = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in h.items()}
+        M, K, N = w.M, w.K, w.N
+        bf = torch.bfloat16
+        self.Y = torch.empty((M, N), dtype=bf, device=dev)
+        self.dX = torch.empty((M, K), dtype=bf, device=dev)
+        self.dW = torch.empty((K, N), dtype=bf, device=dev)
+        self.wsf = torch.empty(coda.rope_fwd_workspace_bytes(1, M, K, N, w.rot, w.head, w.seq),
+                               dtype=torch.uint8, device=dev)
+        self.wsb = torch.empty(coda.rope_bwd_workspace_bytes(1, M, K, N, w.rot, w.head, w.seq),
+                               dtype=torch.uint8, device=dev)
+        # the unfused baseline's rotary table (cos, sin per position and pair), built once
+        pos = (torch.arange(M, device=dev) % w.seq).double()
+        theta = w.base ** (-torch.arange(0, w.head, 2, device=dev, dtype=torch.float64) / w.head)
+        ang = pos[:, None] * theta[None, :]
+        self.cos, self.sin = ang.cos().to(bf), ang.sin().to(bf)
+        self.backward = w.backward
+        self.kernels_per_step = 6
+        self.leaf_names = ("X", "W")
+
+    def flops(self):
+        return self.w.flops_fwd() + (self.w.flops_bwd() if self.backward else 0.0)
+
+    def fused_fwd(self):
+        w, t = self.w, self.t
+        self.coda.coda_rope_fwd(t["X"], t["W"], w.rot, w.head, w.seq, w.base, self.Y, self.wsf)
+
+    def fused_bwd(self):
+        w, t = self.w, self.t
+        self.coda.coda_rope_bwd(t["X"], t["W"], t["dY"], w.rot, w.head, w.seq, w.base, self.dX, self.dW,
+                                self.wsb)
+
+    def unfused_fwd(self):
+        """matmul, then the rotation as separate elementwise ops on the q/k columns."""
+        w, p = self.w, self.leaf
+        P = p["X"] @ p["W"]
+        M = P.shape[0]
+        qk = P[:, :w.rot].reshape(M, w.rot // w.head, w.head // 2, 2)
+        c, s_ = self.cos[:, None, :], self.sin[:, None, :]
+        x0, x1 = qk[..., 0], qk[..., 1]
+        rot = self.torch.stack([x0 * c - x1 * s_, x0 * s_ + x1 * c], dim=-1).reshape(M, w.rot)
+        return self.torch.cat([rot, P[:, w.rot:]], dim=1)
+
+    def grad_outputs(self):
+        return self.t["dY"]
+
+
 class _Steps:
     """The fused and unfused step functions of a case: forward, backward, and
     the training step (forward + backward; the forward alone for a
@@ -279,7 +331,7 @@ class _Steps:
 def make_case(w, torch, coda):
     from gemm_epilogue_fusion_gemm1_amd import synth
     h = synth.workload_inputs(w)
-    cls = {"coda": CodaCase, "swiglu": SwigluCase, "mlp": MlpCase, "ce": CeCase}[w.kind]
+    cls = {"coda": CodaCase, "swiglu": SwigluCase, "mlp": MlpCase, "ce": CeCase, "rope": RopeCase}[w.kind]
     return cls(w, torch, coda, h), h
 
 
@@ -497,7 +549,7 @@ def main():
     also = {}
     if not args.no_also:
         for name in ("llama70b_fwdbwd", "swiglu_fwdbwd", "llama7b_mlp_fwdbwd", "llama7b_ce_fwdbwd",
-                     "llama1b_fwd"):
+                     "llama7b_qkv_rope_fwdbwd", "llama1b_fwd"):
             w2 = synth.WORKLOADS[name]
             print(f"[bench] {name}: inputs + timing", file=sys.stderr, flush=True)
             c2, _ = make_case(w2, torch, coda)
