@@ -60,6 +60,14 @@ What the pages fix, and the readings taken where they are silent:
     width D) on the interleaved pairs (2i, 2i+1) by the angle p theta_i, theta_i
     = base^(-2i/D), p = row mod S (rows are S-token sequences one after
     another); the remaining columns (v) pass through.
+  * An FP8 forward of the fused block (``ref_fwd_mx8``): the pages note that
+    faster FP8/FP4 matrix units make the data movement around a GEMM relatively
+    more costly ([JA] 課題：大モデル訓練の「手抜き税」; [RU] "Налог на лень
+    при обучении больших моделей"; [FR] "Le « impôt de la paresse » pour
+    l'entraînement des grands modèles") but fix no format.  Reading: OCP MXFP8 (E4M3 elements, one E8M0
+    power-of-two scale per 32 along the contraction index), both GEMMs' operands
+    in it; the second GEMM's operand is y diag(gamma) quantised by the first
+    GEMM's epilogue, with r still applied after the second GEMM.
 
 Every function here is pinned by a test against something other than itself
 (brute-force loops, finite differences, torch CPU autograd, closed forms and
@@ -77,6 +85,8 @@ __all__ = [
     "ref_ce_fwd", "ref_ce_bwd", "ref_ce_partials", "ref_ce_fwd_rows", "ref_ce_bwd_sampled",
     "rope_angles", "ref_rope_rotate", "ref_rope_fwd", "ref_rope_bwd", "ref_rope_fwd_rows",
     "ref_rope_bwd_sampled",
+    "E4M3_MAX", "MX_BLOCK", "e4m3_decode", "e4m3_encode", "e8m0_decode", "mx_quantize",
+    "mx_dequantize", "ref_fwd_mx8", "ref_fwd_mx8_rows",
 ]
 
 
@@ -627,3 +637,140 @@ def ref_rope_bwd_sampled(X, W, dY, N_rot: int, D: int, S: int, base: float, rows
     dP = ref_rope_rotate(dY, N_rot, D, S, base, inverse=True)
     rows, cols_N = np.asarray(rows), np.asarray(cols_N)
     return {"rows": rows, "cols_N": cols_N, "dX_rows": dP[rows] @ W.T, "dW_cols": X.T @ dP[:, cols_N]}
+
+
+# ---------------------------------------------------------------------------
+# MX-FP8 (OCP microscaling, E4M3 elements with one E8M0 scale per 32) forward
+# of the fused block
+# ---------------------------------------------------------------------------
+# The pages say that faster low-precision (FP8, FP4) matrix units raise the
+# relative cost of the memory-bound work around a GEMM (the "tax" sections:
+# [JA] 課題：大モデル訓練の「手抜き税」, [RU] "Налог на лень ...", [FR] "Le
+# « impôt de la paresse » ...").  They fix no FP8 format
+# or scaling.  Reading: the OCP Microscaling (MX) v1.0 MXFP8 format.  An
+# element is FP8 E4M3 (the "FN" variant: bias 7, no infinities, S.1111.111 is
+# NaN, largest finite 448); every 32 consecutive elements along the contraction
+# index share one E8M0 scale byte s meaning 2**(s - 127) (255 is NaN).  A block
+# is quantised with the shared exponent floor(log2(amax)) - 8 (8 = E4M3's
+# largest normal exponent), clamped to [-127, 127]; an all-zero block takes
+# exponent -127; each element divided by 2**shared_exp is rounded to the
+# nearest E4M3 value, ties to even, and saturated to +-448.
+
+E4M3_MAX = 448.0
+MX_BLOCK = 32
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """E4M3 (FN) byte -> float64: sign bit 7, exponent bits 6..3 (bias 7),
+    mantissa bits 2..0; exponent 0 is subnormal (m/8 * 2**-6); 0x7F and 0xFF
+    are NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """float64 -> nearest E4M3 (FN) byte, ties to even, saturating at +-448.
+
+    Normal values keep 4 significant bits (spacing 2**(e-3) in the binade
+    [2**e, 2**(e+1)), e >= -6); below 2**-6 the spacing stays 2**-9
+    (subnormals).  The value is scaled so that one step is 1, rounded with
+    numpy's rint (ties to even) and the code is assembled from the rounded
+    magnitude.  NaN is not accepted.
+    """
+    x = _f64(x)
+    if np.isnan(x).any():
+        raise ValueError("e4m3_encode: NaN input")
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    _, fe = np.frexp(a)                       # a = f * 2**fe, 0.5 <= f < 1; a in [2**(fe-1), 2**fe)
+    e = np.maximum(fe - 1, -6)                # binade exponent, subnormals use -6
+    q = np.rint(np.ldexp(a, 3 - e))           # magnitude in steps of 2**(e-3): 8..16 normal, 0..8 subnormal
+    # a carry to 16 steps moves to the next binade (16 * 2**(e-3) = 2**(e+1))
+    carry = q >= 16
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, q / 2, q)
+    sub = q < 8                               # only possible with e == -6
+    exp_field = np.where(sub, 0, e + 7).astype(np.int64)
+    mant = np.where(sub, q, q - 8).astype(np.int64)
+    mag_code = (exp_field << 3) | mant
+    mag_code = np.minimum(mag_code, 0x7E)     # saturate (448 = 0x7E); rounding can reach 480 only above 464
+    code = np.where(np.signbit(x), 0x80, 0) | mag_code
+    return code.astype(np.uint8)
+
+
+def e8m0_decode(scales) -> np.ndarray:
+    """E8M0 scale byte s -> 2**(s - 127); 255 is NaN."""
+    s = np.asarray(scales, dtype=np.uint8).astype(np.float64)
+    return np.where(s == 255, np.nan, np.exp2(s - 127.0))
+
+
+def mx_quantize(V, block: int = MX_BLOCK):
+    """Quantise the rows of V [rows, K] to MXFP8 along K (K % block == 0).
+
+    Per block of ``block`` consecutive elements of a row: amax = max |v|;
+    shared_exp = floor(log2(amax)) - 8, clamped to [-127, 127] (amax == 0 ->
+    -127); scale byte = shared_exp + 127; element codes = e4m3_encode(v /
+    2**shared_exp).  Returns (codes uint8 [rows, K], scales uint8 [rows,
+    K / block]).
+    """
+    V = _f64(V)
+    rows, K = V.shape
+    if K % block:
+        raise ValueError("mx_quantize: K must be a multiple of the block")
+    B = V.reshape(rows, K // block, block)
+    amax = np.max(np.abs(B), axis=2)
+    _, fe = np.frexp(amax)                    # amax in [2**(fe-1), 2**fe): floor(log2) = fe - 1
+    sexp = np.where(amax > 0, fe - 1 - 8, -127)
+    sexp = np.clip(sexp, -127, 127)
+    codes = e4m3_encode(np.ldexp(B, -sexp[:, :, None]))
+    return codes.reshape(rows, K), (sexp + 127).astype(np.uint8)
+
+
+def mx_dequantize(codes, scales, block: int = MX_BLOCK) -> np.ndarray:
+    """MXFP8 [rows, K] codes with [rows, K / block] scales -> float64."""
+    c = np.asarray(codes)
+    rows, K = c.shape
+    v = e4m3_decode(c).reshape(rows, K // block, block) * e8m0_decode(scales)[:, :, None]
+    return v.reshape(rows, K)
+
+
+def ref_fwd_mx8(Xq, Xs, W1q, W1s, R, gamma, W2q, W2s, eps: float) -> dict:
+    """Forward of the fused block with MXFP8 GEMM operands.
+
+    X is [M, K] (codes Xq, scales Xs along K).  The weights are stored with
+    their contraction index contiguous, as [out, in]: W1q [d, K] with W1s
+    [d, K/32], W2q [N, d] with W2s [N, d/32].  R [M, d] and gamma [d] are real.
+
+      y  = deq(X) deq(W1)^T + R;   r_i = (mean_j y_ij^2 + eps)^-1/2;
+      (q, s) = mx_quantize(y diag(gamma))   (blocks along j, the second
+                                             GEMM's contraction index);
+      z  = diag(r) (deq(q, s) deq(W2)^T).
+
+    This is the rewrite of ``ref_fwd_rewritten`` (r deferred past the second
+    GEMM) with its second operand stored in MXFP8.  Reading: what is
+    quantised is y diag(gamma), the tensor the first GEMM's epilogue holds,
+    not the normalised h = diag(r) y diag(gamma); the two differ by one E4M3
+    rounding per element because r is not a power of two.
+    """
+    Xh = mx_dequantize(Xq, Xs)
+    W1h = mx_dequantize(W1q, W1s)
+    W2h = mx_dequantize(W2q, W2s)
+    R, gamma = _f64(R), _f64(gamma)
+    y = Xh @ W1h.T + R
+    r = 1.0 / np.sqrt(np.mean(y * y, axis=1) + eps)
+    q, s = mx_quantize(y * gamma[None, :])
+    z = r[:, None] * (mx_dequantize(q, s) @ W2h.T)
+    return {"y": y, "r": r, "yg_q": q, "yg_s": s, "yg": y * gamma[None, :], "z": z}
+
+
+def ref_fwd_mx8_rows(Xq, Xs, W1q, W1s, R, gamma, W2q, W2s, eps: float, rows) -> dict:
+    """``ref_fwd_mx8`` for the given rows only (every step is row-local)."""
+    rows = np.asarray(rows)
+    out = ref_fwd_mx8(np.asarray(Xq)[rows], np.asarray(Xs)[rows], W1q, W1s, _f64(R[rows]), gamma,
+                      W2q, W2s, eps)
+    out["rows"] = rows
+    return out

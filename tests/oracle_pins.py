@@ -813,6 +813,224 @@ def pin_bf16_rne(O):
     assert np.array_equal(O.bf16_rne(v.astype(np.float64)), t), "bf16_rne vs torch"
 
 
+# ------------------------------------------------------------------ MXFP8 pins
+
+def _e4m3_table():
+    """All finite E4M3 (FN) values by code, built by pure-Python loops from the
+    format's bit fields (sign, 4 exponent bits with bias 7, 3 mantissa bits)."""
+    tab = {}
+    for code in range(256):
+        if code & 0x7F == 0x7F:
+            continue
+        e, m = (code >> 3) & 15, code & 7
+        mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+        tab[code] = -mag if code & 0x80 else mag
+    return tab
+
+
+def _e4m3_nearest(x, tab):
+    """Brute force: the finite code nearest to x (|x| clamped to 448), ties to
+    the even mantissa; the sign of x is kept for zero."""
+    a = min(abs(x), 448.0)
+    best = None
+    for code, v in tab.items():
+        if code & 0x80:
+            continue
+        dv = abs(v - a)
+        if best is None or dv < best[0] or (dv == best[0] and (code & 1) == 0):
+            best = (dv, code)
+    code = best[1]
+    return code | 0x80 if (x < 0 or (x == 0 and math.copysign(1.0, x) < 0)) else code
+
+
+def _shared_exp_loop(amax):
+    """floor(log2(amax)) - 8 clamped to [-127, 127] by repeated halving and
+    doubling (no frexp or log); -127 for amax == 0."""
+    if amax == 0:
+        return -127
+    e = 0
+    while amax >= 2.0 ** (e + 1):
+        e += 1
+    while amax < 2.0 ** e:
+        e -= 1
+    return max(-127, min(127, e - 8))
+
+
+def pin_e4m3_codes(O):
+    """E4M3 (FN) decoding against the bit fields (pure Python) and torch's
+    float8_e4m3fn on all 256 codes; known values; encoding against brute-force
+    nearest-code search (ties to even, saturation at 448) and against torch's
+    float32 -> float8_e4m3fn conversion (round to nearest even) up to 464."""
+    import torch
+    tab = _e4m3_table()
+    codes = np.arange(256, dtype=np.uint8)
+    dec = O.e4m3_decode(codes)
+    for c in range(256):
+        if c in tab:
+            assert dec[c] == tab[c] and math.copysign(1, dec[c]) == math.copysign(1, tab[c]), f"decode {c:#x}"
+        else:
+            assert np.isnan(dec[c]), f"decode {c:#x} should be NaN"
+    t = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    fin = ~np.isnan(t)
+    assert np.array_equal(np.isnan(dec), ~fin) and np.array_equal(dec[fin], t[fin]), "decode vs torch"
+    for c, v in ((0x38, 1.0), (0x7E, 448.0), (0x01, 2.0 ** -9), (0x08, 2.0 ** -6), (0x07, 7 * 2.0 ** -9),
+                 (0xC0, -2.0), (0x78, 256.0)):
+        assert dec[c] == v, f"decode {c:#x} = {dec[c]!r}, want {v!r}"
+    g = _rng(81)
+    pos = sorted(v for c, v in tab.items() if not c & 0x80)
+    xs = [0.0, -0.0, 448.0, 449.0, 463.9, 464.0, 465.0, 479.0, 480.0, 1e6, -1e6, 2.0 ** -10, 2.0 ** -11,
+          3 * 2.0 ** -10, 5 * 2.0 ** -10]
+    for a, b in zip(pos[:-1], pos[1:]):
+        mid = (a + b) / 2
+        xs += [mid, -mid, mid * (1 + 1e-12), mid * (1 - 1e-12)]
+    xs += list(g.uniform(-500, 500, 200)) + list(g.uniform(-0.05, 0.05, 200))
+    enc = O.e4m3_encode(np.array(xs))
+    for x, c in zip(xs, enc):
+        want = _e4m3_nearest(x, tab)
+        assert int(c) == want, f"e4m3_encode({x!r}) = {int(c):#x}, want {want:#x}"
+    v = (g.standard_normal(50000) * np.exp2(g.integers(-12, 9, 50000))).astype(np.float32)
+    v = v[np.abs(v) <= 464]      # above 464 torch rounds to 480, which E4M3 FN spends on NaN
+    tt = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(v.astype(np.float64)), tt), "e4m3_encode vs torch"
+
+
+def pin_mx_quantize(O):
+    """MXFP8 block quantisation: E8M0 decoding; hand-worked blocks (all ones,
+    amax 448, saturation at 500, an all-zero block, a tiny block whose shared
+    exponent clamps at -127); brute force (scale by halving/doubling loops,
+    codes by nearest-code search) on random blocks; exact round trip of blocks
+    that are MXFP8 values; the element error bound of one E4M3 rounding."""
+    assert O.e8m0_decode(np.array([0], np.uint8))[0] == 2.0 ** -127
+    assert O.e8m0_decode(np.array([127], np.uint8))[0] == 1.0
+    assert O.e8m0_decode(np.array([254], np.uint8))[0] == 2.0 ** 127
+    assert np.isnan(O.e8m0_decode(np.array([255], np.uint8))[0])
+    blk = np.ones((1, 32))
+    q, s = O.mx_quantize(blk)
+    assert s[0, 0] == 119 and np.all(q == 0x78), "all-ones block: 2^-8 scale, code 256"
+    blk = np.zeros((1, 32)); blk[0, 0] = 448.0; blk[0, 1] = -1.0; blk[0, 2] = 500.0 / 512 * 448
+    q, s = O.mx_quantize(blk)
+    assert s[0, 0] == 127 and q[0, 0] == 0x7E and q[0, 1] == 0xB8, "amax 448: scale 1"
+    blk[0, 3] = 500.0
+    q, s = O.mx_quantize(blk)
+    assert s[0, 0] == 127 and q[0, 3] == 0x7E, "500 saturates to 448 under scale 1"
+    q, s = O.mx_quantize(np.zeros((2, 64)))
+    assert np.all(s == 0) and np.all(q == 0), "zero blocks"
+    q, s = O.mx_quantize(np.full((1, 32), 2.0 ** -130))
+    assert s[0, 0] == 0 and np.all(q == 0x20), "clamped shared exponent: 2^-130 / 2^-127 = 2^-3"
+    tab = _e4m3_table()
+    g = _rng(82)
+    V = g.standard_normal((3, 96)) * np.exp2(g.integers(-20, 20, (3, 1)))
+    V[1, 32:64] = 0.0
+    q, s = O.mx_quantize(V)
+    for i in range(3):
+        for b in range(3):
+            blkv = [float(x) for x in V[i, 32 * b:32 * b + 32]]
+            e = _shared_exp_loop(max(abs(x) for x in blkv))
+            assert int(s[i, b]) == e + 127, f"scale of block ({i},{b})"
+            for j, x in enumerate(blkv):
+                assert int(q[i, 32 * b + j]) == _e4m3_nearest(x / 2.0 ** e, tab), f"code ({i},{32 * b + j})"
+    # MXFP8 values round-trip exactly (a code with exponent field 15 and
+    # mantissa <= 6 sets the block maximum)
+    codes = g.integers(0, 0x7F, (4, 64)).astype(np.uint8) | (g.integers(0, 2, (4, 64)) << 7).astype(np.uint8)
+    codes[codes & 0x7F == 0x7F] = 0x10
+    codes[:, ::32] = 0x78 | (codes[:, ::32] & 0x80)
+    codes[(codes & 0x78) == 0x78] &= 0xFE                  # exponent field 15: mantissa <= 6 (no 480)
+    codes[(codes & 0x7F) == 0x7E] = 0x7C
+    scales = g.integers(100, 150, (4, 2)).astype(np.uint8)
+    V = O.mx_dequantize(codes, scales)
+    q, s = O.mx_quantize(V)
+    assert np.array_equal(s, scales) and np.array_equal(q, codes), "MXFP8 values must round-trip"
+    V = g.standard_normal((8, 256)) * 3.0
+    q, s = O.mx_quantize(V)
+    D = O.mx_dequantize(q, s)
+    sc = np.repeat(O.e8m0_decode(s), 32, axis=1)
+    u = np.abs(V) / sc
+    bound = np.where(u >= 2.0 ** -6, 2.0 ** -4 * np.abs(V), 2.0 ** -10 * sc)
+    bound = np.where(u > 448.0, np.abs(V) - 448.0 * sc + 1e-300, bound)
+    assert np.all(np.abs(D - V) <= bound * (1 + 1e-12)), "one E4M3 rounding per element"
+    assert np.all(u < 512.0) and np.all(np.max(u.reshape(8, 8, 32), axis=2) >= 256.0), "block max lands in [256, 512)"
+
+
+def _mx8_case(seed, M, K, d, N, eps=1e-6):
+    g = _rng(seed)
+    X = g.standard_normal((M, K))
+    W1t = g.standard_normal((d, K)) / math.sqrt(K)
+    W2t = g.standard_normal((N, d)) / math.sqrt(d)
+    return dict(X=X, W1t=W1t, W2t=W2t, R=g.standard_normal((M, d)), gamma=1 + 0.1 * g.standard_normal(d),
+                eps=eps)
+
+
+def _mx8_quantised(O, c):
+    Xq, Xs = O.mx_quantize(c["X"])
+    W1q, W1s = O.mx_quantize(c["W1t"])
+    W2q, W2s = O.mx_quantize(c["W2t"])
+    return Xq, Xs, W1q, W1s, W2q, W2s
+
+
+def pin_fwd_mx8_exact(O):
+    """With W1 = 0 and gamma = 1, y = R; R made of MXFP8 values makes the
+    quantisation of y gamma exact, so z and r must equal the real-valued
+    forward (ref_fwd, itself pinned) of the dequantised weights exactly, up to
+    float64 rounding: this fixes r applied after the second GEMM, on the
+    unquantised y gamma."""
+    g = _rng(83)
+    M, K, d, N = 5, 64, 96, 7
+    Xq, Xs = O.mx_quantize(g.standard_normal((M, K)))
+    W1q = np.zeros((d, K), np.uint8); W1s = np.full((d, K // 32), 127, np.uint8)
+    codes = g.integers(0, 0x7E, (M, d)).astype(np.uint8) | (g.integers(0, 2, (M, d)) << 7).astype(np.uint8)
+    codes[codes & 0x7F == 0x7F] = 0x11
+    codes[codes == 0x80] = 0x00                             # y = 0 + R turns -0 into +0
+    codes[:, ::32] = 0x70 | (codes[:, ::32] & 0x80)         # block max 128..: exponent field 14
+    codes[:, 1::32] = 0x78 | (codes[:, 1::32] & 0x80)       # exponent field 15, mantissa 0
+    scales = g.integers(115, 130, (M, d // 32)).astype(np.uint8)
+    R = O.mx_dequantize(codes, scales)
+    W2q, W2s = O.mx_quantize(g.standard_normal((N, d)))
+    out = O.ref_fwd_mx8(Xq, Xs, W1q, W1s, R, np.ones(d), W2q, W2s, 1e-6)
+    ref = O.ref_fwd(np.zeros((M, K)), np.zeros((K, d)), R, np.ones(d), O.mx_dequantize(W2q, W2s).T, 1e-6)
+    assert np.array_equal(out["yg_q"], codes) and np.array_equal(out["yg_s"], scales), "exact quantisation"
+    _close(out["z"], ref["z"], 1e-13, "mx8 exact z")
+    _close(out["r"], ref["r"], 1e-13, "mx8 exact r")
+
+
+def pin_fwd_mx8_bruteforce(O):
+    """Pure-Python loops on a tiny case: dequantise the operands from their
+    bit fields, y = X W1^T + R, r, quantise y*gamma per 32-block by the loop
+    scale and nearest-code search, z = r * (q W2^T)."""
+    tab = _e4m3_table()
+    c = _mx8_case(84, 3, 64, 64, 4)
+    Xq, Xs, W1q, W1s, W2q, W2s = _mx8_quantised(O, c)
+    M, K, d, N = 3, 64, 64, 4
+
+    def deq(codes, scales, i, k):
+        return tab[int(codes[i, k])] * 2.0 ** (int(scales[i, k // 32]) - 127)
+
+    out = O.ref_fwd_mx8(Xq, Xs, W1q, W1s, c["R"], c["gamma"], W2q, W2s, c["eps"])
+    for i in range(M):
+        y = [sum(deq(Xq, Xs, i, k) * deq(W1q, W1s, j, k) for k in range(K)) + c["R"][i, j] for j in range(d)]
+        r = 1.0 / math.sqrt(sum(v * v for v in y) / d + c["eps"])
+        assert abs(out["r"][i] - r) <= 1e-12 * r, "mx8 r"
+        hq = []
+        for b in range(d // 32):
+            blk = [y[j] * c["gamma"][j] for j in range(32 * b, 32 * b + 32)]
+            e = _shared_exp_loop(max(abs(v) for v in blk))
+            hq += [tab[_e4m3_nearest(v / 2.0 ** e, tab)] * 2.0 ** e for v in blk]
+        for n in range(N):
+            z = r * sum(hq[j] * deq(W2q, W2s, n, j) for j in range(d))
+            assert abs(out["z"][i, n] - z) <= 1e-12 * max(1.0, abs(z)), f"mx8 z[{i},{n}]"
+        assert max(abs(out["y"][i, j] - y[j]) for j in range(d)) <= 1e-12, "mx8 y"
+
+
+def pin_fwd_mx8_rows(O):
+    """The row form equals the matching rows of the full forward."""
+    c = _mx8_case(85, 40, 64, 96, 24)
+    Xq, Xs, W1q, W1s, W2q, W2s = _mx8_quantised(O, c)
+    full = O.ref_fwd_mx8(Xq, Xs, W1q, W1s, c["R"], c["gamma"], W2q, W2s, c["eps"])
+    rows = np.array([0, 7, 39, 20])
+    part = O.ref_fwd_mx8_rows(Xq, Xs, W1q, W1s, c["R"], c["gamma"], W2q, W2s, c["eps"], rows)
+    for k in ("y", "r", "z", "yg_q", "yg_s"):
+        assert np.array_equal(part[k], full[k][rows]), f"mx8 rows {k}"
+
+
 ALL_PINS = [
     pin_fwd_bruteforce, pin_fwd_torch_rmsnorm, pin_fwd_constant_rows,
     pin_fwd_scale_invariance, pin_partials, pin_rewrite_equals_unfused,
@@ -825,5 +1043,6 @@ ALL_PINS = [
     pin_ce_closed_forms, pin_ce_invariants, pin_ce_partials, pin_ce_sampled,
     pin_rope_bruteforce, pin_rope_torch, pin_rope_finite_differences, pin_rope_properties,
     pin_rope_sampled,
-    pin_bwd_dy_in_finite_differences,
+    pin_bwd_dy_in_finite_differences, pin_e4m3_codes, pin_mx_quantize, pin_fwd_mx8_exact,
+    pin_fwd_mx8_bruteforce, pin_fwd_mx8_rows,
 ]

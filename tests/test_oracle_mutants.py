@@ -259,6 +259,76 @@ def bf16_via_f32(x):
     return t.to(torch.bfloat16).to(torch.float64).numpy()
 
 
+def _mx_mutant(kind):
+    """A mistake in the MXFP8 encoding reaches everything built on it."""
+    def encode(x):
+        x = np.asarray(x, dtype=np.float64)
+        a = np.abs(x) if kind == "no_saturation" else np.minimum(np.abs(x), 448.0)
+        _, fe = np.frexp(a)
+        e = np.maximum(fe - 1, -6)
+        t = np.ldexp(a, 3 - e)
+        if kind == "truncate":
+            q = np.floor(t)
+        elif kind == "ties_away":
+            q = np.floor(t + 0.5)
+        else:
+            q = np.rint(t)
+        if kind == "flush_subnormals":
+            q = np.where(fe - 1 < -6, 0.0, q)
+        carry = q >= 16
+        e = np.where(carry, e + 1, e)
+        q = np.where(carry, q / 2, q)
+        sub = q < 8
+        code = (np.where(sub, 0, e + 7).astype(np.int64) << 3) | np.where(sub, q, q - 8).astype(np.int64)
+        if kind != "no_saturation":
+            code = np.minimum(code, 0x7E)
+        code = np.minimum(code, 0x7F)
+        return (np.where(np.signbit(x), 0x80, 0) | code).astype(np.uint8)
+
+    def quantize(V, block=32):
+        V = np.asarray(V, dtype=np.float64)
+        rows, K = V.shape
+        B = V.reshape(rows, K // block, block)
+        amax = np.max(np.abs(B), axis=2)
+        _, fe = np.frexp(amax)
+        emax = 7 if kind == "emax_7" else 8
+        sexp = np.clip(np.where(amax > 0, fe - 1 - emax, -127), -127, 127)
+        return encode(np.ldexp(B, -sexp[:, :, None])).reshape(rows, K), (sexp + 127).astype(np.uint8)
+
+    def fwd(Xq, Xs, W1q, W1s, R, gamma, W2q, W2s, eps):
+        deq = oracle.mx_dequantize
+        Xh, W1h, W2h = deq(Xq, Xs), deq(W1q, W1s), deq(W2q, W2s)
+        R, gamma = _f(R, gamma)
+        y = Xh @ W1h.T + R
+        r = 1.0 / np.sqrt(np.mean(y * y, axis=1) + eps)
+        if kind == "r_before_quantisation":
+            q, sc = quantize(y * r[:, None] * gamma[None, :])
+            z = deq(q, sc) @ W2h.T
+        else:
+            q, sc = quantize(y * gamma[None, :])
+            z = r[:, None] * (deq(q, sc) @ W2h.T)
+        return {"y": y, "r": r, "yg_q": q, "yg_s": sc, "yg": y * gamma, "z": z}
+
+    def rows_fn(Xq, Xs, W1q, W1s, R, gamma, W2q, W2s, eps, rows):
+        rows = np.asarray(rows)
+        out = fwd(np.asarray(Xq)[rows], np.asarray(Xs)[rows], W1q, W1s, np.asarray(R)[rows], gamma, W2q, W2s, eps)
+        out["rows"] = rows
+        return out
+
+    return {"e4m3_encode": encode, "mx_quantize": quantize, "ref_fwd_mx8": fwd, "ref_fwd_mx8_rows": rows_fn}
+
+
+def e4m3_decode_bias_8(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e, m = (c >> 3) & 15, (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -7, (1.0 + m / 8.0) * np.exp2(e - 8.0))
+    return np.where(c & 0x80, -1.0, 1.0) * mag
+
+
+def e8m0_off_by_one(scales):
+    return np.exp2(np.asarray(scales, dtype=np.float64) - 128.0)
+
+
 MUTANTS = {
     "fwd_eps_outside_sqrt": {"ref_fwd": fwd_eps_outside},
     "fwd_mean_over_N": {"ref_fwd": fwd_mean_over_N},
@@ -294,6 +364,14 @@ MUTANTS = {
     "mlp_bwd_dgu_halves_swapped": {"ref_mlp_bwd": _mlp_bwd_variant("dgu_halves_swapped")},
     "mlp_bwd_ignores_dgu_round": {"ref_mlp_bwd": (lambda *a, **k: oracle.ref_mlp_bwd(*a[:11]))},
     "bf16_double_rounding": {"bf16_rne": bf16_via_f32},
+    "mx_truncating_rounding": _mx_mutant("truncate"),
+    "mx_ties_away": _mx_mutant("ties_away"),
+    "mx_no_saturation": _mx_mutant("no_saturation"),
+    "mx_flush_subnormals": _mx_mutant("flush_subnormals"),
+    "mx_shared_exp_emax_7": _mx_mutant("emax_7"),
+    "mx_r_before_quantisation": _mx_mutant("r_before_quantisation"),
+    "e4m3_decode_bias_8": {"e4m3_decode": e4m3_decode_bias_8},
+    "e8m0_off_by_one": {"e8m0_decode": e8m0_off_by_one},
 }
 
 
@@ -304,6 +382,6 @@ def test_mutant_is_caught(name):
     for pin in P.ALL_PINS:
         try:
             pin(O)
-        except (AssertionError, ValueError, IndexError):
+        except (AssertionError, ValueError, IndexError, KeyError):
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {name}"
