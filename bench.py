@@ -11,8 +11,8 @@ autograd step on the same GPU (for the step, and for the forward and the
 backward alone), the median / min / max step time, per-kernel times from HIP
 events recorded on the stream the kernels run on, the roofline of the
 dominant kernel, the same figures for the 70B-hidden, SwiGLU, MLP sub-layer
-(the two chained), LM-head cross-entropy, rotary QKV projection and
-1B-hidden (forward only) workloads under "also", and the CPU oracle timed on
+(the two chained), LM-head cross-entropy, rotary QKV projection, the
+MXFP8 block forward and the 1B-hidden (forward only) workloads under "also", and the CPU oracle timed on
 a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-also] [--no-cpu-baseline]
@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA peak (vendor figure, no sparsity)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 (incl. MXFP8) MFMA peak
 METRIC = "fused fwd+bwd TFLOP/s & %bf16 MFMA peak; speedup vs unfused, 7B/70B"
 
 
@@ -41,7 +42,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_fwdbwd")
-    ap.add_argument("--no-also", action="store_true", help="skip the 70B, SwiGLU, MLP, cross-entropy, RoPE and 1B workloads")
+    ap.add_argument("--no-also", action="store_true", help="skip the 70B, SwiGLU, MLP, cross-entropy, RoPE, MXFP8 and 1B workloads")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused torch baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
@@ -284,6 +285,69 @@ class RopeCase:
         return self.t["dY"]
 
 
+class Mx8Case:
+    """The block forward on MXFP8 operands.  The bf16 draws are quantised once
+    (the library's quantiser) before timing; weights are stored [out, in]."""
+
+    def __init__(self, w, torch, coda, h):
+        dev = torch.device("cuda:0")
+        self.w, self.torch, self.coda = w, torch, coda
+        bf = torch.bfloat16
+        self.t = {k: torch.from_numpy(v).to(dev).to(bf) for k, v in h.items()}
+        M, K, d, N = w.M, w.K, w.d, w.N
+        self.q = {}
+        for k in ("X", "W1t", "W2t"):
+            self.q[k] = coda.mx8_quantize(self.t[k])
+        torch.cuda.synchronize()
+        self.y = torch.empty((M, d), dtype=bf, device=dev)
+        self.r = torch.empty((M,), dtype=torch.float32, device=dev)
+        self.z = torch.empty((M, N), dtype=bf, device=dev)
+        self.ws = torch.empty(coda.fwd_mx8_workspace_bytes(M, K, d, N), dtype=torch.uint8, device=dev)
+        self.backward = False
+        self.kernels_per_step = 2
+        self.leaf_names = ("R",)
+
+    def flops(self):
+        return self.w.flops_fwd()
+
+    def fused_fwd(self):
+        q, t = self.q, self.t
+        self.coda.coda_fwd_mx8(q["X"][0], q["X"][1], q["W1t"][0], q["W1t"][1], t["R"], t["gamma"],
+                               q["W2t"][0], q["W2t"][1], self.w.eps, self.y, self.r, self.z, self.ws)
+
+    def _mm(self, a, b):
+        """torch's MXFP8 product (hipBLASLt): a [m, k] codes and scales, b [n, k]."""
+        f8, e8 = self.torch.float8_e4m3fn, self.torch.float8_e8m0fnu
+        return self.torch._scaled_mm(a[0].view(f8), b[0].view(f8).t(), scale_a=a[1].view(e8),
+                                     scale_b=b[1].view(e8), out_dtype=self.torch.bfloat16)
+
+    def _quantise(self, v):
+        """MXFP8 quantisation as separate torch ops (amax per 32, exponent,
+        scale, saturate, convert)."""
+        torch = self.torch
+        m, n = v.shape
+        b = v.float().view(m, n // 32, 32)
+        amax = b.abs().amax(dim=2, keepdim=True)
+        e = (torch.frexp(amax)[1] - 9).clamp(-127, 127)
+        codes = (b * torch.exp2(-e.float())).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+        return codes.view(m, n).view(torch.uint8), (e + 127).to(torch.uint8).view(m, n // 32)
+
+    def unfused_fwd(self):
+        F = self.torch.nn.functional
+        y = self._mm(self.q["X"], self.q["W1t"]) + self.t["R"]
+        h = F.rms_norm(y, (self.w.d,), self.t["gamma"], self.w.eps)
+        return self._mm(self._quantise(h), self.q["W2t"])
+
+    def unfused_check(self):
+        """Relative difference between torch's first MXFP8 product + R and the
+        fused y (the same operands), to show the baseline computes the same
+        product."""
+        self.fused_fwd()
+        y = self._mm(self.q["X"], self.q["W1t"]) + self.t["R"]
+        self.torch.cuda.synchronize()
+        return float((y.float() - self.y.float()).abs().max() / self.y.float().abs().max())
+
+
 class _Steps:
     """The fused and unfused step functions of a case: forward, backward, and
     the training step (forward + backward; the forward alone for a
@@ -331,7 +395,8 @@ class _Steps:
 def make_case(w, torch, coda):
     from gemm_epilogue_fusion_gemm1_amd import synth
     h = synth.workload_inputs(w)
-    cls = {"coda": CodaCase, "swiglu": SwigluCase, "mlp": MlpCase, "ce": CeCase, "rope": RopeCase}[w.kind]
+    cls = {"coda": CodaCase, "swiglu": SwigluCase, "mlp": MlpCase, "ce": CeCase, "rope": RopeCase,
+           "mx8": Mx8Case}[w.kind]
     return cls(w, torch, coda, h), h
 
 
@@ -408,6 +473,8 @@ def run_case(case, torch, coda, steps, warmup, unfused):
             res["unfused_fwd_ms"] = time_steps(torch, lambda: _Steps.unfused_fwd(case), steps, 1)
             res["unfused_bwd_ms"] = time_steps(torch, lambda: _Steps.unfused_bwd(case), steps, 1)
         res["unfused_blas"] = str(torch.backends.cuda.preferred_blas_library())
+        if hasattr(case, "unfused_check"):
+            res["unfused_check_rel"] = case.unfused_check()
         del case.leaf, case.graph
     return res
 
@@ -424,6 +491,10 @@ def summary(case, res):
         out["unfused_ms_per_step"] = round(res["unfused_ms_per_step"], 4)
         out["speedup_vs_unfused"] = round(res["unfused_ms_per_step"] / res["ms_per_step"], 3)
         out["unfused_blas"] = res["unfused_blas"]
+        if "unfused_check_rel" in res:
+            out["unfused_first_gemm_vs_fused_y_rel"] = round(res["unfused_check_rel"], 5)
+    if case.w.kind == "mx8":
+        out["pct_fp8_peak"] = round(100.0 * tf / PEAK_FP8_TFLOPS, 2)
     for part, fl in (("fwd", case.w.flops_fwd()), ("bwd", case.w.flops_bwd())):
         if f"{part}_ms" in res:
             d = {"ms": round(res[f"{part}_ms"], 4),
@@ -549,7 +620,7 @@ def main():
     also = {}
     if not args.no_also:
         for name in ("llama70b_fwdbwd", "swiglu_fwdbwd", "llama7b_mlp_fwdbwd", "llama7b_ce_fwdbwd",
-                     "llama7b_qkv_rope_fwdbwd", "llama1b_fwd"):
+                     "llama7b_qkv_rope_fwdbwd", "llama7b_fwd_mx8", "llama1b_fwd"):
             w2 = synth.WORKLOADS[name]
             print(f"[bench] {name}: inputs + timing", file=sys.stderr, flush=True)
             c2, _ = make_case(w2, torch, coda)

@@ -36,6 +36,7 @@ __all__ = [
     "ce_fwd_workspace_bytes", "ce_bwd_workspace_bytes", "coda_rope_fwd", "coda_rope_bwd", "rope_fwd",
     "rope_bwd", "rope_fwd_workspace_bytes", "rope_bwd_workspace_bytes", "fwd_workspace_bytes", "bwd_workspace_bytes",
     "swiglu_bwd_workspace_bytes", "mlp_fwd_workspace_bytes", "mlp_bwd_workspace_bytes",
+    "coda_mx8_quantize", "coda_fwd_mx8", "mx8_quantize", "fwd_mx8", "fwd_mx8_workspace_bytes",
     "version", "trace_start", "trace_read", "trace_stop",
 ]
 
@@ -87,6 +88,7 @@ def load_library() -> ctypes.CDLL:
         "coda_ce_bwd_workspace_bytes": [i32, i64, i64, i64],
         "coda_rope_fwd_workspace_bytes": [i32, i64, i64, i64, i64, i64, i64],
         "coda_rope_bwd_workspace_bytes": [i32, i64, i64, i64, i64, i64, i64],
+        "coda_fwd_mx8_workspace_bytes": [i64, i64, i64, i64],
     }.items():
         getattr(L, name).restype = sz
         getattr(L, name).argtypes = args
@@ -110,6 +112,10 @@ def load_library() -> ctypes.CDLL:
     L.coda_rope_fwd.argtypes = [i32, i64, i64, i64, i64, i64, i64, f32] + [vp] * 3 + [vp, sz, vp]
     L.coda_rope_bwd.restype = i32
     L.coda_rope_bwd.argtypes = [i32, i64, i64, i64, i64, i64, i64, f32] + [vp] * 5 + [vp, sz, vp]
+    L.coda_mx8_quantize.restype = i32
+    L.coda_mx8_quantize.argtypes = [i64, i64, vp, i64, vp, vp, vp]
+    L.coda_fwd_mx8.restype = i32
+    L.coda_fwd_mx8.argtypes = [i64, i64, i64, i64, f32] + [vp] * 11 + [vp, sz, vp]
     L.coda_trace_start.restype = i32
     L.coda_trace_start.argtypes = [i32]
     L.coda_trace_count.restype = i32
@@ -206,6 +212,10 @@ def rope_bwd_workspace_bytes(dtype_code, M, K, N, N_rot, D, S) -> int:
 
 
 # ------------------------------------------------------------ tracing
+
+def fwd_mx8_workspace_bytes(M, K, d, N) -> int:
+    return int(load_library().coda_fwd_mx8_workspace_bytes(M, K, d, N))
+
 
 def trace_start(capacity: int) -> None:
     """Bracket every kernel launch with HIP events (see coda_trace_start)."""
@@ -336,7 +346,62 @@ def coda_rope_bwd(X, W, dY, N_rot, D, S, base, dX, dW, workspace):
         _ptr(workspace), workspace.numel(), _stream()))
 
 
+def _u8(t, name):
+    import torch
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name}: MXFP8 codes and scales are torch.uint8 tensors")
+    return _ptr(t)
+
+
+def coda_mx8_quantize(src, codes, scales):
+    """MXFP8 quantisation of the bf16 rows of src [rows, cols] into codes
+    [rows, cols] and scales [rows, cols/32] (uint8)."""
+    import torch
+    if src.dtype != torch.bfloat16:
+        raise TypeError("coda_mx8_quantize: src must be torch.bfloat16")
+    rows, cols = src.shape
+    _check("coda_mx8_quantize", load_library().coda_mx8_quantize(
+        rows, cols, _ptr(src), cols, _u8(codes, "codes"), _u8(scales, "scales"), _stream()))
+
+
+def coda_fwd_mx8(Xq, Xs, W1tq, W1ts, R, gamma, W2tq, W2ts, eps, y, r, z, workspace):
+    """coda_fwd_mx8 with caller-owned outputs y [M,d] (bf16), r [M] (fp32), z [M,N] (bf16)."""
+    M, K = Xq.shape
+    d, N = W1tq.shape[0], W2tq.shape[0]
+    _check("coda_fwd_mx8", load_library().coda_fwd_mx8(
+        M, K, d, N, float(eps), _u8(Xq, "Xq"), _u8(Xs, "Xs"), _u8(W1tq, "W1tq"), _u8(W1ts, "W1ts"),
+        _ptr(R), _ptr(gamma), _u8(W2tq, "W2tq"), _u8(W2ts, "W2ts"), _ptr(y), _ptr(r), _ptr(z),
+        _ptr(workspace), workspace.numel(), _stream()))
+
+
 # ------------------------------------------------------ convenience calls
+
+def mx8_quantize(src):
+    """MXFP8 codes and scales (uint8 tensors) of the bf16 rows of src."""
+    import torch
+    rows, cols = src.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=src.device)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=src.device)
+    coda_mx8_quantize(src, codes, scales)
+    return codes, scales
+
+
+def fwd_mx8(Xq, Xs, W1tq, W1ts, R, gamma, W2tq, W2ts, eps):
+    """The fused block forward on MXFP8 operands (weights stored [out, in]).
+    Returns (z, y, r)."""
+    import torch
+    M, K = Xq.shape
+    d, N = W1tq.shape[0], W2tq.shape[0]
+    _shape(Xs, M, K // 32, name="Xs"); _shape(W1tq, d, K, name="W1tq"); _shape(W1ts, d, K // 32, name="W1ts")
+    _shape(W2tq, N, d, name="W2tq"); _shape(W2ts, N, d // 32, name="W2ts")
+    _shape(R, M, d, name="R"); _shape(gamma, d, name="gamma")
+    y = torch.empty((M, d), dtype=torch.bfloat16, device=R.device)
+    r = torch.empty((M,), dtype=torch.float32, device=R.device)
+    z = torch.empty((M, N), dtype=torch.bfloat16, device=R.device)
+    ws = _workspace(fwd_mx8_workspace_bytes(M, K, d, N), R.device)
+    coda_fwd_mx8(Xq, Xs, W1tq, W1ts, R, gamma, W2tq, W2ts, eps, y, r, z, ws)
+    return z, y, r
+
 
 def fwd(X, W1, R, gamma, W2, eps):
     """z = RMSNorm(X W1 + R) * gamma @ W2, fused.  Returns (z, y, r)."""

@@ -217,6 +217,47 @@ hipError_t launch_norm_bwd(int64_t M, int64_t K, int64_t d, int64_t N, const voi
   });
 }
 
+// ------------------------------------------------------------- MXFP8
+bool mx_dim_ok(int64_t v, int64_t q) { return v >= q && v % q == 0 && v <= (int64_t)1 << 24; }
+bool fits(int64_t a, int64_t b, int64_t e) { return (uint64_t)a * (uint64_t)b * (uint64_t)e <= kMaxTensorBytes; }
+
+struct Mx8Ws {
+  size_t P, q, qs, total;
+  int Tn;
+};
+Mx8Ws mx8_ws(int64_t M, int64_t d) {
+  Mx8Ws w;
+  w.Tn = (int)cdiv(d, coda::kTileN);
+  w.P = 0;
+  w.q = round_up((size_t)M * w.Tn * 4);
+  w.qs = w.q + round_up((size_t)M * d);
+  w.total = w.qs + round_up((size_t)M * (d / 32));
+  return w;
+}
+
+// An MXFP8 GEMM C = A B with A [M][K] and B^T [N][K] (codes) and their scales.
+GemmArgs gemm_mx8(int64_t M, int64_t N, int64_t K, const void* Aq, const void* As, const void* Bq,
+                  const void* Bs, void* C, int64_t ldc) {
+  GemmArgs g{};
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.A = Aq;
+  g.lda = K;
+  g.A_bytes = (uint32_t)(M * K);
+  g.B = Bq;
+  g.ldb = K;
+  g.B_bytes = (uint32_t)(N * K);
+  g.sA = (const uint8_t*)As;
+  g.sB = (const uint8_t*)Bs;
+  g.sA_bytes = (uint32_t)(M * (K / 32));
+  g.sB_bytes = (uint32_t)(N * (K / 32));
+  g.ld_scale = K / 32;
+  g.C = C;
+  g.ldc = ldc;
+  return g;
+}
+
 }  // namespace
 
 extern "C" {
@@ -861,6 +902,87 @@ coda_status coda_rope_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t N, int
   GemmArgs q5 = gemm(K, N, M, X, K, M * K, dP, N, M * N, dW, N);
   return hip_status(traced("q5_gemm_dW", gemm_flops(K, N, M), mk + mn + kn, s, [&] {
     return coda::launch_gemm_bf16(q5, false, false, coda::EPI_STORE, s);
+  }));
+}
+
+coda_status coda_mx8_quantize(int64_t rows, int64_t cols, const void* src, int64_t ld_src,
+                              void* codes, void* scales, void* stream) {
+  if (!src || !codes || !scales) return CODA_ERR_NULL;
+  if (rows < 1 || !mx_dim_ok(cols, 32) || ld_src < cols || ld_src % 8 != 0 || rows > (int64_t)1 << 24)
+    return CODA_ERR_SHAPE;
+  if (!fits(rows, ld_src, 2) || !fits(rows, cols, 1)) return CODA_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(codes)) return CODA_ERR_ALIGN;
+  const Range in[] = {rng(src, ((rows - 1) * ld_src + cols) * 2)};
+  const Range out[] = {rng(codes, rows * cols), rng(scales, rows * (cols / 32))};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  return hip_status(traced("x0_mx8_quantize", 0.0, rows * cols * (3.0 + 1.0 / 32.0), s, [&] {
+    return coda::launch_mx8_quantize(src, ld_src, rows, cols, (uint8_t*)codes, (uint8_t*)scales, s);
+  }));
+}
+
+size_t coda_fwd_mx8_workspace_bytes(int64_t M, int64_t K, int64_t d, int64_t N) {
+  (void)K;
+  (void)N;
+  if (M < 1 || d < 32 || d % 32 != 0) return 0;
+  return mx8_ws(M, d).total;
+}
+
+coda_status coda_fwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, float eps, const void* Xq,
+                         const void* Xs, const void* W1tq, const void* W1ts, const void* R,
+                         const void* gamma, const void* W2tq, const void* W2ts, void* y, float* r,
+                         void* z, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!Xq || !Xs || !W1tq || !W1ts || !R || !gamma || !W2tq || !W2ts || !y || !r || !z)
+    return CODA_ERR_NULL;
+  if (!mx_dim_ok(M, 8) || !mx_dim_ok(N, 8) || !mx_dim_ok(K, 128) || !mx_dim_ok(d, 128))
+    return CODA_ERR_SHAPE;
+  if (!fits(M, K, 1) || !fits(d, K, 1) || !fits(N, d, 1) || !fits(M, d, 2) || !fits(M, N, 2))
+    return CODA_ERR_SHAPE;
+  if (!std::isfinite(eps) || !(eps > 0.0f)) return CODA_ERR_EPS;
+  for (const void* p : {Xq, Xs, W1tq, W1ts, R, gamma, W2tq, W2ts, (const void*)y, (const void*)r,
+                        (const void*)z})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  const Mx8Ws ws = mx8_ws(M, d);
+  if (!workspace || workspace_bytes < ws.total) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const Range in[] = {rng(Xq, M * K), rng(Xs, M * (K / 32)), rng(W1tq, d * K), rng(W1ts, d * (K / 32)),
+                      rng(R, M * d * 2), rng(gamma, d * 2), rng(W2tq, N * d), rng(W2ts, N * (d / 32))};
+  const Range out[] = {rng(y, M * d * 2), rng(r, M * 4), rng(z, M * N * 2), rng(workspace, ws.total)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)workspace;
+  float* P = (float*)(wsb + ws.P);
+  uint8_t* q = (uint8_t*)(wsb + ws.q);
+  uint8_t* qs = (uint8_t*)(wsb + ws.qs);
+  hipError_t err;
+  // K1: y = deq(X) deq(W1t)^T + R; epilogue: y (bf16), partial sums, y gamma as MXFP8
+  GemmArgs g1 = gemm_mx8(M, d, K, Xq, Xs, W1tq, W1ts, y, d);
+  g1.E = R;
+  g1.lde = d;
+  g1.part_row = P;
+  g1.ld_part_row = ws.Tn;
+  g1.vcol = gamma;
+  g1.q_out = q;
+  g1.qs_out = qs;
+  g1.ldq = d;
+  const double k1_bytes = (M + d) * K * (1.0 + 1.0 / 32.0) + 4.0 * M * d + M * d * (1.0 + 1.0 / 32.0) +
+                          M * ws.Tn * 4.0 + 2.0 * d;
+  if ((err = traced("k1_gemm_mx8_resid_sumsq", gemm_flops(M, d, K), k1_bytes, s, [&] {
+         return coda::launch_gemm_mx8(g1, coda::EPI_RESID_SUMSQ, s);
+       })) != hipSuccess)
+    return hip_status(err);
+  // K2: z = diag(r) (deq(q) deq(W2t)^T); r from the partial sums in the epilogue
+  GemmArgs g2 = gemm_mx8(M, N, d, q, qs, W2tq, W2ts, z, N);
+  g2.part_row = P;
+  g2.ld_part_row = ws.Tn;
+  g2.nparts = ws.Tn;
+  g2.inv_d = 1.0f / (float)d;
+  g2.eps = eps;
+  g2.r_out = r;
+  const double k2_bytes = (M + N) * d * (1.0 + 1.0 / 32.0) + 2.0 * M * N + M * ws.Tn * 4.0 + 4.0 * M;
+  return hip_status(traced("k2_gemm_mx8_rsqrt_rowscale", gemm_flops(M, N, d), k2_bytes, s, [&] {
+    return coda::launch_gemm_mx8(g2, coda::EPI_RSQRT_SCALE, s);
   }));
 }
 

@@ -159,6 +159,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, 
                : "v"(voff), "s"(rs), "s"(m0)
                : "memory", "m0");
 }
+// The same for 4 bytes per lane: lane l's dword lands at `dst` + 4 l.
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, lds_char* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)dst);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rs), "s"(m0)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Contraction index contiguous: the matrix is [MN rows][K].  Load p of wave w
@@ -279,6 +287,33 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 template <bool KMAJ, class KC, int NB>
 struct FragReader;
 
+// MXFP8 operand fragments of v_mfma_scale_f32_32x32x64_f8f6f4 (measured with
+// an in-bounds probe): lane l supplies row (or column) l%32 of a 32-wide block
+// and 32 E4M3 bytes of the sub-step's 64 k: bytes 0..15 from the first
+// 32-block of k, bytes 16..31 from the second, each the 16 k values 16(l/32)
+// .. +15 of that block.  Its scale operand covers (row l%32, k block l/32).
+// The tile is K-contiguous in LDS with the bf16 geometry (128-byte rows, one
+// row per 128 k), so the two halves are 16-byte chunks 4s + l/32 and
+// 4s + 2 + l/32 of sub-step s, read with ds_read_b128 each.
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+template <class KC>
+struct FragReaderMX {
+  int off0[2], off1[2];   // per sub-step s, for block 0; block i adds 32 rows
+  __device__ void init(int mn0, int lane) {
+    const int l32 = lane & 31, khalf = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      off0[s] = KC::kmaj_off(mn0 + l32, 4 * s + khalf);
+      off1[s] = KC::kmaj_off(mn0 + l32, 4 * s + 2 + khalf);
+    }
+  }
+  __device__ i32x8 read(const char* tile, int s, int i) const {
+    const i32x4 lo = *(const i32x4*)(tile + off0[s] + i * 32 * KC::KROW);
+    const i32x4 hi = *(const i32x4*)(tile + off1[s] + i * 32 * KC::KROW);
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+};
+
 // K-contiguous tile: one ds_read_b128 per fragment.
 template <class KC, int NB>
 struct FragReader<true, KC, NB> {
@@ -337,18 +372,28 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)
 __device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
 
 // ---------------------------------------------------------------------------
-// The bf16 MFMA GEMM: C[M,N] = A[M,K] B[K,N] (+ epilogue EPI)
+// The MFMA GEMM: C[M,N] = A[M,K] B[K,N] (+ epilogue EPI), operands in bf16
+// (FMT_BF16) or MXFP8 (FMT_MX8: E4M3 with an E8M0 scale per 32 k, both
+// operands K-contiguous, A [M][K] and B^T [N][K]).  One body serves both:
+// only the main loop differs.
 // ---------------------------------------------------------------------------
-template <int WMv, int WNv, int BKv, int NSTv, bool AK, bool BKM, int EPI>
-__global__ void __launch_bounds__(64 * WMv * WNv)
-    __attribute__((amdgpu_waves_per_eu(WMv * WNv / 4, WMv * WNv / 4)))
-gemm_bf16_kernel(GemmArgs g) {
+enum Fmt : int { FMT_BF16 = 0, FMT_MX8 = 1 };
+
+template <int FMT, int WMv, int WNv, int BKv, int NSTv, bool AK, bool BKM, int EPI>
+__device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   using G = Grid<WMv, WNv>;
   using KC = KCfg<BKv, NSTv>;
   constexpr int FM = G::FM, FN = G::FN, TM = G::TM, TN = G::TN;
   constexpr int BK = KC::BK, NSTAGE = KC::NSTAGE, OPER_BYTES = KC::OPER_BYTES;
   constexpr int STAGE_BYTES = KC::STAGE_BYTES;
-  __shared__ __attribute__((aligned(16))) char smem[KC::LDS_BYTES];
+  // MXFP8: the ring holds E4M3 tiles in the bf16 geometry (a 128-byte row is
+  // 128 k, so one K step of BK bf16 "units" is 2 BK k); each stage's scales,
+  // BM + BN rows x 4 bytes (the step's four 32-blocks), follow the ring
+  constexpr int SC_STAGE = (BM + BN) * 4;
+  constexpr int SMEM_BYTES = KC::LDS_BYTES + (FMT == FMT_MX8 ? NSTAGE * SC_STAGE : 0);
+  static_assert(FMT == FMT_BF16 || (AK && BKM && BK == 64), "MXFP8 operands are K-contiguous");
+  static_assert(SMEM_BYTES <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
   constexpr bool GATED = (EPI == EPI_SWIGLU || EPI == EPI_RSQRT_SWIGLU);
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6, wm = wave / WNv, wn = wave % WNv;
@@ -361,8 +406,10 @@ gemm_bf16_kernel(GemmArgs g) {
 
   typename LoaderSel<AK, KC, G::NT, false, TN>::type la;
   typename LoaderSel<BKM, KC, G::NT, GATED, TN>::type lb;
-  la.init(g.A, g.A_bytes, g.lda, row0, g.M, g.K, t, 0, tm);
-  lb.init(g.B, g.B_bytes, g.ldb, col0, g.N, g.K, t, g.F, tn);
+  // MXFP8: the loaders count in 2-byte units (K / 2, ld / 2)
+  constexpr int U = FMT == FMT_MX8 ? 2 : 1;
+  la.init(g.A, g.A_bytes, g.lda / U, row0, g.M, g.K / U, t, 0, tm);
+  lb.init(g.B, g.B_bytes, g.ldb / U, col0, g.N, g.K / U, t, g.F, tn);
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -370,6 +417,92 @@ gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
+  const int nk = (g.K / U + BK - 1) / BK;
+  lds_char* lsm = (lds_char*)smem;
+  constexpr int LPW = OPER_BYTES / 1024 / (G::NT / 64) * 2;   // loads per wave per step
+  constexpr int VM_NEXT = (NSTAGE - 2) * LPW;                 // loads allowed in flight
+  static_assert(VM_NEXT < 64, "vmcnt range");
+  static_assert(FMT == FMT_BF16 || VM_NEXT == 0, "MXFP8 waits for every load of the next step");
+  // s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 (7 and 15 = no wait)
+  constexpr int WAIT_NEXT = (VM_NEXT & 15) | ((VM_NEXT >> 4) << 14) | (7 << 4) | (15 << 8);
+  auto issue = [&](int step) {
+    lds_char* st = lsm + (step % NSTAGE) * STAGE_BYTES;
+    la.issue(st, step * BK);
+    lb.issue(st + OPER_BYTES, step * BK);
+  };
+
+  if constexpr (FMT == FMT_MX8) {
+    // Same pipeline as the bf16 loop below (two sub-steps of 64 k per K step
+    // of 128), plus the scales: each wave loads 64 rows' 4 scale bytes of the
+    // step (waves 0-3 A rows, 4-7 B rows) with one dword direct-to-LDS load,
+    // and every lane reads the words of its fragment rows after the barrier.
+    // The lane's byte for sub-step s is byte 2s + l/32 of its row's word; the
+    // word is shifted by 8 (l/32) so that op_sel 2s picks it.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const bool sc_a = wv < 4;
+    const int sc_row = (sc_a ? row0 : col0) + 64 * (wv & 3) + lane;
+    const bool sc_ok = sc_row < (sc_a ? g.M : g.N);
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(sc_a ? g.sA : g.sB, sc_a ? g.sA_bytes : g.sB_bytes);
+    const uint32_t sc_base = (uint32_t)sc_row * (uint32_t)g.ld_scale;
+    lds_char* const sc_lds = lsm + KC::LDS_BYTES + (sc_a ? 0 : BM * 4) + 64 * 4 * (wv & 3);
+    auto issue_scales = [&](int step) {
+      dma4(srs, (sc_ok && step < nk) ? sc_base + 4u * (uint32_t)step : OOB, sc_lds + (step % NSTAGE) * SC_STAGE);
+    };
+    const int l32 = lane & 31, sh = 8 * (lane >> 5);
+    auto read_scales = [&](int step, uint32_t (&sa)[FM], uint32_t (&sb)[FN]) {
+      const char* base = smem + KC::LDS_BYTES + (step % NSTAGE) * SC_STAGE;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sa[i] = *(const uint32_t*)(base + (wm * TM + 32 * i + l32) * 4) >> sh;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sb[j] = *(const uint32_t*)(base + BM * 4 + (wn * TN + 32 * j + l32) * 4) >> sh;
+    };
+    FragReaderMX<KC> fra, frb;
+    fra.init(wm * TM, lane);
+    frb.init(wn * TN, lane);
+    i32x8 fa[2][FM], fb[2][FN];
+    uint32_t sa[FM], sb[FN], san[FM], sbn[FN];
+    auto read_frags = [&](const char* stage, int s, i32x8 (&a)[FM], i32x8 (&b)[FN]) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) a[i] = fra.read(stage, s, i);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) b[j] = frb.read(stage + OPER_BYTES, s, j);
+    };
+    // B is the MFMA's first operand (C^T is accumulated), so its scale goes first
+#define CODA_MX_MFMAS(S, A_, B_)                                                                   \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                                 \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j)                                                 \
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(B_[j], A_[i], acc[i][j], 0, 0,   \
+                                                                  2 * (S), sb[j], 2 * (S), sa[i]);
+#pragma unroll
+    for (int st = 0; st < NSTAGE - 1; ++st) {
+      issue(st);
+      issue_scales(st);
+    }
+    __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
+    __syncthreads();
+    read_frags(smem, 0, fa[0], fb[0]);
+    read_scales(0, sa, sb);
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* sc = smem + (kt % NSTAGE) * STAGE_BYTES;
+      const char* sn = smem + ((kt + 1) % NSTAGE) * STAGE_BYTES;
+      issue(kt + NSTAGE - 1);
+      issue_scales(kt + NSTAGE - 1);
+      read_frags(sc, 1, fa[1], fb[1]);
+      CODA_MX_MFMAS(0, fa[0], fb[0])
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(WAIT_NEXT);   // this wave's loads of step kt+1 have landed
+      __syncthreads();
+      read_frags(sn, 0, fa[0], fb[0]);
+      read_scales(kt + 1, san, sbn);
+      CODA_MX_MFMAS(1, fa[1], fb[1])
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sa[i] = san[i];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sb[j] = sbn[j];
+    }
+#undef CODA_MX_MFMAS
+  } else {
   // Software pipeline over a ring of NSTAGE LDS stages (one K step = BK/16
   // MFMA sub-steps of 16):
   //   - the direct-to-LDS loads of step k+NSTAGE-1 are issued at the start of
@@ -382,19 +515,12 @@ gemm_bf16_kernel(GemmArgs g) {
   //     in LDS, and every wave is done reading step k-1's stage), and read
   //     step k+1's first fragments while the last MFMAs of step k run.
   // Fragments are double-buffered in registers.  Loads past K read zeros.
-  const int nk = (g.K + BK - 1) / BK;
   FragReader<AK, KC, FM> fra;
   FragReader<BKM, KC, FN> frb;
   fra.init(wm * TM, lane);
   frb.init(wn * TN, lane);
   bf16x8 fa[2][FM], fb[2][FN];
-  lds_char* lsm = (lds_char*)smem;
   constexpr int NSUB = BK / 16;
-  constexpr int LPW = OPER_BYTES / 1024 / (G::NT / 64) * 2;   // loads per wave per step
-  constexpr int VM_NEXT = (NSTAGE - 2) * LPW;                 // loads allowed in flight
-  static_assert(VM_NEXT < 64, "vmcnt range");
-  // s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 (7 and 15 = no wait)
-  constexpr int WAIT_NEXT = (VM_NEXT & 15) | ((VM_NEXT >> 4) << 14) | (7 << 4) | (15 << 8);
 
   auto read_frags = [&](const char* stage, int s, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
 #pragma unroll
@@ -408,11 +534,6 @@ gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-  };
-  auto issue = [&](int step) {
-    lds_char* st = lsm + (step % NSTAGE) * STAGE_BYTES;
-    la.issue(st, step * BK);
-    lb.issue(st + OPER_BYTES, step * BK);
   };
 
   // The compiler interleaves each sub-step's LDS reads and MFMAs; with two
@@ -440,6 +561,7 @@ gemm_bf16_kernel(GemmArgs g) {
     read_frags(sn, 0, fa[0], fb[0]);
     mfmas(fa[(NSUB - 1) & 1], fb[(NSUB - 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
+  }
   }
   __builtin_amdgcn_s_waitcnt(0);             // no load may still write into LDS
 
@@ -573,7 +695,8 @@ gemm_bf16_kernel(GemmArgs g) {
             lo += elo;
             hi += ehi;
             st8(C + o, lo, hi);
-            if (g.C2) {
+            if constexpr (FMT == FMT_MX8) {
+            } else if (g.C2) {
               if (g.c2_trans) {                         // y * gamma back into the region
                 *(f32x4*)(region + r * 256 + (((2 * c8) ^ (r & 15)) << 4)) = lo * glo;
                 *(f32x4*)(region + r * 256 + (((2 * c8 + 1) ^ (r & 15)) << 4)) = hi * ghi;
@@ -586,6 +709,32 @@ gemm_bf16_kernel(GemmArgs g) {
           }
           s = sum8(s);
           if (c8 == 0) red[wn * BM + lrow_t] = s;
+          if constexpr (FMT == FMT_MX8) {
+            // y * gamma to MXFP8: the 4 lanes c8 = 4b..4b+3 hold one 32-column
+            // block of the row; shared exponent floor(log2 amax) - 8 (clamped
+            // at -127) from amax's exponent field, elements scaled by the
+            // exact power of two, saturated at 448 and rounded to nearest
+            // even by the hardware conversion
+            f32x4 vlo = lo * glo, vhi = hi * ghi;
+            float am = 0.0f;
+            if (ok) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) am = fmaxf(am, fmaxf(fabsf(vlo[e]), fabsf(vhi[e])));
+            }
+            am = fmaxf(am, __shfl_xor(am, 1));
+            am = fmaxf(am, __shfl_xor(am, 2));
+            const int sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
+            const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
+            auto sat = [&](float v) { return fminf(fmaxf(v * inv, -448.0f), 448.0f); };
+            int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(vlo[0]), sat(vlo[1]), 0, false);
+            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(vlo[2]), sat(vlo[3]), w0, true);
+            int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(vhi[0]), sat(vhi[1]), 0, false);
+            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(vhi[2]), sat(vhi[3]), w1, true);
+            if (ok) {
+              *(uint2*)(g.q_out + (int64_t)row * g.ldq + gcol) = uint2{(uint32_t)w0, (uint32_t)w1};
+              if ((c8 & 3) == 0) g.qs_out[(int64_t)row * (g.ldq / 32) + gcol / 32] = (uint8_t)(sexp + 127);
+            }
+          }
         } else if constexpr (EPI == EPI_DN) {
           // dh = acc; dn = gamma dh (stored); row sum of dn*y; column sums of dh*r*y
           float s = 0.0f;
@@ -656,7 +805,7 @@ gemm_bf16_kernel(GemmArgs g) {
         // y * gamma transposed: C2[col][row].  In pass q, lanes 4c..4c+3 take
         // column 16q + c of the wave's 64 and rows 8(l%4)..+7 each, so one
         // store instruction writes 16 columns x 64 contiguous bytes.
-        if (g.C2 && g.c2_trans) {
+        if (FMT == FMT_BF16 && g.C2 && g.c2_trans) {
           __builtin_amdgcn_s_waitcnt(0xc07f);         // this wave's LDS writes are done
           const int rg = 8 * (lane & 3);
 #pragma unroll
@@ -773,6 +922,63 @@ gemm_bf16_kernel(GemmArgs g) {
           st8(Aout + (int64_t)row * g.ldc2 + jj, a0, a1);
         }
       }
+    }
+  }
+}
+
+template <int WMv, int WNv, int BKv, int NSTv, bool AK, bool BKM, int EPI>
+__global__ void __launch_bounds__(64 * WMv * WNv)
+    __attribute__((amdgpu_waves_per_eu(WMv * WNv / 4, WMv * WNv / 4)))
+gemm_bf16_kernel(GemmArgs g) {
+  gemm_body<FMT_BF16, WMv, WNv, BKv, NSTv, AK, BKM, EPI>(g);
+}
+
+template <int WMv, int WNv, int EPI>
+__global__ void __launch_bounds__(64 * WMv * WNv)
+    __attribute__((amdgpu_waves_per_eu(WMv * WNv / 4, WMv * WNv / 4)))
+gemm_mx8_kernel(GemmArgs g) {
+  gemm_body<FMT_MX8, WMv, WNv, 64, 2, true, true, EPI>(g);
+}
+
+// bf16 rows -> MXFP8 along the row.  A lane takes 8 consecutive elements
+// (one 16-byte load), 4 lanes one 32-block: shared exponent and element
+// rounding as in the first GEMM's epilogue.  Grid-stride over 8-element groups.
+__global__ void mx8_quantize_kernel(const __bf16* __restrict__ src, int64_t ld, int64_t rows,
+                                    int64_t cols, uint8_t* __restrict__ codes,
+                                    uint8_t* __restrict__ scales) {
+  const int64_t groups_per_row = cols / 8;
+  const int64_t total = rows * groups_per_row;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // every lane of a wave runs the same number of iterations (the loop bound is
+  // rounded up to whole waves) so that the shuffles see the whole wave
+  const int64_t base0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t iters = (total + stride - 1) / stride;
+  for (int64_t it = 0; it < iters; ++it) {
+    const int64_t gi = base0 + it * stride;
+    const bool ok = gi < total;
+    const int64_t row = ok ? gi / groups_per_row : 0;
+    const int64_t col = ok ? (gi % groups_per_row) * 8 : 0;
+    f32x4 lo{0.f, 0.f, 0.f, 0.f}, hi{0.f, 0.f, 0.f, 0.f};
+    if (ok) {
+      const bf16x8 v = *(const bf16x8*)(src + row * ld + col);
+      lo = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+      hi = f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) am = fmaxf(am, fmaxf(fabsf(lo[e]), fabsf(hi[e])));
+    am = fmaxf(am, __shfl_xor(am, 1));
+    am = fmaxf(am, __shfl_xor(am, 2));
+    const int sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
+    const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
+    auto sat = [&](float v) { return fminf(fmaxf(v * inv, -448.0f), 448.0f); };
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[0]), sat(lo[1]), 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[2]), sat(lo[3]), w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[0]), sat(hi[1]), 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[2]), sat(hi[3]), w1, true);
+    if (ok) {
+      *(uint2*)(codes + row * cols + col) = uint2{(uint32_t)w0, (uint32_t)w1};
+      if ((col & 31) == 0) scales[row * (cols / 32) + col / 32] = (uint8_t)(sexp + 127);
     }
   }
 }
@@ -974,6 +1180,34 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStr
     }
   }
   return hipErrorInvalidValue;
+}
+
+template <int EPI>
+static hipError_t launch_mx8_one(const GemmArgs& g, hipStream_t s) {
+  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_mx8_kernel<kWavesM, kWavesN, EPI>), dim3(tiles),
+                     dim3(64 * kWavesM * kWavesN), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mx8(const GemmArgs& g, Epi epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE: return launch_mx8_one<EPI_STORE>(g, s);
+    case EPI_RESID_SUMSQ: return launch_mx8_one<EPI_RESID_SUMSQ>(g, s);
+    case EPI_RSQRT_SCALE: return launch_mx8_one<EPI_RSQRT_SCALE>(g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_mx8_quantize(const void* src, int64_t ld, int64_t rows, int64_t cols,
+                               uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  // 32 groups of 8 per 256-thread block; the lanes of a 32-block stay in one
+  // wave because cols is a multiple of 32
+  const int64_t total = rows * (cols / 8);
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 256 * 16);
+  hipLaunchKernelGGL(mx8_quantize_kernel, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, s,
+                     (const __bf16*)src, ld, rows, cols, codes, scales);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_f32(const GemmArgs& g, Epi epi, hipStream_t s) {

@@ -6,7 +6,7 @@
 
 namespace coda {
 
-// Output tile of the bf16 MFMA GEMM kernels and of the fp32 fallback kernel.
+// Output tile of the MFMA GEMM kernels (bf16 and MXFP8) and of the fp32 fallback kernel.
 // The partial-sum workspaces are laid out per tile, so the C-ABI sizes them
 // from these constants.
 constexpr int kTileM = 256;
@@ -55,6 +55,14 @@ struct GemmArgs {
   const float* rope_tab; int rope_rot, rope_head, rope_seq;   // EPI_ROPE: tab = [cos | sin],
                                                                // each [rope_seq][rope_head / 2]
   uint32_t A_bytes, B_bytes;     // buffer extents for hardware bounds checks
+  // MXFP8 GEMMs (launch_gemm_mx8): A is [M][K] and B is given as B^T [N][K],
+  // both E4M3 bytes with lda / ldb in bytes; their E8M0 scales are [M][K/32]
+  // and [N][K/32], ld_scale bytes per row
+  const uint8_t* sA; const uint8_t* sB;
+  uint32_t sA_bytes, sB_bytes; int64_t ld_scale;
+  // EPI_RESID_SUMSQ in an MXFP8 GEMM: y * vcol quantised to MXFP8 along the
+  // row, codes [M][ldq] and scales [M][ldq / 32] (instead of C2)
+  uint8_t* q_out; uint8_t* qs_out; int64_t ldq;
 };
 
 // Launchers: enqueue on `stream`, return the hipGetLastError() after launch.
@@ -63,6 +71,13 @@ struct GemmArgs {
 hipError_t launch_gemm_bf16(const GemmArgs& g, bool a_kmajor, bool b_kmajor, Epi epi,
                             hipStream_t stream);
 hipError_t launch_gemm_f32(const GemmArgs& g, Epi epi, hipStream_t stream);
+// MXFP8 x MXFP8 GEMM, both operands K-contiguous (A [M][K], B^T [N][K]);
+// K % 128 == 0; epilogues EPI_STORE, EPI_RESID_SUMSQ (with q_out), EPI_RSQRT_SCALE
+hipError_t launch_gemm_mx8(const GemmArgs& g, Epi epi, hipStream_t stream);
+// codes / scales = the MXFP8 quantisation of the bf16 rows of src along the
+// row (cols % 32 == 0; codes [rows][cols], scales [rows][cols / 32])
+hipError_t launch_mx8_quantize(const void* src, int64_t ld, int64_t rows, int64_t cols,
+                               uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 // r[i] = (sum_t P[i][t] / d + eps)^(-1/2)
 hipError_t launch_row_rsqrt(const float* P, int64_t ldp, int T, int64_t M, int64_t d, float eps,

@@ -28,9 +28,10 @@ class Workload:
 
     name: str
     kind: str            # "coda" (GEMM-Residual-RMSNorm-GEMM), "swiglu", "mlp" (the two
-                         # chained), "ce" (LM-head GEMM + cross-entropy) or "rope"
-                         # (QKV projection with rotary positions in its epilogue)
-    dtype: str           # "f32" or "bf16"
+                         # chained), "ce" (LM-head GEMM + cross-entropy), "rope"
+                         # (QKV projection with rotary positions in its epilogue) or
+                         # "mx8" (the coda block's forward on MXFP8 operands)
+    dtype: str           # "f32", "bf16" or "mxfp8" (bf16 draws, quantised by the caller)
     M: int
     K: int = 0           # coda, mlp: GEMM1 reduction width
     d: int = 0           # coda, mlp: normalised width; swiglu: model width
@@ -47,7 +48,7 @@ class Workload:
 
     def flops_fwd(self) -> float:
         """Algorithmic GEMM flops of the forward pass (elementwise work excluded)."""
-        if self.kind == "coda":
+        if self.kind in ("coda", "mx8"):
             return 2.0 * self.M * (self.K * self.d + self.d * self.N)
         if self.kind == "ce":
             return 2.0 * self.M * self.d * self.N
@@ -93,6 +94,10 @@ WORKLOADS = {
                  rot=8192, head=128, seq=4096, base=10000.0, seed=1007, backward=True,
                  note="LLaMA-7B-shaped QKV projection with rotary positions on q and k "
                       "(two 4096-token sequences), forward+backward"),
+        Workload("llama7b_fwd_mx8", "mx8", "mxfp8", M=8192, K=4096, d=4096, N=11008,
+                 eps=1e-6, seed=1008, backward=False,
+                 note="LLaMA-7B-shaped block forward with MXFP8 operands (weights "
+                      "stored [out, in])"),
     ]
 }
 
@@ -194,6 +199,15 @@ def rope_inputs(M: int, K: int, N: int, seed: int, dtype: str = "bf16", with_dz:
     return {k: _quantise(v, dtype) for k, v in out.items()}
 
 
+def mx8_inputs(M: int, K: int, d: int, N: int, seed: int) -> dict:
+    """The draws of ``coda_inputs`` (bf16) with the weights transposed to
+    [out, in], the layout an MXFP8 weight is quantised from (blocks run along
+    the contraction index).  The quantisation itself is the caller's."""
+    h = coda_inputs(M, K, d, N, seed, "bf16", with_dz=False)
+    return {"X": h["X"], "R": h["R"], "gamma": h["gamma"],
+            "W1t": np.ascontiguousarray(h["W1"].T), "W2t": np.ascontiguousarray(h["W2"].T)}
+
+
 def workload_inputs(w: Workload, with_dz: bool | None = None) -> dict:
     """Inputs of a named workload (dz only when it has a backward pass)."""
     if with_dz is None:
@@ -206,4 +220,6 @@ def workload_inputs(w: Workload, with_dz: bool | None = None) -> dict:
         return ce_inputs(w.M, w.d, w.N, w.seed, w.dtype, with_dz)
     if w.kind == "rope":
         return rope_inputs(w.M, w.K, w.N, w.seed, w.dtype, with_dz)
+    if w.kind == "mx8":
+        return mx8_inputs(w.M, w.K, w.d, w.N, w.seed)
     return swiglu_inputs(w.M, w.d, w.F, w.seed, w.dtype, with_dz)

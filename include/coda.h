@@ -303,6 +303,59 @@ coda_status coda_rope_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t N, int
                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * MXFP8 forward of the GEMM-Residual-RMSNorm-GEMM block, and the quantiser
+ * that makes its operands.  The pages note that faster FP8 / FP4 matrix
+ * units raise the relative cost of the memory-bound work around a GEMM ([JA]
+ * 課題：大モデル訓練の「手抜き税」, [RU] "Налог на лень при обучении больших
+ * моделей", [FR] "Le « impôt de la paresse » ...") but fix no format.  The
+ * format here is OCP MXFP8: E4M3 elements (bias 7, largest finite 448, no
+ * infinities) and one E8M0 scale byte s (value 2^(s-127)) per 32 consecutive
+ * elements along the GEMM's contraction index.
+ *
+ * Quantisation of a 32-block (coda_mx8_quantize, and y * gamma inside
+ * coda_fwd_mx8): shared exponent e = floor(log2(max |v|)) - 8, clamped to
+ * [-127, 127] (-127 for an all-zero block); scale byte e + 127; each element
+ * v / 2^e rounded to the nearest E4M3 value, ties to even, saturated to
+ * +-448.
+ *
+ * coda_mx8_quantize: src [rows, cols] bf16 with row stride ld_src elements
+ *   (ld_src >= cols, a multiple of 8, src 16-byte aligned) -> codes [rows,
+ *   cols] E4M3 bytes (contiguous, 16-byte aligned) and scales [rows, cols/32]
+ *   E8M0 bytes (contiguous).  cols a multiple of 32, rows >= 1.  Blocks run
+ *   along each row, so a weight W [in, out] is quantised from its transpose
+ *   [out, in].  Errors: CODA_ERR_NULL, CODA_ERR_SHAPE, CODA_ERR_ALIGN,
+ *   CODA_ERR_ALIAS (codes or scales overlapping src or each other).
+ *
+ * coda_fwd_mx8 computes, with deq() the MXFP8 value of codes and scales:
+ *   y = deq(X) deq(W1t)^T + R;   r_i = (mean_j y_ij^2 + eps)^(-1/2);
+ *   (q, qs) = MXFP8(y diag(gamma))  (first GEMM's epilogue, blocks along d);
+ *   z = diag(r) (deq(q, qs) deq(W2t)^T)   (r in the second GEMM's epilogue).
+ * The rewrite of coda_fwd with both GEMMs on the MXFP8 matrix cores; what is
+ * quantised for the second GEMM is y * gamma (the tensor the first GEMM's
+ * epilogue holds), not the normalised RMSNorm(y) * gamma.
+ *
+ *   Xq   [M,K] E4M3 in    Xs  [M,K/32] E8M0 in
+ *   W1tq [d,K] E4M3 in    W1ts [d,K/32] in     (W1 stored [out, in])
+ *   W2tq [N,d] E4M3 in    W2ts [N,d/32] in     (W2 stored [out, in])
+ *   R [M,d] bf16 in, gamma [d] bf16 in
+ *   y [M,d] bf16 out (saved for coda_bwd), r [M] float32 out, z [M,N] bf16 out
+ *   M, N: >= 8 and multiples of 8; K, d: >= 128 and multiples of 128 (whole
+ *   K steps of the MXFP8 main loop), else CODA_ERR_SHAPE.  Every pointer
+ *   16-byte aligned.  eps > 0 and finite.
+ *   workspace: >= coda_fwd_mx8_workspace_bytes(M, K, d, N) bytes: the partial
+ *   sums [M, ceil(d/256)] fp32, then q [M, d] E4M3 at the next 256-byte
+ *   boundary, then qs [M, d/32] E8M0 at the next 256-byte boundary.
+ * The backward is coda_bwd (bf16) on the saved y and r.
+ * ---------------------------------------------------------------------- */
+coda_status coda_mx8_quantize(int64_t rows, int64_t cols, const void* src, int64_t ld_src,
+                              void* codes, void* scales, void* stream);
+size_t coda_fwd_mx8_workspace_bytes(int64_t M, int64_t K, int64_t d, int64_t N);
+coda_status coda_fwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, float eps, const void* Xq,
+                         const void* Xs, const void* W1tq, const void* W1ts, const void* R,
+                         const void* gamma, const void* W2tq, const void* W2ts, void* y, float* r,
+                         void* z, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Kernel tracing (measurement aid; off by default).
  *
  * coda_trace_start(capacity) creates 2*capacity timing events (host call,

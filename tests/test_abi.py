@@ -287,3 +287,38 @@ def test_rope_rejects(L):
     assert nb >= need + M * N * 2
     assert L.coda_rope_bwd(BF16, M, K, N, 64, 32, 16, 10000.0, X, W, dY, dX, dW, ws, nb - 16, None) == WORKSPACE
     assert L.coda_rope_bwd(BF16, M, K, N, 64, 32, 16, 10000.0, X, W, dY, dX, X, ws, nb, None) == ALIAS
+
+
+def test_mx8_rejects(L):
+    m = FakeMem()
+    M, K, d, N = 64, 256, 384, 96
+    Xq, Xs = m(M * K), m(M * K // 32)
+    W1q, W1s = m(d * K), m(d * K // 32)
+    W2q, W2s = m(N * d), m(N * d // 32)
+    R, g, y, r, z = m(M * d * 2), m(d * 2), m(M * d * 2), m(M * 4), m(M * N * 2)
+    need = L.coda_fwd_mx8_workspace_bytes(M, K, d, N)
+    # partial sums, codes and scales of y * gamma
+    assert need >= M * 2 * 4 + M * d + M * d // 32
+    ws = m(need)
+
+    def fwd(**o):
+        a = dict(M=M, K=K, d=d, N=N, eps=1e-6, Xq=Xq, R=R, y=y, z=z, ws_bytes=need)
+        a.update(o)
+        return L.coda_fwd_mx8(a["M"], a["K"], a["d"], a["N"], a["eps"], a["Xq"], Xs, W1q, W1s, a["R"], g,
+                              W2q, W2s, a["y"], r, a["z"], ws, a["ws_bytes"], None)
+    assert fwd(K=200) == SHAPE           # K not whole steps of 128
+    assert fwd(d=320) == SHAPE           # d not whole steps of 128
+    assert fwd(M=60) == SHAPE
+    assert fwd(N=0) == SHAPE
+    assert fwd(eps=0.0) == EPS
+    assert fwd(ws_bytes=need - 1) == WORKSPACE
+    assert fwd(Xq=None) == NULL
+    assert fwd(y=R) == ALIAS
+    assert fwd(z=ctypes.c_void_p(z.value + 8)) == ALIGN
+    q_src, q_codes, q_scales = m(M * K * 2), m(M * K), m(M * K // 32)
+    assert L.coda_mx8_quantize(M, 48, q_src, 48, q_codes, q_scales, None) == SHAPE
+    assert L.coda_mx8_quantize(M, K, q_src, K - 8, q_codes, q_scales, None) == SHAPE
+    assert L.coda_mx8_quantize(0, K, q_src, K, q_codes, q_scales, None) == SHAPE
+    assert L.coda_mx8_quantize(M, K, q_src, K, q_src, q_scales, None) == ALIAS
+    assert L.coda_mx8_quantize(M, K, None, K, q_codes, q_scales, None) == NULL
+    assert L.coda_mx8_quantize(M, K, ctypes.c_void_p(q_src.value + 4), K, q_codes, q_scales, None) == ALIGN

@@ -1,0 +1,233 @@
+"""GPU parity of the MXFP8 path through the C-ABI against the CPU oracle.
+
+The oracle quantises the inputs (bf16 draws) to MXFP8 on the host; both sides
+then start from the same codes and scales.
+
+Bars:
+  * the quantiser (bf16 -> MXFP8): bit-exact codes and scales (a bf16 value,
+    its block maximum and the power-of-two scaling are exact in fp32 and in
+    float64, so both sides round the same value);
+  * y, z: max|gpu - ref| / max|ref| <= 2e-2 (bf16 outputs, fp32 accumulation);
+    r per element |dr|/r <= 1e-3;
+  * y * gamma quantised in the first GEMM's epilogue: the value rounded there
+    is the kernel's fp32 y, accumulated by the MXFP8 matrix instruction with
+    reduced precision, while the oracle's is exact, so a code may differ where
+    the exact value lies near a rounding boundary.  Required: every GPU value
+    is the correct rounding (under the GPU's scale) of a value within a slack
+    of the exact one (the slack bounds the accumulation error, see
+    ``accumulation_slack``); a scale differs from the oracle's only where the
+    block's exact maximum lies within that slack of a power of two; at most
+    1e-2 of the codes and scales differ.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gemm_epilogue_fusion_gemm1_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+R_TOL = 1e-3
+FLIP_FRAC = 1e-2
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    coda.load_library()       # raises when the HIP library is missing: no fallback
+    return torch, torch.device("cuda:0")
+
+
+def rel(got, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    den = float(np.max(np.abs(ref))) if ref.size else 1.0
+    return float(np.max(np.abs(got - ref))) / max(den, 1e-300)
+
+
+def report(name, errs):
+    print(f"[parity] {name}: " + ", ".join(f"{k}={v:.2e}" if isinstance(v, float) else f"{k}={v}"
+                                          for k, v in errs.items()), flush=True)
+
+
+def u8(torch, dev, a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(dev)
+
+
+def bf(torch, dev, a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(torch.bfloat16)
+
+
+def quantised(h):
+    Xq, Xs = oracle.mx_quantize(h["X"])
+    W1q, W1s = oracle.mx_quantize(h["W1t"])
+    W2q, W2s = oracle.mx_quantize(h["W2t"])
+    return dict(Xq=Xq, Xs=Xs, W1q=W1q, W1s=W1s, W2q=W2q, W2s=W2s)
+
+
+def run_fwd(torch, dev, h, q, eps):
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    M, K = h["X"].shape
+    d, N = h["W1t"].shape[0], h["W2t"].shape[0]
+    y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    r = torch.empty((M,), dtype=torch.float32, device=dev)
+    z = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    nb = coda.fwd_mx8_workspace_bytes(M, K, d, N)
+    ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
+    coda.coda_fwd_mx8(u8(torch, dev, q["Xq"]), u8(torch, dev, q["Xs"]), u8(torch, dev, q["W1q"]),
+                      u8(torch, dev, q["W1s"]), bf(torch, dev, h["R"]), bf(torch, dev, h["gamma"]),
+                      u8(torch, dev, q["W2q"]), u8(torch, dev, q["W2s"]), eps, y, r, z, ws)
+    torch.cuda.synchronize()
+    # workspace layout (coda.h): partial sums, then q [M, d], then qs [M, d/32],
+    # each at a 256-byte boundary
+    def ru(x):
+        return (x + 255) // 256 * 256
+    off_q = ru(M * ((d + 255) // 256) * 4)
+    off_qs = off_q + ru(M * d)
+    w = ws.cpu().numpy()
+    yq = w[off_q:off_q + M * d].reshape(M, d)
+    ys = w[off_qs:off_qs + M * (d // 32)].reshape(M, d // 32)
+    return y.float().cpu().numpy(), r.cpu().numpy(), z.float().cpu().numpy(), yq, ys
+
+
+def accumulation_slack(Xq, Xs, W1q, W1s, gamma):
+    """Per element (i, j) of y*gamma, the deviation allowed between the
+    kernel's fp32 value and the exact one: 2^-10 times the sum, over the 64-k
+    groups of one MFMA instruction, of the group's largest |X_ik W1_jk|, times
+    |gamma_j|.  The MXFP8 matrix instruction sums its 64 products with
+    reduced precision (an in-bounds probe measured up to 2^-12.6 of the
+    largest product per instruction), so this is 4x that measurement."""
+    X = oracle.mx_dequantize(Xq, Xs)
+    W = oracle.mx_dequantize(W1q, W1s)
+    rows, K = X.shape
+    d = W.shape[0]
+    out = np.empty((rows, d))
+    Wg = np.abs(W).reshape(d, K // 64, 64)
+    for i in range(rows):
+        prod = np.abs(X[i]).reshape(1, K // 64, 64) * Wg          # [d, groups, 64]
+        out[i] = prod.max(axis=2).sum(axis=1)
+    return 2.0 ** -10 * out * np.abs(np.asarray(gamma, dtype=np.float64))[None, :]
+
+
+def check_quantised_yg(name, yq, ys, ref, slack):
+    """Codes and scales of y*gamma against the exact value (see the module
+    docstring).  Each GPU element must be a correct rounding (under the GPU's
+    scale) of a value within `slack` of the exact y*gamma; a scale may differ
+    from the oracle's only where the exact block maximum is within the block's
+    slack of a power of two; at most 1e-2 of the codes may differ."""
+    ora_q, ora_s, yg = ref["yg_q"], ref["yg_s"], ref["yg"]
+    rows, d = yg.shape
+    amax = np.max(np.abs(yg.reshape(rows, d // 32, 32)), axis=2)
+    bslack = np.max(slack.reshape(rows, d // 32, 32), axis=2)
+    p2 = np.exp2(np.round(np.log2(np.maximum(amax, 1e-300))))
+    s_diff = ys != ora_s
+    assert np.all(np.abs(amax - p2)[s_diff] <= bslack[s_diff]), \
+        f"{name}: a scale differs away from a power-of-two boundary"
+    sc = np.repeat(oracle.e8m0_decode(ys), 32, axis=1)
+    got = oracle.e4m3_decode(yq) * sc
+    u = np.abs(yg) / sc
+    half_step = 0.5 * np.where(u >= 2.0 ** -6, np.exp2(np.floor(np.log2(np.maximum(u, 2.0 ** -6))) - 3),
+                               2.0 ** -9) * sc
+    err = np.abs(got - yg)
+    sat = (u > 448.0) & (np.abs(got) == 448.0 * sc) & (np.sign(got) == np.sign(yg))
+    ok = (err <= half_step * (1 + 1e-9) + slack) | sat
+    if not ok.all():
+        i, j = (int(v) for v in np.argwhere(~ok)[0])
+        raise AssertionError(
+            f"{name}: {int((~ok).sum())} codes are not a rounding of a value within the slack; first at "
+            f"({i},{j}): exact {yg[i, j]!r}, gpu code {int(yq[i, j]):#x} -> {got[i, j]!r}, oracle code "
+            f"{int(ora_q[i, j]):#x}, scale byte {int(ys[i, j // 32])}, slack {slack[i, j]:.3e}")
+    nf_c, nf_s = float((yq != ora_q).mean()), float(s_diff.mean())
+    assert nf_c <= FLIP_FRAC and nf_s <= FLIP_FRAC, (nf_c, nf_s)
+    return nf_c, nf_s
+
+
+# --------------------------------------------------------------- quantiser
+
+def _quant_cases():
+    g = np.random.default_rng(7)
+    a = (g.standard_normal((300, 1056)) * np.exp2(g.integers(-20, 20, (300, 1)))).astype(np.float32)
+    a[3, :64] = 0.0                                   # all-zero blocks
+    a[4, :32] = -0.0
+    a[5, :32] = 1e-39                                 # fp32-subnormal block maximum
+    a[6, 7] = 3.0e38                                  # largest exponents
+    a[7, :32] = np.linspace(-470, 470, 32)            # saturating elements under scale 1
+    a[8, :32] = 2.0 ** -133                           # the smallest bf16 subnormal
+    return [("ragged", synth.round_to_bf16(a)),
+            ("one_block", synth.round_to_bf16(g.standard_normal((7, 32)).astype(np.float32))),
+            ("wide", synth.round_to_bf16(g.standard_normal((64, 4096)).astype(np.float32)))]
+
+
+@pytest.mark.parametrize("case", _quant_cases(), ids=lambda c: c[0])
+def test_mx8_quantize_bit_exact(torch_dev, case):
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    name, a = case
+    codes, scales = coda.mx8_quantize(bf(torch, dev, a))
+    torch.cuda.synchronize()
+    oq, os_ = oracle.mx_quantize(a.astype(np.float64))
+    gq, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    nq, ns = int((gq != oq).sum()), int((gs != os_).sum())
+    report(f"mx8 quantize {name} {a.shape}", {"code_mismatches": nq, "scale_mismatches": ns})
+    assert ns == 0 and nq == 0
+
+
+# --------------------------------------------------------------- the block
+
+SMALL_MX8 = [
+    # M, K, d, N
+    (520, 256, 384, 776),       # 3 x 2 x 4 tiles, M and N ragged, d a partial tile
+    (8, 128, 128, 8),           # smallest accepted
+    (256, 256, 256, 256),       # exactly one tile
+    (264, 1152, 128, 40),       # long K loop, narrow d and N
+    (768, 512, 1024, 520),      # several full tiles, 4 partials per row
+]
+
+
+@pytest.mark.parametrize("shape", SMALL_MX8, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_mx8(torch_dev, shape):
+    torch, dev = torch_dev
+    M, K, d, N = shape
+    eps = 1e-6
+    h = synth.mx8_inputs(M, K, d, N, seed=300 + M + K)
+    q = quantised(h)
+    y, r, z, yq, ys = run_fwd(torch, dev, h, q, eps)
+    f = oracle.ref_fwd_mx8(q["Xq"], q["Xs"], q["W1q"], q["W1s"], h["R"], h["gamma"], q["W2q"], q["W2s"], eps)
+    errs = {"y": rel(y, f["y"]), "z": rel(z, f["z"]),
+            "r": float(np.max(np.abs(r - f["r"]) / f["r"]))}
+    report(f"mx8 fwd {shape} (before the code check)", errs)
+    slack = accumulation_slack(q["Xq"], q["Xs"], q["W1q"], q["W1s"], h["gamma"])
+    nf_c, nf_s = check_quantised_yg(f"mx8 {shape}", yq, ys, f, slack)
+    report(f"mx8 fwd {shape}", {**errs, "yg_code_flips": nf_c, "yg_scale_flips": nf_s})
+    assert errs["y"] <= BF16_TOL and errs["z"] <= BF16_TOL and errs["r"] <= R_TOL
+
+
+def test_full_workload_mx8(torch_dev):
+    """LLaMA-7B-shaped block forward on MXFP8 operands, in the launch
+    configuration the benchmark times: y, r, z and the quantised y*gamma on
+    sampled rows (r for every row); the quantiser checked bit-exact on X."""
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    w = synth.WORKLOADS["llama7b_fwd_mx8"]
+    h = synth.workload_inputs(w)
+    q = quantised(h)
+    gq, gs = coda.mx8_quantize(bf(torch, dev, h["X"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(gq.cpu().numpy(), q["Xq"]) and np.array_equal(gs.cpu().numpy(), q["Xs"])
+    del gq, gs
+    y, r, z, yq, ys = run_fwd(torch, dev, h, q, w.eps)
+    rows = np.unique(np.concatenate([np.arange(0, w.M, 173), [w.M - 1]]))
+    f = oracle.ref_fwd_mx8_rows(q["Xq"], q["Xs"], q["W1q"], q["W1s"], h["R"], h["gamma"], q["W2q"],
+                                q["W2s"], w.eps, rows)
+    errs = {"y_rows": rel(y[rows], f["y"]), "z_rows": rel(z[rows], f["z"]),
+            "r_rows": float(np.max(np.abs(r[rows] - f["r"]) / f["r"]))}
+    report(f"{w.name} (before the code check)", errs)
+    slack = accumulation_slack(q["Xq"][rows], q["Xs"][rows], q["W1q"], q["W1s"], h["gamma"])
+    nf_c, nf_s = check_quantised_yg("mx8 7B rows", yq[rows], ys[rows], f, slack)
+    report(w.name, {**errs, "yg_code_flips": nf_c, "yg_scale_flips": nf_s})
+    assert errs["y_rows"] <= BF16_TOL and errs["z_rows"] <= BF16_TOL and errs["r_rows"] <= R_TOL
+    assert np.all(np.isfinite(z)) and np.all(r > 0)
