@@ -299,6 +299,7 @@ class Mx8Case:
         for k in ("X", "W1t", "W2t"):
             self.q[k] = coda.mx8_quantize(self.t[k])
         torch.cuda.synchronize()
+        self._rowmajor = {}
         self.y = torch.empty((M, d), dtype=bf, device=dev)
         self.r = torch.empty((M,), dtype=torch.float32, device=dev)
         self.z = torch.empty((M, N), dtype=bf, device=dev)
@@ -316,10 +317,16 @@ class Mx8Case:
                                q["W2t"][0], q["W2t"][1], self.w.eps, self.y, self.r, self.z, self.ws)
 
     def _mm(self, a, b):
-        """torch's MXFP8 product (hipBLASLt): a [m, k] codes and scales, b [n, k]."""
+        """torch's MXFP8 product (hipBLASLt): a [m, k] codes and row-major scales, b [n, k]."""
         f8, e8 = self.torch.float8_e4m3fn, self.torch.float8_e8m0fnu
         return self.torch._scaled_mm(a[0].view(f8), b[0].view(f8).t(), scale_a=a[1].view(e8),
                                      scale_b=b[1].view(e8), out_dtype=self.torch.bfloat16)
+
+    def _rm(self, name):
+        """The library-quantised operand with its scales row-major, as torch takes them."""
+        if name not in self._rowmajor:
+            self._rowmajor[name] = (self.q[name][0], self.coda.mx8_scales_to_rowmajor(self.q[name][1]))
+        return self._rowmajor[name]
 
     def _quantise(self, v):
         """MXFP8 quantisation as separate torch ops (amax per 32, exponent,
@@ -334,16 +341,16 @@ class Mx8Case:
 
     def unfused_fwd(self):
         F = self.torch.nn.functional
-        y = self._mm(self.q["X"], self.q["W1t"]) + self.t["R"]
+        y = self._mm(self._rm("X"), self._rm("W1t")) + self.t["R"]
         h = F.rms_norm(y, (self.w.d,), self.t["gamma"], self.w.eps)
-        return self._mm(self._quantise(h), self.q["W2t"])
+        return self._mm(self._quantise(h), self._rm("W2t"))
 
     def unfused_check(self):
         """Relative difference between torch's first MXFP8 product + R and the
         fused y (the same operands), to show the baseline computes the same
         product."""
         self.fused_fwd()
-        y = self._mm(self.q["X"], self.q["W1t"]) + self.t["R"]
+        y = self._mm(self._rm("X"), self._rm("W1t")) + self.t["R"]
         self.torch.cuda.synchronize()
         return float((y.float() - self.y.float()).abs().max() / self.y.float().abs().max())
 

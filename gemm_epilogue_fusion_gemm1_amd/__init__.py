@@ -37,6 +37,7 @@ __all__ = [
     "rope_bwd", "rope_fwd_workspace_bytes", "rope_bwd_workspace_bytes", "fwd_workspace_bytes", "bwd_workspace_bytes",
     "swiglu_bwd_workspace_bytes", "mlp_fwd_workspace_bytes", "mlp_bwd_workspace_bytes",
     "coda_mx8_quantize", "coda_fwd_mx8", "mx8_quantize", "fwd_mx8", "fwd_mx8_workspace_bytes",
+    "mx8_scales_to_rowmajor", "mx8_scales_from_rowmajor",
     "version", "trace_start", "trace_read", "trace_stop",
 ]
 
@@ -355,7 +356,7 @@ def _u8(t, name):
 
 def coda_mx8_quantize(src, codes, scales):
     """MXFP8 quantisation of the bf16 rows of src [rows, cols] into codes
-    [rows, cols] and scales [rows, cols/32] (uint8)."""
+    [rows, cols] and step-blocked scales [cols/128, rows, 4] (uint8)."""
     import torch
     if src.dtype != torch.bfloat16:
         raise TypeError("coda_mx8_quantize: src must be torch.bfloat16")
@@ -376,12 +377,26 @@ def coda_fwd_mx8(Xq, Xs, W1tq, W1ts, R, gamma, W2tq, W2ts, eps, y, r, z, workspa
 
 # ------------------------------------------------------ convenience calls
 
+def mx8_scales_to_rowmajor(scales):
+    """Step-blocked scales [cols/128, rows, 4] as the row-major [rows, cols/32]
+    (a view permutation, made contiguous)."""
+    t, rows, _ = scales.shape
+    return scales.permute(1, 0, 2).reshape(rows, 4 * t).contiguous()
+
+
+def mx8_scales_from_rowmajor(scales):
+    """Row-major scales [rows, cols/32] in the step-blocked layout [cols/128, rows, 4]."""
+    rows, nb = scales.shape
+    return scales.reshape(rows, nb // 4, 4).permute(1, 0, 2).contiguous()
+
+
 def mx8_quantize(src):
-    """MXFP8 codes and scales (uint8 tensors) of the bf16 rows of src."""
+    """MXFP8 codes [rows, cols] and step-blocked scales [cols/128, rows, 4]
+    (uint8 tensors) of the bf16 rows of src."""
     import torch
     rows, cols = src.shape
     codes = torch.empty((rows, cols), dtype=torch.uint8, device=src.device)
-    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=src.device)
+    scales = torch.empty((cols // 128, rows, 4), dtype=torch.uint8, device=src.device)
     coda_mx8_quantize(src, codes, scales)
     return codes, scales
 
@@ -392,8 +407,9 @@ def fwd_mx8(Xq, Xs, W1tq, W1ts, R, gamma, W2tq, W2ts, eps):
     import torch
     M, K = Xq.shape
     d, N = W1tq.shape[0], W2tq.shape[0]
-    _shape(Xs, M, K // 32, name="Xs"); _shape(W1tq, d, K, name="W1tq"); _shape(W1ts, d, K // 32, name="W1ts")
-    _shape(W2tq, N, d, name="W2tq"); _shape(W2ts, N, d // 32, name="W2ts")
+    _shape(Xs, K // 128, M, 4, name="Xs"); _shape(W1tq, d, K, name="W1tq")
+    _shape(W1ts, K // 128, d, 4, name="W1ts")
+    _shape(W2tq, N, d, name="W2tq"); _shape(W2ts, d // 128, N, 4, name="W2ts")
     _shape(R, M, d, name="R"); _shape(gamma, d, name="gamma")
     y = torch.empty((M, d), dtype=torch.bfloat16, device=R.device)
     r = torch.empty((M,), dtype=torch.float32, device=R.device)

@@ -252,7 +252,6 @@ GemmArgs gemm_mx8(int64_t M, int64_t N, int64_t K, const void* Aq, const void* A
   g.sB = (const uint8_t*)Bs;
   g.sA_bytes = (uint32_t)(M * (K / 32));
   g.sB_bytes = (uint32_t)(N * (K / 32));
-  g.ld_scale = K / 32;
   g.C = C;
   g.ldc = ldc;
   return g;
@@ -908,7 +907,7 @@ coda_status coda_rope_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t N, int
 coda_status coda_mx8_quantize(int64_t rows, int64_t cols, const void* src, int64_t ld_src,
                               void* codes, void* scales, void* stream) {
   if (!src || !codes || !scales) return CODA_ERR_NULL;
-  if (rows < 1 || !mx_dim_ok(cols, 32) || ld_src < cols || ld_src % 8 != 0 || rows > (int64_t)1 << 24)
+  if (rows < 1 || !mx_dim_ok(cols, 128) || ld_src < cols || ld_src % 8 != 0 || rows > (int64_t)1 << 24)
     return CODA_ERR_SHAPE;
   if (!fits(rows, ld_src, 2) || !fits(rows, cols, 1)) return CODA_ERR_SHAPE;
   if (!aligned16(src) || !aligned16(codes)) return CODA_ERR_ALIGN;

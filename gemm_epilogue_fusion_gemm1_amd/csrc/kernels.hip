@@ -443,10 +443,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     const int sc_row = (sc_a ? row0 : col0) + 64 * (wv & 3) + lane;
     const bool sc_ok = sc_row < (sc_a ? g.M : g.N);
     const __amdgpu_buffer_rsrc_t srs = make_rsrc(sc_a ? g.sA : g.sB, sc_a ? g.sA_bytes : g.sB_bytes);
-    const uint32_t sc_base = (uint32_t)sc_row * (uint32_t)g.ld_scale;
+    // step-blocked scales: the words of one step's rows are contiguous, so a
+    // wave's 64 rows are one 256-byte run
+    const uint32_t sc_base = (uint32_t)sc_row * 4u, sc_step = (uint32_t)(sc_a ? g.M : g.N) * 4u;
     lds_char* const sc_lds = lsm + KC::LDS_BYTES + (sc_a ? 0 : BM * 4) + 64 * 4 * (wv & 3);
     auto issue_scales = [&](int step) {
-      dma4(srs, (sc_ok && step < nk) ? sc_base + 4u * (uint32_t)step : OOB, sc_lds + (step % NSTAGE) * SC_STAGE);
+      dma4(srs, (sc_ok && step < nk) ? sc_base + sc_step * (uint32_t)step : OOB, sc_lds + (step % NSTAGE) * SC_STAGE);
     };
     const int l32 = lane & 31, sh = 8 * (lane >> 5);
     auto read_scales = [&](int step, uint32_t (&sa)[FM], uint32_t (&sb)[FN]) {
@@ -732,7 +734,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(vhi[2]), sat(vhi[3]), w1, true);
             if (ok) {
               *(uint2*)(g.q_out + (int64_t)row * g.ldq + gcol) = uint2{(uint32_t)w0, (uint32_t)w1};
-              if ((c8 & 3) == 0) g.qs_out[(int64_t)row * (g.ldq / 32) + gcol / 32] = (uint8_t)(sexp + 127);
+              if ((c8 & 3) == 0)   // step-blocked: [d/128][M][4]
+                g.qs_out[((int64_t)(gcol >> 7) * g.M + row) * 4 + ((gcol >> 5) & 3)] = (uint8_t)(sexp + 127);
             }
           }
         } else if constexpr (EPI == EPI_DN) {
@@ -942,7 +945,8 @@ gemm_mx8_kernel(GemmArgs g) {
 
 // bf16 rows -> MXFP8 along the row.  A lane takes 8 consecutive elements
 // (one 16-byte load), 4 lanes one 32-block: shared exponent and element
-// rounding as in the first GEMM's epilogue.  Grid-stride over 8-element groups.
+// rounding as in the first GEMM's epilogue; scales stored step-blocked
+// ([cols/128][rows][4]).  Grid-stride over 8-element groups.
 __global__ void mx8_quantize_kernel(const __bf16* __restrict__ src, int64_t ld, int64_t rows,
                                     int64_t cols, uint8_t* __restrict__ codes,
                                     uint8_t* __restrict__ scales) {
@@ -978,7 +982,7 @@ __global__ void mx8_quantize_kernel(const __bf16* __restrict__ src, int64_t ld, 
     w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[2]), sat(hi[3]), w1, true);
     if (ok) {
       *(uint2*)(codes + row * cols + col) = uint2{(uint32_t)w0, (uint32_t)w1};
-      if ((col & 31) == 0) scales[row * (cols / 32) + col / 32] = (uint8_t)(sexp + 127);
+      if ((col & 31) == 0) scales[((col >> 7) * rows + row) * 4 + ((col >> 5) & 3)] = (uint8_t)(sexp + 127);
     }
   }
 }

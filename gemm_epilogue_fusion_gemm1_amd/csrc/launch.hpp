@@ -56,12 +56,13 @@ struct GemmArgs {
                                                                // each [rope_seq][rope_head / 2]
   uint32_t A_bytes, B_bytes;     // buffer extents for hardware bounds checks
   // MXFP8 GEMMs (launch_gemm_mx8): A is [M][K] and B is given as B^T [N][K],
-  // both E4M3 bytes with lda / ldb in bytes; their E8M0 scales are [M][K/32]
-  // and [N][K/32], ld_scale bytes per row
+  // both E4M3 bytes with lda / ldb in bytes.  Their E8M0 scales are stored
+  // step-blocked: [K/128][rows][4], the word of (step t, row r) holding the
+  // scales of r's 32-blocks 4t..4t+3 (rows = M for A, N for B)
   const uint8_t* sA; const uint8_t* sB;
-  uint32_t sA_bytes, sB_bytes; int64_t ld_scale;
+  uint32_t sA_bytes, sB_bytes;
   // EPI_RESID_SUMSQ in an MXFP8 GEMM: y * vcol quantised to MXFP8 along the
-  // row, codes [M][ldq] and scales [M][ldq / 32] (instead of C2)
+  // row, codes [M][ldq] and scales [ldq/128][M][4] (instead of C2)
   uint8_t* q_out; uint8_t* qs_out; int64_t ldq;
 };
 
@@ -75,7 +76,8 @@ hipError_t launch_gemm_f32(const GemmArgs& g, Epi epi, hipStream_t stream);
 // K % 128 == 0; epilogues EPI_STORE, EPI_RESID_SUMSQ (with q_out), EPI_RSQRT_SCALE
 hipError_t launch_gemm_mx8(const GemmArgs& g, Epi epi, hipStream_t stream);
 // codes / scales = the MXFP8 quantisation of the bf16 rows of src along the
-// row (cols % 32 == 0; codes [rows][cols], scales [rows][cols / 32])
+// row (cols % 128 == 0; codes [rows][cols], scales step-blocked
+// [cols/128][rows][4])
 hipError_t launch_mx8_quantize(const void* src, int64_t ld, int64_t rows, int64_t cols,
                                uint8_t* codes, uint8_t* scales, hipStream_t stream);
 

@@ -318,10 +318,17 @@ coda_status coda_rope_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t N, int
  * v / 2^e rounded to the nearest E4M3 value, ties to even, saturated to
  * +-448.
  *
+ * Scale layout ("step-blocked", every scale tensor below): the scales of a
+ * [rows, cols] MXFP8 tensor are [cols/128][rows][4] bytes; byte j of word
+ * (t, r) is the scale of row r's 32-block 4t + j.  One K step (128) of the
+ * GEMMs then reads each tile's scales as one contiguous run.  A row-major
+ * [rows][cols/32] scale tensor s maps to it as s.reshape(rows, cols/128, 4)
+ * with its first two axes swapped.
+ *
  * coda_mx8_quantize: src [rows, cols] bf16 with row stride ld_src elements
  *   (ld_src >= cols, a multiple of 8, src 16-byte aligned) -> codes [rows,
- *   cols] E4M3 bytes (contiguous, 16-byte aligned) and scales [rows, cols/32]
- *   E8M0 bytes (contiguous).  cols a multiple of 32, rows >= 1.  Blocks run
+ *   cols] E4M3 bytes (contiguous, 16-byte aligned) and scales (step-blocked,
+ *   rows * cols/32 bytes).  cols a multiple of 128, rows >= 1.  Blocks run
  *   along each row, so a weight W [in, out] is quantised from its transpose
  *   [out, in].  Errors: CODA_ERR_NULL, CODA_ERR_SHAPE, CODA_ERR_ALIGN,
  *   CODA_ERR_ALIAS (codes or scales overlapping src or each other).
@@ -334,9 +341,9 @@ coda_status coda_rope_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t N, int
  * quantised for the second GEMM is y * gamma (the tensor the first GEMM's
  * epilogue holds), not the normalised RMSNorm(y) * gamma.
  *
- *   Xq   [M,K] E4M3 in    Xs  [M,K/32] E8M0 in
- *   W1tq [d,K] E4M3 in    W1ts [d,K/32] in     (W1 stored [out, in])
- *   W2tq [N,d] E4M3 in    W2ts [N,d/32] in     (W2 stored [out, in])
+ *   Xq   [M,K] E4M3 in    Xs   [K/128][M][4] E8M0 in (step-blocked)
+ *   W1tq [d,K] E4M3 in    W1ts [K/128][d][4] in     (W1 stored [out, in])
+ *   W2tq [N,d] E4M3 in    W2ts [d/128][N][4] in     (W2 stored [out, in])
  *   R [M,d] bf16 in, gamma [d] bf16 in
  *   y [M,d] bf16 out (saved for coda_bwd), r [M] float32 out, z [M,N] bf16 out
  *   M, N: >= 8 and multiples of 8; K, d: >= 128 and multiples of 128 (whole
@@ -344,7 +351,8 @@ coda_status coda_rope_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t N, int
  *   16-byte aligned.  eps > 0 and finite.
  *   workspace: >= coda_fwd_mx8_workspace_bytes(M, K, d, N) bytes: the partial
  *   sums [M, ceil(d/256)] fp32, then q [M, d] E4M3 at the next 256-byte
- *   boundary, then qs [M, d/32] E8M0 at the next 256-byte boundary.
+ *   boundary, then its scales qs (step-blocked, [d/128][M][4]) at the next
+ *   256-byte boundary.
  * The backward is coda_bwd (bf16) on the saved y and r.
  * ---------------------------------------------------------------------- */
 coda_status coda_mx8_quantize(int64_t rows, int64_t cols, const void* src, int64_t ld_src,

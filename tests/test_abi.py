@@ -317,6 +317,7 @@ def test_mx8_rejects(L):
     assert fwd(z=ctypes.c_void_p(z.value + 8)) == ALIGN
     q_src, q_codes, q_scales = m(M * K * 2), m(M * K), m(M * K // 32)
     assert L.coda_mx8_quantize(M, 48, q_src, 48, q_codes, q_scales, None) == SHAPE
+    assert L.coda_mx8_quantize(M, 96, q_src, 96, q_codes, q_scales, None) == SHAPE   # not whole 128-k steps
     assert L.coda_mx8_quantize(M, K, q_src, K - 8, q_codes, q_scales, None) == SHAPE
     assert L.coda_mx8_quantize(0, K, q_src, K, q_codes, q_scales, None) == SHAPE
     assert L.coda_mx8_quantize(M, K, q_src, K, q_src, q_scales, None) == ALIAS

@@ -58,6 +58,18 @@ def u8(torch, dev, a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(dev)
 
 
+def blocked(s):
+    """Row-major scales [rows, K/32] in the library's step-blocked layout [K/128, rows, 4]."""
+    rows, nb = s.shape
+    return np.ascontiguousarray(s.reshape(rows, nb // 4, 4).transpose(1, 0, 2))
+
+
+def unblocked(s):
+    """Step-blocked scales [K/128, rows, 4] as row-major [rows, K/32]."""
+    t, rows, _ = s.shape
+    return np.ascontiguousarray(s.transpose(1, 0, 2).reshape(rows, 4 * t))
+
+
 def bf(torch, dev, a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(torch.bfloat16)
 
@@ -78,19 +90,19 @@ def run_fwd(torch, dev, h, q, eps):
     z = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     nb = coda.fwd_mx8_workspace_bytes(M, K, d, N)
     ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
-    coda.coda_fwd_mx8(u8(torch, dev, q["Xq"]), u8(torch, dev, q["Xs"]), u8(torch, dev, q["W1q"]),
-                      u8(torch, dev, q["W1s"]), bf(torch, dev, h["R"]), bf(torch, dev, h["gamma"]),
-                      u8(torch, dev, q["W2q"]), u8(torch, dev, q["W2s"]), eps, y, r, z, ws)
+    coda.coda_fwd_mx8(u8(torch, dev, q["Xq"]), u8(torch, dev, blocked(q["Xs"])), u8(torch, dev, q["W1q"]),
+                      u8(torch, dev, blocked(q["W1s"])), bf(torch, dev, h["R"]), bf(torch, dev, h["gamma"]),
+                      u8(torch, dev, q["W2q"]), u8(torch, dev, blocked(q["W2s"])), eps, y, r, z, ws)
     torch.cuda.synchronize()
-    # workspace layout (coda.h): partial sums, then q [M, d], then qs [M, d/32],
-    # each at a 256-byte boundary
+    # workspace layout (coda.h): partial sums, then q [M, d], then qs
+    # (step-blocked [d/128, M, 4]), each at a 256-byte boundary
     def ru(x):
         return (x + 255) // 256 * 256
     off_q = ru(M * ((d + 255) // 256) * 4)
     off_qs = off_q + ru(M * d)
     w = ws.cpu().numpy()
     yq = w[off_q:off_q + M * d].reshape(M, d)
-    ys = w[off_qs:off_qs + M * (d // 32)].reshape(M, d // 32)
+    ys = unblocked(w[off_qs:off_qs + M * (d // 32)].reshape(d // 128, M, 4))
     return y.float().cpu().numpy(), r.cpu().numpy(), z.float().cpu().numpy(), yq, ys
 
 
@@ -150,7 +162,7 @@ def check_quantised_yg(name, yq, ys, ref, slack):
 
 def _quant_cases():
     g = np.random.default_rng(7)
-    a = (g.standard_normal((300, 1056)) * np.exp2(g.integers(-20, 20, (300, 1)))).astype(np.float32)
+    a = (g.standard_normal((300, 1152)) * np.exp2(g.integers(-20, 20, (300, 1)))).astype(np.float32)
     a[3, :64] = 0.0                                   # all-zero blocks
     a[4, :32] = -0.0
     a[5, :32] = 1e-39                                 # fp32-subnormal block maximum
@@ -158,7 +170,7 @@ def _quant_cases():
     a[7, :32] = np.linspace(-470, 470, 32)            # saturating elements under scale 1
     a[8, :32] = 2.0 ** -133                           # the smallest bf16 subnormal
     return [("ragged", synth.round_to_bf16(a)),
-            ("one_block", synth.round_to_bf16(g.standard_normal((7, 32)).astype(np.float32))),
+            ("one_step", synth.round_to_bf16(g.standard_normal((7, 128)).astype(np.float32))),
             ("wide", synth.round_to_bf16(g.standard_normal((64, 4096)).astype(np.float32)))]
 
 
@@ -170,7 +182,7 @@ def test_mx8_quantize_bit_exact(torch_dev, case):
     codes, scales = coda.mx8_quantize(bf(torch, dev, a))
     torch.cuda.synchronize()
     oq, os_ = oracle.mx_quantize(a.astype(np.float64))
-    gq, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    gq, gs = codes.cpu().numpy(), unblocked(scales.cpu().numpy())
     nq, ns = int((gq != oq).sum()), int((gs != os_).sum())
     report(f"mx8 quantize {name} {a.shape}", {"code_mismatches": nq, "scale_mismatches": ns})
     assert ns == 0 and nq == 0
@@ -217,7 +229,7 @@ def test_full_workload_mx8(torch_dev):
     q = quantised(h)
     gq, gs = coda.mx8_quantize(bf(torch, dev, h["X"]))
     torch.cuda.synchronize()
-    assert np.array_equal(gq.cpu().numpy(), q["Xq"]) and np.array_equal(gs.cpu().numpy(), q["Xs"])
+    assert np.array_equal(gq.cpu().numpy(), q["Xq"]) and np.array_equal(unblocked(gs.cpu().numpy()), q["Xs"])
     del gq, gs
     y, r, z, yq, ys = run_fwd(torch, dev, h, q, w.eps)
     rows = np.unique(np.concatenate([np.arange(0, w.M, 173), [w.M - 1]]))
