@@ -28,6 +28,8 @@
 //    fixed order, so every result is run-to-run deterministic (no atomics).
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace coda {
 namespace {
 
@@ -102,6 +104,9 @@ __device__ __forceinline__ __bf16 f2bf(float f) { return (__bf16)f; }  // round 
 #endif
 #ifndef CODA_XCD_REMAP
 #define CODA_XCD_REMAP 1
+#endif
+#ifndef CODA_BF16_MFMA16
+#define CODA_BF16_MFMA16 1
 #endif
 __device__ __forceinline__ void map_tile(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
@@ -284,7 +289,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <bool KMAJ, class KC, int NB>
+template <bool KMAJ, class KC, int NB, int MBK>
 struct FragReader;
 
 // MXFP8 operand fragments of v_mfma_scale_f32_32x32x64_f8f6f4 (measured with
@@ -314,17 +319,22 @@ struct FragReaderMX {
   }
 };
 
-// K-contiguous tile: one ds_read_b128 per fragment.
-template <class KC, int NB>
-struct FragReader<true, KC, NB> {
-  int off[KC::BK / 16];   // per sub-step s, for block 0; block i adds 32 rows
+// K-contiguous tile: one ds_read_b128 per fragment.  32-row blocks
+// (v_mfma_f32_32x32x16_bf16): lane l takes row l%32 and the 8 k 16s +
+// 8(l/32)..+7 of sub-step s (16 k); 16-row blocks (v_mfma_f32_16x16x32_bf16):
+// row l%16 and the 8 k 32s + 8(l/16)..+7 of sub-step s (32 k).  A and B are
+// read with the same k assignment, which is all the product needs.
+template <class KC, int NB, int MBK>
+struct FragReader<true, KC, NB, MBK> {
+  static constexpr int SUBK = MBK == 32 ? 16 : 32;   // k per sub-step
+  int off[KC::BK / SUBK];   // per sub-step s, for block 0; block i adds MBK rows
   __device__ void init(int mn0, int lane) {
-    const int l32 = lane & 31, khalf = lane >> 5;
+    const int r = lane % MBK, kq = lane / MBK;
 #pragma unroll
-    for (int s = 0; s < KC::BK / 16; ++s) off[s] = KC::kmaj_off(mn0 + l32, 2 * s + khalf);
+    for (int s = 0; s < KC::BK / SUBK; ++s) off[s] = KC::kmaj_off(mn0 + r, (SUBK / 8) * s + kq);
   }
   __device__ bf16x8 read(const char* tile, int s, int i) const {
-    return *(const bf16x8*)(tile + off[s] + i * 32 * KC::KROW);
+    return *(const bf16x8*)(tile + off[s] + i * MBK * KC::KROW);
   }
 };
 
@@ -332,21 +342,24 @@ struct FragReader<true, KC, NB> {
 // group, ds_read_b64_tr_b16 hands output lane i element i%4 of the 8 bytes
 // addressed by source lanes 4k + i/4 (k = 0..3).  Source lane j points at
 // (k row K0 + j/4, columns c0 + 4(j%4)..+3), so output lane i receives
-// column c0 + i at rows K0..K0+3.
-template <class KC, int NB>
-struct FragReader<false, KC, NB> {
-  int off[NB];  // per block i (32 columns); sub-step s and half h add k rows
+// column c0 + i at rows K0..K0+3.  32-column blocks: lanes 16..31 take
+// columns +16 and lanes 32..63 k rows +8; 16-column blocks: the four 16-lane
+// groups take k rows +0, +8, +16, +24.
+template <class KC, int NB, int MBK>
+struct FragReader<false, KC, NB, MBK> {
+  static constexpr int SUBK = MBK == 32 ? 16 : 32;   // k rows per sub-step
+  int off[NB];  // per block i; sub-step s and half h add k rows
   __device__ void init(int mn0, int lane) {
-    const int j = lane & 15, khalf = lane >> 5;
-    const int krow = 8 * khalf + (j >> 2);                  // + 16 s + 4 h
+    const int j = lane & 15;
+    const int krow = (MBK == 32 ? 8 * (lane >> 5) : 8 * (lane >> 4)) + (j >> 2);   // + SUBK s + 4 h
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int mn = mn0 + i * 32 + (lane & 16) + 4 * (j & 3);
-      off[i] = mnmaj_off(krow, mn >> 3) + ((mn & 7) << 1);  // (krow + 16s + 4h) & 3 == krow & 3
+      const int mn = mn0 + i * MBK + (MBK == 32 ? (lane & 16) : 0) + 4 * (j & 3);
+      off[i] = mnmaj_off(krow, mn >> 3) + ((mn & 7) << 1);  // (krow + SUBK s + 4h) & 3 == krow & 3
     }
   }
   __device__ bf16x8 read(const char* tile, int s, int i) const {
-    const char* p = tile + off[i] + s * 16 * 512;
+    const char* p = tile + off[i] + s * SUBK * 512;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 512));
     const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -411,11 +424,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   la.init(g.A, g.A_bytes, g.lda / U, row0, g.M, g.K / U, t, 0, tm);
   lb.init(g.B, g.B_bytes, g.ldb / U, col0, g.N, g.K / U, t, g.F, tn);
 
-  f32x16 acc[FM][FN];
+  // MFMA blocks: bf16 uses v_mfma_f32_16x16x32_bf16 (16x16 blocks, four
+  // accumulators per lane), which draws less power per flop than the 32x32
+  // form and so sustains a higher clock under the power limit; MXFP8 uses
+  // v_mfma_scale_f32_32x32x64_f8f6f4 (32x32 blocks, sixteen per lane).
+  constexpr int MB = (FMT == FMT_BF16 && CODA_BF16_MFMA16) ? 16 : 32;
+  constexpr int BFM = TM / MB, BFN = TN / MB;
+  using AccV = std::conditional_t<MB == 16, f32x4, f32x16>;
+  AccV acc[BFM][BFN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < BFM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < BFN; ++j) acc[i][j] = AccV{};
 
   const int nk = (g.K / U + BK - 1) / BK;
   lds_char* lsm = (lds_char*)smem;
@@ -517,26 +537,32 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   //     in LDS, and every wave is done reading step k-1's stage), and read
   //     step k+1's first fragments while the last MFMAs of step k run.
   // Fragments are double-buffered in registers.  Loads past K read zeros.
-  FragReader<AK, KC, FM> fra;
-  FragReader<BKM, KC, FN> frb;
+  FragReader<AK, KC, BFM, MB> fra;
+  FragReader<BKM, KC, BFN, MB> frb;
   fra.init(wm * TM, lane);
   frb.init(wn * TN, lane);
-  bf16x8 fa[2][FM], fb[2][FN];
-  constexpr int NSUB = BK / 16;
+  bf16x8 fa[2][BFM], fb[2][BFN];
+  constexpr int NSUB = BK / (MB == 32 ? 16 : 32);
 
-  auto read_frags = [&](const char* stage, int s, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
+  auto read_frags = [&](const char* stage, int s, bf16x8 (&a)[BFM], bf16x8 (&b)[BFN]) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) a[i] = fra.read(stage, s, i);
+    for (int i = 0; i < BFM; ++i) a[i] = fra.read(stage, s, i);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) b[j] = frb.read(stage + OPER_BYTES, s, j);
+    for (int j = 0; j < BFN; ++j) b[j] = frb.read(stage + OPER_BYTES, s, j);
   };
-  auto mfmas = [&](const bf16x8 (&a)[FM], const bf16x8 (&b)[FN]) {
+  // the MFMAs of block rows [i0, i1)
+  auto mfmas_rows = [&](const bf16x8 (&a)[BFM], const bf16x8 (&b)[BFN], int i0, int i1) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = i0; i < i1; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < BFN; ++j) {
+        if constexpr (MB == 16)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+      }
   };
+  auto mfmas = [&](const bf16x8 (&a)[BFM], const bf16x8 (&b)[BFN]) { mfmas_rows(a, b, 0, BFM); };
 
   // The compiler interleaves each sub-step's LDS reads and MFMAs; with two
   // waves per SIMD that measured faster than any forced order (all reads
@@ -548,21 +574,61 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   __builtin_amdgcn_s_waitcnt(WAIT_NEXT);     // step 0 has landed
   __syncthreads();
   read_frags(smem, 0, fa[0], fb[0]);
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* sc = smem + (kt % NSTAGE) * STAGE_BYTES;
-    const char* sn = smem + ((kt + 1) % NSTAGE) * STAGE_BYTES;
-    issue(kt + NSTAGE - 1);
-#pragma unroll
-    for (int s = 0; s + 1 < NSUB; ++s) {
-      read_frags(sc, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-      mfmas(fa[s & 1], fb[s & 1]);
+  if constexpr (NSUB == 2) {
+    // Two sub-steps: the wait and barrier go three quarters through the step
+    // (after the first half of the last sub-step's MFMAs), so the next
+    // stage's loads have as long to land as with four sub-steps, and the
+    // next stage's first fragments are read under the second half.
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* sc = smem + (kt % NSTAGE) * STAGE_BYTES;
+      const char* sn = smem + ((kt + 1) % NSTAGE) * STAGE_BYTES;
+      issue(kt + NSTAGE - 1);
+      read_frags(sc, 1, fa[1], fb[1]);
+      mfmas(fa[0], fb[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas_rows(fa[1], fb[1], 0, BFM / 2);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(WAIT_NEXT);   // this wave's loads of step kt+1 have landed
+      __syncthreads();
+      read_frags(sn, 0, fa[0], fb[0]);
+      mfmas_rows(fa[1], fb[1], BFM / 2, BFM);
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(WAIT_NEXT);   // this wave's loads of step kt+1 have landed
-    __syncthreads();
-    read_frags(sn, 0, fa[0], fb[0]);
-    mfmas(fa[(NSUB - 1) & 1], fb[(NSUB - 1) & 1]);
-    __builtin_amdgcn_sched_barrier(0);
+  } else if constexpr (NSUB % 2 == 0) {
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* sc = smem + (kt % NSTAGE) * STAGE_BYTES;
+      const char* sn = smem + ((kt + 1) % NSTAGE) * STAGE_BYTES;
+      issue(kt + NSTAGE - 1);
+#pragma unroll
+      for (int s = 0; s + 1 < NSUB; ++s) {
+        read_frags(sc, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+        mfmas(fa[s & 1], fb[s & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_waitcnt(WAIT_NEXT);   // this wave's loads of step kt+1 have landed
+      __syncthreads();
+      read_frags(sn, 0, fa[0], fb[0]);
+      mfmas(fa[(NSUB - 1) & 1], fb[(NSUB - 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // one sub-step per K step: the fragment buffers alternate between steps
+    static_assert(NSUB == 1, "odd sub-step counts other than 1");
+    auto step1 = [&](int kt, auto bufc) {
+      constexpr int b = decltype(bufc)::value;
+      issue(kt + NSTAGE - 1);
+      __builtin_amdgcn_s_waitcnt(WAIT_NEXT);   // this wave's loads of step kt+1 have landed
+      __syncthreads();
+      read_frags(smem + ((kt + 1) % NSTAGE) * STAGE_BYTES, 0, fa[b ^ 1], fb[b ^ 1]);
+      mfmas(fa[b], fb[b]);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step1(kt, std::integral_constant<int, 0>{});
+      step1(kt + 1, std::integral_constant<int, 1>{});
+    }
+    if (kt < nk) step1(kt, std::integral_constant<int, 0>{});
   }
   }
   __builtin_amdgcn_s_waitcnt(0);             // no load may still write into LDS
@@ -584,14 +650,27 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   const int c8 = lane & 7, rsub = lane >> 3;
   const int gcol = col0 + wn * TN + 8 * c8;         // first global column of the lane
   const bool colok = gcol < g.N;
-  auto dump = [&](int i) {
+  auto dump = [&](int i) {   // the wave tile's rows 32i..32i+31 into the region
+    if constexpr (MB == 16) {
+      // 16x16 blocks (2i, 2i+1): lane l holds row l%16 and columns
+      // 16j + 4(l/16)..+3 of block (2i+h, j)
+      const int r16 = lane & 15;
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = j * 8 + 2 * q + (lane >> 5);
-        *(f32x4*)(region + l32 * 256 + ((c ^ (l32 & 15)) << 4)) = quad(acc[i][j], q);
-      }
+        for (int j = 0; j < BFN; ++j) {
+          const int row = 16 * h + r16, c = 4 * j + (lane >> 4);
+          *(f32x4*)(region + row * 256 + ((c ^ (row & 15)) << 4)) = acc[2 * i + h][j];
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = j * 8 + 2 * q + (lane >> 5);
+          *(f32x4*)(region + l32 * 256 + ((c ^ (l32 & 15)) << 4)) = quad(acc[i][j], q);
+        }
+    }
   };
   auto fetch8 = [&](int r, int cpair, f32x4& lo, f32x4& hi) {   // 8 fp32: columns 8*cpair..+7 of region row r
     lo = *(const f32x4*)(region + r * 256 + (((2 * cpair) ^ (r & 15)) << 4));
