@@ -75,13 +75,17 @@ static_assert(BM == BN, "operand tiles share one LDS geometry");
 //                 chunk q of rows m..m+15 (m % 16 == 0) hit 16 distinct 16-byte
 //                 bank groups.
 //  MN-contiguous: row k (512 B) at k*512; its 16-byte MN chunk c (mn =
-//                 8c..8c+7) sits at chunk position c ^ ((k & 3) << 2).  A
-//                 transpose read touches 4 rows x 4 chunks per 32 lanes, which
-//                 the swizzle spreads over all 16 bank groups.
+//                 8c..8c+7) sits at chunk position c ^ mn_swz(k), mn_swz(k) =
+//                 ((k & 3) << 2) | (((k >> 3) & 1) << 1).  A transpose read
+//                 of 32 lanes touches either 4 rows x 4 chunks (32-wide
+//                 blocks) or, for 16-wide blocks, 4 rows x 2 chunks in each of
+//                 two row groups 8 apart; the swizzle spreads both over all 16
+//                 bank groups (the k bit 3 term separates the two groups).
 // Both are filled by direct-to-LDS buffer loads: one 64-lane load writes 1 KiB
 // of contiguous LDS (lane l at +16 l), so the swizzle is applied by choosing
 // which global chunk each lane fetches.
-__device__ __forceinline__ int mnmaj_off(int k, int c) { return k * 512 + ((c ^ ((k & 3) << 2)) << 4); }
+__device__ __forceinline__ int mn_swz(int k) { return ((k & 3) << 2) | (((k >> 3) & 1) << 1); }
+__device__ __forceinline__ int mnmaj_off(int k, int c) { return k * 512 + ((c ^ mn_swz(k)) << 4); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   // raw buffer: stride 0, num_records in bytes; dword3 0x00020000 = 32-bit data format
@@ -245,7 +249,7 @@ struct LoaderMNMajor {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int k = 2 * (LP * w + p) + (l >> 5);
-      const int c = (l & 31) ^ ((k & 3) << 2);
+      const int c = (l & 31) ^ mn_swz(k);   // the same for loads p and p + 2 (k + 4)
       int col;
       bool ok;
       if (GATED) {
@@ -355,7 +359,7 @@ struct FragReader<false, KC, NB, MBK> {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int mn = mn0 + i * MBK + (MBK == 32 ? (lane & 16) : 0) + 4 * (j & 3);
-      off[i] = mnmaj_off(krow, mn >> 3) + ((mn & 7) << 1);  // (krow + SUBK s + 4h) & 3 == krow & 3
+      off[i] = mnmaj_off(krow, mn >> 3) + ((mn & 7) << 1);  // mn_swz(krow + SUBK s + 4h) == mn_swz(krow)
     }
   }
   __device__ bf16x8 read(const char* tile, int s, int i) const {
