@@ -494,8 +494,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       for (int j = 0; j < FN; ++j) b[j] = frb.read(stage + OPER_BYTES, s, j);
     };
     // B is the MFMA's first operand (C^T is accumulated), so its scale goes first
-#define CODA_MX_MFMAS(S, A_, B_)                                                                   \
-    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                                 \
+#define CODA_MX_MFMAS(S, A_, B_, I0, I1)                                                           \
+    _Pragma("unroll") for (int i = (I0); i < (I1); ++i)                                            \
     _Pragma("unroll") for (int j = 0; j < FN; ++j)                                                 \
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(B_[j], A_[i], acc[i][j], 0, 0,   \
                                                                   2 * (S), sb[j], 2 * (S), sa[i]);
@@ -514,13 +514,19 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       issue(kt + NSTAGE - 1);
       issue_scales(kt + NSTAGE - 1);
       read_frags(sc, 1, fa[1], fb[1]);
-      CODA_MX_MFMAS(0, fa[0], fb[0])
+      CODA_MX_MFMAS(0, fa[0], fb[0], 0, FM)
+      __builtin_amdgcn_sched_barrier(0);
+      // the wait and barrier three quarters through the step (after half of
+      // the second sub-step's MFMAs): the next stage's loads get one and a
+      // half sub-steps to land, and its first fragments and scales are read
+      // under the second half
+      CODA_MX_MFMAS(1, fa[1], fb[1], 0, FM / 2)
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(WAIT_NEXT);   // this wave's loads of step kt+1 have landed
       __syncthreads();
       read_frags(sn, 0, fa[0], fb[0]);
       read_scales(kt + 1, san, sbn);
-      CODA_MX_MFMAS(1, fa[1], fb[1])
+      CODA_MX_MFMAS(1, fa[1], fb[1], FM / 2, FM)
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < FM; ++i) sa[i] = san[i];
