@@ -9,9 +9,10 @@
 // registers; memory-bound neighbours of a GEMM (residual add, the RMS row
 // scale, SwiGLU) are rewritten to run inside that epilogue.  Here:
 //
-//  * one bf16 MFMA main loop (v_mfma_f32_32x32x16_bf16, fp32 accumulators),
-//    256x256 output tile per 512-thread workgroup, 8 waves of 128x64 (two
-//    per SIMD), K step 64, LDS double buffered;
+//  * one MFMA main loop for bf16 (v_mfma_f32_16x16x32_bf16) and MXFP8
+//    (v_mfma_scale_f32_32x32x64_f8f6f4), fp32 accumulators, 256x256 output
+//    tile per 512-thread workgroup, 8 waves of 128x64 (two per SIMD), a ring
+//    of two or four LDS stages filled by direct-to-LDS loads;
 //  * operand tiles are staged in LDS in the layout they have in memory,
 //    with 16-byte chunks XOR-swizzled so that every LDS access of the loop
 //    is free of bank conflicts on gfx950's 64-bank LDS (16 lanes x 16 bytes
@@ -286,9 +287,8 @@ struct LoaderSel<true, KC, NT, GATED, TN> { using type = LoaderKMajor<KC, NT, GA
 template <class KC, int NT, bool GATED, int TN>
 struct LoaderSel<false, KC, NT, GATED, TN> { using type = LoaderMNMajor<KC, NT, GATED, TN>; };
 
-// MFMA operand fragments of v_mfma_f32_32x32x16_bf16: lane l supplies row
-// (or column) l%32 of a 32-wide block and the 8 k values 16s + 8(l/32) + 0..7
-// of sub-step s.
+// bf16 MFMA operand fragments: 8 k values of one row (or column) of a
+// 16- or 32-wide block per lane (see the readers below).
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -376,11 +376,12 @@ struct FragReader<false, KC, NB, MBK> {
 // ---------------------------------------------------------------------------
 
 // Accumulator layout.  The MFMA is issued with the B fragment as its first
-// operand and the A fragment as its second, so it accumulates C^T blocks:
-// lane l, register r of block (i, j) holds C[row = 32i + l%32][col = 32j +
-// 8(r/4) + 4(l/32) + r%4].  A lane thus owns one row and, per group of four
-// registers, four consecutive columns, which the epilogue writes to LDS as
-// 16-byte vectors.
+// operand and the A fragment as its second, so it accumulates C^T blocks.
+// 32x32 blocks: lane l, register r of block (i, j) holds C[row = 32i + l%32]
+// [col = 32j + 8(r/4) + 4(l/32) + r%4]; 16x16 blocks: register r of block
+// (i, j) holds C[16i + l%16][16j + 4(l/16) + r].  A lane thus owns one row
+// and, per group of four registers, four consecutive columns, which the
+// epilogue writes to LDS as 16-byte vectors.
 __device__ __forceinline__ f32x4 quad(const f32x16& a, int g) {
   return f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
 }
@@ -535,8 +536,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     }
 #undef CODA_MX_MFMAS
   } else {
-  // Software pipeline over a ring of NSTAGE LDS stages (one K step = BK/16
-  // MFMA sub-steps of 16):
+  // Software pipeline over a ring of NSTAGE LDS stages (one K step = NSUB
+  // MFMA sub-steps of 32 k with 16x16 blocks, of 16 k with 32x32 blocks):
   //   - the direct-to-LDS loads of step k+NSTAGE-1 are issued at the start of
   //     step k into the stage step k-1 used (free since the barrier that ended
   //     step k-1);
