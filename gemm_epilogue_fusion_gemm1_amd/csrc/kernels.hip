@@ -389,6 +389,19 @@ __device__ __forceinline__ f32x4 quad(const f32x16& a, int g) {
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 __device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
 
+// Lanes of one wave hand data to each other through LDS in the epilogue.  The
+// compiler treats the lanes as separate threads, so without this it may move
+// one lane's LDS write past another lane's read of the same bytes (a variant
+// of the tile loop did: with part of a wave masked off, the next pass's
+// writes were duplicated into the masked-off lanes' path, which ran before
+// the other lanes' reads).  A convergent wave barrier between two fences
+// pins the order; no instruction is emitted for it.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------------------
 // The MFMA GEMM: C[M,N] = A[M,K] B[K,N] (+ epilogue EPI), operands in bf16
 // (FMT_BF16) or MXFP8 (FMT_MX8: E4M3 with an E8M0 scale per 32 k, both
@@ -733,8 +746,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     if constexpr (EPI == EPI_RSQRT_SCALE) tile_row_rsqrt();
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      wave_lds_sync();                              // the previous pass's reads are done
       dump(i);
       __builtin_amdgcn_s_waitcnt(0xc07f);           // this wave's LDS writes are done
+      wave_lds_sync();
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int r = 8 * p + rsub;
@@ -900,6 +915,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         // store instruction writes 16 columns x 64 contiguous bytes.
         if (FMT == FMT_BF16 && g.C2 && g.c2_trans) {
           __builtin_amdgcn_s_waitcnt(0xc07f);         // this wave's LDS writes are done
+          wave_lds_sync();
           const int rg = 8 * (lane & 3);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -987,8 +1003,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     const bool jok = jj < g.F;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      wave_lds_sync();                              // the previous pass's reads are done
       dump(i);
       __builtin_amdgcn_s_waitcnt(0xc07f);
+      wave_lds_sync();
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const int r = 16 * p + r4;
