@@ -743,9 +743,36 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     if constexpr (EPI == EPI_DN || EPI == EPI_RESID_SUMSQ) {
       if (colok && g.vcol) ld8((const __bf16*)g.vcol + gcol, glo, ghi);
     }
+    // The passes' global inputs (E's 8 columns of the row, the row's scale,
+    // its label) are loaded one row group ahead, so that their latency hides
+    // under the previous group's passes instead of stalling every pass.
+    constexpr bool PRE_E = EPI == EPI_RESID_SUMSQ || EPI == EPI_DN || EPI == EPI_SWIGLU_BWD;
+    bf16x8 epre[2][4], upre[2][4];
+    float vpre[2][4];
+    int lpre[2][4];
+    auto prefetch = [&](int i, int b) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int row = row0 + wm * TM + i * 32 + 8 * p + rsub;
+        const bool ok = colok && row < g.M;
+        const __bf16* ep = (const __bf16*)g.E + (int64_t)row * g.lde + gcol;
+        if constexpr (PRE_E) epre[b][p] = ok ? *(const bf16x8*)ep : bf16x8{};
+        if constexpr (EPI == EPI_SWIGLU_BWD) upre[b][p] = ok ? *(const bf16x8*)(ep + g.F) : bf16x8{};
+        if constexpr (EPI == EPI_ROWSCALE)
+          vpre[b][p] = ok ? (g.vrow ? g.vrow[row] : bf2f(((const __bf16*)g.vcol)[row])) : 0.0f;
+        if constexpr (EPI == EPI_DN) vpre[b][p] = ok ? g.vrow[row] : 0.0f;
+        if constexpr (EPI == EPI_CE_STATS) lpre[b][p] = ok ? g.labels[row] : -1;
+      }
+    };
+    auto unpack8 = [](const bf16x8& v, f32x4& lo, f32x4& hi) {
+      lo = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+      hi = f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+    };
+    prefetch(0, 0);
     if constexpr (EPI == EPI_RSQRT_SCALE) tile_row_rsqrt();
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      if (i + 1 < FM) prefetch(i + 1, (i + 1) & 1);
       wave_lds_sync();                              // the previous pass's reads are done
       dump(i);
       __builtin_amdgcn_s_waitcnt(0xc07f);           // this wave's LDS writes are done
@@ -786,7 +813,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           }
         } else if constexpr (EPI == EPI_ROWSCALE) {
           if (ok) {
-            const float sc = g.vrow ? g.vrow[row] : bf2f(((const __bf16*)g.vcol)[row]);
+            const float sc = vpre[i & 1][p];
             st8(C + o, lo * sc, hi * sc);
           }
         } else if constexpr (EPI == EPI_RSQRT_SCALE) {
@@ -798,7 +825,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           float s = 0.0f;
           if (ok) {
             f32x4 elo, ehi;
-            ld8((const __bf16*)g.E + (int64_t)row * g.lde + gcol, elo, ehi);
+            unpack8(epre[i & 1][p], elo, ehi);
             lo += elo;
             hi += ehi;
             st8(C + o, lo, hi);
@@ -848,8 +875,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           float s = 0.0f;
           if (ok) {
             f32x4 ylo, yhi;
-            ld8((const __bf16*)g.E + (int64_t)row * g.lde + gcol, ylo, yhi);
-            const float rv = g.vrow[row];
+            unpack8(epre[i & 1][p], ylo, yhi);
+            const float rv = vpre[i & 1][p];
             const f32x4 dlo = lo * glo, dhi = hi * ghi;
             st8(C + o, dlo, dhi);
             if (g.C2) st8((__bf16*)g.C2 + (int64_t)row * g.ldc2 + gcol, ylo * rv, yhi * rv);
@@ -868,7 +895,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             st8(C + o, lo, hi);
             mx = fmaxf(fmaxf(fmaxf(lo[0], lo[1]), fmaxf(lo[2], lo[3])),
                        fmaxf(fmaxf(hi[0], hi[1]), fmaxf(hi[2], hi[3])));
-            const int lab = g.labels[row];
+            const int lab = lpre[i & 1][p];
             if (lab >= gcol && lab < gcol + 8) {
               const int e = lab - gcol;
               g.lab_out[row] = e < 4 ? lo[e] : hi[e - 4];
@@ -890,10 +917,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         } else if constexpr (EPI == EPI_SWIGLU_BWD) {
           // da = acc [M, F]; g, u from the saved gu; dgu = [dg | du]
           if (ok) {
-            const __bf16* gp = (const __bf16*)g.E + (int64_t)row * g.lde + gcol;
             f32x4 g0, g1, u0, u1;
-            ld8(gp, g0, g1);
-            ld8(gp + g.F, u0, u1);
+            unpack8(epre[i & 1][p], g0, g1);
+            unpack8(upre[i & 1][p], u0, u1);
             f32x4 dg0, dg1, du0, du1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
