@@ -168,6 +168,58 @@ def test_zero_rows_and_determinism(torch_dev):
     assert rel(z, f["z"]) <= BF16_TOL
 
 
+def test_graph_capture_replays_match_eager(torch_dev):
+    """The block's forward + backward captured into a HIP graph (the library
+    launches only kernels on the caller's stream: no memset, no allocation)
+    replays bitwise equal to the eager calls, on every replay, with eager
+    calls and synchronisations between the replays; the eager result is
+    also checked against the oracle."""
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    M, K, d, N, eps = 520, 264, 392, 776, 1e-6
+    h = synth.coda_inputs(M, K, d, N, seed=91, dtype="bf16")
+    t = {k: up(torch, dev, v, "bf16") for k, v in h.items()}
+    bf = torch.bfloat16
+    bufs = dict(y=torch.empty((M, d), dtype=bf, device=dev), r=torch.empty((M,), dtype=torch.float32, device=dev),
+                z=torch.empty((M, N), dtype=bf, device=dev), dX=torch.empty((M, K), dtype=bf, device=dev),
+                dW1=torch.empty((K, d), dtype=bf, device=dev), dR=torch.empty((M, d), dtype=bf, device=dev),
+                dW2=torch.empty((d, N), dtype=bf, device=dev), dg=torch.empty((d,), dtype=torch.float32, device=dev))
+    wsf = torch.empty(coda.fwd_workspace_bytes(1, M, K, d, N), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(coda.bwd_workspace_bytes(1, M, K, d, N), dtype=torch.uint8, device=dev)
+    b = bufs
+
+    def step():
+        coda.coda_fwd(t["X"], t["W1"], t["R"], t["gamma"], t["W2"], eps, b["y"], b["r"], b["z"], wsf)
+        coda.coda_bwd(t["X"], t["W1"], t["gamma"], t["W2"], b["y"], b["r"], t["dz"], b["dX"], b["dW1"],
+                      b["dR"], b["dW2"], b["dg"], wsb)
+
+    step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in bufs.items()}
+    f = oracle.ref_fwd(h["X"], h["W1"], h["R"], h["gamma"], h["W2"], eps)
+    assert rel(host(ref["z"]), f["z"]) <= BF16_TOL
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in bufs.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in bufs.items():
+            assert torch.equal(v, ref[k]), f"replay {rep}: {k} differs from the eager result"
+        step()                      # eager work between replays
+        torch.cuda.synchronize()
+    report("graph capture", {"replays": 3.0})
+
+
 def test_numerics_no_worse_than_unfused_torch(torch_dev):
     """The pages report the rewritten form's error as comparable to the
     unfused PyTorch reference and sometimes smaller, thanks to the fp32
