@@ -39,8 +39,8 @@ METRIC = "fused fwd+bwd TFLOP/s & %bf16 MFMA peak; speedup vs unfused, 7B/70B"
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama7b_fwdbwd")
     ap.add_argument("--no-also", action="store_true", help="skip the 70B, SwiGLU, MLP, cross-entropy, RoPE, MXFP8 and 1B workloads")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused torch baseline")
