@@ -563,18 +563,29 @@ def sustained_sclk(torch, step, seconds=2.5):
     exe = shutil.which("rocm-smi") or ("/opt/rocm/bin/rocm-smi" if os.path.exists("/opt/rocm/bin/rocm-smi") else None)
     if exe is None:
         return None
-    samples, done = [], threading.Event()
+    # Under rocprofv3 every child process inherits the profiler's preloaded
+    # library, which initialises the GPU before rocm-smi's interpreter starts;
+    # no clock is sampled in profiled runs.
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return None
+    samples, power, done = [], [], threading.Event()
 
     def sample():
         while not done.is_set():
             try:
-                out = subprocess.run([exe, "--showclocks"], capture_output=True, text=True, timeout=5).stdout
+                out = subprocess.run([exe, "--showclocks", "--showpower"], capture_output=True, text=True,
+                                     timeout=5).stdout
             except Exception:  # pragma: no cover - tool failure
                 return
             for line in out.splitlines():
                 m = re.search(r"sclk.*\((\d+)Mhz\)", line)
                 if m:
                     samples.append(int(m.group(1)))
+                    break
+            for line in out.splitlines():
+                m = re.search(r"Package Power \(W\):\s*([\d.]+)", line)
+                if m:
+                    power.append(float(m.group(1)))
                     break
             done.wait(0.25)
 
@@ -591,11 +602,25 @@ def sustained_sclk(torch, step, seconds=2.5):
     done.set()
     th.join(timeout=10)
     samples = samples[2:] if len(samples) > 4 else samples   # drop the ramp
+    power = power[2:] if len(power) > 4 else power
     if not samples:
         return None
     srt = sorted(samples)
-    return {"median_mhz": srt[len(srt) // 2], "min_mhz": srt[0], "max_mhz": srt[-1], "samples": len(srt),
-            "method": "rocm-smi --showclocks every ~0.25 s while the fused step repeats for %.1f s" % seconds}
+    res = {"median_mhz": srt[len(srt) // 2], "min_mhz": srt[0], "max_mhz": srt[-1], "samples": len(srt),
+           "method": "rocm-smi --showclocks --showpower every ~0.25 s while the fused step repeats for %.1f s"
+                     % seconds}
+    if power:
+        pw = sorted(power)
+        res["power_median_w"] = pw[len(pw) // 2]
+        res["power_max_w"] = pw[-1]
+    try:
+        out = subprocess.run([exe, "--showmaxpower"], capture_output=True, text=True, timeout=5).stdout
+        m = re.search(r"Max Graphics Package Power \(W\):\s*([\d.]+)", out)
+        if m:
+            res["power_cap_w"] = float(m.group(1))
+    except Exception:  # pragma: no cover - tool failure
+        pass
+    return res
 
 
 def cpu_baseline(w, h, target_s):

@@ -57,13 +57,14 @@ struct KCfg {
   static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
   static constexpr int KROW = BK * 2;                  // bytes of one K-contiguous tile row
   static constexpr int KCH = BK / 8;                   // 16-byte chunks per such row
-  static constexpr int KRP = 256 / KROW;               // such rows per 256-byte bank line
   static_assert(BK == 32 || BK == 64, "K step");
   static_assert(NSTAGE >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring");
   static_assert(LDS_BYTES >= 8 * 8192 + 6144, "epilogue staging fits in the ring");
-  // K-contiguous tile: row m at m*KROW, chunk q at position q ^ ((m/KRP) % KCH)
+  // K-contiguous tile: row m at m*KROW, chunk q at position q ^ kswz(m); the
+  // position changes every two rows
+  static __device__ __forceinline__ int kswz(int m) { return (m >> 1) % KCH; }
   static __device__ __forceinline__ int kmaj_off(int m, int q) {
-    return m * KROW + ((q ^ ((m / KRP) % KCH)) << 4);
+    return m * KROW + ((q ^ kswz(m)) << 4);
   }
 };
 static_assert(BM == BN, "operand tiles share one LDS geometry");
@@ -71,10 +72,12 @@ static_assert(BM == BN, "operand tiles share one LDS geometry");
 // LDS tile layouts (256 MN x 32 K, bf16):
 // (BK = K step; see KCfg)
 //  K-contiguous:  row m (2 BK bytes) at m*2BK; its 16-byte k chunk q (k =
-//                 8q..8q+7) sits at chunk position q ^ ((m / KRP) % KCH),
-//                 KRP rows sharing one 256-byte bank line.  16 lanes that read
-//                 chunk q of rows m..m+15 (m % 16 == 0) hit 16 distinct 16-byte
-//                 bank groups.
+//                 8q..8q+7) sits at chunk position q ^ ((m / 2) % KCH).  The
+//                 16 lanes that read chunk q of rows m..m+15 (m % 16 == 0)
+//                 are then free of bank conflicts for 128- and 64-byte rows
+//                 (measured with rocprofv3's LDS bank-conflict counter; with
+//                 64-byte rows a position that changed every four rows, one
+//                 256-byte bank line, conflicted 2-way).
 //  MN-contiguous: row k (512 B) at k*512; its 16-byte MN chunk c (mn =
 //                 8c..8c+7) sits at chunk position c ^ mn_swz(k), mn_swz(k) =
 //                 ((k & 3) << 2) | (((k >> 3) & 1) << 1).  A transpose read
@@ -188,7 +191,7 @@ template <class KC, int NT, bool GATED>
 struct LoaderKMajor {
   static constexpr int LP = KC::OPER_BYTES / 1024 / (NT / 64);
   static constexpr int R = 1024 / KC::KROW;       // tile rows per load
-  static_assert(LP % 2 == 0 && (2 * R / KC::KRP) % KC::KCH == 0, "swizzle period");
+  static_assert(LP % 2 == 0 && R % KC::KCH == 0, "swizzle period");
   __amdgpu_buffer_rsrc_t rs;
   uint32_t gbase[2];    // byte offset of the lane's row and chunk at k0 = 0 (loads 0 and 1)
   int kq[2];            // k offset of the lane's chunk (even / odd loads)
@@ -206,7 +209,7 @@ struct LoaderKMajor {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int m = R * (LP * w + p) + l / KC::KCH;
-      const int q = (l % KC::KCH) ^ ((m / KC::KRP) % KC::KCH);
+      const int q = (l % KC::KCH) ^ KC::kswz(m);
       kq[p] = 8 * q;
       gbase[p] = (uint32_t)(row0 + m) * ldb + (uint32_t)(16 * q);
     }
@@ -1273,11 +1276,24 @@ __global__ void dy_kernel(__bf16* __restrict__ dR, const __bf16* __restrict__ y,
 // Wave grid used for every bf16 GEMM: 2 x 4 waves (two per SIMD).
 constexpr int kWavesM = 2, kWavesN = 4;
 
-template <bool AK, bool BKM, int EPI>
+// K step / ring depth: 64 x 2 when an operand is K-contiguous, else 32 x 4.
+// A GEMM with both operands K-contiguous whose operands together outgrow the
+// MALL (the 256 MiB memory-side cache) also takes 32 x 4 (DEEP): its loads
+// then see HBM latency, which loads two 32-k steps ahead hide better than
+// three quarters of a 64-k step, and that outweighs the shorter 64-byte rows
+// (the dh GEMM of the RMSNorm backward, whose contraction runs over the wide
+// dimension N, measured 3.7% faster at the LLaMA-7B shape and 4.5% at the
+// 70B-hidden shape).
+#ifndef CODA_DEEP_MIN_MIB
+#define CODA_DEEP_MIN_MIB 256
+#endif
+constexpr int64_t kDeepMinBytes = (int64_t)CODA_DEEP_MIN_MIB << 20;
+
+template <bool AK, bool BKM, int EPI, bool DEEP = false>
 static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
-  // K step / ring depth: 64 x 2 when an operand is K-contiguous, else 32 x 4
-  constexpr int BKv = (AK || BKM) ? 64 : 32;
-  constexpr int NSTv = (AK || BKM) ? 2 : 4;
+  static_assert(!DEEP || (AK && BKM), "the deep ring is for K-contiguous operand pairs");
+  constexpr int BKv = (AK || BKM) && !DEEP ? 64 : 32;
+  constexpr int NSTv = (AK || BKM) && !DEEP ? 2 : 4;
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (EPI == EPI_SWIGLU || EPI == EPI_RSQRT_SWIGLU) ? (g.N + BN / 2 - 1) / (BN / 2)
                                                                       : (g.N + BN - 1) / BN;
@@ -1302,10 +1318,15 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStr
       default: break;
     }
   } else if (ak && bk) {
+    const bool deep = ((int64_t)g.M + g.N) * g.K * 2 > kDeepMinBytes;
     switch (epi) {
-      case EPI_STORE: return launch_one<true, true, EPI_STORE>(g, s);
-      case EPI_DN: return launch_one<true, true, EPI_DN>(g, s);
-      case EPI_SWIGLU_BWD: return launch_one<true, true, EPI_SWIGLU_BWD>(g, s);
+      case EPI_STORE:
+        return deep ? launch_one<true, true, EPI_STORE, true>(g, s) : launch_one<true, true, EPI_STORE>(g, s);
+      case EPI_DN:
+        return deep ? launch_one<true, true, EPI_DN, true>(g, s) : launch_one<true, true, EPI_DN>(g, s);
+      case EPI_SWIGLU_BWD:
+        return deep ? launch_one<true, true, EPI_SWIGLU_BWD, true>(g, s)
+                    : launch_one<true, true, EPI_SWIGLU_BWD>(g, s);
       default: break;
     }
   } else if (!ak && !bk) {

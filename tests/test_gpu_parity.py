@@ -269,9 +269,27 @@ def _rows(M, rng, k=48):
 
 @pytest.mark.parametrize("name", ["llama1b_fwd", "llama7b_fwdbwd", "llama70b_fwdbwd"])
 def test_full_workload_coda(torch_dev, name):
+    _check_coda_workload(torch_dev, synth.WORKLOADS[name])
+
+
+# Both operands of the dh GEMM (dz [M, N] and W2 [d, N], contraction over N)
+# exceed the 256 MiB memory-side cache here, so it runs on the deep LDS ring
+# (32-k steps, four stages) that large K-contiguous operand pairs take; every
+# dimension is ragged (M, d: 8 past a tile; N: 8 past a 32-k step).
+RAGGED_WIDE = synth.Workload("ragged_wide_fwdbwd", "coda", "bf16", M=4104, K=520, d=1032, N=28680,
+                             eps=1e-6, seed=1011, backward=True)
+
+
+def test_ragged_wide_coda(torch_dev):
+    w = RAGGED_WIDE
+    assert (w.M + w.d) * w.N * 2 > 256 << 20
+    _check_coda_workload(torch_dev, w)
+
+
+def _check_coda_workload(torch_dev, w):
     torch, dev = torch_dev
     import gemm_epilogue_fusion_gemm1_amd as coda
-    w = synth.WORKLOADS[name]
+    name = w.name
     print(f"[parity] {name}: generating inputs", flush=True)
     h = synth.workload_inputs(w)
     t = {k: up(torch, dev, v, w.dtype) for k, v in h.items()}
@@ -308,10 +326,26 @@ def test_full_workload_coda(torch_dev, name):
 
 
 def test_full_workload_swiglu(torch_dev):
+    _check_swiglu_workload(torch_dev, synth.WORKLOADS["swiglu_fwdbwd"])
+
+
+# The dX GEMM (dgu [M, 2F] times W [d, 2F] transposed, contraction over 2F)
+# has operands beyond 256 MiB, so it takes the deep LDS ring; M, d and F are
+# ragged.
+RAGGED_WIDE_SWIGLU = synth.Workload("ragged_wide_swiglu", "swiglu", "bf16", M=4104, d=1032, F=14344,
+                                    seed=1012, backward=True)
+
+
+def test_ragged_wide_swiglu(torch_dev):
+    w = RAGGED_WIDE_SWIGLU
+    assert (w.M + w.d) * 2 * w.F * 2 > 256 << 20
+    _check_swiglu_workload(torch_dev, w)
+
+
+def _check_swiglu_workload(torch_dev, w):
     torch, dev = torch_dev
     import gemm_epilogue_fusion_gemm1_amd as coda
-    w = synth.WORKLOADS["swiglu_fwdbwd"]
-    print("[parity] swiglu_fwdbwd: generating inputs", flush=True)
+    print(f"[parity] {w.name}: generating inputs", flush=True)
     h = synth.workload_inputs(w)
     t = {k: up(torch, dev, v, "bf16") for k, v in h.items()}
     z, gu, a = coda.swiglu_fwd(t["X"], t["W"], t["Wd"])
@@ -319,7 +353,7 @@ def test_full_workload_swiglu(torch_dev):
     torch.cuda.synchronize()
     rng = np.random.default_rng(w.seed)
     rows = _rows(w.M, rng, k=24)
-    print("[parity] swiglu_fwdbwd: oracle", flush=True)
+    print(f"[parity] {w.name}: oracle", flush=True)
     fr = oracle.ref_swiglu_fwd_rows(h["X"], h["W"], h["Wd"], rows)
     cw = np.unique(np.concatenate([[0, w.F - 1, w.F, 2 * w.F - 1], rng.choice(2 * w.F, 12, replace=False)]))
     rd = np.unique(np.concatenate([[0, w.F - 1], rng.choice(w.F, 10, replace=False)]))
@@ -327,7 +361,7 @@ def test_full_workload_swiglu(torch_dev):
     errs = {"z_rows": rel(host(z[rows]), fr["z"]), "gu_rows": rel(host(gu[rows]), fr["gu"]),
             "a_rows": rel(host(a[rows]), fr["a"]), "dX_rows": rel(host(dX[rows]), bs["dX_rows"]),
             "dW_cols": rel(host(dW[:, cw]), bs["dW_cols"]), "dWd_rows": rel(host(dWd[rd]), bs["dWd_rows"])}
-    report("swiglu_fwdbwd", errs)
+    report(w.name, errs)
     for k, v in errs.items():
         assert v <= BF16_TOL, (k, v)
 
