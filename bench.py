@@ -583,7 +583,7 @@ def sustained_sclk(torch, step, seconds=2.5):
                     samples.append(int(m.group(1)))
                     break
             for line in out.splitlines():
-                m = re.search(r"Package Power \(W\):\s*([\d.]+)", line)
+                m = re.search(r"Power.*\(W\):\s*([\d.]+)", line)
                 if m:
                     power.append(float(m.group(1)))
                     break
