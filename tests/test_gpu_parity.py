@@ -342,6 +342,19 @@ def test_ragged_wide_swiglu(torch_dev):
     _check_swiglu_workload(torch_dev, w)
 
 
+# Here the da GEMM of the SwiGLU backward (dz [M, d] times Wd [F, d]
+# transposed, contraction over d, with the SwiGLU-backward epilogue) also
+# has operands beyond 256 MiB and takes the deep ring; ragged everywhere.
+RAGGED_WIDE_SWIGLU_DA = synth.Workload("ragged_wide_swiglu_da", "swiglu", "bf16", M=4104, d=4360, F=28680,
+                                       seed=1013, backward=True)
+
+
+def test_ragged_wide_swiglu_da(torch_dev):
+    w = RAGGED_WIDE_SWIGLU_DA
+    assert (w.M + w.F) * w.d * 2 > 256 << 20
+    _check_swiglu_workload(torch_dev, w)
+
+
 def _check_swiglu_workload(torch_dev, w):
     torch, dev = torch_dev
     import gemm_epilogue_fusion_gemm1_amd as coda
