@@ -550,7 +550,7 @@ def measured_traffic(kernel):
 
 # ------------------------------------------------------------- CPU baseline
 
-def sustained_sclk(torch, step, seconds=2.5):
+def sustained_sclk(torch, step, seconds=4.0):
     """Shader clock while the step runs back to back: rocm-smi's current sclk
     sampled every ~0.25 s from a thread while the GPU repeats the step for
     `seconds`.  Dense MFMA work with changing operands is power-limited on
@@ -569,12 +569,12 @@ def sustained_sclk(torch, step, seconds=2.5):
     if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
         return None
     samples, power, done = [], [], threading.Event()
+    amd = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
 
     def sample():
         while not done.is_set():
             try:
-                out = subprocess.run([exe, "--showclocks", "--showpower"], capture_output=True, text=True,
-                                     timeout=5).stdout
+                out = subprocess.run([exe, "--showclocks"], capture_output=True, text=True, timeout=5).stdout
             except Exception:  # pragma: no cover - tool failure
                 return
             for line in out.splitlines():
@@ -582,11 +582,17 @@ def sustained_sclk(torch, step, seconds=2.5):
                 if m:
                     samples.append(int(m.group(1)))
                     break
-            for line in out.splitlines():
-                m = re.search(r"Power.*\(W\):\s*([\d.]+)", line)
-                if m:
-                    power.append(float(m.group(1)))
-                    break
+            done.wait(0.25)
+
+    def sample_power():   # socket power from amd-smi (rocm-smi reports none on this part)
+        while amd and not done.is_set():
+            try:
+                out = subprocess.run([amd, "metric", "-p", "--json"], capture_output=True, text=True,
+                                     timeout=10).stdout
+                v = json.loads(out)["gpu_data"][0]["power"]["socket_power"]["value"]
+                power.append(float(v))
+            except Exception:  # pragma: no cover - tool failure or another format
+                return
             done.wait(0.25)
 
     for _ in range(3):
@@ -594,6 +600,8 @@ def sustained_sclk(torch, step, seconds=2.5):
     torch.cuda.synchronize()
     th = threading.Thread(target=sample, daemon=True)
     th.start()
+    tp = threading.Thread(target=sample_power, daemon=True)
+    tp.start()
     t0 = time.time()
     while time.time() - t0 < seconds:
         for _ in range(8):
@@ -601,14 +609,15 @@ def sustained_sclk(torch, step, seconds=2.5):
         torch.cuda.synchronize()
     done.set()
     th.join(timeout=10)
+    tp.join(timeout=15)
     samples = samples[2:] if len(samples) > 4 else samples   # drop the ramp
-    power = power[2:] if len(power) > 4 else power
+    power = power[1:] if len(power) > 2 else power
     if not samples:
         return None
     srt = sorted(samples)
     res = {"median_mhz": srt[len(srt) // 2], "min_mhz": srt[0], "max_mhz": srt[-1], "samples": len(srt),
-           "method": "rocm-smi --showclocks --showpower every ~0.25 s while the fused step repeats for %.1f s"
-                     % seconds}
+           "method": "rocm-smi --showclocks (and amd-smi metric -p for the socket power) every ~0.25 s "
+                     "while the fused step repeats for %.1f s" % seconds}
     if power:
         pw = sorted(power)
         res["power_median_w"] = pw[len(pw) // 2]
