@@ -675,7 +675,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the fused block is "
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the fused block is "
                           "benchmarked on a single MI355X; run with --gpus 1"}), flush=True)
         sys.exit(2)
 

@@ -57,7 +57,7 @@ typedef enum {
   CODA_ERR_DTYPE = 5,       /* dtype is not a coda_dtype value */
   CODA_ERR_EPS = 6,         /* eps is not finite or not > 0 */
   CODA_ERR_WORKSPACE = 7,   /* workspace is NULL or smaller than the matching *_workspace_bytes */
-  CODA_ERR_UNSUPPORTED = 8, /* valid request this build does not implement (e.g. f32 backward) */
+  CODA_ERR_UNSUPPORTED = 8, /* valid request this library does not implement (e.g. f32 backward) */
   CODA_ERR_HIP = 9          /* a HIP runtime call or kernel launch failed */
 } coda_status;
 
@@ -117,7 +117,7 @@ coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
  *   dz [M,N]: in.   dX [M,K], dW1 [K,d], dR [M,d], dW2 [d,N]: out (dtype).
  *   dgamma [d]: out, float32.
  *   workspace: >= coda_bwd_workspace_bytes(dtype, M, K, d, N) bytes.
- * CODA_F32 returns CODA_ERR_UNSUPPORTED in this build.
+ * CODA_F32 returns CODA_ERR_UNSUPPORTED in this library.
  * ---------------------------------------------------------------------- */
 size_t coda_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N);
 coda_status coda_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N,
@@ -137,7 +137,7 @@ coda_status coda_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
  *
  *   X [M,d], W [d,2F], Wd [F,d]: in.   gu [M,2F], a [M,F]: out, saved for the
  *   backward.   z [M,d]: out.   No workspace is needed (pass NULL, 0).
- * CODA_F32 returns CODA_ERR_UNSUPPORTED in this build.
+ * CODA_F32 returns CODA_ERR_UNSUPPORTED in this library.
  * ---------------------------------------------------------------------- */
 size_t coda_swiglu_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t d, int64_t F);
 coda_status coda_swiglu_fwd(coda_dtype dtype, int64_t M, int64_t d, int64_t F,
@@ -156,7 +156,7 @@ coda_status coda_swiglu_fwd(coda_dtype dtype, int64_t M, int64_t d, int64_t F,
  *   X [M,d], W [d,2F], Wd [F,d], gu [M,2F], a [M,F], dz [M,d]: in.
  *   dX [M,d], dW [d,2F], dWd [F,d]: out.
  *   workspace: >= coda_swiglu_bwd_workspace_bytes(...) bytes (holds dgu).
- * CODA_F32 returns CODA_ERR_UNSUPPORTED in this build.
+ * CODA_F32 returns CODA_ERR_UNSUPPORTED in this library.
  * ---------------------------------------------------------------------- */
 size_t coda_swiglu_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t d, int64_t F);
 coda_status coda_swiglu_bwd(coda_dtype dtype, int64_t M, int64_t d, int64_t F,
@@ -184,7 +184,7 @@ coda_status coda_swiglu_bwd(coda_dtype dtype, int64_t M, int64_t d, int64_t F,
  *   out, saved for the backward.   z [M,d]: out.
  *   workspace: >= coda_mlp_fwd_workspace_bytes(...) bytes, 16-byte aligned,
  *   contents ignored (partial sums and y*gamma).
- * Errors as coda_fwd; CODA_F32 returns CODA_ERR_UNSUPPORTED in this build.
+ * Errors as coda_fwd; CODA_F32 returns CODA_ERR_UNSUPPORTED in this library.
  * ---------------------------------------------------------------------- */
 size_t coda_mlp_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t F);
 coda_status coda_mlp_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t F, float eps,
@@ -212,7 +212,7 @@ coda_status coda_mlp_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int6
  *   workspace: >= coda_mlp_bwd_workspace_bytes(...) bytes (dgu, then the
  *   block backward's n, partial sums and c).
  * dy_in may not overlap an output (CODA_ERR_ALIAS).  Other errors as
- * coda_bwd; CODA_F32 returns CODA_ERR_UNSUPPORTED in this build.
+ * coda_bwd; CODA_F32 returns CODA_ERR_UNSUPPORTED in this library.
  * ---------------------------------------------------------------------- */
 size_t coda_mlp_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t F);
 coda_status coda_mlp_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t F,
@@ -254,7 +254,7 @@ coda_status coda_ce_fwd(coda_dtype dtype, int64_t M, int64_t d, int64_t V, const
  *   h [M,d], Wv [d,V], labels [M] (int32), logits [M,V], lse [M] (float32),
  *   dloss [M] (float32): in.   dh [M,d], dWv [d,V]: out (dtype).
  *   workspace: >= coda_ce_bwd_workspace_bytes(...) bytes (holds dlogits).
- * CODA_F32 returns CODA_ERR_UNSUPPORTED in this build.
+ * CODA_F32 returns CODA_ERR_UNSUPPORTED in this library.
  * ---------------------------------------------------------------------- */
 size_t coda_ce_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t d, int64_t V);
 coda_status coda_ce_bwd(coda_dtype dtype, int64_t M, int64_t d, int64_t V, const void* h,
@@ -278,7 +278,7 @@ coda_status coda_ce_bwd(coda_dtype dtype, int64_t M, int64_t d, int64_t V, const
  *   N_rot a multiple of D and <= N, 1 <= S, base finite and > 0, else
  *   CODA_ERR_SHAPE.  workspace: >= coda_rope_fwd_workspace_bytes(...) bytes
  *   (the cos / sin table, S x D floats, built per call in double precision).
- * CODA_F32 returns CODA_ERR_UNSUPPORTED in this build.
+ * CODA_F32 returns CODA_ERR_UNSUPPORTED in this library.
  * ---------------------------------------------------------------------- */
 size_t coda_rope_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t N,
                                      int64_t N_rot, int64_t D, int64_t S);
