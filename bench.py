@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-also", action="store_true", help="skip the 70B, SwiGLU, MLP, cross-entropy, RoPE, MXFP8 and 1B workloads")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused torch baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--compiled-baseline", action="store_true",
+                    help="also time the unfused step with its forward under torch.compile (main workload)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (reference for the "
@@ -452,7 +454,7 @@ def kernel_table(trace, steps):
     return out
 
 
-def run_case(case, torch, coda, steps, warmup, unfused):
+def run_case(case, torch, coda, steps, warmup, unfused, compiled=False):
     """Two timed regions of `steps` fused steps each: the first plain (its
     time is the throughput), the second with every kernel bracketed by HIP
     events recorded by the library on the kernel's stream (per-kernel
@@ -483,6 +485,27 @@ def run_case(case, torch, coda, steps, warmup, unfused):
         if hasattr(case, "unfused_check"):
             res["unfused_check_rel"] = case.unfused_check()
         del case.leaf, case.graph
+        if compiled:
+            # The same unfused step with its forward under torch.compile
+            # (inductor fuses the elementwise ops of the forward and of the
+            # backward it derives; the GEMMs stay hipBLASLt calls).
+            try:
+                import torch._functorch.config as fconf
+                fconf.donated_buffer = False   # the backward is replayed with retain_graph
+                case.unfused_fwd = torch.compile(case.unfused_fwd)
+                _Steps.unfused_setup(case)   # compiles the forward
+                res["compiled_ms_per_step"] = time_steps(torch, lambda: _Steps.unfused_step(case), steps,
+                                                         max(warmup, 3))
+                if case.backward:
+                    res["compiled_fwd_ms"] = time_steps(torch, lambda: _Steps.unfused_fwd(case), steps, 1)
+                    res["compiled_bwd_ms"] = time_steps(torch, lambda: _Steps.unfused_bwd(case), steps, 1)
+            except Exception as e:  # reported, not fatal: the baseline is context
+                res["compiled_error"] = repr(e)[:300]
+            finally:
+                del case.unfused_fwd
+                for k in ("leaf", "graph"):
+                    if hasattr(case, k):
+                        delattr(case, k)
     return res
 
 
@@ -500,6 +523,11 @@ def summary(case, res):
         out["unfused_blas"] = res["unfused_blas"]
         if "unfused_check_rel" in res:
             out["unfused_first_gemm_vs_fused_y_rel"] = round(res["unfused_check_rel"], 5)
+    if "compiled_ms_per_step" in res:
+        out["compiled_unfused_ms_per_step"] = round(res["compiled_ms_per_step"], 4)
+        out["speedup_vs_compiled_unfused"] = round(res["compiled_ms_per_step"] / res["ms_per_step"], 3)
+    if "compiled_error" in res:
+        out["compiled_unfused_error"] = res["compiled_error"]
     if case.w.kind == "mx8":
         out["pct_fp8_peak"] = round(100.0 * tf / PEAK_FP8_TFLOPS, 2)
     for part, fl in (("fwd", case.w.flops_fwd()), ("bwd", case.w.flops_bwd())):
@@ -509,6 +537,9 @@ def summary(case, res):
             if f"unfused_{part}_ms" in res:
                 d["unfused_ms"] = round(res[f"unfused_{part}_ms"], 4)
                 d["speedup_vs_unfused"] = round(res[f"unfused_{part}_ms"] / res[f"{part}_ms"], 3)
+            if f"compiled_{part}_ms" in res:
+                d["compiled_unfused_ms"] = round(res[f"compiled_{part}_ms"], 4)
+                d["speedup_vs_compiled_unfused"] = round(res[f"compiled_{part}_ms"] / res[f"{part}_ms"], 3)
             out[part] = d
     return out
 
@@ -700,7 +731,7 @@ def main():
     print(f"[bench] {w.name}: inputs", file=sys.stderr, flush=True)
     case, host = make_case(w, torch, coda)
     print(f"[bench] {w.name}: timing {args.steps} steps", file=sys.stderr, flush=True)
-    res = run_case(case, torch, coda, args.steps, args.warmup, unfused)
+    res = run_case(case, torch, coda, args.steps, args.warmup, unfused, args.compiled_baseline)
     main_sum = summary(case, res)
     kernels = res["kernels"]
     rf = roofline(kernels, res["ms_per_step_traced"])
@@ -749,6 +780,8 @@ def main():
         "speedup_vs_unfused": main_sum.get("speedup_vs_unfused"),
         "unfused_ms_per_step": main_sum.get("unfused_ms_per_step"),
         "unfused_blas": main_sum.get("unfused_blas"),
+        **{k: main_sum[k] for k in ("compiled_unfused_ms_per_step", "speedup_vs_compiled_unfused",
+                                    "compiled_unfused_error") if k in main_sum},
         "ms_per_step_traced": main_sum["ms_per_step_traced"],
         "step_times": main_sum["step_times"],
         "fwd": main_sum.get("fwd"),

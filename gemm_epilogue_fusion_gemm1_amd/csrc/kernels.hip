@@ -1277,13 +1277,15 @@ __global__ void dy_kernel(__bf16* __restrict__ dR, const __bf16* __restrict__ y,
 constexpr int kWavesM = 2, kWavesN = 4;
 
 // K step / ring depth: 64 x 2 when an operand is K-contiguous, else 32 x 4.
-// A GEMM with both operands K-contiguous whose operands together outgrow the
+// A GEMM with a K-contiguous A operand whose operands together outgrow the
 // MALL (the 256 MiB memory-side cache) also takes 32 x 4 (DEEP): its loads
 // then see HBM latency, which loads two 32-k steps ahead hide better than
 // three quarters of a 64-k step, and that outweighs the shorter 64-byte rows
-// (the dh GEMM of the RMSNorm backward, whose contraction runs over the wide
-// dimension N, measured 3.7% faster at the LLaMA-7B shape and 4.5% at the
-// 70B-hidden shape).
+// (measured: the dh GEMM of the RMSNorm backward 3.7% faster at the
+// LLaMA-7B shape and 4.5% at the 70B-hidden shape; the SwiGLU down GEMM 10%,
+// the LM-head logits GEMM 7.5%).  In the forward layout (B MN-contiguous)
+// only the epilogues whose GEMMs reach that size in the block's workloads
+// (plain store, SwiGLU, cross-entropy statistics) take it.
 #ifndef CODA_DEEP_MIN_MIB
 #define CODA_DEEP_MIN_MIB 256
 #endif
@@ -1291,7 +1293,7 @@ constexpr int64_t kDeepMinBytes = (int64_t)CODA_DEEP_MIN_MIB << 20;
 
 template <bool AK, bool BKM, int EPI, bool DEEP = false>
 static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
-  static_assert(!DEEP || (AK && BKM), "the deep ring is for K-contiguous operand pairs");
+  static_assert(!DEEP || AK, "the deep ring is for a K-contiguous A operand");
   constexpr int BKv = (AK || BKM) && !DEEP ? 64 : 32;
   constexpr int NSTv = (AK || BKM) && !DEEP ? 2 : 4;
   const int tiles_m = (g.M + BM - 1) / BM;
@@ -1309,12 +1311,17 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStr
   //   both mn-major:      (y gamma)^T-stored times W2, and the weight
   //                       gradients n^T dz, X^T dy, a^T dz, X^T dgu
   if (ak && !bk) {
+    const bool deep = ((int64_t)g.M + g.N) * g.K * 2 > kDeepMinBytes;
     switch (epi) {
-      case EPI_STORE: return launch_one<true, false, EPI_STORE>(g, s);
+      case EPI_STORE:
+        return deep ? launch_one<true, false, EPI_STORE, true>(g, s) : launch_one<true, false, EPI_STORE>(g, s);
       case EPI_RESID_SUMSQ: return launch_one<true, false, EPI_RESID_SUMSQ>(g, s);
-      case EPI_CE_STATS: return launch_one<true, false, EPI_CE_STATS>(g, s);
+      case EPI_CE_STATS:
+        return deep ? launch_one<true, false, EPI_CE_STATS, true>(g, s)
+                    : launch_one<true, false, EPI_CE_STATS>(g, s);
       case EPI_ROPE: return launch_one<true, false, EPI_ROPE>(g, s);
-      case EPI_SWIGLU: return launch_one<true, false, EPI_SWIGLU>(g, s);
+      case EPI_SWIGLU:
+        return deep ? launch_one<true, false, EPI_SWIGLU, true>(g, s) : launch_one<true, false, EPI_SWIGLU>(g, s);
       default: break;
     }
   } else if (ak && bk) {
