@@ -1277,17 +1277,18 @@ __global__ void dy_kernel(__bf16* __restrict__ dR, const __bf16* __restrict__ y,
 constexpr int kWavesM = 2, kWavesN = 4;
 
 // K step / ring depth: 64 x 2 when an operand is K-contiguous, else 32 x 4.
-// A GEMM with a K-contiguous A operand whose operands together outgrow the
-// MALL (the 256 MiB memory-side cache) also takes 32 x 4 (DEEP): its loads
-// then see HBM latency, which loads two 32-k steps ahead hide better than
-// three quarters of a 64-k step, and that outweighs the shorter 64-byte rows
-// (measured: the dh GEMM of the RMSNorm backward 3.7% faster at the
-// LLaMA-7B shape and 4.5% at the 70B-hidden shape; the SwiGLU down GEMM 10%,
-// the LM-head logits GEMM 7.5%).  In the forward layout (B MN-contiguous)
-// only the epilogues whose GEMMs reach that size in the block's workloads
-// (plain store, SwiGLU, cross-entropy statistics) take it.
+// A GEMM with a K-contiguous A operand whose operands together take more
+// than half the MALL (the 256 MiB memory-side cache) also takes 32 x 4
+// (DEEP): much of its loads then see HBM latency, which loads two 32-k steps
+// ahead hide better than three quarters of a 64-k step, and that outweighs
+// the shorter 64-byte rows (measured: the dh GEMM of the RMSNorm backward
+// 3.7% faster at the LLaMA-7B shape and 4.5% at the 70B-hidden shape, the
+// SwiGLU down GEMM 10%, the LM-head logits GEMM 7.5%, the SwiGLU-backward
+// da GEMMs 3.5-4.7%, the 70B-hidden dX GEMM (201 MB) 5%, the rotary QKV
+// GEMM (167 MB) 4.8%, the 70B-hidden first GEMM 3%; a GEMM with 100 MB of
+// operands, the LLaMA-7B dX GEMM, runs faster on the 64 x 2 ring).
 #ifndef CODA_DEEP_MIN_MIB
-#define CODA_DEEP_MIN_MIB 256
+#define CODA_DEEP_MIN_MIB 128
 #endif
 constexpr int64_t kDeepMinBytes = (int64_t)CODA_DEEP_MIN_MIB << 20;
 
@@ -1315,11 +1316,14 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStr
     switch (epi) {
       case EPI_STORE:
         return deep ? launch_one<true, false, EPI_STORE, true>(g, s) : launch_one<true, false, EPI_STORE>(g, s);
-      case EPI_RESID_SUMSQ: return launch_one<true, false, EPI_RESID_SUMSQ>(g, s);
+      case EPI_RESID_SUMSQ:
+        return deep ? launch_one<true, false, EPI_RESID_SUMSQ, true>(g, s)
+                    : launch_one<true, false, EPI_RESID_SUMSQ>(g, s);
       case EPI_CE_STATS:
         return deep ? launch_one<true, false, EPI_CE_STATS, true>(g, s)
                     : launch_one<true, false, EPI_CE_STATS>(g, s);
-      case EPI_ROPE: return launch_one<true, false, EPI_ROPE>(g, s);
+      case EPI_ROPE:
+        return deep ? launch_one<true, false, EPI_ROPE, true>(g, s) : launch_one<true, false, EPI_ROPE>(g, s);
       case EPI_SWIGLU:
         return deep ? launch_one<true, false, EPI_SWIGLU, true>(g, s) : launch_one<true, false, EPI_SWIGLU>(g, s);
       default: break;

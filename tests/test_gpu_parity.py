@@ -272,17 +272,19 @@ def test_full_workload_coda(torch_dev, name):
     _check_coda_workload(torch_dev, synth.WORKLOADS[name])
 
 
-# Both operands of the dh GEMM (dz [M, N] and W2 [d, N], contraction over N)
-# exceed the 256 MiB memory-side cache here, so it runs on the deep LDS ring
-# (32-k steps, four stages) that large K-contiguous operand pairs take; every
-# dimension is ragged (M, d: 8 past a tile; N: 8 past a 32-k step).
-RAGGED_WIDE = synth.Workload("ragged_wide_fwdbwd", "coda", "bf16", M=4104, K=520, d=1032, N=28680,
+# The operands of the dh GEMM (dz [M, N] and W2 [d, N], contraction over N)
+# exceed the whole 256 MiB memory-side cache here (the deep LDS ring starts at
+# half of it), so it runs on the deep LDS ring
+# (32-k steps, four stages) that large K-contiguous operand pairs take, and
+# so does the first GEMM (X [M, K] and W1 [K, d]: 137 MB); every dimension is
+# ragged (M, d: 8 past a tile; N: 8 past a 32-k step; K: 8 past a 64-k step).
+RAGGED_WIDE = synth.Workload("ragged_wide_fwdbwd", "coda", "bf16", M=4104, K=13320, d=1032, N=28680,
                              eps=1e-6, seed=1011, backward=True)
 
 
 def test_ragged_wide_coda(torch_dev):
     w = RAGGED_WIDE
-    assert (w.M + w.d) * w.N * 2 > 256 << 20
+    assert (w.M + w.d) * w.N * 2 > 256 << 20 and (w.M + w.d) * w.K * 2 > 128 << 20
     _check_coda_workload(torch_dev, w)
 
 
@@ -330,7 +332,8 @@ def test_full_workload_swiglu(torch_dev):
 
 
 # The dX GEMM (dgu [M, 2F] times W [d, 2F] transposed, contraction over 2F)
-# has operands beyond 256 MiB, so it takes the deep LDS ring; M, d and F are
+# has operands beyond 256 MiB (past the deep ring's 128 MiB threshold), so it
+# takes the deep LDS ring; M, d and F are
 # ragged.
 RAGGED_WIDE_SWIGLU = synth.Workload("ragged_wide_swiglu", "swiglu", "bf16", M=4104, d=1032, F=14344,
                                     seed=1012, backward=True)
@@ -571,10 +574,26 @@ def test_rope_fwd_bwd(torch_dev, case):
 
 
 def test_full_workload_rope(torch_dev):
+    _check_rope_workload(torch_dev, synth.WORKLOADS["llama7b_qkv_rope_fwdbwd"])
+
+
+# The rotary projection's operands (X [M, K] and W [K, N]) exceed 128 MiB,
+# so its GEMM takes the deep LDS ring; M, K and N are ragged and positions
+# wrap at 1000 rows.
+RAGGED_WIDE_ROPE = synth.Workload("ragged_wide_rope", "rope", "bf16", M=4104, K=14344, N=1032,
+                                  rot=768, head=128, seq=1000, base=10000.0, seed=1014, backward=True)
+
+
+def test_ragged_wide_rope(torch_dev):
+    w = RAGGED_WIDE_ROPE
+    assert (w.M + w.N) * w.K * 2 > 128 << 20
+    _check_rope_workload(torch_dev, w)
+
+
+def _check_rope_workload(torch_dev, w):
     torch, dev = torch_dev
     import gemm_epilogue_fusion_gemm1_amd as coda
-    w = synth.WORKLOADS["llama7b_qkv_rope_fwdbwd"]
-    print("[parity] llama7b_qkv_rope_fwdbwd: generating inputs", flush=True)
+    print(f"[parity] {w.name}: generating inputs", flush=True)
     h = synth.workload_inputs(w)
     t = {k: up(torch, dev, v, "bf16") for k, v in h.items()}
     Y = coda.rope_fwd(t["X"], t["W"], w.rot, w.head, w.seq, w.base)
@@ -583,11 +602,11 @@ def test_full_workload_rope(torch_dev):
     rng = np.random.default_rng(w.seed)
     rows = np.unique(np.concatenate([_rows(w.M, rng, k=24), [w.seq - 1, w.seq, w.M - 2]]))
     cols = np.unique(np.concatenate([[0, 1, w.rot - 1, w.rot, w.N - 1], rng.choice(w.N, 16, replace=False)]))
-    print("[parity] llama7b_qkv_rope_fwdbwd: oracle", flush=True)
+    print(f"[parity] {w.name}: oracle", flush=True)
     fr = oracle.ref_rope_fwd_rows(h["X"], h["W"], w.rot, w.head, w.seq, w.base, rows)
     bs = oracle.ref_rope_bwd_sampled(h["X"], h["W"], h["dY"], w.rot, w.head, w.seq, w.base, rows, cols)
     errs = {"Y_rows": rel(host(Y[rows]), fr["Y"]), "dX_rows": rel(host(dX[rows]), bs["dX_rows"]),
             "dW_cols": rel(host(dW[:, cols]), bs["dW_cols"])}
-    report("llama7b_qkv_rope_fwdbwd", errs)
+    report(w.name, errs)
     for k, v in errs.items():
         assert v <= BF16_TOL, (k, v)
