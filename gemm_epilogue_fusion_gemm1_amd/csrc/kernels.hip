@@ -1324,6 +1324,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStr
                     : launch_one<true, false, EPI_CE_STATS>(g, s);
       case EPI_ROPE:
         return deep ? launch_one<true, false, EPI_ROPE, true>(g, s) : launch_one<true, false, EPI_ROPE>(g, s);
+      case EPI_RSQRT_SCALE:
+        return deep ? launch_one<true, false, EPI_RSQRT_SCALE, true>(g, s)
+                    : launch_one<true, false, EPI_RSQRT_SCALE>(g, s);
       case EPI_SWIGLU:
         return deep ? launch_one<true, false, EPI_SWIGLU, true>(g, s) : launch_one<true, false, EPI_SWIGLU>(g, s);
       default: break;

@@ -276,15 +276,17 @@ def test_full_workload_coda(torch_dev, name):
 # exceed the whole 256 MiB memory-side cache here (the deep LDS ring starts at
 # half of it), so it runs on the deep LDS ring
 # (32-k steps, four stages) that large K-contiguous operand pairs take, and
-# so does the first GEMM (X [M, K] and W1 [K, d]: 137 MB); every dimension is
+# so does the first GEMM (X [M, K] and W1 [K, d]: 164 MB); the second GEMM's
+# operands (135 MB) take the transposed y*gamma layout; every dimension is
 # ragged (M, d: 8 past a tile; N: 8 past a 32-k step; K: 8 past a 64-k step).
-RAGGED_WIDE = synth.Workload("ragged_wide_fwdbwd", "coda", "bf16", M=4104, K=13320, d=1032, N=28680,
+RAGGED_WIDE = synth.Workload("ragged_wide_fwdbwd", "coda", "bf16", M=4104, K=13320, d=2056, N=28680,
                              eps=1e-6, seed=1011, backward=True)
 
 
 def test_ragged_wide_coda(torch_dev):
     w = RAGGED_WIDE
     assert (w.M + w.d) * w.N * 2 > 256 << 20 and (w.M + w.d) * w.K * 2 > 128 << 20
+    assert (w.M + w.N) * w.d * 2 > 128 << 20
     _check_coda_workload(torch_dev, w)
 
 
