@@ -52,7 +52,8 @@ What the pages fix, and the readings taken where they are silent:
     tiles of a row, which cross-entropy uses ([JA]/[RU]/[FR] primitives
     sections).  Reading: logits = h Wv; lse_i = log sum_j exp(logits_ij);
     loss_i = lse_i - logits_i,label_i (mean-free, one loss per row); the
-    backward of L = sum_i dloss_i loss_i.
+    backward of L = sum_i dloss_i loss_i.  A label outside [0, V) marks an
+    ignored row (loss 0, no gradient), the usual ignore-index convention.
   * A rotary-position epilogue on a QKV projection (``ref_rope_*``): the
     pages list position encodings among the elementwise transforms an
     epilogue can carry ([JA]/[RU]/[FR] primitives sections).  Reading: Y = X W,
@@ -487,15 +488,25 @@ def _logsumexp_rows(x) -> np.ndarray:
     return m + np.log(np.sum(np.exp(x - m[:, None]), axis=1))
 
 
+def _ce_valid(labels, V):
+    """Rows whose label is a column index; the others are ignored rows."""
+    labels = np.asarray(labels, dtype=np.int64)
+    return labels, (labels >= 0) & (labels < V)
+
+
 def ref_ce_fwd(h, Wv, labels) -> dict:
     """logits = h Wv;  lse_i = log sum_j exp(logits_ij);
     loss_i = lse_i - logits_i,label_i.  ([JA]/[RU]/[FR] primitives sections:
-    cross-entropy over the stateful max / sum-exp epilogue.)"""
+    cross-entropy over the stateful max / sum-exp epilogue.)
+    A label outside [0, V) marks an ignored row (reading: the pages define no
+    label format; the usual ignore-index convention): its loss is 0 and it
+    contributes no gradient; its lse is still the row's."""
     h, Wv = _f64(h), _f64(Wv)
-    labels = np.asarray(labels, dtype=np.int64)
     logits = h @ Wv
+    labels, valid = _ce_valid(labels, logits.shape[1])
     lse = _logsumexp_rows(logits)
-    loss = lse - logits[np.arange(logits.shape[0]), labels]
+    picked = logits[np.arange(logits.shape[0]), np.where(valid, labels, 0)]
+    loss = np.where(valid, lse - picked, 0.0)
     return {"logits": logits, "lse": lse, "loss": loss}
 
 
@@ -528,15 +539,17 @@ def ref_ce_bwd(h, Wv, labels, lse, dloss, logits=None) -> dict:
     """Exact gradient of L = sum_i dloss_i loss_i for ``ref_ce_fwd``, given the
     saved lse (and the saved logits, if passed; else they are recomputed):
       p = exp(logits - lse) (softmax by rows);  dlogits = diag(dloss) (p - onehot(labels));
-      dh = dlogits Wv^T;  dWv = h^T dlogits."""
+      dh = dlogits Wv^T;  dWv = h^T dlogits.
+    An ignored row (label outside [0, V)) has loss 0, so its dlogits row is 0."""
     h, Wv = _f64(h), _f64(Wv)
-    labels = np.asarray(labels, dtype=np.int64)
     lse, dloss = _f64(lse), _f64(dloss)
     logits = h @ Wv if logits is None else _f64(logits)
+    labels, valid = _ce_valid(labels, logits.shape[1])
     p = np.exp(logits - lse[:, None])
     dlogits = p
-    dlogits[np.arange(p.shape[0]), labels] -= 1.0
-    dlogits = dlogits * dloss[:, None]
+    rows = np.nonzero(valid)[0]
+    dlogits[rows, labels[rows]] -= 1.0
+    dlogits = dlogits * np.where(valid, dloss, 0.0)[:, None]
     return {"dh": dlogits @ Wv.T, "dWv": h.T @ dlogits, "dlogits": dlogits}
 
 
@@ -553,8 +566,9 @@ def ref_ce_bwd_sampled(h, Wv, labels, lse, dloss, rows, cols_V, logits=None) -> 
     ``cols_V``: dh rows need only those rows' dlogits; dWv columns need every
     row's dlogits in those columns."""
     h, Wv = _f64(h), _f64(Wv)
-    labels = np.asarray(labels, dtype=np.int64)
+    labels, valid = _ce_valid(labels, Wv.shape[1])
     lse, dloss = _f64(lse), _f64(dloss)
+    dloss = np.where(valid, dloss, 0.0)
     rows, cols_V = np.asarray(rows), np.asarray(cols_V)
 
     def dlog(lg, lab, ls, dl, cols):

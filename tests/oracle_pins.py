@@ -549,6 +549,47 @@ def pin_ce_torch(O):
         _close(b["dWv"], tw.grad.numpy(), 1e-12, "ce dWv vs torch")
 
 
+def pin_ce_ignored_rows(O):
+    """Ignored rows (labels outside [0, V)): torch CPU float64
+    F.cross_entropy with ignore_index=-100 and reduction='none' (library
+    routine) gives loss 0 and zero gradients for the rows labelled -100; the
+    other out-of-range labels (-1, V, a large index) give the same loss 0 and
+    zero dlogits row, and the remaining rows equal the result of the call
+    without the ignored rows."""
+    import torch
+    import torch.nn.functional as Fn
+    c = _ce_case(67, 10, 8, 60, scale=2.0)
+    lab = c["labels"].copy()
+    lab[[1, 6]] = -100
+    th = torch.tensor(c["h"], requires_grad=True)
+    tw = torch.tensor(c["Wv"], requires_grad=True)
+    loss = Fn.cross_entropy(th @ tw, torch.tensor(lab), reduction="none", ignore_index=-100)
+    (loss * torch.from_numpy(c["dloss"])).sum().backward()
+    f = O.ref_ce_fwd(c["h"], c["Wv"], lab)
+    _close(f["loss"], loss.detach().numpy(), 1e-13, "ce ignored rows: loss vs torch")
+    b = O.ref_ce_bwd(c["h"], c["Wv"], lab, f["lse"], c["dloss"])
+    _close(b["dh"], th.grad.numpy(), 1e-12, "ce ignored rows: dh vs torch")
+    _close(b["dWv"], tw.grad.numpy(), 1e-12, "ce ignored rows: dWv vs torch")
+    lab2 = c["labels"].copy()
+    bad = [0, 4, 9]
+    lab2[bad] = [-1, 60, 1 << 30]
+    f2 = O.ref_ce_fwd(c["h"], c["Wv"], lab2)
+    b2 = O.ref_ce_bwd(c["h"], c["Wv"], lab2, f2["lse"], c["dloss"])
+    assert np.all(f2["loss"][bad] == 0.0), "ce ignored rows: loss not 0"
+    assert np.all(b2["dlogits"][bad] == 0.0), "ce ignored rows: dlogits row not 0"
+    keep = np.setdiff1d(np.arange(10), bad)
+    fk = O.ref_ce_fwd(c["h"][keep], c["Wv"], c["labels"][keep])
+    bk = O.ref_ce_bwd(c["h"][keep], c["Wv"], c["labels"][keep], fk["lse"], c["dloss"][keep])
+    _close(f2["loss"][keep], fk["loss"], 1e-14, "ce ignored rows: other losses")
+    _close(f2["lse"], O.ref_ce_fwd(c["h"], c["Wv"], c["labels"])["lse"], 1e-14, "ce ignored rows: lse kept")
+    _close(b2["dWv"], bk["dWv"], 1e-12, "ce ignored rows: dWv from the other rows")
+    _close(b2["dh"][keep], bk["dh"], 1e-12, "ce ignored rows: dh of the other rows")
+    assert np.all(b2["dh"][bad] == 0.0), "ce ignored rows: dh row not 0"
+    s = O.ref_ce_bwd_sampled(c["h"], c["Wv"], lab2, f2["lse"], c["dloss"], np.arange(10), np.arange(60))
+    _close(s["dh_rows"], b2["dh"], 1e-12, "ce ignored rows: sampled dh")
+    _close(s["dWv_cols"], b2["dWv"], 1e-12, "ce ignored rows: sampled dWv")
+
+
 def pin_ce_finite_differences(O):
     """Central differences of L = sum_i dloss_i loss_i, tiny shape."""
     c = _ce_case(62, 3, 4, 7)
@@ -1039,7 +1080,7 @@ ALL_PINS = [
     pin_swiglu_finite_differences, pin_swiglu_torch, pin_swiglu_invariants,
     pin_golden_swiglu, pin_swiglu_sampled, pin_bf16_rne, pin_mlp_finite_differences,
     pin_mlp_torch, pin_mlp_invariants, pin_mlp_sampled, pin_mlp_dgu_rounding,
-    pin_mlp_stored_operand_bruteforce, pin_ce_torch, pin_ce_finite_differences,
+    pin_mlp_stored_operand_bruteforce, pin_ce_torch, pin_ce_ignored_rows, pin_ce_finite_differences,
     pin_ce_closed_forms, pin_ce_invariants, pin_ce_partials, pin_ce_sampled,
     pin_rope_bruteforce, pin_rope_torch, pin_rope_finite_differences, pin_rope_properties,
     pin_rope_sampled,

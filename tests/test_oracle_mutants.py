@@ -183,6 +183,25 @@ def _ce_bwd_variant(kind):
     return bwd
 
 
+def ce_fwd_labels_wrap(h, Wv, labels):
+    """Out-of-range labels taken modulo V instead of ignoring the row."""
+    V = np.asarray(Wv).shape[1]
+    return oracle.ref_ce_fwd(h, Wv, np.mod(np.asarray(labels, dtype=np.int64), V))
+
+
+def ce_bwd_ignored_keep_softmax(h, Wv, labels, lse, dloss, logits=None):
+    """Ignored rows keep dloss * softmax (only the one-hot term dropped)."""
+    out = dict(oracle.ref_ce_bwd(h, Wv, labels, lse, dloss, logits))
+    h64, W64 = _f(h, Wv)
+    lab = np.asarray(labels, dtype=np.int64)
+    bad = (lab < 0) | (lab >= W64.shape[1])
+    lg = h64 @ W64 if logits is None else np.asarray(logits, dtype=np.float64)
+    dl = out["dlogits"].copy()
+    dl[bad] = np.exp(lg[bad] - np.asarray(lse, dtype=np.float64)[bad, None]) * np.asarray(dloss)[bad, None]
+    out.update({"dlogits": dl, "dh": dl @ W64.T, "dWv": h64.T @ dl})
+    return out
+
+
 def ce_partials_no_rescale(logits, BN=256):
     out = dict(oracle.ref_ce_partials(logits, BN))
     x = np.asarray(logits, dtype=np.float64)
@@ -352,6 +371,8 @@ MUTANTS = {
     "ce_bwd_no_onehot": {"ref_ce_bwd": _ce_bwd_variant("no_onehot")},
     "ce_bwd_no_dloss": {"ref_ce_bwd": _ce_bwd_variant("no_dloss")},
     "ce_partials_no_rescale": {"ref_ce_partials": ce_partials_no_rescale},
+    "ce_labels_wrap_instead_of_ignore": {"ref_ce_fwd": ce_fwd_labels_wrap},
+    "ce_bwd_ignored_rows_keep_softmax": {"ref_ce_bwd": ce_bwd_ignored_keep_softmax},
     "rope_half_split_pairs": _rope_mutant("half_split"),
     "rope_sin_sign": _rope_mutant("sin_sign"),
     "rope_position_not_wrapped": _rope_mutant("no_wrap"),
