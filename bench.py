@@ -10,10 +10,13 @@ dense bf16 MFMA peak, the speed-up over an unfused hipBLASLt + F.rms_norm +
 autograd step on the same GPU (for the step, and for the forward and the
 backward alone), the median / min / max step time, per-kernel times from HIP
 events recorded on the stream the kernels run on, the roofline of the
-dominant kernel, the same figures for the 70B-hidden, SwiGLU, MLP sub-layer
-(the two chained), LM-head cross-entropy, rotary QKV projection, the
-MXFP8 block forward and the 1B-hidden (forward only) workloads under "also", and the CPU oracle timed on
-a bounded sample of the same workload.
+dominant kernel, and the CPU oracle timed on a bounded sample of the same
+workload.  The 70B-hidden block (M = 4096, K = d = 8192, N = 28672), the
+other half of the headline, is timed with the same steps and warm-up and
+sits beside the 7B figures under "headline"; the other fused patterns
+(SwiGLU, MLP sub-layer, LM-head cross-entropy, rotary QKV projection, MXFP8
+block forward, 1B-hidden forward) get a short entry under "also".  The
+per-kernel tables of every workload go to stderr (and to --details FILE).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-also] [--no-cpu-baseline]
 """
@@ -42,12 +45,15 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama7b_fwdbwd")
-    ap.add_argument("--no-also", action="store_true", help="skip the 70B, SwiGLU, MLP, cross-entropy, RoPE, MXFP8 and 1B workloads")
+    ap.add_argument("--no-also", action="store_true",
+                    help="time the main workload only (skip the 70B-hidden block and the other patterns)")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused torch baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--compiled-baseline", action="store_true",
                     help="also time the unfused step with its forward under torch.compile (main workload)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
+    ap.add_argument("--details", default=None,
+                    help="also write the per-kernel tables of every workload (JSON) to this file")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -581,6 +587,67 @@ def measured_traffic(kernel):
 
 # ------------------------------------------------------------- CPU baseline
 
+class _Children:
+    """Child processes of the clock and power samplers.  Each is started in a
+    session of its own, so that it and anything it spawns form one process
+    group that ``reap`` can end; ``reap`` is called before the benchmark
+    returns, so no sampler outlives it."""
+
+    def __init__(self):
+        import threading
+        self.lock = threading.Lock()
+        self.live = []
+        self.closed = False
+
+    def run(self, cmd, timeout):
+        import subprocess
+        with self.lock:
+            if self.closed:
+                return ""
+            p = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True,
+                                 start_new_session=True)
+            self.live.append(p)
+        try:
+            out, _ = p.communicate(timeout=timeout)
+        except subprocess.TimeoutExpired:
+            self._end(p)
+            out = ""
+        with self.lock:
+            if p in self.live:
+                self.live.remove(p)
+        return out or ""
+
+    @staticmethod
+    def _end(p):
+        import signal
+        import subprocess
+        for sig in (signal.SIGTERM, signal.SIGKILL):
+            if p.poll() is not None:
+                break
+            try:
+                os.killpg(p.pid, sig)
+            except (ProcessLookupError, PermissionError):
+                pass
+            try:
+                p.wait(timeout=3)
+            except subprocess.TimeoutExpired:
+                continue
+        try:
+            os.killpg(p.pid, signal.SIGKILL)   # anything left in the group
+        except (ProcessLookupError, PermissionError):
+            pass
+        if p.poll() is None:
+            p.wait()
+
+    def reap(self):
+        with self.lock:
+            self.closed = True
+            live = list(self.live)
+            self.live.clear()
+        for p in live:
+            self._end(p)
+
+
 def sustained_sclk(torch, step, seconds=4.0):
     """Shader clock while the step runs back to back: rocm-smi's current sclk
     sampled every ~0.25 s from a thread while the GPU repeats the step for
@@ -589,7 +656,6 @@ def sustained_sclk(torch, step, seconds=4.0):
     peak assumes.  None where rocm-smi is not available."""
     import re
     import shutil
-    import subprocess
     import threading
     exe = shutil.which("rocm-smi") or ("/opt/rocm/bin/rocm-smi" if os.path.exists("/opt/rocm/bin/rocm-smi") else None)
     if exe is None:
@@ -601,13 +667,11 @@ def sustained_sclk(torch, step, seconds=4.0):
         return None
     samples, power, done = [], [], threading.Event()
     amd = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+    kids = _Children()
 
     def sample():
         while not done.is_set():
-            try:
-                out = subprocess.run([exe, "--showclocks"], capture_output=True, text=True, timeout=5).stdout
-            except Exception:  # pragma: no cover - tool failure
-                return
+            out = kids.run([exe, "--showclocks"], 5)
             for line in out.splitlines():
                 m = re.search(r"sclk.*\((\d+)Mhz\)", line)
                 if m:
@@ -618,10 +682,8 @@ def sustained_sclk(torch, step, seconds=4.0):
     def sample_power():   # socket power from amd-smi (rocm-smi reports none on this part)
         while amd and not done.is_set():
             try:
-                out = subprocess.run([amd, "metric", "-p", "--json"], capture_output=True, text=True,
-                                     timeout=10).stdout
-                v = json.loads(out)["gpu_data"][0]["power"]["socket_power"]["value"]
-                power.append(float(v))
+                v = json.loads(kids.run([amd, "metric", "-p", "--json"], 10))
+                power.append(float(v["gpu_data"][0]["power"]["socket_power"]["value"]))
             except Exception:  # pragma: no cover - tool failure or another format
                 return
             done.wait(0.25)
@@ -630,36 +692,37 @@ def sustained_sclk(torch, step, seconds=4.0):
         step()
     torch.cuda.synchronize()
     th = threading.Thread(target=sample, daemon=True)
-    th.start()
     tp = threading.Thread(target=sample_power, daemon=True)
+    th.start()
     tp.start()
-    t0 = time.time()
-    while time.time() - t0 < seconds:
-        for _ in range(8):
-            step()
-        torch.cuda.synchronize()
-    done.set()
-    th.join(timeout=10)
-    tp.join(timeout=15)
+    try:
+        t0 = time.time()
+        while time.time() - t0 < seconds:
+            for _ in range(8):
+                step()
+            torch.cuda.synchronize()
+    finally:
+        done.set()
+        kids.reap()
+        th.join(timeout=15)
+        tp.join(timeout=15)
     samples = samples[2:] if len(samples) > 4 else samples   # drop the ramp
     power = power[1:] if len(power) > 2 else power
     if not samples:
         return None
     srt = sorted(samples)
-    res = {"median_mhz": srt[len(srt) // 2], "min_mhz": srt[0], "max_mhz": srt[-1], "samples": len(srt),
-           "method": "rocm-smi --showclocks (and amd-smi metric -p for the socket power) every ~0.25 s "
-                     "while the fused step repeats for %.1f s" % seconds}
+    res = {"median_mhz": srt[len(srt) // 2], "min_mhz": srt[0], "max_mhz": srt[-1], "samples": len(srt)}
     if power:
         pw = sorted(power)
         res["power_median_w"] = pw[len(pw) // 2]
         res["power_max_w"] = pw[-1]
+    kids2 = _Children()
     try:
-        out = subprocess.run([exe, "--showmaxpower"], capture_output=True, text=True, timeout=5).stdout
-        m = re.search(r"Max Graphics Package Power \(W\):\s*([\d.]+)", out)
+        m = re.search(r"Max Graphics Package Power \(W\):\s*([\d.]+)", kids2.run([exe, "--showmaxpower"], 5))
         if m:
             res["power_cap_w"] = float(m.group(1))
-    except Exception:  # pragma: no cover - tool failure
-        pass
+    finally:
+        kids2.reap()
     return res
 
 
@@ -696,11 +759,43 @@ def cpu_baseline(w, h, target_s):
         dt, fl = run(Ms)
     return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads or cores,
             "kind": "oracle",
-            "sample": f"{w.name}: first {Ms} of {w.M} tokens, full weights; fp64 numpy "
-                      f"(BLAS threads {threads}, affinity cores {cores}); one fwd+bwd call {dt:.1f} s"}
+            "sample": f"{w.name}: first {Ms} of {w.M} tokens; fp64 fwd+bwd, one call {dt:.1f} s"}
 
 
 # --------------------------------------------------------------------- main
+
+# The workloads timed besides the main one.  The 70B-hidden block is part of
+# the headline metric; the rest are the other fused patterns.
+HEADLINE_SECOND = "llama70b_fwdbwd"
+ALSO = ("swiglu_fwdbwd", "llama7b_mlp_fwdbwd", "llama7b_ce_fwdbwd", "llama7b_qkv_rope_fwdbwd",
+        "llama7b_fwd_mx8", "llama1b_fwd")
+
+
+def _brief(s):
+    """The few figures of a workload summary that go on the printed line."""
+    out = {"tflops": s["tflops"], "pct_bf16_peak": s["pct_bf16_peak"], "ms_per_step": s["ms_per_step"],
+           "speedup_vs_unfused": s.get("speedup_vs_unfused")}
+    for part in ("fwd", "bwd"):
+        if s.get(part):
+            out[part] = {k: s[part][k] for k in ("ms", "tflops", "speedup_vs_unfused") if k in s[part]}
+    if "pct_fp8_peak" in s:
+        out["pct_fp8_peak"] = s["pct_fp8_peak"]
+    return out
+
+
+def _time_workload(name, torch, coda, args, unfused, compiled=False):
+    from gemm_epilogue_fusion_gemm1_amd import synth
+    w = synth.WORKLOADS[name]
+    print(f"[bench] {name}: inputs", file=sys.stderr, flush=True)
+    case, host = make_case(w, torch, coda)
+    print(f"[bench] {name}: timing {args.steps} steps after {args.warmup} warm-up steps", file=sys.stderr,
+          flush=True)
+    res = run_case(case, torch, coda, args.steps, args.warmup, unfused, compiled)
+    s = summary(case, res)
+    print(f"[bench] {name}: {s['tflops']} TFLOP/s, {s['ms_per_step']} ms/step, "
+          f"x{s.get('speedup_vs_unfused')} vs unfused", file=sys.stderr, flush=True)
+    return w, case, host, res, s
+
 
 def main():
     args = parse()
@@ -712,7 +807,6 @@ def main():
 
     import torch
     import gemm_epilogue_fusion_gemm1_amd as coda
-    from gemm_epilogue_fusion_gemm1_amd import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
@@ -727,12 +821,8 @@ def main():
         return
     coda.load_library()
     unfused = not args.no_unfused
-    w = synth.WORKLOADS[args.workload]
-    print(f"[bench] {w.name}: inputs", file=sys.stderr, flush=True)
-    case, host = make_case(w, torch, coda)
-    print(f"[bench] {w.name}: timing {args.steps} steps", file=sys.stderr, flush=True)
-    res = run_case(case, torch, coda, args.steps, args.warmup, unfused, args.compiled_baseline)
-    main_sum = summary(case, res)
+    w, case, host, res, main_sum = _time_workload(args.workload, torch, coda, args, unfused,
+                                                  args.compiled_baseline)
     kernels = res["kernels"]
     rf = roofline(kernels, res["ms_per_step_traced"])
     sclk = sustained_sclk(torch, lambda: _Steps.fused_step(case))
@@ -743,23 +833,38 @@ def main():
         rf["frac_at_sustained_sclk"] = round(rf["achieved"] / pk, 4)
     del case
     torch.cuda.empty_cache()
+    details = {args.workload: {**main_sum, "kernels": kernels}}
+    headline = {args.workload: _brief(main_sum)}
 
+    names = [] if args.no_also else [HEADLINE_SECOND, *ALSO]
+    if args.workload in names:
+        names.remove(args.workload)
     also = {}
-    if not args.no_also:
-        for name in ("llama70b_fwdbwd", "swiglu_fwdbwd", "llama7b_mlp_fwdbwd", "llama7b_ce_fwdbwd",
-                     "llama7b_qkv_rope_fwdbwd", "llama7b_fwd_mx8", "llama1b_fwd"):
-            w2 = synth.WORKLOADS[name]
-            print(f"[bench] {name}: inputs + timing", file=sys.stderr, flush=True)
-            c2, _ = make_case(w2, torch, coda)
-            r2 = run_case(c2, torch, coda, max(3, args.steps // 2), max(1, args.warmup // 2), unfused)
-            also[name] = {**summary(c2, r2), "kernels": r2["kernels"]}
-            del c2
-            torch.cuda.empty_cache()
+    for name in names:
+        _, c2, _, r2, s2 = _time_workload(name, torch, coda, args, unfused)
+        details[name] = {**s2, "kernels": r2["kernels"]}
+        if name == HEADLINE_SECOND:
+            headline[name] = _brief(s2)
+        else:
+            b = _brief(s2)
+            also[name] = {k: b[k] for k in ("tflops", "ms_per_step", "speedup_vs_unfused", "pct_fp8_peak")
+                          if k in b}
+        del c2
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, host, args.cpu_seconds)
+
+    # everything the printed line leaves out: per-kernel tables, step-time
+    # spread, traced step time, compiled baseline, per workload
+    blob = json.dumps({"details": details, "sclk_sustained": sclk})
+    print("[bench-details] " + blob, file=sys.stderr, flush=True)
+    if args.details:
+        os.makedirs(os.path.dirname(os.path.abspath(args.details)), exist_ok=True)
+        with open(args.details, "w") as fh:
+            fh.write(blob + "\n")
 
     line = {
         "metric": METRIC,
@@ -773,26 +878,17 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded normal inputs of the LLaMA-7B block shape)",
+        "data": "synthetic (seeded normal inputs)",
         "config": {"workload": w.name, "M": w.M, "K": w.K, "d": w.d, "N": w.N, "eps": w.eps,
                    "step": "coda_fwd + coda_bwd", "parallelism": "single GPU"},
-        "pct_bf16_peak": main_sum["pct_bf16_peak"],
-        "speedup_vs_unfused": main_sum.get("speedup_vs_unfused"),
-        "unfused_ms_per_step": main_sum.get("unfused_ms_per_step"),
-        "unfused_blas": main_sum.get("unfused_blas"),
-        **{k: main_sum[k] for k in ("compiled_unfused_ms_per_step", "speedup_vs_compiled_unfused",
-                                    "compiled_unfused_error") if k in main_sum},
-        "ms_per_step_traced": main_sum["ms_per_step_traced"],
-        "step_times": main_sum["step_times"],
-        "fwd": main_sum.get("fwd"),
-        "bwd": main_sum.get("bwd"),
+        "headline": headline,
         "roofline": rf,
-        "sclk_sustained": sclk,
         "cpu_baseline": cpu,
-        "kernels": kernels,
+        "sclk_mhz": sclk and sclk.get("median_mhz"),
+        "power_w": sclk and sclk.get("power_median_w"),
         "also": also,
     }
-    print(json.dumps(line), flush=True)
+    print(json.dumps(line, separators=(",", ":")), flush=True)
 
 
 if __name__ == "__main__":
