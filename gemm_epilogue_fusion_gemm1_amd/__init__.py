@@ -171,6 +171,51 @@ def _shape(t, *dims, name=""):
         raise ValueError(f"{name}: expected shape {tuple(dims)}, got {tuple(t.shape)}")
 
 
+class _Args:
+    """Checks every tensor of one call before any pointer is taken: its dtype,
+    its exact shape, that it lives on the first tensor's device and is
+    contiguous.  The library reads and writes exactly the extents these
+    shapes imply, so a tensor of another dtype or a smaller size is refused
+    here instead of being reinterpreted or overrun."""
+
+    def __init__(self, fn, first, name):
+        if first is None:
+            raise ValueError(f"{fn}: {name} is required")
+        if not first.is_cuda:
+            raise ValueError(f"{fn}: {name} must be a device (HIP) tensor")
+        self.fn, self.dev = fn, first.device
+
+    def __call__(self, t, name, shape, dtype, optional=False):
+        if t is None:
+            if optional:
+                return None
+            raise ValueError(f"{self.fn}: {name} is required")
+        if t.dtype != dtype:
+            raise TypeError(f"{self.fn}: {name} must be {dtype}, got {t.dtype}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{self.fn}: {name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if t.device != self.dev:
+            raise ValueError(f"{self.fn}: {name} is on {t.device}, expected {self.dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{self.fn}: {name} must be contiguous (row-major)")
+        return ctypes.c_void_p(t.data_ptr())
+
+    def ws(self, t, name="workspace", optional=False):
+        """A workspace: a 1-D uint8 tensor on the device; returns (pointer, bytes)."""
+        import torch
+        if t is None:
+            if optional:
+                return None, 0
+            raise ValueError(f"{self.fn}: {name} is required")
+        if t.dtype != torch.uint8 or t.dim() != 1:
+            raise TypeError(f"{self.fn}: {name} must be a 1-D torch.uint8 tensor, got {t.dtype} {tuple(t.shape)}")
+        if t.device != self.dev:
+            raise ValueError(f"{self.fn}: {name} is on {t.device}, expected {self.dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{self.fn}: {name} must be contiguous")
+        return ctypes.c_void_p(t.data_ptr()), t.numel()
+
+
 def _workspace(nbytes, device):
     import torch
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
@@ -241,138 +286,179 @@ def trace_stop() -> None:
 
 
 # ------------------------------------------------------ C-ABI passthroughs
+#
+# Same names and argument order as the C functions; outputs are caller-owned
+# and are checked like the inputs (dtype, exact shape, device).  Float tensors
+# share the dtype of the first argument; r, dgamma, lse, loss and dloss are
+# float32, labels int32, workspaces 1-D uint8.
 
 def coda_fwd(X, W1, R, gamma, W2, eps, y, r, z, workspace):
     """coda_fwd with caller-owned outputs y [M,d], r [M] (fp32), z [M,N]."""
-    L = load_library()
+    import torch
+    a = _Args("coda_fwd", X, "X")
+    dt = X.dtype
+    _dtype_code(X)
     M, K = X.shape
     d, N = W1.shape[1], W2.shape[1]
-    _check("coda_fwd", L.coda_fwd(
-        _dtype_code(X), M, K, d, N, float(eps), _ptr(X), _ptr(W1), _ptr(R), _ptr(gamma), _ptr(W2),
-        _ptr(y), _ptr(r), _ptr(z), _ptr(workspace), workspace.numel(), _stream()))
+    p = [a(X, "X", (M, K), dt), a(W1, "W1", (K, d), dt), a(R, "R", (M, d), dt), a(gamma, "gamma", (d,), dt),
+         a(W2, "W2", (d, N), dt), a(y, "y", (M, d), dt), a(r, "r", (M,), torch.float32),
+         a(z, "z", (M, N), dt)]
+    wp, wn = a.ws(workspace)
+    _check("coda_fwd", load_library().coda_fwd(_dtype_code(X), M, K, d, N, float(eps), *p, wp, wn, _stream()))
 
 
 def coda_bwd(X, W1, gamma, W2, y, r, dz, dX, dW1, dR, dW2, dgamma, workspace):
-    L = load_library()
+    import torch
+    a = _Args("coda_bwd", X, "X")
+    dt = X.dtype
+    _dtype_code(X)
     M, K = X.shape
     d, N = W1.shape[1], W2.shape[1]
-    _check("coda_bwd", L.coda_bwd(
-        _dtype_code(X), M, K, d, N, _ptr(X), _ptr(W1), _ptr(gamma), _ptr(W2), _ptr(y), _ptr(r),
-        _ptr(dz), _ptr(dX), _ptr(dW1), _ptr(dR), _ptr(dW2), _ptr(dgamma), _ptr(workspace),
-        workspace.numel(), _stream()))
+    p = [a(X, "X", (M, K), dt), a(W1, "W1", (K, d), dt), a(gamma, "gamma", (d,), dt), a(W2, "W2", (d, N), dt),
+         a(y, "y", (M, d), dt), a(r, "r", (M,), torch.float32), a(dz, "dz", (M, N), dt),
+         a(dX, "dX", (M, K), dt), a(dW1, "dW1", (K, d), dt), a(dR, "dR", (M, d), dt),
+         a(dW2, "dW2", (d, N), dt), a(dgamma, "dgamma", (d,), torch.float32)]
+    wp, wn = a.ws(workspace)
+    _check("coda_bwd", load_library().coda_bwd(_dtype_code(X), M, K, d, N, *p, wp, wn, _stream()))
 
 
 def coda_swiglu_fwd(X, W, Wd, gu, a, z, workspace=None):
-    L = load_library()
+    c = _Args("coda_swiglu_fwd", X, "X")
+    dt = X.dtype
+    _dtype_code(X)
     M, d = X.shape
     F = Wd.shape[0]
-    ws = _ptr(workspace) if workspace is not None else None
-    _check("coda_swiglu_fwd", L.coda_swiglu_fwd(
-        _dtype_code(X), M, d, F, _ptr(X), _ptr(W), _ptr(Wd), _ptr(gu), _ptr(a), _ptr(z), ws,
-        0 if workspace is None else workspace.numel(), _stream()))
+    p = [c(X, "X", (M, d), dt), c(W, "W", (d, 2 * F), dt), c(Wd, "Wd", (F, d), dt),
+         c(gu, "gu", (M, 2 * F), dt), c(a, "a", (M, F), dt), c(z, "z", (M, d), dt)]
+    wp, wn = c.ws(workspace, optional=True)
+    _check("coda_swiglu_fwd", load_library().coda_swiglu_fwd(_dtype_code(X), M, d, F, *p, wp, wn, _stream()))
 
 
 def coda_swiglu_bwd(X, W, Wd, gu, a, dz, dX, dW, dWd, workspace):
-    L = load_library()
+    c = _Args("coda_swiglu_bwd", X, "X")
+    dt = X.dtype
+    _dtype_code(X)
     M, d = X.shape
     F = Wd.shape[0]
-    _check("coda_swiglu_bwd", L.coda_swiglu_bwd(
-        _dtype_code(X), M, d, F, _ptr(X), _ptr(W), _ptr(Wd), _ptr(gu), _ptr(a), _ptr(dz),
-        _ptr(dX), _ptr(dW), _ptr(dWd), _ptr(workspace), workspace.numel(), _stream()))
+    p = [c(X, "X", (M, d), dt), c(W, "W", (d, 2 * F), dt), c(Wd, "Wd", (F, d), dt),
+         c(gu, "gu", (M, 2 * F), dt), c(a, "a", (M, F), dt), c(dz, "dz", (M, d), dt),
+         c(dX, "dX", (M, d), dt), c(dW, "dW", (d, 2 * F), dt), c(dWd, "dWd", (F, d), dt)]
+    wp, wn = c.ws(workspace)
+    _check("coda_swiglu_bwd", load_library().coda_swiglu_bwd(_dtype_code(X), M, d, F, *p, wp, wn, _stream()))
 
 
 def coda_mlp_fwd(X, W1, R, gamma, W, Wd, eps, y, r, gu, a, z, workspace):
-    L = load_library()
+    import torch
+    c = _Args("coda_mlp_fwd", X, "X")
+    dt = X.dtype
+    _dtype_code(X)
     M, K = X.shape
     d = W1.shape[1]
     F = Wd.shape[0]
-    _check("coda_mlp_fwd", L.coda_mlp_fwd(
-        _dtype_code(X), M, K, d, F, float(eps), _ptr(X), _ptr(W1), _ptr(R), _ptr(gamma), _ptr(W),
-        _ptr(Wd), _ptr(y), _ptr(r), _ptr(gu), _ptr(a), _ptr(z), _ptr(workspace), workspace.numel(),
-        _stream()))
+    p = [c(X, "X", (M, K), dt), c(W1, "W1", (K, d), dt), c(R, "R", (M, d), dt), c(gamma, "gamma", (d,), dt),
+         c(W, "W", (d, 2 * F), dt), c(Wd, "Wd", (F, d), dt), c(y, "y", (M, d), dt),
+         c(r, "r", (M,), torch.float32), c(gu, "gu", (M, 2 * F), dt), c(a, "a", (M, F), dt),
+         c(z, "z", (M, d), dt)]
+    wp, wn = c.ws(workspace)
+    _check("coda_mlp_fwd", load_library().coda_mlp_fwd(_dtype_code(X), M, K, d, F, float(eps), *p, wp, wn,
+                                                        _stream()))
 
 
 def coda_mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in, dX, dW1, dR, dW, dWd, dgamma,
                  workspace):
-    L = load_library()
+    import torch
+    c = _Args("coda_mlp_bwd", X, "X")
+    dt = X.dtype
+    _dtype_code(X)
     M, K = X.shape
     d = W1.shape[1]
     F = Wd.shape[0]
-    _check("coda_mlp_bwd", L.coda_mlp_bwd(
-        _dtype_code(X), M, K, d, F, _ptr(X), _ptr(W1), _ptr(gamma), _ptr(W), _ptr(Wd), _ptr(y),
-        _ptr(r), _ptr(gu), _ptr(a), _ptr(dz), _ptr(dy_in), _ptr(dX), _ptr(dW1), _ptr(dR), _ptr(dW),
-        _ptr(dWd), _ptr(dgamma), _ptr(workspace), workspace.numel(), _stream()))
-
-
-def _labels(t):
-    import torch
-    if t.dtype != torch.int32:
-        raise TypeError(f"labels must be torch.int32, got {t.dtype}")
-    return _ptr(t)
+    p = [c(X, "X", (M, K), dt), c(W1, "W1", (K, d), dt), c(gamma, "gamma", (d,), dt),
+         c(W, "W", (d, 2 * F), dt), c(Wd, "Wd", (F, d), dt), c(y, "y", (M, d), dt),
+         c(r, "r", (M,), torch.float32), c(gu, "gu", (M, 2 * F), dt), c(a, "a", (M, F), dt),
+         c(dz, "dz", (M, d), dt), c(dy_in, "dy_in", (M, d), dt, optional=True),
+         c(dX, "dX", (M, K), dt), c(dW1, "dW1", (K, d), dt), c(dR, "dR", (M, d), dt),
+         c(dW, "dW", (d, 2 * F), dt), c(dWd, "dWd", (F, d), dt), c(dgamma, "dgamma", (d,), torch.float32)]
+    wp, wn = c.ws(workspace)
+    _check("coda_mlp_bwd", load_library().coda_mlp_bwd(_dtype_code(X), M, K, d, F, *p, wp, wn, _stream()))
 
 
 def coda_ce_fwd(h, Wv, labels, logits, lse, loss, workspace):
-    L = load_library()
+    import torch
+    c = _Args("coda_ce_fwd", h, "h")
+    dt = h.dtype
+    _dtype_code(h)
     M, d = h.shape
     V = Wv.shape[1]
-    _check("coda_ce_fwd", L.coda_ce_fwd(
-        _dtype_code(h), M, d, V, _ptr(h), _ptr(Wv), _labels(labels), _ptr(logits), _ptr(lse), _ptr(loss),
-        _ptr(workspace), workspace.numel(), _stream()))
+    p = [c(h, "h", (M, d), dt), c(Wv, "Wv", (d, V), dt), c(labels, "labels", (M,), torch.int32),
+         c(logits, "logits", (M, V), dt), c(lse, "lse", (M,), torch.float32), c(loss, "loss", (M,), torch.float32)]
+    wp, wn = c.ws(workspace)
+    _check("coda_ce_fwd", load_library().coda_ce_fwd(_dtype_code(h), M, d, V, *p, wp, wn, _stream()))
 
 
 def coda_ce_bwd(h, Wv, labels, logits, lse, dloss, dh, dWv, workspace):
-    L = load_library()
+    import torch
+    c = _Args("coda_ce_bwd", h, "h")
+    dt = h.dtype
+    _dtype_code(h)
     M, d = h.shape
     V = Wv.shape[1]
-    _check("coda_ce_bwd", L.coda_ce_bwd(
-        _dtype_code(h), M, d, V, _ptr(h), _ptr(Wv), _labels(labels), _ptr(logits), _ptr(lse), _ptr(dloss),
-        _ptr(dh), _ptr(dWv), _ptr(workspace), workspace.numel(), _stream()))
+    p = [c(h, "h", (M, d), dt), c(Wv, "Wv", (d, V), dt), c(labels, "labels", (M,), torch.int32),
+         c(logits, "logits", (M, V), dt), c(lse, "lse", (M,), torch.float32),
+         c(dloss, "dloss", (M,), torch.float32), c(dh, "dh", (M, d), dt), c(dWv, "dWv", (d, V), dt)]
+    wp, wn = c.ws(workspace)
+    _check("coda_ce_bwd", load_library().coda_ce_bwd(_dtype_code(h), M, d, V, *p, wp, wn, _stream()))
 
 
 def coda_rope_fwd(X, W, N_rot, D, S, base, Y, workspace):
-    L = load_library()
+    c = _Args("coda_rope_fwd", X, "X")
+    dt = X.dtype
+    _dtype_code(X)
     M, K = X.shape
     N = W.shape[1]
-    _check("coda_rope_fwd", L.coda_rope_fwd(
-        _dtype_code(X), M, K, N, N_rot, D, S, float(base), _ptr(X), _ptr(W), _ptr(Y), _ptr(workspace),
-        workspace.numel(), _stream()))
+    p = [c(X, "X", (M, K), dt), c(W, "W", (K, N), dt), c(Y, "Y", (M, N), dt)]
+    wp, wn = c.ws(workspace)
+    _check("coda_rope_fwd", load_library().coda_rope_fwd(_dtype_code(X), M, K, N, N_rot, D, S, float(base),
+                                                          *p, wp, wn, _stream()))
 
 
 def coda_rope_bwd(X, W, dY, N_rot, D, S, base, dX, dW, workspace):
-    L = load_library()
+    c = _Args("coda_rope_bwd", X, "X")
+    dt = X.dtype
+    _dtype_code(X)
     M, K = X.shape
     N = W.shape[1]
-    _check("coda_rope_bwd", L.coda_rope_bwd(
-        _dtype_code(X), M, K, N, N_rot, D, S, float(base), _ptr(X), _ptr(W), _ptr(dY), _ptr(dX), _ptr(dW),
-        _ptr(workspace), workspace.numel(), _stream()))
-
-
-def _u8(t, name):
-    import torch
-    if t.dtype != torch.uint8:
-        raise TypeError(f"{name}: MXFP8 codes and scales are torch.uint8 tensors")
-    return _ptr(t)
+    p = [c(X, "X", (M, K), dt), c(W, "W", (K, N), dt), c(dY, "dY", (M, N), dt), c(dX, "dX", (M, K), dt),
+         c(dW, "dW", (K, N), dt)]
+    wp, wn = c.ws(workspace)
+    _check("coda_rope_bwd", load_library().coda_rope_bwd(_dtype_code(X), M, K, N, N_rot, D, S, float(base),
+                                                          *p, wp, wn, _stream()))
 
 
 def coda_mx8_quantize(src, codes, scales):
     """MXFP8 quantisation of the bf16 rows of src [rows, cols] into codes
     [rows, cols] and step-blocked scales [cols/128, rows, 4] (uint8)."""
     import torch
-    if src.dtype != torch.bfloat16:
-        raise TypeError("coda_mx8_quantize: src must be torch.bfloat16")
+    c = _Args("coda_mx8_quantize", src, "src")
     rows, cols = src.shape
-    _check("coda_mx8_quantize", load_library().coda_mx8_quantize(
-        rows, cols, _ptr(src), cols, _u8(codes, "codes"), _u8(scales, "scales"), _stream()))
+    p = [c(src, "src", (rows, cols), torch.bfloat16), c(codes, "codes", (rows, cols), torch.uint8),
+         c(scales, "scales", (cols // 128, rows, 4), torch.uint8)]
+    _check("coda_mx8_quantize", load_library().coda_mx8_quantize(rows, cols, p[0], cols, p[1], p[2], _stream()))
 
 
 def coda_fwd_mx8(Xq, Xs, W1tq, W1ts, R, gamma, W2tq, W2ts, eps, y, r, z, workspace):
     """coda_fwd_mx8 with caller-owned outputs y [M,d] (bf16), r [M] (fp32), z [M,N] (bf16)."""
+    import torch
+    c = _Args("coda_fwd_mx8", Xq, "Xq")
+    u8, bf = torch.uint8, torch.bfloat16
     M, K = Xq.shape
     d, N = W1tq.shape[0], W2tq.shape[0]
-    _check("coda_fwd_mx8", load_library().coda_fwd_mx8(
-        M, K, d, N, float(eps), _u8(Xq, "Xq"), _u8(Xs, "Xs"), _u8(W1tq, "W1tq"), _u8(W1ts, "W1ts"),
-        _ptr(R), _ptr(gamma), _u8(W2tq, "W2tq"), _u8(W2ts, "W2ts"), _ptr(y), _ptr(r), _ptr(z),
-        _ptr(workspace), workspace.numel(), _stream()))
+    p = [c(Xq, "Xq", (M, K), u8), c(Xs, "Xs", (K // 128, M, 4), u8), c(W1tq, "W1tq", (d, K), u8),
+         c(W1ts, "W1ts", (K // 128, d, 4), u8), c(R, "R", (M, d), bf), c(gamma, "gamma", (d,), bf),
+         c(W2tq, "W2tq", (N, d), u8), c(W2ts, "W2ts", (d // 128, N, 4), u8), c(y, "y", (M, d), bf),
+         c(r, "r", (M,), torch.float32), c(z, "z", (M, N), bf)]
+    wp, wn = c.ws(workspace)
+    _check("coda_fwd_mx8", load_library().coda_fwd_mx8(M, K, d, N, float(eps), *p, wp, wn, _stream()))
 
 
 # ------------------------------------------------------ convenience calls
