@@ -285,10 +285,14 @@ size_t coda_fwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t 
   return fwd_ws(dtype, M, d, N).total;
 }
 
-coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N, float eps,
-                     const void* X, const void* W1, const void* R, const void* gamma,
-                     const void* W2, void* y, float* r, void* z, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// coda_fwd's checks of everything but the workspace.
+coda_status fwd_check(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N, float eps,
+                      const void* X, const void* W1, const void* R, const void* gamma,
+                      const void* W2, void* y, float* r, void* z) {
   if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
   if (!X || !W1 || !R || !gamma || !W2 || !y || !r || !z) return CODA_ERR_NULL;
   if (!dim_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, d) || !dim_ok(dtype, N))
@@ -299,22 +303,29 @@ coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
   if (!std::isfinite(eps) || !(eps > 0.0f)) return CODA_ERR_EPS;
   for (const void* p : {X, W1, R, gamma, W2, (const void*)y, (const void*)r, (const void*)z})
     if (!aligned16(p)) return CODA_ERR_ALIGN;
-  const FwdWs ws = fwd_ws(dtype, M, d, N);
-  if (!workspace || workspace_bytes < ws.total) return CODA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  return CODA_OK;
+}
+
+// Outputs against inputs, each other and the workspace.
+bool fwd_alias_free(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N, const void* X,
+                    const void* W1, const void* R, const void* gamma, const void* W2, void* y,
+                    float* r, void* z, const void* workspace, size_t ws_bytes) {
   const size_t e = esize(dtype);
   const Range in[] = {rng(X, M * K * e), rng(W1, K * d * e), rng(R, M * d * e), rng(gamma, d * e),
                       rng(W2, d * N * e)};
-  const Range out[] = {rng(y, M * d * e), rng(r, M * 4), rng(z, M * N * e),
-                       rng(workspace, ws.total)};
-  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+  const Range out[] = {rng(y, M * d * e), rng(r, M * 4), rng(z, M * N * e), rng(workspace, ws_bytes)};
+  return alias_free(in, out);
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  char* wsb = (char*)workspace;
+// The forward's launches, with the partial sums and y*gamma in `wsb`.
+coda_status fwd_launch(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N, float eps,
+                       const void* X, const void* W1, const void* R, const void* gamma,
+                       const void* W2, void* y, float* r, void* z, const FwdWs& ws, char* wsb,
+                       hipStream_t s) {
   float* P = (float*)(wsb + ws.P);
   void* yg = wsb + ws.yg;
   hipError_t err;
-  const double eb = (double)e;
+  const double eb = (double)esize(dtype);
 
   const bool bf = dtype == CODA_BF16;
   // y*gamma layout: stored transposed ([d, M]) so that K2 runs with both
@@ -351,6 +362,25 @@ coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
   return hip_status(traced("k2_gemm_rowscale", gemm_flops(M, N, d), k2_bytes, s, [&] {
     return coda::launch_gemm_f32(g2, coda::EPI_ROWSCALE, s);
   }));
+}
+
+}  // namespace
+
+extern "C" {
+
+coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N, float eps,
+                     const void* X, const void* W1, const void* R, const void* gamma,
+                     const void* W2, void* y, float* r, void* z, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  const coda_status st = fwd_check(dtype, M, K, d, N, eps, X, W1, R, gamma, W2, y, r, z);
+  if (st != CODA_OK) return st;
+  const FwdWs ws = fwd_ws(dtype, M, d, N);
+  if (!workspace || workspace_bytes < ws.total) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  if (!fwd_alias_free(dtype, M, K, d, N, X, W1, R, gamma, W2, y, r, z, workspace, ws.total))
+    return CODA_ERR_ALIAS;
+  return fwd_launch(dtype, M, K, d, N, eps, X, W1, R, gamma, W2, y, r, z, ws, (char*)workspace,
+                    (hipStream_t)stream);
 }
 
 size_t coda_bwd_workspace_bytes(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N) {
@@ -743,7 +773,7 @@ coda_status coda_ce_fwd(coda_dtype dtype, int64_t M, int64_t d, int64_t V, const
     return hip_status(err);
   // C2: lse and loss from the partials
   return hip_status(traced("c2_ce_combine", 0.0, 8.0 * M * ws.T + 12.0 * M, s, [&] {
-    return coda::launch_ce_combine(pmax, psum, ws.T, ws.T, lab, M, lse, loss, s);
+    return coda::launch_ce_combine(pmax, psum, ws.T, ws.T, lab, labels, V, M, lse, loss, s);
   }));
 }
 

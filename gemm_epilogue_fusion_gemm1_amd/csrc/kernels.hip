@@ -972,10 +972,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         const int row = row0 + t;
         float m = red[t];
         for (int w = 1; w < WNv; ++w) m = fmaxf(m, red[w * BM + t]);
+        // a wave whose columns all lie past N left (max -inf, sum 0) and is
+        // skipped by its zero sum; a NaN logit made its sum NaN, which the
+        // row keeps (fmaxf alone would drop it)
         float sm = 0.0f;
         for (int w = 0; w < WNv; ++w) {
-          const float mw = red[w * BM + t];
-          if (mw > -INFINITY) sm += cered[w * BM + t] * __expf(mw - m);
+          const float sw = cered[w * BM + t];
+          if (sw != 0.0f) sm += sw * __expf(red[w * BM + t] - m);
         }
         if (row < g.M) {
           g.part_row[(int64_t)row * g.ld_part_row + tn] = m;
@@ -1462,8 +1465,15 @@ hipError_t launch_rope_inverse(const void* dY, const float* tab, void* dP, int64
 
 // One wave per row: lane l folds the row's tiles l, l + 64, ... into a running
 // (max, sum-exp) pair, then the 64 lanes combine in a fixed butterfly order.
+// A pair is rescaled only when its sum is non-zero: an empty pair (-inf, 0)
+// adds nothing, and a NaN sum (a NaN logit in that tile) stays NaN.  A row
+// whose label lies outside [0, V) is ignored: loss 0 (its lse is still formed).
+__device__ __forceinline__ float ce_rescale(float s, float m, float nm) {
+  return s != 0.0f ? s * __expf(m - nm) : 0.0f;
+}
 __global__ void ce_combine_kernel(const float* __restrict__ pmax, const float* __restrict__ psum,
-                                  int64_t ldp, int T, const float* __restrict__ lab, int64_t M,
+                                  int64_t ldp, int T, const float* __restrict__ lab,
+                                  const int* __restrict__ labels, int64_t V, int64_t M,
                                   float* __restrict__ lse, float* __restrict__ loss) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -1472,7 +1482,7 @@ __global__ void ce_combine_kernel(const float* __restrict__ pmax, const float* _
     for (int t = lane; t < T; t += 64) {
       const float mt = pmax[row * ldp + t], st = psum[row * ldp + t];
       const float nm = fmaxf(m, mt);
-      sm = (m > -INFINITY ? sm * __expf(m - nm) : 0.0f) + st * __expf(mt - nm);
+      sm = ce_rescale(sm, m, nm) + ce_rescale(st, mt, nm);
       m = nm;
     }
   }
@@ -1480,13 +1490,14 @@ __global__ void ce_combine_kernel(const float* __restrict__ pmax, const float* _
   for (int o = 32; o >= 1; o >>= 1) {
     const float mo = __shfl_xor(m, o), so = __shfl_xor(sm, o);
     const float nm = fmaxf(m, mo);
-    sm = (m > -INFINITY ? sm * __expf(m - nm) : 0.0f) + (mo > -INFINITY ? so * __expf(mo - nm) : 0.0f);
+    sm = ce_rescale(sm, m, nm) + ce_rescale(so, mo, nm);
     m = nm;
   }
   if (row < M && lane == 0) {
     const float l = m + __logf(sm);
+    const int lb = labels[row];
     lse[row] = l;
-    loss[row] = l - lab[row];
+    loss[row] = (lb >= 0 && lb < V) ? l - lab[row] : 0.0f;
   }
 }
 
@@ -1498,8 +1509,9 @@ __global__ void ce_dlogits_kernel(const __bf16* __restrict__ logits, const int* 
   if (e0 >= M * V) return;
   const int64_t i = e0 / V;
   const int64_t j0 = e0 - i * V;
-  const float li = lse[i], di = dloss[i];
+  const float li = lse[i];
   const int lab = labels[i];
+  const float di = (lab >= 0 && lab < V) ? dloss[i] : 0.0f;   // an ignored row has no gradient
   const bf16x8 x = *(const bf16x8*)(logits + e0);
   bf16x8 o;
 #pragma unroll
@@ -1511,9 +1523,10 @@ __global__ void ce_dlogits_kernel(const __bf16* __restrict__ logits, const int* 
 }
 
 hipError_t launch_ce_combine(const float* pmax, const float* psum, int64_t ldp, int T,
-                             const float* lab, int64_t M, float* lse, float* loss, hipStream_t s) {
+                             const float* lab, const int* labels, int64_t V, int64_t M, float* lse,
+                             float* loss, hipStream_t s) {
   hipLaunchKernelGGL(ce_combine_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, pmax, psum,
-                     ldp, T, lab, M, lse, loss);
+                     ldp, T, lab, labels, V, M, lse, loss);
   return hipGetLastError();
 }
 

@@ -96,11 +96,12 @@ hipError_t launch_rope_table(float* tab, int S, int D, double base, hipStream_t 
 hipError_t launch_rope_inverse(const void* dY, const float* tab, void* dP, int64_t M, int64_t N,
                                int N_rot, int D, int S, hipStream_t stream);
 // lse[i] = m + log s over the tiles' (max, sum-exp) pairs combined in order;
-// loss[i] = lse[i] - lab[i]
+// loss[i] = lse[i] - lab[i], or 0 when labels[i] lies outside [0, V)
 hipError_t launch_ce_combine(const float* pmax, const float* psum, int64_t ldp, int T,
-                             const float* lab, int64_t M, float* lse, float* loss,
-                             hipStream_t stream);
-// dlogits[i][j] = dloss[i] (exp(logits[i][j] - lse[i]) - [j == labels[i]])  (bf16)
+                             const float* lab, const int* labels, int64_t V, int64_t M, float* lse,
+                             float* loss, hipStream_t stream);
+// dlogits[i][j] = dloss[i] (exp(logits[i][j] - lse[i]) - [j == labels[i]])  (bf16);
+// 0 for a row whose label lies outside [0, V)
 hipError_t launch_ce_dlogits(const void* logits, const int* labels, const float* lse,
                              const float* dloss, void* dlogits, int64_t M, int64_t V,
                              hipStream_t stream);
@@ -108,5 +109,6 @@ hipError_t launch_ce_dlogits(const void* logits, const int* labels, const float*
 // not NULL)  (dR holds dn on entry)
 hipError_t launch_dy(void* dR, const void* y, const float* r, const float* c, const void* dy_in,
                      int64_t M, int64_t d, hipStream_t stream);
+
 
 }  // namespace coda

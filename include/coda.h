@@ -233,9 +233,12 @@ coda_status coda_mlp_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int6
  * accumulator, plus the label's fp32 logit; a small kernel combines the
  * pairs in tile order into lse and loss.
  *
- *   h [M,d], Wv [d,V]: in (dtype).  labels [M]: in, int32 in [0, V) (a label
- *   outside that range is never used as an index; that row's loss is then
- *   undefined).   logits [M,V]: out (dtype).   lse [M], loss [M]: out, float32.
+ *   h [M,d], Wv [d,V]: in (dtype).  labels [M]: in, int32.  A label outside
+ *   [0, V) (e.g. -100) marks an ignored row: its loss is 0 and coda_ce_bwd
+ *   gives it a zero dlogits row; its lse is still the row's.  Labels are only
+ *   compared, never used as an index.  A NaN logit makes its row's lse (and
+ *   loss, unless ignored) NaN.
+ *   logits [M,V]: out (dtype).   lse [M], loss [M]: out, float32.
  *   workspace: >= coda_ce_fwd_workspace_bytes(...) bytes (the tile pairs).
  * Errors as coda_fwd (no eps); CODA_F32 returns CODA_ERR_UNSUPPORTED.
  * ---------------------------------------------------------------------- */
@@ -250,6 +253,7 @@ coda_status coda_ce_fwd(coda_dtype dtype, int64_t M, int64_t d, int64_t V, const
  * rows, dloss_i = 1/M):
  *   dlogits = diag(dloss) (exp(logits - lse) - onehot(labels));
  *   dh = dlogits Wv^T;  dWv = h^T dlogits.
+ * Rows whose label lies outside [0, V) are ignored (zero dlogits row).
  *
  *   h [M,d], Wv [d,V], labels [M] (int32), logits [M,V], lse [M] (float32),
  *   dloss [M] (float32): in.   dh [M,d], dWv [d,V]: out (dtype).
