@@ -9,7 +9,7 @@ PyTorch fallback: without the built library every call raises.
 
 Low-level calls (same names and argument order as the C functions, outputs
 preallocated by the caller):
-    coda_fwd, coda_bwd, coda_swiglu_fwd, coda_swiglu_bwd, coda_mlp_fwd, coda_mlp_bwd,
+    coda_fwd, coda_fwd_noalloc, coda_bwd, coda_swiglu_fwd, coda_swiglu_bwd, coda_mlp_fwd, coda_mlp_bwd,
     coda_ce_fwd, coda_ce_bwd, coda_rope_fwd, coda_rope_bwd
 Convenience calls (allocate outputs):
     fwd(X, W1, R, gamma, W2, eps)        -> (z, y, r)
@@ -30,7 +30,7 @@ import ctypes
 import os
 
 __all__ = [
-    "CodaError", "lib_path", "load_library", "coda_fwd", "coda_bwd", "coda_swiglu_fwd",
+    "CodaError", "lib_path", "load_library", "coda_fwd", "coda_fwd_noalloc", "coda_bwd", "coda_swiglu_fwd",
     "coda_swiglu_bwd", "coda_mlp_fwd", "coda_mlp_bwd", "fwd", "bwd", "swiglu_fwd",
     "swiglu_bwd", "mlp_fwd", "mlp_bwd", "coda_ce_fwd", "coda_ce_bwd", "ce_fwd", "ce_bwd",
     "ce_fwd_workspace_bytes", "ce_bwd_workspace_bytes", "coda_rope_fwd", "coda_rope_bwd", "rope_fwd",
@@ -95,6 +95,8 @@ def load_library() -> ctypes.CDLL:
         getattr(L, name).argtypes = args
     L.coda_fwd.restype = i32
     L.coda_fwd.argtypes = [i32, i64, i64, i64, i64, f32] + [vp] * 8 + [vp, sz, vp]
+    L.coda_fwd_noalloc.restype = i32
+    L.coda_fwd_noalloc.argtypes = [i32, i64, i64, i64, i64, f32] + [vp] * 8 + [vp]
     L.coda_bwd.restype = i32
     L.coda_bwd.argtypes = [i32, i64, i64, i64, i64] + [vp] * 12 + [vp, sz, vp]
     L.coda_swiglu_fwd.restype = i32
@@ -305,6 +307,23 @@ def coda_fwd(X, W1, R, gamma, W2, eps, y, r, z, workspace):
          a(z, "z", (M, N), dt)]
     wp, wn = a.ws(workspace)
     _check("coda_fwd", load_library().coda_fwd(_dtype_code(X), M, K, d, N, float(eps), *p, wp, wn, _stream()))
+
+
+def coda_fwd_noalloc(X, W1, R, gamma, W2, eps, y, r, z):
+    """coda_fwd without a workspace: the library's built-in device scratch
+    (80 MiB per device) holds the intermediates, so the call allocates
+    nothing.  Calls that overlap on one device race on that scratch."""
+    import torch
+    a = _Args("coda_fwd_noalloc", X, "X")
+    dt = X.dtype
+    _dtype_code(X)
+    M, K = X.shape
+    d, N = W1.shape[1], W2.shape[1]
+    p = [a(X, "X", (M, K), dt), a(W1, "W1", (K, d), dt), a(R, "R", (M, d), dt), a(gamma, "gamma", (d,), dt),
+         a(W2, "W2", (d, N), dt), a(y, "y", (M, d), dt), a(r, "r", (M,), torch.float32),
+         a(z, "z", (M, N), dt)]
+    _check("coda_fwd_noalloc", load_library().coda_fwd_noalloc(_dtype_code(X), M, K, d, N, float(eps), *p,
+                                                                _stream()))
 
 
 def coda_bwd(X, W1, gamma, W2, y, r, dz, dX, dW1, dR, dW2, dgamma, workspace):

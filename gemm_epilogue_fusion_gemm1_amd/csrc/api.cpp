@@ -15,6 +15,7 @@ namespace {
 using coda::GemmArgs;
 
 constexpr uint64_t kMaxTensorBytes = 0x7FFFFFF0ull;   // buffer descriptors address < 2 GiB
+static_assert(coda::kNoAllocScratchBytes == CODA_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
 constexpr size_t kAlign = 256;
 
 size_t esize(coda_dtype t) { return t == CODA_BF16 ? 2 : 4; }
@@ -380,6 +381,23 @@ coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
   if (!fwd_alias_free(dtype, M, K, d, N, X, W1, R, gamma, W2, y, r, z, workspace, ws.total))
     return CODA_ERR_ALIAS;
   return fwd_launch(dtype, M, K, d, N, eps, X, W1, R, gamma, W2, y, r, z, ws, (char*)workspace,
+                    (hipStream_t)stream);
+}
+
+coda_status coda_fwd_noalloc(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N,
+                             float eps, const void* X, const void* W1, const void* R,
+                             const void* gamma, const void* W2, void* y, float* r, void* z,
+                             void* stream) {
+  const coda_status st = fwd_check(dtype, M, K, d, N, eps, X, W1, R, gamma, W2, y, r, z);
+  if (st != CODA_OK) return st;
+  const FwdWs ws = fwd_ws(dtype, M, d, N);
+  if (ws.total > coda::kNoAllocScratchBytes) return CODA_ERR_WORKSPACE;
+  // the scratch is the library's own array, which no caller buffer can overlap
+  if (!fwd_alias_free(dtype, M, K, d, N, X, W1, R, gamma, W2, y, r, z, nullptr, 0))
+    return CODA_ERR_ALIAS;
+  void* scratch = nullptr;
+  if (coda::noalloc_scratch(&scratch) != hipSuccess) return CODA_ERR_HIP;
+  return fwd_launch(dtype, M, K, d, N, eps, X, W1, R, gamma, W2, y, r, z, ws, (char*)scratch,
                     (hipStream_t)stream);
 }
 

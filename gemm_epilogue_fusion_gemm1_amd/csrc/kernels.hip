@@ -29,6 +29,7 @@
 //    fixed order, so every result is run-to-run deterministic (no atomics).
 #include "launch.hpp"
 
+#include <mutex>
 #include <type_traits>
 
 namespace coda {
@@ -1553,6 +1554,39 @@ hipError_t launch_dy(void* dR, const void* y, const float* r, const float* c, co
   hipLaunchKernelGGL(dy_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
                      (__bf16*)dR, (const __bf16*)y, r, c, (const __bf16*)dy_in, M, d);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Built-in scratch for callers that cannot allocate device memory
+// (coda_fwd_noalloc): a file-scope device array, one copy per GPU the library
+// runs on, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not the device copy, so its device address is looked up
+// once per device (with that device current) and only that address is used.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mtx;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mtx);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace coda

@@ -110,5 +110,11 @@ hipError_t launch_ce_dlogits(const void* logits, const int* labels, const float*
 hipError_t launch_dy(void* dR, const void* y, const float* r, const float* c, const void* dy_in,
                      int64_t M, int64_t d, hipStream_t stream);
 
+// Size of the built-in device scratch of coda_fwd_noalloc (80 MiB: the
+// forward workspace of the LLaMA-7B- and 70B-hidden-shaped blocks fits).
+constexpr size_t kNoAllocScratchBytes = (size_t)80 << 20;
+// The current device's copy of that scratch (its address is looked up on the
+// first call on each device and kept); no allocation.
+hipError_t noalloc_scratch(void** ptr);
 
 }  // namespace coda

@@ -16,7 +16,8 @@
  * (HIP device memory of the current device) unless it is marked host.  The
  * caller owns every buffer, including the workspace; the library allocates
  * no device memory and keeps no state between calls (apart from the optional
- * kernel tracing at the end of this header), so calls are reentrant.
+ * kernel tracing at the end of this header, and the built-in scratch of
+ * coda_fwd_noalloc), so calls are reentrant.
  *
  * Element types: `dtype` is the type of every tensor argument except r,
  * dgamma and the workspace: CODA_BF16 (bfloat16, 2 bytes) or CODA_F32.
@@ -101,6 +102,28 @@ coda_status coda_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
                      const void* X, const void* W1, const void* R, const void* gamma,
                      const void* W2, void* y, float* r, void* z,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * coda_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same computation, arguments, checks and results as coda_fwd, without the
+ * workspace: the partial sums and y * gamma go to a scratch array built into
+ * the library (CODA_NOALLOC_SCRATCH_BYTES = 80 MiB, one copy per device,
+ * held until the process ends).  The call allocates nothing; its first call
+ * on a device looks up that device's copy (with the device current).
+ *   Needs coda_fwd_workspace_bytes(dtype, M, K, d, N) <= 80 MiB, else returns
+ *   CODA_ERR_WORKSPACE and enqueues nothing (the LLaMA-7B-shaped and
+ *   70B-hidden-shaped forwards need about 64.5 MiB).
+ * Every call on one device shares that device's scratch, and nothing in it
+ * must start at zero: calls that overlap on one device (on different
+ * streams, or from different threads without ordering) race and give wrong
+ * results.  Calls ordered on one stream are safe.
+ * ---------------------------------------------------------------------- */
+#define CODA_NOALLOC_SCRATCH_BYTES ((size_t)80 << 20)
+coda_status coda_fwd_noalloc(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t N,
+                             float eps, const void* X, const void* W1, const void* R,
+                             const void* gamma, const void* W2, void* y, float* r, void* z,
+                             void* stream);
 
 /* ------------------------------------------------------------------------
  * Backward of the same block: the exact gradient of L = <dz, z>, given the

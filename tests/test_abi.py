@@ -133,6 +133,38 @@ def test_too_large_tensor(L):
     assert call_fwd(L, a) == SHAPE
 
 
+def call_fwd_noalloc(L, a):
+    return L.coda_fwd_noalloc(a["dtype"], a["M"], a["K"], a["d"], a["N"], a["eps"], a["X"], a["W1"], a["R"],
+                              a["gamma"], a["W2"], a["y"], a["r"], a["z"], None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dtype", 5, DTYPE), ("X", None, NULL), ("z", None, NULL), ("M", 0, SHAPE), ("N", 81, SHAPE),
+    ("eps", 0.0, EPS), ("eps", float("nan"), EPS),
+])
+def test_fwd_noalloc_rejects(L, field, value, status):
+    """The workspace-free forward checks its arguments like coda_fwd, before
+    any HIP call."""
+    a = fwd_args()
+    a[field] = value
+    assert call_fwd_noalloc(L, a) == status
+
+
+def test_fwd_noalloc_scratch_limit_and_alias(L):
+    """A forward whose workspace would exceed the built-in 80 MiB scratch is
+    refused with CODA_ERR_WORKSPACE before any HIP call; the LLaMA-7B- and
+    70B-hidden-shaped forwards fit.  Outputs over inputs are still refused."""
+    limit = 80 << 20
+    assert L.coda_fwd_workspace_bytes(BF16, 8192, 4096, 4096, 11008) <= limit
+    assert L.coda_fwd_workspace_bytes(BF16, 4096, 8192, 8192, 28672) <= limit
+    a = fwd_args(M=8192, K=64, d=8192, N=64)          # y * gamma alone is 128 MiB
+    assert L.coda_fwd_workspace_bytes(BF16, 8192, 64, 8192, 64) > limit
+    assert call_fwd_noalloc(L, a) == WORKSPACE
+    a = fwd_args()
+    a["z"] = ctypes.c_void_p(a["X"].value)
+    assert call_fwd_noalloc(L, a) == ALIAS
+
+
 def bwd_call(L, **over):
     m = FakeMem()
     M, K, d, N = 64, 32, 48, 80
