@@ -218,30 +218,40 @@ struct LoaderKMajor {
     pair = 2u * R * ldb;
     ldsoff = __builtin_amdgcn_readfirstlane(w) * LP * 1024;
   }
+  __device__ void issue_one(lds_char* tile, int k0, int p) const {
+    const bool ok = (row + R * p) < 0 && (k0 + kq[p & 1]) < K;
+    dma16(rs, ok ? gbase[p & 1] + (uint32_t)(p >> 1) * pair + (uint32_t)(k0 * 2) : OOB,
+          tile + ldsoff + p * 1024);
+  }
   __device__ void issue(lds_char* tile, int k0) const {
 #pragma unroll
-    for (int p = 0; p < LP; ++p) {
-      const bool ok = (row + R * p) < 0 && (k0 + kq[p & 1]) < K;
-      dma16(rs, ok ? gbase[p & 1] + (uint32_t)(p >> 1) * pair + (uint32_t)(k0 * 2) : OOB,
-            tile + ldsoff + p * 1024);
-    }
+    for (int p = 0; p < LP; ++p) issue_one(tile, k0, p);
   }
 };
 
 // Contraction index strided: the matrix is [K rows][MN cols].  Load p of
 // wave w fills tile k rows 2(LP w + p) and +1: lane l takes row +l/32 and the
-// MN chunk whose swizzled position is l%32 (the swizzle repeats every two
-// loads).  GATED maps tile columns onto the [gate | up] halves of a [d, 2F]
-// weight: the tile is cut into groups of TN columns (one wave's width) whose
-// first half holds gate columns j and second half the up columns F + j of the
-// same j, so one lane ends up holding a gate and its up value.
+// MN chunk whose swizzled position is l%32.  The swizzle of row k depends on
+// k % 4 and bit 3 of k, so the chunk a lane fetches repeats with the load's
+// phase: its parity, and (when a wave fills more than 8 k rows) which half
+// of each 16-row block it falls in.  GATED maps tile columns onto the [gate |
+// up] halves of a [d, 2F] weight: the tile is cut into groups of TN columns
+// (one 64-column epilogue half) whose first half holds gate columns j and
+// second half the up columns F + j of the same j, so one lane ends up holding
+// a gate and its up value.
 template <class KC, int NT, bool GATED, int TN = 64>
 struct LoaderMNMajor {
   static constexpr int LP = KC::OPER_BYTES / 1024 / (NT / 64);
-  static_assert(LP % 2 == 0, "swizzle period");
+  static_assert(LP % 2 == 0 && (LP <= 4 || LP % 8 == 0), "swizzle period");
+  static constexpr int NPH = LP >= 8 ? 4 : 2;   // load phases with distinct chunks
+  // phase of load p: its parity, and bit 2 of (LP w + p) = bit 3 of its k row
+  // (LP w is a multiple of 8 when LP >= 8, so p alone decides it)
+  static __device__ __forceinline__ constexpr int phase(int p) { return (p & 1) | (NPH == 4 ? ((p >> 2) & 1) << 1 : 0); }
+  // first load of phase ph
+  static __device__ __forceinline__ constexpr int first(int ph) { return (ph & 1) | ((ph >> 1) << 2); }
   __amdgpu_buffer_rsrc_t rs;
-  uint32_t gbase[2];    // loads 0 and 1 at k0 = 0
-  bool colok[2];
+  uint32_t gbase[NPH];  // the first load of each phase, at k0 = 0
+  bool colok[NPH];
   int krow;             // the lane's k row in load 0, minus K
   uint32_t ldb;
   int ldsoff;
@@ -252,9 +262,10 @@ struct LoaderMNMajor {
     ldb = (uint32_t)(ld * 2);
     const int w = t >> 6, l = t & 63;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int ph = 0; ph < NPH; ++ph) {
+      const int p = first(ph);
       const int k = 2 * (LP * w + p) + (l >> 5);
-      const int c = (l & 31) ^ mn_swz(k);   // the same for loads p and p + 2 (k + 4)
+      const int c = (l & 31) ^ mn_swz(k);   // the same for every load of this phase
       int col;
       bool ok;
       if (GATED) {
@@ -268,19 +279,22 @@ struct LoaderMNMajor {
         col = col0 + c * 8;
         ok = col < cols;
       }
-      colok[p] = ok;
-      gbase[p] = (uint32_t)k * ldb + (uint32_t)col * 2u;
+      colok[ph] = ok;
+      gbase[ph] = (uint32_t)k * ldb + (uint32_t)col * 2u;
     }
     krow = 2 * LP * w + (l >> 5) - K_;
     ldsoff = __builtin_amdgcn_readfirstlane(w) * LP * 1024;
   }
+  __device__ void issue_one(lds_char* tile, int k0, int p) const {
+    const int ph = phase(p);
+    const bool ok = colok[ph] && (k0 + krow + 2 * p) < 0;
+    // load p's k row is that of its phase's first load plus 2 (p - first)
+    dma16(rs, ok ? gbase[ph] + (uint32_t)(k0 + 2 * (p - first(ph))) * ldb : OOB,
+          tile + ldsoff + p * 1024);
+  }
   __device__ void issue(lds_char* tile, int k0) const {
 #pragma unroll
-    for (int p = 0; p < LP; ++p) {
-      const bool ok = colok[p & 1] && (k0 + krow + 2 * p) < 0;
-      dma16(rs, ok ? gbase[p & 1] + (uint32_t)(k0 + 4 * (p >> 1)) * ldb : OOB,
-            tile + ldsoff + p * 1024);
-    }
+    for (int p = 0; p < LP; ++p) issue_one(tile, k0, p);
   }
 };
 
@@ -440,7 +454,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   const int row0 = tm * BM, col0 = tn * BN;
 
   typename LoaderSel<AK, KC, G::NT, false, TN>::type la;
-  typename LoaderSel<BKM, KC, G::NT, GATED, TN>::type lb;
+  typename LoaderSel<BKM, KC, G::NT, GATED, 64>::type lb;   // gate/up groups of one 64-column half
   // MXFP8: the loaders count in 2-byte units (K / 2, ld / 2)
   constexpr int U = FMT == FMT_MX8 ? 2 : 1;
   la.init(g.A, g.A_bytes, g.lda / U, row0, g.M, g.K / U, t, 0, tm);
@@ -474,6 +488,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   };
 
   if constexpr (FMT == FMT_MX8) {
+    static_assert(WMv * WNv == 8, "the MXFP8 scale staging assumes 8 waves");
     // Same pipeline as the bf16 loop below (two sub-steps of 64 k per K step
     // of 128), plus the scales: each wave loads 64 rows' 4 scale bytes of the
     // step (waves 0-3 A rows, 4-7 B rows) with one dword direct-to-LDS load,
@@ -662,23 +677,29 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   __builtin_amdgcn_s_waitcnt(0);             // no load may still write into LDS
 
   // ------------------------------ epilogue ------------------------------
-  // The accumulators are moved, 32 rows (one block row i) at a time, through
-  // a wave-private LDS region (32 rows x 64 fp32, 16-byte chunks swizzled by
-  // row) into a row-major assignment: in pass p, lane l owns row
-  // 32i + 8p + l/8 of the wave tile and its 8 consecutive columns 8(l%8)..+7.
-  // Every global load and store of the epilogue is then a 16-byte vector and
-  // 8 lanes cover one 128-byte row segment.  Only the cross-wave reductions
-  // need a workgroup barrier.
-  static_assert(TN == 64 && FN == 2, "row-major epilogue assumes 64-column wave tiles");
+  // The epilogue works on "virtual waves" 64 columns wide: a wave whose tile
+  // is TN = 64 NH columns wide runs it NH times, once per 64-column half, so
+  // the row-major assignment, the LDS staging and the cross-wave reductions
+  // below have the same shape for every wave grid (WM x WNV virtual waves of
+  // TM x 64).  Per half, the accumulators are moved, 32 rows (one block row
+  // i) at a time, through a wave-private LDS region (32 rows x 64 fp32,
+  // 16-byte chunks swizzled by row) into a row-major assignment: in pass p,
+  // lane l owns row 32i + 8p + l/8 of the wave tile and its 8 consecutive
+  // columns 8(l%8)..+7 of the half.  Every global load and store of the
+  // epilogue is then a 16-byte vector and 8 lanes cover one 128-byte row
+  // segment.  Only the cross-wave reductions need a workgroup barrier.
+  constexpr int VW = 64;                            // virtual wave width
+  constexpr int NH = TN / VW;                       // halves per wave
+  constexpr int WNV = WNv * NH;                     // virtual waves across the tile
+  constexpr int BFNV = VW / MB;                     // MFMA block columns per half
+  static_assert(TN % VW == 0 && NH >= 1, "wave tiles are whole 64-column halves");
   const int l32 = lane & 31;
   __syncthreads();                                  // main loop done: LDS is free
   char* region = smem + wave * 8192;
-  float* red = (float*)(smem + 8 * 8192);           // [WN][BM] row partials
-  float* redc = red + WNv * BM;                     // [WM][BN] column partials
+  float* red = (float*)(smem + 8 * 8192);           // [WNV][BM] row partials
+  float* redc = red + WNV * BM;                     // [WM][BN] column partials
   const int c8 = lane & 7, rsub = lane >> 3;
-  const int gcol = col0 + wn * TN + 8 * c8;         // first global column of the lane
-  const bool colok = gcol < g.N;
-  auto dump = [&](int i) {   // the wave tile's rows 32i..32i+31 into the region
+  auto dump = [&](int i, int hv) {   // rows 32i..32i+31 of half hv into the region
     if constexpr (MB == 16) {
       // 16x16 blocks (2i, 2i+1): lane l holds row l%16 and columns
       // 16j + 4(l/16)..+3 of block (2i+h, j)
@@ -686,17 +707,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < BFN; ++j) {
+        for (int j = 0; j < BFNV; ++j) {
           const int row = 16 * h + r16, c = 4 * j + (lane >> 4);
-          *(f32x4*)(region + row * 256 + ((c ^ (row & 15)) << 4)) = acc[2 * i + h][j];
+          *(f32x4*)(region + row * 256 + ((c ^ (row & 15)) << 4)) = acc[2 * i + h][hv * BFNV + j];
         }
     } else {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < BFNV; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int c = j * 8 + 2 * q + (lane >> 5);
-          *(f32x4*)(region + l32 * 256 + ((c ^ (l32 & 15)) << 4)) = quad(acc[i][j], q);
+          *(f32x4*)(region + l32 * 256 + ((c ^ (l32 & 15)) << 4)) = quad(acc[i][hv * BFNV + j], q);
         }
     }
   };
@@ -715,8 +736,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   };
   // EPI_RSQRT_*: r for the tile's rows from the first GEMM's partial sums,
   // summed in the same order as the stand-alone reduction kernel, into rrow
-  float* rrow = red + WNv * BM + WMv * BN;          // [BM] row scales
-  float* cered = rrow + BM;                         // [WN][BM] sum-exp partials (EPI_CE_STATS)
+  float* rrow = red + WNV * BM + WMv * BN;          // [BM] row scales
+  float* cered = rrow + BM;                         // [WNV][BM] sum-exp partials (EPI_CE_STATS)
   auto tile_row_rsqrt = [&]() {
     if (t < BM) {
       const int row = row0 + t;
@@ -743,6 +764,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
                 EPI == EPI_DN || EPI == EPI_SWIGLU_BWD || EPI == EPI_RSQRT_SCALE ||
                 EPI == EPI_CE_STATS || EPI == EPI_ROPE) {
     __bf16* C = (__bf16*)g.C;
+    if constexpr (EPI == EPI_RSQRT_SCALE) tile_row_rsqrt();
+#pragma unroll
+    for (int hv = 0; hv < NH; ++hv) {
+    const int wnv = wn * NH + hv;                   // virtual wave column
+    const int gcol = col0 + wnv * VW + 8 * c8;      // first global column of the lane
+    const bool colok = gcol < g.N;
     f32x4 glo{}, ghi{}, clo{0.f, 0.f, 0.f, 0.f}, chi{0.f, 0.f, 0.f, 0.f};
     if constexpr (EPI == EPI_DN || EPI == EPI_RESID_SUMSQ) {
       if (colok && g.vcol) ld8((const __bf16*)g.vcol + gcol, glo, ghi);
@@ -773,12 +800,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       hi = f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
     };
     prefetch(0, 0);
-    if constexpr (EPI == EPI_RSQRT_SCALE) tile_row_rsqrt();
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if (i + 1 < FM) prefetch(i + 1, (i + 1) & 1);
       wave_lds_sync();                              // the previous pass's reads are done
-      dump(i);
+      dump(i, hv);
       __builtin_amdgcn_s_waitcnt(0xc07f);           // this wave's LDS writes are done
       wave_lds_sync();
 #pragma unroll
@@ -846,7 +872,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             s = sq[0] + sq[1] + sq[2] + sq[3];
           }
           s = sum8(s);
-          if (c8 == 0) red[wn * BM + lrow_t] = s;
+          if (c8 == 0) red[wnv * BM + lrow_t] = s;
           if constexpr (FMT == FMT_MX8) {
             // y * gamma to MXFP8: the 4 lanes c8 = 4b..4b+3 hold one 32-column
             // block of the row; shared exponent floor(log2 amax) - 8 (clamped
@@ -890,10 +916,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             chi += hi * yhi * rv;
           }
           s = sum8(s);
-          if (c8 == 0) red[wn * BM + lrow_t] = s;
+          if (c8 == 0) red[wnv * BM + lrow_t] = s;
         } else if constexpr (EPI == EPI_CE_STATS) {
           // logits stored; the stateful max / sum-exp of the row over this
-          // wave's 64 columns (8 lanes x 8), columns past N left out
+          // half's 64 columns (8 lanes x 8), columns past N left out
           float mx = -INFINITY;
           if (ok) {
             st8(C + o, lo, hi);
@@ -915,8 +941,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           }
           se = sum8(se);
           if (c8 == 0) {
-            red[wn * BM + lrow_t] = mx;
-            cered[wn * BM + lrow_t] = se;
+            red[wnv * BM + lrow_t] = mx;
+            cered[wnv * BM + lrow_t] = se;
           }
         } else if constexpr (EPI == EPI_SWIGLU_BWD) {
           // da = acc [M, F]; g, u from the saved gu; dgu = [dg | du]
@@ -941,7 +967,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       }
       if constexpr (EPI == EPI_RESID_SUMSQ) {
         // y * gamma transposed: C2[col][row].  In pass q, lanes 4c..4c+3 take
-        // column 16q + c of the wave's 64 and rows 8(l%4)..+7 each, so one
+        // column 16q + c of the half's 64 and rows 8(l%4)..+7 each, so one
         // store instruction writes 16 columns x 64 contiguous bytes.
         if (FMT == FMT_BF16 && g.C2 && g.c2_trans) {
           __builtin_amdgcn_s_waitcnt(0xc07f);         // this wave's LDS writes are done
@@ -956,7 +982,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
               const int r = rg + e;
               v[e] = *(const float*)(region + r * 256 + (((c >> 2) ^ (r & 15)) << 4) + (c & 3) * 4);
             }
-            const int colT = col0 + wn * TN + c;
+            const int colT = col0 + wnv * VW + c;
             const int rowT = row0 + wm * TM + i * 32 + rg;
             if (colT < g.N && rowT < g.M)
               *(bf16x8*)((__bf16*)g.C2 + (int64_t)colT * g.ldc2 + rowT) =
@@ -966,18 +992,36 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         }
       }
     }
+    if constexpr (EPI == EPI_DN) {
+      // column partials of this half: reduce over the 8 row groups of lanes
+      // (l/8); the WM waves that share these columns combine through LDS below
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        clo[e] += __shfl_xor(clo[e], 8);
+        clo[e] += __shfl_xor(clo[e], 16);
+        clo[e] += __shfl_xor(clo[e], 32);
+        chi[e] += __shfl_xor(chi[e], 8);
+        chi[e] += __shfl_xor(chi[e], 16);
+        chi[e] += __shfl_xor(chi[e], 32);
+      }
+      if (lane < 8) {
+        *(f32x4*)(redc + wm * BN + wnv * VW + 8 * c8) = clo;
+        *(f32x4*)(redc + wm * BN + wnv * VW + 8 * c8 + 4) = chi;
+      }
+    }
+    }   // halves
     if constexpr (EPI == EPI_CE_STATS) {
-      // combine the WN waves' (max, sum-exp) of each row in wave order
+      // combine the WNV virtual waves' (max, sum-exp) of each row in order; a
+      // virtual wave whose columns all lie past N left (max -inf, sum 0) and
+      // is skipped by its zero sum; a NaN logit made its sum NaN, which the
+      // row keeps (fmaxf alone would drop it)
       __syncthreads();
       if (t < BM) {
         const int row = row0 + t;
         float m = red[t];
-        for (int w = 1; w < WNv; ++w) m = fmaxf(m, red[w * BM + t]);
-        // a wave whose columns all lie past N left (max -inf, sum 0) and is
-        // skipped by its zero sum; a NaN logit made its sum NaN, which the
-        // row keeps (fmaxf alone would drop it)
+        for (int w = 1; w < WNV; ++w) m = fmaxf(m, red[w * BM + t]);
         float sm = 0.0f;
-        for (int w = 0; w < WNv; ++w) {
+        for (int w = 0; w < WNV; ++w) {
           const float sw = cered[w * BM + t];
           if (sw != 0.0f) sm += sw * __expf(red[w * BM + t] - m);
         }
@@ -988,29 +1032,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       }
     }
     if constexpr (EPI == EPI_RESID_SUMSQ || EPI == EPI_DN) {
-      if constexpr (EPI == EPI_DN) {
-        // column partials: reduce over the 8 row groups of lanes (l/8), then
-        // combine the WM waves that share these columns through LDS
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          clo[e] += __shfl_xor(clo[e], 8);
-          clo[e] += __shfl_xor(clo[e], 16);
-          clo[e] += __shfl_xor(clo[e], 32);
-          chi[e] += __shfl_xor(chi[e], 8);
-          chi[e] += __shfl_xor(chi[e], 16);
-          chi[e] += __shfl_xor(chi[e], 32);
-        }
-        if (lane < 8) {
-          *(f32x4*)(redc + wm * BN + wn * TN + 8 * c8) = clo;
-          *(f32x4*)(redc + wm * BN + wn * TN + 8 * c8 + 4) = chi;
-        }
-      }
       __syncthreads();
       if (t < BM) {
         const int row = row0 + t;
         float s = 0.0f;
 #pragma unroll
-        for (int w = 0; w < WNv; ++w) s += red[w * BM + t];
+        for (int w = 0; w < WNV; ++w) s += red[w * BM + t];
         if (row < g.M) g.part_row[(int64_t)row * g.ld_part_row + tn] = s;
       }
       if constexpr (EPI == EPI_DN) {
@@ -1024,20 +1051,22 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_RSQRT_SWIGLU) {
-    // The wave tile's 64 columns are 32 gate columns j and the 32 up columns
-    // of the same j.  Pass p: lane l owns row 16p + l/4 and gate/up column
-    // group l%4 (8 columns each).  EPI_RSQRT_SWIGLU first scales both by the
-    // row's RMS factor r (the GEMM's A operand is the un-normalised y gamma).
+    // Each half's 64 columns are 32 gate columns j and the 32 up columns of
+    // the same j.  Pass p: lane l owns row 16p + l/4 and gate/up column group
+    // l%4 (8 columns each).  EPI_RSQRT_SWIGLU first scales both by the row's
+    // RMS factor r (the GEMM's A operand is the un-normalised y gamma).
     if constexpr (EPI == EPI_RSQRT_SWIGLU) tile_row_rsqrt();
     __bf16* GU = (__bf16*)g.C;
     __bf16* Aout = (__bf16*)g.C2;
     const int c4 = lane & 3, r4 = lane >> 2;
-    const int jj = tn * (BN / 2) + wn * (TN / 2) + 8 * c4;
+#pragma unroll
+    for (int hv = 0; hv < NH; ++hv) {
+    const int jj = tn * (BN / 2) + (wn * NH + hv) * (VW / 2) + 8 * c4;
     const bool jok = jj < g.F;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       wave_lds_sync();                              // the previous pass's reads are done
-      dump(i);
+      dump(i, hv);
       __builtin_amdgcn_s_waitcnt(0xc07f);
       wave_lds_sync();
 #pragma unroll
@@ -1067,6 +1096,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         }
       }
     }
+    }   // halves
   }
 }
 
@@ -1277,8 +1307,12 @@ __global__ void dy_kernel(__bf16* __restrict__ dR, const __bf16* __restrict__ y,
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-// Wave grid used for every bf16 GEMM: 2 x 4 waves (two per SIMD).
+// Wave grid of every bf16 and MXFP8 GEMM: 2 x 4 waves of 128 x 64 (two per
+// SIMD).  A 2 x 2 grid of 128 x 128 wave tiles (one wave per SIMD, a third
+// fewer LDS reads per MFMA) measured 13-15% slower: with no second wave on the
+// SIMD its stalls are not covered, and it still ran into the power limit.
 constexpr int kWavesM = 2, kWavesN = 4;
+constexpr int kMxWavesM = kWavesM, kMxWavesN = kWavesN;
 
 // K step / ring depth: 64 x 2 when an operand is K-contiguous, else 32 x 4.
 // A GEMM with a K-contiguous A operand whose operands together take more
@@ -1362,8 +1396,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStr
 template <int EPI>
 static hipError_t launch_mx8_one(const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_mx8_kernel<kWavesM, kWavesN, EPI>), dim3(tiles),
-                     dim3(64 * kWavesM * kWavesN), 0, s, g);
+  hipLaunchKernelGGL((gemm_mx8_kernel<kMxWavesM, kMxWavesN, EPI>), dim3(tiles),
+                     dim3(64 * kMxWavesM * kMxWavesN), 0, s, g);
   return hipGetLastError();
 }
 
