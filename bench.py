@@ -767,8 +767,8 @@ def cpu_baseline(w, h, target_s):
 # The workloads timed besides the main one.  The 70B-hidden block is part of
 # the headline metric; the rest are the other fused patterns.
 HEADLINE_SECOND = "llama70b_fwdbwd"
-ALSO = ("swiglu_fwdbwd", "llama7b_mlp_fwdbwd", "llama7b_ce_fwdbwd", "llama7b_qkv_rope_fwdbwd",
-        "llama7b_fwd_mx8", "llama1b_fwd")
+ALSO = ("swiglu_fwdbwd", "llama7b_mlp_fwdbwd", "llama7b_ce_fwdbwd", "llama3_8b_ce_fwdbwd",
+        "llama7b_qkv_rope_fwdbwd", "llama7b_fwd_mx8", "llama1b_fwd")
 
 
 def _brief(s):

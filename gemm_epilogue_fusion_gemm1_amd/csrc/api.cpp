@@ -4,6 +4,7 @@
 // nor the stream.
 #include "../../include/coda.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <vector>
@@ -14,7 +15,16 @@ namespace {
 
 using coda::GemmArgs;
 
-constexpr uint64_t kMaxTensorBytes = 0x7FFFFFF0ull;   // buffer descriptors address < 2 GiB
+// Size limits.  The GEMM loaders reach an operand through buffer windows of
+// at most 2 GiB: a K-contiguous operand's window holds the tile's 256 rows, an
+// MN-contiguous operand's window one K step (at most 64 rows), so a tensor may
+// be far larger than 2 GiB as long as its rows are not too long.  Every
+// contiguous row length (K, d, N, F, 2F, V) is at most 2^21 elements, the row
+// count M at most 2^23 (M is the contiguous index of y*gamma stored
+// transposed), and no tensor exceeds 1 TiB.
+constexpr uint64_t kMaxTensorBytes = 1ull << 40;
+constexpr int64_t kMaxRowLen = (int64_t)1 << 21;
+constexpr int64_t kMaxRows = (int64_t)1 << 23;
 static_assert(coda::kNoAllocScratchBytes == CODA_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
 constexpr size_t kAlign = 256;
 
@@ -23,9 +33,14 @@ bool dtype_ok(int t) { return t == CODA_F32 || t == CODA_BF16; }
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// a row length (K, d, N, F, V); the token count M goes through rows_ok
 bool dim_ok(coda_dtype t, int64_t v) {
   const int64_t q = t == CODA_BF16 ? 8 : 4;
-  return v >= q && v % q == 0 && v <= (int64_t)1 << 24;
+  return v >= q && v % q == 0 && v <= kMaxRowLen;
+}
+bool rows_ok(coda_dtype t, int64_t v) {
+  const int64_t q = t == CODA_BF16 ? 8 : 4;
+  return v >= q && v % q == 0 && v <= kMaxRows;
 }
 bool bytes_ok(coda_dtype t, int64_t a, int64_t b) {
   return (uint64_t)a * (uint64_t)b * esize(t) <= kMaxTensorBytes;
@@ -125,10 +140,12 @@ GemmArgs gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, uint6
   g.K = (int)K;
   g.A = A;
   g.lda = lda;
-  g.A_bytes = (uint32_t)(A_elems * 2);
+  g.A_total = A_elems * 2;
+  g.A_bytes = (uint32_t)std::min<uint64_t>(g.A_total, 0x7FFFFFF0ull);
   g.B = B;
   g.ldb = ldb;
-  g.B_bytes = (uint32_t)(B_elems * 2);
+  g.B_total = B_elems * 2;
+  g.B_bytes = (uint32_t)std::min<uint64_t>(g.B_total, 0x7FFFFFF0ull);
   g.C = C;
   g.ldc = ldc;
   return g;
@@ -219,8 +236,11 @@ hipError_t launch_norm_bwd(int64_t M, int64_t K, int64_t d, int64_t N, const voi
 }
 
 // ------------------------------------------------------------- MXFP8
-bool mx_dim_ok(int64_t v, int64_t q) { return v >= q && v % q == 0 && v <= (int64_t)1 << 24; }
+bool mx_dim_ok(int64_t v, int64_t q) { return v >= q && v % q == 0 && v <= kMaxRowLen; }
+bool mx_rows_ok(int64_t v, int64_t q) { return v >= q && v % q == 0 && v <= kMaxRows; }
 bool fits(int64_t a, int64_t b, int64_t e) { return (uint64_t)a * (uint64_t)b * (uint64_t)e <= kMaxTensorBytes; }
+// MXFP8 scales are read through one buffer of at most 2 GiB
+bool scales_fit(int64_t rows, int64_t cols) { return (uint64_t)rows * (uint64_t)(cols / 32) <= 0x7FFFFFF0ull; }
 
 struct Mx8Ws {
   size_t P, q, qs, total;
@@ -245,10 +265,12 @@ GemmArgs gemm_mx8(int64_t M, int64_t N, int64_t K, const void* Aq, const void* A
   g.K = (int)K;
   g.A = Aq;
   g.lda = K;
-  g.A_bytes = (uint32_t)(M * K);
+  g.A_total = (uint64_t)(M * K);
+  g.A_bytes = (uint32_t)std::min<uint64_t>(g.A_total, 0x7FFFFFF0ull);
   g.B = Bq;
   g.ldb = K;
-  g.B_bytes = (uint32_t)(N * K);
+  g.B_total = (uint64_t)(N * K);
+  g.B_bytes = (uint32_t)std::min<uint64_t>(g.B_total, 0x7FFFFFF0ull);
   g.sA = (const uint8_t*)As;
   g.sB = (const uint8_t*)Bs;
   g.sA_bytes = (uint32_t)(M * (K / 32));
@@ -296,7 +318,7 @@ coda_status fwd_check(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t
                       const void* W2, void* y, float* r, void* z) {
   if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
   if (!X || !W1 || !R || !gamma || !W2 || !y || !r || !z) return CODA_ERR_NULL;
-  if (!dim_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, d) || !dim_ok(dtype, N))
+  if (!rows_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, d) || !dim_ok(dtype, N))
     return CODA_ERR_SHAPE;
   if (!bytes_ok(dtype, M, K) || !bytes_ok(dtype, K, d) || !bytes_ok(dtype, M, d) ||
       !bytes_ok(dtype, d, N) || !bytes_ok(dtype, M, N))
@@ -416,7 +438,7 @@ coda_status coda_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int64_t 
   if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
   if (!X || !W1 || !gamma || !W2 || !y || !r || !dz || !dX || !dW1 || !dR || !dW2 || !dgamma)
     return CODA_ERR_NULL;
-  if (!dim_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, d) || !dim_ok(dtype, N))
+  if (!rows_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, d) || !dim_ok(dtype, N))
     return CODA_ERR_SHAPE;
   if (!bytes_ok(dtype, M, K) || !bytes_ok(dtype, K, d) || !bytes_ok(dtype, M, d) ||
       !bytes_ok(dtype, d, N) || !bytes_ok(dtype, M, N))
@@ -457,7 +479,8 @@ coda_status coda_swiglu_fwd(coda_dtype dtype, int64_t M, int64_t d, int64_t F, c
   (void)workspace_bytes;
   if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
   if (!X || !W || !Wd || !gu || !a || !z) return CODA_ERR_NULL;
-  if (!dim_ok(dtype, M) || !dim_ok(dtype, d) || !dim_ok(dtype, F)) return CODA_ERR_SHAPE;
+  if (!rows_ok(dtype, M) || !dim_ok(dtype, d) || !dim_ok(dtype, F) || !dim_ok(dtype, 2 * F))
+    return CODA_ERR_SHAPE;
   if (!bytes_ok(dtype, M, d) || !bytes_ok(dtype, d, 2 * F) || !bytes_ok(dtype, F, d) ||
       !bytes_ok(dtype, M, 2 * F))
     return CODA_ERR_SHAPE;
@@ -498,7 +521,8 @@ coda_status coda_swiglu_bwd(coda_dtype dtype, int64_t M, int64_t d, int64_t F, c
                             size_t workspace_bytes, void* stream) {
   if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
   if (!X || !W || !Wd || !gu || !a || !dz || !dX || !dW || !dWd) return CODA_ERR_NULL;
-  if (!dim_ok(dtype, M) || !dim_ok(dtype, d) || !dim_ok(dtype, F)) return CODA_ERR_SHAPE;
+  if (!rows_ok(dtype, M) || !dim_ok(dtype, d) || !dim_ok(dtype, F) || !dim_ok(dtype, 2 * F))
+    return CODA_ERR_SHAPE;
   if (!bytes_ok(dtype, M, d) || !bytes_ok(dtype, d, 2 * F) || !bytes_ok(dtype, F, d) ||
       !bytes_ok(dtype, M, 2 * F))
     return CODA_ERR_SHAPE;
@@ -605,7 +629,8 @@ coda_status coda_mlp_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int6
                          void* z, void* workspace, size_t workspace_bytes, void* stream) {
   if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
   if (!X || !W1 || !R || !gamma || !W || !Wd || !y || !r || !gu || !a || !z) return CODA_ERR_NULL;
-  if (!dim_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, d) || !dim_ok(dtype, F))
+  if (!rows_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, d) || !dim_ok(dtype, F) ||
+      !dim_ok(dtype, 2 * F))
     return CODA_ERR_SHAPE;
   if (!bytes_ok(dtype, M, K) || !bytes_ok(dtype, K, d) || !bytes_ok(dtype, M, d) ||
       !bytes_ok(dtype, d, 2 * F) || !bytes_ok(dtype, F, d) || !bytes_ok(dtype, M, 2 * F))
@@ -673,7 +698,8 @@ coda_status coda_mlp_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t d, int6
   if (!X || !W1 || !gamma || !W || !Wd || !y || !r || !gu || !a || !dz || !dX || !dW1 || !dR ||
       !dW || !dWd || !dgamma)
     return CODA_ERR_NULL;
-  if (!dim_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, d) || !dim_ok(dtype, F))
+  if (!rows_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, d) || !dim_ok(dtype, F) ||
+      !dim_ok(dtype, 2 * F))
     return CODA_ERR_SHAPE;
   if (!bytes_ok(dtype, M, K) || !bytes_ok(dtype, K, d) || !bytes_ok(dtype, M, d) ||
       !bytes_ok(dtype, d, 2 * F) || !bytes_ok(dtype, F, d) || !bytes_ok(dtype, M, 2 * F))
@@ -754,7 +780,7 @@ coda_status coda_ce_fwd(coda_dtype dtype, int64_t M, int64_t d, int64_t V, const
                         float* loss, void* workspace, size_t workspace_bytes, void* stream) {
   if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
   if (!h || !Wv || !labels || !logits || !lse || !loss) return CODA_ERR_NULL;
-  if (!dim_ok(dtype, M) || !dim_ok(dtype, d) || !dim_ok(dtype, V)) return CODA_ERR_SHAPE;
+  if (!rows_ok(dtype, M) || !dim_ok(dtype, d) || !dim_ok(dtype, V)) return CODA_ERR_SHAPE;
   if (!bytes_ok(dtype, M, d) || !bytes_ok(dtype, d, V) || !bytes_ok(dtype, M, V))
     return CODA_ERR_SHAPE;
   if (dtype != CODA_BF16) return CODA_ERR_UNSUPPORTED;
@@ -807,7 +833,7 @@ coda_status coda_ce_bwd(coda_dtype dtype, int64_t M, int64_t d, int64_t V, const
                         void* workspace, size_t workspace_bytes, void* stream) {
   if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
   if (!h || !Wv || !labels || !logits || !lse || !dloss || !dh || !dWv) return CODA_ERR_NULL;
-  if (!dim_ok(dtype, M) || !dim_ok(dtype, d) || !dim_ok(dtype, V)) return CODA_ERR_SHAPE;
+  if (!rows_ok(dtype, M) || !dim_ok(dtype, d) || !dim_ok(dtype, V)) return CODA_ERR_SHAPE;
   if (!bytes_ok(dtype, M, d) || !bytes_ok(dtype, d, V) || !bytes_ok(dtype, M, V))
     return CODA_ERR_SHAPE;
   if (dtype != CODA_BF16) return CODA_ERR_UNSUPPORTED;
@@ -870,7 +896,7 @@ coda_status coda_rope_fwd(coda_dtype dtype, int64_t M, int64_t K, int64_t N, int
                           void* workspace, size_t workspace_bytes, void* stream) {
   if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
   if (!X || !W || !Y) return CODA_ERR_NULL;
-  if (!dim_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, N)) return CODA_ERR_SHAPE;
+  if (!rows_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, N)) return CODA_ERR_SHAPE;
   if (!bytes_ok(dtype, M, K) || !bytes_ok(dtype, K, N) || !bytes_ok(dtype, M, N))
     return CODA_ERR_SHAPE;
   if (!rope_args_ok(N, N_rot, D, S, base)) return CODA_ERR_SHAPE;
@@ -917,7 +943,7 @@ coda_status coda_rope_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t N, int
                           size_t workspace_bytes, void* stream) {
   if (!dtype_ok(dtype)) return CODA_ERR_DTYPE;
   if (!X || !W || !dY || !dX || !dW) return CODA_ERR_NULL;
-  if (!dim_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, N)) return CODA_ERR_SHAPE;
+  if (!rows_ok(dtype, M) || !dim_ok(dtype, K) || !dim_ok(dtype, N)) return CODA_ERR_SHAPE;
   if (!bytes_ok(dtype, M, K) || !bytes_ok(dtype, K, N) || !bytes_ok(dtype, M, N))
     return CODA_ERR_SHAPE;
   if (!rope_args_ok(N, N_rot, D, S, base)) return CODA_ERR_SHAPE;
@@ -963,9 +989,10 @@ coda_status coda_rope_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t N, int
 coda_status coda_mx8_quantize(int64_t rows, int64_t cols, const void* src, int64_t ld_src,
                               void* codes, void* scales, void* stream) {
   if (!src || !codes || !scales) return CODA_ERR_NULL;
-  if (rows < 1 || !mx_dim_ok(cols, 128) || ld_src < cols || ld_src % 8 != 0 || rows > (int64_t)1 << 24)
+  if (rows < 1 || !mx_dim_ok(cols, 128) || ld_src < cols || ld_src % 8 != 0 || ld_src > kMaxRowLen ||
+      rows > kMaxRows)
     return CODA_ERR_SHAPE;
-  if (!fits(rows, ld_src, 2) || !fits(rows, cols, 1)) return CODA_ERR_SHAPE;
+  if (!fits(rows, ld_src, 2) || !fits(rows, cols, 1) || !scales_fit(rows, cols)) return CODA_ERR_SHAPE;
   if (!aligned16(src) || !aligned16(codes)) return CODA_ERR_ALIGN;
   const Range in[] = {rng(src, ((rows - 1) * ld_src + cols) * 2)};
   const Range out[] = {rng(codes, rows * cols), rng(scales, rows * (cols / 32))};
@@ -989,9 +1016,10 @@ coda_status coda_fwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, float eps, 
                          void* z, void* workspace, size_t workspace_bytes, void* stream) {
   if (!Xq || !Xs || !W1tq || !W1ts || !R || !gamma || !W2tq || !W2ts || !y || !r || !z)
     return CODA_ERR_NULL;
-  if (!mx_dim_ok(M, 8) || !mx_dim_ok(N, 8) || !mx_dim_ok(K, 128) || !mx_dim_ok(d, 128))
+  if (!mx_rows_ok(M, 8) || !mx_dim_ok(N, 8) || !mx_dim_ok(K, 128) || !mx_dim_ok(d, 128))
     return CODA_ERR_SHAPE;
-  if (!fits(M, K, 1) || !fits(d, K, 1) || !fits(N, d, 1) || !fits(M, d, 2) || !fits(M, N, 2))
+  if (!fits(M, K, 1) || !fits(d, K, 1) || !fits(N, d, 1) || !fits(M, d, 2) || !fits(M, N, 2) ||
+      !scales_fit(M, K) || !scales_fit(d, K) || !scales_fit(N, d) || !scales_fit(M, d))
     return CODA_ERR_SHAPE;
   if (!std::isfinite(eps) || !(eps > 0.0f)) return CODA_ERR_EPS;
   for (const void* p : {Xq, Xs, W1tq, W1ts, R, gamma, W2tq, W2ts, (const void*)y, (const void*)r,

@@ -96,6 +96,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   // raw buffer: stride 0, num_records in bytes; dword3 0x00020000 = 32-bit data format
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
+// A buffer that starts `off` bytes into a tensor of `total` bytes.  Offsets
+// within it are 32-bit and OOB (2^31) must lie past its end, so it covers at
+// most kMaxWindow bytes; a tensor larger than that is reached through windows
+// based nearer the data (a tile's first row, a K step's first row).
+constexpr uint64_t kMaxWindow = 0x7FFFFFF0ull;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t window_rsrc(const void* p, uint64_t total, uint64_t off) {
+  const uint64_t left = off < total ? total - off : 0;
+  return make_rsrc((const char*)p + off, (uint32_t)(left < kMaxWindow ? left : kMaxWindow));
+}
 
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
@@ -183,12 +192,13 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, l
 }
 #pragma clang diagnostic pop
 
-// Contraction index contiguous: the matrix is [MN rows][K].  Load p of wave w
+// Contraction index contiguous: the matrix is [MN rows][K], reached through a
+// buffer based at the tile's first row.  Load p of wave w
 // fills the 1 KiB of tile rows R(LP w + p) .. +R-1 (R = 1024 / 2BK): lane l
 // takes row +l/KCH and the k chunk whose swizzled position is l%KCH.  The
 // swizzle repeats every two loads, so a lane keeps one base offset and one
 // chunk per load parity and derives the rest.
-template <class KC, int NT, bool GATED>
+template <class KC, int NT, bool GATED, bool WIN>
 struct LoaderKMajor {
   static constexpr int LP = KC::OPER_BYTES / 1024 / (NT / 64);
   static constexpr int R = 1024 / KC::KROW;       // tile rows per load
@@ -201,18 +211,20 @@ struct LoaderKMajor {
   int K;
   int ldsoff;           // wave's first byte within an operand tile
 
-  __device__ void init(const void* ptr, uint32_t bytes, int64_t ld, int row0, int rows, int K_,
+  __device__ void init(const void* ptr, uint64_t bytes, int64_t ld, int row0, int rows, int K_,
                        int t, int, int) {
-    rs = make_rsrc(ptr, bytes);
+    // WIN: the buffer starts at the tile's first row, so offsets stay below
+    // 256 rows; else it covers the whole matrix (at most 2 GiB)
+    const uint32_t ldb = (uint32_t)(ld * 2);
+    rs = WIN ? window_rsrc(ptr, bytes, (uint64_t)row0 * ldb) : make_rsrc(ptr, (uint32_t)bytes);
     K = K_;
     const int w = t >> 6, l = t & 63;
-    const uint32_t ldb = (uint32_t)(ld * 2);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int m = R * (LP * w + p) + l / KC::KCH;
       const int q = (l % KC::KCH) ^ KC::kswz(m);
       kq[p] = 8 * q;
-      gbase[p] = (uint32_t)(row0 + m) * ldb + (uint32_t)(16 * q);
+      gbase[p] = (uint32_t)(WIN ? m : row0 + m) * ldb + (uint32_t)(16 * q);
     }
     row = row0 + R * LP * w + l / KC::KCH - rows;
     pair = 2u * R * ldb;
@@ -229,7 +241,8 @@ struct LoaderKMajor {
   }
 };
 
-// Contraction index strided: the matrix is [K rows][MN cols].  Load p of
+// Contraction index strided: the matrix is [K rows][MN cols], reached
+// through a buffer based at each K step's first row.  Load p of
 // wave w fills tile k rows 2(LP w + p) and +1: lane l takes row +l/32 and the
 // MN chunk whose swizzled position is l%32.  The swizzle of row k depends on
 // k % 4 and bit 3 of k, so the chunk a lane fetches repeats with the load's
@@ -239,7 +252,7 @@ struct LoaderKMajor {
 // (one 64-column epilogue half) whose first half holds gate columns j and
 // second half the up columns F + j of the same j, so one lane ends up holding
 // a gate and its up value.
-template <class KC, int NT, bool GATED, int TN = 64>
+template <class KC, int NT, bool GATED, int TN, bool WIN>
 struct LoaderMNMajor {
   static constexpr int LP = KC::OPER_BYTES / 1024 / (NT / 64);
   static_assert(LP % 2 == 0 && (LP <= 4 || LP % 8 == 0), "swizzle period");
@@ -249,16 +262,19 @@ struct LoaderMNMajor {
   static __device__ __forceinline__ constexpr int phase(int p) { return (p & 1) | (NPH == 4 ? ((p >> 2) & 1) << 1 : 0); }
   // first load of phase ph
   static __device__ __forceinline__ constexpr int first(int ph) { return (ph & 1) | ((ph >> 1) << 2); }
-  __amdgpu_buffer_rsrc_t rs;
+  __amdgpu_buffer_rsrc_t rs;     // one buffer over the whole matrix (at most 2 GiB) ...
+  const char* base;              // ... or (WIN) the matrix, read through a buffer
+                                 // based at each K step's first row
   uint32_t gbase[NPH];  // the first load of each phase, at k0 = 0
   bool colok[NPH];
   int krow;             // the lane's k row in load 0, minus K
   uint32_t ldb;
   int ldsoff;
 
-  __device__ void init(const void* ptr, uint32_t bytes, int64_t ld, int col0, int cols, int K_,
+  __device__ void init(const void* ptr, uint64_t bytes, int64_t ld, int col0, int cols, int K_,
                        int t, int F, int tn) {
-    rs = make_rsrc(ptr, bytes);
+    if constexpr (WIN) base = (const char*)ptr;
+    else rs = make_rsrc(ptr, (uint32_t)bytes);
     ldb = (uint32_t)(ld * 2);
     const int w = t >> 6, l = t & 63;
 #pragma unroll
@@ -293,17 +309,31 @@ struct LoaderMNMajor {
           tile + ldsoff + p * 1024);
   }
   __device__ void issue(lds_char* tile, int k0) const {
+    if constexpr (WIN) {
+      // The window starts at the step's first row and spans the largest
+      // 32-bit range below OOB.  Every lane whose row or column lies outside
+      // the matrix is sent to OOB by its own check, so the window's end never
+      // has to match the matrix's: scalar arithmetic only, no branch.
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (uint64_t)(uint32_t)k0 * ldb, (uint32_t)kMaxWindow);
 #pragma unroll
-    for (int p = 0; p < LP; ++p) issue_one(tile, k0, p);
+      for (int p = 0; p < LP; ++p) {
+        const int ph = phase(p);
+        const bool ok = colok[ph] && (k0 + krow + 2 * p) < 0;
+        dma16(r, ok ? gbase[ph] + (uint32_t)(2 * (p - first(ph))) * ldb : OOB, tile + ldsoff + p * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < LP; ++p) issue_one(tile, k0, p);
+    }
   }
 };
 
-template <bool KMAJ, class KC, int NT, bool GATED, int TN>
+template <bool KMAJ, class KC, int NT, bool GATED, int TN, bool WIN>
 struct LoaderSel;
-template <class KC, int NT, bool GATED, int TN>
-struct LoaderSel<true, KC, NT, GATED, TN> { using type = LoaderKMajor<KC, NT, GATED>; };
-template <class KC, int NT, bool GATED, int TN>
-struct LoaderSel<false, KC, NT, GATED, TN> { using type = LoaderMNMajor<KC, NT, GATED, TN>; };
+template <class KC, int NT, bool GATED, int TN, bool WIN>
+struct LoaderSel<true, KC, NT, GATED, TN, WIN> { using type = LoaderKMajor<KC, NT, GATED, WIN>; };
+template <class KC, int NT, bool GATED, int TN, bool WIN>
+struct LoaderSel<false, KC, NT, GATED, TN, WIN> { using type = LoaderMNMajor<KC, NT, GATED, TN, WIN>; };
 
 // bf16 MFMA operand fragments: 8 k values of one row (or column) of a
 // 16- or 32-wide block per lane (see the readers below).
@@ -428,7 +458,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // ---------------------------------------------------------------------------
 enum Fmt : int { FMT_BF16 = 0, FMT_MX8 = 1 };
 
-template <int FMT, int WMv, int WNv, int BKv, int NSTv, bool AK, bool BKM, int EPI>
+template <int FMT, int WMv, int WNv, int BKv, int NSTv, bool AK, bool BKM, int EPI, bool WIN>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   using G = Grid<WMv, WNv>;
   using KC = KCfg<BKv, NSTv>;
@@ -453,12 +483,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int row0 = tm * BM, col0 = tn * BN;
 
-  typename LoaderSel<AK, KC, G::NT, false, TN>::type la;
-  typename LoaderSel<BKM, KC, G::NT, GATED, 64>::type lb;   // gate/up groups of one 64-column half
+  typename LoaderSel<AK, KC, G::NT, false, TN, WIN>::type la;
+  typename LoaderSel<BKM, KC, G::NT, GATED, 64, WIN>::type lb;   // gate/up groups of one 64-column half
   // MXFP8: the loaders count in 2-byte units (K / 2, ld / 2)
   constexpr int U = FMT == FMT_MX8 ? 2 : 1;
-  la.init(g.A, g.A_bytes, g.lda / U, row0, g.M, g.K / U, t, 0, tm);
-  lb.init(g.B, g.B_bytes, g.ldb / U, col0, g.N, g.K / U, t, g.F, tn);
+  la.init(g.A, WIN ? g.A_total : g.A_bytes, g.lda / U, row0, g.M, g.K / U, t, 0, tm);
+  lb.init(g.B, WIN ? g.B_total : g.B_bytes, g.ldb / U, col0, g.N, g.K / U, t, g.F, tn);
 
   // MFMA blocks: bf16 uses v_mfma_f32_16x16x32_bf16 (16x16 blocks, four
   // accumulators per lane), which draws less power per flop than the 32x32
@@ -1100,18 +1130,20 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   }
 }
 
-template <int WMv, int WNv, int BKv, int NSTv, bool AK, bool BKM, int EPI>
+// WIN: operands reached through windows (an operand past 2 GiB); else one
+// buffer descriptor per operand (the plain, slightly faster loaders).
+template <int WMv, int WNv, int BKv, int NSTv, bool AK, bool BKM, int EPI, bool WIN>
 __global__ void __launch_bounds__(64 * WMv * WNv)
     __attribute__((amdgpu_waves_per_eu(WMv * WNv / 4, WMv * WNv / 4)))
 gemm_bf16_kernel(GemmArgs g) {
-  gemm_body<FMT_BF16, WMv, WNv, BKv, NSTv, AK, BKM, EPI>(g);
+  gemm_body<FMT_BF16, WMv, WNv, BKv, NSTv, AK, BKM, EPI, WIN>(g);
 }
 
-template <int WMv, int WNv, int EPI>
+template <int WMv, int WNv, int EPI, bool WIN>
 __global__ void __launch_bounds__(64 * WMv * WNv)
     __attribute__((amdgpu_waves_per_eu(WMv * WNv / 4, WMv * WNv / 4)))
 gemm_mx8_kernel(GemmArgs g) {
-  gemm_body<FMT_MX8, WMv, WNv, 64, 2, true, true, EPI>(g);
+  gemm_body<FMT_MX8, WMv, WNv, 64, 2, true, true, EPI, WIN>(g);
 }
 
 // bf16 rows -> MXFP8 along the row.  A lane takes 8 consecutive elements
@@ -1330,6 +1362,9 @@ constexpr int kMxWavesM = kWavesM, kMxWavesN = kWavesN;
 #endif
 constexpr int64_t kDeepMinBytes = (int64_t)CODA_DEEP_MIN_MIB << 20;
 
+// an operand that one 32-bit buffer descriptor cannot cover
+static bool needs_windows(const GemmArgs& g) { return g.A_total > kMaxWindow || g.B_total > kMaxWindow; }
+
 template <bool AK, bool BKM, int EPI, bool DEEP = false>
 static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   static_assert(!DEEP || AK, "the deep ring is for a K-contiguous A operand");
@@ -1338,8 +1373,12 @@ static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (EPI == EPI_SWIGLU || EPI == EPI_RSQRT_SWIGLU) ? (g.N + BN / 2 - 1) / (BN / 2)
                                                                       : (g.N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<kWavesM, kWavesN, BKv, NSTv, AK, BKM, EPI>),
-                     dim3(tiles_m * tiles_n), dim3(64 * kWavesM * kWavesN), 0, s, g);
+  if (needs_windows(g))
+    hipLaunchKernelGGL((gemm_bf16_kernel<kWavesM, kWavesN, BKv, NSTv, AK, BKM, EPI, true>),
+                       dim3(tiles_m * tiles_n), dim3(64 * kWavesM * kWavesN), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<kWavesM, kWavesN, BKv, NSTv, AK, BKM, EPI, false>),
+                       dim3(tiles_m * tiles_n), dim3(64 * kWavesM * kWavesN), 0, s, g);
   return hipGetLastError();
 }
 
@@ -1396,8 +1435,12 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStr
 template <int EPI>
 static hipError_t launch_mx8_one(const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_mx8_kernel<kMxWavesM, kMxWavesN, EPI>), dim3(tiles),
-                     dim3(64 * kMxWavesM * kMxWavesN), 0, s, g);
+  if (needs_windows(g))
+    hipLaunchKernelGGL((gemm_mx8_kernel<kMxWavesM, kMxWavesN, EPI, true>), dim3(tiles),
+                       dim3(64 * kMxWavesM * kMxWavesN), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_mx8_kernel<kMxWavesM, kMxWavesN, EPI, false>), dim3(tiles),
+                       dim3(64 * kMxWavesM * kMxWavesN), 0, s, g);
   return hipGetLastError();
 }
 

@@ -54,7 +54,7 @@ struct GemmArgs {
   const int* labels; float* lab_out;   // EPI_CE_STATS
   const float* rope_tab; int rope_rot, rope_head, rope_seq;   // EPI_ROPE: tab = [cos | sin],
                                                                // each [rope_seq][rope_head / 2]
-  uint32_t A_bytes, B_bytes;     // buffer extents for hardware bounds checks
+  uint32_t A_bytes, B_bytes;     // operand extents when they fit one buffer (<= 2 GiB)
   // MXFP8 GEMMs (launch_gemm_mx8): A is [M][K] and B is given as B^T [N][K],
   // both E4M3 bytes with lda / ldb in bytes.  Their E8M0 scales are stored
   // step-blocked: [K/128][rows][4], the word of (step t, row r) holding the
@@ -64,6 +64,10 @@ struct GemmArgs {
   // EPI_RESID_SUMSQ in an MXFP8 GEMM: y * vcol quantised to MXFP8 along the
   // row, codes [M][ldq] and scales [ldq/128][M][4] (instead of C2)
   uint8_t* q_out; uint8_t* qs_out; int64_t ldq;
+  // full operand extents; past 2 GiB the loaders reach an operand through
+  // windows (a K-contiguous operand's 256 tile rows, an MN-contiguous
+  // operand's K step)
+  uint64_t A_total, B_total;
 };
 
 // Launchers: enqueue on `stream`, return the hipGetLastError() after launch.

@@ -90,6 +90,11 @@ WORKLOADS = {
                  seed=1006, backward=True,
                  note="LLaMA-7B-shaped LM head (vocabulary 32000) with cross-entropy, "
                       "forward+backward"),
+        Workload("llama3_8b_ce_fwdbwd", "ce", "bf16", M=16384, d=4096, N=128256,
+                 seed=1009, backward=True,
+                 note="LLaMA-3-8B-shaped LM head (vocabulary 128256) over two 8192-token "
+                      "sequences, with cross-entropy, forward+backward; logits and dlogits "
+                      "are 4.2 GB each"),
         Workload("llama7b_qkv_rope_fwdbwd", "rope", "bf16", M=8192, K=4096, N=12288,
                  rot=8192, head=128, seq=4096, base=10000.0, seed=1007, backward=True,
                  note="LLaMA-7B-shaped QKV projection with rotary positions on q and k "

@@ -128,9 +128,18 @@ def test_fwd_f32_multiple_of_four(L):
     assert call_fwd(L, a) == SHAPE                   # ... 30 is not a multiple of 4
 
 
-def test_too_large_tensor(L):
-    a = fwd_args(M=1 << 16, N=1 << 15)               # z would be 4 GiB of bf16
+def test_size_limits(L):
+    """Tensors past 2 GiB are accepted (the call here then stops at the
+    missing workspace, before any HIP call); row lengths past 2^21 and row
+    counts past 2^23 are refused."""
+    a = fwd_args(M=1 << 16, N=1 << 15)               # z is 4 GiB of bf16
+    assert call_fwd(L, a) == WORKSPACE
+    a = fwd_args(N=(1 << 21) + 8)                    # a row length past 2^21
     assert call_fwd(L, a) == SHAPE
+    a = fwd_args(M=(1 << 23) + 8)                    # a row count past 2^23
+    assert call_fwd(L, a) == SHAPE
+    a = fwd_args(M=1 << 23, K=8, d=8, N=8)           # at the row-count limit
+    assert call_fwd(L, a) == WORKSPACE
 
 
 def call_fwd_noalloc(L, a):

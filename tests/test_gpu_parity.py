@@ -623,6 +623,72 @@ def test_full_workload_ce(torch_dev):
         assert errs[k] <= BF16_TOL, (k, errs[k])
 
 
+class _SavedLogits:
+    """The saved logits bf16(h Wv) of the storage contract, formed on demand
+    for the row and column slices the sampled oracle asks for (the full
+    matrix would need 8 GB in float64)."""
+
+    def __init__(self, h, Wv):
+        self.h, self.Wv = h, Wv
+
+    def __getitem__(self, key):
+        if isinstance(key, tuple):
+            rows, cols = key
+            return oracle.bf16_rne(oracle.ref_ce_fwd(self.h[rows], self.Wv[:, cols],
+                                                     np.zeros(self.h[rows].shape[0], np.int64))["logits"])
+        return oracle.bf16_rne(oracle.ref_ce_fwd(self.h[key], self.Wv,
+                                                 np.zeros(len(key), np.int64))["logits"])
+
+
+# LLaMA-3-8B LM head (V = 128256) over 9224 tokens (ragged: 36 row tiles and 8
+# rows): logits and dlogits (2.37 GB each) exceed 2 GiB, so the dh and dWv
+# GEMMs reach them through buffer windows.
+LLAMA3_CE = synth.Workload("llama3_vocab_ragged_ce", "ce", "bf16", M=9224, d=4096, N=128256,
+                           seed=1015, backward=True)
+
+
+def test_full_workload_ce_llama3_vocab(torch_dev):
+    """lse and loss for every row (the oracle in row chunks); logits and dh
+    on stratified rows; dWv on stratified columns; two ignored rows."""
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    w = LLAMA3_CE
+    assert w.M * w.N * 2 > (2 << 30)
+    print("[parity] llama3_vocab_ragged_ce: generating inputs", flush=True)
+    h = synth.workload_inputs(w)
+    h["labels"][[5, 4100]] = -100                  # two ignored rows
+    th, tW = up(torch, dev, h["h"], "bf16"), up(torch, dev, h["Wv"], "bf16")
+    tl = torch.from_numpy(h["labels"]).to(dev)
+    td = torch.from_numpy(h["dloss"]).to(dev)
+    loss, lse, logits = coda.ce_fwd(th, tW, tl)
+    dh, dWv = coda.ce_bwd(th, tW, tl, logits, lse, td)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed)
+    rows = _rows(w.M, rng)
+    cols = _cols(w.N, rng, extra=h["labels"][rows[:4]][h["labels"][rows[:4]] >= 0])
+    logits_rows = host(logits[rows])
+    del logits
+    print("[parity] llama3_vocab_ragged_ce: oracle lse and loss (row chunks)", flush=True)
+    lse_ref = np.empty(w.M)
+    loss_ref = np.empty(w.M)
+    for r0 in range(0, w.M, 512):
+        ch = np.arange(r0, min(r0 + 512, w.M))
+        f = oracle.ref_ce_fwd_rows(h["h"], h["Wv"], h["labels"], ch)
+        lse_ref[ch], loss_ref[ch] = f["lse"], f["loss"]
+    fr = oracle.ref_ce_fwd_rows(h["h"], h["Wv"], h["labels"], rows)
+    errs = {"loss": rel(loss.cpu().numpy(), loss_ref), "lse": rel(lse.cpu().numpy(), lse_ref),
+            "logits_rows": rel(logits_rows, fr["logits"])}
+    print("[parity] llama3_vocab_ragged_ce: oracle backward (sampled)", flush=True)
+    bs = oracle.ref_ce_bwd_sampled(h["h"], h["Wv"], h["labels"], lse_ref, h["dloss"], rows, cols,
+                                   logits=_SavedLogits(h["h"], h["Wv"]))
+    errs.update({"dh_rows": rel(host(dh[rows]), bs["dh_rows"]), "dWv_cols": rel(host(dWv[:, cols]), bs["dWv_cols"])})
+    report("llama3_vocab_ragged_ce", errs)
+    assert float(loss[5]) == 0.0 and float(loss[4100]) == 0.0
+    assert errs["loss"] <= CE_TOL and errs["lse"] <= CE_TOL, errs
+    for k in ("logits_rows", "dh_rows", "dWv_cols"):
+        assert errs[k] <= BF16_TOL, (k, errs[k])
+
+
 # ------------------------------------------ QKV projection with rotary positions
 
 SMALL_ROPE = [
