@@ -33,7 +33,7 @@
  * that each row starts on a 16-byte boundary.  Sizes need not be multiples of
  * the kernels' tile sizes; edge tiles are masked.  The token count M may be up
  * to 2^23; every other size (K, d, N, F and 2F, V) up to 2^21; a tensor may be
- * larger than 2 GiB (e.g. LLaMA-3 logits, 8192 x 128256 bf16), up to 1 TiB.
+ * larger than 2 GiB (e.g. LLaMA-3 logits, 16384 x 128256 bf16), up to 1 TiB.
  * Larger sizes return CODA_ERR_SHAPE.
  *
  * Errors: every argument is checked before anything is enqueued; a failing
