@@ -69,6 +69,11 @@ What the pages fix, and the readings taken where they are silent:
     power-of-two scale per 32 along the contraction index), both GEMMs' operands
     in it; the second GEMM's operand is y diag(gamma) quantised by the first
     GEMM's epilogue, with r still applied after the second GEMM.
+  * An FP8 backward of the block (``ref_bwd_mx8``): the same format; the
+    gradient of the unquantised block (the forward's quantisation passes the
+    gradient straight through), each backward GEMM on MXFP8 operands quantised
+    along its own contraction index, the intermediates that feed a quantiser
+    (dn, n, dy) held in bf16 first, as the bf16 backward stores them.
 
 Every function here is pinned by a test against something other than itself
 (brute-force loops, finite differences, torch CPU autograd, closed forms and
@@ -87,7 +92,8 @@ __all__ = [
     "rope_angles", "ref_rope_rotate", "ref_rope_fwd", "ref_rope_bwd", "ref_rope_fwd_rows",
     "ref_rope_bwd_sampled",
     "E4M3_MAX", "MX_BLOCK", "e4m3_decode", "e4m3_encode", "e8m0_decode", "mx_quantize",
-    "mx_dequantize", "ref_fwd_mx8", "ref_fwd_mx8_rows",
+    "mx_dequantize", "ref_fwd_mx8", "ref_fwd_mx8_rows", "mx_matmul", "ref_bwd_mx8",
+    "ref_bwd_mx8_sampled",
 ]
 
 
@@ -779,6 +785,81 @@ def ref_fwd_mx8(Xq, Xs, W1q, W1s, R, gamma, W2q, W2s, eps: float) -> dict:
     q, s = mx_quantize(y * gamma[None, :])
     z = r[:, None] * (mx_dequantize(q, s) @ W2h.T)
     return {"y": y, "r": r, "yg_q": q, "yg_s": s, "yg": y * gamma[None, :], "z": z}
+
+
+def mx_matmul(A, B) -> np.ndarray:
+    """A B with both operands in MXFP8, quantised along the contraction index:
+    deq(mx_quantize(A)) deq(mx_quantize(B^T))^T, A [m, k], B [k, n],
+    k % 32 == 0 (each operand's 32-blocks run along k, as block-scaled
+    matrix units require)."""
+    Aq, As = mx_quantize(A)
+    Bq, Bs = mx_quantize(np.ascontiguousarray(_f64(B).T))
+    return mx_dequantize(Aq, As) @ mx_dequantize(Bq, Bs).T
+
+
+def ref_bwd_mx8(X, W1, gamma, W2, y, r, dz, store=bf16_rne) -> dict:
+    """Backward of the block with every GEMM on MXFP8 operands.
+
+    The pages argue that FP8 matrix units make the memory-bound work around a
+    GEMM relatively costlier ([JA] 課題; [RU] "Налог на лень"); they give no
+    FP8 training recipe.  Reading: the gradient is the calculus of the
+    unquantised block (``ref_bwd``: the forward's quantisation passes the
+    gradient straight through), and each of the four backward GEMMs runs on
+    MXFP8 operands quantised along its own contraction index (``mx_matmul``):
+      dh  = mx(dz, W2^T)                 (contraction over N)
+      dgamma_j = sum_i dh_ij r_i y_ij;  dn = dh diag(gamma);
+      s_i = sum_j dn_ij y_ij;  c_i = r_i^3 s_i / d;
+      dy  = diag(r) store(dn) - diag(c) y;  dR = store(dy)
+      dW2 = diag(gamma) mx(store(n)^T, dz),  n = diag(r) y   (contraction over M)
+      dX  = mx(store(dy), W1^T)          (contraction over d)
+      dW1 = mx(X^T, store(dy))           (contraction over M)
+    ``store`` is the storage contract of the intermediates that feed a
+    quantiser (dn, n and dy are kept in bf16): bf16_rne by default; pass the
+    identity for unrounded intermediates.  y and r are the saved forward
+    tensors; X, W1, W2 the unquantised (bf16) inputs.
+    """
+    X, W1, gamma, W2, y, r, dz = map(_f64, (X, W1, gamma, W2, y, r, dz))
+    d = y.shape[1]
+    dh = mx_matmul(dz, W2.T)
+    n = y * r[:, None]
+    dgamma = np.sum(dh * n, axis=0)
+    dn = dh * gamma[None, :]
+    s = np.sum(dn * y, axis=1)
+    c = r ** 3 * s / d
+    dy = r[:, None] * store(dn) - c[:, None] * y
+    dy_s = store(dy)
+    dW2 = gamma[:, None] * mx_matmul(store(n).T, dz)
+    dX = mx_matmul(dy_s, W1.T)
+    dW1 = mx_matmul(X.T, dy_s)
+    return {"dX": dX, "dW1": dW1, "dR": dy, "dW2": dW2, "dgamma": dgamma,
+            "dh": dh, "dn": dn, "n": n, "s": s, "c": c, "dy": dy}
+
+
+def ref_bwd_mx8_sampled(X, W1, gamma, W2, y, r, dz, rows, cols_d, cols_N, store=bf16_rne) -> dict:
+    """``ref_bwd_mx8`` with dX and dR restricted to ``rows``, dW1 to the columns
+    ``cols_d`` and dW2 to the columns ``cols_N``; dgamma, s and c in full.
+
+    A quantisation block runs along its GEMM's contraction index, so a row of
+    dX needs only that row of dy (blocks along d) and the whole of W1; a
+    column of dW1 needs that column of dy over every row (blocks along M);
+    a column of dW2 that column of dz over every row.  dh is formed whole.
+    """
+    X, W1, gamma, W2, y, r, dz = map(_f64, (X, W1, gamma, W2, y, r, dz))
+    d = y.shape[1]
+    rows, cols_d, cols_N = map(np.asarray, (rows, cols_d, cols_N))
+    dh = mx_matmul(dz, W2.T)
+    n = y * r[:, None]
+    dgamma = np.sum(dh * n, axis=0)
+    dn = dh * gamma[None, :]
+    s = np.sum(dn * y, axis=1)
+    c = r ** 3 * s / d
+    dy_s = store(r[:, None] * store(dn) - c[:, None] * y)
+    dX_rows = mx_matmul(dy_s[rows], W1.T)
+    dW1_cols = mx_matmul(X.T, dy_s[:, cols_d])
+    dW2_cols = gamma[:, None] * mx_matmul(store(n).T, dz[:, cols_N])
+    dR_rows = r[rows, None] * store(dn[rows]) - c[rows, None] * y[rows]
+    return {"rows": rows, "cols_d": cols_d, "cols_N": cols_N, "dX_rows": dX_rows, "dR_rows": dR_rows,
+            "dW1_cols": dW1_cols, "dW2_cols": dW2_cols, "dgamma": dgamma, "s": s, "c": c}
 
 
 def ref_fwd_mx8_rows(Xq, Xs, W1q, W1s, R, gamma, W2q, W2s, eps: float, rows) -> dict:

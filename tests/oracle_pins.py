@@ -1072,6 +1072,142 @@ def pin_fwd_mx8_rows(O):
         assert np.array_equal(part[k], full[k][rows]), f"mx8 rows {k}"
 
 
+def _bf16_loop(x):
+    """Nearest bfloat16 value of a float (8 significant bits, ties to even), by
+    frexp and Python's round (banker's rounding) - no numpy, no oracle code."""
+    if x == 0.0 or not math.isfinite(x):
+        return x
+    m, e = math.frexp(x)                      # x = m 2**e, 0.5 <= |m| < 1
+    e = max(e, -125)                          # below 2**-126 the spacing stays 2**-133
+    return math.ldexp(round(math.ldexp(x, 8 - e)), e - 8)
+
+
+def _mx_block_loop(vals, tab):
+    """MXFP8 of one 32-block by loops: scale exponent from the block max,
+    nearest code per element; returns the dequantised values."""
+    e = _shared_exp_loop(max(abs(v) for v in vals))
+    return [tab[_e4m3_nearest(v / 2.0 ** e, tab)] * 2.0 ** e for v in vals]
+
+
+def _mx_matmul_loop(A, B, tab):
+    """A [m][k] B [k][n] with A's rows and B's columns quantised in 32-blocks
+    along k, by loops."""
+    m, k, n = len(A), len(A[0]), len(B[0])
+    Aq = [sum((_mx_block_loop(A[i][b:b + 32], tab) for b in range(0, k, 32)), []) for i in range(m)]
+    Bq = [sum((_mx_block_loop([B[kk][j] for kk in range(b, b + 32)], tab) for b in range(0, k, 32)), [])
+          for j in range(n)]
+    return [[sum(Aq[i][kk] * Bq[j][kk] for kk in range(k)) for j in range(n)] for i in range(m)]
+
+
+def _mx_grid(g, shape):
+    """Values exactly representable in MXFP8 along the last axis: per 32-block
+    a power of two 2**e and E4M3 values v (|v| <= 448) with the block's largest
+    |v| in [256, 448], so that the block maximum gives back exponent e."""
+    tab = _e4m3_table()
+    vals = np.array(sorted(v for v in tab.values()))
+    top = vals[(np.abs(vals) >= 256.0)]
+    nb = shape[-1] // 32
+    out = g.choice(vals[np.abs(vals) < 256.0], size=shape[:-1] + (nb, 32))
+    lead = g.integers(0, 32, size=shape[:-1] + (nb,))
+    np.put_along_axis(out, lead[..., None], g.choice(top, size=shape[:-1] + (nb, 1)), axis=-1)
+    blk = 2.0 ** g.integers(-14, -6, size=shape[:-1] + (nb, 1))
+    return (out * blk).reshape(shape)
+
+
+def pin_mx_matmul(O):
+    """The MXFP8 product against loops (each operand quantised along the
+    contraction index from the format's bit fields); grid-exact operands give
+    the exact product; the product of the transposes is the transpose."""
+    tab = _e4m3_table()
+    g = _rng(90)
+    A = g.standard_normal((3, 64)) * 3.0
+    B = g.standard_normal((64, 2)) * 0.2
+    A[1, 40] = 0.0
+    got = O.mx_matmul(A, B)
+    want = np.array(_mx_matmul_loop(A.tolist(), B.tolist(), tab))
+    _close(got, want, 1e-12, "mx_matmul vs loops")
+    Ag, Bg = _mx_grid(g, (5, 96)), _mx_grid(g, (7, 96)).T
+    _close(O.mx_matmul(Ag, Bg), Ag @ Bg, 1e-13, "mx_matmul of grid-exact operands")
+    C = g.standard_normal((64, 4))
+    assert np.array_equal(O.mx_matmul(A, C), O.mx_matmul(C.T, A.T).T), "mx_matmul transposition"
+
+
+def _bwd_mx8_case(seed, M, K, d, N):
+    g = _rng(seed)
+    return dict(X=g.standard_normal((M, K)), W1=g.standard_normal((K, d)) / math.sqrt(K),
+                gamma=1 + 0.1 * g.standard_normal(d), W2=g.standard_normal((d, N)) / math.sqrt(d),
+                y=g.standard_normal((M, d)) * 1.5, dz=g.standard_normal((M, N)))
+
+
+def pin_bwd_mx8_bruteforce(O):
+    """The MXFP8 backward by pure-Python loops on a tiny case (every dimension
+    two 32-blocks): each GEMM's operands quantised along its contraction
+    index, dn, n and dy rounded to bf16 before they are quantised."""
+    tab = _e4m3_table()
+    M = K = d = N = 64
+    c = _bwd_mx8_case(91, M, K, d, N)
+    y = c["y"]
+    r = 1.0 / np.sqrt(np.mean(y * y, axis=1) + 1e-6)
+    out = O.ref_bwd_mx8(c["X"], c["W1"], c["gamma"], c["W2"], y, r, c["dz"])
+    Ly, Lr, Lg = y.tolist(), r.tolist(), c["gamma"].tolist()
+    W2T = c["W2"].T.tolist()                       # [N][d]: the product dz W2^T
+    dh = _mx_matmul_loop(c["dz"].tolist(), W2T, tab)
+    dgam = [sum(dh[i][j] * Lr[i] * Ly[i][j] for i in range(M)) for j in range(d)]
+    dn = [[dh[i][j] * Lg[j] for j in range(d)] for i in range(M)]
+    s_ = [sum(dn[i][j] * Ly[i][j] for j in range(d)) for i in range(M)]
+    cc = [Lr[i] ** 3 * s_[i] / d for i in range(M)]
+    dy = [[_bf16_loop(Lr[i] * _bf16_loop(dn[i][j]) - cc[i] * Ly[i][j]) for j in range(d)] for i in range(M)]
+    nT = [[_bf16_loop(Lr[i] * Ly[i][j]) for i in range(M)] for j in range(d)]
+    dW2 = _mx_matmul_loop(nT, c["dz"].tolist(), tab)
+    dW2 = [[dW2[j][k] * Lg[j] for k in range(N)] for j in range(d)]
+    dX = _mx_matmul_loop(dy, c["W1"].T.tolist(), tab)
+    XT = c["X"].T.tolist()
+    dW1 = _mx_matmul_loop(XT, dy, tab)
+    _close(out["dh"], np.array(dh), 1e-12, "mx8 bwd dh")
+    _close(out["dgamma"], np.array(dgam), 1e-12, "mx8 bwd dgamma")
+    _close(out["c"], np.array(cc), 1e-12, "mx8 bwd c")
+    _close(O.bf16_rne(out["dy"]), np.array(dy), 1e-12, "mx8 bwd dy (stored)")
+    _close(out["dW2"], np.array(dW2), 1e-12, "mx8 bwd dW2")
+    _close(out["dX"], np.array(dX), 1e-12, "mx8 bwd dX")
+    _close(out["dW1"], np.array(dW1), 1e-12, "mx8 bwd dW1")
+
+
+def pin_bwd_mx8_grid_exact(O):
+    """With dz and W2 on the MXFP8 grid the dh product is exact, so dh,
+    dgamma, s and c equal those of the unquantised backward (ref_bwd, pinned by
+    finite differences and torch autograd); with every quantised operand on
+    the grid and the identity as storage, dX, dW1 and dW2 equal ref_bwd's
+    products of the same operands."""
+    g = _rng(92)
+    M, K, d, N = 64, 32, 64, 96
+    c = _bwd_mx8_case(93, M, K, d, N)
+    dz = _mx_grid(g, (M, N))
+    W2 = _mx_grid(g, (d, N))
+    y = c["y"]
+    r = 1.0 / np.sqrt(np.mean(y * y, axis=1) + 1e-6)
+    q = O.ref_bwd_mx8(c["X"], c["W1"], c["gamma"], W2, y, r, dz, store=lambda v: v)
+    e = O.ref_bwd(c["X"], c["W1"], c["gamma"], W2, y, r, dz)
+    for k in ("dh", "dgamma", "s", "c"):
+        _close(q[k], e[k], 1e-12, f"mx8 bwd {k} on grid operands")
+    _close(q["dR"], e["dR"], 1e-12, "mx8 bwd dR (identity storage)")
+
+
+def pin_bwd_mx8_sampled(O):
+    """The sampled form equals slices of the full MXFP8 backward."""
+    M, K, d, N = 96, 64, 64, 128
+    c = _bwd_mx8_case(94, M, K, d, N)
+    y = O.bf16_rne(c["y"])
+    r = 1.0 / np.sqrt(np.mean(y * y, axis=1) + 1e-6)
+    full = O.ref_bwd_mx8(c["X"], c["W1"], c["gamma"], c["W2"], y, r, c["dz"])
+    rows, cd, cn = np.array([0, 17, 95]), np.array([1, 63]), np.array([0, 5, 127])
+    sm = O.ref_bwd_mx8_sampled(c["X"], c["W1"], c["gamma"], c["W2"], y, r, c["dz"], rows, cd, cn)
+    _close(sm["dX_rows"], full["dX"][rows], 1e-12, "mx8 sampled dX rows")
+    _close(sm["dR_rows"], full["dR"][rows], 1e-12, "mx8 sampled dR rows")
+    _close(sm["dW1_cols"], full["dW1"][:, cd], 1e-12, "mx8 sampled dW1 cols")
+    _close(sm["dW2_cols"], full["dW2"][:, cn], 1e-12, "mx8 sampled dW2 cols")
+    _close(sm["dgamma"], full["dgamma"], 1e-12, "mx8 sampled dgamma")
+
+
 ALL_PINS = [
     pin_fwd_bruteforce, pin_fwd_torch_rmsnorm, pin_fwd_constant_rows,
     pin_fwd_scale_invariance, pin_partials, pin_rewrite_equals_unfused,
@@ -1085,5 +1221,6 @@ ALL_PINS = [
     pin_rope_bruteforce, pin_rope_torch, pin_rope_finite_differences, pin_rope_properties,
     pin_rope_sampled,
     pin_bwd_dy_in_finite_differences, pin_e4m3_codes, pin_mx_quantize, pin_fwd_mx8_exact,
-    pin_fwd_mx8_bruteforce, pin_fwd_mx8_rows,
+    pin_fwd_mx8_bruteforce, pin_fwd_mx8_rows, pin_mx_matmul, pin_bwd_mx8_bruteforce,
+    pin_bwd_mx8_grid_exact, pin_bwd_mx8_sampled,
 ]

@@ -202,6 +202,32 @@ def ce_bwd_ignored_keep_softmax(h, Wv, labels, lse, dloss, logits=None):
     return out
 
 
+def mx_matmul_B_along_n(A, B):
+    """B quantised along its rows (the output index) instead of the contraction index."""
+    Aq, As = oracle.mx_quantize(A)
+    Bq, Bs = oracle.mx_quantize(np.asarray(B, dtype=np.float64))
+    return oracle.mx_dequantize(Aq, As) @ oracle.mx_dequantize(Bq, Bs)
+
+
+def _bwd_mx8_variant(kind):
+    def bwd(X, W1, gamma, W2, y, r, dz, store=oracle.bf16_rne):
+        out = dict(oracle.ref_bwd_mx8(X, W1, gamma, W2, y, r, dz, store))
+        X64, W1_64, g64 = _f(X, W1, gamma)
+        if kind == "dW2_no_gamma":
+            out["dW2"] = out["dW2"] / g64[:, None]
+        elif kind == "dX_W1_along_K":
+            dyq, dys = oracle.mx_quantize(store(out["dy"]))
+            wtq, wts = oracle.mx_quantize(np.ascontiguousarray(W1_64.T))   # blocks along K, not d
+            out["dX"] = oracle.mx_dequantize(dyq, dys) @ oracle.mx_dequantize(wtq, wts)
+        elif kind == "dy_not_stored":
+            out["dX"] = oracle.mx_matmul(out["dy"], W1_64.T)
+            out["dW1"] = oracle.mx_matmul(X64.T, out["dy"])
+        elif kind == "dgamma_from_stored_n":
+            out["dgamma"] = np.sum(out["dh"] * store(out["n"]), axis=0)
+        return out
+    return bwd
+
+
 def ce_partials_no_rescale(logits, BN=256):
     out = dict(oracle.ref_ce_partials(logits, BN))
     x = np.asarray(logits, dtype=np.float64)
@@ -392,6 +418,11 @@ MUTANTS = {
     "mx_shared_exp_emax_7": _mx_mutant("emax_7"),
     "mx_r_before_quantisation": _mx_mutant("r_before_quantisation"),
     "e4m3_decode_bias_8": {"e4m3_decode": e4m3_decode_bias_8},
+    "mx_matmul_B_along_output_index": {"mx_matmul": mx_matmul_B_along_n},
+    "mx8_bwd_dW2_without_gamma": {"ref_bwd_mx8": _bwd_mx8_variant("dW2_no_gamma")},
+    "mx8_bwd_dX_W1_quantised_along_K": {"ref_bwd_mx8": _bwd_mx8_variant("dX_W1_along_K")},
+    "mx8_bwd_dy_quantised_unstored": {"ref_bwd_mx8": _bwd_mx8_variant("dy_not_stored")},
+    "mx8_bwd_dgamma_from_stored_n": {"ref_bwd_mx8": _bwd_mx8_variant("dgamma_from_stored_n")},
     "e8m0_off_by_one": {"e8m0_decode": e8m0_off_by_one},
 }
 
