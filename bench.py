@@ -294,8 +294,11 @@ class RopeCase:
 
 
 class Mx8Case:
-    """The block forward on MXFP8 operands.  The bf16 draws are quantised once
-    (the library's quantiser) before timing; weights are stored [out, in]."""
+    """The block forward on MXFP8 operands, and (for a workload with a
+    backward) the MXFP8 backward.  The forward's bf16 draws are quantised once
+    (the library's quantiser) before timing; weights are stored [out, in].
+    The backward takes the bf16 tensors, as a training step keeps them, and
+    quantises them itself inside the timed step."""
 
     def __init__(self, w, torch, coda, h):
         dev = torch.device("cuda:0")
@@ -312,17 +315,51 @@ class Mx8Case:
         self.r = torch.empty((M,), dtype=torch.float32, device=dev)
         self.z = torch.empty((M, N), dtype=bf, device=dev)
         self.ws = torch.empty(coda.fwd_mx8_workspace_bytes(M, K, d, N), dtype=torch.uint8, device=dev)
-        self.backward = False
+        self.backward = w.backward
         self.kernels_per_step = 2
         self.leaf_names = ("R",)
+        if self.backward:
+            self.dX = torch.empty((M, K), dtype=bf, device=dev)
+            self.dW1 = torch.empty((K, d), dtype=bf, device=dev)
+            self.dR = torch.empty((M, d), dtype=bf, device=dev)
+            self.dW2 = torch.empty((d, N), dtype=bf, device=dev)
+            self.dg = torch.empty((d,), dtype=torch.float32, device=dev)
+            self.wsb = torch.empty(coda.bwd_mx8_workspace_bytes(M, K, d, N), dtype=torch.uint8, device=dev)
+            self.kernels_per_step = 2 + 14
+            self.manual_bwd = True
 
     def flops(self):
-        return self.w.flops_fwd()
+        return self.w.flops_fwd() + (self.w.flops_bwd() if self.backward else 0.0)
 
     def fused_fwd(self):
         q, t = self.q, self.t
         self.coda.coda_fwd_mx8(q["X"][0], q["X"][1], q["W1t"][0], q["W1t"][1], t["R"], t["gamma"],
                                q["W2t"][0], q["W2t"][1], self.w.eps, self.y, self.r, self.z, self.ws)
+
+    def fused_bwd(self):
+        t = self.t
+        self.coda.coda_bwd_mx8(t["X"], t["W1"], t["gamma"], t["W2"], self.y, self.r, t["dz"], self.dX, self.dW1,
+                               self.dR, self.dW2, self.dg, self.wsb)
+
+    def unfused_bwd_manual(self):
+        """The same backward as separate torch ops: torch-side MXFP8
+        quantisation along each GEMM's contraction index, hipBLASLt's MXFP8
+        product, the RMS-norm backward elementwise."""
+        torch, t, w = self.torch, self.t, self.w
+        c = lambda v: v.contiguous()  # noqa: E731
+        dh = self._mm(self._quantise(t["dz"]), self._quantise(t["W2"]))
+        y, r = self.y.float(), self.r
+        n = (y * r[:, None])
+        dgamma = (dh.float() * n).sum(0)
+        dn = (dh.float() * t["gamma"].float()).to(torch.bfloat16)
+        s_ = (dn.float() * y).sum(1)
+        cc = r ** 3 * s_ / w.d
+        dy = (r[:, None] * dn.float() - cc[:, None] * y).to(torch.bfloat16)
+        dW2 = self._mm(self._quantise(c(n.to(torch.bfloat16).t())), self._quantise(c(t["dz"].t())))
+        dW2 = (dW2.float() * t["gamma"].float()[:, None]).to(torch.bfloat16)
+        dX = self._mm(self._quantise(dy), self._quantise(t["W1"]))
+        dW1 = self._mm(self._quantise(c(t["X"].t())), self._quantise(c(dy.t())))
+        return dX, dW1, dy, dW2, dgamma
 
     def _mm(self, a, b):
         """torch's MXFP8 product (hipBLASLt): a [m, k] codes and row-major scales, b [n, k]."""
@@ -378,13 +415,13 @@ class _Steps:
 
     @staticmethod
     def unfused_setup(case):
-        grad = case.backward
+        grad = case.backward and not getattr(case, "manual_bwd", False)
         case.leaf = {k: case.t[k].detach().clone().requires_grad_(grad) for k in case.leaf_names}
         case.graph = case.unfused_fwd() if grad else None
 
     @staticmethod
     def unfused_fwd(case):
-        if case.backward:
+        if case.backward and not getattr(case, "manual_bwd", False):
             case.unfused_fwd()
         else:
             with case.torch.no_grad():
@@ -397,11 +434,18 @@ class _Steps:
 
     @staticmethod
     def unfused_bwd(case):
+        if getattr(case, "manual_bwd", False):
+            with case.torch.no_grad():
+                case.unfused_bwd_manual()
+            return
         _Steps._grad(case, case.graph, True)
 
     @staticmethod
     def unfused_step(case):
-        if case.backward:
+        if getattr(case, "manual_bwd", False):
+            _Steps.unfused_fwd(case)
+            _Steps.unfused_bwd(case)
+        elif case.backward:
             _Steps._grad(case, case.unfused_fwd(), False)
         else:
             _Steps.unfused_fwd(case)
@@ -768,7 +812,7 @@ def cpu_baseline(w, h, target_s):
 # the headline metric; the rest are the other fused patterns.
 HEADLINE_SECOND = "llama70b_fwdbwd"
 ALSO = ("swiglu_fwdbwd", "llama7b_mlp_fwdbwd", "llama7b_ce_fwdbwd", "llama3_8b_ce_fwdbwd",
-        "llama7b_qkv_rope_fwdbwd", "llama7b_fwd_mx8", "llama1b_fwd")
+        "llama7b_qkv_rope_fwdbwd", "llama7b_fwd_mx8", "llama7b_fwdbwd_mx8", "llama1b_fwd")
 
 
 def _brief(s):

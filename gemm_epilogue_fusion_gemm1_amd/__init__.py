@@ -23,6 +23,7 @@ Convenience calls (allocate outputs):
     ce_bwd(h, Wv, labels, logits, lse, dloss) -> (dh, dWv)
     rope_fwd(X, W, N_rot, D, S, base)    -> Y
     rope_bwd(X, W, dY, N_rot, D, S, base) -> (dX, dW)
+    bwd_mx8(X, W1, gamma, W2, y, r, dz)  -> (dX, dW1, dR, dW2, dgamma), MXFP8 GEMMs
 """
 from __future__ import annotations
 
@@ -37,6 +38,7 @@ __all__ = [
     "rope_bwd", "rope_fwd_workspace_bytes", "rope_bwd_workspace_bytes", "fwd_workspace_bytes", "bwd_workspace_bytes",
     "swiglu_bwd_workspace_bytes", "mlp_fwd_workspace_bytes", "mlp_bwd_workspace_bytes",
     "coda_mx8_quantize", "coda_fwd_mx8", "mx8_quantize", "fwd_mx8", "fwd_mx8_workspace_bytes",
+    "coda_bwd_mx8", "bwd_mx8", "bwd_mx8_workspace_bytes",
     "mx8_scales_to_rowmajor", "mx8_scales_from_rowmajor",
     "version", "trace_start", "trace_read", "trace_stop",
 ]
@@ -90,6 +92,7 @@ def load_library() -> ctypes.CDLL:
         "coda_rope_fwd_workspace_bytes": [i32, i64, i64, i64, i64, i64, i64],
         "coda_rope_bwd_workspace_bytes": [i32, i64, i64, i64, i64, i64, i64],
         "coda_fwd_mx8_workspace_bytes": [i64, i64, i64, i64],
+        "coda_bwd_mx8_workspace_bytes": [i64, i64, i64, i64],
     }.items():
         getattr(L, name).restype = sz
         getattr(L, name).argtypes = args
@@ -117,6 +120,8 @@ def load_library() -> ctypes.CDLL:
     L.coda_rope_bwd.argtypes = [i32, i64, i64, i64, i64, i64, i64, f32] + [vp] * 5 + [vp, sz, vp]
     L.coda_mx8_quantize.restype = i32
     L.coda_mx8_quantize.argtypes = [i64, i64, vp, i64, vp, vp, vp]
+    L.coda_bwd_mx8.restype = i32
+    L.coda_bwd_mx8.argtypes = [i64, i64, i64, i64] + [vp] * 12 + [vp, sz, vp]
     L.coda_fwd_mx8.restype = i32
     L.coda_fwd_mx8.argtypes = [i64, i64, i64, i64, f32] + [vp] * 11 + [vp, sz, vp]
     L.coda_trace_start.restype = i32
@@ -480,6 +485,22 @@ def coda_fwd_mx8(Xq, Xs, W1tq, W1ts, R, gamma, W2tq, W2ts, eps, y, r, z, workspa
     _check("coda_fwd_mx8", load_library().coda_fwd_mx8(M, K, d, N, float(eps), *p, wp, wn, _stream()))
 
 
+def coda_bwd_mx8(X, W1, gamma, W2, y, r, dz, dX, dW1, dR, dW2, dgamma, workspace):
+    """coda_bwd_mx8: the block backward on MXFP8 GEMM operands (bf16 tensors in
+    and out, as coda_bwd)."""
+    import torch
+    a = _Args("coda_bwd_mx8", X, "X")
+    bf = torch.bfloat16
+    M, K = X.shape
+    d, N = W1.shape[1], W2.shape[1]
+    p = [a(X, "X", (M, K), bf), a(W1, "W1", (K, d), bf), a(gamma, "gamma", (d,), bf), a(W2, "W2", (d, N), bf),
+         a(y, "y", (M, d), bf), a(r, "r", (M,), torch.float32), a(dz, "dz", (M, N), bf),
+         a(dX, "dX", (M, K), bf), a(dW1, "dW1", (K, d), bf), a(dR, "dR", (M, d), bf),
+         a(dW2, "dW2", (d, N), bf), a(dgamma, "dgamma", (d,), torch.float32)]
+    wp, wn = a.ws(workspace)
+    _check("coda_bwd_mx8", load_library().coda_bwd_mx8(M, K, d, N, *p, wp, wn, _stream()))
+
+
 # ------------------------------------------------------ convenience calls
 
 def mx8_scales_to_rowmajor(scales):
@@ -522,6 +543,26 @@ def fwd_mx8(Xq, Xs, W1tq, W1ts, R, gamma, W2tq, W2ts, eps):
     ws = _workspace(fwd_mx8_workspace_bytes(M, K, d, N), R.device)
     coda_fwd_mx8(Xq, Xs, W1tq, W1ts, R, gamma, W2tq, W2ts, eps, y, r, z, ws)
     return z, y, r
+
+
+def bwd_mx8_workspace_bytes(M, K, d, N) -> int:
+    return int(load_library().coda_bwd_mx8_workspace_bytes(M, K, d, N))
+
+
+def bwd_mx8(X, W1, gamma, W2, y, r, dz):
+    """The block backward with every GEMM on MXFP8 operands (bf16 in and out).
+    Returns (dX, dW1, dR, dW2, dgamma)."""
+    import torch
+    M, K = X.shape
+    d, N = W1.shape[1], W2.shape[1]
+    dX = torch.empty_like(X)
+    dW1 = torch.empty_like(W1)
+    dR = torch.empty((M, d), dtype=X.dtype, device=X.device)
+    dW2 = torch.empty_like(W2)
+    dgamma = torch.empty((d,), dtype=torch.float32, device=X.device)
+    ws = _workspace(bwd_mx8_workspace_bytes(M, K, d, N), X.device)
+    coda_bwd_mx8(X, W1, gamma, W2, y, r, dz, dX, dW1, dR, dW2, dgamma, ws)
+    return dX, dW1, dR, dW2, dgamma
 
 
 def fwd(X, W1, R, gamma, W2, eps):

@@ -1069,4 +1069,139 @@ coda_status coda_fwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, float eps, 
   }));
 }
 
+// ------------------------------------------------------ MXFP8 backward
+
+}  // extern "C"
+
+namespace {
+// Workspace of coda_bwd_mx8: every GEMM operand in MXFP8 (codes, then
+// step-blocked scales), plus n (bf16) and the partial sums of the bf16
+// backward.
+struct BwdMx8Ws {
+  size_t dzq, dzs, w2q, w2s, n, S, G, c, nTq, nTs, dzTq, dzTs, dyq, dys, w1q, w1s, XTq, XTs, dyTq, dyTs, total;
+  int Tn, Tm;
+};
+BwdMx8Ws bwd_mx8_ws(int64_t M, int64_t K, int64_t d, int64_t N) {
+  BwdMx8Ws w;
+  w.Tn = (int)cdiv(d, coda::kTileN);
+  w.Tm = (int)cdiv(M, coda::kTileM);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += round_up(bytes); return at; };
+  w.dzq = take((size_t)M * N);       w.dzs = take((size_t)M * (N / 32));
+  w.w2q = take((size_t)d * N);       w.w2s = take((size_t)d * (N / 32));
+  w.n = take((size_t)M * d * 2);
+  w.S = take((size_t)M * w.Tn * 4);  w.G = take((size_t)w.Tm * d * 4);  w.c = take((size_t)M * 4);
+  w.nTq = take((size_t)d * M);       w.nTs = take((size_t)d * (M / 32));
+  w.dzTq = take((size_t)N * M);      w.dzTs = take((size_t)N * (M / 32));
+  w.dyq = take((size_t)M * d);       w.dys = take((size_t)M * (d / 32));
+  w.w1q = take((size_t)K * d);       w.w1s = take((size_t)K * (d / 32));
+  w.XTq = take((size_t)K * M);       w.XTs = take((size_t)K * (M / 32));
+  w.dyTq = take((size_t)d * M);      w.dyTs = take((size_t)d * (M / 32));
+  w.total = o;
+  return w;
+}
+}  // namespace
+
+extern "C" {
+
+size_t coda_bwd_mx8_workspace_bytes(int64_t M, int64_t K, int64_t d, int64_t N) {
+  if (M < 128 || K < 8 || d < 128 || N < 128 || M % 128 || d % 128 || N % 128) return 0;
+  return bwd_mx8_ws(M, K, d, N).total;
+}
+
+coda_status coda_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, const void* X, const void* W1,
+                         const void* gamma, const void* W2, const void* y, const float* r,
+                         const void* dz, void* dX, void* dW1, void* dR, void* dW2, float* dgamma,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!X || !W1 || !gamma || !W2 || !y || !r || !dz || !dX || !dW1 || !dR || !dW2 || !dgamma)
+    return CODA_ERR_NULL;
+  // the contraction dimensions of the four GEMMs (N, M, d) are whole K steps
+  if (!mx_rows_ok(M, 128) || !mx_dim_ok(K, 8) || !mx_dim_ok(d, 128) || !mx_dim_ok(N, 128))
+    return CODA_ERR_SHAPE;
+  if (!fits(M, K, 2) || !fits(K, d, 2) || !fits(M, d, 2) || !fits(d, N, 2) || !fits(M, N, 2) ||
+      !scales_fit(M, N) || !scales_fit(d, N) || !scales_fit(N, M) || !scales_fit(d, M) ||
+      !scales_fit(M, d) || !scales_fit(K, d) || !scales_fit(K, M))
+    return CODA_ERR_SHAPE;
+  for (const void* p : {X, W1, gamma, W2, y, (const void*)r, dz, (const void*)dX, (const void*)dW1,
+                        (const void*)dR, (const void*)dW2, (const void*)dgamma})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  const BwdMx8Ws ws = bwd_mx8_ws(M, K, d, N);
+  if (!workspace || workspace_bytes < ws.total) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const size_t e = 2;
+  const Range in[] = {rng(X, M * K * e), rng(W1, K * d * e), rng(gamma, d * e), rng(W2, d * N * e),
+                      rng(y, M * d * e), rng(r, M * 4), rng(dz, M * N * e)};
+  const Range out[] = {rng(dX, M * K * e), rng(dW1, K * d * e), rng(dR, M * d * e),
+                       rng(dW2, d * N * e), rng(dgamma, d * 4), rng(workspace, ws.total)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wb = (char*)workspace;
+  auto u8 = [&](size_t off) { return (uint8_t*)(wb + off); };
+  float* S = (float*)(wb + ws.S);
+  float* G = (float*)(wb + ws.G);
+  float* c = (float*)(wb + ws.c);
+  void* n = wb + ws.n;
+  hipError_t err;
+  const double md = (double)M * d, mn = (double)M * N, dn2 = (double)d * N, mk = (double)M * K, kd = (double)K * d;
+  auto quant = [&](const char* name, const void* src, int64_t rows, int64_t cols, uint8_t* q, uint8_t* qs) {
+    return traced(name, 0.0, rows * cols * (3.0 + 1.0 / 32.0), s, [&] {
+      return coda::launch_mx8_quantize(src, cols, rows, cols, q, qs, s);
+    });
+  };
+  auto quant_t = [&](const char* name, const void* src, int64_t rows, int64_t cols, uint8_t* q, uint8_t* qs) {
+    return traced(name, 0.0, rows * cols * (3.0 + 1.0 / 32.0), s, [&] {
+      return coda::launch_mx8_quantize_t(src, cols, rows, cols, q, qs, s);
+    });
+  };
+  // dz and W2 along N, the contraction index of the dh GEMM
+  if ((err = quant("x1_mx8_quantize_dz", dz, M, N, u8(ws.dzq), u8(ws.dzs))) != hipSuccess) return hip_status(err);
+  if ((err = quant("x2_mx8_quantize_W2", W2, d, N, u8(ws.w2q), u8(ws.w2s))) != hipSuccess) return hip_status(err);
+  // B1: dh = dz W2^T on MXFP8; epilogue dn (into dR), n, S, G as in the bf16 backward
+  GemmArgs b1 = gemm_mx8(M, d, N, u8(ws.dzq), u8(ws.dzs), u8(ws.w2q), u8(ws.w2s), dR, d);
+  b1.E = y;
+  b1.lde = d;
+  b1.vrow = r;
+  b1.vcol = gamma;
+  b1.part_row = S;
+  b1.ld_part_row = ws.Tn;
+  b1.part_col = G;
+  b1.ld_part_col = d;
+  b1.C2 = n;
+  b1.ldc2 = d;
+  if ((err = traced("b1_gemm_mx8_dh_epilogue", gemm_flops(M, d, N),
+                    mn * (1 + 1.0 / 32) + dn2 * (1 + 1.0 / 32) + 3.0 * md * e + M * ws.Tn * 4.0 + ws.Tm * d * 4.0, s,
+                    [&] { return coda::launch_gemm_mx8(b1, coda::EPI_DN, s); })) != hipSuccess)
+    return hip_status(err);
+  // R2, E2 as in the bf16 backward
+  if ((err = traced("r2_bwd_reduce", 0.0, M * ws.Tn * 4.0 + ws.Tm * d * 4.0 + 8.0 * M + 4.0 * d, s, [&] {
+         return coda::launch_bwd_reduce(S, ws.Tn, ws.Tn, r, M, d, G, ws.Tm, c, dgamma, s);
+       })) != hipSuccess)
+    return hip_status(err);
+  if ((err = traced("e2_dy", 0.0, 3.0 * md * e + 8.0 * M, s,
+                    [&] { return coda::launch_dy(dR, y, r, c, nullptr, M, d, s); })) != hipSuccess)
+    return hip_status(err);
+  // B2: dW2 = diag(gamma) n^T dz, contraction over M: n and dz along M, stored transposed
+  if ((err = quant_t("x3_mx8_quantize_nT", n, M, d, u8(ws.nTq), u8(ws.nTs))) != hipSuccess) return hip_status(err);
+  if ((err = quant_t("x4_mx8_quantize_dzT", dz, M, N, u8(ws.dzTq), u8(ws.dzTs))) != hipSuccess) return hip_status(err);
+  GemmArgs b2 = gemm_mx8(d, N, M, u8(ws.nTq), u8(ws.nTs), u8(ws.dzTq), u8(ws.dzTs), dW2, N);
+  b2.vcol = gamma;
+  if ((err = traced("b2_gemm_mx8_dW2", gemm_flops(d, N, M), (md + mn) * (1 + 1.0 / 32) + dn2 * e + 2.0 * d, s,
+                    [&] { return coda::launch_gemm_mx8(b2, coda::EPI_ROWSCALE, s); })) != hipSuccess)
+    return hip_status(err);
+  // B3: dX = dy W1^T, contraction over d: dy and W1 along d
+  if ((err = quant("x5_mx8_quantize_dy", dR, M, d, u8(ws.dyq), u8(ws.dys))) != hipSuccess) return hip_status(err);
+  if ((err = quant("x6_mx8_quantize_W1", W1, K, d, u8(ws.w1q), u8(ws.w1s))) != hipSuccess) return hip_status(err);
+  GemmArgs b3 = gemm_mx8(M, K, d, u8(ws.dyq), u8(ws.dys), u8(ws.w1q), u8(ws.w1s), dX, K);
+  if ((err = traced("b3_gemm_mx8_dX", gemm_flops(M, K, d), (md + kd) * (1 + 1.0 / 32) + mk * e, s,
+                    [&] { return coda::launch_gemm_mx8(b3, coda::EPI_STORE, s); })) != hipSuccess)
+    return hip_status(err);
+  // B4: dW1 = X^T dy, contraction over M: X and dy along M, stored transposed
+  if ((err = quant_t("x7_mx8_quantize_XT", X, M, K, u8(ws.XTq), u8(ws.XTs))) != hipSuccess) return hip_status(err);
+  if ((err = quant_t("x8_mx8_quantize_dyT", dR, M, d, u8(ws.dyTq), u8(ws.dyTs))) != hipSuccess) return hip_status(err);
+  GemmArgs b4 = gemm_mx8(K, d, M, u8(ws.XTq), u8(ws.XTs), u8(ws.dyTq), u8(ws.dyTs), dW1, d);
+  return hip_status(traced("b4_gemm_mx8_dW1", gemm_flops(K, d, M), (mk + md) * (1 + 1.0 / 32) + kd * e, s,
+                           [&] { return coda::launch_gemm_mx8(b4, coda::EPI_STORE, s); }));
+}
+
 }  // extern "C"

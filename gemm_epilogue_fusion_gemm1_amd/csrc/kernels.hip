@@ -1190,6 +1190,57 @@ __global__ void mx8_quantize_kernel(const __bf16* __restrict__ src, int64_t ld, 
   }
 }
 
+// bf16 [rows, cols] -> MXFP8 along the columns' direction, stored transposed:
+// codes [cols][rows] (a column's 32-blocks of consecutive rows are contiguous
+// 32 bytes), scales step-blocked [rows/128][cols][4].  This is the operand
+// layout of a GEMM that contracts over the rows (X^T dy, n^T dz).  A
+// workgroup stages a 128 x 64 tile in LDS (each 16-byte row piece read
+// once); thread (b, c) then quantises column c's rows 32b..32b+31 exactly as
+// the row quantiser does a 32-block and writes its 32 codes as two 16-byte
+// stores.  rows % 128 == 0.
+__global__ void __launch_bounds__(256) mx8_quantize_t_kernel(const __bf16* __restrict__ src, int64_t ld,
+                                                             int64_t rows, int64_t cols,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+  __shared__ __bf16 tile[128][64];
+  const int64_t row0 = (int64_t)blockIdx.y * 128, col0 = (int64_t)blockIdx.x * 64;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {           // 1024 pieces of 8 values, 4 per thread
+    const int piece = t + 256 * k;
+    const int r = piece >> 3, c8 = (piece & 7) * 8;
+    const int64_t col = col0 + c8;
+    bf16x8 v{};
+    if (col < cols) v = *(const bf16x8*)(src + (row0 + r) * ld + col);
+    *(bf16x8*)&tile[r][c8] = v;
+  }
+  __syncthreads();
+  const int c = t & 63, b = t >> 6;       // column, 32-row block
+  const int64_t col = col0 + c;
+  float v[32];
+  float am = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    v[e] = (float)tile[32 * b + e][c];
+    am = fmaxf(am, fabsf(v[e]));
+  }
+  const int sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
+  const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
+  auto sat = [&](float x) { return fminf(fmaxf(x * inv, -448.0f), 448.0f); };
+  uint32_t w[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(sat(v[4 * q]), sat(v[4 * q + 1]), 0, false);
+    w[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(v[4 * q + 2]), sat(v[4 * q + 3]), x, true);
+  }
+  if (col < cols) {
+    uint8_t* dst = codes + col * rows + row0 + 32 * b;
+    *(uint4*)dst = uint4{w[0], w[1], w[2], w[3]};
+    *(uint4*)(dst + 16) = uint4{w[4], w[5], w[6], w[7]};
+    scales[((int64_t)blockIdx.y * cols + col) * 4 + b] = (uint8_t)(sexp + 127);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 forward path: a plain LDS-tiled FMA GEMM (64x64 tile, 4x4 per thread)
 // with the same epilogue semantics.  A is [M,K] (k contiguous), B is [K,N].
@@ -1449,8 +1500,18 @@ hipError_t launch_gemm_mx8(const GemmArgs& g, Epi epi, hipStream_t s) {
     case EPI_STORE: return launch_mx8_one<EPI_STORE>(g, s);
     case EPI_RESID_SUMSQ: return launch_mx8_one<EPI_RESID_SUMSQ>(g, s);
     case EPI_RSQRT_SCALE: return launch_mx8_one<EPI_RSQRT_SCALE>(g, s);
+    case EPI_DN: return launch_mx8_one<EPI_DN>(g, s);
+    case EPI_ROWSCALE: return launch_mx8_one<EPI_ROWSCALE>(g, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_mx8_quantize_t(const void* src, int64_t ld, int64_t rows, int64_t cols, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t s) {
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)(rows / 128));
+  hipLaunchKernelGGL(mx8_quantize_t_kernel, grid, dim3(256), 0, s, (const __bf16*)src, ld, rows, cols, codes,
+                     scales);
+  return hipGetLastError();
 }
 
 hipError_t launch_mx8_quantize(const void* src, int64_t ld, int64_t rows, int64_t cols,

@@ -77,8 +77,14 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool a_kmajor, bool b_kmajor, Epi
                             hipStream_t stream);
 hipError_t launch_gemm_f32(const GemmArgs& g, Epi epi, hipStream_t stream);
 // MXFP8 x MXFP8 GEMM, both operands K-contiguous (A [M][K], B^T [N][K]);
-// K % 128 == 0; epilogues EPI_STORE, EPI_RESID_SUMSQ (with q_out), EPI_RSQRT_SCALE
+// K % 128 == 0; epilogues EPI_STORE, EPI_RESID_SUMSQ (with q_out),
+// EPI_RSQRT_SCALE, EPI_DN, EPI_ROWSCALE
 hipError_t launch_gemm_mx8(const GemmArgs& g, Epi epi, hipStream_t stream);
+// codes / scales = the MXFP8 quantisation of src [rows, cols] (bf16, row
+// stride ld) along its rows, stored transposed: codes [cols][rows], scales
+// step-blocked [rows/128][cols][4] (rows % 128 == 0, cols % 8 == 0)
+hipError_t launch_mx8_quantize_t(const void* src, int64_t ld, int64_t rows, int64_t cols,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t stream);
 // codes / scales = the MXFP8 quantisation of the bf16 rows of src along the
 // row (cols % 128 == 0; codes [rows][cols], scales step-blocked
 // [cols/128][rows][4])

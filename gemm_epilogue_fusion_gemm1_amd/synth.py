@@ -103,6 +103,11 @@ WORKLOADS = {
                  eps=1e-6, seed=1008, backward=False,
                  note="LLaMA-7B-shaped block forward with MXFP8 operands (weights "
                       "stored [out, in])"),
+        Workload("llama7b_fwdbwd_mx8", "mx8", "mxfp8", M=8192, K=4096, d=4096, N=11008,
+                 eps=1e-6, seed=1010, backward=True,
+                 note="LLaMA-7B-shaped block forward+backward with every GEMM on MXFP8 "
+                      "operands (the backward quantises its bf16 inputs along each "
+                      "GEMM's contraction index)"),
     ]
 }
 
@@ -204,13 +209,17 @@ def rope_inputs(M: int, K: int, N: int, seed: int, dtype: str = "bf16", with_dz:
     return {k: _quantise(v, dtype) for k, v in out.items()}
 
 
-def mx8_inputs(M: int, K: int, d: int, N: int, seed: int) -> dict:
+def mx8_inputs(M: int, K: int, d: int, N: int, seed: int, with_dz: bool = False) -> dict:
     """The draws of ``coda_inputs`` (bf16) with the weights transposed to
     [out, in], the layout an MXFP8 weight is quantised from (blocks run along
-    the contraction index).  The quantisation itself is the caller's."""
-    h = coda_inputs(M, K, d, N, seed, "bf16", with_dz=False)
-    return {"X": h["X"], "R": h["R"], "gamma": h["gamma"],
-            "W1t": np.ascontiguousarray(h["W1"].T), "W2t": np.ascontiguousarray(h["W2"].T)}
+    the contraction index), and (for a backward) the weights as drawn and dz.
+    The quantisation itself is the caller's."""
+    h = coda_inputs(M, K, d, N, seed, "bf16", with_dz=with_dz)
+    out = {"X": h["X"], "R": h["R"], "gamma": h["gamma"],
+           "W1t": np.ascontiguousarray(h["W1"].T), "W2t": np.ascontiguousarray(h["W2"].T)}
+    if with_dz:
+        out.update(W1=h["W1"], W2=h["W2"], dz=h["dz"])
+    return out
 
 
 def workload_inputs(w: Workload, with_dz: bool | None = None) -> dict:
@@ -226,5 +235,5 @@ def workload_inputs(w: Workload, with_dz: bool | None = None) -> dict:
     if w.kind == "rope":
         return rope_inputs(w.M, w.K, w.N, w.seed, w.dtype, with_dz)
     if w.kind == "mx8":
-        return mx8_inputs(w.M, w.K, w.d, w.N, w.seed)
+        return mx8_inputs(w.M, w.K, w.d, w.N, w.seed, with_dz)
     return swiglu_inputs(w.M, w.d, w.F, w.seed, w.dtype, with_dz)

@@ -382,7 +382,7 @@ coda_status coda_rope_bwd(coda_dtype dtype, int64_t M, int64_t K, int64_t N, int
  *   sums [M, ceil(d/256)] fp32, then q [M, d] E4M3 at the next 256-byte
  *   boundary, then its scales qs (step-blocked, [d/128][M][4]) at the next
  *   256-byte boundary.
- * The backward is coda_bwd (bf16) on the saved y and r.
+ * The backward is coda_bwd (bf16) or coda_bwd_mx8 (below) on the saved y and r.
  * ---------------------------------------------------------------------- */
 coda_status coda_mx8_quantize(int64_t rows, int64_t cols, const void* src, int64_t ld_src,
                               void* codes, void* scales, void* stream);
@@ -391,6 +391,37 @@ coda_status coda_fwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, float eps, 
                          const void* Xs, const void* W1tq, const void* W1ts, const void* R,
                          const void* gamma, const void* W2tq, const void* W2ts, void* y, float* r,
                          void* z, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backward of the block with every GEMM on the MXFP8 matrix units.  The pages
+ * argue that faster FP8 matrix units make the memory-bound work around a
+ * GEMM relatively costlier ([JA] 課題：大モデル訓練の「手抜き税」; [RU] "Налог
+ * на лень при обучении больших моделей"), which is what the fused epilogues
+ * remove.  Gradient: that of coda_bwd (the forward's quantisation passes it
+ * straight through), with each of the four GEMMs on MXFP8 operands (the
+ * format of coda_fwd_mx8) quantised along its own contraction index:
+ *   dh  = dz W2^T          dz and W2 quantised along N;  epilogue as coda_bwd
+ *                          (dn, n = r y, the partial sums of s and dgamma)
+ *   dR  = dy = r dn - c y  (bf16, as coda_bwd)
+ *   dW2 = diag(gamma) n^T dz   n and dz quantised along M
+ *   dX  = dy W1^T          dy and W1 quantised along d
+ *   dW1 = X^T dy           X and dy quantised along M
+ * dn, n and dy are stored in bf16 before they are quantised.  The weights and
+ * activations come in bf16, as for coda_bwd (a training step keeps bf16
+ * weights); the call quantises them itself.
+ *
+ *   Arguments as coda_bwd (bf16 tensors, r and dgamma float32).
+ *   M, d, N: multiples of 128 (the contraction dimensions are whole 128-k
+ *   steps); K: a multiple of 8.
+ *   workspace: >= coda_bwd_mx8_workspace_bytes(M, K, d, N) bytes (every GEMM
+ *   operand in MXFP8, n, the partial sums), 16-byte aligned.
+ * Errors as coda_bwd.
+ * ---------------------------------------------------------------------- */
+size_t coda_bwd_mx8_workspace_bytes(int64_t M, int64_t K, int64_t d, int64_t N);
+coda_status coda_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, const void* X, const void* W1,
+                         const void* gamma, const void* W2, const void* y, const float* r,
+                         const void* dz, void* dX, void* dW1, void* dR, void* dW2, float* dgamma,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Kernel tracing (measurement aid; off by default).

@@ -364,3 +364,35 @@ def test_mx8_rejects(L):
     assert L.coda_mx8_quantize(M, K, q_src, K, q_src, q_scales, None) == ALIAS
     assert L.coda_mx8_quantize(M, K, None, K, q_codes, q_scales, None) == NULL
     assert L.coda_mx8_quantize(M, K, ctypes.c_void_p(q_src.value + 4), K, q_codes, q_scales, None) == ALIGN
+
+def bwd_mx8_call(L, **over):
+    m = FakeMem()
+    M, K, d, N = 256, 40, 128, 384
+    a = dict(M=M, K=K, d=d, N=N, X=m(M * K * 2), W1=m(K * d * 2), gamma=m(d * 2), W2=m(d * N * 2),
+             y=m(M * d * 2), r=m(M * 4), dz=m(M * N * 2), dX=m(M * K * 2), dW1=m(K * d * 2), dR=m(M * d * 2),
+             dW2=m(d * N * 2), dg=m(d * 4))
+    a["ws_bytes"] = L.coda_bwd_mx8_workspace_bytes(M, K, d, N)
+    a["ws"] = m(a["ws_bytes"])
+    a.update(over)
+    return L.coda_bwd_mx8(a["M"], a["K"], a["d"], a["N"], a["X"], a["W1"], a["gamma"], a["W2"], a["y"], a["r"],
+                          a["dz"], a["dX"], a["dW1"], a["dR"], a["dW2"], a["dg"], a["ws"], a["ws_bytes"], None)
+
+
+def test_bwd_mx8_rejects(L):
+    """The MXFP8 backward checks like coda_bwd, and needs M, d, N in whole
+    128-element K steps; every rejection comes before any HIP call."""
+    assert L.coda_bwd_mx8_workspace_bytes(256, 40, 128, 384) > 256 * 384 * 2
+    assert L.coda_bwd_mx8_workspace_bytes(200, 40, 128, 384) == 0
+    assert bwd_mx8_call(L, X=None) == NULL
+    assert bwd_mx8_call(L, dg=None) == NULL
+    assert bwd_mx8_call(L, M=200) == SHAPE
+    assert bwd_mx8_call(L, d=136) == SHAPE
+    assert bwd_mx8_call(L, N=392) == SHAPE
+    assert bwd_mx8_call(L, K=12) == SHAPE
+    assert bwd_mx8_call(L, ws_bytes=1024) == WORKSPACE
+    assert bwd_mx8_call(L, ws=None) == WORKSPACE
+    m = FakeMem()
+    x = m(1 << 20)
+    assert bwd_mx8_call(L, X=x, dX=x) == ALIAS
+    assert bwd_mx8_call(L, r=ctypes.c_void_p(m(4096).value + 4)) == ALIGN
+

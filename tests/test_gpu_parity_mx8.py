@@ -246,3 +246,84 @@ def test_full_workload_mx8(torch_dev):
     report(w.name, {**errs, "yg_code_flips": nf_c, "yg_scale_flips": nf_s})
     assert errs["y_rows"] <= BF16_TOL and errs["z_rows"] <= BF16_TOL and errs["r_rows"] <= R_TOL
     assert np.all(np.isfinite(z)) and np.all(r > 0)
+
+# ----------------------------------------------------------- MXFP8 backward
+
+SMALL_BWD_MX8 = [
+    # M, K, d, N (M, d, N whole 128-k steps; K ragged)
+    (256, 136, 256, 384),
+    (128, 8, 128, 128),          # smallest accepted
+    (640, 1032, 384, 1152),      # several tiles, K tail, d and N not multiples of 256
+    (384, 264, 512, 256),
+]
+
+
+def _mx8_bwd_inputs(M, K, d, N, seed, eps=1e-6):
+    """The backward's inputs: the draws of the bf16 block and its saved y
+    (rounded to bf16) and r from the oracle's forward."""
+    h = synth.coda_inputs(M, K, d, N, seed=seed, dtype="bf16")
+    yr = oracle.ref_y_r(h["X"], h["W1"], h["R"], eps)
+    return h, oracle.bf16_rne(yr["y"]), yr["r"]
+
+
+def _run_bwd_mx8(torch, dev, h, y, r):
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    t = {k: bf(torch, dev, v) for k, v in h.items() if k != "R"}
+    ty = bf(torch, dev, y)
+    tr = torch.from_numpy(np.asarray(r, np.float32)).to(dev)
+    out = coda.bwd_mx8(t["X"], t["W1"], t["gamma"], t["W2"], ty, tr, t["dz"])
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("shape", SMALL_BWD_MX8, ids=lambda s: "x".join(map(str, s)))
+def test_bwd_mx8(torch_dev, shape):
+    torch, dev = torch_dev
+    M, K, d, N = shape
+    h, y, r = _mx8_bwd_inputs(M, K, d, N, seed=800 + M + K)
+    dX, dW1, dR, dW2, dg = _run_bwd_mx8(torch, dev, h, y, r)
+    b = oracle.ref_bwd_mx8(h["X"], h["W1"], h["gamma"], h["W2"], y, r, h["dz"])
+    f = lambda t: t.float().cpu().numpy()  # noqa: E731
+    errs = {"dX": rel(f(dX), b["dX"]), "dW1": rel(f(dW1), b["dW1"]), "dR": rel(f(dR), b["dR"]),
+            "dW2": rel(f(dW2), b["dW2"]), "dgamma": rel(dg.cpu().numpy(), b["dgamma"])}
+    # beside it: the distance from the unquantised backward (the MXFP8 error itself)
+    e = oracle.ref_bwd(h["X"], h["W1"], h["gamma"], h["W2"], y, r, h["dz"])
+    info = {f"{k}_vs_unquantised": rel(f(v), e[k]) for k, v in (("dX", dX), ("dW1", dW1), ("dW2", dW2))}
+    report(f"mx8 bwd {shape}", {**errs, **info})
+    for k in ("dX", "dW1", "dR", "dW2"):
+        assert errs[k] <= BF16_TOL, (k, errs[k])
+    assert errs["dgamma"] <= 1e-3
+
+
+def test_bwd_mx8_deterministic(torch_dev):
+    torch, dev = torch_dev
+    h, y, r = _mx8_bwd_inputs(640, 1032, 384, 1152, seed=820)
+    a = _run_bwd_mx8(torch, dev, h, y, r)
+    b = _run_bwd_mx8(torch, dev, h, y, r)
+    for x_, y_ in zip(a, b):
+        assert torch.equal(x_, y_)
+
+
+def test_full_workload_bwd_mx8(torch_dev):
+    """LLaMA-7B-shaped MXFP8 backward: dX and dR on stratified rows (one per
+    128-row band), dW1 and dW2 on stratified columns (one per 64-column
+    band), dgamma in full."""
+    torch, dev = torch_dev
+    w = synth.WORKLOADS["llama7b_fwdbwd_mx8"]
+    print(f"[parity] {w.name}: inputs and the oracle's forward", flush=True)
+    h, y, r = _mx8_bwd_inputs(w.M, w.K, w.d, w.N, seed=w.seed, eps=w.eps)
+    dX, dW1, dR, dW2, dg = _run_bwd_mx8(torch, dev, h, y, r)
+    rng = np.random.default_rng(w.seed)
+    strata = lambda n, band: np.unique(np.concatenate([[0, n - 1], [rng.integers(b0, min(b0 + band, n)) for b0 in range(0, n, band)]]))  # noqa: E731
+    rows, cd, cn = strata(w.M, 128), strata(w.d, 64), strata(w.N, 64)
+    print(f"[parity] {w.name}: oracle backward (sampled)", flush=True)
+    b = oracle.ref_bwd_mx8_sampled(h["X"], h["W1"], h["gamma"], h["W2"], y, r, h["dz"], rows, cd, cn)
+    f = lambda t: t.float().cpu().numpy()  # noqa: E731
+    errs = {"dX_rows": rel(f(dX[rows]), b["dX_rows"]), "dR_rows": rel(f(dR[rows]), b["dR_rows"]),
+            "dW1_cols": rel(f(dW1[:, cd]), b["dW1_cols"]), "dW2_cols": rel(f(dW2[:, cn]), b["dW2_cols"]),
+            "dgamma": rel(dg.cpu().numpy(), b["dgamma"])}
+    report(w.name, errs)
+    for k in ("dX_rows", "dR_rows", "dW1_cols", "dW2_cols"):
+        assert errs[k] <= BF16_TOL, (k, errs[k])
+    assert errs["dgamma"] <= 1e-3
+
