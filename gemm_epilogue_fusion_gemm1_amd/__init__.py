@@ -61,13 +61,14 @@ def lib_path() -> str:
     return os.path.join(_PKG, "libcoda.so")
 
 
-def load_library() -> ctypes.CDLL:
-    """Load libcoda.so (built in-tree by build.py).  torch is imported first so
-    that the library binds to the HIP runtime torch already loaded."""
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libcoda.so (built in-tree by build.py), or another build of the
+    same sources at `path` (the first call decides).  torch is imported first
+    so that the library binds to the HIP runtime torch already loaded."""
     global _LIB
     if _LIB is not None:
         return _LIB
-    path = lib_path()
+    path = path or lib_path()
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m gemm_epilogue_fusion_gemm1_amd.build`; "

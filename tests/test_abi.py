@@ -21,13 +21,20 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(coda_[a-z_0-9]+)\s*\(", src)))
 
 
+def _lib_under_test():
+    """libcoda.so, or the build named by CODA_ABI_TEST_LIB (the sanitized
+    copy that test_abi_asan.py runs this file against)."""
+    from gemm_epilogue_fusion_gemm1_amd import lib_path
+    return os.environ.get("CODA_ABI_TEST_LIB") or lib_path()
+
+
 @pytest.fixture(scope="module")
 def L():
     from gemm_epilogue_fusion_gemm1_amd import lib_path, load_library
-    if not os.path.exists(lib_path()):
+    if not os.path.exists(_lib_under_test()) and _lib_under_test() == lib_path():
         import __graft_entry__
         __graft_entry__.build()
-    return load_library()
+    return load_library(_lib_under_test())
 
 
 def test_header_declares_the_boundary():
@@ -37,8 +44,8 @@ def test_header_declares_the_boundary():
 
 
 def test_library_exports_every_declared_symbol(L):
-    from gemm_epilogue_fusion_gemm1_amd import lib_path
-    out = subprocess.run(["nm", "-D", "--defined-only", lib_path()], capture_output=True, text=True).stdout
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib_under_test()], capture_output=True,
+                         text=True).stdout
     exported = set(re.findall(r"\bT (coda_[a-z_0-9]+)", out))
     missing = [f for f in declared_functions() if f not in exported]
     assert not missing, f"declared but not exported: {missing}"
