@@ -461,13 +461,28 @@ def make_case(w, torch, coda):
 
 # ------------------------------------------------------------------- timing
 
-def time_steps(torch, fn, steps, warmup, per_step=None):
-    """Mean ms per step over `steps` steps after `warmup` untimed ones.  With
+# Untimed work before a timed region: `warmup` steps, extended (when warmup
+# > 0) until this much wall time has passed.  The clock and power state of the
+# GPU takes tens of milliseconds to settle after an idle or a change of load:
+# measured on the LLaMA-1B-shaped forward (0.3 ms per step), 5 warm-up steps
+# from idle gave 0.339 ms per step and the settled state 0.297 ms (unfused:
+# 0.359 and 0.309); steps of a few milliseconds are not affected.  The fused
+# and unfused regions get the same treatment.
+SETTLE_MS = 200.0
+
+
+def time_steps(torch, fn, steps, warmup, per_step=None, settle_ms=SETTLE_MS):
+    """Mean ms per step over `steps` steps after `warmup` untimed ones (and,
+    when warmup > 0, more untimed steps until `settle_ms` have passed).  With
     `per_step` (a dict), an event is also recorded between steps and the
     median / min / max step time is stored there."""
+    t0 = time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    while warmup > 0 and (time.perf_counter() - t0) * 1e3 < settle_ms:
+        fn()
+        torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_step is not None else 2)]
     ev[0].record()
     for i in range(steps):
