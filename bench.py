@@ -325,7 +325,7 @@ class Mx8Case:
             self.dW2 = torch.empty((d, N), dtype=bf, device=dev)
             self.dg = torch.empty((d,), dtype=torch.float32, device=dev)
             self.wsb = torch.empty(coda.bwd_mx8_workspace_bytes(M, K, d, N), dtype=torch.uint8, device=dev)
-            self.kernels_per_step = 2 + 14
+            self.kernels_per_step = 2 + 11
             self.manual_bwd = True
 
     def flops(self):

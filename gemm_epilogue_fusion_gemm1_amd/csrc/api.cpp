@@ -1078,7 +1078,7 @@ namespace {
 // step-blocked scales), plus n (bf16) and the partial sums of the bf16
 // backward.
 struct BwdMx8Ws {
-  size_t dzq, dzs, w2q, w2s, n, S, G, c, nTq, nTs, dzTq, dzTs, dyq, dys, w1q, w1s, XTq, XTs, dyTq, dyTs, total;
+  size_t dzq, dzs, w2q, w2s, S, G, c, nTq, nTs, dzTq, dzTs, dyq, dys, w1q, w1s, XTq, XTs, dyTq, dyTs, total;
   int Tn, Tm;
 };
 BwdMx8Ws bwd_mx8_ws(int64_t M, int64_t K, int64_t d, int64_t N) {
@@ -1089,7 +1089,6 @@ BwdMx8Ws bwd_mx8_ws(int64_t M, int64_t K, int64_t d, int64_t N) {
   auto take = [&](size_t bytes) { const size_t at = o; o += round_up(bytes); return at; };
   w.dzq = take((size_t)M * N);       w.dzs = take((size_t)M * (N / 32));
   w.w2q = take((size_t)d * N);       w.w2s = take((size_t)d * (N / 32));
-  w.n = take((size_t)M * d * 2);
   w.S = take((size_t)M * w.Tn * 4);  w.G = take((size_t)w.Tm * d * 4);  w.c = take((size_t)M * 4);
   w.nTq = take((size_t)d * M);       w.nTs = take((size_t)d * (M / 32));
   w.dzTq = take((size_t)N * M);      w.dzTs = take((size_t)N * (M / 32));
@@ -1141,23 +1140,36 @@ coda_status coda_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, const void*
   float* S = (float*)(wb + ws.S);
   float* G = (float*)(wb + ws.G);
   float* c = (float*)(wb + ws.c);
-  void* n = wb + ws.n;
   hipError_t err;
   const double md = (double)M * d, mn = (double)M * N, dn2 = (double)d * N, mk = (double)M * K, kd = (double)K * d;
+  const double q8 = 1.0 + 1.0 / 32.0;   // MXFP8 bytes per element (code + a scale per 32)
   auto quant = [&](const char* name, const void* src, int64_t rows, int64_t cols, uint8_t* q, uint8_t* qs) {
-    return traced(name, 0.0, rows * cols * (3.0 + 1.0 / 32.0), s, [&] {
+    return traced(name, 0.0, rows * cols * (2.0 + q8), s, [&] {
       return coda::launch_mx8_quantize(src, cols, rows, cols, q, qs, s);
     });
   };
-  auto quant_t = [&](const char* name, const void* src, int64_t rows, int64_t cols, uint8_t* q, uint8_t* qs) {
-    return traced(name, 0.0, rows * cols * (3.0 + 1.0 / 32.0), s, [&] {
-      return coda::launch_mx8_quantize_t(src, cols, rows, cols, q, qs, s);
-    });
+  auto fused = [&](const char* name, double bytes, int mode, const coda::MxQuantArgs& q) {
+    return traced(name, 0.0, bytes, s, [&] { return coda::launch_mx8_quantize_fused(q, mode, s); });
   };
-  // dz and W2 along N, the contraction index of the dh GEMM
-  if ((err = quant("x1_mx8_quantize_dz", dz, M, N, u8(ws.dzq), u8(ws.dzs))) != hipSuccess) return hip_status(err);
+  auto qargs = [&](const void* src, int64_t rows, int64_t cols) {
+    coda::MxQuantArgs q{};
+    q.src = src;
+    q.ld = cols;
+    q.rows = rows;
+    q.cols = cols;
+    return q;
+  };
+  // dz along N (the dh GEMM's contraction index) and along M, stored
+  // transposed (the dW2 GEMM's), in one pass; W2 along N
+  coda::MxQuantArgs qdz = qargs(dz, M, N);
+  qdz.qr = u8(ws.dzq);
+  qdz.sr = u8(ws.dzs);
+  qdz.qt = u8(ws.dzTq);
+  qdz.st = u8(ws.dzTs);
+  if ((err = fused("x1_mx8_quantize_dz_both", mn * (2.0 + 2.0 * q8), 0, qdz)) != hipSuccess) return hip_status(err);
   if ((err = quant("x2_mx8_quantize_W2", W2, d, N, u8(ws.w2q), u8(ws.w2s))) != hipSuccess) return hip_status(err);
-  // B1: dh = dz W2^T on MXFP8; epilogue dn (into dR), n, S, G as in the bf16 backward
+  // B1: dh = dz W2^T on MXFP8; epilogue dn (into dR), S, G as in the bf16
+  // backward (n is made from y and r where it is quantised)
   GemmArgs b1 = gemm_mx8(M, d, N, u8(ws.dzq), u8(ws.dzs), u8(ws.w2q), u8(ws.w2s), dR, d);
   b1.E = y;
   b1.lde = d;
@@ -1167,40 +1179,54 @@ coda_status coda_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, const void*
   b1.ld_part_row = ws.Tn;
   b1.part_col = G;
   b1.ld_part_col = d;
-  b1.C2 = n;
-  b1.ldc2 = d;
   if ((err = traced("b1_gemm_mx8_dh_epilogue", gemm_flops(M, d, N),
-                    mn * (1 + 1.0 / 32) + dn2 * (1 + 1.0 / 32) + 3.0 * md * e + M * ws.Tn * 4.0 + ws.Tm * d * 4.0, s,
+                    (mn + dn2) * q8 + 2.0 * md * e + M * ws.Tn * 4.0 + ws.Tm * d * 4.0 + 4.0 * M, s,
                     [&] { return coda::launch_gemm_mx8(b1, coda::EPI_DN, s); })) != hipSuccess)
     return hip_status(err);
-  // R2, E2 as in the bf16 backward
+  // R2 as in the bf16 backward
   if ((err = traced("r2_bwd_reduce", 0.0, M * ws.Tn * 4.0 + ws.Tm * d * 4.0 + 8.0 * M + 4.0 * d, s, [&] {
          return coda::launch_bwd_reduce(S, ws.Tn, ws.Tn, r, M, d, G, ws.Tm, c, dgamma, s);
        })) != hipSuccess)
     return hip_status(err);
-  if ((err = traced("e2_dy", 0.0, 3.0 * md * e + 8.0 * M, s,
-                    [&] { return coda::launch_dy(dR, y, r, c, nullptr, M, d, s); })) != hipSuccess)
+  // E2 with the quantisations of dy: dy = r dn - c y written over dn (dR),
+  // then along d (the dX GEMM's contraction index) and along M, transposed
+  // (the dW1 GEMM's)
+  coda::MxQuantArgs qdy = qargs(dR, M, d);
+  qdy.r = r;
+  qdy.c = c;
+  qdy.y = y;
+  qdy.out = dR;
+  qdy.qr = u8(ws.dyq);
+  qdy.sr = u8(ws.dys);
+  qdy.qt = u8(ws.dyTq);
+  qdy.st = u8(ws.dyTs);
+  if ((err = fused("e2_dy_mx8_quantize_both", md * (3.0 * e + 2.0 * q8) + 8.0 * M, 1, qdy)) != hipSuccess)
     return hip_status(err);
-  // B2: dW2 = diag(gamma) n^T dz, contraction over M: n and dz along M, stored transposed
-  if ((err = quant_t("x3_mx8_quantize_nT", n, M, d, u8(ws.nTq), u8(ws.nTs))) != hipSuccess) return hip_status(err);
-  if ((err = quant_t("x4_mx8_quantize_dzT", dz, M, N, u8(ws.dzTq), u8(ws.dzTs))) != hipSuccess) return hip_status(err);
+  // B2: dW2 = diag(gamma) n^T dz, contraction over M: n = r y (bf16) along M,
+  // transposed
+  coda::MxQuantArgs qn = qargs(y, M, d);
+  qn.r = r;
+  qn.qt = u8(ws.nTq);
+  qn.st = u8(ws.nTs);
+  if ((err = fused("x3_mx8_quantize_nT", md * (e + q8) + 4.0 * M, 2, qn)) != hipSuccess) return hip_status(err);
   GemmArgs b2 = gemm_mx8(d, N, M, u8(ws.nTq), u8(ws.nTs), u8(ws.dzTq), u8(ws.dzTs), dW2, N);
   b2.vcol = gamma;
-  if ((err = traced("b2_gemm_mx8_dW2", gemm_flops(d, N, M), (md + mn) * (1 + 1.0 / 32) + dn2 * e + 2.0 * d, s,
+  if ((err = traced("b2_gemm_mx8_dW2", gemm_flops(d, N, M), (md + mn) * q8 + dn2 * e + 2.0 * d, s,
                     [&] { return coda::launch_gemm_mx8(b2, coda::EPI_ROWSCALE, s); })) != hipSuccess)
     return hip_status(err);
-  // B3: dX = dy W1^T, contraction over d: dy and W1 along d
-  if ((err = quant("x5_mx8_quantize_dy", dR, M, d, u8(ws.dyq), u8(ws.dys))) != hipSuccess) return hip_status(err);
+  // B3: dX = dy W1^T, contraction over d: W1 along d
   if ((err = quant("x6_mx8_quantize_W1", W1, K, d, u8(ws.w1q), u8(ws.w1s))) != hipSuccess) return hip_status(err);
   GemmArgs b3 = gemm_mx8(M, K, d, u8(ws.dyq), u8(ws.dys), u8(ws.w1q), u8(ws.w1s), dX, K);
-  if ((err = traced("b3_gemm_mx8_dX", gemm_flops(M, K, d), (md + kd) * (1 + 1.0 / 32) + mk * e, s,
+  if ((err = traced("b3_gemm_mx8_dX", gemm_flops(M, K, d), (md + kd) * q8 + mk * e, s,
                     [&] { return coda::launch_gemm_mx8(b3, coda::EPI_STORE, s); })) != hipSuccess)
     return hip_status(err);
-  // B4: dW1 = X^T dy, contraction over M: X and dy along M, stored transposed
-  if ((err = quant_t("x7_mx8_quantize_XT", X, M, K, u8(ws.XTq), u8(ws.XTs))) != hipSuccess) return hip_status(err);
-  if ((err = quant_t("x8_mx8_quantize_dyT", dR, M, d, u8(ws.dyTq), u8(ws.dyTs))) != hipSuccess) return hip_status(err);
+  // B4: dW1 = X^T dy, contraction over M: X along M, transposed
+  if ((err = traced("x7_mx8_quantize_XT", 0.0, mk * (e + q8), s, [&] {
+         return coda::launch_mx8_quantize_t(X, K, M, K, u8(ws.XTq), u8(ws.XTs), s);
+       })) != hipSuccess)
+    return hip_status(err);
   GemmArgs b4 = gemm_mx8(K, d, M, u8(ws.XTq), u8(ws.XTs), u8(ws.dyTq), u8(ws.dyTs), dW1, d);
-  return hip_status(traced("b4_gemm_mx8_dW1", gemm_flops(K, d, M), (mk + md) * (1 + 1.0 / 32) + kd * e, s,
+  return hip_status(traced("b4_gemm_mx8_dW1", gemm_flops(K, d, M), (mk + md) * q8 + kd * e, s,
                            [&] { return coda::launch_gemm_mx8(b4, coda::EPI_STORE, s); }));
 }
 

@@ -1241,6 +1241,112 @@ __global__ void __launch_bounds__(256) mx8_quantize_t_kernel(const __bf16* __res
   }
 }
 
+// One 32-block of a row to MXFP8, shared by 4 consecutive lanes holding 8
+// values each (lanes 4j..4j+3 of the wave): the block maximum by two
+// shuffles, the shared exponent floor(log2 amax) - 8 (clamped at -127) from
+// its exponent field, the 8 values scaled by the exact power of two,
+// saturated at 448 and rounded to nearest even by the hardware conversion.
+// Returns the lane's 8 codes; `sexp` receives the exponent.
+__device__ __forceinline__ uint2 mx8_block_of_4_lanes(f32x4 lo, f32x4 hi, int& sexp) {
+  float am = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) am = fmaxf(am, fmaxf(fabsf(lo[e]), fabsf(hi[e])));
+  am = fmaxf(am, __shfl_xor(am, 1));
+  am = fmaxf(am, __shfl_xor(am, 2));
+  sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
+  const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
+  auto sat = [&](float v) { return fminf(fmaxf(v * inv, -448.0f), 448.0f); };
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[0]), sat(lo[1]), 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[2]), sat(lo[3]), w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[0]), sat(hi[1]), 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[2]), sat(hi[3]), w1, true);
+  return uint2{(uint32_t)w0, (uint32_t)w1};
+}
+
+// The MXFP8 operands of the block's backward that come from one bf16 [rows,
+// cols] tensor, in one pass over it (rows % 128 == 0):
+//   QUANT_SRC: v = src; quantised along the row (codes qr [rows][cols], scales
+//              sr [cols/128][rows][4]; cols % 128 == 0) and along the column,
+//              stored transposed (codes qt [cols][rows], scales st
+//              [rows/128][cols][4]) -- dz for the dh and dW2 GEMMs;
+//   QUANT_DY:  v = dy = r_i dn - c_i y (bf16), written over dn (src = out =
+//              dR); quantised both ways -- dy for the dX and dW1 GEMMs;
+//   QUANT_NROW: v = n = r_i y (bf16; src = y); quantised along the column
+//              only -- n for the dW2 GEMM.
+// The values are rounded to bf16 before they are quantised (the stored dn,
+// n and dy of the bf16 backward).  A workgroup takes a 128 x 64 tile: each
+// thread produces 4 pieces of 8 values, quantises them along the row with
+// its 3 neighbours (the row quantiser's arithmetic), and stages them in LDS;
+// thread (b, c) then quantises column c's rows 32b..32b+31 as the transposed
+// quantiser does.
+enum QuantMode : int { QUANT_SRC = 0, QUANT_DY = 1, QUANT_NROW = 2 };
+template <int MODE>
+__global__ void __launch_bounds__(256) mx8_quantize_fused_kernel(MxQuantArgs q) {
+  __shared__ __bf16 tile[128][64];
+  const int64_t row0 = (int64_t)blockIdx.y * 128, col0 = (int64_t)blockIdx.x * 64;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {           // 1024 pieces of 8 values, 4 per thread
+    const int piece = t + 256 * k;
+    const int r = piece >> 3, c8 = (piece & 7) * 8;
+    const int64_t row = row0 + r, col = col0 + c8;
+    const bool ok = col < q.cols;
+    bf16x8 v{};
+    if (ok) {
+      const bf16x8 a = *(const bf16x8*)((const __bf16*)q.src + row * q.ld + col);
+      if constexpr (MODE == QUANT_SRC) {
+        v = a;
+      } else if constexpr (MODE == QUANT_DY) {
+        const bf16x8 yv = *(const bf16x8*)((const __bf16*)q.y + row * q.ld + col);
+        const float ri = q.r[row], ci = q.c[row];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = f2bf(ri * bf2f(a[e]) - ci * bf2f(yv[e]));
+        *(bf16x8*)((__bf16*)q.out + row * q.ld + col) = v;
+      } else {
+        const float ri = q.r[row];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = f2bf(ri * bf2f(a[e]));
+      }
+    }
+    *(bf16x8*)&tile[r][c8] = v;
+    if constexpr (MODE != QUANT_NROW) {
+      const f32x4 lo{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+      const f32x4 hi{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+      int sexp;
+      const uint2 w = mx8_block_of_4_lanes(lo, hi, sexp);
+      if (ok) {
+        *(uint2*)(q.qr + row * q.cols + col) = w;
+        if ((col & 31) == 0) q.sr[((col >> 7) * q.rows + row) * 4 + ((col >> 5) & 3)] = (uint8_t)(sexp + 127);
+      }
+    }
+  }
+  __syncthreads();
+  const int c = t & 63, b = t >> 6;       // column, 32-row block
+  const int64_t col = col0 + c;
+  float v[32];
+  float am = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    v[e] = (float)tile[32 * b + e][c];
+    am = fmaxf(am, fabsf(v[e]));
+  }
+  const int sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
+  const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
+  auto sat = [&](float x) { return fminf(fmaxf(x * inv, -448.0f), 448.0f); };
+  uint32_t w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(sat(v[4 * j]), sat(v[4 * j + 1]), 0, false);
+    w[j] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(v[4 * j + 2]), sat(v[4 * j + 3]), x, true);
+  }
+  if (col < q.cols) {
+    uint8_t* dst = q.qt + col * q.rows + row0 + 32 * b;
+    *(uint4*)dst = uint4{w[0], w[1], w[2], w[3]};
+    *(uint4*)(dst + 16) = uint4{w[4], w[5], w[6], w[7]};
+    q.st[((int64_t)blockIdx.y * q.cols + col) * 4 + b] = (uint8_t)(sexp + 127);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 forward path: a plain LDS-tiled FMA GEMM (64x64 tile, 4x4 per thread)
 // with the same epilogue semantics.  A is [M,K] (k contiguous), B is [K,N].
@@ -1511,6 +1617,17 @@ hipError_t launch_mx8_quantize_t(const void* src, int64_t ld, int64_t rows, int6
   const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)(rows / 128));
   hipLaunchKernelGGL(mx8_quantize_t_kernel, grid, dim3(256), 0, s, (const __bf16*)src, ld, rows, cols, codes,
                      scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx8_quantize_fused(const MxQuantArgs& q, int mode, hipStream_t s) {
+  const dim3 grid((unsigned)((q.cols + 63) / 64), (unsigned)(q.rows / 128));
+  switch (mode) {
+    case QUANT_SRC: hipLaunchKernelGGL(mx8_quantize_fused_kernel<QUANT_SRC>, grid, dim3(256), 0, s, q); break;
+    case QUANT_DY: hipLaunchKernelGGL(mx8_quantize_fused_kernel<QUANT_DY>, grid, dim3(256), 0, s, q); break;
+    case QUANT_NROW: hipLaunchKernelGGL(mx8_quantize_fused_kernel<QUANT_NROW>, grid, dim3(256), 0, s, q); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -91,6 +91,22 @@ hipError_t launch_mx8_quantize_t(const void* src, int64_t ld, int64_t rows, int6
 hipError_t launch_mx8_quantize(const void* src, int64_t ld, int64_t rows, int64_t cols,
                                uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
+// One pass over a bf16 [rows, cols] tensor (row stride ld) that makes MXFP8
+// operands of the backward (rows % 128 == 0).  mode 0: v = src; mode 1: v =
+// dy = r_i src - c_i y, rounded to bf16 and written to out (out may be src);
+// mode 2: v = r_i src rounded to bf16.  qr / sr: v quantised along the row
+// (codes [rows][cols], scales step-blocked [cols/128][rows][4]; cols % 128 ==
+// 0; not made in mode 2); qt / st: v quantised along the column, stored
+// transposed (codes [cols][rows], scales [rows/128][cols][4]).
+struct MxQuantArgs {
+  const void* src; int64_t ld;
+  int64_t rows, cols;
+  const float* r; const float* c; const void* y; void* out;
+  uint8_t* qr; uint8_t* sr;
+  uint8_t* qt; uint8_t* st;
+};
+hipError_t launch_mx8_quantize_fused(const MxQuantArgs& q, int mode, hipStream_t stream);
+
 // r[i] = (sum_t P[i][t] / d + eps)^(-1/2)
 hipError_t launch_row_rsqrt(const float* P, int64_t ldp, int T, int64_t M, int64_t d, float eps,
                             float* r, hipStream_t stream);

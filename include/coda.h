@@ -406,7 +406,8 @@ coda_status coda_fwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, float eps, 
  *   dW2 = diag(gamma) n^T dz   n and dz quantised along M
  *   dX  = dy W1^T          dy and W1 quantised along d
  *   dW1 = X^T dy           X and dy quantised along M
- * dn, n and dy are stored in bf16 before they are quantised.  The weights and
+ * dn, n and dy are rounded to bf16 before they are quantised (dn and dy are
+ * stored; n = r y is formed where it is quantised).  The weights and
  * activations come in bf16, as for coda_bwd (a training step keeps bf16
  * weights); the call quantises them itself.
  *
@@ -414,7 +415,7 @@ coda_status coda_fwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, float eps, 
  *   M, d, N: multiples of 128 (the contraction dimensions are whole 128-k
  *   steps); K: a multiple of 8.
  *   workspace: >= coda_bwd_mx8_workspace_bytes(M, K, d, N) bytes (every GEMM
- *   operand in MXFP8, n, the partial sums), 16-byte aligned.
+ *   operand in MXFP8 and the partial sums), 16-byte aligned.
  * Errors as coda_bwd.
  * ---------------------------------------------------------------------- */
 size_t coda_bwd_mx8_workspace_bytes(int64_t M, int64_t K, int64_t d, int64_t N);
