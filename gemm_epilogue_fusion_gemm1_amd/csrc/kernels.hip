@@ -1348,8 +1348,13 @@ __global__ void __launch_bounds__(256) mx8_quantize_fused_kernel(MxQuantArgs q) 
 }
 
 // ---------------------------------------------------------------------------
-// fp32 forward path: a plain LDS-tiled FMA GEMM (64x64 tile, 4x4 per thread)
-// with the same epilogue semantics.  A is [M,K] (k contiguous), B is [K,N].
+// fp32 forward path: an LDS-tiled GEMM on the fp32 matrix instruction
+// (v_mfma_f32_16x16x4f32) with the same epilogue semantics.  A is [M,K] (k
+// contiguous), B is [K,N].  A 64x64 tile, four waves of 32x32 (2x2 blocks of
+// 16x16), K staged 16 at a time.  In a 16x16x4 block lane l supplies
+// A[l%16][l/16] and B[l/16][l%16] and holds C[4(l/16)+q][l%16], q = 0..3.
+// The accumulators go through LDS to a 4x4-per-thread layout for the
+// epilogue.
 // ---------------------------------------------------------------------------
 constexpr int FT = kTileF32;
 constexpr int FK = 16;
@@ -1358,14 +1363,21 @@ template <int EPI>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
   __shared__ float sA[FK][FT + 4];
   __shared__ float sB[FK][FT + 4];
+  __shared__ float sC[FT][FT + 1];
   __shared__ float red[FT][17];
   const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+  const int lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
+  const int l16 = lane & 15, lk = lane >> 4;
   const int tiles_n = (g.N + FT - 1) / FT;
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
   const int row0 = tm * FT, col0 = tn * FT;
   const float* A = (const float*)g.A;
   const float* B = (const float*)g.B;
-  float acc[4][4] = {};
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < g.K; k0 += FK) {
     for (int e = t; e < FT * FK; e += 256) {
       const int m = e / FK, k = e % FK;
@@ -1377,19 +1389,26 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < FK; ++k) {
-      float a[4], b[4];
+    for (int k = 0; k < FK; k += 4) {
+      float a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = sA[k][ty * 4 + i];
+      for (int i = 0; i < 2; ++i) a[i] = sA[k + lk][wm * 32 + 16 * i + l16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = sB[k][tx * 4 + j];
+      for (int j = 0; j < 2; ++j) b[j] = sB[k + lk][wn * 32 + 16 * j + l16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
   }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sC[wm * 32 + 16 * i + 4 * lk + q][wn * 32 + 16 * j + l16] = acc[i][j][q];
+  __syncthreads();
   float* C = (float*)g.C;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1399,7 +1418,7 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
     for (int j = 0; j < 4; ++j) {
       const int col = col0 + tx * 4 + j;
       if (row < g.M && col < g.N) {
-        float v = acc[i][j];
+        float v = sC[ty * 4 + i][tx * 4 + j];
         if constexpr (EPI == EPI_RESID_SUMSQ) {
           v += ((const float*)g.E)[(int64_t)row * g.lde + col];
           s += v * v;
