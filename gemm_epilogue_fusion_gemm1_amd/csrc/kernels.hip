@@ -126,6 +126,15 @@ __device__ __forceinline__ __bf16 f2bf(float f) { return (__bf16)f; }  // round 
 #ifndef CODA_BF16_MFMA16
 #define CODA_BF16_MFMA16 1
 #endif
+// Two-stage main loops: issue a stage's loads right after the previous
+// step's barrier instead of at the start of the step before its use
+// (MXFP8, and the bf16 loop with 64-k steps)
+#ifndef CODA_MX_EARLY_ISSUE
+#define CODA_MX_EARLY_ISSUE 1
+#endif
+#ifndef CODA_BF16_EARLY_ISSUE
+#define CODA_BF16_EARLY_ISSUE 1
+#endif
 __device__ __forceinline__ void map_tile(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
   int t = wg;
@@ -571,11 +580,21 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     __syncthreads();
     read_frags(smem, 0, fa[0], fb[0]);
     read_scales(0, sa, sb);
+#if CODA_MX_EARLY_ISSUE
+    // the loads of step kt + 2 go out right after step kt's barrier (their
+    // stage, step kt's, has been read by then), a step and a quarter before
+    // they are waited for; step 1's go out here
+    static_assert(NSTAGE == 2, "early issue assumes a two-stage ring");
+    issue(1);
+    issue_scales(1);
+#endif
     for (int kt = 0; kt < nk; ++kt) {
       const char* sc = smem + (kt % NSTAGE) * STAGE_BYTES;
       const char* sn = smem + ((kt + 1) % NSTAGE) * STAGE_BYTES;
+#if !CODA_MX_EARLY_ISSUE
       issue(kt + NSTAGE - 1);
       issue_scales(kt + NSTAGE - 1);
+#endif
       read_frags(sc, 1, fa[1], fb[1]);
       CODA_MX_MFMAS(0, fa[0], fb[0], 0, FM)
       __builtin_amdgcn_sched_barrier(0);
@@ -587,6 +606,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(WAIT_NEXT);   // this wave's loads of step kt+1 have landed
       __syncthreads();
+#if CODA_MX_EARLY_ISSUE
+      issue(kt + 2);
+      issue_scales(kt + 2);
+#endif
       read_frags(sn, 0, fa[0], fb[0]);
       read_scales(kt + 1, san, sbn);
       CODA_MX_MFMAS(1, fa[1], fb[1], FM / 2, FM)
@@ -647,15 +670,22 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   __builtin_amdgcn_s_waitcnt(WAIT_NEXT);     // step 0 has landed
   __syncthreads();
   read_frags(smem, 0, fa[0], fb[0]);
+  // measured: faster with both operands K-contiguous (the LLaMA-7B dX GEMM
+  // 226 -> 218 us), slower with an N-contiguous B (the first GEMM 244 -> 256)
+  constexpr bool EARLY = CODA_BF16_EARLY_ISSUE && NSUB == 2 && NSTAGE == 2 && AK && BKM;
+  if constexpr (EARLY) issue(1);
   if constexpr (NSUB == 2) {
     // Two sub-steps: the wait and barrier go three quarters through the step
     // (after the first half of the last sub-step's MFMAs), so the next
     // stage's loads have as long to land as with four sub-steps, and the
-    // next stage's first fragments are read under the second half.
+    // next stage's first fragments are read under the second half.  EARLY:
+    // the loads of step kt + 2 go out right after step kt's barrier (their
+    // stage, step kt's, has been read by then), a step and a quarter before
+    // they are waited for.
     for (int kt = 0; kt < nk; ++kt) {
       const char* sc = smem + (kt % NSTAGE) * STAGE_BYTES;
       const char* sn = smem + ((kt + 1) % NSTAGE) * STAGE_BYTES;
-      issue(kt + NSTAGE - 1);
+      if constexpr (!EARLY) issue(kt + NSTAGE - 1);
       read_frags(sc, 1, fa[1], fb[1]);
       mfmas(fa[0], fb[0]);
       __builtin_amdgcn_sched_barrier(0);
@@ -663,6 +693,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(WAIT_NEXT);   // this wave's loads of step kt+1 have landed
       __syncthreads();
+      if constexpr (EARLY) issue(kt + 2);
       read_frags(sn, 0, fa[0], fb[0]);
       mfmas_rows(fa[1], fb[1], BFM / 2, BFM);
       __builtin_amdgcn_sched_barrier(0);
@@ -1146,6 +1177,28 @@ gemm_mx8_kernel(GemmArgs g) {
   gemm_body<FMT_MX8, WMv, WNv, 64, 2, true, true, EPI, WIN>(g);
 }
 
+// One 32-block of a row to MXFP8, shared by 4 consecutive lanes holding 8
+// values each (lanes 4j..4j+3 of the wave): the block maximum by two
+// shuffles, the shared exponent floor(log2 amax) - 8 (clamped at -127) from
+// its exponent field, the 8 values scaled by the exact power of two,
+// saturated at 448 and rounded to nearest even by the hardware conversion.
+// Returns the lane's 8 codes; `sexp` receives the exponent.
+__device__ __forceinline__ uint2 mx8_block_of_4_lanes(f32x4 lo, f32x4 hi, int& sexp) {
+  float am = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) am = fmaxf(am, fmaxf(fabsf(lo[e]), fabsf(hi[e])));
+  am = fmaxf(am, __shfl_xor(am, 1));
+  am = fmaxf(am, __shfl_xor(am, 2));
+  sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
+  const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
+  auto sat = [&](float v) { return fminf(fmaxf(v * inv, -448.0f), 448.0f); };
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[0]), sat(lo[1]), 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[2]), sat(lo[3]), w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[0]), sat(hi[1]), 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[2]), sat(hi[3]), w1, true);
+  return uint2{(uint32_t)w0, (uint32_t)w1};
+}
+
 // bf16 rows -> MXFP8 along the row.  A lane takes 8 consecutive elements
 // (one 16-byte load), 4 lanes one 32-block: shared exponent and element
 // rounding as in the first GEMM's epilogue; scales stored step-blocked
@@ -1171,20 +1224,10 @@ __global__ void mx8_quantize_kernel(const __bf16* __restrict__ src, int64_t ld, 
       lo = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
       hi = f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
     }
-    float am = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) am = fmaxf(am, fmaxf(fabsf(lo[e]), fabsf(hi[e])));
-    am = fmaxf(am, __shfl_xor(am, 1));
-    am = fmaxf(am, __shfl_xor(am, 2));
-    const int sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
-    const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
-    auto sat = [&](float v) { return fminf(fmaxf(v * inv, -448.0f), 448.0f); };
-    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[0]), sat(lo[1]), 0, false);
-    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[2]), sat(lo[3]), w0, true);
-    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[0]), sat(hi[1]), 0, false);
-    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[2]), sat(hi[3]), w1, true);
+    int sexp;
+    const uint2 w = mx8_block_of_4_lanes(lo, hi, sexp);
     if (ok) {
-      *(uint2*)(codes + row * cols + col) = uint2{(uint32_t)w0, (uint32_t)w1};
+      *(uint2*)(codes + row * cols + col) = w;
       if ((col & 31) == 0) scales[((col >> 7) * rows + row) * 4 + ((col >> 5) & 3)] = (uint8_t)(sexp + 127);
     }
   }
@@ -1239,28 +1282,6 @@ __global__ void __launch_bounds__(256) mx8_quantize_t_kernel(const __bf16* __res
     *(uint4*)(dst + 16) = uint4{w[4], w[5], w[6], w[7]};
     scales[((int64_t)blockIdx.y * cols + col) * 4 + b] = (uint8_t)(sexp + 127);
   }
-}
-
-// One 32-block of a row to MXFP8, shared by 4 consecutive lanes holding 8
-// values each (lanes 4j..4j+3 of the wave): the block maximum by two
-// shuffles, the shared exponent floor(log2 amax) - 8 (clamped at -127) from
-// its exponent field, the 8 values scaled by the exact power of two,
-// saturated at 448 and rounded to nearest even by the hardware conversion.
-// Returns the lane's 8 codes; `sexp` receives the exponent.
-__device__ __forceinline__ uint2 mx8_block_of_4_lanes(f32x4 lo, f32x4 hi, int& sexp) {
-  float am = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) am = fmaxf(am, fmaxf(fabsf(lo[e]), fabsf(hi[e])));
-  am = fmaxf(am, __shfl_xor(am, 1));
-  am = fmaxf(am, __shfl_xor(am, 2));
-  sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
-  const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
-  auto sat = [&](float v) { return fminf(fmaxf(v * inv, -448.0f), 448.0f); };
-  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[0]), sat(lo[1]), 0, false);
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[2]), sat(lo[3]), w0, true);
-  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[0]), sat(hi[1]), 0, false);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[2]), sat(hi[3]), w1, true);
-  return uint2{(uint32_t)w0, (uint32_t)w1};
 }
 
 // The MXFP8 operands of the block's backward that come from one bf16 [rows,
