@@ -74,6 +74,9 @@ What the pages fix, and the readings taken where they are silent:
     gradient straight through), each backward GEMM on MXFP8 operands quantised
     along its own contraction index, the intermediates that feed a quantiser
     (dn, n, dy) held in bf16 first, as the bf16 backward stores them.
+  * The SwiGLU block on MXFP8 (``ref_swiglu_fwd_mx8``, ``ref_swiglu_bwd_mx8``):
+    the same reading for the gate/up pattern; a = silu(g) u from the GEMM's
+    unrounded result, a and dgu held in bf16 before they are quantised.
 
 Every function here is pinned by a test against something other than itself
 (brute-force loops, finite differences, torch CPU autograd, closed forms and
@@ -93,7 +96,8 @@ __all__ = [
     "ref_rope_bwd_sampled",
     "E4M3_MAX", "MX_BLOCK", "e4m3_decode", "e4m3_encode", "e8m0_decode", "mx_quantize",
     "mx_dequantize", "ref_fwd_mx8", "ref_fwd_mx8_rows", "mx_matmul", "ref_bwd_mx8",
-    "ref_bwd_mx8_sampled",
+    "ref_bwd_mx8_sampled", "ref_swiglu_fwd_mx8", "ref_swiglu_bwd_mx8", "ref_swiglu_fwd_mx8_rows",
+    "ref_swiglu_bwd_mx8_sampled",
 ]
 
 
@@ -860,6 +864,89 @@ def ref_bwd_mx8_sampled(X, W1, gamma, W2, y, r, dz, rows, cols_d, cols_N, store=
     dR_rows = r[rows, None] * store(dn[rows]) - c[rows, None] * y[rows]
     return {"rows": rows, "cols_d": cols_d, "cols_N": cols_N, "dX_rows": dX_rows, "dR_rows": dR_rows,
             "dW1_cols": dW1_cols, "dW2_cols": dW2_cols, "dgamma": dgamma, "s": s, "c": c}
+
+
+def ref_swiglu_fwd_mx8(X, W, Wd, store=bf16_rne) -> dict:
+    """SwiGLU block with both GEMMs on MXFP8 operands quantised along their
+    contraction index (the format of ``mx_matmul``; the reading of the FP8
+    block carried over to the SwiGLU pattern, [JA] 課題; [RU] "Налог на лень"):
+      gu = mx(X, W)                 (contraction over d)
+      a  = silu(g) u, from the unrounded gu = [g | u] (the activation epilogue
+           works on the GEMM's fp32 result)
+      z  = mx(store(a), Wd)         (contraction over F; a is stored in bf16
+           and quantised from there)
+    X, W, Wd are the unquantised (bf16) inputs."""
+    X, W, Wd = map(_f64, (X, W, Wd))
+    F = W.shape[1] // 2
+    gu = mx_matmul(X, W)
+    g, u = gu[:, :F], gu[:, F:]
+    a = g * sigmoid(g) * u
+    return {"gu": gu, "a": a, "z": mx_matmul(store(a), Wd)}
+
+
+def ref_swiglu_bwd_mx8(X, W, Wd, gu, a, dz, store=bf16_rne) -> dict:
+    """Backward of ``ref_swiglu_fwd_mx8``: the gradient of the unquantised
+    block (``ref_swiglu_bwd``; quantisation passes it straight through), each
+    GEMM on MXFP8 operands quantised along its own contraction index:
+      da  = mx(dz, Wd^T)            (contraction over d)
+      dg  = da u sg (1 + g (1 - sg)), du = da g sg, sg = sigmoid(g), from the
+            saved gu = [g | u];  dgu = [dg | du]
+      dWd = mx(a^T, dz)             (contraction over M; a the saved a)
+      dX  = mx(store(dgu), W^T)     (contraction over 2F)
+      dW  = mx(X^T, store(dgu))     (contraction over M)
+    ``store`` is the storage of dgu before it is quantised (bf16)."""
+    X, W, Wd, gu, a, dz = map(_f64, (X, W, Wd, gu, a, dz))
+    F = W.shape[1] // 2
+    g, u = gu[:, :F], gu[:, F:]
+    sg = sigmoid(g)
+    da = mx_matmul(dz, Wd.T)
+    dgu = np.concatenate([da * u * sg * (1.0 + g * (1.0 - sg)), da * g * sg], axis=1)
+    dgu_s = store(dgu)
+    return {"dX": mx_matmul(dgu_s, W.T), "dW": mx_matmul(X.T, dgu_s), "dWd": mx_matmul(a.T, dz),
+            "dgu": dgu, "da": da}
+
+
+def ref_swiglu_fwd_mx8_rows(X, W, Wd, rows, store=bf16_rne) -> dict:
+    """``ref_swiglu_fwd_mx8`` for the given rows only (X's blocks run along
+    its rows, a's along its rows: every step is row-local)."""
+    rows = np.asarray(rows)
+    out = ref_swiglu_fwd_mx8(_f64(X)[rows], W, Wd, store)
+    out["rows"] = rows
+    return out
+
+
+def ref_swiglu_bwd_mx8_sampled(X, W, Wd, dz, rows, cols_W, rows_Wd, store=bf16_rne) -> dict:
+    """``ref_swiglu_bwd_mx8`` restricted: dX and dgu on ``rows``, dW on the
+    columns ``cols_W`` (indices into [0, 2F)), dWd on the rows ``rows_Wd``
+    (indices into [0, F)), with the saved gu and a those of
+    ``ref_swiglu_fwd_mx8`` rounded by ``store`` (recomputed here where needed).
+
+    The columns of a product with B's blocks along the contraction index are
+    independent (mx(A, B[:, c]) = mx(A, B)[:, c]), and so are the rows of one
+    with A's blocks along it; a column of dW needs that column of dgu over
+    every row (its blocks run along M)."""
+    X, W, Wd, dz = map(_f64, (X, W, Wd, dz))
+    F = W.shape[1] // 2
+    rows, cols_W, rows_Wd = map(np.asarray, (rows, cols_W, rows_Wd))
+    # rows: dgu and dX for these tokens (row-local: blocks along d and 2F)
+    gu_r = store(ref_swiglu_fwd_mx8(X[rows], W, Wd, store)["gu"])
+    g_r, u_r = gu_r[:, :F], gu_r[:, F:]
+    sg_r = sigmoid(g_r)
+    da_r = mx_matmul(dz[rows], Wd.T)
+    dgu_r = np.concatenate([da_r * u_r * sg_r * (1.0 + g_r * (1.0 - sg_r)), da_r * g_r * sg_r], axis=1)
+    # dW columns: dgu[:, c] over every token
+    jg = cols_W % F
+    g = store(mx_matmul(X, W[:, jg]))
+    u = store(mx_matmul(X, W[:, F + jg]))
+    da = mx_matmul(dz, Wd[jg, :].T)
+    sg = sigmoid(g)
+    dgu_c = np.where((cols_W < F)[None, :], da * u * sg * (1.0 + g * (1.0 - sg)), da * g * sg)
+    # dWd rows: a[:, j] over every token
+    gj = mx_matmul(X, W[:, rows_Wd])
+    uj = mx_matmul(X, W[:, F + rows_Wd])
+    a_c = store(gj * sigmoid(gj) * uj)
+    return {"rows": rows, "cols_W": cols_W, "rows_Wd": rows_Wd, "dX_rows": mx_matmul(store(dgu_r), W.T),
+            "dgu_rows": dgu_r, "dW_cols": mx_matmul(X.T, store(dgu_c)), "dWd_rows": mx_matmul(a_c.T, dz)}
 
 
 def ref_fwd_mx8_rows(Xq, Xs, W1q, W1s, R, gamma, W2q, W2s, eps: float, rows) -> dict:

@@ -1208,6 +1208,107 @@ def pin_bwd_mx8_sampled(O):
     _close(sm["dgamma"], full["dgamma"], 1e-12, "mx8 sampled dgamma")
 
 
+def _swiglu_mx8_case(seed, M, d, F):
+    g = _rng(seed)
+    return dict(X=g.standard_normal((M, d)), W=g.standard_normal((d, 2 * F)) / math.sqrt(d),
+                Wd=g.standard_normal((F, d)) / math.sqrt(F), dz=g.standard_normal((M, d)))
+
+
+def pin_swiglu_mx8_bruteforce(O):
+    """The MXFP8 SwiGLU forward and backward by pure-Python loops (every
+    dimension whole 32-blocks): each GEMM's operands quantised along its
+    contraction index from the format's bit fields, a = silu(g) u from the
+    unrounded gu, a and dgu rounded to bf16 before they are quantised."""
+    tab = _e4m3_table()
+    M, d, F = 64, 64, 32
+    c = _swiglu_mx8_case(95, M, d, F)
+    X, W, Wd, dz = (c[k].tolist() for k in ("X", "W", "Wd", "dz"))
+    sig = lambda t: 1.0 / (1.0 + math.exp(-t))  # noqa: E731
+    gu = _mx_matmul_loop(X, W, tab)
+    a = [[gu[i][j] * sig(gu[i][j]) * gu[i][F + j] for j in range(F)] for i in range(M)]
+    a_s = [[_bf16_loop(v) for v in row] for row in a]
+    z = _mx_matmul_loop(a_s, Wd, tab)
+    f = O.ref_swiglu_fwd_mx8(c["X"], c["W"], c["Wd"])
+    _close(f["gu"], np.array(gu), 1e-12, "swiglu mx8 gu vs loops")
+    _close(f["a"], np.array(a), 1e-12, "swiglu mx8 a vs loops")
+    _close(f["z"], np.array(z), 1e-12, "swiglu mx8 z vs loops")
+    gu_s = [[_bf16_loop(v) for v in row] for row in gu]
+    b = O.ref_swiglu_bwd_mx8(c["X"], c["W"], c["Wd"], np.array(gu_s), np.array(a_s), c["dz"])
+    WdT = [[Wd[j][k] for j in range(F)] for k in range(d)]            # [d][F]
+    da = _mx_matmul_loop(dz, WdT, tab)
+    dgu = []
+    for i in range(M):
+        row_g, row_u = [], []
+        for j in range(F):
+            g_, u_ = gu_s[i][j], gu_s[i][F + j]
+            sg = sig(g_)
+            row_g.append(da[i][j] * u_ * sg * (1.0 + g_ * (1.0 - sg)))
+            row_u.append(da[i][j] * g_ * sg)
+        dgu.append(row_g + row_u)
+    dgu_s = [[_bf16_loop(v) for v in row] for row in dgu]
+    aT = [[a_s[i][j] for i in range(M)] for j in range(F)]
+    WT = [[W[k][j] for k in range(d)] for j in range(2 * F)]
+    XT = [[X[i][k] for i in range(M)] for k in range(d)]
+    _close(b["da"], np.array(da), 1e-12, "swiglu mx8 da vs loops")
+    _close(b["dgu"], np.array(dgu), 1e-12, "swiglu mx8 dgu vs loops")
+    _close(b["dWd"], np.array(_mx_matmul_loop(aT, dz, tab)), 1e-12, "swiglu mx8 dWd vs loops")
+    _close(b["dX"], np.array(_mx_matmul_loop(dgu_s, WT, tab)), 1e-12, "swiglu mx8 dX vs loops")
+    _close(b["dW"], np.array(_mx_matmul_loop(XT, dgu_s, tab)), 1e-12, "swiglu mx8 dW vs loops")
+
+
+def _mx_grid_both(g, shape):
+    """A matrix exactly representable in MXFP8 along both axes: E4M3 values
+    times one power of two, with |v| = 256 wherever i % 32 == j % 32, so that
+    every 32-block of a row and of a column has its maximum in [256, 448]."""
+    tab = _e4m3_table()
+    vals = np.array(sorted(v for v in tab.values() if abs(v) <= 256.0))
+    out = g.choice(vals, size=shape)
+    i, j = np.indices(shape)
+    out[(i % 32) == (j % 32)] = 256.0 * g.choice([-1.0, 1.0], size=int(np.sum((i % 32) == (j % 32))))
+    return out * 2.0 ** -12
+
+
+def pin_swiglu_mx8_grid_exact(O):
+    """With operands on the MXFP8 grid the quantised products are exact, so
+    the MXFP8 SwiGLU reduces to the pinned ref_swiglu_fwd / ref_swiglu_bwd:
+    gu and a (X, W on the grid along d); da, dgu (dz, Wd on the grid along d)
+    and dWd (the saved a and dz on the grid along M)."""
+    g = _rng(96)
+    M, d, F = 64, 64, 96
+    X = _mx_grid(g, (M, d))
+    W = _mx_grid(g, (2 * F, d)).T.copy()
+    Wd = _mx_grid(g, (F, d))
+    dz = _mx_grid_both(g, (M, d))
+    a_saved = _mx_grid(g, (F, M)).T.copy()
+    q = O.ref_swiglu_fwd_mx8(X, W, Wd, store=lambda v: v)
+    e = O.ref_swiglu_fwd(X, W, Wd)
+    _close(q["gu"], e["gu"], 1e-13, "swiglu mx8 gu on grid operands")
+    _close(q["a"], e["a"], 1e-13, "swiglu mx8 a on grid operands")
+    qb = O.ref_swiglu_bwd_mx8(X, W, Wd, e["gu"], a_saved, dz, store=lambda v: v)
+    eb = O.ref_swiglu_bwd(X, W, Wd, e["gu"], a_saved, dz)
+    for k in ("da", "dgu", "dWd"):
+        _close(qb[k], eb[k], 1e-13, f"swiglu mx8 {k} on grid operands")
+
+
+def pin_swiglu_mx8_sampled(O):
+    """The sampled forms equal slices of the full MXFP8 SwiGLU forward and
+    backward (with the saved gu and a rounded to bf16)."""
+    M, d, F = 96, 64, 64
+    c = _swiglu_mx8_case(97, M, d, F)
+    f = O.ref_swiglu_fwd_mx8(c["X"], c["W"], c["Wd"])
+    rows = np.array([0, 33, 95])
+    fr = O.ref_swiglu_fwd_mx8_rows(c["X"], c["W"], c["Wd"], rows)
+    for k in ("gu", "a", "z"):
+        _close(fr[k], f[k][rows], 1e-13, f"swiglu mx8 rows {k}")
+    b = O.ref_swiglu_bwd_mx8(c["X"], c["W"], c["Wd"], O.bf16_rne(f["gu"]), O.bf16_rne(f["a"]), c["dz"])
+    cols_W, rows_Wd = np.array([0, 63, 64, 127]), np.array([1, 62])
+    sm = O.ref_swiglu_bwd_mx8_sampled(c["X"], c["W"], c["Wd"], c["dz"], rows, cols_W, rows_Wd)
+    _close(sm["dX_rows"], b["dX"][rows], 1e-12, "swiglu mx8 sampled dX rows")
+    _close(sm["dgu_rows"], b["dgu"][rows], 1e-12, "swiglu mx8 sampled dgu rows")
+    _close(sm["dW_cols"], b["dW"][:, cols_W], 1e-12, "swiglu mx8 sampled dW cols")
+    _close(sm["dWd_rows"], b["dWd"][rows_Wd], 1e-12, "swiglu mx8 sampled dWd rows")
+
+
 ALL_PINS = [
     pin_fwd_bruteforce, pin_fwd_torch_rmsnorm, pin_fwd_constant_rows,
     pin_fwd_scale_invariance, pin_partials, pin_rewrite_equals_unfused,
@@ -1222,5 +1323,6 @@ ALL_PINS = [
     pin_rope_sampled,
     pin_bwd_dy_in_finite_differences, pin_e4m3_codes, pin_mx_quantize, pin_fwd_mx8_exact,
     pin_fwd_mx8_bruteforce, pin_fwd_mx8_rows, pin_mx_matmul, pin_bwd_mx8_bruteforce,
-    pin_bwd_mx8_grid_exact, pin_bwd_mx8_sampled,
+    pin_bwd_mx8_grid_exact, pin_bwd_mx8_sampled, pin_swiglu_mx8_bruteforce, pin_swiglu_mx8_grid_exact,
+    pin_swiglu_mx8_sampled,
 ]

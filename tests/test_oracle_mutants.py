@@ -228,6 +228,45 @@ def _bwd_mx8_variant(kind):
     return bwd
 
 
+def _swiglu_fwd_mx8_variant(kind):
+    def fwd(X, W, Wd, store=oracle.bf16_rne):
+        X64, W64, Wd64 = _f(X, W, Wd)
+        F = W64.shape[1] // 2
+        if kind == "W_along_output":
+            xq, xs = oracle.mx_quantize(X64)
+            wq, ws = oracle.mx_quantize(W64)                              # blocks along 2F, not d
+            gu = oracle.mx_dequantize(xq, xs) @ oracle.mx_dequantize(wq, ws)
+        else:
+            gu = oracle.mx_matmul(X64, W64)
+        g, u = gu[:, :F], gu[:, F:]
+        if kind == "a_from_stored_gu":
+            g, u = store(g), store(u)
+        a = g * oracle.sigmoid(g) * u
+        z = oracle.mx_matmul(a if kind == "a_unstored" else store(a), Wd64)
+        return {"gu": gu, "a": a, "z": z}
+    return fwd
+
+
+def _swiglu_bwd_mx8_variant(kind):
+    def bwd(X, W, Wd, gu, a, dz, store=oracle.bf16_rne):
+        out = dict(oracle.ref_swiglu_bwd_mx8(X, W, Wd, gu, a, dz, store))
+        X64, W64, a64, dz64, gu64 = _f(X, W, a, dz, gu)
+        F = W64.shape[1] // 2
+        if kind == "dWd_a_along_F":
+            aq, as_ = oracle.mx_quantize(a64)                             # blocks along F, not M
+            dq, ds = oracle.mx_quantize(np.ascontiguousarray(dz64.T))
+            out["dWd"] = oracle.mx_dequantize(aq, as_).T @ oracle.mx_dequantize(dq, ds).T
+        elif kind == "dgu_unstored":
+            out["dX"] = oracle.mx_matmul(out["dgu"], W64.T)
+            out["dW"] = oracle.mx_matmul(X64.T, out["dgu"])
+        elif kind == "du_sign":
+            g = gu64[:, :F]
+            du = -out["da"] * g * oracle.sigmoid(g)
+            out["dgu"] = np.concatenate([out["dgu"][:, :F], du], axis=1)
+        return out
+    return bwd
+
+
 def ce_partials_no_rescale(logits, BN=256):
     out = dict(oracle.ref_ce_partials(logits, BN))
     x = np.asarray(logits, dtype=np.float64)
@@ -423,6 +462,12 @@ MUTANTS = {
     "mx8_bwd_dX_W1_quantised_along_K": {"ref_bwd_mx8": _bwd_mx8_variant("dX_W1_along_K")},
     "mx8_bwd_dy_quantised_unstored": {"ref_bwd_mx8": _bwd_mx8_variant("dy_not_stored")},
     "mx8_bwd_dgamma_from_stored_n": {"ref_bwd_mx8": _bwd_mx8_variant("dgamma_from_stored_n")},
+    "swiglu_mx8_W_quantised_along_output": {"ref_swiglu_fwd_mx8": _swiglu_fwd_mx8_variant("W_along_output")},
+    "swiglu_mx8_a_from_stored_gu": {"ref_swiglu_fwd_mx8": _swiglu_fwd_mx8_variant("a_from_stored_gu")},
+    "swiglu_mx8_z_from_unstored_a": {"ref_swiglu_fwd_mx8": _swiglu_fwd_mx8_variant("a_unstored")},
+    "swiglu_mx8_dWd_a_quantised_along_F": {"ref_swiglu_bwd_mx8": _swiglu_bwd_mx8_variant("dWd_a_along_F")},
+    "swiglu_mx8_dgu_quantised_unstored": {"ref_swiglu_bwd_mx8": _swiglu_bwd_mx8_variant("dgu_unstored")},
+    "swiglu_mx8_du_sign": {"ref_swiglu_bwd_mx8": _swiglu_bwd_mx8_variant("du_sign")},
     "e8m0_off_by_one": {"e8m0_decode": e8m0_off_by_one},
 }
 
