@@ -400,6 +400,72 @@ class Mx8Case:
         return float((y.float() - self.y.float()).abs().max() / self.y.float().abs().max())
 
 
+class SwigluMx8Case(Mx8Case):
+    """The SwiGLU block forward+backward with every GEMM on MXFP8 operands.
+    The calls take the bf16 tensors and quantise them.  The unfused step is
+    the same computation as torch ops: each GEMM torch's MXFP8 product on
+    operands quantised by torch ops along the contraction index, the
+    activation and its backward elementwise."""
+
+    def __init__(self, w, torch, coda, h):
+        dev = torch.device("cuda:0")
+        self.w, self.torch, self.coda = w, torch, coda
+        bf = torch.bfloat16
+        self.t = {k: torch.from_numpy(v).to(dev).to(bf) for k, v in h.items()}
+        M, d, F = w.M, w.d, w.F
+        self.gu = torch.empty((M, 2 * F), dtype=bf, device=dev)
+        self.a = torch.empty((M, F), dtype=bf, device=dev)
+        self.z = torch.empty((M, d), dtype=bf, device=dev)
+        self.dX = torch.empty((M, d), dtype=bf, device=dev)
+        self.dW = torch.empty((d, 2 * F), dtype=bf, device=dev)
+        self.dWd = torch.empty((F, d), dtype=bf, device=dev)
+        self.ws = torch.empty(coda.swiglu_fwd_mx8_workspace_bytes(M, d, F), dtype=torch.uint8, device=dev)
+        self.wsb = torch.empty(coda.swiglu_bwd_mx8_workspace_bytes(M, d, F), dtype=torch.uint8, device=dev)
+        self.backward = w.backward
+        self.kernels_per_step = 5 + 10
+        self.leaf_names = ("X",)
+        self.manual_bwd = True
+
+    def fused_fwd(self):
+        t = self.t
+        self.coda.coda_swiglu_fwd_mx8(t["X"], t["W"], t["Wd"], self.gu, self.a, self.z, self.ws)
+
+    def fused_bwd(self):
+        t = self.t
+        self.coda.coda_swiglu_bwd_mx8(t["X"], t["W"], t["Wd"], self.gu, self.a, t["dz"], self.dX, self.dW,
+                                      self.dWd, self.wsb)
+
+    def unfused_fwd(self):
+        t, q, c = self.t, self._quantise, lambda v: v.contiguous()  # noqa: E731
+        F = self.w.F
+        gu = self._mm(q(t["X"]), q(c(t["W"].t())))
+        g, u = gu[:, :F], gu[:, F:]
+        a = self.torch.nn.functional.silu(g) * u
+        self._saved = (gu, a)
+        return self._mm(q(a), q(c(t["Wd"].t())))
+
+    def unfused_bwd_manual(self):
+        t, q, c = self.t, self._quantise, lambda v: v.contiguous()  # noqa: E731
+        F = self.w.F
+        gu, a = self._saved if hasattr(self, "_saved") else (self.gu, self.a)
+        g, u = gu[:, :F].float(), gu[:, F:].float()
+        da = self._mm(q(t["dz"]), q(t["Wd"])).float()
+        sg = self.torch.sigmoid(g)
+        dgu = self.torch.cat([da * u * sg * (1.0 + g * (1.0 - sg)), da * g * sg], dim=1).to(self.torch.bfloat16)
+        dWd = self._mm(q(c(a.t())), q(c(t["dz"].t())))
+        dX = self._mm(q(dgu), q(t["W"]))
+        dW = self._mm(q(c(t["X"].t())), q(c(dgu.t())))
+        return dX, dW, dWd
+
+    def unfused_check(self):
+        """Relative difference between torch's first MXFP8 product and the
+        fused gu (the same operands)."""
+        self.fused_fwd()
+        gu = self._mm(self._quantise(self.t["X"]), self._quantise(self.t["W"].t().contiguous()))
+        self.torch.cuda.synchronize()
+        return float((gu.float() - self.gu.float()).abs().max() / self.gu.float().abs().max())
+
+
 class _Steps:
     """The fused and unfused step functions of a case: forward, backward, and
     the training step (forward + backward; the forward alone for a
@@ -455,7 +521,7 @@ def make_case(w, torch, coda):
     from gemm_epilogue_fusion_gemm1_amd import synth
     h = synth.workload_inputs(w)
     cls = {"coda": CodaCase, "swiglu": SwigluCase, "mlp": MlpCase, "ce": CeCase, "rope": RopeCase,
-           "mx8": Mx8Case}[w.kind]
+           "mx8": Mx8Case, "swiglu_mx8": SwigluMx8Case}[w.kind]
     return cls(w, torch, coda, h), h
 
 
@@ -593,7 +659,7 @@ def summary(case, res):
         out["speedup_vs_compiled_unfused"] = round(res["compiled_ms_per_step"] / res["ms_per_step"], 3)
     if "compiled_error" in res:
         out["compiled_unfused_error"] = res["compiled_error"]
-    if case.w.kind == "mx8":
+    if case.w.kind in ("mx8", "swiglu_mx8"):
         out["pct_fp8_peak"] = round(100.0 * tf / PEAK_FP8_TFLOPS, 2)
     for part, fl in (("fwd", case.w.flops_fwd()), ("bwd", case.w.flops_bwd())):
         if f"{part}_ms" in res:
@@ -826,8 +892,13 @@ def cpu_baseline(w, h, target_s):
 # The workloads timed besides the main one.  The 70B-hidden block is part of
 # the headline metric; the rest are the other fused patterns.
 HEADLINE_SECOND = "llama70b_fwdbwd"
+# the C-ABI calls one step makes, per workload kind
+STEP_CALLS = {"coda": "coda_fwd + coda_bwd", "swiglu": "coda_swiglu_fwd + coda_swiglu_bwd",
+              "mlp": "coda_mlp_fwd + coda_mlp_bwd", "ce": "coda_ce_fwd + coda_ce_bwd",
+              "rope": "coda_rope_fwd + coda_rope_bwd", "mx8": "coda_fwd_mx8 + coda_bwd_mx8",
+              "swiglu_mx8": "coda_swiglu_fwd_mx8 + coda_swiglu_bwd_mx8"}
 ALSO = ("swiglu_fwdbwd", "llama7b_mlp_fwdbwd", "llama7b_ce_fwdbwd", "llama3_8b_ce_fwdbwd",
-        "llama7b_qkv_rope_fwdbwd", "llama7b_fwd_mx8", "llama7b_fwdbwd_mx8", "llama1b_fwd")
+        "llama7b_qkv_rope_fwdbwd", "llama7b_fwd_mx8", "llama7b_fwdbwd_mx8", "swiglu_fwdbwd_mx8", "llama1b_fwd")
 
 
 def _brief(s):
@@ -936,10 +1007,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic (seeded normal inputs)",
-        "config": {"workload": w.name, "M": w.M, "K": w.K, "d": w.d, "N": w.N, "eps": w.eps,
-                   "step": "coda_fwd + coda_bwd", "parallelism": "single GPU"},
+        "config": {"workload": w.name,
+                   **{k: getattr(w, k) for k in ("M", "K", "d", "N", "F") if getattr(w, k, 0)},
+                   **({"eps": w.eps} if w.kind in ("coda", "mlp", "mx8") else {}),
+                   "step": STEP_CALLS[w.kind] if w.backward else STEP_CALLS[w.kind].split(" + ")[0],
+                   "parallelism": "single GPU"},
         "headline": headline,
         "roofline": rf,
         "cpu_baseline": cpu,

@@ -38,7 +38,8 @@ __all__ = [
     "rope_bwd", "rope_fwd_workspace_bytes", "rope_bwd_workspace_bytes", "fwd_workspace_bytes", "bwd_workspace_bytes",
     "swiglu_bwd_workspace_bytes", "mlp_fwd_workspace_bytes", "mlp_bwd_workspace_bytes",
     "coda_mx8_quantize", "coda_fwd_mx8", "mx8_quantize", "fwd_mx8", "fwd_mx8_workspace_bytes",
-    "coda_bwd_mx8", "bwd_mx8", "bwd_mx8_workspace_bytes",
+    "coda_bwd_mx8", "bwd_mx8", "bwd_mx8_workspace_bytes", "coda_swiglu_fwd_mx8", "coda_swiglu_bwd_mx8",
+    "swiglu_fwd_mx8", "swiglu_bwd_mx8", "swiglu_fwd_mx8_workspace_bytes", "swiglu_bwd_mx8_workspace_bytes",
     "mx8_scales_to_rowmajor", "mx8_scales_from_rowmajor",
     "version", "trace_start", "trace_read", "trace_stop",
 ]
@@ -94,6 +95,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "coda_rope_bwd_workspace_bytes": [i32, i64, i64, i64, i64, i64, i64],
         "coda_fwd_mx8_workspace_bytes": [i64, i64, i64, i64],
         "coda_bwd_mx8_workspace_bytes": [i64, i64, i64, i64],
+        "coda_swiglu_fwd_mx8_workspace_bytes": [i64, i64, i64],
+        "coda_swiglu_bwd_mx8_workspace_bytes": [i64, i64, i64],
     }.items():
         getattr(L, name).restype = sz
         getattr(L, name).argtypes = args
@@ -123,6 +126,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     L.coda_mx8_quantize.argtypes = [i64, i64, vp, i64, vp, vp, vp]
     L.coda_bwd_mx8.restype = i32
     L.coda_bwd_mx8.argtypes = [i64, i64, i64, i64] + [vp] * 12 + [vp, sz, vp]
+    L.coda_swiglu_fwd_mx8.restype = i32
+    L.coda_swiglu_fwd_mx8.argtypes = [i64, i64, i64] + [vp] * 6 + [vp, sz, vp]
+    L.coda_swiglu_bwd_mx8.restype = i32
+    L.coda_swiglu_bwd_mx8.argtypes = [i64, i64, i64] + [vp] * 9 + [vp, sz, vp]
     L.coda_fwd_mx8.restype = i32
     L.coda_fwd_mx8.argtypes = [i64, i64, i64, i64, f32] + [vp] * 11 + [vp, sz, vp]
     L.coda_trace_start.restype = i32
@@ -502,6 +509,35 @@ def coda_bwd_mx8(X, W1, gamma, W2, y, r, dz, dX, dW1, dR, dW2, dgamma, workspace
     _check("coda_bwd_mx8", load_library().coda_bwd_mx8(M, K, d, N, *p, wp, wn, _stream()))
 
 
+def coda_swiglu_fwd_mx8(X, W, Wd, gu, a, z, workspace):
+    """coda_swiglu_fwd_mx8: the SwiGLU block forward on MXFP8 GEMM operands
+    (bf16 tensors in and out, as coda_swiglu_fwd)."""
+    import torch
+    c = _Args("coda_swiglu_fwd_mx8", X, "X")
+    bf = torch.bfloat16
+    M, d = X.shape
+    F = Wd.shape[0]
+    p = [c(X, "X", (M, d), bf), c(W, "W", (d, 2 * F), bf), c(Wd, "Wd", (F, d), bf),
+         c(gu, "gu", (M, 2 * F), bf), c(a, "a", (M, F), bf), c(z, "z", (M, d), bf)]
+    wp, wn = c.ws(workspace)
+    _check("coda_swiglu_fwd_mx8", load_library().coda_swiglu_fwd_mx8(M, d, F, *p, wp, wn, _stream()))
+
+
+def coda_swiglu_bwd_mx8(X, W, Wd, gu, a, dz, dX, dW, dWd, workspace):
+    """coda_swiglu_bwd_mx8: the SwiGLU block backward on MXFP8 GEMM operands
+    (bf16 tensors in and out, as coda_swiglu_bwd)."""
+    import torch
+    c = _Args("coda_swiglu_bwd_mx8", X, "X")
+    bf = torch.bfloat16
+    M, d = X.shape
+    F = Wd.shape[0]
+    p = [c(X, "X", (M, d), bf), c(W, "W", (d, 2 * F), bf), c(Wd, "Wd", (F, d), bf),
+         c(gu, "gu", (M, 2 * F), bf), c(a, "a", (M, F), bf), c(dz, "dz", (M, d), bf),
+         c(dX, "dX", (M, d), bf), c(dW, "dW", (d, 2 * F), bf), c(dWd, "dWd", (F, d), bf)]
+    wp, wn = c.ws(workspace)
+    _check("coda_swiglu_bwd_mx8", load_library().coda_swiglu_bwd_mx8(M, d, F, *p, wp, wn, _stream()))
+
+
 # ------------------------------------------------------ convenience calls
 
 def mx8_scales_to_rowmajor(scales):
@@ -564,6 +600,42 @@ def bwd_mx8(X, W1, gamma, W2, y, r, dz):
     ws = _workspace(bwd_mx8_workspace_bytes(M, K, d, N), X.device)
     coda_bwd_mx8(X, W1, gamma, W2, y, r, dz, dX, dW1, dR, dW2, dgamma, ws)
     return dX, dW1, dR, dW2, dgamma
+
+
+def swiglu_fwd_mx8_workspace_bytes(M, d, F) -> int:
+    return int(load_library().coda_swiglu_fwd_mx8_workspace_bytes(M, d, F))
+
+
+def swiglu_bwd_mx8_workspace_bytes(M, d, F) -> int:
+    return int(load_library().coda_swiglu_bwd_mx8_workspace_bytes(M, d, F))
+
+
+def swiglu_fwd_mx8(X, W, Wd):
+    """The SwiGLU block forward with both GEMMs on MXFP8 operands (bf16 in and
+    out).  Returns (z, gu, a)."""
+    import torch
+    M, d = X.shape
+    F = Wd.shape[0]
+    gu = torch.empty((M, 2 * F), dtype=X.dtype, device=X.device)
+    a = torch.empty((M, F), dtype=X.dtype, device=X.device)
+    z = torch.empty((M, d), dtype=X.dtype, device=X.device)
+    ws = _workspace(swiglu_fwd_mx8_workspace_bytes(M, d, F), X.device)
+    coda_swiglu_fwd_mx8(X, W, Wd, gu, a, z, ws)
+    return z, gu, a
+
+
+def swiglu_bwd_mx8(X, W, Wd, gu, a, dz):
+    """The SwiGLU block backward with every GEMM on MXFP8 operands.  Returns
+    (dX, dW, dWd)."""
+    import torch
+    M, d = X.shape
+    F = Wd.shape[0]
+    dX = torch.empty_like(X)
+    dW = torch.empty((d, 2 * F), dtype=X.dtype, device=X.device)
+    dWd = torch.empty((F, d), dtype=X.dtype, device=X.device)
+    ws = _workspace(swiglu_bwd_mx8_workspace_bytes(M, d, F), X.device)
+    coda_swiglu_bwd_mx8(X, W, Wd, gu, a, dz, dX, dW, dWd, ws)
+    return dX, dW, dWd
 
 
 def fwd(X, W1, R, gamma, W2, eps):

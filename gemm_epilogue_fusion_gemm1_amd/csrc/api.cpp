@@ -1231,3 +1231,198 @@ coda_status coda_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, const void*
 }
 
 }  // extern "C"
+
+namespace {
+// Workspaces of the MXFP8 SwiGLU block: every GEMM operand in MXFP8 (codes
+// and step-blocked scales) and, in the backward, dgu.
+struct SwigluMx8Ws {
+  size_t xq, xs, wq, ws, wdq, wds, aq, as, total;          // forward
+  size_t dzq, dzs, dzTq, dzTs, wdrq, wdrs, dgu, aTq, aTs, dguq, dgus, dguTq, dguTs, wrq, wrs, XTq, XTs;
+};
+SwigluMx8Ws swiglu_mx8_ws(int64_t M, int64_t d, int64_t F, bool bwd) {
+  SwigluMx8Ws w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += round_up(bytes); return at; };
+  auto mx = [&](size_t rows, size_t k, size_t& q, size_t& sc) { q = take(rows * k); sc = take(rows * (k / 32)); };
+  if (!bwd) {
+    mx(M, d, w.xq, w.xs);            // X along d
+    mx(2 * F, d, w.wq, w.ws);        // W along d, transposed, gate/up order
+    mx(d, F, w.wdq, w.wds);          // Wd along F, transposed
+    mx(M, F, w.aq, w.as);            // a along F (from the gate/up GEMM's epilogue)
+  } else {
+    mx(M, d, w.dzq, w.dzs);          // dz along d
+    mx(d, M, w.dzTq, w.dzTs);        // dz along M, transposed
+    mx(F, d, w.wdrq, w.wdrs);        // Wd along d
+    w.dgu = take((size_t)M * 2 * F * 2);
+    mx(F, M, w.aTq, w.aTs);          // a along M, transposed
+    mx(M, 2 * F, w.dguq, w.dgus);    // dgu along 2F
+    mx(2 * F, M, w.dguTq, w.dguTs);  // dgu along M, transposed
+    mx(d, 2 * F, w.wrq, w.wrs);      // W along 2F
+    mx(d, M, w.XTq, w.XTs);          // X along M, transposed
+  }
+  w.total = o;
+  return w;
+}
+bool swiglu_mx8_shape_ok(int64_t M, int64_t d, int64_t F) {
+  return mx_rows_ok(M, 128) && mx_dim_ok(d, 128) && mx_dim_ok(F, 128) && mx_dim_ok(2 * F, 128) &&
+         fits(M, 2 * F, 2) && fits(d, 2 * F, 2) && scales_fit(M, 2 * F) && scales_fit(2 * F, M) &&
+         scales_fit(d, 2 * F) && scales_fit(2 * F, d) && scales_fit(M, d) && scales_fit(d, M) &&
+         scales_fit(F, M) && scales_fit(M, F) && scales_fit(F, d) && scales_fit(d, F);
+}
+}  // namespace
+
+extern "C" {
+
+size_t coda_swiglu_fwd_mx8_workspace_bytes(int64_t M, int64_t d, int64_t F) {
+  if (!swiglu_mx8_shape_ok(M, d, F)) return 0;
+  return swiglu_mx8_ws(M, d, F, false).total;
+}
+
+size_t coda_swiglu_bwd_mx8_workspace_bytes(int64_t M, int64_t d, int64_t F) {
+  if (!swiglu_mx8_shape_ok(M, d, F)) return 0;
+  return swiglu_mx8_ws(M, d, F, true).total;
+}
+
+coda_status coda_swiglu_fwd_mx8(int64_t M, int64_t d, int64_t F, const void* X, const void* W,
+                                const void* Wd, void* gu, void* a, void* z, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!X || !W || !Wd || !gu || !a || !z) return CODA_ERR_NULL;
+  if (!swiglu_mx8_shape_ok(M, d, F)) return CODA_ERR_SHAPE;
+  for (const void* p : {X, W, Wd, (const void*)gu, (const void*)a, (const void*)z})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  const SwigluMx8Ws ws = swiglu_mx8_ws(M, d, F, false);
+  if (!workspace || workspace_bytes < ws.total) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const size_t e = 2;
+  const Range in[] = {rng(X, M * d * e), rng(W, d * 2 * F * e), rng(Wd, F * d * e)};
+  const Range out[] = {rng(gu, M * 2 * F * e), rng(a, M * F * e), rng(z, M * d * e), rng(workspace, ws.total)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wb = (char*)workspace;
+  auto u8 = [&](size_t off) { return (uint8_t*)(wb + off); };
+  hipError_t err;
+  const double q8 = 1.0 + 1.0 / 32.0, Md = (double)M * d, dF = (double)d * F, MF = (double)M * F;
+  // operands: X along d; W along d, transposed into gate/up order; Wd along F, transposed
+  if ((err = traced("x1_mx8_quantize_X", 0.0, Md * (e + q8), s, [&] {
+         return coda::launch_mx8_quantize(X, d, M, d, u8(ws.xq), u8(ws.xs), s);
+       })) != hipSuccess)
+    return hip_status(err);
+  coda::MxQuantArgs qw{};
+  qw.src = W;
+  qw.ld = 2 * F;
+  qw.rows = d;
+  qw.cols = 2 * F;
+  qw.qt = u8(ws.wq);
+  qw.st = u8(ws.ws);
+  qw.gated_F = F;
+  if ((err = traced("x2_mx8_quantize_W_gateup", 0.0, 2.0 * dF * (e + q8), s,
+                    [&] { return coda::launch_mx8_quantize_fused(qw, 0, s); })) != hipSuccess)
+    return hip_status(err);
+  if ((err = traced("x3_mx8_quantize_WdT", 0.0, dF * (e + q8), s, [&] {
+         return coda::launch_mx8_quantize_t(Wd, d, F, d, u8(ws.wdq), u8(ws.wds), s);
+       })) != hipSuccess)
+    return hip_status(err);
+  // S1: [g | u] = X W on MXFP8; epilogue gu, a = silu(g) u (bf16) and a to MXFP8 along F
+  GemmArgs s1 = gemm_mx8(M, F, d, u8(ws.xq), u8(ws.xs), u8(ws.wq), u8(ws.ws), gu, 2 * F);
+  s1.B_total = (uint64_t)(2 * F * d);
+  s1.B_bytes = (uint32_t)std::min<uint64_t>(s1.B_total, 0x7FFFFFF0ull);
+  s1.sB_bytes = (uint32_t)(2 * F * (d / 32));
+  s1.C2 = a;
+  s1.ldc2 = F;
+  s1.F = (int)F;
+  s1.q_out = u8(ws.aq);
+  s1.qs_out = u8(ws.as);
+  s1.ldq = F;
+  if ((err = traced("s1_gemm_mx8_gateup_swiglu", gemm_flops(M, 2 * F, d),
+                    (Md + 2.0 * dF) * q8 + 3.0 * MF * e + MF * q8, s,
+                    [&] { return coda::launch_gemm_mx8(s1, coda::EPI_SWIGLU, s); })) != hipSuccess)
+    return hip_status(err);
+  // S2: z = a Wd on MXFP8
+  GemmArgs s2 = gemm_mx8(M, d, F, u8(ws.aq), u8(ws.as), u8(ws.wdq), u8(ws.wds), z, d);
+  return hip_status(traced("s2_gemm_mx8_down", gemm_flops(M, d, F), (MF + dF) * q8 + Md * e, s,
+                           [&] { return coda::launch_gemm_mx8(s2, coda::EPI_STORE, s); }));
+}
+
+coda_status coda_swiglu_bwd_mx8(int64_t M, int64_t d, int64_t F, const void* X, const void* W,
+                                const void* Wd, const void* gu, const void* a, const void* dz, void* dX,
+                                void* dW, void* dWd, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (!X || !W || !Wd || !gu || !a || !dz || !dX || !dW || !dWd) return CODA_ERR_NULL;
+  if (!swiglu_mx8_shape_ok(M, d, F)) return CODA_ERR_SHAPE;
+  for (const void* p : {X, W, Wd, gu, a, dz, (const void*)dX, (const void*)dW, (const void*)dWd})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  const SwigluMx8Ws ws = swiglu_mx8_ws(M, d, F, true);
+  if (!workspace || workspace_bytes < ws.total) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const size_t e = 2;
+  const Range in[] = {rng(X, M * d * e), rng(W, d * 2 * F * e), rng(Wd, F * d * e),
+                      rng(gu, M * 2 * F * e), rng(a, M * F * e), rng(dz, M * d * e)};
+  const Range out[] = {rng(dX, M * d * e), rng(dW, d * 2 * F * e), rng(dWd, F * d * e),
+                       rng(workspace, ws.total)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wb = (char*)workspace;
+  auto u8 = [&](size_t off) { return (uint8_t*)(wb + off); };
+  void* dgu = wb + ws.dgu;
+  hipError_t err;
+  const double q8 = 1.0 + 1.0 / 32.0, Md = (double)M * d, dF = (double)d * F, MF = (double)M * F;
+  auto both = [&](const char* name, const void* src, int64_t rows, int64_t cols, size_t qr, size_t sr, size_t qt,
+                  size_t st) {
+    coda::MxQuantArgs q{};
+    q.src = src;
+    q.ld = cols;
+    q.rows = rows;
+    q.cols = cols;
+    q.qr = u8(qr);
+    q.sr = u8(sr);
+    q.qt = u8(qt);
+    q.st = u8(st);
+    return traced(name, 0.0, (double)rows * cols * (e + 2.0 * q8), s,
+                  [&] { return coda::launch_mx8_quantize_fused(q, 0, s); });
+  };
+  // S3: da = dz Wd^T (contraction over d); epilogue dgu from the saved gu
+  if ((err = both("x1_mx8_quantize_dz_both", dz, M, d, ws.dzq, ws.dzs, ws.dzTq, ws.dzTs)) != hipSuccess)
+    return hip_status(err);
+  if ((err = traced("x2_mx8_quantize_Wd", 0.0, dF * (e + q8), s, [&] {
+         return coda::launch_mx8_quantize(Wd, d, F, d, u8(ws.wdrq), u8(ws.wdrs), s);
+       })) != hipSuccess)
+    return hip_status(err);
+  GemmArgs s3 = gemm_mx8(M, F, d, u8(ws.dzq), u8(ws.dzs), u8(ws.wdrq), u8(ws.wdrs), dgu, 2 * F);
+  s3.E = gu;
+  s3.lde = 2 * F;
+  s3.F = (int)F;
+  if ((err = traced("s3_gemm_mx8_da_swiglu_bwd", gemm_flops(M, F, d), (Md + dF) * q8 + 4.0 * MF * e, s,
+                    [&] { return coda::launch_gemm_mx8(s3, coda::EPI_SWIGLU_BWD, s); })) != hipSuccess)
+    return hip_status(err);
+  // S4: dWd = a^T dz (contraction over M): a along M, transposed
+  if ((err = traced("x3_mx8_quantize_aT", 0.0, MF * (e + q8), s, [&] {
+         return coda::launch_mx8_quantize_t(a, F, M, F, u8(ws.aTq), u8(ws.aTs), s);
+       })) != hipSuccess)
+    return hip_status(err);
+  GemmArgs s4 = gemm_mx8(F, d, M, u8(ws.aTq), u8(ws.aTs), u8(ws.dzTq), u8(ws.dzTs), dWd, d);
+  if ((err = traced("s4_gemm_mx8_dWd", gemm_flops(F, d, M), (MF + Md) * q8 + dF * e, s,
+                    [&] { return coda::launch_gemm_mx8(s4, coda::EPI_STORE, s); })) != hipSuccess)
+    return hip_status(err);
+  // S5: dX = dgu W^T (contraction over 2F); S6: dW = X^T dgu (contraction over M)
+  if ((err = both("x4_mx8_quantize_dgu_both", dgu, M, 2 * F, ws.dguq, ws.dgus, ws.dguTq, ws.dguTs)) != hipSuccess)
+    return hip_status(err);
+  if ((err = traced("x5_mx8_quantize_W", 0.0, 2.0 * dF * (e + q8), s, [&] {
+         return coda::launch_mx8_quantize(W, 2 * F, d, 2 * F, u8(ws.wrq), u8(ws.wrs), s);
+       })) != hipSuccess)
+    return hip_status(err);
+  GemmArgs s5 = gemm_mx8(M, d, 2 * F, u8(ws.dguq), u8(ws.dgus), u8(ws.wrq), u8(ws.wrs), dX, d);
+  if ((err = traced("s5_gemm_mx8_dX", gemm_flops(M, d, 2 * F), (2.0 * MF + 2.0 * dF) * q8 + Md * e, s,
+                    [&] { return coda::launch_gemm_mx8(s5, coda::EPI_STORE, s); })) != hipSuccess)
+    return hip_status(err);
+  if ((err = traced("x6_mx8_quantize_XT", 0.0, Md * (e + q8), s, [&] {
+         return coda::launch_mx8_quantize_t(X, d, M, d, u8(ws.XTq), u8(ws.XTs), s);
+       })) != hipSuccess)
+    return hip_status(err);
+  GemmArgs s6 = gemm_mx8(d, 2 * F, M, u8(ws.XTq), u8(ws.XTs), u8(ws.dguTq), u8(ws.dguTs), dW, 2 * F);
+  return hip_status(traced("s6_gemm_mx8_dW", gemm_flops(d, 2 * F, M), (Md + 2.0 * MF) * q8 + 2.0 * dF * e, s,
+                           [&] { return coda::launch_gemm_mx8(s6, coda::EPI_STORE, s); }));
+}
+
+}  // extern "C"

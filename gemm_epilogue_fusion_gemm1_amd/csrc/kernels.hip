@@ -467,6 +467,29 @@ __device__ __forceinline__ void wave_lds_sync() {
 // ---------------------------------------------------------------------------
 enum Fmt : int { FMT_BF16 = 0, FMT_MX8 = 1 };
 
+// One 32-block of a row to MXFP8, shared by 4 consecutive lanes holding 8
+// values each (lanes 4j..4j+3 of the wave): the block maximum by two
+// shuffles, the shared exponent floor(log2 amax) - 8 (clamped at -127) from
+// its exponent field, the 8 values scaled by the exact power of two,
+// saturated at 448 and rounded to nearest even by the hardware conversion.
+// Returns the lane's 8 codes; `sexp` receives the exponent.
+__device__ __forceinline__ uint2 mx8_block_of_4_lanes(f32x4 lo, f32x4 hi, int& sexp) {
+  float am = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) am = fmaxf(am, fmaxf(fabsf(lo[e]), fabsf(hi[e])));
+  am = fmaxf(am, __shfl_xor(am, 1));
+  am = fmaxf(am, __shfl_xor(am, 2));
+  sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
+  const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
+  auto sat = [&](float v) { return fminf(fmaxf(v * inv, -448.0f), 448.0f); };
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[0]), sat(lo[1]), 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[2]), sat(lo[3]), w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[0]), sat(hi[1]), 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[2]), sat(hi[3]), w1, true);
+  return uint2{(uint32_t)w0, (uint32_t)w1};
+}
+
+
 template <int FMT, int WMv, int WNv, int BKv, int NSTv, bool AK, bool BKM, int EPI, bool WIN>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   using G = Grid<WMv, WNv>;
@@ -497,7 +520,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   // MXFP8: the loaders count in 2-byte units (K / 2, ld / 2)
   constexpr int U = FMT == FMT_MX8 ? 2 : 1;
   la.init(g.A, WIN ? g.A_total : g.A_bytes, g.lda / U, row0, g.M, g.K / U, t, 0, tm);
-  lb.init(g.B, WIN ? g.B_total : g.B_bytes, g.ldb / U, col0, g.N, g.K / U, t, g.F, tn);
+  // rows of the B operand: N, or for a gate/up GEMM on MXFP8 the 2F rows of
+  // the weight stored with each 64-row group holding 32 gate rows j and the
+  // 32 up rows of the same j (the order a gated tile's columns take), so that
+  // the plain K-contiguous loader reads a gated tile as rows col0..col0+255
+  const int nb = (FMT == FMT_MX8 && GATED) ? 2 * g.F : g.N;
+  lb.init(g.B, WIN ? g.B_total : g.B_bytes, g.ldb / U, col0, nb, g.K / U, t, g.F, tn);
 
   // MFMA blocks: bf16 uses v_mfma_f32_16x16x32_bf16 (16x16 blocks, four
   // accumulators per lane), which draws less power per flop than the 32x32
@@ -537,11 +565,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const bool sc_a = wv < 4;
     const int sc_row = (sc_a ? row0 : col0) + 64 * (wv & 3) + lane;
-    const bool sc_ok = sc_row < (sc_a ? g.M : g.N);
+    const bool sc_ok = sc_row < (sc_a ? g.M : nb);
     const __amdgpu_buffer_rsrc_t srs = make_rsrc(sc_a ? g.sA : g.sB, sc_a ? g.sA_bytes : g.sB_bytes);
     // step-blocked scales: the words of one step's rows are contiguous, so a
     // wave's 64 rows are one 256-byte run
-    const uint32_t sc_base = (uint32_t)sc_row * 4u, sc_step = (uint32_t)(sc_a ? g.M : g.N) * 4u;
+    const uint32_t sc_base = (uint32_t)sc_row * 4u, sc_step = (uint32_t)(sc_a ? g.M : nb) * 4u;
     lds_char* const sc_lds = lsm + KC::LDS_BYTES + (sc_a ? 0 : BM * 4) + 64 * 4 * (wv & 3);
     auto issue_scales = [&](int step) {
       dma4(srs, (sc_ok && step < nk) ? sc_base + sc_step * (uint32_t)step : OOB, sc_lds + (step % NSTAGE) * SC_STAGE);
@@ -1144,16 +1172,37 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           u0 *= sc;
           u1 *= sc;
         }
-        if (jok && row < g.M) {
+        f32x4 a0, a1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a0[e] = silu_f(g0[e]) * u0[e];
+          a1[e] = silu_f(g1[e]) * u1[e];
+        }
+        const bool ok = jok && row < g.M;
+        if (ok) {
           st8(GU + (int64_t)row * g.ldc + jj, g0, g1);
           st8(GU + (int64_t)row * g.ldc + g.F + jj, u0, u1);
-          f32x4 a0, a1;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a0[e] = silu_f(g0[e]) * u0[e];
-            a1[e] = silu_f(g1[e]) * u1[e];
-          }
           st8(Aout + (int64_t)row * g.ldc2 + jj, a0, a1);
+        }
+        if constexpr (FMT == FMT_MX8) {
+          // a (as stored, bf16) to MXFP8 along F for the down GEMM: the 4
+          // lanes c4 = 0..3 of a row hold its 32-block jj0..jj0+31
+          // (jj0 = jj - 8 c4, a multiple of 32); step-blocked scales
+          // [F/128][M][4]
+          f32x4 b0 = f32x4{0.f, 0.f, 0.f, 0.f}, b1 = b0;
+          if (ok) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              b0[e] = bf2f(f2bf(a0[e]));
+              b1[e] = bf2f(f2bf(a1[e]));
+            }
+          }
+          int sexp;
+          const uint2 w = mx8_block_of_4_lanes(b0, b1, sexp);
+          if (ok) {
+            *(uint2*)(g.q_out + (int64_t)row * g.ldq + jj) = w;
+            if (c4 == 0) g.qs_out[((int64_t)(jj >> 7) * g.M + row) * 4 + ((jj >> 5) & 3)] = (uint8_t)(sexp + 127);
+          }
         }
       }
     }
@@ -1175,28 +1224,6 @@ __global__ void __launch_bounds__(64 * WMv * WNv)
     __attribute__((amdgpu_waves_per_eu(WMv * WNv / 4, WMv * WNv / 4)))
 gemm_mx8_kernel(GemmArgs g) {
   gemm_body<FMT_MX8, WMv, WNv, 64, 2, true, true, EPI, WIN>(g);
-}
-
-// One 32-block of a row to MXFP8, shared by 4 consecutive lanes holding 8
-// values each (lanes 4j..4j+3 of the wave): the block maximum by two
-// shuffles, the shared exponent floor(log2 amax) - 8 (clamped at -127) from
-// its exponent field, the 8 values scaled by the exact power of two,
-// saturated at 448 and rounded to nearest even by the hardware conversion.
-// Returns the lane's 8 codes; `sexp` receives the exponent.
-__device__ __forceinline__ uint2 mx8_block_of_4_lanes(f32x4 lo, f32x4 hi, int& sexp) {
-  float am = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) am = fmaxf(am, fmaxf(fabsf(lo[e]), fabsf(hi[e])));
-  am = fmaxf(am, __shfl_xor(am, 1));
-  am = fmaxf(am, __shfl_xor(am, 2));
-  sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
-  const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
-  auto sat = [&](float v) { return fminf(fmaxf(v * inv, -448.0f), 448.0f); };
-  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[0]), sat(lo[1]), 0, false);
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[2]), sat(lo[3]), w0, true);
-  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[0]), sat(hi[1]), 0, false);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[2]), sat(hi[3]), w1, true);
-  return uint2{(uint32_t)w0, (uint32_t)w1};
 }
 
 // bf16 rows -> MXFP8 along the row.  A lane takes 8 consecutive elements
@@ -1294,6 +1321,8 @@ __global__ void __launch_bounds__(256) mx8_quantize_t_kernel(const __bf16* __res
 //              dR); quantised both ways -- dy for the dX and dW1 GEMMs;
 //   QUANT_NROW: v = n = r_i y (bf16; src = y); quantised along the column
 //              only -- n for the dW2 GEMM.
+// With qr NULL only the transposed codes are made; with gated_F > 0 (a
+// gate/up weight [d, 2F], F % 32 == 0) they are written in gate/up order.
 // The values are rounded to bf16 before they are quantised (the stored dn,
 // n and dy of the bf16 backward).  A workgroup takes a 128 x 64 tile: each
 // thread produces 4 pieces of 8 values, quantises them along the row with
@@ -1330,7 +1359,7 @@ __global__ void __launch_bounds__(256) mx8_quantize_fused_kernel(MxQuantArgs q) 
       }
     }
     *(bf16x8*)&tile[r][c8] = v;
-    if constexpr (MODE != QUANT_NROW) {
+    if (MODE != QUANT_NROW && q.qr) {             // uniform over the grid
       const f32x4 lo{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
       const f32x4 hi{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
       int sexp;
@@ -1361,10 +1390,18 @@ __global__ void __launch_bounds__(256) mx8_quantize_fused_kernel(MxQuantArgs q) 
     w[j] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(v[4 * j + 2]), sat(v[4 * j + 3]), x, true);
   }
   if (col < q.cols) {
-    uint8_t* dst = q.qt + col * q.rows + row0 + 32 * b;
+    // gated_F: column c of a [.., 2F] gate/up weight goes to row 64 (j / 32)
+    // + 32 [c is an up column] + j % 32, j = c mod F (the order of a gated
+    // tile's columns)
+    int64_t tr = col;
+    if (q.gated_F > 0) {
+      const int64_t j = col < q.gated_F ? col : col - q.gated_F;
+      tr = 64 * (j >> 5) + (col < q.gated_F ? 0 : 32) + (j & 31);
+    }
+    uint8_t* dst = q.qt + tr * q.rows + row0 + 32 * b;
     *(uint4*)dst = uint4{w[0], w[1], w[2], w[3]};
     *(uint4*)(dst + 16) = uint4{w[4], w[5], w[6], w[7]};
-    q.st[((int64_t)blockIdx.y * q.cols + col) * 4 + b] = (uint8_t)(sexp + 127);
+    q.st[((int64_t)blockIdx.y * q.cols + tr) * 4 + b] = (uint8_t)(sexp + 127);
   }
 }
 
@@ -1631,7 +1668,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStr
 
 template <int EPI>
 static hipError_t launch_mx8_one(const GemmArgs& g, hipStream_t s) {
-  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  constexpr bool gated = EPI == EPI_SWIGLU;
+  const int tiles = ((g.M + BM - 1) / BM) * (gated ? (g.N + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN);
   if (needs_windows(g))
     hipLaunchKernelGGL((gemm_mx8_kernel<kMxWavesM, kMxWavesN, EPI, true>), dim3(tiles),
                        dim3(64 * kMxWavesM * kMxWavesN), 0, s, g);
@@ -1648,6 +1686,8 @@ hipError_t launch_gemm_mx8(const GemmArgs& g, Epi epi, hipStream_t s) {
     case EPI_RSQRT_SCALE: return launch_mx8_one<EPI_RSQRT_SCALE>(g, s);
     case EPI_DN: return launch_mx8_one<EPI_DN>(g, s);
     case EPI_ROWSCALE: return launch_mx8_one<EPI_ROWSCALE>(g, s);
+    case EPI_SWIGLU: return launch_mx8_one<EPI_SWIGLU>(g, s);
+    case EPI_SWIGLU_BWD: return launch_mx8_one<EPI_SWIGLU_BWD>(g, s);
     default: return hipErrorInvalidValue;
   }
 }

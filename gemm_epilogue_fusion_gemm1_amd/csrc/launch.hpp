@@ -97,13 +97,18 @@ hipError_t launch_mx8_quantize(const void* src, int64_t ld, int64_t rows, int64_
 // mode 2: v = r_i src rounded to bf16.  qr / sr: v quantised along the row
 // (codes [rows][cols], scales step-blocked [cols/128][rows][4]; cols % 128 ==
 // 0; not made in mode 2); qt / st: v quantised along the column, stored
-// transposed (codes [cols][rows], scales [rows/128][cols][4]).
+// transposed (codes [cols][rows], scales [rows/128][cols][4]).  qr NULL: no
+// row-wise codes.  gated_F > 0: src is a gate/up weight [d, 2F] and its
+// column c is written to transposed row 64 (j / 32) + 32 [c >= F] + j % 32,
+// j = c mod F: each 64-row group holds 32 gate rows and the 32 up rows of the
+// same j, the column order of a gate/up GEMM's tile (F % 32 == 0).
 struct MxQuantArgs {
   const void* src; int64_t ld;
   int64_t rows, cols;
   const float* r; const float* c; const void* y; void* out;
   uint8_t* qr; uint8_t* sr;
   uint8_t* qt; uint8_t* st;
+  int64_t gated_F;
 };
 hipError_t launch_mx8_quantize_fused(const MxQuantArgs& q, int mode, hipStream_t stream);
 

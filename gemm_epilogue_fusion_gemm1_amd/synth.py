@@ -29,8 +29,9 @@ class Workload:
     name: str
     kind: str            # "coda" (GEMM-Residual-RMSNorm-GEMM), "swiglu", "mlp" (the two
                          # chained), "ce" (LM-head GEMM + cross-entropy), "rope"
-                         # (QKV projection with rotary positions in its epilogue) or
-                         # "mx8" (the coda block's forward on MXFP8 operands)
+                         # (QKV projection with rotary positions in its epilogue),
+                         # "mx8" (the coda block on MXFP8 operands) or "swiglu_mx8"
+                         # (the SwiGLU block on MXFP8 operands)
     dtype: str           # "f32", "bf16" or "mxfp8" (bf16 draws, quantised by the caller)
     M: int
     K: int = 0           # coda, mlp: GEMM1 reduction width
@@ -108,6 +109,10 @@ WORKLOADS = {
                  note="LLaMA-7B-shaped block forward+backward with every GEMM on MXFP8 "
                       "operands (the backward quantises its bf16 inputs along each "
                       "GEMM's contraction index)"),
+        Workload("swiglu_fwdbwd_mx8", "swiglu_mx8", "mxfp8", M=8192, d=4096, F=14336,
+                 seed=1011, backward=True,
+                 note="SwiGLU block forward+backward (the swiglu_fwdbwd shape) with every "
+                      "GEMM on MXFP8 operands (bf16 draws, quantised by the calls)"),
     ]
 }
 
@@ -236,4 +241,6 @@ def workload_inputs(w: Workload, with_dz: bool | None = None) -> dict:
         return rope_inputs(w.M, w.K, w.N, w.seed, w.dtype, with_dz)
     if w.kind == "mx8":
         return mx8_inputs(w.M, w.K, w.d, w.N, w.seed, with_dz)
+    if w.kind == "swiglu_mx8":     # bf16 draws; the MXFP8 calls quantise them
+        return swiglu_inputs(w.M, w.d, w.F, w.seed, "bf16", with_dz)
     return swiglu_inputs(w.M, w.d, w.F, w.seed, w.dtype, with_dz)

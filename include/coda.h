@@ -425,6 +425,43 @@ coda_status coda_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, const void*
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * The SwiGLU block (coda_swiglu_fwd / coda_swiglu_bwd) with every GEMM on the
+ * MXFP8 matrix units, for the same reason as the block's MXFP8 entry points
+ * ([JA] 課題：大モデル訓練の「手抜き税」; [RU] "Налог на лень при обучении
+ * больших моделей").  Each GEMM's operands are quantised (the format of
+ * coda_fwd_mx8) along its own contraction index:
+ *   gu  = X W          X and W along d;   a = silu(g) u from the GEMM's fp32
+ *                      result;  gu and a stored in bf16, a also quantised
+ *                      along F in the epilogue
+ *   z   = a Wd         a and Wd along F
+ * and the backward is the gradient of the unquantised block (the forward's
+ * quantisation passes it straight through), as coda_swiglu_bwd:
+ *   da  = dz Wd^T      dz and Wd along d;  epilogue dgu from the saved gu
+ *   dWd = a^T dz       a and dz along M
+ *   dX  = dgu W^T      dgu and W along 2F
+ *   dW  = X^T dgu      X and dgu along M
+ * a and dgu are rounded to bf16 before they are quantised.  The tensors come
+ * and go in bf16 (X [M,d], W [d,2F] gate columns first, Wd [F,d], gu [M,2F],
+ * a [M,F], z and dz [M,d], dX [M,d], dW [d,2F], dWd [F,d]); the calls
+ * quantise them.
+ *   M, d, F: multiples of 128 (every contraction index is whole 128-k steps).
+ *   workspace: >= the matching _workspace_bytes(M, d, F) bytes (every GEMM
+ *   operand in MXFP8; dgu in the backward), 16-byte aligned; the query
+ *   returns 0 for a shape the calls refuse.
+ * Errors as coda_swiglu_fwd / coda_swiglu_bwd (CODA_ERR_SHAPE for a shape
+ * that is not whole 128-blocks).
+ * ---------------------------------------------------------------------- */
+size_t coda_swiglu_fwd_mx8_workspace_bytes(int64_t M, int64_t d, int64_t F);
+coda_status coda_swiglu_fwd_mx8(int64_t M, int64_t d, int64_t F, const void* X, const void* W,
+                                const void* Wd, void* gu, void* a, void* z, void* workspace,
+                                size_t workspace_bytes, void* stream);
+size_t coda_swiglu_bwd_mx8_workspace_bytes(int64_t M, int64_t d, int64_t F);
+coda_status coda_swiglu_bwd_mx8(int64_t M, int64_t d, int64_t F, const void* X, const void* W,
+                                const void* Wd, const void* gu, const void* a, const void* dz, void* dX,
+                                void* dW, void* dWd, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* ------------------------------------------------------------------------
  * Kernel tracing (measurement aid; off by default).
  *
  * coda_trace_start(capacity) creates 2*capacity timing events (host call,

@@ -403,3 +403,43 @@ def test_bwd_mx8_rejects(L):
     assert bwd_mx8_call(L, X=x, dX=x) == ALIAS
     assert bwd_mx8_call(L, r=ctypes.c_void_p(m(4096).value + 4)) == ALIGN
 
+
+
+def swiglu_mx8_call(L, bwd, **over):
+    m = FakeMem()
+    M, d, F = 256, 128, 384
+    a = dict(M=M, d=d, F=F, X=m(M * d * 2), W=m(d * 2 * F * 2), Wd=m(F * d * 2), gu=m(M * 2 * F * 2),
+             a=m(M * F * 2), z=m(M * d * 2), dz=m(M * d * 2), dX=m(M * d * 2), dW=m(d * 2 * F * 2),
+             dWd=m(F * d * 2))
+    q = L.coda_swiglu_bwd_mx8_workspace_bytes if bwd else L.coda_swiglu_fwd_mx8_workspace_bytes
+    a["ws_bytes"] = q(M, d, F)
+    a["ws"] = m(a["ws_bytes"])
+    a.update(over)
+    if bwd:
+        return L.coda_swiglu_bwd_mx8(a["M"], a["d"], a["F"], a["X"], a["W"], a["Wd"], a["gu"], a["a"], a["dz"],
+                                     a["dX"], a["dW"], a["dWd"], a["ws"], a["ws_bytes"], None)
+    return L.coda_swiglu_fwd_mx8(a["M"], a["d"], a["F"], a["X"], a["W"], a["Wd"], a["gu"], a["a"], a["z"],
+                                 a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("bwd", [False, True], ids=["fwd", "bwd"])
+def test_swiglu_mx8_rejects(L, bwd):
+    """The MXFP8 SwiGLU calls need M, d, F in whole 128-element blocks and
+    check pointers, alignment, aliasing and the workspace before any HIP
+    call; the workspace query returns 0 for a refused shape."""
+    q = L.coda_swiglu_bwd_mx8_workspace_bytes if bwd else L.coda_swiglu_fwd_mx8_workspace_bytes
+    assert q(256, 128, 384) > 0
+    for bad in ((200, 128, 384), (256, 136, 384), (256, 128, 392), (0, 128, 384)):
+        assert q(*bad) == 0
+    assert swiglu_mx8_call(L, bwd, X=None) == NULL
+    assert swiglu_mx8_call(L, bwd, Wd=None) == NULL
+    assert swiglu_mx8_call(L, bwd, M=200) == SHAPE
+    assert swiglu_mx8_call(L, bwd, d=136) == SHAPE
+    assert swiglu_mx8_call(L, bwd, F=392) == SHAPE
+    assert swiglu_mx8_call(L, bwd, ws_bytes=1024) == WORKSPACE
+    assert swiglu_mx8_call(L, bwd, ws=None) == WORKSPACE
+    m = FakeMem()
+    x = m(1 << 22)
+    out = "dX" if bwd else "z"
+    assert swiglu_mx8_call(L, bwd, X=x, **{out: x}) == ALIAS
+    assert swiglu_mx8_call(L, bwd, W=ctypes.c_void_p(m(4096).value + 4)) == ALIGN

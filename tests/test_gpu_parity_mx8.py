@@ -327,3 +327,89 @@ def test_full_workload_bwd_mx8(torch_dev):
         assert errs[k] <= BF16_TOL, (k, errs[k])
     assert errs["dgamma"] <= 1e-3
 
+
+
+# ---------------------------------------------------------------- SwiGLU block
+
+SMALL_SWIGLU_MX8 = [
+    (128, 128, 128),           # smallest accepted: one gated tile, one K step
+    (256, 384, 256),
+    (384, 256, 640),           # F not a multiple of the 256-column tile
+    (640, 1152, 384),          # several tiles, d not a multiple of 256
+    (1024, 512, 1280),
+]
+
+
+def _run_swiglu_mx8(torch, dev, h, gu=None, a=None):
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    t = {k: bf(torch, dev, v) for k, v in h.items()}
+    if gu is None:
+        out = coda.swiglu_fwd_mx8(t["X"], t["W"], t["Wd"])
+    else:
+        out = coda.swiglu_bwd_mx8(t["X"], t["W"], t["Wd"], bf(torch, dev, gu), bf(torch, dev, a), t["dz"])
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("shape", SMALL_SWIGLU_MX8, ids=lambda s: "x".join(map(str, s)))
+def test_swiglu_mx8(torch_dev, shape):
+    """Forward outputs against ``ref_swiglu_fwd_mx8``; the backward, fed the
+    oracle's saved gu and a (bf16), against ``ref_swiglu_bwd_mx8``; the
+    distance from the unquantised block reported beside them."""
+    torch, dev = torch_dev
+    M, d, F = shape
+    h = synth.swiglu_inputs(M, d, F, seed=830 + M + F)
+    z, gu, a = _run_swiglu_mx8(torch, dev, h)
+    f = oracle.ref_swiglu_fwd_mx8(h["X"], h["W"], h["Wd"])
+    g = lambda v: v.float().cpu().numpy()  # noqa: E731
+    errs = {"z": rel(g(z), f["z"]), "gu": rel(g(gu), f["gu"]), "a": rel(g(a), f["a"])}
+    gu_s, a_s = oracle.bf16_rne(f["gu"]), oracle.bf16_rne(f["a"])
+    dX, dW, dWd = _run_swiglu_mx8(torch, dev, h, gu_s, a_s)
+    b = oracle.ref_swiglu_bwd_mx8(h["X"], h["W"], h["Wd"], gu_s, a_s, h["dz"])
+    errs.update(dX=rel(g(dX), b["dX"]), dW=rel(g(dW), b["dW"]), dWd=rel(g(dWd), b["dWd"]))
+    e = oracle.ref_swiglu_bwd(h["X"], h["W"], h["Wd"], gu_s, a_s, h["dz"])
+    info = {f"{k}_vs_unquantised": rel(g(v), e[k]) for k, v in (("dX", dX), ("dW", dW), ("dWd", dWd))}
+    report(f"swiglu mx8 {shape}", {**errs, **info})
+    for k, v in errs.items():
+        assert v <= BF16_TOL, (k, v)
+
+
+def test_swiglu_mx8_deterministic(torch_dev):
+    torch, dev = torch_dev
+    h = synth.swiglu_inputs(384, 256, 640, seed=850)
+    f1 = _run_swiglu_mx8(torch, dev, h)
+    f2 = _run_swiglu_mx8(torch, dev, h)
+    gu, a = f1[1].float().cpu().numpy(), f1[2].float().cpu().numpy()
+    b1 = _run_swiglu_mx8(torch, dev, h, gu, a)
+    b2 = _run_swiglu_mx8(torch, dev, h, gu, a)
+    for x_, y_ in zip(f1 + b1, f2 + b2):
+        assert torch.equal(x_, y_)
+
+
+def test_full_workload_swiglu_mx8(torch_dev):
+    """The SwiGLU shape (M = 8192, d = 4096, F = 14336) on MXFP8: forward rows
+    and the backward (fed the GPU forward's saved gu and a, as in training)
+    on stratified rows, dW columns and dWd rows, one from every 128-row /
+    64-column band, against the oracle's chain."""
+    torch, dev = torch_dev
+    w = synth.WORKLOADS["swiglu_fwdbwd_mx8"]
+    print(f"[parity] {w.name}: inputs", flush=True)
+    h = synth.workload_inputs(w)
+    z, gu, a = _run_swiglu_mx8(torch, dev, h)
+    t = {k: bf(torch, dev, v) for k, v in h.items()}
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    dX, dW, dWd = coda.swiglu_bwd_mx8(t["X"], t["W"], t["Wd"], gu, a, t["dz"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed)
+    strata = lambda n, band: np.unique(np.concatenate([[0, n - 1], [rng.integers(b0, min(b0 + band, n)) for b0 in range(0, n, band)]]))  # noqa: E731
+    rows, cols_W, rows_Wd = strata(w.M, 128), strata(2 * w.F, 64), strata(w.F, 64)
+    print(f"[parity] {w.name}: oracle (sampled)", flush=True)
+    fr = oracle.ref_swiglu_fwd_mx8_rows(h["X"], h["W"], h["Wd"], rows)
+    b = oracle.ref_swiglu_bwd_mx8_sampled(h["X"], h["W"], h["Wd"], h["dz"], rows, cols_W, rows_Wd)
+    g = lambda v: v.float().cpu().numpy()  # noqa: E731
+    errs = {"z_rows": rel(g(z[rows]), fr["z"]), "gu_rows": rel(g(gu[rows]), fr["gu"]),
+            "a_rows": rel(g(a[rows]), fr["a"]), "dX_rows": rel(g(dX[rows]), b["dX_rows"]),
+            "dW_cols": rel(g(dW[:, cols_W]), b["dW_cols"]), "dWd_rows": rel(g(dWd[rows_Wd]), b["dWd_rows"])}
+    report(w.name, errs)
+    for k, v in errs.items():
+        assert v <= BF16_TOL, (k, v)
