@@ -77,6 +77,9 @@ What the pages fix, and the readings taken where they are silent:
   * The SwiGLU block on MXFP8 (``ref_swiglu_fwd_mx8``, ``ref_swiglu_bwd_mx8``):
     the same reading for the gate/up pattern; a = silu(g) u from the GEMM's
     unrounded result, a and dgu held in bf16 before they are quantised.
+  * The MLP sub-layer on MXFP8 (``ref_mlp_fwd_mx8``, ``ref_mlp_bwd_mx8``): the
+    two readings composed, y diag(gamma) quantised as in the block's MXFP8
+    forward, dy_in added to dy as in the bf16 MLP.
 
 Every function here is pinned by a test against something other than itself
 (brute-force loops, finite differences, torch CPU autograd, closed forms and
@@ -97,7 +100,8 @@ __all__ = [
     "E4M3_MAX", "MX_BLOCK", "e4m3_decode", "e4m3_encode", "e8m0_decode", "mx_quantize",
     "mx_dequantize", "ref_fwd_mx8", "ref_fwd_mx8_rows", "mx_matmul", "ref_bwd_mx8",
     "ref_bwd_mx8_sampled", "ref_swiglu_fwd_mx8", "ref_swiglu_bwd_mx8", "ref_swiglu_fwd_mx8_rows",
-    "ref_swiglu_bwd_mx8_sampled",
+    "ref_swiglu_bwd_mx8_sampled", "ref_mlp_fwd_mx8", "ref_mlp_fwd_mx8_rows", "ref_mlp_bwd_mx8",
+    "ref_mlp_bwd_mx8_sampled",
 ]
 
 
@@ -801,7 +805,7 @@ def mx_matmul(A, B) -> np.ndarray:
     return mx_dequantize(Aq, As) @ mx_dequantize(Bq, Bs).T
 
 
-def ref_bwd_mx8(X, W1, gamma, W2, y, r, dz, store=bf16_rne) -> dict:
+def ref_bwd_mx8(X, W1, gamma, W2, y, r, dz, store=bf16_rne, dy_in=None) -> dict:
     """Backward of the block with every GEMM on MXFP8 operands.
 
     The pages argue that FP8 matrix units make the memory-bound work around a
@@ -813,14 +817,16 @@ def ref_bwd_mx8(X, W1, gamma, W2, y, r, dz, store=bf16_rne) -> dict:
       dh  = mx(dz, W2^T)                 (contraction over N)
       dgamma_j = sum_i dh_ij r_i y_ij;  dn = dh diag(gamma);
       s_i = sum_j dn_ij y_ij;  c_i = r_i^3 s_i / d;
-      dy  = diag(r) store(dn) - diag(c) y;  dR = store(dy)
+      dy  = diag(r) store(dn) - diag(c) y (+ dy_in);  dR = store(dy)
       dW2 = diag(gamma) mx(store(n)^T, dz),  n = diag(r) y   (contraction over M)
       dX  = mx(store(dy), W1^T)          (contraction over d)
       dW1 = mx(X^T, store(dy))           (contraction over M)
     ``store`` is the storage contract of the intermediates that feed a
     quantiser (dn, n and dy are kept in bf16): bf16_rne by default; pass the
     identity for unrounded intermediates.  y and r are the saved forward
-    tensors; X, W1, W2 the unquantised (bf16) inputs.
+    tensors; X, W1, W2 the unquantised (bf16) inputs; dy_in (optional) the
+    gradient that reaches y from later layers (the MLP sub-layer's residual
+    stream), added to dy as in ``ref_bwd``.
     """
     X, W1, gamma, W2, y, r, dz = map(_f64, (X, W1, gamma, W2, y, r, dz))
     d = y.shape[1]
@@ -831,6 +837,8 @@ def ref_bwd_mx8(X, W1, gamma, W2, y, r, dz, store=bf16_rne) -> dict:
     s = np.sum(dn * y, axis=1)
     c = r ** 3 * s / d
     dy = r[:, None] * store(dn) - c[:, None] * y
+    if dy_in is not None:
+        dy = dy + _f64(dy_in)
     dy_s = store(dy)
     dW2 = gamma[:, None] * mx_matmul(store(n).T, dz)
     dX = mx_matmul(dy_s, W1.T)
@@ -839,7 +847,7 @@ def ref_bwd_mx8(X, W1, gamma, W2, y, r, dz, store=bf16_rne) -> dict:
             "dh": dh, "dn": dn, "n": n, "s": s, "c": c, "dy": dy}
 
 
-def ref_bwd_mx8_sampled(X, W1, gamma, W2, y, r, dz, rows, cols_d, cols_N, store=bf16_rne) -> dict:
+def ref_bwd_mx8_sampled(X, W1, gamma, W2, y, r, dz, rows, cols_d, cols_N, store=bf16_rne, dy_in=None) -> dict:
     """``ref_bwd_mx8`` with dX and dR restricted to ``rows``, dW1 to the columns
     ``cols_d`` and dW2 to the columns ``cols_N``; dgamma, s and c in full.
 
@@ -857,11 +865,14 @@ def ref_bwd_mx8_sampled(X, W1, gamma, W2, y, r, dz, rows, cols_d, cols_N, store=
     dn = dh * gamma[None, :]
     s = np.sum(dn * y, axis=1)
     c = r ** 3 * s / d
-    dy_s = store(r[:, None] * store(dn) - c[:, None] * y)
+    dy = r[:, None] * store(dn) - c[:, None] * y
+    if dy_in is not None:
+        dy = dy + _f64(dy_in)
+    dy_s = store(dy)
     dX_rows = mx_matmul(dy_s[rows], W1.T)
     dW1_cols = mx_matmul(X.T, dy_s[:, cols_d])
     dW2_cols = gamma[:, None] * mx_matmul(store(n).T, dz[:, cols_N])
-    dR_rows = r[rows, None] * store(dn[rows]) - c[rows, None] * y[rows]
+    dR_rows = dy[rows]
     return {"rows": rows, "cols_d": cols_d, "cols_N": cols_N, "dX_rows": dX_rows, "dR_rows": dR_rows,
             "dW1_cols": dW1_cols, "dW2_cols": dW2_cols, "dgamma": dgamma, "s": s, "c": c}
 
@@ -947,6 +958,72 @@ def ref_swiglu_bwd_mx8_sampled(X, W, Wd, dz, rows, cols_W, rows_Wd, store=bf16_r
     a_c = store(gj * sigmoid(gj) * uj)
     return {"rows": rows, "cols_W": cols_W, "rows_Wd": rows_Wd, "dX_rows": mx_matmul(store(dgu_r), W.T),
             "dgu_rows": dgu_r, "dW_cols": mx_matmul(X.T, store(dgu_c)), "dWd_rows": mx_matmul(a_c.T, dz)}
+
+
+def ref_mlp_fwd_mx8(X, W1, R, gamma, W, Wd, eps: float, store=bf16_rne) -> dict:
+    """The MLP sub-layer (``ref_mlp_fwd``) with its three GEMMs on MXFP8
+    operands quantised along their contraction index:
+      y  = mx(X, W1) + R                    (contraction over K)
+      r_i = (mean_j y_ij^2 + eps)^-1/2
+      gu = diag(r) mx(y diag(gamma), W)     (contraction over d; as in
+           ``ref_fwd_mx8``, y diag(gamma) is quantised from the unrounded y
+           and r applied after the product)
+      a  = silu(g) u;  z = mx(store(a), Wd) (contraction over F)
+    X, W1, R, gamma, W, Wd are the unquantised (bf16) inputs."""
+    X, W1, R, gamma, W, Wd = map(_f64, (X, W1, R, gamma, W, Wd))
+    F = W.shape[1] // 2
+    y = mx_matmul(X, W1) + R
+    r = 1.0 / np.sqrt(np.mean(y * y, axis=1) + eps)
+    gu = r[:, None] * mx_matmul(y * gamma[None, :], W)
+    g, u = gu[:, :F], gu[:, F:]
+    a = g * sigmoid(g) * u
+    return {"y": y, "r": r, "gu": gu, "a": a, "z": mx_matmul(store(a), Wd)}
+
+
+def ref_mlp_fwd_mx8_rows(X, W1, R, gamma, W, Wd, eps: float, rows, store=bf16_rne) -> dict:
+    """``ref_mlp_fwd_mx8`` for the given rows only (every quantisation block
+    of X, y diag(gamma) and a runs along a row)."""
+    rows = np.asarray(rows)
+    out = ref_mlp_fwd_mx8(_f64(X)[rows], W1, _f64(R)[rows], gamma, W, Wd, eps, store)
+    out["rows"] = rows
+    return out
+
+
+def ref_mlp_bwd_mx8(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in=None, store=bf16_rne) -> dict:
+    """Backward of ``ref_mlp_fwd_mx8``: the SwiGLU part of
+    ``ref_swiglu_bwd_mx8`` (da = mx(dz, Wd^T), dgu from the saved gu, dWd =
+    mx(a^T, dz)), then, with dgu rounded by ``store`` as the second GEMM's
+    output gradient, the block backward ``ref_bwd_mx8`` with W2 = W (dW = its
+    dW2) and dy_in added to dy."""
+    X, W1, gamma, W, Wd, y, r, gu, a, dz = map(_f64, (X, W1, gamma, W, Wd, y, r, gu, a, dz))
+    F = W.shape[1] // 2
+    g, u = gu[:, :F], gu[:, F:]
+    sg = sigmoid(g)
+    da = mx_matmul(dz, Wd.T)
+    dgu = np.concatenate([da * u * sg * (1.0 + g * (1.0 - sg)), da * g * sg], axis=1)
+    b = ref_bwd_mx8(X, W1, gamma, W, y, r, store(dgu), store, dy_in)
+    return {"dX": b["dX"], "dW1": b["dW1"], "dR": b["dR"], "dW": b["dW2"], "dWd": mx_matmul(a.T, dz),
+            "dgamma": b["dgamma"], "dgu": dgu, "da": da, "dh": b["dh"], "s": b["s"], "c": b["c"]}
+
+
+def ref_mlp_bwd_mx8_sampled(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in, rows, cols_d, cols_2F, rows_F,
+                            store=bf16_rne) -> dict:
+    """``ref_mlp_bwd_mx8`` with dX and dR on ``rows``, dW1 on the columns
+    ``cols_d``, dW on the columns ``cols_2F``, dWd on the rows ``rows_F``;
+    dgamma, s and c in full (they need every row, so dgu is formed whole and
+    the block part is ``ref_bwd_mx8_sampled``)."""
+    X, W1, gamma, W, Wd, y, r, gu, a, dz = map(_f64, (X, W1, gamma, W, Wd, y, r, gu, a, dz))
+    F = W.shape[1] // 2
+    g, u = gu[:, :F], gu[:, F:]
+    sg = sigmoid(g)
+    da = mx_matmul(dz, Wd.T)
+    dgu = np.concatenate([da * u * sg * (1.0 + g * (1.0 - sg)), da * g * sg], axis=1)
+    rows_F = np.asarray(rows_F)
+    b = ref_bwd_mx8_sampled(X, W1, gamma, W, y, r, store(dgu), rows, cols_d, cols_2F, store, dy_in)
+    return {"rows": b["rows"], "cols_d": b["cols_d"], "cols_2F": b["cols_N"], "rows_F": rows_F,
+            "dX_rows": b["dX_rows"], "dR_rows": b["dR_rows"], "dW1_cols": b["dW1_cols"],
+            "dW_cols": b["dW2_cols"], "dWd_rows": mx_matmul(a[:, rows_F].T, dz), "dgamma": b["dgamma"],
+            "s": b["s"], "c": b["c"]}
 
 
 def ref_fwd_mx8_rows(Xq, Xs, W1q, W1s, R, gamma, W2q, W2s, eps: float, rows) -> dict:

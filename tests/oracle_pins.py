@@ -1139,6 +1139,27 @@ def _bwd_mx8_case(seed, M, K, d, N):
                 y=g.standard_normal((M, d)) * 1.5, dz=g.standard_normal((M, N)))
 
 
+def _bwd_mx8_loops(X, W1, gamma, W2, y, r, dz, dy_in, tab):
+    """The MXFP8 block backward by loops (lists in, lists out): dh, dgamma, c,
+    the stored dy, dW2, dX, dW1."""
+    M, d, N = len(y), len(y[0]), len(dz[0])
+    W2T = [[W2[j][k] for j in range(d)] for k in range(N)]          # [N][d]: the product dz W2^T
+    dh = _mx_matmul_loop(dz, W2T, tab)
+    dgam = [sum(dh[i][j] * r[i] * y[i][j] for i in range(M)) for j in range(d)]
+    dn = [[dh[i][j] * gamma[j] for j in range(d)] for i in range(M)]
+    s_ = [sum(dn[i][j] * y[i][j] for j in range(d)) for i in range(M)]
+    cc = [r[i] ** 3 * s_[i] / d for i in range(M)]
+    dy = [[_bf16_loop(r[i] * _bf16_loop(dn[i][j]) - cc[i] * y[i][j] + (dy_in[i][j] if dy_in else 0.0))
+           for j in range(d)] for i in range(M)]
+    nT = [[_bf16_loop(r[i] * y[i][j]) for i in range(M)] for j in range(d)]
+    dW2 = _mx_matmul_loop(nT, dz, tab)
+    dW2 = [[dW2[j][k] * gamma[j] for k in range(N)] for j in range(d)]
+    W1T = [[W1[k][j] for k in range(len(W1))] for j in range(d)]
+    XT = [[X[i][k] for i in range(M)] for k in range(len(X[0]))]
+    return {"dh": dh, "dgamma": dgam, "c": cc, "dy": dy, "dW2": dW2,
+            "dX": _mx_matmul_loop(dy, W1T, tab), "dW1": _mx_matmul_loop(XT, dy, tab)}
+
+
 def pin_bwd_mx8_bruteforce(O):
     """The MXFP8 backward by pure-Python loops on a tiny case (every dimension
     two 32-blocks): each GEMM's operands quantised along its contraction
@@ -1149,27 +1170,15 @@ def pin_bwd_mx8_bruteforce(O):
     y = c["y"]
     r = 1.0 / np.sqrt(np.mean(y * y, axis=1) + 1e-6)
     out = O.ref_bwd_mx8(c["X"], c["W1"], c["gamma"], c["W2"], y, r, c["dz"])
-    Ly, Lr, Lg = y.tolist(), r.tolist(), c["gamma"].tolist()
-    W2T = c["W2"].T.tolist()                       # [N][d]: the product dz W2^T
-    dh = _mx_matmul_loop(c["dz"].tolist(), W2T, tab)
-    dgam = [sum(dh[i][j] * Lr[i] * Ly[i][j] for i in range(M)) for j in range(d)]
-    dn = [[dh[i][j] * Lg[j] for j in range(d)] for i in range(M)]
-    s_ = [sum(dn[i][j] * Ly[i][j] for j in range(d)) for i in range(M)]
-    cc = [Lr[i] ** 3 * s_[i] / d for i in range(M)]
-    dy = [[_bf16_loop(Lr[i] * _bf16_loop(dn[i][j]) - cc[i] * Ly[i][j]) for j in range(d)] for i in range(M)]
-    nT = [[_bf16_loop(Lr[i] * Ly[i][j]) for i in range(M)] for j in range(d)]
-    dW2 = _mx_matmul_loop(nT, c["dz"].tolist(), tab)
-    dW2 = [[dW2[j][k] * Lg[j] for k in range(N)] for j in range(d)]
-    dX = _mx_matmul_loop(dy, c["W1"].T.tolist(), tab)
-    XT = c["X"].T.tolist()
-    dW1 = _mx_matmul_loop(XT, dy, tab)
-    _close(out["dh"], np.array(dh), 1e-12, "mx8 bwd dh")
-    _close(out["dgamma"], np.array(dgam), 1e-12, "mx8 bwd dgamma")
-    _close(out["c"], np.array(cc), 1e-12, "mx8 bwd c")
-    _close(O.bf16_rne(out["dy"]), np.array(dy), 1e-12, "mx8 bwd dy (stored)")
-    _close(out["dW2"], np.array(dW2), 1e-12, "mx8 bwd dW2")
-    _close(out["dX"], np.array(dX), 1e-12, "mx8 bwd dX")
-    _close(out["dW1"], np.array(dW1), 1e-12, "mx8 bwd dW1")
+    L = _bwd_mx8_loops(c["X"].tolist(), c["W1"].tolist(), c["gamma"].tolist(), c["W2"].tolist(), y.tolist(),
+                       r.tolist(), c["dz"].tolist(), None, tab)
+    _close(out["dh"], np.array(L["dh"]), 1e-12, "mx8 bwd dh")
+    _close(out["dgamma"], np.array(L["dgamma"]), 1e-12, "mx8 bwd dgamma")
+    _close(out["c"], np.array(L["c"]), 1e-12, "mx8 bwd c")
+    _close(O.bf16_rne(out["dy"]), np.array(L["dy"]), 1e-12, "mx8 bwd dy (stored)")
+    _close(out["dW2"], np.array(L["dW2"]), 1e-12, "mx8 bwd dW2")
+    _close(out["dX"], np.array(L["dX"]), 1e-12, "mx8 bwd dX")
+    _close(out["dW1"], np.array(L["dW1"]), 1e-12, "mx8 bwd dW1")
 
 
 def pin_bwd_mx8_grid_exact(O):
@@ -1309,6 +1318,113 @@ def pin_swiglu_mx8_sampled(O):
     _close(sm["dWd_rows"], b["dWd"][rows_Wd], 1e-12, "swiglu mx8 sampled dWd rows")
 
 
+def _mlp_mx8_case(seed, M, K, d, F):
+    g = _rng(seed)
+    return dict(X=g.standard_normal((M, K)), W1=g.standard_normal((K, d)) / math.sqrt(K),
+                R=g.standard_normal((M, d)), gamma=1 + 0.1 * g.standard_normal(d),
+                W=g.standard_normal((d, 2 * F)) / math.sqrt(d), Wd=g.standard_normal((F, d)) / math.sqrt(F),
+                dz=g.standard_normal((M, d)), dy_in=0.3 * g.standard_normal((M, d)), eps=1e-6)
+
+
+def pin_mlp_mx8_bruteforce(O):
+    """The MXFP8 MLP sub-layer by pure-Python loops (M = 64, K = d = F = 32):
+    y from the MXFP8 product, r, gu = r (y gamma quantised along d) W, a, z
+    from the stored a; the backward's SwiGLU part, then the block backward by
+    loops with dgu (stored) as its output gradient and dy_in added to dy."""
+    tab = _e4m3_table()
+    M, K, d, F = 64, 32, 32, 32
+    c = _mlp_mx8_case(98, M, K, d, F)
+    L = {k: (v.tolist() if isinstance(v, np.ndarray) else v) for k, v in c.items()}
+    sig = lambda t: 1.0 / (1.0 + math.exp(-t))  # noqa: E731
+    xw = _mx_matmul_loop(L["X"], L["W1"], tab)
+    y = [[xw[i][j] + L["R"][i][j] for j in range(d)] for i in range(M)]
+    r = [1.0 / math.sqrt(sum(v * v for v in y[i]) / d + c["eps"]) for i in range(M)]
+    yg = [[y[i][j] * L["gamma"][j] for j in range(d)] for i in range(M)]
+    p = _mx_matmul_loop(yg, L["W"], tab)
+    gu = [[r[i] * p[i][j] for j in range(2 * F)] for i in range(M)]
+    a = [[gu[i][j] * sig(gu[i][j]) * gu[i][F + j] for j in range(F)] for i in range(M)]
+    z = _mx_matmul_loop([[_bf16_loop(v) for v in row] for row in a], L["Wd"], tab)
+    f = O.ref_mlp_fwd_mx8(c["X"], c["W1"], c["R"], c["gamma"], c["W"], c["Wd"], c["eps"])
+    for k, v in (("y", y), ("r", r), ("gu", gu), ("a", a), ("z", z)):
+        _close(f[k], np.array(v), 1e-12, f"mlp mx8 {k} vs loops")
+    y_s = [[_bf16_loop(v) for v in row] for row in y]
+    gu_s = [[_bf16_loop(v) for v in row] for row in gu]
+    a_s = [[_bf16_loop(v) for v in row] for row in a]
+    b = O.ref_mlp_bwd_mx8(c["X"], c["W1"], c["gamma"], c["W"], c["Wd"], np.array(y_s), np.array(r),
+                          np.array(gu_s), np.array(a_s), c["dz"], c["dy_in"])
+    WdT = [[L["Wd"][j][k] for j in range(F)] for k in range(d)]
+    da = _mx_matmul_loop(L["dz"], WdT, tab)
+    dgu = []
+    for i in range(M):
+        rg, ru = [], []
+        for j in range(F):
+            g_, u_ = gu_s[i][j], gu_s[i][F + j]
+            sg = sig(g_)
+            rg.append(da[i][j] * u_ * sg * (1.0 + g_ * (1.0 - sg)))
+            ru.append(da[i][j] * g_ * sg)
+        dgu.append(rg + ru)
+    dgu_s = [[_bf16_loop(v) for v in row] for row in dgu]
+    B = _bwd_mx8_loops(L["X"], L["W1"], L["gamma"], L["W"], y_s, r, dgu_s, L["dy_in"], tab)
+    aT = [[a_s[i][j] for i in range(M)] for j in range(F)]
+    _close(b["dgu"], np.array(dgu), 1e-12, "mlp mx8 dgu vs loops")
+    _close(b["dWd"], np.array(_mx_matmul_loop(aT, L["dz"], tab)), 1e-12, "mlp mx8 dWd vs loops")
+    _close(b["dgamma"], np.array(B["dgamma"]), 1e-12, "mlp mx8 dgamma vs loops")
+    _close(O.bf16_rne(b["dR"]), np.array(B["dy"]), 1e-12, "mlp mx8 dR (stored) vs loops")
+    for k, kk in (("dW", "dW2"), ("dX", "dX"), ("dW1", "dW1")):
+        _close(b[k], np.array(B[kk]), 1e-12, f"mlp mx8 {k} vs loops")
+
+
+def pin_mlp_mx8_grid_exact(O):
+    """On the MXFP8 grid the MLP's quantised products are exact: X and W1 on
+    the grid along K give ref_mlp_fwd's y and r; dz and Wd on it along d,
+    the saved a and dz along M, give ref_mlp_bwd's da, dgu and dWd (with the
+    same saved gu and identity storage); and with dy_in, dR moves by dy_in
+    exactly (identity storage)."""
+    g = _rng(99)
+    M, K, d, F = 64, 64, 64, 64
+    c = _mlp_mx8_case(100, M, K, d, F)
+    X, W1 = _mx_grid(g, (M, K)), _mx_grid(g, (d, K)).T.copy()
+    q = O.ref_mlp_fwd_mx8(X, W1, c["R"], c["gamma"], c["W"], c["Wd"], c["eps"], store=lambda v: v)
+    e = O.ref_mlp_fwd(X, W1, c["R"], c["gamma"], c["W"], c["Wd"], c["eps"])
+    _close(q["y"], e["y"], 1e-13, "mlp mx8 y on grid operands")
+    _close(q["r"], e["r"], 1e-13, "mlp mx8 r on grid operands")
+    dz = _mx_grid_both(g, (M, d))
+    Wd = _mx_grid(g, (F, d))
+    a_saved = _mx_grid(g, (F, M)).T.copy()
+    gu = e["gu"]
+    ident = lambda v: v  # noqa: E731
+    qb = O.ref_mlp_bwd_mx8(X, W1, c["gamma"], c["W"], Wd, e["y"], e["r"], gu, a_saved, dz, None, ident)
+    eb = O.ref_mlp_bwd(X, W1, c["gamma"], c["W"], Wd, e["y"], e["r"], gu, a_saved, dz)
+    for k in ("da", "dgu", "dWd"):
+        _close(qb[k], eb[k], 1e-13, f"mlp mx8 {k} on grid operands")
+    qi = O.ref_mlp_bwd_mx8(X, W1, c["gamma"], c["W"], Wd, e["y"], e["r"], gu, a_saved, dz, c["dy_in"], ident)
+    _close(qi["dR"] - qb["dR"], c["dy_in"], 1e-13, "mlp mx8 dR moves by dy_in")
+
+
+def pin_mlp_mx8_sampled(O):
+    """The row and sampled forms equal slices of the full MXFP8 MLP forward
+    and backward."""
+    M, K, d, F = 96, 64, 64, 64
+    c = _mlp_mx8_case(101, M, K, d, F)
+    f = O.ref_mlp_fwd_mx8(c["X"], c["W1"], c["R"], c["gamma"], c["W"], c["Wd"], c["eps"])
+    rows = np.array([0, 45, 95])
+    fr = O.ref_mlp_fwd_mx8_rows(c["X"], c["W1"], c["R"], c["gamma"], c["W"], c["Wd"], c["eps"], rows)
+    for k in ("y", "r", "gu", "a", "z"):
+        _close(fr[k], f[k][rows], 1e-13, f"mlp mx8 rows {k}")
+    sv = {k: O.bf16_rne(f[k]) for k in ("y", "gu", "a")}
+    b = O.ref_mlp_bwd_mx8(c["X"], c["W1"], c["gamma"], c["W"], c["Wd"], sv["y"], f["r"], sv["gu"], sv["a"],
+                          c["dz"], c["dy_in"])
+    cd, c2, rF = np.array([0, 63]), np.array([1, 64, 127]), np.array([3, 60])
+    sm = O.ref_mlp_bwd_mx8_sampled(c["X"], c["W1"], c["gamma"], c["W"], c["Wd"], sv["y"], f["r"], sv["gu"],
+                                   sv["a"], c["dz"], c["dy_in"], rows, cd, c2, rF)
+    _close(sm["dX_rows"], b["dX"][rows], 1e-12, "mlp mx8 sampled dX rows")
+    _close(sm["dR_rows"], b["dR"][rows], 1e-12, "mlp mx8 sampled dR rows")
+    _close(sm["dW1_cols"], b["dW1"][:, cd], 1e-12, "mlp mx8 sampled dW1 cols")
+    _close(sm["dW_cols"], b["dW"][:, c2], 1e-12, "mlp mx8 sampled dW cols")
+    _close(sm["dWd_rows"], b["dWd"][rF], 1e-12, "mlp mx8 sampled dWd rows")
+    _close(sm["dgamma"], b["dgamma"], 1e-12, "mlp mx8 sampled dgamma")
+
+
 ALL_PINS = [
     pin_fwd_bruteforce, pin_fwd_torch_rmsnorm, pin_fwd_constant_rows,
     pin_fwd_scale_invariance, pin_partials, pin_rewrite_equals_unfused,
@@ -1324,5 +1440,5 @@ ALL_PINS = [
     pin_bwd_dy_in_finite_differences, pin_e4m3_codes, pin_mx_quantize, pin_fwd_mx8_exact,
     pin_fwd_mx8_bruteforce, pin_fwd_mx8_rows, pin_mx_matmul, pin_bwd_mx8_bruteforce,
     pin_bwd_mx8_grid_exact, pin_bwd_mx8_sampled, pin_swiglu_mx8_bruteforce, pin_swiglu_mx8_grid_exact,
-    pin_swiglu_mx8_sampled,
+    pin_swiglu_mx8_sampled, pin_mlp_mx8_bruteforce, pin_mlp_mx8_grid_exact, pin_mlp_mx8_sampled,
 ]
