@@ -466,6 +466,85 @@ class SwigluMx8Case(Mx8Case):
         return float((gu.float() - self.gu.float()).abs().max() / self.gu.float().abs().max())
 
 
+class MlpMx8Case(Mx8Case):
+    """The MLP sub-layer forward+backward (with dy_in) with every GEMM on MXFP8
+    operands; the unfused step is the same computation as torch ops (torch's
+    MXFP8 products on operands quantised by torch ops along the contraction
+    index, the norm, activation and their backward elementwise)."""
+
+    def __init__(self, w, torch, coda, h):
+        dev = torch.device("cuda:0")
+        self.w, self.torch, self.coda = w, torch, coda
+        bf = torch.bfloat16
+        self.t = {k: torch.from_numpy(v).to(dev).to(bf) for k, v in h.items()}
+        M, K, d, F = w.M, w.K, w.d, w.F
+        e = lambda *shape: torch.empty(shape, dtype=bf, device=dev)  # noqa: E731
+        self.y, self.gu, self.a, self.z = e(M, d), e(M, 2 * F), e(M, F), e(M, d)
+        self.r = torch.empty((M,), dtype=torch.float32, device=dev)
+        self.dX, self.dW1, self.dR, self.dW, self.dWd = e(M, K), e(K, d), e(M, d), e(d, 2 * F), e(F, d)
+        self.dg = torch.empty((d,), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(coda.mlp_fwd_mx8_workspace_bytes(M, K, d, F), dtype=torch.uint8, device=dev)
+        self.wsb = torch.empty(coda.mlp_bwd_mx8_workspace_bytes(M, K, d, F), dtype=torch.uint8, device=dev)
+        self.backward = w.backward
+        self.kernels_per_step = 7 + 5 + 11
+        self.leaf_names = ("X",)
+        self.manual_bwd = True
+
+    def fused_fwd(self):
+        t = self.t
+        self.coda.coda_mlp_fwd_mx8(t["X"], t["W1"], t["R"], t["gamma"], t["W"], t["Wd"], self.w.eps, self.y,
+                                   self.r, self.gu, self.a, self.z, self.ws)
+
+    def fused_bwd(self):
+        t = self.t
+        self.coda.coda_mlp_bwd_mx8(t["X"], t["W1"], t["gamma"], t["W"], t["Wd"], self.y, self.r, self.gu, self.a,
+                                   t["dz"], t["dy_in"], self.dX, self.dW1, self.dR, self.dW, self.dWd, self.dg,
+                                   self.wsb)
+
+    def unfused_fwd(self):
+        torch, t, q = self.torch, self.t, self._quantise
+        c = lambda v: v.contiguous()  # noqa: E731
+        F, d = self.w.F, self.w.d
+        y = self._mm(q(t["X"]), q(c(t["W1"].t()))) + t["R"]
+        r = torch.rsqrt(y.float().pow(2).mean(dim=1) + self.w.eps)
+        gu = (self._mm(q((y.float() * t["gamma"].float()).to(torch.bfloat16)), q(c(t["W"].t()))).float()
+              * r[:, None]).to(torch.bfloat16)
+        a = torch.nn.functional.silu(gu[:, :F]) * gu[:, F:]
+        self._saved = (y, r, gu, a)
+        return self._mm(q(a), q(c(t["Wd"].t())))
+
+    def unfused_bwd_manual(self):
+        torch, t, q = self.torch, self.t, self._quantise
+        c = lambda v: v.contiguous()  # noqa: E731
+        F, d = self.w.F, self.w.d
+        y, r, gu, a = self._saved if hasattr(self, "_saved") else (self.y, self.r, self.gu, self.a)
+        g, u = gu[:, :F].float(), gu[:, F:].float()
+        da = self._mm(q(t["dz"]), q(t["Wd"])).float()
+        sg = torch.sigmoid(g)
+        dgu = torch.cat([da * u * sg * (1.0 + g * (1.0 - sg)), da * g * sg], dim=1).to(torch.bfloat16)
+        dWd = self._mm(q(c(a.t())), q(c(t["dz"].t())))
+        dh = self._mm(q(dgu), q(t["W"]))
+        yf = y.float()
+        n = yf * r[:, None]
+        dgamma = (dh.float() * n).sum(0)
+        dn = (dh.float() * t["gamma"].float()).to(torch.bfloat16)
+        cc = r ** 3 * (dn.float() * yf).sum(1) / d
+        dy = (r[:, None] * dn.float() - cc[:, None] * yf + t["dy_in"].float()).to(torch.bfloat16)
+        dW = self._mm(q(c(n.to(torch.bfloat16).t())), q(c(dgu.t())))
+        dW = (dW.float() * t["gamma"].float()[:, None]).to(torch.bfloat16)
+        dX = self._mm(q(dy), q(t["W1"]))
+        dW1 = self._mm(q(c(t["X"].t())), q(c(dy.t())))
+        return dX, dW1, dy, dW, dWd, dgamma
+
+    def unfused_check(self):
+        """Relative difference between torch's first MXFP8 product + R and the
+        fused y (the same operands)."""
+        self.fused_fwd()
+        y = self._mm(self._quantise(self.t["X"]), self._quantise(self.t["W1"].t().contiguous())) + self.t["R"]
+        self.torch.cuda.synchronize()
+        return float((y.float() - self.y.float()).abs().max() / self.y.float().abs().max())
+
+
 class _Steps:
     """The fused and unfused step functions of a case: forward, backward, and
     the training step (forward + backward; the forward alone for a
@@ -521,7 +600,7 @@ def make_case(w, torch, coda):
     from gemm_epilogue_fusion_gemm1_amd import synth
     h = synth.workload_inputs(w)
     cls = {"coda": CodaCase, "swiglu": SwigluCase, "mlp": MlpCase, "ce": CeCase, "rope": RopeCase,
-           "mx8": Mx8Case, "swiglu_mx8": SwigluMx8Case}[w.kind]
+           "mx8": Mx8Case, "swiglu_mx8": SwigluMx8Case, "mlp_mx8": MlpMx8Case}[w.kind]
     return cls(w, torch, coda, h), h
 
 
@@ -659,7 +738,7 @@ def summary(case, res):
         out["speedup_vs_compiled_unfused"] = round(res["compiled_ms_per_step"] / res["ms_per_step"], 3)
     if "compiled_error" in res:
         out["compiled_unfused_error"] = res["compiled_error"]
-    if case.w.kind in ("mx8", "swiglu_mx8"):
+    if case.w.kind in ("mx8", "swiglu_mx8", "mlp_mx8"):
         out["pct_fp8_peak"] = round(100.0 * tf / PEAK_FP8_TFLOPS, 2)
     for part, fl in (("fwd", case.w.flops_fwd()), ("bwd", case.w.flops_bwd())):
         if f"{part}_ms" in res:
@@ -896,9 +975,11 @@ HEADLINE_SECOND = "llama70b_fwdbwd"
 STEP_CALLS = {"coda": "coda_fwd + coda_bwd", "swiglu": "coda_swiglu_fwd + coda_swiglu_bwd",
               "mlp": "coda_mlp_fwd + coda_mlp_bwd", "ce": "coda_ce_fwd + coda_ce_bwd",
               "rope": "coda_rope_fwd + coda_rope_bwd", "mx8": "coda_fwd_mx8 + coda_bwd_mx8",
-              "swiglu_mx8": "coda_swiglu_fwd_mx8 + coda_swiglu_bwd_mx8"}
+              "swiglu_mx8": "coda_swiglu_fwd_mx8 + coda_swiglu_bwd_mx8",
+              "mlp_mx8": "coda_mlp_fwd_mx8 + coda_mlp_bwd_mx8"}
 ALSO = ("swiglu_fwdbwd", "llama7b_mlp_fwdbwd", "llama7b_ce_fwdbwd", "llama3_8b_ce_fwdbwd",
-        "llama7b_qkv_rope_fwdbwd", "llama7b_fwd_mx8", "llama7b_fwdbwd_mx8", "swiglu_fwdbwd_mx8", "llama1b_fwd")
+        "llama7b_qkv_rope_fwdbwd", "llama7b_fwd_mx8", "llama7b_fwdbwd_mx8", "swiglu_fwdbwd_mx8",
+        "llama7b_mlp_fwdbwd_mx8", "llama1b_fwd")
 
 
 def _brief(s):
@@ -1011,7 +1092,7 @@ def main():
         "data": "synthetic (seeded normal inputs)",
         "config": {"workload": w.name,
                    **{k: getattr(w, k) for k in ("M", "K", "d", "N", "F") if getattr(w, k, 0)},
-                   **({"eps": w.eps} if w.kind in ("coda", "mlp", "mx8") else {}),
+                   **({"eps": w.eps} if w.kind in ("coda", "mlp", "mx8", "mlp_mx8") else {}),
                    "step": STEP_CALLS[w.kind] if w.backward else STEP_CALLS[w.kind].split(" + ")[0],
                    "parallelism": "single GPU"},
         "headline": headline,

@@ -40,6 +40,8 @@ __all__ = [
     "coda_mx8_quantize", "coda_fwd_mx8", "mx8_quantize", "fwd_mx8", "fwd_mx8_workspace_bytes",
     "coda_bwd_mx8", "bwd_mx8", "bwd_mx8_workspace_bytes", "coda_swiglu_fwd_mx8", "coda_swiglu_bwd_mx8",
     "swiglu_fwd_mx8", "swiglu_bwd_mx8", "swiglu_fwd_mx8_workspace_bytes", "swiglu_bwd_mx8_workspace_bytes",
+    "coda_mlp_fwd_mx8", "coda_mlp_bwd_mx8", "mlp_fwd_mx8", "mlp_bwd_mx8", "mlp_fwd_mx8_workspace_bytes",
+    "mlp_bwd_mx8_workspace_bytes",
     "mx8_scales_to_rowmajor", "mx8_scales_from_rowmajor",
     "version", "trace_start", "trace_read", "trace_stop",
 ]
@@ -97,6 +99,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "coda_bwd_mx8_workspace_bytes": [i64, i64, i64, i64],
         "coda_swiglu_fwd_mx8_workspace_bytes": [i64, i64, i64],
         "coda_swiglu_bwd_mx8_workspace_bytes": [i64, i64, i64],
+        "coda_mlp_fwd_mx8_workspace_bytes": [i64, i64, i64, i64],
+        "coda_mlp_bwd_mx8_workspace_bytes": [i64, i64, i64, i64],
     }.items():
         getattr(L, name).restype = sz
         getattr(L, name).argtypes = args
@@ -130,6 +134,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     L.coda_swiglu_fwd_mx8.argtypes = [i64, i64, i64] + [vp] * 6 + [vp, sz, vp]
     L.coda_swiglu_bwd_mx8.restype = i32
     L.coda_swiglu_bwd_mx8.argtypes = [i64, i64, i64] + [vp] * 9 + [vp, sz, vp]
+    L.coda_mlp_fwd_mx8.restype = i32
+    L.coda_mlp_fwd_mx8.argtypes = [i64, i64, i64, i64, f32] + [vp] * 11 + [vp, sz, vp]
+    L.coda_mlp_bwd_mx8.restype = i32
+    L.coda_mlp_bwd_mx8.argtypes = [i64, i64, i64, i64] + [vp] * 17 + [vp, sz, vp]
     L.coda_fwd_mx8.restype = i32
     L.coda_fwd_mx8.argtypes = [i64, i64, i64, i64, f32] + [vp] * 11 + [vp, sz, vp]
     L.coda_trace_start.restype = i32
@@ -538,6 +546,41 @@ def coda_swiglu_bwd_mx8(X, W, Wd, gu, a, dz, dX, dW, dWd, workspace):
     _check("coda_swiglu_bwd_mx8", load_library().coda_swiglu_bwd_mx8(M, d, F, *p, wp, wn, _stream()))
 
 
+def coda_mlp_fwd_mx8(X, W1, R, gamma, W, Wd, eps, y, r, gu, a, z, workspace):
+    """coda_mlp_fwd_mx8: the MLP sub-layer forward on MXFP8 GEMM operands
+    (bf16 tensors in and out, r float32, as coda_mlp_fwd)."""
+    import torch
+    c = _Args("coda_mlp_fwd_mx8", X, "X")
+    bf = torch.bfloat16
+    M, K = X.shape
+    d = W1.shape[1]
+    F = Wd.shape[0]
+    p = [c(X, "X", (M, K), bf), c(W1, "W1", (K, d), bf), c(R, "R", (M, d), bf), c(gamma, "gamma", (d,), bf),
+         c(W, "W", (d, 2 * F), bf), c(Wd, "Wd", (F, d), bf), c(y, "y", (M, d), bf),
+         c(r, "r", (M,), torch.float32), c(gu, "gu", (M, 2 * F), bf), c(a, "a", (M, F), bf), c(z, "z", (M, d), bf)]
+    wp, wn = c.ws(workspace)
+    _check("coda_mlp_fwd_mx8", load_library().coda_mlp_fwd_mx8(M, K, d, F, float(eps), *p, wp, wn, _stream()))
+
+
+def coda_mlp_bwd_mx8(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in, dX, dW1, dR, dW, dWd, dgamma, workspace):
+    """coda_mlp_bwd_mx8: the MLP sub-layer backward on MXFP8 GEMM operands
+    (dy_in may be None)."""
+    import torch
+    c = _Args("coda_mlp_bwd_mx8", X, "X")
+    bf = torch.bfloat16
+    M, K = X.shape
+    d = W1.shape[1]
+    F = Wd.shape[0]
+    p = [c(X, "X", (M, K), bf), c(W1, "W1", (K, d), bf), c(gamma, "gamma", (d,), bf),
+         c(W, "W", (d, 2 * F), bf), c(Wd, "Wd", (F, d), bf), c(y, "y", (M, d), bf),
+         c(r, "r", (M,), torch.float32), c(gu, "gu", (M, 2 * F), bf), c(a, "a", (M, F), bf),
+         c(dz, "dz", (M, d), bf), c(dy_in, "dy_in", (M, d), bf, optional=True), c(dX, "dX", (M, K), bf),
+         c(dW1, "dW1", (K, d), bf), c(dR, "dR", (M, d), bf), c(dW, "dW", (d, 2 * F), bf),
+         c(dWd, "dWd", (F, d), bf), c(dgamma, "dgamma", (d,), torch.float32)]
+    wp, wn = c.ws(workspace)
+    _check("coda_mlp_bwd_mx8", load_library().coda_mlp_bwd_mx8(M, K, d, F, *p, wp, wn, _stream()))
+
+
 # ------------------------------------------------------ convenience calls
 
 def mx8_scales_to_rowmajor(scales):
@@ -636,6 +679,49 @@ def swiglu_bwd_mx8(X, W, Wd, gu, a, dz):
     ws = _workspace(swiglu_bwd_mx8_workspace_bytes(M, d, F), X.device)
     coda_swiglu_bwd_mx8(X, W, Wd, gu, a, dz, dX, dW, dWd, ws)
     return dX, dW, dWd
+
+
+def mlp_fwd_mx8_workspace_bytes(M, K, d, F) -> int:
+    return int(load_library().coda_mlp_fwd_mx8_workspace_bytes(M, K, d, F))
+
+
+def mlp_bwd_mx8_workspace_bytes(M, K, d, F) -> int:
+    return int(load_library().coda_mlp_bwd_mx8_workspace_bytes(M, K, d, F))
+
+
+def mlp_fwd_mx8(X, W1, R, gamma, W, Wd, eps):
+    """The MLP sub-layer forward with its GEMMs on MXFP8 operands.  Returns
+    (z, y, r, gu, a)."""
+    import torch
+    M, K = X.shape
+    d = W1.shape[1]
+    F = Wd.shape[0]
+    y = torch.empty((M, d), dtype=X.dtype, device=X.device)
+    r = torch.empty((M,), dtype=torch.float32, device=X.device)
+    gu = torch.empty((M, 2 * F), dtype=X.dtype, device=X.device)
+    a = torch.empty((M, F), dtype=X.dtype, device=X.device)
+    z = torch.empty((M, d), dtype=X.dtype, device=X.device)
+    ws = _workspace(mlp_fwd_mx8_workspace_bytes(M, K, d, F), X.device)
+    coda_mlp_fwd_mx8(X, W1, R, gamma, W, Wd, eps, y, r, gu, a, z, ws)
+    return z, y, r, gu, a
+
+
+def mlp_bwd_mx8(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in=None):
+    """The MLP sub-layer backward with its GEMMs on MXFP8 operands.  Returns
+    (dX, dW1, dR, dW, dWd, dgamma)."""
+    import torch
+    M, K = X.shape
+    d = W1.shape[1]
+    F = Wd.shape[0]
+    dX = torch.empty_like(X)
+    dW1 = torch.empty_like(W1)
+    dR = torch.empty((M, d), dtype=X.dtype, device=X.device)
+    dW = torch.empty_like(W)
+    dWd = torch.empty_like(Wd)
+    dgamma = torch.empty((d,), dtype=torch.float32, device=X.device)
+    ws = _workspace(mlp_bwd_mx8_workspace_bytes(M, K, d, F), X.device)
+    coda_mlp_bwd_mx8(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in, dX, dW1, dR, dW, dWd, dgamma, ws)
+    return dX, dW1, dR, dW, dWd, dgamma
 
 
 def fwd(X, W1, R, gamma, W2, eps):

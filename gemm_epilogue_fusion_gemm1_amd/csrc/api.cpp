@@ -1099,42 +1099,14 @@ BwdMx8Ws bwd_mx8_ws(int64_t M, int64_t K, int64_t d, int64_t N) {
   w.total = o;
   return w;
 }
-}  // namespace
 
-extern "C" {
-
-size_t coda_bwd_mx8_workspace_bytes(int64_t M, int64_t K, int64_t d, int64_t N) {
-  if (M < 128 || K < 8 || d < 128 || N < 128 || M % 128 || d % 128 || N % 128) return 0;
-  return bwd_mx8_ws(M, K, d, N).total;
-}
-
-coda_status coda_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, const void* X, const void* W1,
-                         const void* gamma, const void* W2, const void* y, const float* r,
-                         const void* dz, void* dX, void* dW1, void* dR, void* dW2, float* dgamma,
-                         void* workspace, size_t workspace_bytes, void* stream) {
-  if (!X || !W1 || !gamma || !W2 || !y || !r || !dz || !dX || !dW1 || !dR || !dW2 || !dgamma)
-    return CODA_ERR_NULL;
-  // the contraction dimensions of the four GEMMs (N, M, d) are whole K steps
-  if (!mx_rows_ok(M, 128) || !mx_dim_ok(K, 8) || !mx_dim_ok(d, 128) || !mx_dim_ok(N, 128))
-    return CODA_ERR_SHAPE;
-  if (!fits(M, K, 2) || !fits(K, d, 2) || !fits(M, d, 2) || !fits(d, N, 2) || !fits(M, N, 2) ||
-      !scales_fit(M, N) || !scales_fit(d, N) || !scales_fit(N, M) || !scales_fit(d, M) ||
-      !scales_fit(M, d) || !scales_fit(K, d) || !scales_fit(K, M))
-    return CODA_ERR_SHAPE;
-  for (const void* p : {X, W1, gamma, W2, y, (const void*)r, dz, (const void*)dX, (const void*)dW1,
-                        (const void*)dR, (const void*)dW2, (const void*)dgamma})
-    if (!aligned16(p)) return CODA_ERR_ALIGN;
-  const BwdMx8Ws ws = bwd_mx8_ws(M, K, d, N);
-  if (!workspace || workspace_bytes < ws.total) return CODA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+// The MXFP8 backward of the block (coda_bwd_mx8; the MLP sub-layer's second
+// half with W2 = W, dz = dgu and dy_in): every argument already checked.
+coda_status norm_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, const void* X, const void* W1,
+                         const void* gamma, const void* W2, const void* y, const float* r, const void* dz,
+                         const void* dy_in, void* dX, void* dW1, void* dR, void* dW2, float* dgamma,
+                         void* workspace, const BwdMx8Ws& ws, hipStream_t s) {
   const size_t e = 2;
-  const Range in[] = {rng(X, M * K * e), rng(W1, K * d * e), rng(gamma, d * e), rng(W2, d * N * e),
-                      rng(y, M * d * e), rng(r, M * 4), rng(dz, M * N * e)};
-  const Range out[] = {rng(dX, M * K * e), rng(dW1, K * d * e), rng(dR, M * d * e),
-                       rng(dW2, d * N * e), rng(dgamma, d * 4), rng(workspace, ws.total)};
-  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
-
-  hipStream_t s = (hipStream_t)stream;
   char* wb = (char*)workspace;
   auto u8 = [&](size_t off) { return (uint8_t*)(wb + off); };
   float* S = (float*)(wb + ws.S);
@@ -1195,6 +1167,7 @@ coda_status coda_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, const void*
   qdy.r = r;
   qdy.c = c;
   qdy.y = y;
+  qdy.dy_in = dy_in;
   qdy.out = dR;
   qdy.qr = u8(ws.dyq);
   qdy.sr = u8(ws.dys);
@@ -1228,6 +1201,44 @@ coda_status coda_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, const void*
   GemmArgs b4 = gemm_mx8(K, d, M, u8(ws.XTq), u8(ws.XTs), u8(ws.dyTq), u8(ws.dyTs), dW1, d);
   return hip_status(traced("b4_gemm_mx8_dW1", gemm_flops(K, d, M), (mk + md) * q8 + kd * e, s,
                            [&] { return coda::launch_gemm_mx8(b4, coda::EPI_STORE, s); }));
+}
+}  // namespace
+
+extern "C" {
+
+size_t coda_bwd_mx8_workspace_bytes(int64_t M, int64_t K, int64_t d, int64_t N) {
+  if (M < 128 || K < 8 || d < 128 || N < 128 || M % 128 || d % 128 || N % 128) return 0;
+  return bwd_mx8_ws(M, K, d, N).total;
+}
+
+coda_status coda_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, const void* X, const void* W1,
+                         const void* gamma, const void* W2, const void* y, const float* r,
+                         const void* dz, void* dX, void* dW1, void* dR, void* dW2, float* dgamma,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!X || !W1 || !gamma || !W2 || !y || !r || !dz || !dX || !dW1 || !dR || !dW2 || !dgamma)
+    return CODA_ERR_NULL;
+  // the contraction dimensions of the four GEMMs (N, M, d) are whole K steps
+  if (!mx_rows_ok(M, 128) || !mx_dim_ok(K, 8) || !mx_dim_ok(d, 128) || !mx_dim_ok(N, 128))
+    return CODA_ERR_SHAPE;
+  if (!fits(M, K, 2) || !fits(K, d, 2) || !fits(M, d, 2) || !fits(d, N, 2) || !fits(M, N, 2) ||
+      !scales_fit(M, N) || !scales_fit(d, N) || !scales_fit(N, M) || !scales_fit(d, M) ||
+      !scales_fit(M, d) || !scales_fit(K, d) || !scales_fit(K, M))
+    return CODA_ERR_SHAPE;
+  for (const void* p : {X, W1, gamma, W2, y, (const void*)r, dz, (const void*)dX, (const void*)dW1,
+                        (const void*)dR, (const void*)dW2, (const void*)dgamma})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  const BwdMx8Ws ws = bwd_mx8_ws(M, K, d, N);
+  if (!workspace || workspace_bytes < ws.total) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const size_t e = 2;
+  const Range in[] = {rng(X, M * K * e), rng(W1, K * d * e), rng(gamma, d * e), rng(W2, d * N * e),
+                      rng(y, M * d * e), rng(r, M * 4), rng(dz, M * N * e)};
+  const Range out[] = {rng(dX, M * K * e), rng(dW1, K * d * e), rng(dR, M * d * e),
+                       rng(dW2, d * N * e), rng(dgamma, d * 4), rng(workspace, ws.total)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  return norm_bwd_mx8(M, K, d, N, X, W1, gamma, W2, y, r, dz, nullptr, dX, dW1, dR, dW2, dgamma, workspace, ws,
+                      (hipStream_t)stream);
 }
 
 }  // extern "C"
@@ -1423,6 +1434,232 @@ coda_status coda_swiglu_bwd_mx8(int64_t M, int64_t d, int64_t F, const void* X, 
   GemmArgs s6 = gemm_mx8(d, 2 * F, M, u8(ws.XTq), u8(ws.XTs), u8(ws.dguTq), u8(ws.dguTs), dW, 2 * F);
   return hip_status(traced("s6_gemm_mx8_dW", gemm_flops(d, 2 * F, M), (Md + 2.0 * MF) * q8 + 2.0 * dF * e, s,
                            [&] { return coda::launch_gemm_mx8(s6, coda::EPI_STORE, s); }));
+}
+
+// --------------------------------------------------- MXFP8 MLP sub-layer
+
+}  // extern "C"
+
+namespace {
+struct MlpMx8FwdWs {
+  size_t xq, xs, w1q, w1s, P, ygq, ygs, wq, ws, wdq, wds, aq, as, total;
+  int Tn;
+};
+MlpMx8FwdWs mlp_mx8_fwd_ws(int64_t M, int64_t K, int64_t d, int64_t F) {
+  MlpMx8FwdWs w{};
+  w.Tn = (int)cdiv(d, coda::kTileN);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += round_up(bytes); return at; };
+  auto mx = [&](size_t rows, size_t k, size_t& q, size_t& sc) { q = take(rows * k); sc = take(rows * (k / 32)); };
+  mx(M, K, w.xq, w.xs);          // X along K
+  mx(d, K, w.w1q, w.w1s);        // W1 along K, transposed
+  w.P = take((size_t)M * w.Tn * 4);
+  mx(M, d, w.ygq, w.ygs);        // y gamma along d (the first GEMM's epilogue)
+  mx(2 * F, d, w.wq, w.ws);      // W along d, transposed, gate/up order
+  mx(d, F, w.wdq, w.wds);        // Wd along F, transposed
+  mx(M, F, w.aq, w.as);          // a along F (the gate/up GEMM's epilogue)
+  w.total = o;
+  return w;
+}
+// The backward: the SwiGLU part's operands and dgu, then the block part's
+// workspace (coda_bwd_mx8's with N = 2F)
+struct MlpMx8BwdWs {
+  size_t dzq, dzs, dzTq, dzTs, wdq, wds, dgu, aTq, aTs, blk, total;
+  BwdMx8Ws b;
+};
+MlpMx8BwdWs mlp_mx8_bwd_ws(int64_t M, int64_t K, int64_t d, int64_t F) {
+  MlpMx8BwdWs w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += round_up(bytes); return at; };
+  auto mx = [&](size_t rows, size_t k, size_t& q, size_t& sc) { q = take(rows * k); sc = take(rows * (k / 32)); };
+  mx(M, d, w.dzq, w.dzs);
+  mx(d, M, w.dzTq, w.dzTs);
+  mx(F, d, w.wdq, w.wds);
+  w.dgu = take((size_t)M * 2 * F * 2);
+  mx(F, M, w.aTq, w.aTs);
+  w.b = bwd_mx8_ws(M, K, d, 2 * F);
+  w.blk = take(w.b.total);
+  w.total = o;
+  return w;
+}
+bool mlp_mx8_shape_ok(int64_t M, int64_t K, int64_t d, int64_t F) {
+  return mx_rows_ok(M, 128) && mx_dim_ok(K, 128) && swiglu_mx8_shape_ok(M, d, F) && fits(M, K, 2) &&
+         fits(K, d, 2) && scales_fit(M, K) && scales_fit(d, K) && scales_fit(K, d) && scales_fit(K, M);
+}
+}  // namespace
+
+extern "C" {
+
+size_t coda_mlp_fwd_mx8_workspace_bytes(int64_t M, int64_t K, int64_t d, int64_t F) {
+  if (!mlp_mx8_shape_ok(M, K, d, F)) return 0;
+  return mlp_mx8_fwd_ws(M, K, d, F).total;
+}
+
+size_t coda_mlp_bwd_mx8_workspace_bytes(int64_t M, int64_t K, int64_t d, int64_t F) {
+  if (!mlp_mx8_shape_ok(M, K, d, F)) return 0;
+  return mlp_mx8_bwd_ws(M, K, d, F).total;
+}
+
+coda_status coda_mlp_fwd_mx8(int64_t M, int64_t K, int64_t d, int64_t F, float eps, const void* X,
+                             const void* W1, const void* R, const void* gamma, const void* W, const void* Wd,
+                             void* y, float* r, void* gu, void* a, void* z, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!X || !W1 || !R || !gamma || !W || !Wd || !y || !r || !gu || !a || !z) return CODA_ERR_NULL;
+  if (!mlp_mx8_shape_ok(M, K, d, F)) return CODA_ERR_SHAPE;
+  if (!std::isfinite(eps) || !(eps > 0.0f)) return CODA_ERR_EPS;
+  for (const void* p : {X, W1, R, gamma, W, Wd, (const void*)y, (const void*)r, (const void*)gu, (const void*)a,
+                        (const void*)z})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  const MlpMx8FwdWs ws = mlp_mx8_fwd_ws(M, K, d, F);
+  if (!workspace || workspace_bytes < ws.total) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const size_t e = 2;
+  const Range in[] = {rng(X, M * K * e), rng(W1, K * d * e), rng(R, M * d * e), rng(gamma, d * e),
+                      rng(W, d * 2 * F * e), rng(Wd, F * d * e)};
+  const Range out[] = {rng(y, M * d * e), rng(r, M * 4), rng(gu, M * 2 * F * e), rng(a, M * F * e),
+                       rng(z, M * d * e), rng(workspace, ws.total)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wb = (char*)workspace;
+  auto u8 = [&](size_t off) { return (uint8_t*)(wb + off); };
+  float* P = (float*)(wb + ws.P);
+  hipError_t err;
+  const double q8 = 1.0 + 1.0 / 32.0, MK = (double)M * K, Kd = (double)K * d, Md = (double)M * d,
+               dF = (double)d * F, MF = (double)M * F;
+  // operands: X along K; W1 along K, transposed
+  if ((err = traced("x1_mx8_quantize_X", 0.0, MK * (e + q8), s, [&] {
+         return coda::launch_mx8_quantize(X, K, M, K, u8(ws.xq), u8(ws.xs), s);
+       })) != hipSuccess)
+    return hip_status(err);
+  if ((err = traced("x2_mx8_quantize_W1T", 0.0, Kd * (e + q8), s, [&] {
+         return coda::launch_mx8_quantize_t(W1, d, K, d, u8(ws.w1q), u8(ws.w1s), s);
+       })) != hipSuccess)
+    return hip_status(err);
+  // K1: y = X W1 + R on MXFP8; epilogue y, partial sums, y gamma along d
+  GemmArgs g1 = gemm_mx8(M, d, K, u8(ws.xq), u8(ws.xs), u8(ws.w1q), u8(ws.w1s), y, d);
+  g1.E = R;
+  g1.lde = d;
+  g1.part_row = P;
+  g1.ld_part_row = ws.Tn;
+  g1.vcol = gamma;
+  g1.q_out = u8(ws.ygq);
+  g1.qs_out = u8(ws.ygs);
+  g1.ldq = d;
+  if ((err = traced("k1_gemm_mx8_resid_sumsq", gemm_flops(M, d, K),
+                    (MK + Kd) * q8 + 2.0 * Md * e + Md * q8 + M * ws.Tn * 4.0 + d * e, s,
+                    [&] { return coda::launch_gemm_mx8(g1, coda::EPI_RESID_SUMSQ, s); })) != hipSuccess)
+    return hip_status(err);
+  // M1: [g | u] = diag(r) (y gamma) W on MXFP8; epilogue r from the partial
+  // sums, gu, a = silu(g) u (bf16) and a along F
+  coda::MxQuantArgs qw{};
+  qw.src = W;
+  qw.ld = 2 * F;
+  qw.rows = d;
+  qw.cols = 2 * F;
+  qw.qt = u8(ws.wq);
+  qw.st = u8(ws.ws);
+  qw.gated_F = F;
+  if ((err = traced("x3_mx8_quantize_W_gateup", 0.0, 2.0 * dF * (e + q8), s,
+                    [&] { return coda::launch_mx8_quantize_fused(qw, 0, s); })) != hipSuccess)
+    return hip_status(err);
+  GemmArgs m1 = gemm_mx8(M, F, d, u8(ws.ygq), u8(ws.ygs), u8(ws.wq), u8(ws.ws), gu, 2 * F);
+  m1.B_total = (uint64_t)(2 * F * d);
+  m1.B_bytes = (uint32_t)std::min<uint64_t>(m1.B_total, 0x7FFFFFF0ull);
+  m1.sB_bytes = (uint32_t)(2 * F * (d / 32));
+  m1.C2 = a;
+  m1.ldc2 = F;
+  m1.F = (int)F;
+  m1.q_out = u8(ws.aq);
+  m1.qs_out = u8(ws.as);
+  m1.ldq = F;
+  m1.part_row = P;
+  m1.ld_part_row = ws.Tn;
+  m1.nparts = ws.Tn;
+  m1.inv_d = 1.0f / (float)d;
+  m1.eps = eps;
+  m1.r_out = r;
+  if ((err = traced("m1_gemm_mx8_gateup_rsqrt_swiglu", gemm_flops(M, 2 * F, d),
+                    (Md + 2.0 * dF) * q8 + 3.0 * MF * e + MF * q8 + M * ws.Tn * 4.0 + 4.0 * M, s,
+                    [&] { return coda::launch_gemm_mx8(m1, coda::EPI_RSQRT_SWIGLU, s); })) != hipSuccess)
+    return hip_status(err);
+  // M2: z = a Wd on MXFP8
+  if ((err = traced("x4_mx8_quantize_WdT", 0.0, dF * (e + q8), s, [&] {
+         return coda::launch_mx8_quantize_t(Wd, d, F, d, u8(ws.wdq), u8(ws.wds), s);
+       })) != hipSuccess)
+    return hip_status(err);
+  GemmArgs m2 = gemm_mx8(M, d, F, u8(ws.aq), u8(ws.as), u8(ws.wdq), u8(ws.wds), z, d);
+  return hip_status(traced("m2_gemm_mx8_down", gemm_flops(M, d, F), (MF + dF) * q8 + Md * e, s,
+                           [&] { return coda::launch_gemm_mx8(m2, coda::EPI_STORE, s); }));
+}
+
+coda_status coda_mlp_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t F, const void* X, const void* W1,
+                             const void* gamma, const void* W, const void* Wd, const void* y, const float* r,
+                             const void* gu, const void* a, const void* dz, const void* dy_in, void* dX,
+                             void* dW1, void* dR, void* dW, void* dWd, float* dgamma, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!X || !W1 || !gamma || !W || !Wd || !y || !r || !gu || !a || !dz || !dX || !dW1 || !dR || !dW || !dWd ||
+      !dgamma)
+    return CODA_ERR_NULL;
+  if (!mlp_mx8_shape_ok(M, K, d, F)) return CODA_ERR_SHAPE;
+  for (const void* p : {X, W1, gamma, W, Wd, y, (const void*)r, gu, a, dz, (const void*)dX, (const void*)dW1,
+                        (const void*)dR, (const void*)dW, (const void*)dWd, (const void*)dgamma})
+    if (!aligned16(p)) return CODA_ERR_ALIGN;
+  if (dy_in && !aligned16(dy_in)) return CODA_ERR_ALIGN;
+  const MlpMx8BwdWs ws = mlp_mx8_bwd_ws(M, K, d, F);
+  if (!workspace || workspace_bytes < ws.total) return CODA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CODA_ERR_ALIGN;
+  const size_t e = 2;
+  const Range in[] = {rng(X, M * K * e), rng(W1, K * d * e), rng(gamma, d * e), rng(W, d * 2 * F * e),
+                      rng(Wd, F * d * e), rng(y, M * d * e), rng(r, M * 4), rng(gu, M * 2 * F * e),
+                      rng(a, M * F * e), rng(dz, M * d * e), rng(dy_in, dy_in ? M * d * e : 0)};
+  const Range out[] = {rng(dX, M * K * e), rng(dW1, K * d * e), rng(dR, M * d * e), rng(dW, d * 2 * F * e),
+                       rng(dWd, F * d * e), rng(dgamma, d * 4), rng(workspace, ws.total)};
+  if (!alias_free(in, out)) return CODA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wb = (char*)workspace;
+  auto u8 = [&](size_t off) { return (uint8_t*)(wb + off); };
+  void* dgu = wb + ws.dgu;
+  hipError_t err;
+  const double q8 = 1.0 + 1.0 / 32.0, Md = (double)M * d, dF = (double)d * F, MF = (double)M * F;
+  // the SwiGLU part: dz along d and along M (one pass), Wd along d
+  coda::MxQuantArgs qdz{};
+  qdz.src = dz;
+  qdz.ld = d;
+  qdz.rows = M;
+  qdz.cols = d;
+  qdz.qr = u8(ws.dzq);
+  qdz.sr = u8(ws.dzs);
+  qdz.qt = u8(ws.dzTq);
+  qdz.st = u8(ws.dzTs);
+  if ((err = traced("w1_mx8_quantize_dz_both", 0.0, Md * (e + 2.0 * q8), s,
+                    [&] { return coda::launch_mx8_quantize_fused(qdz, 0, s); })) != hipSuccess)
+    return hip_status(err);
+  if ((err = traced("w2_mx8_quantize_Wd", 0.0, dF * (e + q8), s, [&] {
+         return coda::launch_mx8_quantize(Wd, d, F, d, u8(ws.wdq), u8(ws.wds), s);
+       })) != hipSuccess)
+    return hip_status(err);
+  // M3: da = dz Wd^T on MXFP8; epilogue dgu from the saved gu
+  GemmArgs m3 = gemm_mx8(M, F, d, u8(ws.dzq), u8(ws.dzs), u8(ws.wdq), u8(ws.wds), dgu, 2 * F);
+  m3.E = gu;
+  m3.lde = 2 * F;
+  m3.F = (int)F;
+  if ((err = traced("m3_gemm_mx8_da_swiglu_bwd", gemm_flops(M, F, d), (Md + dF) * q8 + 4.0 * MF * e, s,
+                    [&] { return coda::launch_gemm_mx8(m3, coda::EPI_SWIGLU_BWD, s); })) != hipSuccess)
+    return hip_status(err);
+  // M4: dWd = a^T dz on MXFP8: a along M, transposed
+  if ((err = traced("w3_mx8_quantize_aT", 0.0, MF * (e + q8), s, [&] {
+         return coda::launch_mx8_quantize_t(a, F, M, F, u8(ws.aTq), u8(ws.aTs), s);
+       })) != hipSuccess)
+    return hip_status(err);
+  GemmArgs m4 = gemm_mx8(F, d, M, u8(ws.aTq), u8(ws.aTs), u8(ws.dzTq), u8(ws.dzTs), dWd, d);
+  if ((err = traced("m4_gemm_mx8_dWd", gemm_flops(F, d, M), (MF + Md) * q8 + dF * e, s,
+                    [&] { return coda::launch_gemm_mx8(m4, coda::EPI_STORE, s); })) != hipSuccess)
+    return hip_status(err);
+  // the block's MXFP8 backward with dz = dgu, W2 = W (N = 2F) and dy_in
+  return norm_bwd_mx8(M, K, d, 2 * F, X, W1, gamma, W, y, r, dgu, dy_in, dX, dW1, dR, dW, dgamma,
+                      wb + ws.blk, ws.b, s);
 }
 
 }  // extern "C"

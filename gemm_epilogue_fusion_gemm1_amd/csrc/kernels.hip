@@ -1317,8 +1317,9 @@ __global__ void __launch_bounds__(256) mx8_quantize_t_kernel(const __bf16* __res
 //              sr [cols/128][rows][4]; cols % 128 == 0) and along the column,
 //              stored transposed (codes qt [cols][rows], scales st
 //              [rows/128][cols][4]) -- dz for the dh and dW2 GEMMs;
-//   QUANT_DY:  v = dy = r_i dn - c_i y (bf16), written over dn (src = out =
-//              dR); quantised both ways -- dy for the dX and dW1 GEMMs;
+//   QUANT_DY:  v = dy = r_i dn - c_i y (+ dy_in when given; bf16), written
+//              over dn (src = out = dR); quantised both ways -- dy for the
+//              dX and dW1 GEMMs;
 //   QUANT_NROW: v = n = r_i y (bf16; src = y); quantised along the column
 //              only -- n for the dW2 GEMM.
 // With qr NULL only the transposed codes are made; with gated_F > 0 (a
@@ -1349,8 +1350,14 @@ __global__ void __launch_bounds__(256) mx8_quantize_fused_kernel(MxQuantArgs q) 
       } else if constexpr (MODE == QUANT_DY) {
         const bf16x8 yv = *(const bf16x8*)((const __bf16*)q.y + row * q.ld + col);
         const float ri = q.r[row], ci = q.c[row];
+        if (q.dy_in) {
+          const bf16x8 din = *(const bf16x8*)((const __bf16*)q.dy_in + row * q.ld + col);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = f2bf(ri * bf2f(a[e]) - ci * bf2f(yv[e]));
+          for (int e = 0; e < 8; ++e) v[e] = f2bf(ri * bf2f(a[e]) - ci * bf2f(yv[e]) + bf2f(din[e]));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = f2bf(ri * bf2f(a[e]) - ci * bf2f(yv[e]));
+        }
         *(bf16x8*)((__bf16*)q.out + row * q.ld + col) = v;
       } else {
         const float ri = q.r[row];
@@ -1668,7 +1675,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStr
 
 template <int EPI>
 static hipError_t launch_mx8_one(const GemmArgs& g, hipStream_t s) {
-  constexpr bool gated = EPI == EPI_SWIGLU;
+  constexpr bool gated = EPI == EPI_SWIGLU || EPI == EPI_RSQRT_SWIGLU;
   const int tiles = ((g.M + BM - 1) / BM) * (gated ? (g.N + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN);
   if (needs_windows(g))
     hipLaunchKernelGGL((gemm_mx8_kernel<kMxWavesM, kMxWavesN, EPI, true>), dim3(tiles),
@@ -1687,6 +1694,7 @@ hipError_t launch_gemm_mx8(const GemmArgs& g, Epi epi, hipStream_t s) {
     case EPI_DN: return launch_mx8_one<EPI_DN>(g, s);
     case EPI_ROWSCALE: return launch_mx8_one<EPI_ROWSCALE>(g, s);
     case EPI_SWIGLU: return launch_mx8_one<EPI_SWIGLU>(g, s);
+    case EPI_RSQRT_SWIGLU: return launch_mx8_one<EPI_RSQRT_SWIGLU>(g, s);
     case EPI_SWIGLU_BWD: return launch_mx8_one<EPI_SWIGLU_BWD>(g, s);
     default: return hipErrorInvalidValue;
   }

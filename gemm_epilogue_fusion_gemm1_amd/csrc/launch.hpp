@@ -78,7 +78,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool a_kmajor, bool b_kmajor, Epi
 hipError_t launch_gemm_f32(const GemmArgs& g, Epi epi, hipStream_t stream);
 // MXFP8 x MXFP8 GEMM, both operands K-contiguous (A [M][K], B^T [N][K]);
 // K % 128 == 0; epilogues EPI_STORE, EPI_RESID_SUMSQ (with q_out),
-// EPI_RSQRT_SCALE, EPI_DN, EPI_ROWSCALE
+// EPI_RSQRT_SCALE, EPI_DN, EPI_ROWSCALE, EPI_SWIGLU and EPI_RSQRT_SWIGLU
+// (B = the gate/up weight's 2F rows in gate/up order; a quantised into
+// q_out along F), EPI_SWIGLU_BWD
 hipError_t launch_gemm_mx8(const GemmArgs& g, Epi epi, hipStream_t stream);
 // codes / scales = the MXFP8 quantisation of src [rows, cols] (bf16, row
 // stride ld) along its rows, stored transposed: codes [cols][rows], scales
@@ -93,7 +95,8 @@ hipError_t launch_mx8_quantize(const void* src, int64_t ld, int64_t rows, int64_
 
 // One pass over a bf16 [rows, cols] tensor (row stride ld) that makes MXFP8
 // operands of the backward (rows % 128 == 0).  mode 0: v = src; mode 1: v =
-// dy = r_i src - c_i y, rounded to bf16 and written to out (out may be src);
+// dy = r_i src - c_i y (+ dy_in unless NULL), rounded to bf16 and written to
+// out (out may be src);
 // mode 2: v = r_i src rounded to bf16.  qr / sr: v quantised along the row
 // (codes [rows][cols], scales step-blocked [cols/128][rows][4]; cols % 128 ==
 // 0; not made in mode 2); qt / st: v quantised along the column, stored
@@ -105,7 +108,7 @@ hipError_t launch_mx8_quantize(const void* src, int64_t ld, int64_t rows, int64_
 struct MxQuantArgs {
   const void* src; int64_t ld;
   int64_t rows, cols;
-  const float* r; const float* c; const void* y; void* out;
+  const float* r; const float* c; const void* y; const void* dy_in; void* out;
   uint8_t* qr; uint8_t* sr;
   uint8_t* qt; uint8_t* st;
   int64_t gated_F;

@@ -30,8 +30,9 @@ class Workload:
     kind: str            # "coda" (GEMM-Residual-RMSNorm-GEMM), "swiglu", "mlp" (the two
                          # chained), "ce" (LM-head GEMM + cross-entropy), "rope"
                          # (QKV projection with rotary positions in its epilogue),
-                         # "mx8" (the coda block on MXFP8 operands) or "swiglu_mx8"
-                         # (the SwiGLU block on MXFP8 operands)
+                         # "mx8" (the coda block on MXFP8 operands), "swiglu_mx8"
+                         # (the SwiGLU block on MXFP8 operands) or "mlp_mx8" (the MLP
+                         # sub-layer on MXFP8 operands)
     dtype: str           # "f32", "bf16" or "mxfp8" (bf16 draws, quantised by the caller)
     M: int
     K: int = 0           # coda, mlp: GEMM1 reduction width
@@ -56,7 +57,7 @@ class Workload:
         if self.kind == "rope":
             return 2.0 * self.M * self.K * self.N
         swiglu = 2.0 * self.M * self.d * 2 * self.F + 2.0 * self.M * self.F * self.d
-        if self.kind == "mlp":
+        if self.kind in ("mlp", "mlp_mx8"):
             return 2.0 * self.M * self.K * self.d + swiglu
         return swiglu
 
@@ -113,6 +114,10 @@ WORKLOADS = {
                  seed=1011, backward=True,
                  note="SwiGLU block forward+backward (the swiglu_fwdbwd shape) with every "
                       "GEMM on MXFP8 operands (bf16 draws, quantised by the calls)"),
+        Workload("llama7b_mlp_fwdbwd_mx8", "mlp_mx8", "mxfp8", M=8192, K=4096, d=4096, F=11008,
+                 eps=1e-6, seed=1012, backward=True,
+                 note="LLaMA-7B-shaped MLP sub-layer forward+backward with dy_in (the "
+                      "llama7b_mlp_fwdbwd shape) with every GEMM on MXFP8 operands"),
     ]
 }
 
@@ -243,4 +248,6 @@ def workload_inputs(w: Workload, with_dz: bool | None = None) -> dict:
         return mx8_inputs(w.M, w.K, w.d, w.N, w.seed, with_dz)
     if w.kind == "swiglu_mx8":     # bf16 draws; the MXFP8 calls quantise them
         return swiglu_inputs(w.M, w.d, w.F, w.seed, "bf16", with_dz)
+    if w.kind == "mlp_mx8":
+        return mlp_inputs(w.M, w.K, w.d, w.F, w.seed, "bf16", with_dz)
     return swiglu_inputs(w.M, w.d, w.F, w.seed, w.dtype, with_dz)

@@ -462,6 +462,39 @@ coda_status coda_swiglu_bwd_mx8(int64_t M, int64_t d, int64_t F, const void* X, 
                                 void* stream);
 
 /* ------------------------------------------------------------------------
+ * The MLP sub-layer (coda_mlp_fwd / coda_mlp_bwd) with every GEMM on the
+ * MXFP8 matrix units: the block's MXFP8 reading (coda_fwd_mx8,
+ * coda_bwd_mx8) and the SwiGLU block's (coda_swiglu_fwd_mx8) composed.
+ *   y  = X W1 + R          X and W1 along K; the epilogue stores y (bf16), the
+ *                          partial sums of squares and y diag(gamma) quantised
+ *                          along d (from the unrounded y)
+ *   [g | u] = diag(r) (y diag(gamma)) W   along d; r from the partial sums in
+ *                          the epilogue; gu, a = silu(g) u stored in bf16, a
+ *                          also quantised along F
+ *   z  = a Wd              along F
+ * and the backward is the gradient of the unquantised sub-layer (with dy_in,
+ * as coda_mlp_bwd): da = dz Wd^T (along d; dgu from the saved gu), dWd = a^T
+ * dz (along M), then the block's MXFP8 backward with dz := dgu (rounded to
+ * bf16) and W2 := W, dy_in added to dy.  Tensors bf16 as coda_mlp_fwd /
+ * coda_mlp_bwd (r and dgamma float32); the calls quantise them.
+ *   M, K, d, F: multiples of 128.  dy_in: [M,d] or NULL.
+ *   workspace: >= the matching _workspace_bytes(M, K, d, F) bytes, 16-byte
+ *   aligned; the query returns 0 for a shape the calls refuse.
+ * Errors as coda_mlp_fwd / coda_mlp_bwd.
+ * ---------------------------------------------------------------------- */
+size_t coda_mlp_fwd_mx8_workspace_bytes(int64_t M, int64_t K, int64_t d, int64_t F);
+coda_status coda_mlp_fwd_mx8(int64_t M, int64_t K, int64_t d, int64_t F, float eps, const void* X,
+                             const void* W1, const void* R, const void* gamma, const void* W, const void* Wd,
+                             void* y, float* r, void* gu, void* a, void* z, void* workspace,
+                             size_t workspace_bytes, void* stream);
+size_t coda_mlp_bwd_mx8_workspace_bytes(int64_t M, int64_t K, int64_t d, int64_t F);
+coda_status coda_mlp_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t F, const void* X, const void* W1,
+                             const void* gamma, const void* W, const void* Wd, const void* y, const float* r,
+                             const void* gu, const void* a, const void* dz, const void* dy_in, void* dX,
+                             void* dW1, void* dR, void* dW, void* dWd, float* dgamma, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Kernel tracing (measurement aid; off by default).
  *
  * coda_trace_start(capacity) creates 2*capacity timing events (host call,

@@ -443,3 +443,50 @@ def test_swiglu_mx8_rejects(L, bwd):
     out = "dX" if bwd else "z"
     assert swiglu_mx8_call(L, bwd, X=x, **{out: x}) == ALIAS
     assert swiglu_mx8_call(L, bwd, W=ctypes.c_void_p(m(4096).value + 4)) == ALIGN
+
+
+def mlp_mx8_call(L, bwd, **over):
+    m = FakeMem()
+    M, K, d, F = 256, 128, 128, 256
+    a = dict(M=M, K=K, d=d, F=F, eps=1e-6, X=m(M * K * 2), W1=m(K * d * 2), R=m(M * d * 2), gamma=m(d * 2),
+             W=m(d * 2 * F * 2), Wd=m(F * d * 2), y=m(M * d * 2), r=m(M * 4), gu=m(M * 2 * F * 2),
+             a=m(M * F * 2), z=m(M * d * 2), dz=m(M * d * 2), dy_in=m(M * d * 2), dX=m(M * K * 2),
+             dW1=m(K * d * 2), dR=m(M * d * 2), dW=m(d * 2 * F * 2), dWd=m(F * d * 2), dg=m(d * 4))
+    q = L.coda_mlp_bwd_mx8_workspace_bytes if bwd else L.coda_mlp_fwd_mx8_workspace_bytes
+    a["ws_bytes"] = q(M, K, d, F)
+    a["ws"] = m(a["ws_bytes"])
+    a.update(over)
+    if bwd:
+        return L.coda_mlp_bwd_mx8(a["M"], a["K"], a["d"], a["F"], a["X"], a["W1"], a["gamma"], a["W"], a["Wd"],
+                                  a["y"], a["r"], a["gu"], a["a"], a["dz"], a["dy_in"], a["dX"], a["dW1"], a["dR"],
+                                  a["dW"], a["dWd"], a["dg"], a["ws"], a["ws_bytes"], None)
+    return L.coda_mlp_fwd_mx8(a["M"], a["K"], a["d"], a["F"], a["eps"], a["X"], a["W1"], a["R"], a["gamma"],
+                              a["W"], a["Wd"], a["y"], a["r"], a["gu"], a["a"], a["z"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("bwd", [False, True], ids=["fwd", "bwd"])
+def test_mlp_mx8_rejects(L, bwd):
+    """The MXFP8 MLP calls need M, K, d, F in whole 128-element blocks and
+    check pointers, eps, alignment, aliasing and the workspace before any HIP
+    call; dy_in is optional."""
+    q = L.coda_mlp_bwd_mx8_workspace_bytes if bwd else L.coda_mlp_fwd_mx8_workspace_bytes
+    assert q(256, 128, 128, 256) > 0
+    for bad in ((200, 128, 128, 256), (256, 136, 128, 256), (256, 128, 136, 256), (256, 128, 128, 264)):
+        assert q(*bad) == 0
+    assert mlp_mx8_call(L, bwd, X=None) == NULL
+    assert mlp_mx8_call(L, bwd, gamma=None) == NULL
+    assert mlp_mx8_call(L, bwd, M=200) == SHAPE
+    assert mlp_mx8_call(L, bwd, K=136) == SHAPE
+    assert mlp_mx8_call(L, bwd, F=264) == SHAPE
+    assert mlp_mx8_call(L, bwd, ws_bytes=1024) == WORKSPACE
+    m = FakeMem()
+    x = m(1 << 22)
+    out = "dX" if bwd else "z"
+    assert mlp_mx8_call(L, bwd, X=x, **{out: x}) == ALIAS
+    assert mlp_mx8_call(L, bwd, W1=ctypes.c_void_p(m(4096).value + 4)) == ALIGN
+    if bwd:
+        d_ = m(1 << 20)
+        assert mlp_mx8_call(L, bwd, dy_in=d_, dR=d_) == ALIAS
+        assert mlp_mx8_call(L, bwd, dy_in=ctypes.c_void_p(m(4096).value + 8)) == ALIGN
+    else:
+        assert mlp_mx8_call(L, bwd, eps=0.0) == EPS

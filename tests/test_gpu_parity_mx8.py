@@ -413,3 +413,133 @@ def test_full_workload_swiglu_mx8(torch_dev):
     report(w.name, errs)
     for k, v in errs.items():
         assert v <= BF16_TOL, (k, v)
+
+
+# ----------------------------------------------------------- MLP sub-layer
+
+SMALL_MLP_MX8 = [
+    (128, 128, 128, 128),        # smallest accepted
+    (256, 384, 256, 384),
+    (384, 256, 384, 640),        # F not a multiple of the 256-column tile
+    (640, 1152, 256, 128),       # several row tiles, long K
+]
+R_ELEM_TOL = 1e-3
+# Behind a quantisation point (y*gamma, a, dgu, dn/n/dy) the GPU rounds values
+# that differ from the oracle's by the matrix instruction's accumulation
+# error, so an E4M3 code flips wherever a value lies that close to a rounding
+# boundary, and a flip moves its element by one E4M3 step.  Four such points
+# in a row make the outputs' max-norm error a matter of which flips land
+# where; the bar there is normwise (Frobenius) 2e-2, with 1e-1 on the
+# max-norm as a guard.  An emulation of the chain with every GPU-computed
+# product perturbed by 2^-12 (relative) gives 1.0-1.8e-2 normwise and up to
+# 6e-2 max-norm at these shapes; a wiring mistake (an operand, a scale
+# layout, dy_in) moves the normwise error far beyond 5e-2.
+CHAIN_NORM_TOL = 2e-2
+CHAIN_MAX_TOL = 1e-1
+
+
+def nrel(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(got - ref)) / max(float(np.linalg.norm(ref)), 1e-300)
+
+
+def _check_chain(errs, nerrs, keys):
+    for k in keys:
+        assert nerrs[k] <= CHAIN_NORM_TOL, (k, "normwise", nerrs[k])
+        assert errs[k] <= CHAIN_MAX_TOL, (k, "max-norm", errs[k])
+
+
+def _mlp_mx8_gpu(torch, dev, h, saved=None):
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    t = {k: bf(torch, dev, v) for k, v in h.items()}
+    if saved is None:
+        out = coda.mlp_fwd_mx8(t["X"], t["W1"], t["R"], t["gamma"], t["W"], t["Wd"], 1e-6)
+    else:
+        y, r, gu, a = saved
+        out = coda.mlp_bwd_mx8(t["X"], t["W1"], t["gamma"], t["W"], t["Wd"], y, r, gu, a, t["dz"], t["dy_in"])
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("shape", SMALL_MLP_MX8, ids=lambda s: "x".join(map(str, s)))
+def test_mlp_mx8(torch_dev, shape):
+    """Forward against ``ref_mlp_fwd_mx8``; the backward (with dy_in), fed the
+    oracle's saved y, r, gu and a, against ``ref_mlp_bwd_mx8``."""
+    torch, dev = torch_dev
+    M, K, d, F = shape
+    h = synth.mlp_inputs(M, K, d, F, seed=860 + M + F)
+    z, y, r, gu, a = _mlp_mx8_gpu(torch, dev, h)
+    f = oracle.ref_mlp_fwd_mx8(h["X"], h["W1"], h["R"], h["gamma"], h["W"], h["Wd"], 1e-6)
+    g = lambda v: v.float().cpu().numpy()  # noqa: E731
+    errs = {"y": rel(g(y), f["y"]), "gu": rel(g(gu), f["gu"]), "a": rel(g(a), f["a"]), "z": rel(g(z), f["z"])}
+    rr = float(np.max(np.abs(r.cpu().numpy() - f["r"]) / f["r"]))
+    sv = {k: oracle.bf16_rne(f[k]) for k in ("y", "gu", "a")}
+    saved = (bf(torch, dev, sv["y"]), torch.from_numpy(np.asarray(f["r"], np.float32)).to(dev),
+             bf(torch, dev, sv["gu"]), bf(torch, dev, sv["a"]))
+    dX, dW1, dR, dW, dWd, dg = _mlp_mx8_gpu(torch, dev, h, saved)
+    b = oracle.ref_mlp_bwd_mx8(h["X"], h["W1"], h["gamma"], h["W"], h["Wd"], sv["y"], f["r"], sv["gu"], sv["a"],
+                               h["dz"], h["dy_in"])
+    errs.update(dX=rel(g(dX), b["dX"]), dW1=rel(g(dW1), b["dW1"]), dR=rel(g(dR), b["dR"]), dW=rel(g(dW), b["dW"]),
+                dWd=rel(g(dWd), b["dWd"]), dgamma=rel(dg.cpu().numpy(), b["dgamma"]))
+    outs = {"gu": (gu, f["gu"]), "a": (a, f["a"]), "z": (z, f["z"]), "dX": (dX, b["dX"]), "dW1": (dW1, b["dW1"]),
+            "dR": (dR, b["dR"]), "dW": (dW, b["dW"]), "dWd": (dWd, b["dWd"]), "dgamma": (dg, b["dgamma"])}
+    nerrs = {k: nrel(g(v), ref) for k, (v, ref) in outs.items()}
+    report(f"mlp mx8 {shape}", {**errs, "r": rr})
+    report(f"mlp mx8 {shape} normwise", nerrs)
+    assert rr <= R_ELEM_TOL
+    assert errs["y"] <= BF16_TOL
+    _check_chain(errs, nerrs, outs)
+
+
+def test_mlp_mx8_deterministic(torch_dev):
+    torch, dev = torch_dev
+    h = synth.mlp_inputs(384, 256, 384, 640, seed=870)
+    f1 = _mlp_mx8_gpu(torch, dev, h)
+    f2 = _mlp_mx8_gpu(torch, dev, h)
+    b1 = _mlp_mx8_gpu(torch, dev, h, f1[1:])
+    b2 = _mlp_mx8_gpu(torch, dev, h, f1[1:])
+    for x_, y_ in zip(f1 + b1, f2 + b2):
+        assert torch.equal(x_, y_)
+
+
+def test_full_workload_mlp_mx8(torch_dev):
+    """The LLaMA-7B MLP shape on MXFP8 (M = 8192, K = d = 4096, F = 11008, with
+    dy_in): forward rows; the backward, fed the GPU forward's saved tensors,
+    on stratified rows and columns with dgamma in full, against the oracle's
+    chain (its own forward, saved tensors rounded to bf16)."""
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    w = synth.WORKLOADS["llama7b_mlp_fwdbwd_mx8"]
+    print(f"[parity] {w.name}: inputs", flush=True)
+    h = synth.workload_inputs(w)
+    t = {k: bf(torch, dev, v) for k, v in h.items()}
+    z, y, r, gu, a = coda.mlp_fwd_mx8(t["X"], t["W1"], t["R"], t["gamma"], t["W"], t["Wd"], w.eps)
+    dX, dW1, dR, dW, dWd, dg = coda.mlp_bwd_mx8(t["X"], t["W1"], t["gamma"], t["W"], t["Wd"], y, r, gu, a, t["dz"],
+                                               t["dy_in"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed)
+    strata = lambda n, band: np.unique(np.concatenate([[0, n - 1], [rng.integers(b0, min(b0 + band, n)) for b0 in range(0, n, band)]]))  # noqa: E731
+    rows, cd, c2, rF = strata(w.M, 128), strata(w.d, 64), strata(2 * w.F, 64), strata(w.F, 64)
+    print(f"[parity] {w.name}: oracle forward (full: the backward needs every row)", flush=True)
+    f = oracle.ref_mlp_fwd_mx8(h["X"], h["W1"], h["R"], h["gamma"], h["W"], h["Wd"], w.eps)
+    g = lambda v: v.float().cpu().numpy()  # noqa: E731
+    errs = {"z_rows": rel(g(z[rows]), f["z"][rows]), "y_rows": rel(g(y[rows]), f["y"][rows]),
+            "gu_rows": rel(g(gu[rows]), f["gu"][rows]), "a_rows": rel(g(a[rows]), f["a"][rows])}
+    rr = float(np.max(np.abs(r.cpu().numpy() - f["r"]) / f["r"]))
+    print(f"[parity] {w.name}: oracle backward (sampled)", flush=True)
+    sv = {k: oracle.bf16_rne(f[k]) for k in ("y", "gu", "a")}
+    b = oracle.ref_mlp_bwd_mx8_sampled(h["X"], h["W1"], h["gamma"], h["W"], h["Wd"], sv["y"], f["r"], sv["gu"],
+                                       sv["a"], h["dz"], h["dy_in"], rows, cd, c2, rF)
+    outs = {"z_rows": (z[rows], f["z"][rows]), "gu_rows": (gu[rows], f["gu"][rows]),
+            "a_rows": (a[rows], f["a"][rows]), "dX_rows": (dX[rows], b["dX_rows"]),
+            "dR_rows": (dR[rows], b["dR_rows"]), "dW1_cols": (dW1[:, cd], b["dW1_cols"]),
+            "dW_cols": (dW[:, c2], b["dW_cols"]), "dWd_rows": (dWd[rF], b["dWd_rows"]),
+            "dgamma": (dg, b["dgamma"])}
+    errs.update({k: rel(g(v), ref) for k, (v, ref) in outs.items()})
+    nerrs = {k: nrel(g(v), ref) for k, (v, ref) in outs.items()}
+    report(w.name, {**errs, "r": rr})
+    report(f"{w.name} normwise", nerrs)
+    assert rr <= R_ELEM_TOL
+    assert errs["y_rows"] <= BF16_TOL
+    _check_chain(errs, nerrs, outs)
