@@ -467,6 +467,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 // ---------------------------------------------------------------------------
 enum Fmt : int { FMT_BF16 = 0, FMT_MX8 = 1 };
 
+// x scaled into the E4M3 range and saturated at +-448 for the conversion; a
+// NaN or an infinity passes through (fminf / fmaxf would turn a NaN into a
+// finite bound), so the conversion makes it the NaN code and it propagates
+// through the GEMMs instead of vanishing.  Finite values are unchanged.
+__device__ __forceinline__ float mx8_sat(float x, float inv) {
+  const float v = x * inv;
+  return __builtin_isfinite(v) ? fminf(fmaxf(v, -448.0f), 448.0f) : v;
+}
+
 // One 32-block of a row to MXFP8, shared by 4 consecutive lanes holding 8
 // values each (lanes 4j..4j+3 of the wave): the block maximum by two
 // shuffles, the shared exponent floor(log2 amax) - 8 (clamped at -127) from
@@ -481,7 +490,7 @@ __device__ __forceinline__ uint2 mx8_block_of_4_lanes(f32x4 lo, f32x4 hi, int& s
   am = fmaxf(am, __shfl_xor(am, 2));
   sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
   const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
-  auto sat = [&](float v) { return fminf(fmaxf(v * inv, -448.0f), 448.0f); };
+  auto sat = [&](float v) { return mx8_sat(v, inv); };
   int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[0]), sat(lo[1]), 0, false);
   w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(lo[2]), sat(lo[3]), w0, true);
   int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(hi[0]), sat(hi[1]), 0, false);
@@ -978,7 +987,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
             am = fmaxf(am, __shfl_xor(am, 2));
             const int sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
             const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
-            auto sat = [&](float v) { return fminf(fmaxf(v * inv, -448.0f), 448.0f); };
+            auto sat = [&](float v) { return mx8_sat(v, inv); };
             int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(vlo[0]), sat(vlo[1]), 0, false);
             w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(vlo[2]), sat(vlo[3]), w0, true);
             int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat(vhi[0]), sat(vhi[1]), 0, false);
@@ -1296,7 +1305,7 @@ __global__ void __launch_bounds__(256) mx8_quantize_t_kernel(const __bf16* __res
   }
   const int sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
   const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
-  auto sat = [&](float x) { return fminf(fmaxf(x * inv, -448.0f), 448.0f); };
+  auto sat = [&](float x) { return mx8_sat(x, inv); };
   uint32_t w[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
@@ -1389,7 +1398,7 @@ __global__ void __launch_bounds__(256) mx8_quantize_fused_kernel(MxQuantArgs q) 
   }
   const int sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
   const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
-  auto sat = [&](float x) { return fminf(fmaxf(x * inv, -448.0f), 448.0f); };
+  auto sat = [&](float x) { return mx8_sat(x, inv); };
   uint32_t w[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {

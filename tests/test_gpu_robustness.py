@@ -287,3 +287,86 @@ def test_ce_ignored_labels(env):
     for k, g_ in (("dh", dh), ("dWv", dWv)):
         ref = b[k]
         assert float(np.max(np.abs(host(g_) - ref))) / float(np.max(np.abs(ref))) <= BF16_TOL, k
+
+
+def _nonfinite_split(clean, dirty, mask):
+    """dirty is non-finite exactly where mask says, and bitwise the clean
+    result elsewhere."""
+    import torch
+    bad = ~torch.isfinite(dirty.float())
+    m = torch.as_tensor(mask, device=dirty.device)
+    assert bool(bad[m].all()), "a dependent element stayed finite"
+    assert not bool(bad[~m].any()), "a non-finite value reached an independent element"
+    assert torch.equal(dirty[~m], clean[~m]), "an independent element changed"
+
+
+def test_mx8_nonfinite_propagates(env):
+    """The MXFP8 quantisers keep a NaN or an infinity (as the NaN code; a
+    saturating clamp would turn it into a finite bound): it reaches every
+    output element that depends on it, and every other element is bitwise
+    the clean run's.  Block forward (NaN in X, Inf in R), block backward (NaN
+    in dz), SwiGLU forward and backward (NaN in X, in dz)."""
+    torch, dev, coda = env
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(torch.bfloat16)  # noqa: E731
+    M, K, d, N = 256, 256, 256, 384
+    h = synth.mx8_inputs(M, K, d, N, seed=717, with_dz=True)
+
+    def fwd(X, R):
+        xq, xs = coda.mx8_quantize(bf(X))
+        w1q, w1s = coda.mx8_quantize(bf(h["W1t"]))
+        w2q, w2s = coda.mx8_quantize(bf(h["W2t"]))
+        z, y, r = coda.fwd_mx8(xq, xs, w1q, w1s, bf(R), bf(h["gamma"]), w2q, w2s, 1e-6)
+        torch.cuda.synchronize()
+        return z, y, r
+    X, R = h["X"].copy(), h["R"].copy()
+    X[3, 5] = np.nan
+    R[9, 7] = np.inf
+    zc, yc, rc = fwd(h["X"], h["R"])
+    zd, yd, rd = fwd(X, R)
+    rows = np.zeros((M, N), bool)
+    rows[[3, 9]] = True
+    _nonfinite_split(zc, zd, rows)
+
+    def bwd(dz):
+        y = yc
+        out = coda.bwd_mx8(bf(h["X"]), bf(h["W1"]), bf(h["gamma"]), bf(h["W2"]), y, rc, bf(dz))
+        torch.cuda.synchronize()
+        return out
+    dz = h["dz"].copy()
+    dz[7, 2] = np.nan
+    cl, di = bwd(h["dz"]), bwd(dz)
+    r7 = np.zeros((M, K), bool)
+    r7[7] = True
+    _nonfinite_split(cl[0], di[0], r7)                                  # dX: row 7
+    rd7 = np.zeros((M, d), bool)
+    rd7[7] = True
+    _nonfinite_split(cl[2], di[2], rd7)                                 # dR: row 7
+    c2 = np.zeros((d, N), bool)
+    c2[:, 2] = True
+    _nonfinite_split(cl[3], di[3], c2)                                  # dW2: column 2
+    _nonfinite_split(cl[1], di[1], np.ones((K, d), bool))              # dW1: every column sums over row 7
+    _nonfinite_split(cl[4], di[4], np.ones((d,), bool))                # dgamma: sums over every row
+
+    Ms, ds, F = 256, 256, 256
+    hs = synth.swiglu_inputs(Ms, ds, F, seed=718)
+    Xs = hs["X"].copy()
+    Xs[4, 9] = np.nan
+    zc, guc, ac = coda.swiglu_fwd_mx8(bf(hs["X"]), bf(hs["W"]), bf(hs["Wd"]))
+    zd, gud, ad = coda.swiglu_fwd_mx8(bf(Xs), bf(hs["W"]), bf(hs["Wd"]))
+    torch.cuda.synchronize()
+    for c_, d_, w_ in ((zc, zd, ds), (guc, gud, 2 * F), (ac, ad, F)):
+        m = np.zeros((Ms, w_), bool)
+        m[4] = True
+        _nonfinite_split(c_, d_, m)
+    dzs = hs["dz"].copy()
+    dzs[6, 3] = np.nan
+    cl = coda.swiglu_bwd_mx8(bf(hs["X"]), bf(hs["W"]), bf(hs["Wd"]), guc, ac, bf(hs["dz"]))
+    di = coda.swiglu_bwd_mx8(bf(hs["X"]), bf(hs["W"]), bf(hs["Wd"]), guc, ac, bf(dzs))
+    torch.cuda.synchronize()
+    m = np.zeros((Ms, ds), bool)
+    m[6] = True
+    _nonfinite_split(cl[0], di[0], m)                                   # dX: row 6
+    _nonfinite_split(cl[1], di[1], np.ones((ds, 2 * F), bool))         # dW: every column sums over row 6
+    m = np.zeros((F, ds), bool)
+    m[:, 3] = True
+    _nonfinite_split(cl[2], di[2], m)                                   # dWd: column 3
