@@ -543,3 +543,57 @@ def test_full_workload_mlp_mx8(torch_dev):
     assert rr <= R_ELEM_TOL
     assert errs["y_rows"] <= BF16_TOL
     _check_chain(errs, nerrs, outs)
+
+
+def test_mx8_graph_capture_replays_match_eager(torch_dev):
+    """The MXFP8 SwiGLU and MLP steps (forward + backward; the calls quantise
+    their inputs, so every quantiser runs too) captured into a HIP graph
+    replay bitwise equal to the eager calls, on every replay, with eager
+    calls and synchronisations between the replays."""
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    M, K, d, F = 384, 256, 384, 640
+    hs = synth.swiglu_inputs(M, d, F, seed=880)
+    hm = synth.mlp_inputs(M, K, d, F, seed=881)
+    ts = {k: bf(torch, dev, v) for k, v in hs.items()}
+    tm = {k: bf(torch, dev, v) for k, v in hm.items()}
+    e = lambda *shape, dt=torch.bfloat16: torch.empty(shape, dtype=dt, device=dev)  # noqa: E731
+    b = dict(gu=e(M, 2 * F), a=e(M, F), z=e(M, d), dX=e(M, d), dW=e(d, 2 * F), dWd=e(F, d),
+             y=e(M, d), r=e(M, dt=torch.float32), gu2=e(M, 2 * F), a2=e(M, F), z2=e(M, d), dX2=e(M, K),
+             dW1=e(K, d), dR=e(M, d), dW2=e(d, 2 * F), dWd2=e(F, d), dg=e(d, dt=torch.float32))
+    u8 = lambda n: torch.empty((n,), dtype=torch.uint8, device=dev)  # noqa: E731
+    ws = [u8(coda.swiglu_fwd_mx8_workspace_bytes(M, d, F)), u8(coda.swiglu_bwd_mx8_workspace_bytes(M, d, F)),
+          u8(coda.mlp_fwd_mx8_workspace_bytes(M, K, d, F)), u8(coda.mlp_bwd_mx8_workspace_bytes(M, K, d, F))]
+
+    def step():
+        coda.coda_swiglu_fwd_mx8(ts["X"], ts["W"], ts["Wd"], b["gu"], b["a"], b["z"], ws[0])
+        coda.coda_swiglu_bwd_mx8(ts["X"], ts["W"], ts["Wd"], b["gu"], b["a"], ts["dz"], b["dX"], b["dW"], b["dWd"],
+                                 ws[1])
+        coda.coda_mlp_fwd_mx8(tm["X"], tm["W1"], tm["R"], tm["gamma"], tm["W"], tm["Wd"], 1e-6, b["y"], b["r"],
+                              b["gu2"], b["a2"], b["z2"], ws[2])
+        coda.coda_mlp_bwd_mx8(tm["X"], tm["W1"], tm["gamma"], tm["W"], tm["Wd"], b["y"], b["r"], b["gu2"], b["a2"],
+                              tm["dz"], tm["dy_in"], b["dX2"], b["dW1"], b["dR"], b["dW2"], b["dWd2"], b["dg"], ws[3])
+
+    step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in b.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in b.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in b.items():
+            assert torch.equal(v, ref[k]), f"replay {rep}: {k} differs from the eager result"
+        step()
+        torch.cuda.synchronize()
+    report("mx8 graph capture", {"replays": 3.0})
