@@ -422,7 +422,7 @@ class SwigluMx8Case(Mx8Case):
         self.ws = torch.empty(coda.swiglu_fwd_mx8_workspace_bytes(M, d, F), dtype=torch.uint8, device=dev)
         self.wsb = torch.empty(coda.swiglu_bwd_mx8_workspace_bytes(M, d, F), dtype=torch.uint8, device=dev)
         self.backward = w.backward
-        self.kernels_per_step = 5 + 10
+        self.kernels_per_step = 5 + 9
         self.leaf_names = ("X",)
         self.manual_bwd = True
 
@@ -486,7 +486,7 @@ class MlpMx8Case(Mx8Case):
         self.ws = torch.empty(coda.mlp_fwd_mx8_workspace_bytes(M, K, d, F), dtype=torch.uint8, device=dev)
         self.wsb = torch.empty(coda.mlp_bwd_mx8_workspace_bytes(M, K, d, F), dtype=torch.uint8, device=dev)
         self.backward = w.backward
-        self.kernels_per_step = 7 + 5 + 11
+        self.kernels_per_step = 7 + 5 + 10
         self.leaf_names = ("X",)
         self.manual_bwd = True
 

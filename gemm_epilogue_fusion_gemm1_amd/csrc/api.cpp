@@ -1101,7 +1101,9 @@ BwdMx8Ws bwd_mx8_ws(int64_t M, int64_t K, int64_t d, int64_t N) {
 }
 
 // The MXFP8 backward of the block (coda_bwd_mx8; the MLP sub-layer's second
-// half with W2 = W, dz = dgu and dy_in): every argument already checked.
+// half with W2 = W, dz = dgu and dy_in): every argument already checked.  dz
+// NULL: dz's MXFP8 operands (along N and along M) are already in the
+// workspace.
 coda_status norm_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, const void* X, const void* W1,
                          const void* gamma, const void* W2, const void* y, const float* r, const void* dz,
                          const void* dy_in, void* dX, void* dW1, void* dR, void* dW2, float* dgamma,
@@ -1138,7 +1140,10 @@ coda_status norm_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, const void*
   qdz.sr = u8(ws.dzs);
   qdz.qt = u8(ws.dzTq);
   qdz.st = u8(ws.dzTs);
-  if ((err = fused("x1_mx8_quantize_dz_both", mn * (2.0 + 2.0 * q8), 0, qdz)) != hipSuccess) return hip_status(err);
+  // (dz NULL: its codes are already in the workspace, written by the GEMM
+  // that produced it)
+  if (dz && (err = fused("x1_mx8_quantize_dz_both", mn * (2.0 + 2.0 * q8), 0, qdz)) != hipSuccess)
+    return hip_status(err);
   if ((err = quant("x2_mx8_quantize_W2", W2, d, N, u8(ws.w2q), u8(ws.w2s))) != hipSuccess) return hip_status(err);
   // B1: dh = dz W2^T on MXFP8; epilogue dn (into dR), S, G as in the bf16
   // backward (n is made from y and r where it is quantised)
@@ -1245,10 +1250,10 @@ coda_status coda_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t N, const void*
 
 namespace {
 // Workspaces of the MXFP8 SwiGLU block: every GEMM operand in MXFP8 (codes
-// and step-blocked scales) and, in the backward, dgu.
+// and step-blocked scales; dgu exists only as such).
 struct SwigluMx8Ws {
   size_t xq, xs, wq, ws, wdq, wds, aq, as, total;          // forward
-  size_t dzq, dzs, dzTq, dzTs, wdrq, wdrs, dgu, aTq, aTs, dguq, dgus, dguTq, dguTs, wrq, wrs, XTq, XTs;
+  size_t dzq, dzs, dzTq, dzTs, wdrq, wdrs, aTq, aTs, dguq, dgus, dguTq, dguTs, wrq, wrs, XTq, XTs;
 };
 SwigluMx8Ws swiglu_mx8_ws(int64_t M, int64_t d, int64_t F, bool bwd) {
   SwigluMx8Ws w{};
@@ -1264,7 +1269,6 @@ SwigluMx8Ws swiglu_mx8_ws(int64_t M, int64_t d, int64_t F, bool bwd) {
     mx(M, d, w.dzq, w.dzs);          // dz along d
     mx(d, M, w.dzTq, w.dzTs);        // dz along M, transposed
     mx(F, d, w.wdrq, w.wdrs);        // Wd along d
-    w.dgu = take((size_t)M * 2 * F * 2);
     mx(F, M, w.aTq, w.aTs);          // a along M, transposed
     mx(M, 2 * F, w.dguq, w.dgus);    // dgu along 2F
     mx(2 * F, M, w.dguTq, w.dguTs);  // dgu along M, transposed
@@ -1376,7 +1380,6 @@ coda_status coda_swiglu_bwd_mx8(int64_t M, int64_t d, int64_t F, const void* X, 
   hipStream_t s = (hipStream_t)stream;
   char* wb = (char*)workspace;
   auto u8 = [&](size_t off) { return (uint8_t*)(wb + off); };
-  void* dgu = wb + ws.dgu;
   hipError_t err;
   const double q8 = 1.0 + 1.0 / 32.0, Md = (double)M * d, dF = (double)d * F, MF = (double)M * F;
   auto both = [&](const char* name, const void* src, int64_t rows, int64_t cols, size_t qr, size_t sr, size_t qt,
@@ -1400,12 +1403,20 @@ coda_status coda_swiglu_bwd_mx8(int64_t M, int64_t d, int64_t F, const void* X, 
          return coda::launch_mx8_quantize(Wd, d, F, d, u8(ws.wdrq), u8(ws.wdrs), s);
        })) != hipSuccess)
     return hip_status(err);
-  GemmArgs s3 = gemm_mx8(M, F, d, u8(ws.dzq), u8(ws.dzs), u8(ws.wdrq), u8(ws.wdrs), dgu, 2 * F);
+  // (dgu is not stored: the epilogue quantises it, as bf16, along 2F and
+  // along M for the dX and dW GEMMs)
+  GemmArgs s3 = gemm_mx8(M, F, d, u8(ws.dzq), u8(ws.dzs), u8(ws.wdrq), u8(ws.wdrs), nullptr, 2 * F);
   s3.E = gu;
   s3.lde = 2 * F;
   s3.F = (int)F;
-  if ((err = traced("s3_gemm_mx8_da_swiglu_bwd", gemm_flops(M, F, d), (Md + dF) * q8 + 4.0 * MF * e, s,
-                    [&] { return coda::launch_gemm_mx8(s3, coda::EPI_SWIGLU_BWD, s); })) != hipSuccess)
+  s3.q_out = u8(ws.dguq);
+  s3.qs_out = u8(ws.dgus);
+  s3.ldq = 2 * F;
+  s3.qt_out = u8(ws.dguTq);
+  s3.qts_out = u8(ws.dguTs);
+  s3.ldqt = M;
+  if ((err = traced("s3_gemm_mx8_da_swiglu_bwd", gemm_flops(M, F, d), (Md + dF) * q8 + 2.0 * MF * e + 4.0 * MF * q8,
+                    s, [&] { return coda::launch_gemm_mx8(s3, coda::EPI_SWIGLU_BWD, s); })) != hipSuccess)
     return hip_status(err);
   // S4: dWd = a^T dz (contraction over M): a along M, transposed
   if ((err = traced("x3_mx8_quantize_aT", 0.0, MF * (e + q8), s, [&] {
@@ -1417,8 +1428,6 @@ coda_status coda_swiglu_bwd_mx8(int64_t M, int64_t d, int64_t F, const void* X, 
                     [&] { return coda::launch_gemm_mx8(s4, coda::EPI_STORE, s); })) != hipSuccess)
     return hip_status(err);
   // S5: dX = dgu W^T (contraction over 2F); S6: dW = X^T dgu (contraction over M)
-  if ((err = both("x4_mx8_quantize_dgu_both", dgu, M, 2 * F, ws.dguq, ws.dgus, ws.dguTq, ws.dguTs)) != hipSuccess)
-    return hip_status(err);
   if ((err = traced("x5_mx8_quantize_W", 0.0, 2.0 * dF * (e + q8), s, [&] {
          return coda::launch_mx8_quantize(W, 2 * F, d, 2 * F, u8(ws.wrq), u8(ws.wrs), s);
        })) != hipSuccess)
@@ -1461,10 +1470,10 @@ MlpMx8FwdWs mlp_mx8_fwd_ws(int64_t M, int64_t K, int64_t d, int64_t F) {
   w.total = o;
   return w;
 }
-// The backward: the SwiGLU part's operands and dgu, then the block part's
-// workspace (coda_bwd_mx8's with N = 2F)
+// The backward: the SwiGLU part's operands, then the block part's workspace
+// (coda_bwd_mx8's with N = 2F; its dz operands receive dgu's codes)
 struct MlpMx8BwdWs {
-  size_t dzq, dzs, dzTq, dzTs, wdq, wds, dgu, aTq, aTs, blk, total;
+  size_t dzq, dzs, dzTq, dzTs, wdq, wds, aTq, aTs, blk, total;
   BwdMx8Ws b;
 };
 MlpMx8BwdWs mlp_mx8_bwd_ws(int64_t M, int64_t K, int64_t d, int64_t F) {
@@ -1475,7 +1484,6 @@ MlpMx8BwdWs mlp_mx8_bwd_ws(int64_t M, int64_t K, int64_t d, int64_t F) {
   mx(M, d, w.dzq, w.dzs);
   mx(d, M, w.dzTq, w.dzTs);
   mx(F, d, w.wdq, w.wds);
-  w.dgu = take((size_t)M * 2 * F * 2);
   mx(F, M, w.aTq, w.aTs);
   w.b = bwd_mx8_ws(M, K, d, 2 * F);
   w.blk = take(w.b.total);
@@ -1620,7 +1628,6 @@ coda_status coda_mlp_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t F, const v
   hipStream_t s = (hipStream_t)stream;
   char* wb = (char*)workspace;
   auto u8 = [&](size_t off) { return (uint8_t*)(wb + off); };
-  void* dgu = wb + ws.dgu;
   hipError_t err;
   const double q8 = 1.0 + 1.0 / 32.0, Md = (double)M * d, dF = (double)d * F, MF = (double)M * F;
   // the SwiGLU part: dz along d and along M (one pass), Wd along d
@@ -1640,13 +1647,21 @@ coda_status coda_mlp_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t F, const v
          return coda::launch_mx8_quantize(Wd, d, F, d, u8(ws.wdq), u8(ws.wds), s);
        })) != hipSuccess)
     return hip_status(err);
-  // M3: da = dz Wd^T on MXFP8; epilogue dgu from the saved gu
-  GemmArgs m3 = gemm_mx8(M, F, d, u8(ws.dzq), u8(ws.dzs), u8(ws.wdq), u8(ws.wds), dgu, 2 * F);
+  // M3: da = dz Wd^T on MXFP8; epilogue dgu from the saved gu, quantised (as
+  // bf16) along 2F and along M straight into the block part's dz operands
+  char* blk = wb + ws.blk;
+  GemmArgs m3 = gemm_mx8(M, F, d, u8(ws.dzq), u8(ws.dzs), u8(ws.wdq), u8(ws.wds), nullptr, 2 * F);
   m3.E = gu;
   m3.lde = 2 * F;
   m3.F = (int)F;
-  if ((err = traced("m3_gemm_mx8_da_swiglu_bwd", gemm_flops(M, F, d), (Md + dF) * q8 + 4.0 * MF * e, s,
-                    [&] { return coda::launch_gemm_mx8(m3, coda::EPI_SWIGLU_BWD, s); })) != hipSuccess)
+  m3.q_out = (uint8_t*)(blk + ws.b.dzq);
+  m3.qs_out = (uint8_t*)(blk + ws.b.dzs);
+  m3.ldq = 2 * F;
+  m3.qt_out = (uint8_t*)(blk + ws.b.dzTq);
+  m3.qts_out = (uint8_t*)(blk + ws.b.dzTs);
+  m3.ldqt = M;
+  if ((err = traced("m3_gemm_mx8_da_swiglu_bwd", gemm_flops(M, F, d), (Md + dF) * q8 + 2.0 * MF * e + 4.0 * MF * q8,
+                    s, [&] { return coda::launch_gemm_mx8(m3, coda::EPI_SWIGLU_BWD, s); })) != hipSuccess)
     return hip_status(err);
   // M4: dWd = a^T dz on MXFP8: a along M, transposed
   if ((err = traced("w3_mx8_quantize_aT", 0.0, MF * (e + q8), s, [&] {
@@ -1657,9 +1672,10 @@ coda_status coda_mlp_bwd_mx8(int64_t M, int64_t K, int64_t d, int64_t F, const v
   if ((err = traced("m4_gemm_mx8_dWd", gemm_flops(F, d, M), (MF + Md) * q8 + dF * e, s,
                     [&] { return coda::launch_gemm_mx8(m4, coda::EPI_STORE, s); })) != hipSuccess)
     return hip_status(err);
-  // the block's MXFP8 backward with dz = dgu, W2 = W (N = 2F) and dy_in
-  return norm_bwd_mx8(M, K, d, 2 * F, X, W1, gamma, W, y, r, dgu, dy_in, dX, dW1, dR, dW, dgamma,
-                      wb + ws.blk, ws.b, s);
+  // the block's MXFP8 backward with dz = dgu (its operands already made),
+  // W2 = W (N = 2F) and dy_in
+  return norm_bwd_mx8(M, K, d, 2 * F, X, W1, gamma, W, y, r, nullptr, dy_in, dX, dW1, dR, dW, dgamma, blk,
+                      ws.b, s);
 }
 
 }  // extern "C"

@@ -476,6 +476,24 @@ __device__ __forceinline__ float mx8_sat(float x, float inv) {
   return __builtin_isfinite(v) ? fminf(fmaxf(v, -448.0f), 448.0f) : v;
 }
 
+// One 32-block held by one lane to MXFP8: its 32 codes packed four to a
+// word (w[j] holds elements 4j..4j+3), the shared exponent returned.  Same
+// arithmetic as the 4-lane routine below.
+__device__ __forceinline__ int mx8_block32(const float (&v)[32], uint32_t (&w)[8]) {
+  float am = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) am = fmaxf(am, fabsf(v[e]));
+  const int sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
+  const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(mx8_sat(v[4 * j], inv), mx8_sat(v[4 * j + 1], inv), 0, false);
+    w[j] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(mx8_sat(v[4 * j + 2], inv), mx8_sat(v[4 * j + 3], inv), x,
+                                                     true);
+  }
+  return sexp;
+}
+
 // One 32-block of a row to MXFP8, shared by 4 consecutive lanes holding 8
 // values each (lanes 4j..4j+3 of the wave): the block maximum by two
 // shuffles, the shared exponent floor(log2 amax) - 8 (clamped at -127) from
@@ -1044,11 +1062,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           }
         } else if constexpr (EPI == EPI_SWIGLU_BWD) {
           // da = acc [M, F]; g, u from the saved gu; dgu = [dg | du]
+          f32x4 dg0{0.f, 0.f, 0.f, 0.f}, dg1 = dg0, du0 = dg0, du1 = dg0;   // zero out of range
           if (ok) {
             f32x4 g0, g1, u0, u1;
             unpack8(epre[i & 1][p], g0, g1);
             unpack8(upre[i & 1][p], u0, u1);
-            f32x4 dg0, dg1, du0, du1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               float sg = sigmoid_f(g0[e]);
@@ -1058,8 +1076,75 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
               dg1[e] = hi[e] * u1[e] * sg * (1.0f + g1[e] * (1.0f - sg));
               du1[e] = hi[e] * g1[e] * sg;
             }
-            st8(C + o, dg0, dg1);
-            st8(C + o + g.F, du0, du1);
+            if (C) {
+              st8(C + o, dg0, dg1);
+              st8(C + o + g.F, du0, du1);
+            }
+          }
+          if constexpr (FMT == FMT_MX8) {
+            // dgu as stored (bf16) to MXFP8 without storing it: along 2F here
+            // (the 4 lanes c8 = 4b..4b+3 of a row hold a 32-column block of
+            // dg, and of du; step-blocked scales [2F/128][M][4]), and along M
+            // after the group's passes, from the bf16 values kept in this
+            // row of the region (whose fp32 accumulators this pass has read)
+            f32x4 b0, b1, c0, c1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              b0[e] = bf2f(f2bf(dg0[e]));
+              b1[e] = bf2f(f2bf(dg1[e]));
+              c0[e] = bf2f(f2bf(du0[e]));
+              c1[e] = bf2f(f2bf(du1[e]));
+            }
+            if (g.q_out) {
+              int sg_, su_;
+              const uint2 wg = mx8_block_of_4_lanes(b0, b1, sg_);
+              const uint2 wu = mx8_block_of_4_lanes(c0, c1, su_);
+              if (ok) {
+                *(uint2*)(g.q_out + (int64_t)row * g.ldq + gcol) = wg;
+                *(uint2*)(g.q_out + (int64_t)row * g.ldq + g.F + gcol) = wu;
+                if ((c8 & 3) == 0) {
+                  const int cu = g.F + gcol;
+                  g.qs_out[((int64_t)(gcol >> 7) * g.M + row) * 4 + ((gcol >> 5) & 3)] = (uint8_t)(sg_ + 127);
+                  g.qs_out[((int64_t)(cu >> 7) * g.M + row) * 4 + ((cu >> 5) & 3)] = (uint8_t)(su_ + 127);
+                }
+              }
+            }
+            if (g.qt_out) {
+              wave_lds_sync();                      // after this pass's region reads
+              *(bf16x8*)(region + r * 256 + c8 * 16) =
+                  bf16x8{f2bf(b0[0]), f2bf(b0[1]), f2bf(b0[2]), f2bf(b0[3]),
+                         f2bf(b1[0]), f2bf(b1[1]), f2bf(b1[2]), f2bf(b1[3])};
+              *(bf16x8*)(region + r * 256 + 128 + c8 * 16) =
+                  bf16x8{f2bf(c0[0]), f2bf(c0[1]), f2bf(c0[2]), f2bf(c0[3]),
+                         f2bf(c1[0]), f2bf(c1[1]), f2bf(c1[2]), f2bf(c1[3])};
+            }
+          }
+        }
+      }
+      if constexpr (EPI == EPI_SWIGLU_BWD && FMT == FMT_MX8) {
+        // dgu along M: the region holds the group's 32 rows x [dg 64 | du 64]
+        // (bf16); lane l quantises column l of dg and of du over those rows
+        // (the transposing quantiser's arithmetic) into codes [2F][ldqt] and
+        // scales [M/128][2F][4]
+        if (g.qt_out) {
+          __builtin_amdgcn_s_waitcnt(0xc07f);         // this wave's LDS writes are done
+          wave_lds_sync();
+          const int rowT = row0 + wm * TM + i * 32;
+          const int colT = col0 + wnv * VW + lane;
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            float v[32];
+#pragma unroll
+            for (int e = 0; e < 32; ++e) v[e] = bf2f(*(const __bf16*)(region + e * 256 + h2 * 128 + lane * 2));
+            uint32_t w[8];
+            const int sexp = mx8_block32(v, w);
+            if (colT < g.N && rowT < g.M) {
+              const int64_t cT = (int64_t)colT + h2 * g.F;
+              uint8_t* dst = g.qt_out + cT * g.ldqt + rowT;
+              *(uint4*)dst = uint4{w[0], w[1], w[2], w[3]};
+              *(uint4*)(dst + 16) = uint4{w[4], w[5], w[6], w[7]};
+              g.qts_out[((int64_t)(rowT >> 7) * (2 * g.F) + cT) * 4 + ((rowT >> 5) & 3)] = (uint8_t)(sexp + 127);
+            }
           }
         }
       }
@@ -1297,21 +1382,10 @@ __global__ void __launch_bounds__(256) mx8_quantize_t_kernel(const __bf16* __res
   const int c = t & 63, b = t >> 6;       // column, 32-row block
   const int64_t col = col0 + c;
   float v[32];
-  float am = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    v[e] = (float)tile[32 * b + e][c];
-    am = fmaxf(am, fabsf(v[e]));
-  }
-  const int sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
-  const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
-  auto sat = [&](float x) { return mx8_sat(x, inv); };
+  for (int e = 0; e < 32; ++e) v[e] = (float)tile[32 * b + e][c];
   uint32_t w[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    int x = __builtin_amdgcn_cvt_pk_fp8_f32(sat(v[4 * q]), sat(v[4 * q + 1]), 0, false);
-    w[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(v[4 * q + 2]), sat(v[4 * q + 3]), x, true);
-  }
+  const int sexp = mx8_block32(v, w);
   if (col < cols) {
     uint8_t* dst = codes + col * rows + row0 + 32 * b;
     *(uint4*)dst = uint4{w[0], w[1], w[2], w[3]};
@@ -1390,21 +1464,10 @@ __global__ void __launch_bounds__(256) mx8_quantize_fused_kernel(MxQuantArgs q) 
   const int c = t & 63, b = t >> 6;       // column, 32-row block
   const int64_t col = col0 + c;
   float v[32];
-  float am = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    v[e] = (float)tile[32 * b + e][c];
-    am = fmaxf(am, fabsf(v[e]));
-  }
-  const int sexp = max((int)((__float_as_uint(am) >> 23) & 255) - 135, -127);
-  const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);
-  auto sat = [&](float x) { return mx8_sat(x, inv); };
+  for (int e = 0; e < 32; ++e) v[e] = (float)tile[32 * b + e][c];
   uint32_t w[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int x = __builtin_amdgcn_cvt_pk_fp8_f32(sat(v[4 * j]), sat(v[4 * j + 1]), 0, false);
-    w[j] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(v[4 * j + 2]), sat(v[4 * j + 3]), x, true);
-  }
+  const int sexp = mx8_block32(v, w);
   if (col < q.cols) {
     // gated_F: column c of a [.., 2F] gate/up weight goes to row 64 (j / 32)
     // + 32 [c is an up column] + j % 32, j = c mod F (the order of a gated

@@ -68,6 +68,11 @@ struct GemmArgs {
   // windows (a K-contiguous operand's 256 tile rows, an MN-contiguous
   // operand's K step)
   uint64_t A_total, B_total;
+  // EPI_SWIGLU_BWD in an MXFP8 GEMM: dgu (as stored, bf16) quantised to MXFP8
+  // along 2F into q_out / qs_out (ldq = 2F) and, when qt_out is set, along M
+  // into qt_out [2F][ldqt] / qts_out [M/128][2F][4] (M % 128 == 0); C (the
+  // bf16 dgu) may then be NULL
+  uint8_t* qt_out; uint8_t* qts_out; int64_t ldqt;
 };
 
 // Launchers: enqueue on `stream`, return the hipGetLastError() after launch.
