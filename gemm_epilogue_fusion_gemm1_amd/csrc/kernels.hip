@@ -145,9 +145,9 @@ __device__ __forceinline__ __bf16 f2bf(float f) { return (__bf16)f; }  // round 
 // 8 loading waves to 86% with 4.
 // Measured per GEMM on the LLaMA-7B/70B and SwiGLU steps: 4 loading waves
 // are 1.5-7.5% faster for the bf16 GEMMs with an MN-contiguous operand and
-// 1-5% slower for those with both operands K-contiguous (whose 64-k steps
-// already issue their loads a step and a quarter ahead) and for MXFP8, which
-// keep all 8.
+// for the 64-k two-stage ring with both operands K-contiguous, and 1-5%
+// slower for the 32-k four-stage ring with both operands K-contiguous and
+// for MXFP8, which keep all 8.
 #ifndef CODA_LOAD_WAVES
 #define CODA_LOAD_WAVES 4
 #endif
@@ -568,7 +568,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   const int row0 = tm * BM, col0 = tn * BN;
 
   // the loaders split each operand tile over the loading waves (64 threads each)
-  constexpr int LNT = (FMT == FMT_MX8 ? CODA_MX_LOAD_WAVES : (AK && BKM) ? CODA_KK_LOAD_WAVES : CODA_LOAD_WAVES) * 64;
+  constexpr int LNT =
+      (FMT == FMT_MX8 ? CODA_MX_LOAD_WAVES : (AK && BKM && BKv == 32) ? CODA_KK_LOAD_WAVES : CODA_LOAD_WAVES) * 64;
   static_assert(LNT <= G::NT, "loading waves");
   typename LoaderSel<AK, KC, LNT, false, TN, WIN>::type la;
   typename LoaderSel<BKM, KC, LNT, GATED, 64, WIN>::type lb;   // gate/up groups of one 64-column half
