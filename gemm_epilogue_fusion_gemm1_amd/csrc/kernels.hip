@@ -144,21 +144,15 @@ __device__ __forceinline__ __bf16 f2bf(float f) { return (__bf16)f; }  // round 
 // MFMAs per wave, L2-resident operands), MFMA utilisation went from 72% with
 // 8 loading waves to 86% with 4.
 // Measured per GEMM on the LLaMA-7B/70B and SwiGLU steps: 4 loading waves
-// are 1.5-7.5% faster for the bf16 GEMMs with an MN-contiguous operand and
-// for the 64-k two-stage ring with both operands K-contiguous, and 1-5%
-// slower for the 32-k four-stage ring with both operands K-contiguous and
-// for MXFP8, which keep all 8.
+// are 1.5-7.5% faster for the bf16 GEMMs (every layout, with the K-step /
+// ring choice below) and 1-3% slower for MXFP8, which keeps all 8.
 #ifndef CODA_LOAD_WAVES
 #define CODA_LOAD_WAVES 4
-#endif
-#ifndef CODA_KK_LOAD_WAVES
-#define CODA_KK_LOAD_WAVES 8
 #endif
 #ifndef CODA_MX_LOAD_WAVES
 #define CODA_MX_LOAD_WAVES 8
 #endif
-static_assert((CODA_LOAD_WAVES == 4 || CODA_LOAD_WAVES == 8) && (CODA_KK_LOAD_WAVES == 4 || CODA_KK_LOAD_WAVES == 8) &&
-                  (CODA_MX_LOAD_WAVES == 4 || CODA_MX_LOAD_WAVES == 8),
+static_assert((CODA_LOAD_WAVES == 4 || CODA_LOAD_WAVES == 8) && (CODA_MX_LOAD_WAVES == 4 || CODA_MX_LOAD_WAVES == 8),
               "loading waves: 4 (one per SIMD) or all 8");
 __device__ __forceinline__ void map_tile(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
@@ -568,8 +562,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   const int row0 = tm * BM, col0 = tn * BN;
 
   // the loaders split each operand tile over the loading waves (64 threads each)
-  constexpr int LNT =
-      (FMT == FMT_MX8 ? CODA_MX_LOAD_WAVES : (AK && BKM && BKv == 32) ? CODA_KK_LOAD_WAVES : CODA_LOAD_WAVES) * 64;
+  constexpr int LNT = (FMT == FMT_MX8 ? CODA_MX_LOAD_WAVES : CODA_LOAD_WAVES) * 64;
   static_assert(LNT <= G::NT, "loading waves");
   typename LoaderSel<AK, KC, LNT, false, TN, WIN>::type la;
   typename LoaderSel<BKM, KC, LNT, GATED, 64, WIN>::type lb;   // gate/up groups of one 64-column half
@@ -1695,16 +1688,19 @@ constexpr int kWavesM = 2, kWavesN = 4;
 constexpr int kMxWavesM = kWavesM, kMxWavesN = kWavesN;
 
 // K step / ring depth: 64 x 2 when an operand is K-contiguous, else 32 x 4.
-// A GEMM with a K-contiguous A operand whose operands together take more
-// than half the MALL (the 256 MiB memory-side cache) also takes 32 x 4
-// (DEEP): much of its loads then see HBM latency, which loads two 32-k steps
-// ahead hide better than three quarters of a 64-k step, and that outweighs
-// the shorter 64-byte rows (measured: the dh GEMM of the RMSNorm backward
-// 3.7% faster at the LLaMA-7B shape and 4.5% at the 70B-hidden shape, the
-// SwiGLU down GEMM 10%, the LM-head logits GEMM 7.5%, the SwiGLU-backward
-// da GEMMs 3.5-4.7%, the 70B-hidden dX GEMM (201 MB) 5%, the rotary QKV
-// GEMM (167 MB) 4.8%, the 70B-hidden first GEMM 3%; a GEMM with 100 MB of
-// operands, the LLaMA-7B dX GEMM, runs faster on the 64 x 2 ring).
+// A GEMM with a K-contiguous A and an N-contiguous B operand (the forward
+// layout) whose operands together take more than half the MALL (the 256 MiB
+// memory-side cache) also takes 32 x 4 (DEEP): much of its loads then see
+// HBM latency, which loads two 32-k steps ahead hide better than three
+// quarters of a 64-k step, and that outweighs the shorter 64-byte rows
+// (measured, 32 x 4 against 64 x 2: the SwiGLU gate/up GEMM 9% faster, the
+// down GEMM 5%, the LM-head logits GEMM 4%, the rotary QKV GEMM 2.5%, the
+// 70B-hidden first GEMM 1.3%).  With both operands K-contiguous the 64 x 2
+// ring, whose loads go out a step and a quarter ahead from one wave per
+// SIMD, is faster at every size measured (the dh GEMM of the RMSNorm
+// backward 4.5% at the LLaMA-7B shape and 9% at the 70B-hidden shape, the
+// SwiGLU dX GEMM 10% and da GEMM 8%, the LM-head dh GEMM 8%, the rotary dX
+// GEMM 10%, the 70B-hidden dX GEMM 5%).
 #ifndef CODA_DEEP_MIN_MIB
 #define CODA_DEEP_MIN_MIB 128
 #endif
@@ -1715,7 +1711,7 @@ static bool needs_windows(const GemmArgs& g) { return g.A_total > kMaxWindow || 
 
 template <bool AK, bool BKM, int EPI, bool DEEP = false>
 static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
-  static_assert(!DEEP || AK, "the deep ring is for a K-contiguous A operand");
+  static_assert(!DEEP || (AK && !BKM), "the deep ring is for the forward layout (A K-, B N-contiguous)");
   constexpr int BKv = (AK || BKM) && !DEEP ? 64 : 32;
   constexpr int NSTv = (AK || BKM) && !DEEP ? 2 : 4;
   const int tiles_m = (g.M + BM - 1) / BM;
@@ -1757,15 +1753,10 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool ak, bool bk, Epi epi, hipStr
       default: break;
     }
   } else if (ak && bk) {
-    const bool deep = ((int64_t)g.M + g.N) * g.K * 2 > kDeepMinBytes;
     switch (epi) {
-      case EPI_STORE:
-        return deep ? launch_one<true, true, EPI_STORE, true>(g, s) : launch_one<true, true, EPI_STORE>(g, s);
-      case EPI_DN:
-        return deep ? launch_one<true, true, EPI_DN, true>(g, s) : launch_one<true, true, EPI_DN>(g, s);
-      case EPI_SWIGLU_BWD:
-        return deep ? launch_one<true, true, EPI_SWIGLU_BWD, true>(g, s)
-                    : launch_one<true, true, EPI_SWIGLU_BWD>(g, s);
+      case EPI_STORE: return launch_one<true, true, EPI_STORE>(g, s);
+      case EPI_DN: return launch_one<true, true, EPI_DN>(g, s);
+      case EPI_SWIGLU_BWD: return launch_one<true, true, EPI_SWIGLU_BWD>(g, s);
       default: break;
     }
   } else if (!ak && !bk) {

@@ -304,12 +304,13 @@ def test_full_workload_coda(torch_dev, name):
 
 
 # The operands of the dh GEMM (dz [M, N] and W2 [d, N], contraction over N)
-# exceed the whole 256 MiB memory-side cache here (the deep LDS ring starts at
-# half of it), so it runs on the deep LDS ring
-# (32-k steps, four stages) that large K-contiguous operand pairs take, and
-# so does the first GEMM (X [M, K] and W1 [K, d]: 164 MB); the second GEMM's
-# operands (135 MB) take the transposed y*gamma layout; every dimension is
-# ragged (M, d: 8 past a tile; N: 8 past a 32-k step; K: 8 past a 64-k step).
+# exceed the whole 256 MiB memory-side cache here; like every GEMM with both
+# operands K-contiguous it runs on the 64-k two-stage ring.  The first GEMM
+# (X [M, K] and W1 [K, d]: 164 MB, past half the cache, in the forward
+# layout) takes the deep LDS ring (32-k steps, four stages); the second
+# GEMM's operands (135 MB) take the transposed y*gamma layout; every
+# dimension is ragged (M, d: 8 past a tile; N: 8 past a 32-k step; K: 8 past
+# a 64-k step).
 RAGGED_WIDE = synth.Workload("ragged_wide_fwdbwd", "coda", "bf16", M=4104, K=13320, d=2056, N=28680,
                              eps=1e-6, seed=1011, backward=True)
 
@@ -399,9 +400,8 @@ def test_full_workload_swiglu(torch_dev):
 
 
 # The dX GEMM (dgu [M, 2F] times W [d, 2F] transposed, contraction over 2F)
-# has operands beyond 256 MiB (past the deep ring's 128 MiB threshold), so it
-# takes the deep LDS ring; M, d and F are
-# ragged.
+# has operands beyond 256 MiB, past the whole memory-side cache; M, d and F
+# are ragged.
 RAGGED_WIDE_SWIGLU = synth.Workload("ragged_wide_swiglu", "swiglu", "bf16", M=4104, d=1032, F=14344,
                                     seed=1012, backward=True)
 
@@ -414,7 +414,8 @@ def test_ragged_wide_swiglu(torch_dev):
 
 # Here the da GEMM of the SwiGLU backward (dz [M, d] times Wd [F, d]
 # transposed, contraction over d, with the SwiGLU-backward epilogue) also
-# has operands beyond 256 MiB and takes the deep ring; ragged everywhere.
+# has operands beyond 256 MiB, and the gate/up GEMM (X [M, d], W [d, 2F]:
+# 536 MB, forward layout) takes the deep ring; ragged everywhere.
 RAGGED_WIDE_SWIGLU_DA = synth.Workload("ragged_wide_swiglu_da", "swiglu", "bf16", M=4104, d=4360, F=28680,
                                        seed=1013, backward=True)
 
