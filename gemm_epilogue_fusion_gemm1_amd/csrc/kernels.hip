@@ -745,17 +745,20 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 
   // The compiler interleaves each sub-step's LDS reads and MFMAs; with two
   // waves per SIMD that measured faster than any forced order (all reads
-  // first, reads after one MFMA, one read per MFMA), and than issuing the
-  // next stage's loads earlier (right after the barrier, or after the first
-  // MFMAs of the last sub-step).  sched_barrier keeps the sub-steps apart.
+  // first, reads after one MFMA, one read per MFMA).  The four-stage ring
+  // issues a stage's loads at the start of the step (right after the
+  // barrier, or after the first MFMAs of the last sub-step, measured
+  // slower); the two-stage ring issues them right after the barrier (EARLY
+  // below).  sched_barrier keeps the sub-steps apart.
 #pragma unroll
   for (int st = 0; st < NSTAGE - 1; ++st) issue(st);
   __builtin_amdgcn_s_waitcnt(WAIT_NEXT);     // step 0 has landed
   __syncthreads();
   read_frags(smem, 0, fa[0], fb[0]);
-  // measured: faster with both operands K-contiguous (the LLaMA-7B dX GEMM
-  // 226 -> 218 us), slower with an N-contiguous B (the first GEMM 244 -> 256)
-  constexpr bool EARLY = CODA_BF16_EARLY_ISSUE && NSUB == 2 && NSTAGE == 2 && AK && BKM;
+  // measured: faster on every 64-k two-stage loop with four loading waves
+  // (the LLaMA-7B dX GEMM 226 -> 218 us already with eight; the first GEMM
+  // 234 -> 229 us at the LLaMA-7B shape and 82 -> 80 us at the 1B one)
+  constexpr bool EARLY = CODA_BF16_EARLY_ISSUE && NSUB == 2 && NSTAGE == 2;
   if constexpr (EARLY) issue(1);
   if constexpr (NSUB == 2) {
     // Two sub-steps: the wait and barrier go three quarters through the step
