@@ -1354,45 +1354,58 @@ gemm_mx8_kernel(GemmArgs g) {
 // bf16 rows -> MXFP8 along the row.  A lane takes 8 consecutive elements
 // (one 16-byte load), 4 lanes one 32-block: shared exponent and element
 // rounding as in the first GEMM's epilogue; scales stored step-blocked
-// ([cols/128][rows][4]).  Grid-stride over 8-element groups.
-__global__ void mx8_quantize_kernel(const __bf16* __restrict__ src, int64_t ld, int64_t rows,
-                                    int64_t cols, uint8_t* __restrict__ codes,
-                                    uint8_t* __restrict__ scales) {
-  const int64_t groups_per_row = cols / 8;
-  const int64_t total = rows * groups_per_row;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  // every lane of a wave runs the same number of iterations (the loop bound is
-  // rounded up to whole waves) so that the shuffles see the whole wave
-  const int64_t base0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t iters = (total + stride - 1) / stride;
-  for (int64_t it = 0; it < iters; ++it) {
-    const int64_t gi = base0 + it * stride;
-    const bool ok = gi < total;
-    const int64_t row = ok ? gi / groups_per_row : 0;
-    const int64_t col = ok ? (gi % groups_per_row) * 8 : 0;
-    f32x4 lo{0.f, 0.f, 0.f, 0.f}, hi{0.f, 0.f, 0.f, 0.f};
-    if (ok) {
-      const bf16x8 v = *(const bf16x8*)(src + row * ld + col);
-      lo = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-      hi = f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+// ([cols/128][rows][4]).  A workgroup takes G x 256 groups of 8 of one row
+// (blockIdx.x: the chunk of the row, blockIdx.y: the first row, strided by
+// gridDim.y); a thread issues its G loads before it quantises any, so that
+// they are in flight together.  Every lane takes part in the shuffles
+// (cols % 32 == 0 keeps a 32-block's 4 lanes together and either all in
+// range or all out).
+template <int G>
+__global__ void __launch_bounds__(256) mx8_quantize_kernel(const __bf16* __restrict__ src, int64_t ld,
+                                                           int64_t rows, int64_t cols,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales) {
+  const int gpr = (int)(cols / 8);                  // groups of 8 per row
+  const int g0 = (int)blockIdx.x * (256 * G) + (int)threadIdx.x;
+  for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
+    const __bf16* s_row = src + row * ld;
+    bf16x8 v[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int g = g0 + 256 * k;
+      v[k] = g < gpr ? *(const bf16x8*)(s_row + (int64_t)g * 8) : bf16x8{};
     }
-    int sexp;
-    const uint2 w = mx8_block_of_4_lanes(lo, hi, sexp);
-    if (ok) {
-      *(uint2*)(codes + row * cols + col) = w;
-      if ((col & 31) == 0) scales[((col >> 7) * rows + row) * 4 + ((col >> 5) & 3)] = (uint8_t)(sexp + 127);
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int g = g0 + 256 * k;
+      const f32x4 lo{(float)v[k][0], (float)v[k][1], (float)v[k][2], (float)v[k][3]};
+      const f32x4 hi{(float)v[k][4], (float)v[k][5], (float)v[k][6], (float)v[k][7]};
+      int sexp;
+      const uint2 w = mx8_block_of_4_lanes(lo, hi, sexp);
+      if (g < gpr) {
+        const int64_t col = (int64_t)g * 8;
+        *(uint2*)(codes + row * cols + col) = w;
+        if ((g & 3) == 0) scales[((col >> 7) * rows + row) * 4 + ((col >> 5) & 3)] = (uint8_t)(sexp + 127);
+      }
     }
   }
 }
+
+// Column position of element (r, c) in the 128 x 64 staging tile of the
+// column quantisers: 16-byte piece c / 8 of row r moves to piece
+// (c / 8) ^ 2 (r / 32 % 4), so that the four 32-row blocks a group of 4
+// lanes reads (one column, blocks b = 0..3) fall in different banks.
+__device__ __forceinline__ int qt_col(int r, int c) { return ((((c >> 3) ^ (((r >> 5) & 3) << 1))) << 3) | (c & 7); }
 
 // bf16 [rows, cols] -> MXFP8 along the columns' direction, stored transposed:
 // codes [cols][rows] (a column's 32-blocks of consecutive rows are contiguous
 // 32 bytes), scales step-blocked [rows/128][cols][4].  This is the operand
 // layout of a GEMM that contracts over the rows (X^T dy, n^T dz).  A
 // workgroup stages a 128 x 64 tile in LDS (each 16-byte row piece read
-// once); thread (b, c) then quantises column c's rows 32b..32b+31 exactly as
-// the row quantiser does a 32-block and writes its 32 codes as two 16-byte
-// stores.  rows % 128 == 0.
+// once); thread t = 4c + b then quantises column c's rows 32b..32b+31
+// exactly as the row quantiser does a 32-block and writes its 32 codes as
+// two 16-byte stores, so that the 4 lanes of a column fill one 128-byte run
+// of the output.  rows % 128 == 0.
 __global__ void __launch_bounds__(256) mx8_quantize_t_kernel(const __bf16* __restrict__ src, int64_t ld,
                                                              int64_t rows, int64_t cols,
                                                              uint8_t* __restrict__ codes,
@@ -1407,14 +1420,14 @@ __global__ void __launch_bounds__(256) mx8_quantize_t_kernel(const __bf16* __res
     const int64_t col = col0 + c8;
     bf16x8 v{};
     if (col < cols) v = *(const bf16x8*)(src + (row0 + r) * ld + col);
-    *(bf16x8*)&tile[r][c8] = v;
+    *(bf16x8*)&tile[r][qt_col(r, c8)] = v;
   }
   __syncthreads();
-  const int c = t & 63, b = t >> 6;       // column, 32-row block
+  const int c = t >> 2, b = t & 3;        // column, 32-row block
   const int64_t col = col0 + c;
   float v[32];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) v[e] = (float)tile[32 * b + e][c];
+  for (int e = 0; e < 32; ++e) v[e] = (float)tile[32 * b + e][qt_col(32 * b, c)];
   uint32_t w[8];
   const int sexp = mx8_block32(v, w);
   if (col < cols) {
@@ -1442,7 +1455,7 @@ __global__ void __launch_bounds__(256) mx8_quantize_t_kernel(const __bf16* __res
 // n and dy of the bf16 backward).  A workgroup takes a 128 x 64 tile: each
 // thread produces 4 pieces of 8 values, quantises them along the row with
 // its 3 neighbours (the row quantiser's arithmetic), and stages them in LDS;
-// thread (b, c) then quantises column c's rows 32b..32b+31 as the transposed
+// thread 4c + b then quantises column c's rows 32b..32b+31 as the transposed
 // quantiser does.
 enum QuantMode : int { QUANT_SRC = 0, QUANT_DY = 1, QUANT_NROW = 2 };
 template <int MODE>
@@ -1479,7 +1492,7 @@ __global__ void __launch_bounds__(256) mx8_quantize_fused_kernel(MxQuantArgs q) 
         for (int e = 0; e < 8; ++e) v[e] = f2bf(ri * bf2f(a[e]));
       }
     }
-    *(bf16x8*)&tile[r][c8] = v;
+    *(bf16x8*)&tile[r][qt_col(r, c8)] = v;
     if (MODE != QUANT_NROW && q.qr) {             // uniform over the grid
       const f32x4 lo{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
       const f32x4 hi{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
@@ -1492,11 +1505,11 @@ __global__ void __launch_bounds__(256) mx8_quantize_fused_kernel(MxQuantArgs q) 
     }
   }
   __syncthreads();
-  const int c = t & 63, b = t >> 6;       // column, 32-row block
+  const int c = t >> 2, b = t & 3;        // column, 32-row block (4 lanes per column)
   const int64_t col = col0 + c;
   float v[32];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) v[e] = (float)tile[32 * b + e][c];
+  for (int e = 0; e < 32; ++e) v[e] = (float)tile[32 * b + e][qt_col(32 * b, c)];
   uint32_t w[8];
   const int sexp = mx8_block32(v, w);
   if (col < q.cols) {
@@ -1822,12 +1835,29 @@ hipError_t launch_mx8_quantize_fused(const MxQuantArgs& q, int mode, hipStream_t
 
 hipError_t launch_mx8_quantize(const void* src, int64_t ld, int64_t rows, int64_t cols,
                                uint8_t* codes, uint8_t* scales, hipStream_t s) {
-  // 32 groups of 8 per 256-thread block; the lanes of a 32-block stay in one
-  // wave because cols is a multiple of 32
-  const int64_t total = rows * (cols / 8);
-  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 256 * 16);
-  hipLaunchKernelGGL(mx8_quantize_kernel, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, s,
-                     (const __bf16*)src, ld, rows, cols, codes, scales);
+  // groups of 8 per thread (1, 2 or 4): the count that leaves the fewest
+  // threads of a row's last chunk idle, the larger on a tie; rows beyond the
+  // grid's 65535 are strided
+  const int64_t gpr = cols / 8;
+  int G = 4;
+  int64_t idle = (gpr + 1023) / 1024 * 1024 - gpr;
+  for (int g : {2, 1}) {
+    const int64_t per = 256 * (int64_t)g, i = (gpr + per - 1) / per * per - gpr;
+    if (i < idle) {
+      idle = i;
+      G = g;
+    }
+  }
+  const dim3 grid((unsigned)((gpr + 256 * G - 1) / (256 * G)), (unsigned)std::min<int64_t>(rows, 65535));
+  if (G == 4)
+    hipLaunchKernelGGL(mx8_quantize_kernel<4>, grid, dim3(256), 0, s, (const __bf16*)src, ld, rows, cols, codes,
+                       scales);
+  else if (G == 2)
+    hipLaunchKernelGGL(mx8_quantize_kernel<2>, grid, dim3(256), 0, s, (const __bf16*)src, ld, rows, cols, codes,
+                       scales);
+  else
+    hipLaunchKernelGGL(mx8_quantize_kernel<1>, grid, dim3(256), 0, s, (const __bf16*)src, ld, rows, cols, codes,
+                       scales);
   return hipGetLastError();
 }
 
