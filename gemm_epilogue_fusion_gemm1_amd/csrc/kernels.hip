@@ -1413,14 +1413,21 @@ __global__ void __launch_bounds__(256) mx8_quantize_t_kernel(const __bf16* __res
   __shared__ __bf16 tile[128][64];
   const int64_t row0 = (int64_t)blockIdx.y * 128, col0 = (int64_t)blockIdx.x * 64;
   const int t = threadIdx.x;
+  // 1024 pieces of 8 values, 4 per thread.  A piece past the last column
+  // reads the row's last piece instead (cols % 8 == 0) and stages zeros, so
+  // the four loads carry no branch and are in flight together.
+  bf16x8 raw[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {           // 1024 pieces of 8 values, 4 per thread
+  for (int k = 0; k < 4; ++k) {
     const int piece = t + 256 * k;
     const int r = piece >> 3, c8 = (piece & 7) * 8;
-    const int64_t col = col0 + c8;
-    bf16x8 v{};
-    if (col < cols) v = *(const bf16x8*)(src + (row0 + r) * ld + col);
-    *(bf16x8*)&tile[r][qt_col(r, c8)] = v;
+    raw[k] = *(const bf16x8*)(src + (row0 + r) * ld + min(col0 + c8, cols - 8));
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int piece = t + 256 * k;
+    const int r = piece >> 3, c8 = (piece & 7) * 8;
+    *(bf16x8*)&tile[r][qt_col(r, c8)] = col0 + c8 < cols ? raw[k] : bf16x8{};
   }
   __syncthreads();
   const int c = t >> 2, b = t & 3;        // column, 32-row block
@@ -1463,35 +1470,48 @@ __global__ void __launch_bounds__(256) mx8_quantize_fused_kernel(MxQuantArgs q) 
   __shared__ __bf16 tile[128][64];
   const int64_t row0 = (int64_t)blockIdx.y * 128, col0 = (int64_t)blockIdx.x * 64;
   const int t = threadIdx.x;
+  // 1024 pieces of 8 values, 4 per thread.  Every operand of the 4 pieces is
+  // loaded before any is used, a piece past the last column reading the
+  // row's last piece (cols % 8 == 0; its values are dropped), so the loads
+  // carry no branch and are in flight together.
+  bf16x8 a[4], yv[4], din[4];
+  float ri[4], ci[4];
+  const bool has_din = MODE == QUANT_DY && q.dy_in;   // uniform over the grid
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {           // 1024 pieces of 8 values, 4 per thread
+  for (int k = 0; k < 4; ++k) {
+    const int piece = t + 256 * k;
+    const int64_t row = row0 + (piece >> 3), col = min(col0 + (piece & 7) * 8, q.cols - 8);
+    a[k] = *(const bf16x8*)((const __bf16*)q.src + row * q.ld + col);
+    if constexpr (MODE == QUANT_DY) {
+      yv[k] = *(const bf16x8*)((const __bf16*)q.y + row * q.ld + col);
+      ci[k] = q.c[row];
+      if (has_din) din[k] = *(const bf16x8*)((const __bf16*)q.dy_in + row * q.ld + col);
+    }
+    if constexpr (MODE != QUANT_SRC) ri[k] = q.r[row];
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
     const int piece = t + 256 * k;
     const int r = piece >> 3, c8 = (piece & 7) * 8;
     const int64_t row = row0 + r, col = col0 + c8;
     const bool ok = col < q.cols;
     bf16x8 v{};
-    if (ok) {
-      const bf16x8 a = *(const bf16x8*)((const __bf16*)q.src + row * q.ld + col);
-      if constexpr (MODE == QUANT_SRC) {
-        v = a;
-      } else if constexpr (MODE == QUANT_DY) {
-        const bf16x8 yv = *(const bf16x8*)((const __bf16*)q.y + row * q.ld + col);
-        const float ri = q.r[row], ci = q.c[row];
-        if (q.dy_in) {
-          const bf16x8 din = *(const bf16x8*)((const __bf16*)q.dy_in + row * q.ld + col);
+    if constexpr (MODE == QUANT_SRC) {
+      v = a[k];
+    } else if constexpr (MODE == QUANT_DY) {
+      if (has_din) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = f2bf(ri * bf2f(a[e]) - ci * bf2f(yv[e]) + bf2f(din[e]));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = f2bf(ri * bf2f(a[e]) - ci * bf2f(yv[e]));
-        }
-        *(bf16x8*)((__bf16*)q.out + row * q.ld + col) = v;
+        for (int e = 0; e < 8; ++e) v[e] = f2bf(ri[k] * bf2f(a[k][e]) - ci[k] * bf2f(yv[k][e]) + bf2f(din[k][e]));
       } else {
-        const float ri = q.r[row];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = f2bf(ri * bf2f(a[e]));
+        for (int e = 0; e < 8; ++e) v[e] = f2bf(ri[k] * bf2f(a[k][e]) - ci[k] * bf2f(yv[k][e]));
       }
+      if (ok) *(bf16x8*)((__bf16*)q.out + row * q.ld + col) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = f2bf(ri[k] * bf2f(a[k][e]));
     }
+    if (!ok) v = bf16x8{};
     *(bf16x8*)&tile[r][qt_col(r, c8)] = v;
     if (MODE != QUANT_NROW && q.qr) {             // uniform over the grid
       const f32x4 lo{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
