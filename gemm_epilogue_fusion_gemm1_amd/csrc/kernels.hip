@@ -1411,7 +1411,10 @@ __global__ void __launch_bounds__(256) mx8_quantize_t_kernel(const __bf16* __res
                                                              uint8_t* __restrict__ codes,
                                                              uint8_t* __restrict__ scales) {
   __shared__ __bf16 tile[128][64];
-  const int64_t row0 = (int64_t)blockIdx.y * 128, col0 = (int64_t)blockIdx.x * 64;
+  // one-dimensional grid, column blocks fastest: block (rb, cb)
+  const uint32_t ncb = (uint32_t)((cols + 63) / 64);
+  const uint32_t rb = blockIdx.x / ncb, cb = blockIdx.x - rb * ncb;
+  const int64_t row0 = (int64_t)rb * 128, col0 = (int64_t)cb * 64;
   const int t = threadIdx.x;
   // 1024 pieces of 8 values, 4 per thread.  A piece past the last column
   // reads the row's last piece instead (cols % 8 == 0) and stages zeros, so
@@ -1441,7 +1444,7 @@ __global__ void __launch_bounds__(256) mx8_quantize_t_kernel(const __bf16* __res
     uint8_t* dst = codes + col * rows + row0 + 32 * b;
     *(uint4*)dst = uint4{w[0], w[1], w[2], w[3]};
     *(uint4*)(dst + 16) = uint4{w[4], w[5], w[6], w[7]};
-    scales[((int64_t)blockIdx.y * cols + col) * 4 + b] = (uint8_t)(sexp + 127);
+    scales[((int64_t)rb * cols + col) * 4 + b] = (uint8_t)(sexp + 127);
   }
 }
 
@@ -1468,7 +1471,10 @@ enum QuantMode : int { QUANT_SRC = 0, QUANT_DY = 1, QUANT_NROW = 2 };
 template <int MODE>
 __global__ void __launch_bounds__(256) mx8_quantize_fused_kernel(MxQuantArgs q) {
   __shared__ __bf16 tile[128][64];
-  const int64_t row0 = (int64_t)blockIdx.y * 128, col0 = (int64_t)blockIdx.x * 64;
+  // one-dimensional grid, column blocks fastest: block (rb, cb)
+  const uint32_t ncb = (uint32_t)((q.cols + 63) / 64);
+  const uint32_t rb = blockIdx.x / ncb, cb = blockIdx.x - rb * ncb;
+  const int64_t row0 = (int64_t)rb * 128, col0 = (int64_t)cb * 64;
   const int t = threadIdx.x;
   // 1024 pieces of 8 values, 4 per thread.  Every operand of the 4 pieces is
   // loaded before any is used, a piece past the last column reading the
@@ -1544,7 +1550,7 @@ __global__ void __launch_bounds__(256) mx8_quantize_fused_kernel(MxQuantArgs q) 
     uint8_t* dst = q.qt + tr * q.rows + row0 + 32 * b;
     *(uint4*)dst = uint4{w[0], w[1], w[2], w[3]};
     *(uint4*)(dst + 16) = uint4{w[4], w[5], w[6], w[7]};
-    q.st[((int64_t)blockIdx.y * q.cols + tr) * 4 + b] = (uint8_t)(sexp + 127);
+    q.st[((int64_t)rb * q.cols + tr) * 4 + b] = (uint8_t)(sexp + 127);
   }
 }
 
@@ -1836,14 +1842,20 @@ hipError_t launch_gemm_mx8(const GemmArgs& g, Epi epi, hipStream_t s) {
 
 hipError_t launch_mx8_quantize_t(const void* src, int64_t ld, int64_t rows, int64_t cols, uint8_t* codes,
                                  uint8_t* scales, hipStream_t s) {
-  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)(rows / 128));
+  // (cols / 64 rounded up) x (rows / 128) blocks in one dimension: rows up
+  // to 2^23 would overflow the 65535 limit of a second grid dimension
+  const int64_t blocks = (cols + 63) / 64 * (rows / 128);
+  if (blocks < 1 || blocks > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks);
   hipLaunchKernelGGL(mx8_quantize_t_kernel, grid, dim3(256), 0, s, (const __bf16*)src, ld, rows, cols, codes,
                      scales);
   return hipGetLastError();
 }
 
 hipError_t launch_mx8_quantize_fused(const MxQuantArgs& q, int mode, hipStream_t s) {
-  const dim3 grid((unsigned)((q.cols + 63) / 64), (unsigned)(q.rows / 128));
+  const int64_t blocks = (q.cols + 63) / 64 * (q.rows / 128);   // as the transposing quantiser
+  if (blocks < 1 || blocks > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks);
   switch (mode) {
     case QUANT_SRC: hipLaunchKernelGGL(mx8_quantize_fused_kernel<QUANT_SRC>, grid, dim3(256), 0, s, q); break;
     case QUANT_DY: hipLaunchKernelGGL(mx8_quantize_fused_kernel<QUANT_DY>, grid, dim3(256), 0, s, q); break;
