@@ -1217,6 +1217,33 @@ def pin_bwd_mx8_sampled(O):
     _close(sm["dgamma"], full["dgamma"], 1e-12, "mx8 sampled dgamma")
 
 
+def pin_bwd_mx8_row_blocks(O):
+    """MXFP8 blocks along M are local: with dz zero outside a few rows, dn,
+    s, c and dy vanish there, so dX and dR are zero on every other row, and
+    the backward on the whole aligned 32-row blocks holding those rows alone
+    equals the full backward exactly (their quantisation along M is the same
+    inside the full matrix).  The GPU test at the largest row count relies on
+    this."""
+    M, K, d, N = 512, 32, 64, 96
+    c = _bwd_mx8_case(95, M, K, d, N)
+    y = O.bf16_rne(c["y"])
+    r = 1.0 / np.sqrt(np.mean(y * y, axis=1) + 1e-6)
+    hot = np.array([0, 45, 200, M - 100, M - 1])
+    dz = np.zeros((M, N))
+    dz[hot] = c["dz"][hot]
+    full = O.ref_bwd_mx8(c["X"], c["W1"], c["gamma"], c["W2"], y, r, dz)
+    blocks = np.unique(hot // 32)
+    rows = (blocks[:, None] * 32 + np.arange(32)[None, :]).ravel()
+    rest = np.setdiff1d(np.arange(M), rows)
+    sub = O.ref_bwd_mx8(c["X"][rows], c["W1"], c["gamma"], c["W2"], y[rows], r[rows], dz[rows])
+    if np.any(full["dX"][rest]) or np.any(full["dR"][rest]):
+        raise AssertionError("mx8 bwd: dX / dR nonzero outside the rows with a gradient")
+    for k in ("dW1", "dW2", "dgamma"):
+        _close(sub[k], full[k], 1e-12, f"mx8 bwd {k} from the gathered row blocks")
+    _close(sub["dX"], full["dX"][rows], 1e-12, "mx8 bwd dX on the gathered row blocks")
+    _close(sub["dR"], full["dR"][rows], 1e-12, "mx8 bwd dR on the gathered row blocks")
+
+
 def _swiglu_mx8_case(seed, M, d, F):
     g = _rng(seed)
     return dict(X=g.standard_normal((M, d)), W=g.standard_normal((d, 2 * F)) / math.sqrt(d),
@@ -1439,6 +1466,7 @@ ALL_PINS = [
     pin_rope_sampled,
     pin_bwd_dy_in_finite_differences, pin_e4m3_codes, pin_mx_quantize, pin_fwd_mx8_exact,
     pin_fwd_mx8_bruteforce, pin_fwd_mx8_rows, pin_mx_matmul, pin_bwd_mx8_bruteforce,
-    pin_bwd_mx8_grid_exact, pin_bwd_mx8_sampled, pin_swiglu_mx8_bruteforce, pin_swiglu_mx8_grid_exact,
+    pin_bwd_mx8_grid_exact, pin_bwd_mx8_sampled, pin_bwd_mx8_row_blocks, pin_swiglu_mx8_bruteforce,
+    pin_swiglu_mx8_grid_exact,
     pin_swiglu_mx8_sampled, pin_mlp_mx8_bruteforce, pin_mlp_mx8_grid_exact, pin_mlp_mx8_sampled,
 ]

@@ -328,6 +328,58 @@ def test_full_workload_bwd_mx8(torch_dev):
     assert errs["dgamma"] <= 1e-3
 
 
+def test_bwd_mx8_max_rows(torch_dev):
+    """The largest accepted token count, M = 2^23: the passes that quantise
+    along M run over 65536 blocks of 128 rows.  K = 8, d = N = 128, and dz
+    is nonzero in six rows only (the first, the last, one in the last
+    128-row block and three between), so every gradient vanishes outside
+    those rows (dn = 0 there, hence s = c = 0 and dy = 0) and every sum over
+    M gets terms from their 32-row quantisation blocks alone.  Whole aligned
+    32-row blocks quantise along M as they do inside the full matrix, so the
+    oracle's backward on the gathered blocks is the full one: dX and dR are
+    compared on those rows and must be exactly zero on every other row;
+    dW1, dW2 and dgamma are compared in full.  The bulk inputs come from
+    torch's seeded generator on the device; W1, W2 and gamma from the
+    workload draws."""
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    M, K, d, N = 1 << 23, 8, 128, 128
+    hot = np.array([0, 77, 123457, (1 << 22) + 3, M - 100, M - 1])
+    blocks = np.unique(hot // 32)
+    rows = (blocks[:, None] * 32 + np.arange(32)[None, :]).ravel()
+    print(f"[parity] mx8 bwd M=2^23: inputs ({len(rows)} rows in {len(blocks)} blocks checked)", flush=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(9090)
+    X = torch.randn((M, K), generator=g, device=dev, dtype=torch.bfloat16)
+    y = torch.randn((M, d), generator=g, device=dev, dtype=torch.bfloat16)
+    r = 0.5 + torch.rand((M,), generator=g, device=dev, dtype=torch.float32)
+    dz = torch.zeros((M, N), dtype=torch.bfloat16, device=dev)
+    hot_t = torch.from_numpy(hot).to(dev)
+    dz[hot_t] = torch.randn((len(hot), N), generator=g, device=dev, dtype=torch.bfloat16)
+    w = synth.coda_inputs(128, K, d, N, seed=9091, dtype="bf16")
+    W1, gamma, W2 = bf(torch, dev, w["W1"]), bf(torch, dev, w["gamma"]), bf(torch, dev, w["W2"])
+    print("[parity] mx8 bwd M=2^23: coda_bwd_mx8", flush=True)
+    dX, dW1, dR, dW2, dg = coda.bwd_mx8(X, W1, gamma, W2, y, r, dz)
+    torch.cuda.synchronize()
+    rows_t = torch.from_numpy(rows).to(dev)
+    rest = torch.ones((M,), dtype=torch.bool, device=dev)
+    rest[rows_t] = False
+    zero_dX = int(torch.count_nonzero(dX[rest]))
+    zero_dR = int(torch.count_nonzero(dR[rest]))
+    f = lambda t: t.float().cpu().numpy()  # noqa: E731
+    print("[parity] mx8 bwd M=2^23: oracle on the gathered blocks", flush=True)
+    b = oracle.ref_bwd_mx8(f(X[rows_t]), f(W1), f(gamma), f(W2), f(y[rows_t]), r[rows_t].cpu().numpy(),
+                           f(dz[rows_t]))
+    errs = {"dX_rows": rel(f(dX[rows_t]), b["dX"]), "dR_rows": rel(f(dR[rows_t]), b["dR"]),
+            "dW1": rel(f(dW1), b["dW1"]), "dW2": rel(f(dW2), b["dW2"]),
+            "dgamma": rel(dg.cpu().numpy(), b["dgamma"]), "nonzero_dX_elsewhere": zero_dX,
+            "nonzero_dR_elsewhere": zero_dR}
+    report("mx8 bwd M=2^23", errs)
+    assert zero_dX == 0 and zero_dR == 0
+    for k in ("dX_rows", "dR_rows", "dW1", "dW2"):
+        assert errs[k] <= BF16_TOL, (k, errs[k])
+    assert errs["dgamma"] <= 1e-3
+
 
 # ---------------------------------------------------------------- SwiGLU block
 
