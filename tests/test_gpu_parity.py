@@ -99,6 +99,61 @@ def test_coda_fwd_bwd_bf16(torch_dev, shape):
     assert errs["dgamma"] <= DGAMMA_TOL
 
 
+def test_coda_max_rows(torch_dev):
+    """The largest accepted token count, M = 2^23, in bf16 (K = 8, d = N =
+    128): y*gamma stored transposed, n, dz and dR are 2 GiB each, so K2 and
+    the backward's GEMMs reach them through buffer windows over 32768 row
+    tiles, and dW1 and dW2 contract over 2^23 rows.  Forward: y, z and r on
+    sampled rows (the first and last tiles' edges, one row per 2^20, the
+    hot rows), which are row-local.  Backward, fed the forward's y and r:
+    dz is nonzero in six rows, so every gradient vanishes on the other rows
+    (dn = 0, hence s = c = 0 and dy = 0) and the sums over M take those rows
+    alone; the oracle's backward on them is the full one, and dX and dR must
+    be exactly zero on every other row.  The bulk inputs come from torch's
+    seeded generator on the device; W1, W2 and gamma from the workload
+    draws."""
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    M, K, d, N = 1 << 23, 8, 128, 128
+    eps = 1e-6
+    hot = np.array([0, 77, 123457, (1 << 22) + 3, M - 100, M - 1])
+    print("[parity] coda bf16 M=2^23: inputs", flush=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(9190)
+    X = torch.randn((M, K), generator=g, device=dev, dtype=torch.bfloat16)
+    R = torch.randn((M, d), generator=g, device=dev, dtype=torch.bfloat16)
+    dz = torch.zeros((M, N), dtype=torch.bfloat16, device=dev)
+    hot_t = torch.from_numpy(hot).to(dev)
+    dz[hot_t] = torch.randn((len(hot), N), generator=g, device=dev, dtype=torch.bfloat16)
+    w = synth.coda_inputs(128, K, d, N, seed=9191, dtype="bf16")
+    W1, gamma, W2 = (up(torch, dev, w[k], "bf16") for k in ("W1", "gamma", "W2"))
+    print("[parity] coda bf16 M=2^23: coda_fwd, coda_bwd", flush=True)
+    z, y, r = coda.fwd(X, W1, R, gamma, W2, eps)
+    dX, dW1, dR, dW2, dg = coda.bwd(X, W1, gamma, W2, y, r, dz)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(M - 8, M), np.arange(5, M, 1 << 20), hot]))
+    rows_t = torch.from_numpy(rows).to(dev)
+    rest = torch.ones((M,), dtype=torch.bool, device=dev)
+    rest[hot_t] = False
+    nz_dX, nz_dR = int(torch.count_nonzero(dX[rest])), int(torch.count_nonzero(dR[rest]))
+    print("[parity] coda bf16 M=2^23: oracle on the sampled and hot rows", flush=True)
+    Wh = [host(t) for t in (W1, gamma, W2)]
+    f = oracle.ref_fwd(host(X[rows_t]), Wh[0], host(R[rows_t]), Wh[1], Wh[2], eps)
+    b = oracle.ref_bwd(host(X[hot_t]), Wh[0], Wh[1], Wh[2], host(y[hot_t]), r[hot_t].cpu().numpy(),
+                       host(dz[hot_t]))
+    errs = {"y_rows": rel(host(y[rows_t]), f["y"]), "z_rows": rel(host(z[rows_t]), f["z"]),
+            "r_rows": float(np.max(np.abs(r[rows_t].cpu().numpy() - f["r"]) / f["r"])),
+            "dX_hot": rel(host(dX[hot_t]), b["dX"]), "dR_hot": rel(host(dR[hot_t]), b["dR"]),
+            "dW1": rel(host(dW1), b["dW1"]), "dW2": rel(host(dW2), b["dW2"]),
+            "dgamma": rel(dg.cpu().numpy(), b["dgamma"])}
+    report("coda bf16 M=2^23", {**errs, "nonzero_dX_elsewhere": float(nz_dX), "nonzero_dR_elsewhere": float(nz_dR)})
+    assert nz_dX == 0 and nz_dR == 0
+    for k in ("y_rows", "z_rows", "dX_hot", "dR_hot", "dW1", "dW2"):
+        assert errs[k] <= BF16_TOL, (k, errs[k])
+    assert errs["r_rows"] <= R_TOL
+    assert errs["dgamma"] <= DGAMMA_TOL
+
+
 @pytest.mark.parametrize("shape", [(128, 256, 256, 512), (132, 260, 196, 68), (4, 4, 4, 4)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_coda_fwd_f32(torch_dev, shape):
