@@ -1304,6 +1304,30 @@ def _mx_grid_both(g, shape):
     return out * 2.0 ** -12
 
 
+def pin_swiglu_mx8_row_blocks(O):
+    """As pin_bwd_mx8_row_blocks for the SwiGLU block: with dz zero outside
+    a few rows, da, dgu and dX vanish there, and the backward on the whole
+    aligned 32-row blocks holding those rows equals the full one."""
+    g = _rng(96)
+    M, d, F = 512, 64, 96
+    c = _swiglu_mx8_case(97, M, d, F)
+    f = O.ref_swiglu_fwd_mx8(c["X"], c["W"], c["Wd"])
+    gu, a = O.bf16_rne(f["gu"]), O.bf16_rne(f["a"])
+    hot = np.array([0, 45, 200, M - 100, M - 1])
+    dz = np.zeros((M, d))
+    dz[hot] = g.standard_normal((len(hot), d))
+    full = O.ref_swiglu_bwd_mx8(c["X"], c["W"], c["Wd"], gu, a, dz)
+    blocks = np.unique(hot // 32)
+    rows = (blocks[:, None] * 32 + np.arange(32)[None, :]).ravel()
+    rest = np.setdiff1d(np.arange(M), rows)
+    sub = O.ref_swiglu_bwd_mx8(c["X"][rows], c["W"], c["Wd"], gu[rows], a[rows], dz[rows])
+    if np.any(full["dX"][rest]) or np.any(full["dgu"][rest]):
+        raise AssertionError("swiglu mx8 bwd: dX / dgu nonzero outside the rows with a gradient")
+    for k in ("dW", "dWd"):
+        _close(sub[k], full[k], 1e-12, f"swiglu mx8 bwd {k} from the gathered row blocks")
+    _close(sub["dX"], full["dX"][rows], 1e-12, "swiglu mx8 bwd dX on the gathered row blocks")
+
+
 def pin_swiglu_mx8_grid_exact(O):
     """With operands on the MXFP8 grid the quantised products are exact, so
     the MXFP8 SwiGLU reduces to the pinned ref_swiglu_fwd / ref_swiglu_bwd:
@@ -1467,6 +1491,6 @@ ALL_PINS = [
     pin_bwd_dy_in_finite_differences, pin_e4m3_codes, pin_mx_quantize, pin_fwd_mx8_exact,
     pin_fwd_mx8_bruteforce, pin_fwd_mx8_rows, pin_mx_matmul, pin_bwd_mx8_bruteforce,
     pin_bwd_mx8_grid_exact, pin_bwd_mx8_sampled, pin_bwd_mx8_row_blocks, pin_swiglu_mx8_bruteforce,
-    pin_swiglu_mx8_grid_exact,
+    pin_swiglu_mx8_grid_exact, pin_swiglu_mx8_row_blocks,
     pin_swiglu_mx8_sampled, pin_mlp_mx8_bruteforce, pin_mlp_mx8_grid_exact, pin_mlp_mx8_sampled,
 ]

@@ -198,6 +198,54 @@ def test_swiglu_fwd_bwd(torch_dev, shape):
         assert v <= BF16_TOL, (k, v)
 
 
+def test_swiglu_max_rows(torch_dev):
+    """The SwiGLU block in bf16 at the largest accepted token count, M = 2^23
+    (d = F = 128): X, a, dz and dX are 2 GiB and gu and dgu 4 GiB, so every
+    GEMM reaches its token-sized operand through buffer windows (the gate/up
+    weight's interleaving loader included), and dW and dWd contract over
+    2^23 rows.  The forward on sampled rows (row-local).  The backward, fed
+    the forward's gu and a, with dz nonzero in six rows: da, dgu and dX
+    vanish on every other row and the sums over M take those rows alone, so
+    the oracle's backward on them is the full one; dX must be exactly zero
+    on every other row.  The bulk inputs come from torch's seeded generator
+    on the device; W and Wd from the workload draws."""
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    M, d, F = 1 << 23, 128, 128
+    hot = np.array([0, 77, 123457, (1 << 22) + 3, M - 100, M - 1])
+    print("[parity] swiglu bf16 M=2^23: inputs", flush=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(9390)
+    X = torch.randn((M, d), generator=g, device=dev, dtype=torch.bfloat16)
+    dz = torch.zeros((M, d), dtype=torch.bfloat16, device=dev)
+    hot_t = torch.from_numpy(hot).to(dev)
+    dz[hot_t] = torch.randn((len(hot), d), generator=g, device=dev, dtype=torch.bfloat16)
+    w = synth.swiglu_inputs(128, d, F, seed=9391)
+    W, Wd = up(torch, dev, w["W"], "bf16"), up(torch, dev, w["Wd"], "bf16")
+    print("[parity] swiglu bf16 M=2^23: forward and backward", flush=True)
+    z, gu, a = coda.swiglu_fwd(X, W, Wd)
+    dX, dW, dWd = coda.swiglu_bwd(X, W, Wd, gu, a, dz)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(M - 8, M), np.arange(5, M, 1 << 20), hot]))
+    rows_t = torch.from_numpy(rows).to(dev)
+    rest = torch.ones((M,), dtype=torch.bool, device=dev)
+    rest[hot_t] = False
+    nz_dX = int(torch.count_nonzero(dX[rest]))
+    print("[parity] swiglu bf16 M=2^23: oracle on the sampled and hot rows", flush=True)
+    Wh, Wdh = host(W), host(Wd)
+    f = oracle.ref_swiglu_fwd(host(X[rows_t]), Wh, Wdh)
+    b = oracle.ref_swiglu_bwd(host(X[hot_t]), Wh, Wdh, host(gu[hot_t]), host(a[hot_t]), host(dz[hot_t]))
+    errs = {"z_rows": rel(host(z[rows_t]), f["z"]), "gu_rows": rel(host(gu[rows_t]), f["gu"]),
+            "a_rows": rel(host(a[rows_t]), f["a"]), "dX_hot": rel(host(dX[hot_t]), b["dX"]),
+            "dW": rel(host(dW), b["dW"]), "dWd": rel(host(dWd), b["dWd"])}
+    report("swiglu bf16 M=2^23", {**errs, "nonzero_dX_elsewhere": float(nz_dX)})
+    del X, dz, z, gu, a, dX, rest                      # ~20 GB: give it back before the next test
+    torch.cuda.empty_cache()
+    assert nz_dX == 0
+    for k, v in errs.items():
+        assert v <= BF16_TOL, (k, v)
+
+
 # ------------------------------------------------------------- edge cases
 
 def test_zero_rows_and_determinism(torch_dev):

@@ -469,6 +469,59 @@ def test_full_workload_swiglu_mx8(torch_dev):
         assert v <= BF16_TOL, (k, v)
 
 
+def test_swiglu_mx8_max_rows(torch_dev):
+    """The SwiGLU block on MXFP8 at the largest accepted token count, M =
+    2^23 (d = F = 128): gu is 4 GiB and the MXFP8 dgu 2 GiB, so the backward
+    GEMMs reach dgu through buffer windows, and the passes along M (a, X and
+    dz, and dgu in the da GEMM's epilogue) run over 65536 row blocks.  The
+    forward on sampled rows (row-local: X, a and the weights are quantised
+    along d and F).  The backward, fed the forward's gu and a, with dz
+    nonzero in six rows: da, dgu and dX vanish on every other row and the
+    sums over M take terms from those rows' 32-row quantisation blocks alone,
+    so the oracle on the gathered blocks is the full one (a CPU pin checks
+    this); dX must be exactly zero outside those blocks.  The bulk inputs
+    come from torch's seeded generator on the device; W and Wd from the
+    workload draws."""
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    M, d, F = 1 << 23, 128, 128
+    hot = np.array([0, 77, 123457, (1 << 22) + 3, M - 100, M - 1])
+    blocks = np.unique(hot // 32)
+    brows = (blocks[:, None] * 32 + np.arange(32)[None, :]).ravel()
+    print("[parity] swiglu mx8 M=2^23: inputs", flush=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(9290)
+    X = torch.randn((M, d), generator=g, device=dev, dtype=torch.bfloat16)
+    dz = torch.zeros((M, d), dtype=torch.bfloat16, device=dev)
+    hot_t = torch.from_numpy(hot).to(dev)
+    dz[hot_t] = torch.randn((len(hot), d), generator=g, device=dev, dtype=torch.bfloat16)
+    w = synth.swiglu_inputs(128, d, F, seed=9291)
+    W, Wd = bf(torch, dev, w["W"]), bf(torch, dev, w["Wd"])
+    print("[parity] swiglu mx8 M=2^23: forward and backward", flush=True)
+    z, gu, a = coda.swiglu_fwd_mx8(X, W, Wd)
+    dX, dW, dWd = coda.swiglu_bwd_mx8(X, W, Wd, gu, a, dz)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(M - 8, M), np.arange(5, M, 1 << 20), hot]))
+    rows_t, brows_t = torch.from_numpy(rows).to(dev), torch.from_numpy(brows).to(dev)
+    rest = torch.ones((M,), dtype=torch.bool, device=dev)
+    rest[brows_t] = False
+    nz_dX = int(torch.count_nonzero(dX[rest]))
+    h = lambda v: v.float().cpu().numpy()  # noqa: E731
+    Wh, Wdh = h(W), h(Wd)
+    print("[parity] swiglu mx8 M=2^23: oracle on the sampled rows and gathered blocks", flush=True)
+    f = oracle.ref_swiglu_fwd_mx8(h(X[rows_t]), Wh, Wdh)
+    b = oracle.ref_swiglu_bwd_mx8(h(X[brows_t]), Wh, Wdh, h(gu[brows_t]), h(a[brows_t]), h(dz[brows_t]))
+    errs = {"z_rows": rel(h(z[rows_t]), f["z"]), "gu_rows": rel(h(gu[rows_t]), f["gu"]),
+            "a_rows": rel(h(a[rows_t]), f["a"]), "dX_blocks": rel(h(dX[brows_t]), b["dX"]),
+            "dW": rel(h(dW), b["dW"]), "dWd": rel(h(dWd), b["dWd"])}
+    report("swiglu mx8 M=2^23", {**errs, "nonzero_dX_elsewhere": nz_dX})
+    del X, dz, z, gu, a, dX, rest                      # ~25 GB: give it back before the next test
+    torch.cuda.empty_cache()
+    assert nz_dX == 0
+    for k, v in errs.items():
+        assert v <= BF16_TOL, (k, v)
+
+
 # ----------------------------------------------------------- MLP sub-layer
 
 SMALL_MLP_MX8 = [
