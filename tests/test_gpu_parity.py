@@ -661,6 +661,68 @@ def test_full_workload_mlp(torch_dev):
     assert errs["dgamma"] <= DGAMMA_TOL
 
 
+def test_mlp_max_rows(torch_dev):
+    """The MLP sub-layer in bf16 at the largest accepted token count, M = 2^23
+    (K = 8, d = F = 128): y*gamma stored transposed is 2 GiB, so the gate/up
+    GEMM that applies r in its epilogue reads it through buffer windows, as
+    the backward's GEMMs read gu, dgu, dz and dR, over 32768 row tiles.  The
+    forward on sampled rows (row-local).  The backward, fed the forward's y,
+    r, gu and a, with dz and dy_in nonzero in six rows: every gradient
+    vanishes on the other rows and the sums over M take those rows alone, so
+    the oracle's backward on them (dgu rounded to bf16, the storage
+    contract) is the full one; dX and dR must be exactly zero on every other
+    row.  The bulk inputs come from torch's seeded generator on the device;
+    the weights from the workload draws."""
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    M, K, d, F = 1 << 23, 8, 128, 128
+    eps = 1e-6
+    hot = np.array([0, 77, 123457, (1 << 22) + 3, M - 100, M - 1])
+    print("[parity] mlp bf16 M=2^23: inputs", flush=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(9490)
+    X = torch.randn((M, K), generator=g, device=dev, dtype=torch.bfloat16)
+    R = torch.randn((M, d), generator=g, device=dev, dtype=torch.bfloat16)
+    hot_t = torch.from_numpy(hot).to(dev)
+    dz = torch.zeros((M, d), dtype=torch.bfloat16, device=dev)
+    dy_in = torch.zeros((M, d), dtype=torch.bfloat16, device=dev)
+    dz[hot_t] = torch.randn((len(hot), d), generator=g, device=dev, dtype=torch.bfloat16)
+    dy_in[hot_t] = torch.randn((len(hot), d), generator=g, device=dev, dtype=torch.bfloat16)
+    w = synth.mlp_inputs(128, K, d, F, seed=9491)
+    W1, gamma, W, Wd = (up(torch, dev, w[k], "bf16") for k in ("W1", "gamma", "W", "Wd"))
+    print("[parity] mlp bf16 M=2^23: coda_mlp_fwd, coda_mlp_bwd", flush=True)
+    z, y, r, gu, a = coda.mlp_fwd(X, W1, R, gamma, W, Wd, eps)
+    dX, dW1, dR, dW, dWd, dg = coda.mlp_bwd(X, W1, gamma, W, Wd, y, r, gu, a, dz, dy_in)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(M - 8, M), np.arange(5, M, 1 << 20), hot]))
+    rows_t = torch.from_numpy(rows).to(dev)
+    rest = torch.ones((M,), dtype=torch.bool, device=dev)
+    rest[hot_t] = False
+    nz_dX, nz_dR = int(torch.count_nonzero(dX[rest])), int(torch.count_nonzero(dR[rest]))
+    print("[parity] mlp bf16 M=2^23: oracle on the sampled and hot rows", flush=True)
+    W1h, gh, Wh, Wdh = (host(t) for t in (W1, gamma, W, Wd))
+    f = oracle.ref_mlp_fwd(host(X[rows_t]), W1h, host(R[rows_t]), gh, Wh, Wdh, eps)
+    b = oracle.ref_mlp_bwd(host(X[hot_t]), W1h, gh, Wh, Wdh, host(y[hot_t]), r[hot_t].cpu().numpy(),
+                           host(gu[hot_t]), host(a[hot_t]), host(dz[hot_t]), host(dy_in[hot_t]),
+                           dgu_round=oracle.bf16_rne)
+    errs = {"y_rows": rel(host(y[rows_t]), f["y"]), "gu_rows": rel(host(gu[rows_t]), f["gu"]),
+            "a_rows": rel(host(a[rows_t]), f["a"]), "z_rows": rel(host(z[rows_t]), f["z"]),
+            "dX_hot": rel(host(dX[hot_t]), b["dX"]), "dR_hot": rel(host(dR[hot_t]), b["dR"]),
+            "dW1": rel(host(dW1), b["dW1"]), "dW": rel(host(dW), b["dW"]), "dWd": rel(host(dWd), b["dWd"]),
+            "dgamma": rel(dg.cpu().numpy(), b["dgamma"])}
+    rr = float(np.max(np.abs(r[rows_t].cpu().numpy() - f["r"]) / f["r"]))
+    report("mlp bf16 M=2^23", {**errs, "r_rows": rr, "nonzero_dX_elsewhere": float(nz_dX),
+                               "nonzero_dR_elsewhere": float(nz_dR)})
+    del X, R, dz, dy_in, z, y, r, gu, a, dX, dR, rest   # ~28 GB: give it back before the next test
+    torch.cuda.empty_cache()
+    assert nz_dX == 0 and nz_dR == 0
+    assert rr <= R_TOL
+    for k, v in errs.items():
+        if k != "dgamma":
+            assert v <= BF16_TOL, (k, v)
+    assert errs["dgamma"] <= DGAMMA_TOL
+
+
 # ------------------------------------------- LM-head GEMM with cross-entropy
 
 CE_TOL = 1e-4      # fp32 loss / lse: max|diff| / max|ref|
