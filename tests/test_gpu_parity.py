@@ -156,6 +156,39 @@ def test_coda_max_rows(torch_dev):
     assert errs["dgamma"] <= DGAMMA_TOL
 
 
+def test_coda_max_row_length(torch_dev):
+    """The longest accepted row, d = 2^21, in bf16 (M = K = N = 8): 8192
+    partial sums per row combined in K2's epilogue, 8192 column tiles in K1,
+    B1 and the weight-gradient GEMMs, and K2 and the dX GEMM contracting over
+    2^21 in one workgroup each.  Checked against the whole oracle."""
+    torch, dev = torch_dev
+    import gemm_epilogue_fusion_gemm1_amd as coda
+    M, K, d, N = 8, 8, 1 << 21, 8
+    eps = 1e-6
+    print("[parity] coda bf16 d=2^21: inputs", flush=True)
+    h = synth.coda_inputs(M, K, d, N, seed=9590, dtype="bf16")
+    t = {k: up(torch, dev, v, "bf16") for k, v in h.items()}
+    print("[parity] coda bf16 d=2^21: coda_fwd, coda_bwd", flush=True)
+    z, y, r = coda.fwd(t["X"], t["W1"], t["R"], t["gamma"], t["W2"], eps)
+    dX, dW1, dR, dW2, dg = coda.bwd(t["X"], t["W1"], t["gamma"], t["W2"], y, r, t["dz"])
+    torch.cuda.synchronize()
+    print("[parity] coda bf16 d=2^21: oracle", flush=True)
+    f = oracle.ref_fwd(h["X"], h["W1"], h["R"], h["gamma"], h["W2"], eps)
+    b = oracle.ref_bwd(h["X"], h["W1"], h["gamma"], h["W2"], oracle.bf16_rne(f["y"]), f["r"], h["dz"])
+    errs = {"y": rel(host(y), f["y"]), "z": rel(host(z), f["z"]),
+            "dX": rel(host(dX), b["dX"]), "dW1": rel(host(dW1), b["dW1"]),
+            "dR": rel(host(dR), b["dR"]), "dW2": rel(host(dW2), b["dW2"]),
+            "dgamma": rel(dg.cpu().numpy(), b["dgamma"])}
+    rr = float(np.max(np.abs(r.cpu().numpy() - f["r"]) / f["r"]))
+    report("coda bf16 d=2^21", {**errs, "r": rr})
+    del t, z, y, dX, dW1, dR, dW2, f, b
+    torch.cuda.empty_cache()
+    for k in ("y", "z", "dX", "dW1", "dR", "dW2"):
+        assert errs[k] <= BF16_TOL, (k, errs[k])
+    assert rr <= R_TOL
+    assert errs["dgamma"] <= DGAMMA_TOL
+
+
 @pytest.mark.parametrize("shape", [(128, 256, 256, 512), (132, 260, 196, 68), (4, 4, 4, 4)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_coda_fwd_f32(torch_dev, shape):
